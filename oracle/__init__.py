@@ -1,0 +1,235 @@
+"""CPU oracle for NF4 double-quantized storage and the NF4 + LoRA linear layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the benchmark's ``cpu_baseline`` leg, never by the GPU product path.
+
+The arithmetic lives in ``nf4_oracle.c`` (plain C, fp64 accumulation, no FMA
+contraction); this module builds it with gcc, loads it with ctypes and converts
+numpy arrays in and out. See the C file's header for the passages each function
+follows and for the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nf4_oracle.c")
+_LIB = os.path.join(_HERE, "libnf4_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library with gcc (always, when force is true)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            lib.orc_norm_ppf.restype = ctypes.c_double
+            lib.orc_norm_ppf.argtypes = [ctypes.c_double]
+            lib.orc_nf4_table.argtypes = [P, P]
+            lib.orc_dyn8_table.argtypes = [P, P]
+            lib.orc_thresholds.argtypes = [P, ctypes.c_int, P]
+            lib.orc_encode_array.argtypes = [P, ctypes.c_int, P, I64, P]
+            lib.orc_layout.argtypes = [I64, ctypes.c_int, P]
+            lib.orc_quantize.restype = ctypes.c_int
+            lib.orc_quantize.argtypes = [P, I64, ctypes.c_int, P, P, P, P, P]
+            lib.orc_dequantize.argtypes = [P, I64, ctypes.c_int, P, P, P, ctypes.c_float, P, P]
+            lib.orc_linear_fwd.argtypes = [P, I64, I64, P, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
+            lib.orc_linear_bwd_input.argtypes = [P, I64, I64, P, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
+            lib.orc_lora_grad.argtypes = [P, P, I64, I64, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
+            lib.orc_set_threads.argtypes = [ctypes.c_int]
+            lib.orc_get_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())
+
+
+# --------------------------------------------------------------------------- tables
+
+def norm_ppf(p: float) -> float:
+    return float(_load().orc_norm_ppf(float(p)))
+
+
+def nf4_table(f64: bool = False) -> np.ndarray:
+    t64 = np.zeros(16, np.float64)
+    t32 = np.zeros(16, np.float32)
+    _load().orc_nf4_table(_ptr(t64), _ptr(t32))
+    return t64 if f64 else t32
+
+
+def dyn8_table(f64: bool = False) -> np.ndarray:
+    t64 = np.zeros(256, np.float64)
+    t32 = np.zeros(256, np.float32)
+    _load().orc_dyn8_table(_ptr(t64), _ptr(t32))
+    return t64 if f64 else t32
+
+
+def thresholds(table: np.ndarray) -> np.ndarray:
+    table = _c(table, np.float32)
+    thr = np.zeros(table.size - 1, np.float32)
+    _load().orc_thresholds(_ptr(table), int(table.size), _ptr(thr))
+    return thr
+
+
+def encode(thr: np.ndarray, x: np.ndarray) -> np.ndarray:
+    thr = _c(thr, np.float32)
+    x = _c(x, np.float32).ravel()
+    out = np.zeros(x.size, np.uint8)
+    _load().orc_encode_array(_ptr(thr), int(thr.size), _ptr(x), int(x.size), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------- storage
+
+def layout(n: int, double_quant: bool) -> Dict[str, int]:
+    out = np.zeros(8, np.int64)
+    _load().orc_layout(int(n), int(bool(double_quant)), _ptr(out))
+    keys = ["codes", "scales", "nested", "offset", "device_bytes", "total_bytes", "nb", "nn"]
+    return {k: int(v) for k, v in zip(keys, out)}
+
+
+def quantize(w: np.ndarray, double_quant: bool = True) -> Dict[str, np.ndarray]:
+    """Quantize a flat (or flattened row-major) fp32 weight array.
+
+    Returns codes u8[ceil(n/2)], absmax f32[nb] and, with double quantization,
+    qabs u8[nb], nested f32[nn] and offset f32[1]. Raises ValueError on
+    non-finite weights."""
+    w = _c(w, np.float32).ravel()
+    n = w.size
+    lay = layout(n, double_quant)
+    codes = np.zeros(lay["codes"], np.uint8)
+    absmax = np.zeros(lay["nb"], np.float32)
+    qabs = np.zeros(lay["nb"] if double_quant else 0, np.uint8)
+    nested = np.zeros(lay["nn"] if double_quant else 0, np.float32)
+    offset = np.zeros(1 if double_quant else 0, np.float32)
+    rc = _load().orc_quantize(_ptr(w), n, int(bool(double_quant)), _ptr(codes), _ptr(absmax),
+                              _ptr(qabs) if double_quant else None, _ptr(nested) if double_quant else None,
+                              _ptr(offset) if double_quant else None)
+    if rc != 0:
+        raise ValueError("non-finite weight")
+    out = dict(n=n, double_quant=bool(double_quant), codes=codes, absmax=absmax)
+    if double_quant:
+        out.update(qabs=qabs, nested=nested, offset=offset)
+    return out
+
+
+def dequantize(q: Dict[str, np.ndarray], out: str = "f32") -> np.ndarray:
+    """Reconstruct the weights of a packed tensor from `quantize` (or one with the
+    same keys). out='f32' gives fp32 values, out='bf16' gives uint16 bf16 bits."""
+    n = int(q["n"])
+    dq = bool(q["double_quant"])
+    codes = _c(q["codes"], np.uint8)
+    absmax = _c(q["absmax"], np.float32) if not dq else None
+    qabs = _c(q["qabs"], np.uint8) if dq else None
+    nested = _c(q["nested"], np.float32) if dq else None
+    offset = float(np.float32(q["offset"][0])) if dq else 0.0
+    f = np.zeros(n, np.float32) if out == "f32" else None
+    h = np.zeros(n, np.uint16) if out == "bf16" else None
+    _load().orc_dequantize(_ptr(codes), n, int(dq), _ptr(absmax), _ptr(qabs), _ptr(nested),
+                           ctypes.c_float(offset), _ptr(f), _ptr(h))
+    return f if out == "f32" else h
+
+
+# --------------------------------------------------------------------------- bf16 helpers
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact: the bits become the top half)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------- linear
+
+def linear_fwd(x: np.ndarray, W: np.ndarray, A: Optional[np.ndarray] = None, B: Optional[np.ndarray] = None,
+               s: float = 0.0):
+    """y = x W^T + s (x A^T) B^T in fp64. x [M,K] and W [N,K] hold fp32 values
+    (bf16 operands are passed as their exact fp32 values). Returns (y, T)."""
+    x = _c(x, np.float32)
+    W = _c(W, np.float32)
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    r = 0 if A is None else int(A.shape[0])
+    A = _c(A, np.float32) if r else None
+    B = _c(B, np.float32) if r else None
+    y = np.zeros((M, N), np.float64)
+    T = np.zeros((M, r), np.float64)
+    _load().orc_linear_fwd(_ptr(x), M, K, _ptr(W), N, _ptr(A), _ptr(B), r, ctypes.c_float(np.float32(s)),
+                           _ptr(y), _ptr(T) if r else None)
+    return y, T
+
+
+def linear_bwd_input(dy: np.ndarray, W: np.ndarray, A: Optional[np.ndarray] = None,
+                     B: Optional[np.ndarray] = None, s: float = 0.0):
+    """dX = dY W + s (dY B) A in fp64. Returns (dX, U)."""
+    dy = _c(dy, np.float32)
+    W = _c(W, np.float32)
+    M, N = dy.shape
+    K = W.shape[1]
+    assert W.shape[0] == N
+    r = 0 if A is None else int(A.shape[0])
+    A = _c(A, np.float32) if r else None
+    B = _c(B, np.float32) if r else None
+    dx = np.zeros((M, K), np.float64)
+    U = np.zeros((M, r), np.float64)
+    _load().orc_linear_bwd_input(_ptr(dy), M, N, _ptr(W), K, _ptr(A), _ptr(B), r,
+                                 ctypes.c_float(np.float32(s)), _ptr(dx), _ptr(U) if r else None)
+    return dx, U
+
+
+def lora_grad(x: np.ndarray, dy: np.ndarray, T: np.ndarray, U: Optional[np.ndarray], s: float,
+              fa: bool = False):
+    """dA = s U^T x (None when fa, LoRA-FA) and dB = s dY^T T, in fp64."""
+    x = _c(x, np.float32)
+    dy = _c(dy, np.float32)
+    M, K = x.shape
+    N = dy.shape[1]
+    T = _c(T, np.float64)
+    r = T.shape[1]
+    Uc = None if fa else _c(U, np.float64)
+    dA = None if fa else np.zeros((r, K), np.float64)
+    dB = np.zeros((N, r), np.float64)
+    _load().orc_lora_grad(_ptr(x), _ptr(dy), M, K, N, _ptr(T), _ptr(Uc), r, ctypes.c_float(np.float32(s)),
+                          _ptr(dA), _ptr(dB))
+    return dA, dB
+
+
+def lora_scale(alpha: float, r: int, rslora: bool = False) -> np.float32:
+    """Resolved adapter scale s = alpha / r (LoRA) or alpha / sqrt(r) (rsLoRA),
+    formed in fp64 and rounded once to fp32."""
+    return np.float32(alpha / (np.sqrt(r) if rslora else r))

@@ -1,0 +1,236 @@
+"""Pins of the oracle's quantize / double-quantize / dequantize.
+
+Format: Aner docs, "Native model adaptation and NF4", section "Packed NF4 and
+the portable QLoRA profile"; determinism: Soup gate results, "P3 is solved".
+The checks use facts that do not depend on the oracle's own code: a
+hand-derived worked example, nearest-code search by argmin (no thresholds),
+exact special cases, the round-trip error bound implied by nearest rounding,
+and torch's own bf16 conversion.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "nf4_worked_example.json")))
+
+
+def unpack(codes: np.ndarray, n: int) -> np.ndarray:
+    hi = codes >> 4
+    lo = codes & 0x0F
+    return np.stack([hi, lo], axis=1).ravel()[:n]
+
+
+def blocks(a: np.ndarray, size: int):
+    return [a[i:i + size] for i in range(0, a.size, size)]
+
+
+def weights(n, seed=7, outliers=True):
+    if outliers:
+        return workloads.weight_with_outliers((n,), seed=seed).numpy()
+    return workloads.normal_f32((n,), 0.02, seed).numpy()
+
+
+# ----------------------------------------------------------------------------- worked example
+
+def test_worked_example(orc):
+    c4 = orc.nf4_table()
+    w = np.concatenate([np.float32(2.0) * c4[np.arange(64) % 16], np.zeros(64, np.float32),
+                        np.array([-0.5], np.float32)]).astype(np.float32)
+    assert w.size == GOLD["n"]
+    for dq in (False, True):
+        q = orc.quantize(w, double_quant=dq)
+        assert q["codes"].tobytes().hex() == GOLD["expected_codes_hex"]
+        np.testing.assert_array_equal(q["absmax"], np.array(GOLD["expected_absmax"], np.float32))
+    q = orc.quantize(w, double_quant=False)
+    r = orc.dequantize(q)
+    np.testing.assert_array_equal(r[:64], w[:64])
+    np.testing.assert_array_equal(r[64:128], np.zeros(64, np.float32))
+    assert r[128] == np.float32(-0.5)
+
+
+# ----------------------------------------------------------------------------- codes
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 1001, 16385, 70001])
+def test_codes_are_nearest(orc, n):
+    w = weights(n, seed=n)
+    q = orc.quantize(w, double_quant=True)
+    c4 = orc.nf4_table().astype(np.float64)
+    codes = unpack(q["codes"], n)
+    if n % 2:
+        assert q["codes"][-1] & 0x0F == 0, "odd tail pads the low nibble with 0"
+    absmax = np.array([np.abs(b).max() for b in blocks(w, 64)], np.float32)
+    np.testing.assert_array_equal(q["absmax"], absmax)
+    a = np.repeat(absmax, 64)[:n]
+    x = (w / a).astype(np.float32)            # IEEE fp32 division
+    want = np.argmin(np.abs(x[:, None].astype(np.float64) - c4[None, :]), axis=1)  # first min = lower index
+    np.testing.assert_array_equal(codes, want)
+
+
+def test_repeat_is_byte_identical(orc):
+    w = weights(300_001, seed=3)
+    q1 = orc.quantize(w, True)
+    q2 = orc.quantize(w.copy(), True)
+    for k in ("codes", "qabs", "nested", "offset"):
+        assert q1[k].tobytes() == q2[k].tobytes()
+
+
+def test_nonfinite_rejected(orc):
+    w = weights(1000)
+    for bad in (np.nan, np.inf, -np.inf):
+        v = w.copy()
+        v[500] = bad
+        with pytest.raises(ValueError):
+            orc.quantize(v, True)
+
+
+# ----------------------------------------------------------------------------- double quantization
+
+def test_double_quant_fields(orc):
+    n = 64 * 1000 + 33
+    w = weights(n, seed=11)
+    q = orc.quantize(w, True)
+    absmax = q["absmax"]
+    nb = absmax.size
+    # mean of the block maxima: the fp64 sum is exact for these values (checked
+    # against the correctly rounded fsum), so the stored mean is fixed.
+    S = math.fsum(float(v) for v in absmax)
+    assert np.float32(S / nb) == q["offset"][0]
+    mu = q["offset"][0]
+    c = (absmax - mu).astype(np.float32)
+    m = np.array([np.abs(b).max() for b in blocks(c, 256)], np.float32)
+    np.testing.assert_array_equal(q["nested"], m)
+    d8 = orc.dyn8_table().astype(np.float64)
+    y = (c / np.repeat(m, 256)[:nb]).astype(np.float32)
+    want = np.argmin(np.abs(y[:, None].astype(np.float64) - d8[None, :]), axis=1)
+    np.testing.assert_array_equal(q["qabs"], want)
+
+
+def test_mean_small_example(orc):
+    # four blocks with maxima 1, 2, 3, 4 -> mean 2.5; centred 1.5 is the nested max
+    w = np.concatenate([np.full(64, v, np.float32) for v in (1.0, -2.0, 3.0, -4.0)])
+    q = orc.quantize(w, True)
+    assert q["offset"][0] == np.float32(2.5)
+    assert q["nested"][0] == np.float32(1.5)
+    d8 = orc.dyn8_table()
+    # centred values -1.5, -0.5, 0.5, 1.5 over 1.5: -1, -1/3, 1/3, 1
+    assert d8[q["qabs"][3]] == 1.0 and q["qabs"][0] == 0  # -1 -> nearest is the smallest entry
+    codes = unpack(q["codes"], w.size)
+    assert set(codes[:64]) == {15} and set(codes[64:128]) == {0}
+
+
+def test_constant_magnitude_reconstructs_exactly(orc):
+    rng = np.random.default_rng(5)
+    w = (np.where(rng.random(64 * 700) < 0.5, -1, 1) * 0.25).astype(np.float32)
+    q = orc.quantize(w, True)
+    assert q["offset"][0] == np.float32(0.25)
+    assert np.all(q["nested"] == 0) and np.all(q["qabs"] == 127)
+    np.testing.assert_array_equal(orc.dequantize(q), w)
+
+
+def test_zero_matrix(orc):
+    w = np.zeros(64 * 300 + 5, np.float32)
+    for dq in (False, True):
+        q = orc.quantize(w, dq)
+        assert np.all(unpack(q["codes"], w.size) == 7)
+        r = orc.dequantize(q)
+        assert np.all(r == 0)
+    q = orc.quantize(w, True)
+    assert q["offset"][0] == 0 and np.all(q["qabs"] == 127) and np.all(q["nested"] == 0)
+
+
+def test_block_max_reconstructs_exactly_single(orc):
+    w = weights(64 * 512, seed=21)
+    q = orc.quantize(w, False)
+    r = orc.dequantize(q)
+    for b, (wb, rb) in enumerate(zip(blocks(w, 64), blocks(r, 64))):
+        i = int(np.argmax(np.abs(wb)))
+        assert rb[i] == wb[i], b  # the max element sits on code 0 or 15 (= -1 or +1)
+
+
+# ----------------------------------------------------------------------------- round trip
+
+def _half_gaps(table):
+    t = table.astype(np.float64)
+    g = np.diff(t)
+    left = np.concatenate([[0.0], g]) / 2
+    right = np.concatenate([g, [0.0]]) / 2
+    return np.maximum(left, right)
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_round_trip_bound(orc, dq):
+    """|w - w_hat| <= a * halfgap(code) + |C4[code]| * |a - a'| + rounding, where the
+    nearest-code choice bounds the first term and the dynamic8 grid the second."""
+    n = 64 * 4096 + 17
+    w = weights(n, seed=99)
+    q = orc.quantize(w, dq)
+    r = orc.dequantize(q).astype(np.float64)
+    c4 = orc.nf4_table().astype(np.float64)
+    codes = unpack(q["codes"], n)
+    a = np.repeat(q["absmax"].astype(np.float64), 64)[:n]
+    eps = 2.0 ** -23
+    bound = a * (_half_gaps(c4)[codes] + eps) + np.abs(r) * eps
+    if dq:
+        d8 = orc.dyn8_table()
+        nb = q["absmax"].size
+        m = np.repeat(q["nested"].astype(np.float64), 256)[:nb]
+        ascale = m * (_half_gaps(d8).max() + 4 * eps) + q["absmax"] * 4 * eps
+        bound += np.abs(c4[codes]) * np.repeat(ascale, 64)[:n]
+    err = np.abs(w.astype(np.float64) - r)
+    assert np.all(err <= bound)
+    assert err.max() > 0.25 * bound.max()  # the bound is not vacuous
+
+
+def test_bf16_output_matches_torch_rounding(orc):
+    w = weights(64 * 2000 + 3, seed=4)
+    q = orc.quantize(w, True)
+    f = orc.dequantize(q, "f32")
+    h = orc.dequantize(q, "bf16")
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(h, ref)
+
+
+def test_normalisation_is_true_division(orc):
+    """Inputs placed within a few ulps of the decision boundaries, where
+    w * (1/a) and the correctly rounded w / a fall on different sides; the codes
+    must follow w / a (reading: IEEE division, round to nearest)."""
+    c4 = orc.nf4_table().astype(np.float64)
+    mids = (c4[:-1] + c4[1:]) / 2
+    rng = np.random.default_rng(123)
+    blocks_out, disagreements = [], 0
+    for a in rng.uniform(0.01, 0.1, 400).astype(np.float32):
+        cand = []
+        for mid in mids:
+            w0 = np.float32(mid * float(a))
+            for d in range(-6, 7):
+                w = np.float32(w0)
+                for _ in range(abs(d)):
+                    w = np.nextafter(w, np.float32(np.inf if d > 0 else -np.inf))
+                if abs(w) < a:
+                    cand.append(w)
+        cand = np.array(cand, np.float32)
+        x_div = (cand / a).astype(np.float32)
+        x_rcp = (cand * np.float32(np.float32(1) / a)).astype(np.float32)
+        code_div = np.argmin(np.abs(x_div[:, None].astype(np.float64) - c4[None, :]), axis=1)
+        code_rcp = np.argmin(np.abs(x_rcp[:, None].astype(np.float64) - c4[None, :]), axis=1)
+        pick = cand[code_div != code_rcp][:63]
+        disagreements += pick.size
+        if pick.size:
+            blk = np.zeros(64, np.float32)
+            blk[0] = a
+            blk[1:1 + pick.size] = pick
+            blocks_out.append(blk)
+    assert disagreements > 20
+    w = np.concatenate(blocks_out)
+    q = orc.quantize(w, False)
+    codes = unpack(q["codes"], w.size)
+    a = np.repeat(q["absmax"], 64)
+    x = (w / a).astype(np.float32)
+    want = np.argmin(np.abs(x[:, None].astype(np.float64) - c4[None, :]), axis=1)
+    np.testing.assert_array_equal(codes, want)
