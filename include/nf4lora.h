@@ -1,0 +1,180 @@
+/*
+ * nf4lora.h - C ABI of the MI355X (gfx950) NF4 double-quantized weight store
+ * and the fused NF4 + LoRA linear layer.
+ *
+ * What the operations compute (the pages' definitions):
+ *  - Storage. Aner docs "Native model adaptation and NF4", section "Packed NF4
+ *    and the portable QLoRA profile": each matrix is split into 64-element
+ *    blocks of its flattened row-major elements; each block stores its
+ *    absolute maximum and one 4-bit index into the 16-value NF4 codebook per
+ *    element, two indices per byte. With double quantization the block maxima
+ *    are centred by their FP32 mean and coded with the signed dynamic8
+ *    codebook in blocks of 256 maxima. Soup "NF4 Layer Streaming - Gate
+ *    results", section "P3 is solved": N/2 + N/64 + N/4096 + 4 bytes per
+ *    N-element weight; the two code tables are the same for every weight.
+ *  - Decoding. Aner native training accelerated qualification (31 Oct 2026),
+ *    key jit.kernel_identity: decoding is separately rounded fp32 operations
+ *    (no fused multiply-add) and uses no global decoded scratch; Aner docs
+ *    section "Mixed precision keeps stable state in FP32": decoded weights are
+ *    rounded to the half type before the multiply, accumulation is FP32, and
+ *    adapter contractions stay FP32.
+ *  - Linear layer. Aner docs sections "Adapter API" and "LoRA FA includes
+ *    gradient preconditioning": y = x W^T + s (x A^T) B^T with s = alpha/rank
+ *    (rsLoRA: alpha/sqrt(rank)); the input gradient runs through the frozen
+ *    base and no base-weight gradient exists; LoRA-FA freezes A.
+ *
+ * Exact format (readings where the pages are silent are marked READING):
+ *  - n elements, nb = ceil(n/64) blocks, nn = ceil(nb/256) nested blocks, all
+ *    over the flattened row-major matrix (blocks may straddle rows).
+ *  - codes: ceil(n/2) bytes; element 2p is the HIGH nibble of byte p, element
+ *    2p+1 the low nibble; an odd n leaves a zero low nibble (READING).
+ *  - code of w in block b: a = max|w| over b; if a == 0 the code is 7 (the 0.0
+ *    entry, READING); else x = w / a (IEEE fp32 division, round to nearest)
+ *    and the code is the nearest NF4 entry, ties to the lower index (READING).
+ *  - single quant: scales = fp32 absmax[nb].
+ *  - double quant: offset mu = fp32( fp64 pairwise sum of absmax[0..nb), in
+ *    index order, zero-padded to a power of two / nb ) (READING: the pages fix
+ *    only "global FP32 mean"); c_b = fl32(absmax_b - mu); nested[j] =
+ *    max |c_b| over nested block j; scales = u8 qabs[nb], qabs_b = nearest
+ *    dynamic8 entry to fl32(c_b / nested[j]) (ties lower), or 127 (the 0.0
+ *    entry) when nested[j] == 0.
+ *  - decode: a'_b = absmax_b (single) or fl32(fl32(D8[qabs_b] * nested[j]) + mu)
+ *    (double); w_hat = fl32(C4[code] * a'_b); bf16 output = round-to-nearest-
+ *    even of w_hat.
+ *
+ * Conventions for every entry point:
+ *  - Memory: every array argument is a DEVICE pointer owned by the caller,
+ *    row-major and contiguous; the library allocates nothing, keeps no pointer
+ *    after returning, and has no mutable global state except a once-per-device
+ *    capability check. Calls are thread-safe.
+ *  - Streams: work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without synchronizing. Buffers must stay
+ *    valid until the stream has run the work.
+ *  - Shapes follow nn.Linear: x [M,K], weight [N,K] (N outputs, K inputs),
+ *    y [M,N], A [r,K], B [N,r], T = x A^T [M,r], U = dY B [M,r]. A, B, T, U,
+ *    dA, dB are fp32; x, y, dY, dX are of the call's dtype.
+ *  - Alignment: packed `codes`, and x / y / dY / dX / out pointers, must be
+ *    16-byte aligned (NF4_EALIGN otherwise). Any M, N, K >= 1 is accepted.
+ *  - Errors: 0 (NF4_OK) or a negative NF4_E* code. Every argument error is
+ *    detected on the host before anything is enqueued. Data-dependent errors
+ *    (non-finite weights) are written to an optional device status word. No
+ *    C++ exception crosses this interface.
+ *  - Device: the current HIP device must be gfx950 (NF4_EUNSUPPORTED otherwise).
+ */
+#ifndef NF4LORA_H
+#define NF4LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4LORA_ABI_VERSION 1
+
+enum nf4_status {
+  NF4_OK = 0,
+  NF4_EINVAL = -1,       /* null pointer, non-positive size, bad rank or flag */
+  NF4_EALIGN = -2,       /* a pointer that must be 16-byte aligned is not */
+  NF4_EUNSUPPORTED = -3, /* dtype not F32/BF16, or the device is not gfx950 */
+  NF4_EDEVICE = -4,      /* HIP runtime or launch failure */
+  NF4_ENONFINITE = -5,   /* written to the status word: a weight was NaN/Inf */
+  NF4_EWORKSPACE = -6    /* workspace pointer NULL or smaller than required */
+};
+
+typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
+
+/* Opaque stream handle: pass a hipStream_t (or NULL). */
+typedef void* nf4_stream_t;
+
+/* Byte counts of one packed matrix (see nf4_layout). */
+typedef struct nf4_sizes {
+  int64_t codes_bytes;     /* ceil(n/2) */
+  int64_t scales_bytes;    /* 4*nb (single) or nb (double) */
+  int64_t nested_bytes;    /* 4*nn (double) or 0 */
+  int64_t offset_bytes;    /* 4 (double) or 0 */
+  int64_t nb;              /* ceil(n/64) */
+  int64_t nn;              /* ceil(nb/256) (double) or 0 */
+  int64_t quantize_workspace_bytes; /* scratch nf4_quantize needs */
+} nf4_sizes;
+
+/* One packed matrix. All pointers are device pointers owned by the caller.
+ * double_quant == 0: scales is float[nb]; nested and offset are unused.
+ * double_quant == 1: scales is uint8_t[nb]; nested is float[nn]; offset
+ *                    points to one float. */
+typedef struct nf4_tensor {
+  uint8_t* codes;
+  void* scales;
+  float* nested;
+  float* offset;
+  int64_t n;
+  int32_t double_quant;
+} nf4_tensor;
+
+/* Sizes of the packed buffers for n elements (Aner docs "Packed NF4 and the
+ * portable QLoRA profile"; Soup gate results "P3 is solved"). Host-only; no
+ * device needed. Returns NF4_EINVAL for n < 1, a bad flag or out == NULL. */
+int nf4_layout(int64_t n, int double_quant, nf4_sizes* out);
+
+/* Host copies of the library's constant code tables: nf4[16] (QLoRA normal
+ * float, ascending, nf4[7] == 0) and dyn8[256] (signed dynamic tree,
+ * ascending, dyn8[127] == 0, dyn8[255] == +1). Host-only. */
+int nf4_code_tables(float nf4[16], float dyn8[256]);
+
+/* Quantize n fp32 weights `w` (device) into `out` (buffers sized by
+ * nf4_layout; out->n and out->double_quant must equal n and double_quant).
+ * `workspace` must hold quantize_workspace_bytes (may be NULL when that is 0).
+ * `status` (optional device int32) is set to 0 and then to NF4_ENONFINITE if
+ * any weight is NaN or infinite; the outputs are then unspecified.
+ * Deterministic: repeated calls give identical bytes. */
+int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* out, void* workspace,
+                 size_t workspace_bytes, int32_t* status, nf4_stream_t stream);
+
+/* Decode all n weights of `w` into `out` (device, fp32 or bf16, n elements):
+ * w_hat = fl32(C4[code] * a'_b), bf16 by round-to-nearest-even. */
+int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream);
+
+/* Fused forward: y = x W_hat^T + s (x A^T) B^T, W_hat decoded inside the
+ * matrix kernel (no decoded copy of W is written to memory). x [M,K] and y
+ * [M,N] are `dtype` (F32: fp32 weights; BF16: weights rounded to bf16 before
+ * the multiply); accumulation is fp32. r == 0 disables the adapter (A, B,
+ * t_out may be NULL); r in [1, 256] requires A [r,K], B [N,r] and t_out [M,r]
+ * (receives T = x A^T in fp32, kept for lora_grad). W->n must equal N*K. */
+int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
+                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out,
+                   nf4_stream_t stream);
+
+/* Fused input gradient through the frozen base: dX = dY W_hat + s (dY B) A.
+ * dY [M,N] and dX [M,K] are `dtype`. r == 0 disables the adapter; r >= 1
+ * requires A, B and u_out [M,r] (receives U = dY B in fp32). No weight
+ * gradient is produced for W. */
+int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W,
+                         int64_t K, const float* A, const float* B, int32_t r, float s, void* dx,
+                         float* u_out, nf4_stream_t stream);
+
+/* LoRA factor gradients: dA = s U^T x [r,K] and dB = s dY^T T [N,r] (fp32),
+ * sums over the M tokens in a fixed order (no atomics, run-to-run identical).
+ * LoRA-FA (A frozen): pass dA == NULL and u == NULL; only dB is computed.
+ * x [M,K] and dY [M,N] are `dtype`; t [M,r] and u [M,r] fp32 as produced by
+ * nf4_linear_fwd / nf4_linear_bwd_input. `workspace` must hold
+ * lora_grad_workspace_bytes(M, K, N, r, fa) bytes. */
+int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* t,
+              const float* u, int32_t r, float s, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+              nf4_stream_t stream);
+
+/* Workspace bytes lora_grad needs for these sizes (fa != 0: LoRA-FA). Returns
+ * a negative NF4_E* code for invalid sizes. Host-only. */
+int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
+
+/* Static text for a status code. */
+const char* nf4_status_string(int status);
+
+/* NF4LORA_ABI_VERSION of the built library. */
+int nf4lora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4LORA_H */

@@ -1,0 +1,166 @@
+// C ABI entry points (include/nf4lora.h): argument validation on the host,
+// then launches on the caller's stream. Every argument error is returned before
+// anything is enqueued; no exception leaves this file.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "nf4_internal.hpp"
+
+using namespace nf4;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::mutex g_device_mu;
+
+// The current device must be gfx950 (checked once per device).
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NF4_EDEVICE;
+  if (dev >= kMaxDevices) return NF4_EUNSUPPORTED;
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    std::lock_guard<std::mutex> lock(g_device_mu);
+    state = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NF4_EDEVICE;
+      state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+      g_device_ok[dev].store(state, std::memory_order_release);
+    }
+  }
+  return state == 1 ? NF4_OK : NF4_EUNSUPPORTED;
+}
+
+bool valid_dtype(nf4_dtype d) { return d == NF4_F32 || d == NF4_BF16; }
+
+// Structural checks of a packed tensor that holds n elements.
+int check_tensor(const nf4_tensor* t, int64_t n) {
+  if (!t || !t->codes || !t->scales) return NF4_EINVAL;
+  if (t->n != n || n < 1) return NF4_EINVAL;
+  if (t->double_quant != 0 && t->double_quant != 1) return NF4_EINVAL;
+  if (t->double_quant && (!t->nested || !t->offset)) return NF4_EINVAL;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 16)) return NF4_EALIGN;
+  if (t->double_quant && (!aligned(t->nested, 4) || !aligned(t->offset, 4))) return NF4_EALIGN;
+  return NF4_OK;
+}
+
+hipStream_t as_stream(nf4_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const nf4_tensor* W, const float* A,
+                  const float* B, int32_t r, float s, void* out, float* side, bool backward, nf4_stream_t stream) {
+  if (!valid_dtype(dt)) return NF4_EUNSUPPORTED;
+  if (!a || !out || M < 1 || K < 1 || N < 1) return NF4_EINVAL;
+  if (K > INT64_MAX / N) return NF4_EINVAL;
+  if (int rc = check_tensor(W, N * K)) return rc;
+  if (r < 0 || r > 256) return NF4_EINVAL;
+  if (r > 0 && (!A || !B || !side || r > (K < N ? K : N))) return NF4_EINVAL;
+  if (r > 0 && !std::isfinite(s)) return NF4_EINVAL;
+  if (!aligned(a, 16) || !aligned(out, 16)) return NF4_EALIGN;
+  if (r > 0 && (!aligned(A, 4) || !aligned(B, 4) || !aligned(side, 4))) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward};
+  return launch_linear(g, as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4lora_abi_version(void) { return NF4LORA_ABI_VERSION; }
+
+const char* nf4_status_string(int status) {
+  switch (status) {
+    case NF4_OK: return "ok";
+    case NF4_EINVAL: return "invalid argument";
+    case NF4_EALIGN: return "pointer not 16-byte aligned";
+    case NF4_EUNSUPPORTED: return "unsupported dtype or device (gfx950 required)";
+    case NF4_EDEVICE: return "HIP runtime or launch failure";
+    case NF4_ENONFINITE: return "non-finite weight";
+    case NF4_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int nf4_layout(int64_t n, int double_quant, nf4_sizes* out) {
+  if (!out || n < 1 || (double_quant != 0 && double_quant != 1)) return NF4_EINVAL;
+  const int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);
+  out->codes_bytes = (n + 1) / 2;
+  out->scales_bytes = double_quant ? nb : 4 * nb;
+  out->nested_bytes = double_quant ? 4 * nn : 0;
+  out->offset_bytes = double_quant ? 4 : 0;
+  out->nb = nb;
+  out->nn = double_quant ? nn : 0;
+  out->quantize_workspace_bytes = (int64_t)quantize_ws_bytes(n, double_quant);
+  return NF4_OK;
+}
+
+int nf4_code_tables(float nf4_out[16], float dyn8_out[256]) {
+  if (!nf4_out || !dyn8_out) return NF4_EINVAL;
+  std::memcpy(nf4_out, kHostNF4, sizeof(kHostNF4));
+  std::memcpy(dyn8_out, kHostDyn8, sizeof(kHostDyn8));
+  return NF4_OK;
+}
+
+int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* out, void* workspace,
+                 size_t workspace_bytes, int32_t* status, nf4_stream_t stream) {
+  if (!w || n < 1 || (double_quant != 0 && double_quant != 1)) return NF4_EINVAL;
+  if (int rc = check_tensor(out, n)) return rc;
+  if (out->double_quant != double_quant) return NF4_EINVAL;
+  if (!aligned(w, 16)) return NF4_EALIGN;
+  if (status && !aligned(status, 4)) return NF4_EALIGN;
+  const size_t need = quantize_ws_bytes(n, double_quant);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NF4_EWORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_quantize(w, n, out, workspace, status, as_stream(stream));
+}
+
+int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream) {
+  if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;
+  if (!w || !out) return NF4_EINVAL;
+  if (int rc = check_tensor(w, w->n)) return rc;
+  if (!aligned(out, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_dequantize(w, out_dtype, out, as_stream(stream));
+}
+
+int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
+                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out,
+                   nf4_stream_t stream) {
+  return linear_common(x, dtype, M, K, N, W, A, B, r, s, y, t_out, false, stream);
+}
+
+int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W, int64_t K,
+                         const float* A, const float* B, int32_t r, float s, void* dx, float* u_out,
+                         nf4_stream_t stream) {
+  return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, true, stream);
+}
+
+int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
+  if (M < 1 || K < 1 || N < 1 || r < 1 || r > 256) return NF4_EINVAL;
+  return (int64_t)lora_grad_ws(M, K, N, r, fa);
+}
+
+int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* t,
+              const float* u, int32_t r, float s, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+              nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (M < 1 || K < 1 || N < 1 || r < 1 || r > 256) return NF4_EINVAL;
+  const bool fa = (dA == nullptr);
+  if (!dy || !t || !dB) return NF4_EINVAL;
+  if (!fa && (!x || !u)) return NF4_EINVAL;
+  if (!std::isfinite(s)) return NF4_EINVAL;
+  if (!aligned(dy, 16) || !aligned(t, 4) || !aligned(dB, 4)) return NF4_EALIGN;
+  if (!fa && (!aligned(x, 16) || !aligned(u, 4) || !aligned(dA, 4))) return NF4_EALIGN;
+  const size_t need = lora_grad_ws(M, K, N, r, fa);
+  if (!workspace || workspace_bytes < need) return NF4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_lora_grad(x, dy, dtype, M, K, N, t, fa ? nullptr : u, r, s, dA, dB, workspace, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the library's translation units (host side
+// launchers and small device helpers). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "../../include/nf4lora.h"
+#include "nf4_tables.inc"
+
+namespace nf4 {
+
+constexpr int64_t kBlock = 64;    // elements per absmax block
+constexpr int64_t kNested = 256;  // absmax values per nested block
+
+// Host copies of the constant tables (bit patterns), used by nf4_code_tables.
+extern const uint32_t kHostNF4[NF4_CODES_COUNT];
+extern const uint32_t kHostDyn8[DYN8_CODES_COUNT];
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Scratch layout of nf4_quantize with double quantization: fp32 absmax[nb]
+// (256-byte aligned) followed by fp64 partial sums[nn].
+inline size_t quantize_ws_bytes(int64_t n, int dq) {
+  if (!dq) return 0;
+  int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);
+  return round_up(sizeof(float) * (size_t)nb, 256) + sizeof(double) * (size_t)nn;
+}
+
+// Launchers (return NF4_OK or NF4_EDEVICE). Arguments are already validated.
+int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s);
+int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s);
+
+struct LinearArgs {
+  const void* a;        // x (forward) or dY (input gradient): [M, Kred]
+  nf4_dtype dtype;
+  int64_t M;
+  int64_t K;            // weight inputs (columns of W)
+  int64_t N;            // weight outputs (rows of W)
+  const nf4_tensor* W;
+  const float* A;       // [r, K]
+  const float* B;       // [N, r]
+  int32_t r;
+  float s;
+  void* out;            // y [M, N] or dX [M, K]
+  float* side;          // T = x A^T or U = dY B, [M, r]
+  bool backward;        // false: y = x W^T + s T B^T; true: dX = dY W + s U A
+};
+int launch_linear(const LinearArgs& a, hipStream_t s);
+
+size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
+int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
+                     const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st);
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EDEVICE; }
+
+}  // namespace nf4

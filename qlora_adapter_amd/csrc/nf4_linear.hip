@@ -1,0 +1,298 @@
+// Fused NF4 + LoRA linear layer for gfx950: forward y = x W^T + s (x A^T) B^T,
+// input gradient dX = dY W + s (dY B) A, and the LoRA gradients dA = s U^T x,
+// dB = s dY^T T (Aner docs "Adapter API", "LoRA FA includes gradient
+// preconditioning", "Mixed precision keeps stable state in FP32"; decoding as in
+// include/nf4lora.h). Weights are decoded inside the matrix kernels (no decoded
+// copy of W is written to memory) with the same separately rounded fp32
+// operations as nf4_dequantize, then rounded to bf16 on the bf16 path.
+//
+// This file holds the shape-general kernels: any M, N, K, either dtype, any
+// alignment of the row pitch. The large-tile bf16 kernels for 64-multiple
+// shapes live in nf4_gemm_fast.hip and are chosen by launch_linear when they
+// apply.
+#include "nf4_internal.hpp"
+#include "nf4_device.hpp"
+
+namespace nf4 {
+namespace {
+
+// ---------------------------------------------------------------------------
+// General fused linear: C[m][j] = sum_i A[m][i] * Wop[i][j] (+ LoRA epilogue)
+//   forward : A = x  [M, K], i = k, j = n, Wop[k][n] = W_hat[n][k]
+//   backward: A = dY [M, N], i = n, j = k, Wop[n][k] = W_hat[n][k]
+// Tile 64 (m) x 64 (j), reduction step 32; 4 waves in 2 x 2, each owning one
+// 32 x 32 MFMA accumulator. Operands are staged in LDS as [row][i] so that each
+// lane reads its 8 (bf16) or 1 (fp32) consecutive reduction elements.
+// ---------------------------------------------------------------------------
+constexpr int GT = 64, GR = 32, GPAD = 8;
+
+template <typename T, bool BWD, bool DQ>
+__global__ __launch_bounds__(256) void k_linear_general(const T* __restrict__ a, int64_t M, int64_t K, int64_t N,
+                                                        NF4View w, const float* __restrict__ Afac,
+                                                        const float* __restrict__ Bfac, int r, float s,
+                                                        const float* __restrict__ side, T* __restrict__ out) {
+  __shared__ T As[GT][GR + GPAD];
+  __shared__ T Bs[GT][GR + GPAD];
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_value(threadIdx.x);
+  const int64_t I = BWD ? N : K;  // reduction length
+  const int64_t J = BWD ? K : N;  // output columns
+  const int64_t m0 = (int64_t)blockIdx.y * GT, j0 = (int64_t)blockIdx.x * GT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const int lrow = tid >> 2, lcol = (tid & 3) * 8;  // loader: row, first of 8 reduction slots
+  const float mu = DQ ? w.offset[0] : 0.0f;
+  f32x16 acc = {};
+  __syncthreads();
+  for (int64_t i0 = 0; i0 < I; i0 += GR) {
+    // stage A rows m0..m0+63 and decoded weights for columns j0..j0+63
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t m = m0 + lrow, i = i0 + lcol + q;
+      As[lrow][lcol + q] = (m < M && i < I) ? a[m * I + i] : (T)0.0f;
+      const int64_t j = j0 + lrow;
+      float v = 0.0f;
+      if (j < J && i < I) {
+        const int64_t f = BWD ? i * K + j : j * K + i;  // flat weight index n*K + k
+        v = decode_one<DQ>(w, mu, lut, f);
+      }
+      Bs[lrow][lcol + q] = (T)v;
+    }
+    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ks = 0; ks < GR; ks += 16) {
+        bf16x8 av, bv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          av[e] = As[wm + (lane & 31)][ks + (lane >> 5) * 8 + e];
+          bv[e] = Bs[wj + (lane & 31)][ks + (lane >> 5) * 8 + e];
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < GR; ks += 2) {
+        const float av = As[wm + (lane & 31)][ks + (lane >> 5)];
+        const float bv = Bs[wj + (lane & 31)][ks + (lane >> 5)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // LoRA epilogue: forward adds s * T[m][rho] * B[n][rho]; backward adds
+  // s * U[m][rho] * A[rho][k]; fp32 products and sums (32x32x2 fp32 MFMA).
+  const int64_t mrow = m0 + wm + (lane & 31), jcol = j0 + wj + (lane & 31);
+  for (int rho0 = 0; rho0 < r; rho0 += 2) {
+    const int rho = rho0 + (lane >> 5);
+    float av = 0.0f, bv = 0.0f;
+    if (rho < r) {
+      if (mrow < M) av = s * side[mrow * r + rho];
+      if (jcol < J) bv = BWD ? Afac[(int64_t)rho * K + jcol] : Bfac[jcol * r + rho];
+    }
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t m = m0 + wm + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+    if (m < M && jcol < J) out[m * J + jcol] = (T)acc[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Adapter side product S[m][rho] = sum_i A[m][i] * R[i][rho] in fp32, i ascending:
+//   forward : A = x  [M, K], R[k][rho] = Afac[rho][k]   (T = x A^T)
+//   backward: A = dY [M, N], R[n][rho] = Bfac[n][rho]   (U = dY B)
+// A workgroup owns 16 rows; thread (row, g) owns rho = g, g+16, ...
+// ---------------------------------------------------------------------------
+constexpr int SR = 16, SI = 32;
+
+template <typename T, bool BWD>
+__global__ __launch_bounds__(256) void k_side(const T* __restrict__ a, int64_t M, int64_t I,
+                                              const float* __restrict__ fac, int r, float* __restrict__ outS) {
+  __shared__ float As[SR][SI + 1];
+  __shared__ float Rs[SI][kMaxRank + 1];
+  const int tid = threadIdx.x;
+  const int row = tid >> 4, g = tid & 15;
+  const int64_t m0 = (int64_t)blockIdx.x * SR;
+  float acc[kMaxRank / 16];
+#pragma unroll
+  for (int q = 0; q < kMaxRank / 16; ++q) acc[q] = 0.0f;
+  for (int64_t i0 = 0; i0 < I; i0 += SI) {
+    for (int e = tid; e < SR * SI; e += 256) {
+      const int rr = e / SI, ii = e % SI;
+      const int64_t m = m0 + rr, i = i0 + ii;
+      As[rr][ii] = (m < M && i < I) ? (float)a[m * I + i] : 0.0f;
+    }
+    for (int e = tid; e < SI * r; e += 256) {
+      const int ii = e / r, rho = e % r;
+      const int64_t i = i0 + ii;
+      Rs[ii][rho] = (i < I) ? (BWD ? fac[i * r + rho] : fac[(int64_t)rho * I + i]) : 0.0f;
+    }
+    __syncthreads();
+    for (int ii = 0; ii < SI; ++ii) {
+      const float av = As[row][ii];
+#pragma unroll
+      for (int q = 0; q < kMaxRank / 16; ++q) {
+        const int rho = g + 16 * q;
+        if (rho < r) acc[q] = fmaf(av, Rs[ii][rho], acc[q]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t m = m0 + row;
+  if (m < M) {
+#pragma unroll
+    for (int q = 0; q < kMaxRank / 16; ++q) {
+      const int rho = g + 16 * q;
+      if (rho < r) outS[m * r + rho] = acc[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LoRA gradients, stage 1: partial[c][rho][j] = sum over m in chunk c (in
+// order) of P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J].
+// Workgroup (column tile of 64, chunk c); thread (jj, g) owns rho = g, g+4, ...
+// Stage 2 sums the chunks in order c = 0, 1, ..., scales by s and writes dA
+// ([r][J] layout) or dB ([J][r] layout).
+// ---------------------------------------------------------------------------
+constexpr int LJ = 64, LM = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ P, const T* __restrict__ Q, int64_t M,
+                                                      int64_t J, int r, int64_t chunk, float* __restrict__ partial) {
+  __shared__ float Qs[LM][LJ + 1];
+  __shared__ float Ps[LM][kMaxRank + 1];
+  const int tid = threadIdx.x, jj = tid & 63, g = tid >> 6;
+  const int64_t j0 = (int64_t)blockIdx.x * LJ;
+  const int64_t c = blockIdx.y;
+  const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
+  float acc[kMaxRank / 4];
+#pragma unroll
+  for (int q = 0; q < kMaxRank / 4; ++q) acc[q] = 0.0f;
+  for (int64_t m0 = mb; m0 < me; m0 += LM) {
+    for (int e = tid; e < LM * LJ; e += 256) {
+      const int mm = e / LJ, jx = e % LJ;
+      const int64_t m = m0 + mm, j = j0 + jx;
+      Qs[mm][jx] = (m < me && j < J) ? (float)Q[m * J + j] : 0.0f;
+    }
+    for (int e = tid; e < LM * r; e += 256) {
+      const int mm = e / r, rho = e % r;
+      const int64_t m = m0 + mm;
+      Ps[mm][rho] = (m < me) ? P[m * r + rho] : 0.0f;
+    }
+    __syncthreads();
+    for (int mm = 0; mm < LM; ++mm) {
+      const float qv = Qs[mm][jj];
+#pragma unroll
+      for (int q = 0; q < kMaxRank / 4; ++q) {
+        const int rho = g + 4 * q;
+        if (rho < r) acc[q] = fmaf(Ps[mm][rho], qv, acc[q]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t j = j0 + jj;
+  if (j < J) {
+#pragma unroll
+    for (int q = 0; q < kMaxRank / 4; ++q) {
+      const int rho = g + 4 * q;
+      if (rho < r) partial[(c * r + rho) * J + j] = acc[q];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_lora_combine(const float* __restrict__ partial, int64_t chunks, int r,
+                                                      int64_t J, float s, bool transpose_out,
+                                                      float* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)r * J) return;
+  const int64_t rho = idx / J, j = idx % J;
+  float sum = 0.0f;
+  for (int64_t c = 0; c < chunks; ++c) sum += partial[(c * r + rho) * J + j];
+  const float v = s * sum;
+  if (transpose_out)
+    out[j * r + rho] = v;
+  else
+    out[rho * J + j] = v;
+}
+
+template <typename T>
+int run_linear_general(const LinearArgs& g, hipStream_t st) {
+  const NF4View w = make_view(g.W);
+  const int64_t I = g.backward ? g.N : g.K, J = g.backward ? g.K : g.N;
+  const T* a = static_cast<const T*>(g.a);
+  if (g.r > 0) {
+    const dim3 sg((unsigned)ceil_div(g.M, SR));
+    if (g.backward)
+      hipLaunchKernelGGL((k_side<T, true>), sg, dim3(256), 0, st, a, g.M, I, g.B, g.r, g.side);
+    else
+      hipLaunchKernelGGL((k_side<T, false>), sg, dim3(256), 0, st, a, g.M, I, g.A, g.r, g.side);
+  }
+  const dim3 grid((unsigned)ceil_div(J, GT), (unsigned)ceil_div(g.M, GT));
+  T* out = static_cast<T*>(g.out);
+#define NF4_GEN(BWD, DQ)                                                                                            \
+  hipLaunchKernelGGL((k_linear_general<T, BWD, DQ>), grid, dim3(256), 0, st, a, g.M, g.K, g.N, w, g.A, g.B, g.r, \
+                     g.s, g.side, out)
+  const bool dq = g.W->double_quant != 0;
+  if (g.backward && dq) NF4_GEN(true, true);
+  else if (g.backward) NF4_GEN(true, false);
+  else if (dq) NF4_GEN(false, true);
+  else NF4_GEN(false, false);
+#undef NF4_GEN
+  return launch_status();
+}
+
+}  // namespace
+
+int launch_linear(const LinearArgs& g, hipStream_t st) {
+  if (g.dtype == NF4_BF16) {
+    if (fast_linear_applies(g)) return launch_linear_fast(g, st);
+    return run_linear_general<__bf16>(g, st);
+  }
+  return run_linear_general<float>(g, st);
+}
+
+size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
+  const int64_t chunk = lora_chunk(M);
+  const int64_t chunks = ceil_div(M, chunk);
+  size_t bytes = round_up(sizeof(float) * (size_t)(chunks * r * N), 256);
+  if (!fa) bytes += round_up(sizeof(float) * (size_t)(chunks * r * K), 256);
+  return bytes;
+}
+
+int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
+                     const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st) {
+  const int64_t chunk = lora_chunk(M);
+  const int64_t chunks = ceil_div(M, chunk);
+  float* partB = static_cast<float*>(ws);
+  float* partA = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunks * r * N), 256));
+  // dB[n][rho] = s * sum_m dY[m][n] T[m][rho]
+  {
+    const dim3 grid((unsigned)ceil_div(N, LJ), (unsigned)chunks);
+    if (dt == NF4_BF16)
+      hipLaunchKernelGGL((k_lora_partial<__bf16>), grid, dim3(256), 0, st, t, static_cast<const __bf16*>(dy), M, N, r,
+                         chunk, partB);
+    else
+      hipLaunchKernelGGL((k_lora_partial<float>), grid, dim3(256), 0, st, t, static_cast<const float*>(dy), M, N, r,
+                         chunk, partB);
+    hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * N, 256)), dim3(256), 0, st, partB,
+                       chunks, r, N, s, true, dB);
+  }
+  // dA[rho][k] = s * sum_m U[m][rho] x[m][k]
+  if (dA) {
+    const dim3 grid((unsigned)ceil_div(K, LJ), (unsigned)chunks);
+    if (dt == NF4_BF16)
+      hipLaunchKernelGGL((k_lora_partial<__bf16>), grid, dim3(256), 0, st, u, static_cast<const __bf16*>(x), M, K, r,
+                         chunk, partA);
+    else
+      hipLaunchKernelGGL((k_lora_partial<float>), grid, dim3(256), 0, st, u, static_cast<const float*>(x), M, K, r,
+                         chunk, partA);
+    hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * K, 256)), dim3(256), 0, st, partA,
+                       chunks, r, K, s, false, dA);
+  }
+  return launch_status();
+}
+
+}  // namespace nf4

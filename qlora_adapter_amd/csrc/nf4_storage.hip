@@ -1,0 +1,292 @@
+// NF4 blockwise quantization with double quantization, and dequantization, for
+// gfx950. Format and rounding rules: include/nf4lora.h (Aner docs "Packed NF4 and
+// the portable QLoRA profile"; jit.kernel_identity "decode-separate-rn").
+//
+// Both directions are HBM-bound streams. Quantize reads 4 B/weight and writes
+// 0.5 B (+ scales); dequantize reads 0.5 B (+ 1/64 B of scales) and writes 2 B
+// (bf16) or 4 B (fp32). Every wave moves contiguous runs of 256 B to 1 KB per
+// instruction; block maxima are reduced across the 8 lanes that hold one block,
+// and the fp64 sum behind the double-quantization mean is formed as a fixed
+// pairwise tree so that it is identical on every run.
+#include "nf4_device.hpp"
+
+namespace nf4 {
+
+const uint32_t kHostNF4[NF4_CODES_COUNT] = {NF4_CODES_LIST};
+const uint32_t kHostDyn8[DYN8_CODES_COUNT] = {DYN8_CODES_LIST};
+
+namespace {
+
+constexpr uint32_t kNF4Thr[NF4_THRESHOLDS_COUNT] = {NF4_THRESHOLDS_LIST};
+
+// NF4 code of x in [-1, 1]: the number of thresholds strictly below x (the
+// thresholds are compile-time constants, so this is 15 compares with literals).
+__device__ __forceinline__ uint32_t nf4_code(float x) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < NF4_THRESHOLDS_COUNT; ++k) c += (x > __uint_as_float(kNF4Thr[k])) ? 1u : 0u;
+  return c;
+}
+
+// dynamic8 code of x in [-1, 1]: binary search for the number of the 255
+// thresholds strictly below x.
+__device__ __forceinline__ uint32_t dyn8_code(float x) {
+  uint32_t c = 0;
+#pragma unroll
+  for (uint32_t step = 128; step >= 1; step >>= 1)
+    if (x > __uint_as_float(c_dyn8_thr[c + step - 1])) c += step;
+  return c;
+}
+
+__global__ void k_set_status(int32_t* status) {
+  if (threadIdx.x == 0) *status = 0;
+}
+
+// One workgroup = 256 blocks of 64 weights = one nested block (16384 weights).
+// Wave w owns blocks [64w, 64w+64) of the group; in pass `it` lane l holds the
+// 8 weights starting at 512*it + 8*l of the wave's range, so 8 lanes hold one
+// block. Writes codes, absmax (to `absmax`), and with DQ the group's pairwise
+// fp64 sum of its 256 maxima (zero beyond nb) to partials[blockIdx.x].
+template <bool DQ>
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, int64_t n,
+                                                  uint8_t* __restrict__ codes, float* __restrict__ absmax,
+                                                  double* __restrict__ partials, int32_t* __restrict__ status) {
+  __shared__ float s_max[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nbytes = (n + 1) / 2;
+  const int64_t base = (int64_t)blockIdx.x * 16384 + (int64_t)wave * 4096 + 8 * lane;
+  bool bad = false;
+#pragma unroll 2
+  for (int it = 0; it < 8; ++it) {
+    const int64_t e0 = base + 512 * it;
+    float v[8];
+    if (e0 + 8 <= n) {
+      const float4 p = *reinterpret_cast<const float4*>(w + e0);
+      const float4 q = *reinterpret_cast<const float4*>(w + e0 + 4);
+      v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w; v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (e0 + j < n) ? w[e0 + j] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bad |= !isfinite(v[j]);
+      m = fmaxf(m, fabsf(v[j]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c = (m > 0.0f) ? nf4_code(v[j] / m) : 7u;  // IEEE division
+      if (e0 + j >= n) c = 0;                             // padding nibble past the end
+      // element 2p -> high nibble of byte p, element 2p+1 -> low nibble
+      packed |= c << (8 * (j >> 1) + ((j & 1) ? 0 : 4));
+    }
+    if (e0 + 8 <= n) {
+      *reinterpret_cast<uint32_t*>(codes + e0 / 2) = packed;
+    } else if (e0 < n) {
+      for (int p = 0; p < 4; ++p)
+        if (e0 / 2 + p < nbytes) codes[e0 / 2 + p] = (uint8_t)(packed >> (8 * p));
+    }
+    if ((lane & 7) == 0) {
+      const int local = wave * 64 + it * 8 + (lane >> 3);
+      s_max[local] = (e0 < n) ? m : 0.0f;
+      if (e0 < n) absmax[e0 / 64] = m;
+    }
+  }
+  if (bad && status) *status = NF4_ENONFINITE;
+  if (!DQ) return;
+  __syncthreads();
+  if (wave == 0) {
+    // Leaves 4l..4l+3 in tree order, then a butterfly that pairs lane l with
+    // l^1, l^2, ...: every step adds two adjacent, equally sized subtrees.
+    double t = ((double)s_max[4 * lane] + (double)s_max[4 * lane + 1]) +
+               ((double)s_max[4 * lane + 2] + (double)s_max[4 * lane + 3]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) t = t + __shfl_xor(t, off);
+    if (lane == 0) partials[blockIdx.x] = t;
+  }
+}
+
+// One workgroup. Pairwise fp64 sum of partials[0..C) zero-padded to a power
+// of two, then offset = fp32(sum / nb). Thread t sums an aligned run of L
+// leaves with a binary-counter stack (left + right at every level); the 256
+// thread sums are then combined by a butterfly inside each wave and by
+// (w0 + w1) + (w2 + w3) across the four waves.
+__global__ __launch_bounds__(256) void k_dq_mean(const double* __restrict__ partials, int64_t C, int64_t nb,
+                                                 float* __restrict__ offset) {
+  __shared__ double s_wave[4];
+  int64_t P = 1;
+  while (P < C) P <<= 1;
+  const int64_t L = P >= 256 ? P / 256 : 1;
+  const int64_t first = (int64_t)threadIdx.x * L;
+  double stack[48];
+  int top = 0;
+  for (int64_t i = 0; i < L; ++i) {
+    double v = (first + i < C) ? partials[first + i] : 0.0;
+    int lv = 0;
+    for (int64_t idx = i; idx & 1; idx >>= 1, ++lv) v = stack[lv] + v;
+    stack[lv] = v;
+    top = lv;
+  }
+  double t = stack[top];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) t = t + __shfl_xor(t, off);
+  if (lane == 0) s_wave[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double S = (s_wave[0] + s_wave[1]) + (s_wave[2] + s_wave[3]);
+    offset[0] = (float)(S / (double)nb);
+  }
+}
+
+// One wave per nested block j: lane l holds maxima 4l..4l+3 of the block.
+// c = fl32(absmax - mu); nested[j] = max |c|; qabs = dynamic8 code of c / m.
+__global__ __launch_bounds__(256) void k_dq_nested(const float* __restrict__ absmax, int64_t nb,
+                                                   const float* __restrict__ offset, uint8_t* __restrict__ qabs,
+                                                   float* __restrict__ nested) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t nn = (nb + 255) / 256;
+  if (j >= nn) return;
+  const float mu = offset[0];
+  const int64_t b0 = j * 256 + 4 * lane;
+  float c[4];
+  float m = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = (b0 + q < nb) ? __fsub_rn(absmax[b0 + q], mu) : 0.0f;
+    m = fmaxf(m, fabsf(c[q]));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  uint32_t packed = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) packed |= ((m > 0.0f) ? dyn8_code(c[q] / m) : 127u) << (8 * q);
+  if (b0 + 4 <= nb) {
+    *reinterpret_cast<uint32_t*>(qabs + b0) = packed;
+  } else {
+    for (int q = 0; q < 4; ++q)
+      if (b0 + q < nb) qabs[b0 + q] = (uint8_t)(packed >> (8 * q));
+  }
+  if (lane == 0) nested[j] = m;
+}
+
+// Decode scale of block b (separately rounded multiply and add, no FMA).
+template <bool DQ>
+__device__ __forceinline__ float block_scale(const void* scales, const float* nested, float mu, int64_t b) {
+  if (DQ) {
+    const uint8_t q = static_cast<const uint8_t*>(scales)[b];
+    return __fadd_rn(__fmul_rn(__uint_as_float(c_dyn8[q]), nested[b >> 8]), mu);
+  }
+  return static_cast<const float*>(scales)[b];
+}
+
+// A unit is the 8 weights of one 32-bit code word (bytes 4u..4u+3). Wave w of
+// group g handles units 256*(4g+w) + l + 64q, q = 0..3: each code load is 256
+// contiguous bytes per wave and each bf16 store 1 KB. Units past the last full
+// one (n not a multiple of 8) are decoded element by element by group 0.
+template <bool DQ, bool BF16>
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                                    const float* __restrict__ nested, const float* __restrict__ offset,
+                                                    int64_t n, void* __restrict__ out) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = __uint_as_float(c_nf4[threadIdx.x]);
+  __syncthreads();
+  const float mu = DQ ? offset[0] : 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t units = n / 8;
+  const int64_t ubase = ((int64_t)blockIdx.x * 4 + wave) * 256 + lane;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
+  uint32_t word[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t u = ubase + 64 * q;
+    word[q] = (u < units) ? words[u] : 0u;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t u = ubase + 64 * q;
+    if (u >= units) break;
+    const float a = block_scale<DQ>(scales, nested, mu, u >> 3);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t nib = (word[q] >> (8 * (j >> 1) + ((j & 1) ? 0 : 4))) & 15u;
+      v[j] = __fmul_rn(lut[nib], a);
+    }
+    if (BF16) {
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const __bf16 lo = (__bf16)v[2 * p], hi = (__bf16)v[2 * p + 1];  // round to nearest even
+        o[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      reinterpret_cast<uint4*>(out)[u] = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      float4* o = reinterpret_cast<float4*>(out) + 2 * u;
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t e = units * 8 + threadIdx.x; e < n; e += blockDim.x) {
+      const float a = block_scale<DQ>(scales, nested, mu, e >> 6);
+      const uint8_t byte = codes[e >> 1];
+      const float v = __fmul_rn(lut[(e & 1) ? (byte & 15) : (byte >> 4)], a);
+      if (BF16)
+        static_cast<__bf16*>(out)[e] = (__bf16)v;
+      else
+        static_cast<float*>(out)[e] = v;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s) {
+  const int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);
+  const int64_t groups = nn;  // one workgroup per 16384 weights
+  int32_t* st = status;
+  if (st) {
+    hipLaunchKernelGGL(k_set_status, dim3(1), dim3(64), 0, s, st);
+  }
+  // The quantize kernels write the status word only on a non-finite weight.
+  if (!t->double_quant) {
+    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes,
+                       static_cast<float*>(t->scales), nullptr, st);
+    return launch_status();
+  }
+  float* absmax = static_cast<float*>(ws);
+  double* partials = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)nb, 256));
+  hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes, absmax, partials, st);
+  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, partials, nn, nb, t->offset);
+  hipLaunchKernelGGL(k_dq_nested, dim3((unsigned)ceil_div(nn, 4)), dim3(256), 0, s, absmax, nb, t->offset,
+                     static_cast<uint8_t*>(t->scales), t->nested);
+  return launch_status();
+}
+
+int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s) {
+  const int64_t units = t->n / 8;
+  const unsigned groups = (unsigned)(units > 0 ? ceil_div(units, 1024) : 1);
+  const bool dq = t->double_quant != 0;
+  if (dq && dt == NF4_BF16)
+    hipLaunchKernelGGL((k_dequantize<true, true>), dim3(groups), dim3(256), 0, s, t->codes, t->scales, t->nested,
+                       t->offset, t->n, out);
+  else if (dq)
+    hipLaunchKernelGGL((k_dequantize<true, false>), dim3(groups), dim3(256), 0, s, t->codes, t->scales, t->nested,
+                       t->offset, t->n, out);
+  else if (dt == NF4_BF16)
+    hipLaunchKernelGGL((k_dequantize<false, true>), dim3(groups), dim3(256), 0, s, t->codes, t->scales, t->nested,
+                       t->offset, t->n, out);
+  else
+    hipLaunchKernelGGL((k_dequantize<false, false>), dim3(groups), dim3(256), 0, s, t->codes, t->scales,
+                       t->nested, t->offset, t->n, out);
+  return launch_status();
+}
+
+}  // namespace nf4

@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libnf4lora.so (include/nf4lora.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch
+supplies device memory and the current HIP stream. There is no fallback: if the
+library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
+
+NF4_F32, NF4_BF16 = 0, 1
+_DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
+
+EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_linear_fwd",
+           "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "nf4_status_string",
+           "nf4lora_abi_version"]
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {code})")
+        self.code = code
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("codes_bytes", ctypes.c_int64), ("scales_bytes", ctypes.c_int64),
+                ("nested_bytes", ctypes.c_int64), ("offset_bytes", ctypes.c_int64),
+                ("nb", ctypes.c_int64), ("nn", ctypes.c_int64),
+                ("quantize_workspace_bytes", ctypes.c_int64)]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("nested", ctypes.c_void_p),
+                ("offset", ctypes.c_void_p), ("n", ctypes.c_int64), ("double_quant", ctypes.c_int32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load() -> ctypes.CDLL:
+    """Load libnf4lora.so (built in-tree by qlora_adapter_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m qlora_adapter_amd.build` "
+                                   "(the NF4 path has no CPU fallback)")
+            lib = ctypes.CDLL(LIB_PATH)
+            P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+            lib.nf4_layout.argtypes = [I64, ctypes.c_int, ctypes.POINTER(_Sizes)]
+            lib.nf4_code_tables.argtypes = [P, P]
+            lib.nf4_quantize.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, ctypes.c_size_t, P, P]
+            lib.nf4_dequantize.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, P, P]
+            lib.nf4_linear_fwd.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32, F, P,
+                                           P, P]
+            lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
+                                                 F, P, P, P]
+            lib.lora_grad.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, P, I32, F, P, P, P, ctypes.c_size_t, P]
+            lib.lora_grad_workspace_bytes.restype = I64
+            lib.lora_grad_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int]
+            lib.nf4_status_string.restype = ctypes.c_char_p
+            lib.nf4_status_string.argtypes = [ctypes.c_int]
+            for fn in EXPORTS:
+                getattr(lib, fn).restype = getattr(lib, fn).restype or ctypes.c_int
+            lib.lora_grad_workspace_bytes.restype = I64
+            lib.nf4_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise NF4Error(fn, rc, load().nf4_status_string(rc).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# --------------------------------------------------------------------------- layout and tables
+
+def layout(n: int, double_quant: bool = True) -> dict:
+    s = _Sizes()
+    _check("nf4_layout", load().nf4_layout(int(n), int(bool(double_quant)), ctypes.byref(s)))
+    return {f: int(getattr(s, f)) for f, _ in _Sizes._fields_}
+
+
+def code_tables() -> Tuple[np.ndarray, np.ndarray]:
+    a = np.zeros(16, np.float32)
+    b = np.zeros(256, np.float32)
+    _check("nf4_code_tables", load().nf4_code_tables(a.ctypes.data_as(ctypes.c_void_p),
+                                                     b.ctypes.data_as(ctypes.c_void_p)))
+    return a, b
+
+
+def lora_scale(alpha: float, r: int, rslora: bool = False) -> float:
+    """s = alpha / r (LoRA) or alpha / sqrt(r) (rsLoRA), rounded once to fp32."""
+    return float(np.float32(alpha / (math.sqrt(r) if rslora else r)))
+
+
+# --------------------------------------------------------------------------- packed tensor
+
+@dataclasses.dataclass
+class NF4Tensor:
+    """A packed NF4 matrix on the device: codes, scales (fp32 absmax or u8 qabs),
+    nested fp32 maxima and the fp32 offset (double quantization)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    nested: Optional[torch.Tensor]
+    offset: Optional[torch.Tensor]
+    shape: Tuple[int, ...]
+    double_quant: bool
+
+    @property
+    def n(self) -> int:
+        return int(np.prod(self.shape))
+
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
+    def nbytes(self, with_offset: bool = True) -> int:
+        b = self.codes.numel() + self.scales.numel() * self.scales.element_size()
+        if self.double_quant:
+            b += self.nested.numel() * 4 + (4 if with_offset else 0)
+        return b
+
+    def c_struct(self) -> _Tensor:
+        return _Tensor(self.codes.data_ptr(), self.scales.data_ptr(),
+                       self.nested.data_ptr() if self.double_quant else None,
+                       self.offset.data_ptr() if self.double_quant else None,
+                       self.n, int(self.double_quant))
+
+    @staticmethod
+    def empty(shape, double_quant: bool = True, device="cuda") -> "NF4Tensor":
+        n = int(np.prod(shape))
+        lay = layout(n, double_quant)
+        codes = torch.empty(lay["codes_bytes"], dtype=torch.uint8, device=device)
+        if double_quant:
+            scales = torch.empty(lay["nb"], dtype=torch.uint8, device=device)
+            nested = torch.empty(lay["nn"], dtype=torch.float32, device=device)
+            offset = torch.empty(1, dtype=torch.float32, device=device)
+        else:
+            scales = torch.empty(lay["nb"], dtype=torch.float32, device=device)
+            nested = offset = None
+        return NF4Tensor(codes, scales, nested, offset, tuple(int(s) for s in shape), double_quant)
+
+
+# --------------------------------------------------------------------------- operations
+
+def quantize(w: torch.Tensor, double_quant: bool = True, out: Optional[NF4Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> NF4Tensor:
+    """Pack an fp32 device tensor (flattened row-major) into NF4."""
+    _dev(w, "w", torch.float32)
+    n = w.numel()
+    lay = layout(n, double_quant)
+    if out is None:
+        out = NF4Tensor.empty(tuple(w.shape), double_quant, w.device)
+    need = lay["quantize_workspace_bytes"]
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    st = out.c_struct()
+    _check("nf4_quantize", load().nf4_quantize(_ptr(w), n, int(bool(double_quant)), ctypes.byref(st),
+                                               _ptr(workspace), need, _ptr(status), _stream(w.device)))
+    return out
+
+
+def dequantize(t: NF4Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(t.shape, dtype=dtype, device=t.device)
+    _dev(out, "out", dtype)
+    st = t.c_struct()
+    _check("nf4_dequantize", load().nf4_dequantize(ctypes.byref(st), _DT[dtype], _ptr(out), _stream(t.device)))
+    return out
+
+
+def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
+               s: float = 0.0, y: Optional[torch.Tensor] = None,
+               t_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """y = x W^T + s (x A^T) B^T; returns (y, T) with T = x A^T (fp32) or None."""
+    _dev(x, "x")
+    M, K = x.shape
+    N = W.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if r and t_out is None:
+        t_out = torch.empty((M, r), dtype=torch.float32, device=x.device)
+    if r:
+        _dev(A, "A", torch.float32)
+        _dev(B, "B", torch.float32)
+    st = W.c_struct()
+    _check("nf4_linear_fwd", load().nf4_linear_fwd(_ptr(x), _DT[x.dtype], M, K, ctypes.byref(st), N, _ptr(A),
+                                                   _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _stream(x.device)))
+    return y, t_out
+
+
+def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None,
+                     B: Optional[torch.Tensor] = None, s: float = 0.0, dx: Optional[torch.Tensor] = None,
+                     u_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dX = dY W + s (dY B) A; returns (dX, U) with U = dY B (fp32) or None."""
+    _dev(dy, "dy")
+    M, N = dy.shape
+    K = W.shape[1]
+    r = 0 if A is None else A.shape[0]
+    if dx is None:
+        dx = torch.empty((M, K), dtype=dy.dtype, device=dy.device)
+    if r and u_out is None:
+        u_out = torch.empty((M, r), dtype=torch.float32, device=dy.device)
+    st = W.c_struct()
+    _check("nf4_linear_bwd_input",
+           load().nf4_linear_bwd_input(_ptr(dy), _DT[dy.dtype], M, N, ctypes.byref(st), K, _ptr(A), _ptr(B), r,
+                                       float(s), _ptr(dx), _ptr(u_out), _stream(dy.device)))
+    return dx, u_out
+
+
+def lora_grad_workspace_bytes(M: int, K: int, N: int, r: int, fa: bool = False) -> int:
+    v = int(load().lora_grad_workspace_bytes(M, K, N, r, int(fa)))
+    if v < 0:
+        _check("lora_grad_workspace_bytes", v)
+    return v
+
+
+def lora_grad(x: Optional[torch.Tensor], dy: torch.Tensor, T: torch.Tensor, U: Optional[torch.Tensor], s: float,
+              fa: bool = False, dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """dA = s U^T x ([r,K], None for LoRA-FA) and dB = s dY^T T ([N,r])."""
+    _dev(dy, "dy")
+    M, N = dy.shape
+    r = T.shape[1]
+    K = x.shape[1] if x is not None else 1
+    if not fa and dA is None:
+        dA = torch.empty((r, K), dtype=torch.float32, device=dy.device)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.float32, device=dy.device)
+    need = lora_grad_workspace_bytes(M, K, N, r, fa)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    _check("lora_grad", load().lora_grad(_ptr(x), _ptr(dy), _DT[dy.dtype], M, K, N, _ptr(T), _ptr(None if fa else U),
+                                         r, float(s), _ptr(None if fa else dA), _ptr(dB), _ptr(workspace), need,
+                                         _stream(dy.device)))
+    return (None if fa else dA), dB

@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/nf4lora.h declares, answers the host-only queries, and
+rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4lora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from qlora_adapter_amd import nf4lora
+    return nf4lora.load(), nf4lora
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"nf4_quantize", "nf4_dequantize", "nf4_linear_fwd", "nf4_linear_bwd_input", "lora_grad"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", lib[1].LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\S+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib[0], n)
+
+
+def test_abi_version(lib):
+    assert lib[0].nf4lora_abi_version() == 1
+
+
+def test_layout_matches_oracle(lib, orc):
+    for n in [1, 2, 63, 64, 65, 331776, 4096 * 14336, 3 * 16384 + 17]:
+        for dq in (False, True):
+            a = lib[1].layout(n, dq)
+            o = orc.layout(n, dq)
+            assert a["codes_bytes"] == o["codes"] and a["scales_bytes"] == o["scales"]
+            assert a["nested_bytes"] == o["nested"] and a["offset_bytes"] == o["offset"]
+            assert a["nb"] == o["nb"] and a["nn"] == o["nn"]
+
+
+def test_code_tables_match_oracle_bitwise(lib, orc):
+    c4, d8 = lib[1].code_tables()
+    np.testing.assert_array_equal(c4.view(np.uint32), orc.nf4_table().view(np.uint32))
+    np.testing.assert_array_equal(d8.view(np.uint32), orc.dyn8_table().view(np.uint32))
+
+
+def test_generated_tables_are_current():
+    """nf4_tables.inc is what gen_tables.py produces."""
+    import io
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("gen_tables", os.path.join(ROOT, "qlora_adapter_amd", "csrc",
+                                                                             "gen_tables.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    buf = io.StringIO()
+    mod.main(buf)
+    assert buf.getvalue() == open(os.path.join(ROOT, "qlora_adapter_amd", "csrc", "nf4_tables.inc")).read()
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        assert len(lib[0].nf4_status_string(code)) > 0
+
+
+def test_argument_errors_before_device(lib):
+    L, m = lib
+    EINVAL, EALIGN, EUNSUP, EWS = -1, -2, -3, -6
+    s = m._Sizes()
+    assert L.nf4_layout(0, 1, ctypes.byref(s)) == EINVAL
+    assert L.nf4_layout(10, 2, ctypes.byref(s)) == EINVAL
+    assert L.nf4_layout(10, 1, None) == EINVAL
+    # null weights, zero size, bad flag
+    t = m._Tensor(16, 16, 16, 16, 64, 1)
+    assert L.nf4_quantize(None, 64, 1, ctypes.byref(t), None, 0, None, None) == EINVAL
+    assert L.nf4_quantize(16, 0, 1, ctypes.byref(t), None, 0, None, None) == EINVAL
+    assert L.nf4_quantize(16, 64, 3, ctypes.byref(t), None, 0, None, None) == EINVAL
+    # tensor size mismatch and double-quant flag mismatch
+    t2 = m._Tensor(16, 16, 16, 16, 65, 1)
+    assert L.nf4_quantize(16, 64, 1, ctypes.byref(t2), None, 0, None, None) == EINVAL
+    assert L.nf4_quantize(16, 64, 0, ctypes.byref(t), None, 0, None, None) == EINVAL
+    # misaligned codes pointer
+    t3 = m._Tensor(17, 16, 16, 16, 64, 1)
+    assert L.nf4_quantize(16, 64, 1, ctypes.byref(t3), None, 0, None, None) == EALIGN
+    # missing workspace for double quantization
+    assert L.nf4_quantize(16, 64, 1, ctypes.byref(t), None, 0, None, None) == EWS
+    # unsupported dtype
+    assert L.nf4_dequantize(ctypes.byref(t), 7, 16, None) == EUNSUP
+    # linear: bad rank, missing adapter buffers, size mismatch
+    w = m._Tensor(16, 16, 16, 16, 64 * 32, 1)
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, None, None, 4, 1.0, 16, None, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 257, 1.0, 16, 16, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 33, None, None, 0, 0.0, 16, None, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 4, float("nan"), 16, 16, None) == EINVAL
+    assert L.nf4_linear_fwd(24, 1, 8, 64, ctypes.byref(w), 32, None, None, 0, 0.0, 16, None, None) == EALIGN
+    assert L.nf4_linear_bwd_input(16, 5, 8, 32, ctypes.byref(w), 64, None, None, 0, 0.0, 16, None, None) == EUNSUP
+    # lora_grad: rank bounds, workspace
+    assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 0, 1.0, 16, 16, 256, 1 << 20, None) == EINVAL
+    assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 4, 1.0, 16, 16, None, 0, None) == EWS
+    assert L.lora_grad_workspace_bytes(8, 64, 32, 0, 0) == EINVAL
+    assert L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 0) > L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 1)

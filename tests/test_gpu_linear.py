@@ -1,0 +1,134 @@
+"""GPU parity of the fused NF4 + LoRA linear layer against the fp64 CPU oracle.
+
+y = x W^T + s (x A^T) B^T, dX = dY W + s (dY B) A, dA = s U^T x, dB = s dY^T T
+(Aner docs "Adapter API", "LoRA FA includes gradient preconditioning", "Mixed
+precision keeps stable state in FP32"). The GPU quantizes W itself; the oracle
+quantizes the same fp32 W on the CPU and multiplies its own decoded weights
+(bf16-rounded on the bf16 path), so the two sides share only the inputs.
+Tolerances: tests/parity.py. B is random in every case so the adapter path is
+exercised (Soup gate results, "What the gate caught").
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.parity import assert_close, bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(M, K, N, r, dtype, seed=0, dy_std=1.0, device="cuda"):
+    lay = workloads.Linear("t", N, K, r)
+    inp = workloads.lora_inputs(lay, M, seed_offset=seed, device=device, dy_std=dy_std)
+    W = workloads.normal_f32((N, K), 0.02, workloads.weight_seed(seed), device)
+    if dtype == torch.float32:
+        inp["x"] = inp["x"].float()
+        inp["dy"] = inp["dy"].float()
+    inp["W"] = W
+    return inp
+
+
+def oracle_weight(orc, W: torch.Tensor, dtype, dq=True):
+    q = orc.quantize(W.cpu().numpy(), dq)
+    if dtype == torch.bfloat16:
+        return orc.bf16_bits_to_f32(orc.dequantize(q, "bf16")).reshape(W.shape)
+    return orc.dequantize(q, "f32").reshape(W.shape)
+
+
+def run_all(gpu, c, s, dq=True, fa=False):
+    Wq = gpu.quantize(c["W"], dq)
+    A, B = c.get("A"), c.get("B")
+    y, T = gpu.linear_fwd(c["x"], Wq, A, B, s)
+    dx, U = gpu.linear_bwd_input(c["dy"], Wq, A, B, s)
+    grads = gpu.lora_grad(c["x"], c["dy"], T, U, s, fa=fa) if A is not None else (None, None)
+    torch.cuda.synchronize()
+    return Wq, y, T, dx, U, grads
+
+
+CASES = [
+    # (M, K, N, r): the 576x576 layer, tails in every dimension, rank 1 and odd ranks
+    (512, 576, 576, 16),
+    (37, 100, 70, 3),
+    (1, 64, 1, 1),
+    (130, 192, 576, 8),
+    (64, 1536, 576, 8),
+    (200, 576, 1536, 16),
+    (33, 129, 65, 5),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,K,N,r", CASES)
+def test_linear_parity(gpu, orc, M, K, N, r, dt):
+    print(f"[linear] M={M} K={K} N={N} r={r} {dt}", flush=True)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    c = make_case(M, K, N, r, dtype, seed=M + K)
+    s = gpu.lora_scale(32.0, r)
+    Wq, y, T, dx, U, (dA, dB) = run_all(gpu, c, s)
+    Wref = oracle_weight(orc, c["W"], dtype)
+    x, dy = to_np(c["x"]), to_np(c["dy"])
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    y_ref, T_ref = orc.linear_fwd(x, Wref, A, B, s)
+    dx_ref, U_ref = orc.linear_bwd_input(dy, Wref, A, B, s)
+    assert_close(to_np(y), y_ref, dt, "y")
+    assert_close(to_np(dx), dx_ref, dt, "dx")
+    # adapter side products and gradients are fp32 arithmetic on both paths
+    assert_close(T.cpu().numpy(), T_ref, "f32", "T")
+    assert_close(U.cpu().numpy(), U_ref, "f32", "U")
+    dA_ref, dB_ref = orc.lora_grad(x, dy, T.cpu().numpy().astype(np.float64), U.cpu().numpy().astype(np.float64), s)
+    assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
+    assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
+    assert np.any(dA.cpu().numpy() != 0) and np.any(dB.cpu().numpy() != 0)
+
+
+def test_single_quant_and_rslora(gpu, orc):
+    M, K, N, r = 96, 256, 192, 8
+    c = make_case(M, K, N, r, torch.bfloat16, seed=5)
+    s = gpu.lora_scale(16.0, r, rslora=True)
+    _, y, T, dx, U, _ = run_all(gpu, c, s, dq=False)
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16, dq=False)
+    y_ref, _ = orc.linear_fwd(to_np(c["x"]), Wref, c["A"].cpu().numpy(), c["B"].cpu().numpy(), s)
+    dx_ref, _ = orc.linear_bwd_input(to_np(c["dy"]), Wref, c["A"].cpu().numpy(), c["B"].cpu().numpy(), s)
+    assert_close(to_np(y), y_ref, "bf16", "y")
+    assert_close(to_np(dx), dx_ref, "bf16", "dx")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_zero_B_equals_base_bitwise(gpu, dt):
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    c = make_case(256, 576, 576, 16, dtype, seed=2)
+    Wq = gpu.quantize(c["W"], True)
+    B0 = torch.zeros_like(c["B"])
+    y_lora, T = gpu.linear_fwd(c["x"], Wq, c["A"], B0, 2.0)
+    y_base, _ = gpu.linear_fwd(c["x"], Wq)
+    dx_lora, U = gpu.linear_bwd_input(c["dy"], Wq, c["A"], B0, 2.0)
+    dx_base, _ = gpu.linear_bwd_input(c["dy"], Wq)
+    torch.cuda.synchronize()
+    assert torch.equal(y_lora, y_base) and torch.equal(dx_lora, dx_base)
+    dA, dB = gpu.lora_grad(c["x"], c["dy"], T, U, 2.0)
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) > 0
+
+
+def test_repeat_bitwise_and_lora_fa(gpu):
+    c = make_case(300, 576, 192, 8, torch.bfloat16, seed=3)
+    r1 = run_all(gpu, c, 2.0)
+    r2 = run_all(gpu, c, 2.0)
+    for a, b in zip(r1[1:5], r2[1:5]):
+        assert torch.equal(a, b)
+    assert torch.equal(r1[5][0], r2[5][0]) and torch.equal(r1[5][1], r2[5][1])
+    _, dB_fa = gpu.lora_grad(None, c["dy"], r1[2], None, 2.0, fa=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dB_fa, r1[5][1])
+
+
+def test_fused_matches_dequantize_then_matmul(gpu):
+    """The fused kernel against torch's own GEMM on nf4_dequantize's bf16 output
+    (fp32 copies, so torch uses an fp32 GEMM)."""
+    c = make_case(256, 1024, 512, 0, torch.bfloat16, seed=9)
+    Wq = gpu.quantize(c["W"], True)
+    y, _ = gpu.linear_fwd(c["x"], Wq)
+    Wd = gpu.dequantize(Wq, torch.bfloat16).float()
+    ref = c["x"].float() @ Wd.T
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref.double().cpu().numpy(), "bf16", "y vs torch")

@@ -1,0 +1,106 @@
+"""GPU parity of nf4_quantize / nf4_dequantize against the CPU oracle: packed
+codes, scales, nested maxima, offset and decoded weights must match bit for bit
+(Aner docs "Packed NF4 and the portable QLoRA profile"; Soup gate results "P3
+is solved": repeated quantization is byte-identical)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.parity import bits
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 2, 7, 8, 9, 63, 64, 65, 127, 1001, 16383, 16384, 16385, 3 * 16384 + 17, 192 * 576, 576 * 576,
+         1536 * 576, 64 * 1000 + 33, 4 * 16384 * 3 + 5]
+
+
+def _gpu_quant(gpu, w: np.ndarray, dq: bool):
+    wt = torch.from_numpy(w).cuda()
+    status = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    q = gpu.quantize(wt, dq, status=status)
+    torch.cuda.synchronize()
+    return q, int(status.item())
+
+
+def _compare_packed(q, ref, dq):
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), ref["codes"])
+    if dq:
+        np.testing.assert_array_equal(q.scales.cpu().numpy(), ref["qabs"])
+        np.testing.assert_array_equal(bits(q.nested), ref["nested"].view(np.uint32))
+        np.testing.assert_array_equal(bits(q.offset), ref["offset"].view(np.uint32))
+    else:
+        np.testing.assert_array_equal(bits(q.scales), ref["absmax"].view(np.uint32))
+
+
+@pytest.mark.parametrize("dq", [True, False])
+@pytest.mark.parametrize("n", SIZES)
+def test_quantize_dequantize_bitexact(gpu, orc, n, dq):
+    print(f"[storage] n={n} dq={dq}", flush=True)
+    w = workloads.weight_with_outliers((n,), seed=n).numpy()
+    q, status = _gpu_quant(gpu, w, dq)
+    assert status == 0
+    ref = orc.quantize(w, dq)
+    _compare_packed(q, ref, dq)
+    f32 = gpu.dequantize(q, torch.float32)
+    b16 = gpu.dequantize(q, torch.bfloat16)
+    np.testing.assert_array_equal(bits(f32), orc.dequantize(ref, "f32").view(np.uint32))
+    np.testing.assert_array_equal(bits(b16), orc.dequantize(ref, "bf16"))
+
+
+def test_special_blocks(gpu, orc):
+    """Zero blocks, constant-magnitude blocks, fp32 denormals and values on the
+    codebook grid, in one matrix."""
+    c4 = orc.nf4_table()
+    parts = [np.zeros(64 * 3, np.float32),
+             np.full(64 * 5, -0.25, np.float32),
+             (np.arange(64 * 4) % 7 - 3).astype(np.float32) * np.float32(1e-42),   # denormals
+             np.float32(4.0) * c4[np.arange(64 * 2) % 16],
+             workloads.normal_f32((64 * 300 + 11,), 0.02, 77).numpy()]
+    w = np.concatenate(parts).astype(np.float32)
+    for dq in (True, False):
+        q, status = _gpu_quant(gpu, w, dq)
+        assert status == 0
+        ref = orc.quantize(w, dq)
+        _compare_packed(q, ref, dq)
+        np.testing.assert_array_equal(bits(gpu.dequantize(q, torch.float32)), orc.dequantize(ref).view(np.uint32))
+
+
+def test_repeat_identical_and_nonfinite(gpu):
+    w = workloads.weight_with_outliers((64 * 5000 + 3,), seed=8).cuda()
+    a = gpu.quantize(w, True)
+    b = gpu.quantize(w.clone(), True)
+    torch.cuda.synchronize()
+    for x, y in [(a.codes, b.codes), (a.scales, b.scales), (a.nested, b.nested), (a.offset, b.offset)]:
+        assert torch.equal(x, y)
+    for bad in (float("nan"), float("inf")):
+        v = w.clone()
+        v[1234] = bad
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        gpu.quantize(v, True, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == -5  # NF4_ENONFINITE
+
+
+def test_dequantize_from_oracle_packed(gpu, orc):
+    """Decode buffers written by the oracle (not by the GPU quantizer)."""
+    n = 4096 * 37 + 5
+    w = workloads.weight_with_outliers((n,), seed=3).numpy()
+    ref = orc.quantize(w, True)
+    t = gpu.NF4Tensor(torch.from_numpy(ref["codes"]).cuda(), torch.from_numpy(ref["qabs"]).cuda(),
+                      torch.from_numpy(ref["nested"]).cuda(), torch.from_numpy(ref["offset"]).cuda(), (n,), True)
+    np.testing.assert_array_equal(bits(gpu.dequantize(t, torch.bfloat16)), orc.dequantize(ref, "bf16"))
+
+
+@pytest.mark.parametrize("shape", [(4096, 14336), (4096, 4096)])
+def test_full_size_matrix(gpu, orc, shape):
+    """One matrix of each shape of the 7.5e9-parameter quantize/dequantize
+    workload (N(0, 0.02) with 1% outliers at 10x), full comparison."""
+    print(f"[storage] full {shape}", flush=True)
+    w = workloads.weight_with_outliers(shape, seed=workloads.weight_seed(0), device="cuda")
+    q = gpu.quantize(w, True)
+    d = gpu.dequantize(q, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = orc.quantize(w.cpu().numpy(), True)
+    _compare_packed(q, ref, True)
+    np.testing.assert_array_equal(bits(d).ravel(), orc.dequantize(ref, "bf16"))
