@@ -1,0 +1,240 @@
+"""Benchmark of the NF4 double-quant + LoRA hot path on one MI355X.
+
+One step = the whole path over one batch of the Llama-8B-shaped decoder layer
+(hidden 4096, kv 1024, intermediate 14336; q/k/v/o/gate/up/down, 4096 tokens,
+LoRA r = 16, alpha = 32 on all 7 projections), per projection:
+  nf4_quantize (absmax + NF4 codes + double quantization of the fp32 weight)
+  nf4_linear_fwd (fused dequant-GEMM + LoRA side path)
+  nf4_linear_bwd_input (fused dequant-GEMM through the frozen base + LoRA)
+  lora_grad (dA, dB)
+  nf4_dequantize (packed -> bf16)
+with every input already resident in device memory. Prints one JSON line.
+
+value = algorithmic FLOPs of the step (4MNK + 6Mr(N+K) per projection) /
+step time: whole-step throughput including the quantize and dequantize work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48, help="token rows of the oracle sample")
+    return p.parse_args()
+
+
+def layer_flops(M, N, K, r):
+    base = 4 * M * N * K
+    lora = 6 * M * r * (N + K)
+    return base, lora
+
+
+def packed_bytes(n, nl):
+    lay = nl.layout(n, True)
+    return lay["codes_bytes"] + lay["scales_bytes"] + lay["nested_bytes"] + lay["offset_bytes"]
+
+
+def cpu_baseline(layers, M, r, s, rows):
+    """The oracle on the host cores over a bounded sample of the same step:
+    quantize + dequantize of all 7 weights, and forward, input gradient and
+    LoRA gradients for the first `rows` token rows of every projection."""
+    import numpy as np
+    import oracle
+    import workloads
+    oracle.build(force=False)
+    threads = oracle.get_threads()
+    t_total, flops = 0.0, 0
+    for i, L in enumerate(layers):
+        W = workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(i)).numpy()
+        inp = workloads.lora_inputs(L, rows, seed_offset=i)
+        x = inp["x"].float().numpy()
+        dy = inp["dy"].float().numpy()
+        A, B = inp["A"].numpy(), inp["B"].numpy()
+        t0 = time.perf_counter()
+        q = oracle.quantize(W, True)
+        Wd = oracle.bf16_bits_to_f32(oracle.dequantize(q, "bf16")).reshape(W.shape)
+        y, T = oracle.linear_fwd(x, Wd, A, B, s)
+        dx, U = oracle.linear_bwd_input(dy, Wd, A, B, s)
+        oracle.lora_grad(x, dy, T, U, s)
+        t_total += time.perf_counter() - t0
+        b, l = layer_flops(rows, L.n_out, L.k_in, r)
+        flops += b + l
+    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"all 7 weights quantized + dequantized, fwd/bwd-input/LoRA grads on {rows} of {M} "
+                       f"token rows per projection; {flops / 1e9:.1f} GFLOP in {t_total:.1f} s (fp64 accumulation)",
+                seconds=round(t_total, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    from qlora_adapter_amd import nf4lora as nl
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nl.load()
+    wl = workloads.WORKLOADS["llama8b_layer"]
+    layers, M = wl["layers"], wl["tokens"]
+    r = layers[0].lora_rank
+    s = nl.lora_scale(wl["alpha"], r)
+
+    # ---- resident inputs and outputs (untimed) ----
+    P = []
+    for i, L in enumerate(layers):
+        inp = workloads.lora_inputs(L, M, seed_offset=i, device="cuda")
+        W = workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(i), "cuda")
+        n = W.numel()
+        lay = nl.layout(n, True)
+        P.append(dict(
+            L=L, W=W, x=inp["x"], dy=inp["dy"], A=inp["A"], B=inp["B"],
+            Wq=nl.NF4Tensor.empty(W.shape, True, dev),
+            qws=torch.empty(lay["quantize_workspace_bytes"], dtype=torch.uint8, device=dev),
+            status=torch.zeros(1, dtype=torch.int32, device=dev),
+            y=torch.empty((M, L.n_out), dtype=torch.bfloat16, device=dev),
+            T=torch.empty((M, r), dtype=torch.float32, device=dev),
+            dx=torch.empty((M, L.k_in), dtype=torch.bfloat16, device=dev),
+            U=torch.empty((M, r), dtype=torch.float32, device=dev),
+            dA=torch.empty((r, L.k_in), dtype=torch.float32, device=dev),
+            dB=torch.empty((L.n_out, r), dtype=torch.float32, device=dev),
+            gws=torch.empty(nl.lora_grad_workspace_bytes(M, L.k_in, L.n_out, r), dtype=torch.uint8, device=dev),
+            Wd=torch.empty(W.shape, dtype=torch.bfloat16, device=dev),
+        ))
+    stream = torch.cuda.current_stream(dev)
+    kinds = ["quantize", "fwd", "bwd", "grad", "dequant"]
+
+    def step(events=None):
+        def mark(kind, i, fn):
+            if events is None:
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            events.append((kind, i, e0, e1))
+        for i, p in enumerate(P):
+            mark("quantize", i, lambda p=p: nl.quantize(p["W"], True, out=p["Wq"], workspace=p["qws"],
+                                                        status=p["status"]))
+        for i, p in enumerate(P):
+            mark("fwd", i, lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"], t_out=p["T"]))
+        for i, p in enumerate(P):
+            mark("bwd", i, lambda p=p: nl.linear_bwd_input(p["dy"], p["Wq"], p["A"], p["B"], s, dx=p["dx"],
+                                                           u_out=p["U"]))
+        for i, p in enumerate(P):
+            mark("grad", i, lambda p=p: nl.lora_grad(p["x"], p["dy"], p["T"], p["U"], s, dA=p["dA"], dB=p["dB"],
+                                                     workspace=p["gws"]))
+        for i, p in enumerate(P):
+            mark("dequant", i, lambda p=p: nl.dequantize(p["Wq"], torch.bfloat16, out=p["Wd"]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert all(int(p["status"].item()) == 0 for p in P)
+
+    # ---- timed region: whole steps, no per-call events ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # ---- per-call HIP events on the launch stream (separate pass, same work) ----
+    events = []
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    per = {k: [0.0] * len(P) for k in kinds}
+    for kind, i, e0, e1 in events:
+        per[kind][i] += e0.elapsed_time(e1) / args.steps  # ms per call
+
+    flops_base = flops_lora = 0
+    fwd_flops = fwd_ms = bwd_flops = bwd_ms = 0.0
+    dq_bytes = dq_ms = q_bytes = q_ms = 0.0
+    for i, p in enumerate(P):
+        L = p["L"]
+        b, l = layer_flops(M, L.n_out, L.k_in, r)
+        flops_base += b
+        flops_lora += l
+        fwd_flops += 2 * M * L.n_out * L.k_in + 2 * M * r * (L.n_out + L.k_in)
+        bwd_flops += 2 * M * L.n_out * L.k_in + 2 * M * r * (L.n_out + L.k_in)
+        fwd_ms += per["fwd"][i]
+        bwd_ms += per["bwd"][i]
+        n = L.n_out * L.k_in
+        pb = packed_bytes(n, nl)
+        dq_bytes += pb + 2 * n
+        dq_ms += per["dequant"][i]
+        q_bytes += 4 * n + pb
+        q_ms += per["quantize"][i]
+    total_flops = flops_base + flops_lora
+    fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    dominant = "nf4_linear_fwd" if fwd_ms >= bwd_ms else "nf4_linear_bwd_input"
+    dom_tf = fwd_tf if fwd_ms >= bwd_ms else bwd_tf
+    dq_gbps = dq_bytes / (dq_ms * 1e-3) / 1e9
+    q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, M, r, s, args.cpu_rows)
+
+    out = {
+        "metric": "fused NF4+LoRA linear TFLOP/s & dequant GB/s, % of MI355X roofline",
+        "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) fp32 weights, N(0,1) bf16 activations and upstream gradients)",
+        "config": {"workload": "llama8b_layer", "tokens": M, "hidden": 4096, "kv_dim": 1024,
+                   "intermediate": 14336, "projections": 7, "lora_rank": r, "lora_alpha": wl["alpha"],
+                   "double_quant": True, "block": 64, "nested_block": 256,
+                   "step": "quantize + fused fwd + fused bwd-input + lora_grad + dequantize, all 7 projections"},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "roofline_dequant": {"kernel": "nf4_dequantize (bf16 out)", "bound": "hbm", "achieved": round(dq_gbps, 1),
+                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
+                             "traffic": None},
+        "kernels": {"fwd_tflops": round(fwd_tf, 1), "bwd_tflops": round(bwd_tf, 1),
+                    "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+                    "grad_ms": round(sum(per["grad"]), 3), "quantize_ms": round(q_ms, 3),
+                    "quantize_gbps": round(q_gbps, 1), "dequant_ms": round(dq_ms, 3),
+                    "dequant_gbps": round(dq_gbps, 1),
+                    "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

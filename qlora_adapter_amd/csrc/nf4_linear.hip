@@ -100,53 +100,82 @@ __global__ __launch_bounds__(256) void k_linear_general(const T* __restrict__ a,
 }
 
 // ---------------------------------------------------------------------------
-// Adapter side product S[m][rho] = sum_i A[m][i] * R[i][rho] in fp32, i ascending:
-//   forward : A = x  [M, K], R[k][rho] = Afac[rho][k]   (T = x A^T)
-//   backward: A = dY [M, N], R[n][rho] = Bfac[n][rho]   (U = dY B)
-// A workgroup owns 16 rows; thread (row, g) owns rho = g, g+16, ...
+// Adapter side product S[m][rho] = sum_i L[m][i] * R[i][rho] in fp32:
+//   forward : L = x  [M, K], R[k][rho] = Afac[rho][k]   (T = x A^T)
+//   backward: L = dY [M, N], R[n][rho] = Bfac[n][rho]   (U = dY B)
+// A workgroup owns 16 rows; its 4 waves split the reduction into 4 contiguous
+// slices, each accumulated with the 16x16x4 fp32 MFMA (lane l: row l % 16,
+// reduction group G = l / 16 holding 8 consecutive i; MFMA step q uses element
+// q, so step q covers i = 8G + q). The 4 slice sums are added in the fixed order
+// (w0 + w1) + (w2 + w3).
 // ---------------------------------------------------------------------------
-constexpr int SR = 16, SI = 32;
+constexpr int SR = 16;
+
+template <typename T>
+__device__ __forceinline__ void load8_row(const T* __restrict__ p, int64_t row_off, int64_t i, int64_t I, bool ok,
+                                          float v[8]) {
+  if (ok && i + 8 <= I && ((row_off + i) % 8) == 0) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 q = *reinterpret_cast<const bf16x8*>(p + row_off + i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(p + row_off + i);
+      const float4 b = *reinterpret_cast<const float4*>(p + row_off + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (ok && i + e < I) ? (float)p[row_off + i + e] : 0.0f;
+  }
+}
 
 template <typename T, bool BWD>
-__global__ __launch_bounds__(256) void k_side(const T* __restrict__ a, int64_t M, int64_t I,
+__global__ __launch_bounds__(256) void k_side(const T* __restrict__ L, int64_t M, int64_t I,
                                               const float* __restrict__ fac, int r, float* __restrict__ outS) {
-  __shared__ float As[SR][SI + 1];
-  __shared__ float Rs[SI][kMaxRank + 1];
-  const int tid = threadIdx.x;
-  const int row = tid >> 4, g = tid & 15;
+  __shared__ float red[4][16 * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, G = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * SR;
-  float acc[kMaxRank / 16];
-#pragma unroll
-  for (int q = 0; q < kMaxRank / 16; ++q) acc[q] = 0.0f;
-  for (int64_t i0 = 0; i0 < I; i0 += SI) {
-    for (int e = tid; e < SR * SI; e += 256) {
-      const int rr = e / SI, ii = e % SI;
-      const int64_t m = m0 + rr, i = i0 + ii;
-      As[rr][ii] = (m < M && i < I) ? (float)a[m * I + i] : 0.0f;
-    }
-    for (int e = tid; e < SI * r; e += 256) {
-      const int ii = e / r, rho = e % r;
-      const int64_t i = i0 + ii;
-      Rs[ii][rho] = (i < I) ? (BWD ? fac[i * r + rho] : fac[(int64_t)rho * I + i]) : 0.0f;
-    }
-    __syncthreads();
-    for (int ii = 0; ii < SI; ++ii) {
-      const float av = As[row][ii];
-#pragma unroll
-      for (int q = 0; q < kMaxRank / 16; ++q) {
-        const int rho = g + 16 * q;
-        if (rho < r) acc[q] = fmaf(av, Rs[ii][rho], acc[q]);
-      }
-    }
-    __syncthreads();
-  }
   const int64_t m = m0 + row;
-  if (m < M) {
+  const bool mok = m < M;
+  // reduction slice of this wave, a multiple of 32 long
+  const int64_t slice = ((I + 3) / 4 + 31) / 32 * 32;
+  const int64_t ib = wave * slice, ie = (ib + slice < I) ? ib + slice : I;
+  const int RT = (r + 15) / 16;
+  f32x4 acc[kMaxRank / 16];
 #pragma unroll
-    for (int q = 0; q < kMaxRank / 16; ++q) {
-      const int rho = g + 16 * q;
-      if (rho < r) outS[m * r + rho] = acc[q];
+  for (int t = 0; t < kMaxRank / 16; ++t) acc[t] = f32x4{};
+  for (int64_t i0 = ib; i0 < ie; i0 += 32) {
+    const int64_t i = i0 + 8 * G;
+    float lv[8];
+    load8_row<T>(L, m * I, i, ie, mok, lv);
+#pragma unroll
+    for (int t = 0; t < kMaxRank / 16; ++t) {
+      if (t >= RT) break;
+      const int rho = 16 * t + row;
+      float rv[8];
+      if (BWD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rv[e] = (rho < r && i + e < ie) ? fac[(i + e) * r + rho] : 0.0f;
+      } else {
+        load8_row<float>(fac, (int64_t)rho * I, i, ie, rho < r, rv);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(lv[q], rv[q], acc[t], 0, 0, 0);
     }
+  }
+  // accumulator element j of lane l: row 4 * (l / 16) + j, column l % 16
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wave][(4 * G + j) * 16 + row] = acc[t][j];
+    __syncthreads();
+    const int rr = tid >> 4, cc = tid & 15;
+    const float v = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    const int64_t mm = m0 + rr;
+    const int rho = 16 * t + cc;
+    if (mm < M && rho < r) outS[mm * r + rho] = v;
+    __syncthreads();
   }
 }
 
@@ -218,18 +247,25 @@ __global__ __launch_bounds__(256) void k_lora_combine(const float* __restrict__ 
     out[rho * J + j] = v;
 }
 
+// Adapter side product (T = x A^T or U = dY B), needed by the main kernel's epilogue.
+template <typename T>
+void launch_side(const LinearArgs& g, hipStream_t st) {
+  if (g.r <= 0) return;
+  const int64_t I = g.backward ? g.N : g.K;
+  const T* a = static_cast<const T*>(g.a);
+  const dim3 sg((unsigned)ceil_div(g.M, SR));
+  if (g.backward)
+    hipLaunchKernelGGL((k_side<T, true>), sg, dim3(256), 0, st, a, g.M, I, g.B, g.r, g.side);
+  else
+    hipLaunchKernelGGL((k_side<T, false>), sg, dim3(256), 0, st, a, g.M, I, g.A, g.r, g.side);
+}
+
 template <typename T>
 int run_linear_general(const LinearArgs& g, hipStream_t st) {
   const NF4View w = make_view(g.W);
-  const int64_t I = g.backward ? g.N : g.K, J = g.backward ? g.K : g.N;
+  const int64_t J = g.backward ? g.K : g.N;
   const T* a = static_cast<const T*>(g.a);
-  if (g.r > 0) {
-    const dim3 sg((unsigned)ceil_div(g.M, SR));
-    if (g.backward)
-      hipLaunchKernelGGL((k_side<T, true>), sg, dim3(256), 0, st, a, g.M, I, g.B, g.r, g.side);
-    else
-      hipLaunchKernelGGL((k_side<T, false>), sg, dim3(256), 0, st, a, g.M, I, g.A, g.r, g.side);
-  }
+  launch_side<T>(g, st);
   const dim3 grid((unsigned)ceil_div(J, GT), (unsigned)ceil_div(g.M, GT));
   T* out = static_cast<T*>(g.out);
 #define NF4_GEN(BWD, DQ)                                                                                            \
@@ -248,7 +284,10 @@ int run_linear_general(const LinearArgs& g, hipStream_t st) {
 
 int launch_linear(const LinearArgs& g, hipStream_t st) {
   if (g.dtype == NF4_BF16) {
-    if (fast_linear_applies(g)) return launch_linear_fast(g, st);
+    if (fast_linear_applies(g)) {
+      launch_side<__bf16>(g, st);
+      return launch_linear_fast(g, st);
+    }
     return run_linear_general<__bf16>(g, st);
   }
   return run_linear_general<float>(g, st);

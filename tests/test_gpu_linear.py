@@ -132,3 +132,59 @@ def test_fused_matches_dequantize_then_matmul(gpu):
     ref = c["x"].float() @ Wd.T
     torch.cuda.synchronize()
     assert_close(to_np(y), ref.double().cpu().numpy(), "bf16", "y vs torch")
+
+
+@pytest.mark.parametrize("K,N,dq", [(576, 192, True), (4096, 1024, True), (640, 4100, False), (1536, 576, True)])
+def test_fused_decode_bitexact(gpu, K, N, dq):
+    """With x = I (M = K), y[m][n] = W_hat[n][m] exactly (one nonzero product per
+    output, exact in fp32), so the weights decoded inside the GEMM must equal
+    nf4_dequantize's bf16 output bit for bit."""
+    W = workloads.weight_with_outliers((N, K), seed=K + N, device="cuda")
+    Wq = gpu.quantize(W, dq)
+    eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+    y, _ = gpu.linear_fwd(eye, Wq)
+    d = gpu.dequantize(Wq, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y, d.T.contiguous())
+
+
+FULL = [("q_proj", 4096, 4096), ("gate_proj", 14336, 4096), ("down_proj", 4096, 14336)]
+
+
+@pytest.mark.parametrize("name,N,K", FULL)
+def test_llama8b_shapes_sampled(gpu, orc, name, N, K):
+    """Llama-8B-shaped projections at 4096 tokens, r = 16, in the launch
+    configuration the benchmark times: y and dX on 24 sampled token rows, T and
+    U on the same rows, dA and dB in full (given the GPU's T and U)."""
+    print(f"[linear] full {name} {N}x{K}", flush=True)
+    M, r = 4096, 16
+    c = make_case(M, K, N, r, torch.bfloat16, seed=11)
+    s = gpu.lora_scale(32.0, r)
+    Wq, y, T, dx, U, (dA, dB) = run_all(gpu, c, s)
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16)
+    rows = np.sort(np.random.default_rng(N + K).choice(M, 24, replace=False))
+    x = to_np(c["x"])
+    dy = to_np(c["dy"])
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    y_ref, T_ref = orc.linear_fwd(x[rows], Wref, A, B, s)
+    dx_ref, U_ref = orc.linear_bwd_input(dy[rows], Wref, A, B, s)
+    assert_close(to_np(y)[rows], y_ref, "bf16", "y rows")
+    assert_close(to_np(dx)[rows], dx_ref, "bf16", "dx rows")
+    assert_close(T.cpu().numpy()[rows], T_ref, "f32", "T rows")
+    assert_close(U.cpu().numpy()[rows], U_ref, "f32", "U rows")
+    dA_ref, dB_ref = orc.lora_grad(x, dy, T.cpu().numpy().astype(np.float64), U.cpu().numpy().astype(np.float64), s)
+    assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
+    assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
+
+
+@pytest.mark.parametrize("K,N,dq", [(576, 192, True), (4096, 1024, True), (640, 4096, False), (576, 1536, True)])
+def test_fused_decode_bitexact_bwd(gpu, K, N, dq):
+    """With dY = I (M = N), dX[m][k] = W_hat[m][k] exactly: the weights the input
+    gradient decodes (transposed, in LDS) equal nf4_dequantize's bf16 output."""
+    W = workloads.weight_with_outliers((N, K), seed=K * 3 + N, device="cuda")
+    Wq = gpu.quantize(W, dq)
+    eye = torch.eye(N, dtype=torch.bfloat16, device="cuda")
+    dx, _ = gpu.linear_bwd_input(eye, Wq)
+    d = gpu.dequantize(Wq, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, d)
