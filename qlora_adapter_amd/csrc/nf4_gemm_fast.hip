@@ -113,140 +113,238 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t MT, int64_t NT, i
 }
 
 constexpr int FBM = 256, FBN = 128, FBK = 64;
-constexpr int XPITCH = 72;  // bf16 per LDS row of the x tile (64 + 8 pad)
+constexpr int XPITCH = 72;  // bf16 per padded LDS row (64 + 8) of the input-gradient kernel
 
-template <bool DQ>
-__global__ __launch_bounds__(256) void k_fwd_fast(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N,
-                                                  NF4View w, const float* __restrict__ Bfac, int r, float s,
-                                                  const float* __restrict__ T, __bf16* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][FBM * XPITCH];
+// 16-byte chunk swizzle of the dense [rows][128 B] LDS tiles: chunk c of row r
+// is stored at chunk c ^ swz(r). Eight consecutive rows hit eight different
+// chunks, and sixteen consecutive rows cover all 64 four-byte banks, so the
+// 16-byte MFMA operand reads are free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// Split an fp32 value into three bf16 parts whose sum is the value exactly.
+__device__ __forceinline__ void split3(float v, __bf16& a, __bf16& b, __bf16& c) {
+  a = (__bf16)v;
+  const float r1 = v - (float)a;
+  b = (__bf16)r1;
+  const float r2 = r1 - (float)b;
+  c = (__bf16)r2;
+}
+
+// Eight consecutive fp32 values p[0..7] with entries at or past `limit` read
+// as zero, split into three bf16x8 vectors.
+__device__ __forceinline__ void load_split8(const float* __restrict__ p, int avail, float scale, bf16x8& h,
+                                            bf16x8& m, bf16x8& l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = (e < avail) ? scale * p[e] : 0.0f;
+    __bf16 a, b, c;
+    split3(v, a, b, c);
+    h[e] = a;
+    m[e] = b;
+    l[e] = c;
+  }
+}
+
+// One weight-operand step: 16 bytes of codes per subtile and its block scale inputs.
+template <int NS>
+struct WStep {
+  uint4 q[NS];
+  uint32_t qa[NS];  // dynamic8 code (double quant) of the block
+  float nv[NS];     // nested max (double quant) or absmax (single quant)
+};
+
+// 16-byte direct global -> LDS load: lane l writes dst + 16 l (dst wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int XI>
+__device__ __forceinline__ void fwd_issue_x(const __bf16* __restrict__ x, const int64_t (&xoff)[XI], int64_t kt,
+                                            __bf16* buf, int wave) {
+#pragma unroll
+  for (int i = 0; i < XI; ++i)
+    lds_dma16(x + xoff[i] + kt * 64, buf + (4 * i + wave) * 512);
+}
+
+template <bool DQ, int NS>
+__device__ __forceinline__ void fwd_load_w(const NF4View& w, const uint8_t* const (&wp)[NS],
+                                           const int64_t (&nrow)[NS], int64_t KT, int64_t kt, WStep<NS>& st) {
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    st.q[t] = *reinterpret_cast<const uint4*>(wp[t] + 32 * kt);
+    const int64_t blk = nrow[t] * KT + kt;
+    if (DQ) {
+      st.qa[t] = static_cast<const uint8_t*>(w.scales)[blk];
+      st.nv[t] = w.nested[blk >> 8];
+    } else {
+      st.nv[t] = static_cast<const float*>(w.scales)[blk];
+    }
+  }
+}
+
+template <bool DQ, int NS>
+__device__ __forceinline__ void fwd_decode(const WStep<NS>& st, const float* d8s, float mu, bf16x8 (&bop)[NS][4]) {
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const float a = DQ ? __fadd_rn(__fmul_rn(d8s[st.qa[t]], st.nv[t]), mu) : st.nv[t];
+    const Bf16Table tb = build_table(a);
+    bop[t][0] = decode_word(st.q[t].x, tb);
+    bop[t][1] = decode_word(st.q[t].y, tb);
+    bop[t][2] = decode_word(st.q[t].z, tb);
+    bop[t][3] = decode_word(st.q[t].w, tb);
+  }
+}
+
+template <int MS, int NS>
+__device__ __forceinline__ void fwd_mfma(const __bf16* xb, const bf16x8 (&bop)[NS][4], f32x16 (&acc)[MS][NS], int g,
+                                         int l32) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int row = 32 * i + l32;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xb[row * 64 + 8 * ((4 * g + j) ^ swz(row))]);
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[t][j], acc[i][t], 0, 0, 0);
+    }
+  }
+}
+
+// Forward y = x W_hat^T + s T B^T, K % 64 == 0. Tile (32 MS) x (128 NS): each of
+// the 4 waves owns all 32 MS rows and 32 NS weight rows, so every weight row is
+// decoded by exactly one wave and the decode cost is spread over MS 32x32 MFMA
+// tiles. x arrives by direct global->LDS loads into two swizzled stages; weight
+// codes for step k+2 are loaded and step k+1 is decoded while step k multiplies.
+template <bool DQ, int MS, int NS>
+__global__ __launch_bounds__(256, 1)
+void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4View w, const float* __restrict__ Bfac,
+           int r, float s, const float* __restrict__ T, __bf16* __restrict__ y) {
+  constexpr int BM = 32 * MS, WN = 32 * NS, BN = 4 * WN;
+  constexpr int STAGE = BM * 64;   // bf16 per x stage
+  constexpr int XI = BM / 32;      // 1 KB direct loads per wave per stage
+  __shared__ __attribute__((aligned(16))) __bf16 xs0[STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 xs1[STAGE];
+  __shared__ float d8s[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
-  const int64_t MT = (M + FBM - 1) / FBM, NT = (N + FBN - 1) / FBN;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t MT = (M + BM - 1) / BM, NT = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_coords(blockIdx.x, MT, NT, mt, nt);
-  const int64_t m0 = mt * FBM, n0 = nt * FBN;
-  const int64_t KT = K / FBK;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t KT = K / 64;
+  if (DQ) d8s[tid] = dyn8_value((uint32_t)tid);
   const float mu = DQ ? w.offset[0] : 0.0f;
 
-  // x loader: thread t copies 16-byte chunk (t & 7) of rows (t >> 3) + 32 i.
-  const int xc = tid & 7, xr = tid >> 3;
-  uint4 xreg[8];
-  // weight rows of this lane (one per 32-wide output subtile)
-  int64_t nrow[2];
-  bool nok[2];
+  // Direct x loads: instruction i of this wave fills rows 8G..8G+7, G = 4i + wave;
+  // lane l writes physical chunk l % 8 of row 8G + l / 8, i.e. logical chunk
+  // (l % 8) ^ swz(row). Rows past M are clamped (their outputs are not stored).
+  int64_t xoff[XI];
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    nrow[ni] = n0 + wn * 64 + ni * 32 + l32;
-    nok[ni] = nrow[ni] < N;
+  for (int i = 0; i < XI; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int64_t m = (m0 + row < M) ? m0 + row : M - 1;
+    xoff[i] = m * K + 8 * ((lane & 7) ^ swz(row));
   }
-  uint4 wreg[2];
-  float wsc[2];
+  // weight rows of this lane (clamped past N)
+  int64_t nrow[NS];
+  const uint8_t* wp[NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const int64_t n = n0 + wave * WN + 32 * t + l32;
+    nrow[t] = n < N ? n : N - 1;
+    wp[t] = w.codes + nrow[t] * (K / 2) + 16 * g;
+  }
 
-  auto load_x = [&](int64_t kt) {
+  f32x16 acc[MS][NS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      xreg[i] = (m < M) ? *reinterpret_cast<const uint4*>(x + m * K + kt * FBK + 8 * xc) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_x = [&](int buf) {
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&xs[buf][(xr + 32 * i) * XPITCH + 8 * xc]) = xreg[i];
-  };
-  auto load_w = [&](int64_t kt) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      if (nok[ni]) {
-        wreg[ni] = *reinterpret_cast<const uint4*>(w.codes + (nrow[ni] * K + kt * FBK) / 2 + 16 * g);
-        wsc[ni] = block_scale_of<DQ>(w, mu, nrow[ni] * (K / FBK) + kt);
-      } else {
-        wreg[ni] = make_uint4(0, 0, 0, 0);
-        wsc[ni] = 0.0f;
-      }
-    }
-  };
+    for (int t = 0; t < NS; ++t) acc[i][t] = f32x16{};
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
-
-  load_x(0);
-  load_w(0);
-  store_x(0);
+  WStep<NS> wa, wb;
+  bf16x8 bopa[NS][4], bopb[NS][4];
+  fwd_issue_x<XI>(x, xoff, 0, xs0, wave);
+  fwd_load_w<DQ, NS>(w, wp, nrow, KT, 0, wb);
+  if (KT > 1) fwd_load_w<DQ, NS>(w, wp, nrow, KT, 1, wa);
   __syncthreads();
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    const int cur = (int)(kt & 1);
-    const uint4 wc0 = wreg[0], wc1 = wreg[1];
-    const float sc0 = wsc[0], sc1 = wsc[1];
-    if (kt + 1 < KT) {
-      load_x(kt + 1);
-      load_w(kt + 1);
-    }
-    bf16x8 bop[2][4];
-    {
-      const Bf16Table t0 = build_table(sc0);
-      bop[0][0] = decode_word(wc0.x, t0);
-      bop[0][1] = decode_word(wc0.y, t0);
-      bop[0][2] = decode_word(wc0.z, t0);
-      bop[0][3] = decode_word(wc0.w, t0);
-      const Bf16Table t1 = build_table(sc1);
-      bop[1][0] = decode_word(wc1.x, t1);
-      bop[1][1] = decode_word(wc1.y, t1);
-      bop[1][2] = decode_word(wc1.z, t1);
-      bop[1][3] = decode_word(wc1.w, t1);
-    }
-    const __bf16* xb = xs[cur];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 aop[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        aop[mi] = *reinterpret_cast<const bf16x8*>(&xb[(wm * 128 + mi * 32 + l32) * XPITCH + 32 * g + 8 * j]);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[mi], bop[ni][j], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < KT) store_x(cur ^ 1);
+  fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
+
+  // Step kt multiplies one x stage with the decoded weights of step kt while the
+  // next x stage lands in the other buffer, the codes of step kt + 2 are loaded
+  // and the codes of step kt + 1 are decoded. Unrolled by two so that the two x
+  // buffers and register sets keep fixed roles.
+  int64_t kt = 0;
+  // Steady state: every load and decode of both half-steps is in range, so the
+  // body has no branches (keeps the accumulators in place across iterations).
+  for (; kt + 3 < KT; kt += 2) {
+    fwd_issue_x<XI>(x, xoff, kt + 1, xs1, wave);
+    fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
+    fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
+    fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
+    __syncthreads();
+    fwd_issue_x<XI>(x, xoff, kt + 2, xs0, wave);
+    fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
+    fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
+    fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
+    __syncthreads();
+  }
+  // Last one to three steps.
+  for (; kt < KT; kt += 2) {
+    if (kt + 1 < KT) fwd_issue_x<XI>(x, xoff, kt + 1, xs1, wave);
+    if (kt + 2 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
+    if (kt + 1 < KT) fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
+    fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
+    __syncthreads();
+    if (kt + 1 >= KT) break;
+    if (kt + 2 < KT) fwd_issue_x<XI>(x, xoff, kt + 2, xs0, wave);
+    if (kt + 3 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
+    if (kt + 2 < KT) fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
+    fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
     __syncthreads();
   }
 
-  // LoRA: acc += (s T[m][rho]) * B[n][rho], two ranks per fp32 MFMA step.
+  // LoRA: acc += (s T[m][:]) . B[n][:], as six bf16 MFMA products of three-part
+  // splits of both factors (the products that reach fp32 precision).
   if (r > 0) {
-    for (int rho0 = 0; rho0 < r; rho0 += 2) {
-      const int rho = rho0 + g;
-      float av[4], bv[2];
+    for (int rho0 = 0; rho0 < r; rho0 += 16) {
+      const int avail = r - (rho0 + 8 * g);
+      bf16x8 b1[NS], b2[NS], b3[NS];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int64_t m = m0 + wm * 128 + mi * 32 + l32;
-        av[mi] = (rho < r && m < M) ? s * T[m * r + rho] : 0.0f;
+      for (int t = 0; t < NS; ++t) load_split8(Bfac + nrow[t] * r + rho0 + 8 * g, avail, 1.0f, b1[t], b2[t], b3[t]);
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const int64_t m = (m0 + 32 * i + l32 < M) ? m0 + 32 * i + l32 : M - 1;
+        bf16x8 a1, a2, a3;
+        load_split8(T + m * r + rho0 + 8 * g, avail, s, a1, a2, a3);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          f32x16 c = acc[i][t];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b1[t], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2[t], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b3[t], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1[t], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b2[t], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1[t], c, 0, 0, 0);
+          acc[i][t] = c;
+        }
       }
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bv[ni] = (rho < r && nok[ni]) ? Bfac[nrow[ni] * r + rho] : 0.0f;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
     }
   }
 
-  // Store: accumulator element e of subtile (mi, ni) is row (e/4)*8 + 4g + e%4, column l32.
+  // Store: element e of accumulator (i, t) is row 32 i + 8 (e / 4) + 4 g + e % 4, column l32.
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int t = 0; t < NS; ++t) {
+    const int64_t n = n0 + wave * WN + 32 * t + l32;
+    if (n >= N) continue;
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      if (!nok[ni]) continue;
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + mi * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (m < M) y[m * N + nrow[ni]] = (__bf16)acc[mi][ni][e];
+        const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (m < M) y[m * N + n] = (__bf16)acc[i][t][e];
       }
-    }
+  }
 }
 
 template <bool DQ>
@@ -424,14 +522,28 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
       hipLaunchKernelGGL(k_bwd_fast<false>, grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, dx);
     return launch_status();
   }
-  const int64_t MT = ceil_div(g.M, FBM), NT = ceil_div(g.N, FBN);
-  const dim3 grid((unsigned)(MT * NT));
   const __bf16* x = static_cast<const __bf16*>(g.a);
   __bf16* y = static_cast<__bf16*>(g.out);
-  if (dq)
-    hipLaunchKernelGGL(k_fwd_fast<true>, grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s, g.side, y);
+  // Tile choice: 256 x 256 unless that leaves most of the 256 CUs idle.
+  const int64_t wg22 = ceil_div(g.M, 256) * ceil_div(g.N, 256);
+  const int64_t wg21 = ceil_div(g.M, 256) * ceil_div(g.N, 128);
+#define NF4_FWD(MS, NS)                                                                                         \
+  do {                                                                                                          \
+    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.N, 128 * NS)));                            \
+    if (dq)                                                                                                     \
+      hipLaunchKernelGGL((k_fwd<true, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,     \
+                         g.side, y);                                                                            \
+    else                                                                                                        \
+      hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,    \
+                         g.side, y);                                                                            \
+  } while (0)
+  if (wg22 >= 224)
+    NF4_FWD(8, 2);
+  else if (wg21 >= 224)
+    NF4_FWD(8, 1);
   else
-    hipLaunchKernelGGL(k_fwd_fast<false>, grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s, g.side, y);
+    NF4_FWD(4, 1);
+#undef NF4_FWD
   return launch_status();
 }
 

@@ -180,55 +180,90 @@ __global__ __launch_bounds__(256) void k_side(const T* __restrict__ L, int64_t M
 }
 
 // ---------------------------------------------------------------------------
-// LoRA gradients, stage 1: partial[c][rho][j] = sum over m in chunk c (in
-// order) of P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J].
-// Workgroup (column tile of 64, chunk c); thread (jj, g) owns rho = g, g+4, ...
-// Stage 2 sums the chunks in order c = 0, 1, ..., scales by s and writes dA
-// ([r][J] layout) or dB ([J][r] layout).
+// LoRA gradients, stage 1: partial[c][rho][j] = sum over m in chunk c of
+// P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J]. One workgroup per
+// (64-column tile, chunk). 32 tokens at a time are staged in LDS (Q as fp32);
+// wave w owns columns 16w..16w+15 and every 16-rank tile, accumulated with the
+// 16x16x4 fp32 MFMA (A = P^T: lane l holds rank 16t + l % 16 of token
+// 4q + l / 16; B = Q: column 16w + l % 16 of the same token).
+// Stage 2 (k_lora_combine) adds the chunks in order c = 0, 1, ..., scales by s
+// and writes dA ([r][J]) or dB ([J][r]).
 // ---------------------------------------------------------------------------
-constexpr int LJ = 64, LM = 16;
+constexpr int LJ = 64, LSM = 32, LPP = kMaxRank + 4, LQP = LJ + 4;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ P, const T* __restrict__ Q, int64_t M,
                                                       int64_t J, int r, int64_t chunk, float* __restrict__ partial) {
-  __shared__ float Qs[LM][LJ + 1];
-  __shared__ float Ps[LM][kMaxRank + 1];
-  const int tid = threadIdx.x, jj = tid & 63, g = tid >> 6;
+  __shared__ float Ps[LSM * LPP];
+  __shared__ float Qs[LSM * LQP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
   const int64_t j0 = (int64_t)blockIdx.x * LJ;
   const int64_t c = blockIdx.y;
   const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
-  float acc[kMaxRank / 4];
+  const int RT = (r + 15) / 16;
+  f32x4 acc[kMaxRank / 16];
 #pragma unroll
-  for (int q = 0; q < kMaxRank / 4; ++q) acc[q] = 0.0f;
-  for (int64_t m0 = mb; m0 < me; m0 += LM) {
-    for (int e = tid; e < LM * LJ; e += 256) {
-      const int mm = e / LJ, jx = e % LJ;
-      const int64_t m = m0 + mm, j = j0 + jx;
-      Qs[mm][jx] = (m < me && j < J) ? (float)Q[m * J + j] : 0.0f;
+  for (int t = 0; t < kMaxRank / 16; ++t) acc[t] = f32x4{};
+  // Q loader: thread t -> token row t / 8, columns 8 (t % 8) .. + 8
+  const int qr = tid >> 3, qc = 8 * (tid & 7);
+  for (int64_t m0 = mb; m0 < me; m0 += LSM) {
+    {
+      const int64_t m = m0 + qr, j = j0 + qc;
+      float v[8];
+      const bool ok = m < me;
+      if (ok && j + 8 <= J && ((m * J + j) % 8) == 0) {
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 q = *reinterpret_cast<const bf16x8*>(Q + m * J + j);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
+        } else {
+          const float4 a = *reinterpret_cast<const float4*>(Q + m * J + j);
+          const float4 b = *reinterpret_cast<const float4*>(Q + m * J + j + 4);
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (ok && j + e < J) ? (float)Q[m * J + j + e] : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Qs[qr * LQP + qc + e] = v[e];
     }
-    for (int e = tid; e < LM * r; e += 256) {
-      const int mm = e / r, rho = e % r;
+    for (int e = tid; e < LSM * r; e += 256) {
+      const int mm = e / r, rho = e - mm * r;
       const int64_t m = m0 + mm;
-      Ps[mm][rho] = (m < me) ? P[m * r + rho] : 0.0f;
+      Ps[mm * LPP + rho] = (m < me) ? P[m * r + rho] : 0.0f;
+    }
+    if (r % 16) {
+      for (int e = tid; e < LSM * (RT * 16 - r); e += 256) {
+        const int pad = RT * 16 - r;
+        const int mm = e / pad, rho = r + (e - mm * pad);
+        Ps[mm * LPP + rho] = 0.0f;
+      }
     }
     __syncthreads();
-    for (int mm = 0; mm < LM; ++mm) {
-      const float qv = Qs[mm][jj];
 #pragma unroll
-      for (int q = 0; q < kMaxRank / 4; ++q) {
-        const int rho = g + 4 * q;
-        if (rho < r) acc[q] = fmaf(Ps[mm][rho], qv, acc[q]);
+    for (int q = 0; q < LSM / 4; ++q) {
+      const int mm = 4 * q + lg;
+      const float qv = Qs[mm * LQP + 16 * wave + l16];
+#pragma unroll
+      for (int t = 0; t < kMaxRank / 16; ++t) {
+        if (t >= RT) break;
+        const float pv = Ps[mm * LPP + 16 * t + l16];
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, qv, acc[t], 0, 0, 0);
       }
     }
     __syncthreads();
   }
-  const int64_t j = j0 + jj;
+  // lane l holds C[4 (l / 16) + i][l % 16] of each rank tile: rank 16t + 4 lg + i, column 16 wave + l16
+  const int64_t j = j0 + 16 * wave + l16;
   if (j < J) {
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int q = 0; q < kMaxRank / 4; ++q) {
-      const int rho = g + 4 * q;
-      if (rho < r) partial[(c * r + rho) * J + j] = acc[q];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int rho = 16 * t + 4 * lg + i;
+        if (rho < r) partial[(c * r + rho) * J + j] = acc[t][i];
+      }
   }
 }
 
