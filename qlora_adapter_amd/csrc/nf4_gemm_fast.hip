@@ -159,7 +159,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
 }
 
 template <int XI>
-__device__ __forceinline__ void fwd_issue_x(const __bf16* __restrict__ x, const int64_t (&xoff)[XI], int64_t kt,
+__device__ __forceinline__ void fwd_issue_x(const __bf16* __restrict__ x, const int32_t (&xoff)[XI], int64_t kt,
                                             __bf16* buf, int wave) {
 #pragma unroll
   for (int i = 0; i < XI; ++i)
@@ -217,7 +217,7 @@ __device__ __forceinline__ void fwd_mfma(const __bf16* xb, const bf16x8 (&bop)[N
 // tiles. x arrives by direct global->LDS loads into two swizzled stages; weight
 // codes for step k+2 are loaded and step k+1 is decoded while step k multiplies.
 template <bool DQ, int MS, int NS>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, NS == 1 ? 2 : 1)
 void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4View w, const float* __restrict__ Bfac,
            int r, float s, const float* __restrict__ T, __bf16* __restrict__ y) {
   constexpr int BM = 32 * MS, WN = 32 * NS, BN = 4 * WN;
@@ -239,12 +239,14 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // Direct x loads: instruction i of this wave fills rows 8G..8G+7, G = 4i + wave;
   // lane l writes physical chunk l % 8 of row 8G + l / 8, i.e. logical chunk
   // (l % 8) ^ swz(row). Rows past M are clamped (their outputs are not stored).
-  int64_t xoff[XI];
+  // (offsets relative to row m0, so they fit in 32 bits: rows < 256, K < 2^22)
+  const __bf16* xt = x + m0 * K;
+  int32_t xoff[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int row = 8 * (4 * i + wave) + (lane >> 3);
-    const int64_t m = (m0 + row < M) ? m0 + row : M - 1;
-    xoff[i] = m * K + 8 * ((lane & 7) ^ swz(row));
+    const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
+    xoff[i] = (int32_t)(m * K) + 8 * ((lane & 7) ^ swz(row));
   }
   // weight rows of this lane (clamped past N)
   int64_t nrow[NS];
@@ -264,7 +266,7 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
 
   WStep<NS> wa, wb;
   bf16x8 bopa[NS][4], bopb[NS][4];
-  fwd_issue_x<XI>(x, xoff, 0, xs0, wave);
+  fwd_issue_x<XI>(xt, xoff, 0, xs0, wave);
   fwd_load_w<DQ, NS>(w, wp, nrow, KT, 0, wb);
   if (KT > 1) fwd_load_w<DQ, NS>(w, wp, nrow, KT, 1, wa);
   __syncthreads();
@@ -278,12 +280,12 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // Steady state: every load and decode of both half-steps is in range, so the
   // body has no branches (keeps the accumulators in place across iterations).
   for (; kt + 3 < KT; kt += 2) {
-    fwd_issue_x<XI>(x, xoff, kt + 1, xs1, wave);
+    fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
     fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
     fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     __syncthreads();
-    fwd_issue_x<XI>(x, xoff, kt + 2, xs0, wave);
+    fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
     fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
     fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
@@ -291,13 +293,13 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   }
   // Last one to three steps.
   for (; kt < KT; kt += 2) {
-    if (kt + 1 < KT) fwd_issue_x<XI>(x, xoff, kt + 1, xs1, wave);
+    if (kt + 1 < KT) fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
     if (kt + 2 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
     if (kt + 1 < KT) fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     __syncthreads();
     if (kt + 1 >= KT) break;
-    if (kt + 2 < KT) fwd_issue_x<XI>(x, xoff, kt + 2, xs0, wave);
+    if (kt + 2 < KT) fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
     if (kt + 3 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
     if (kt + 2 < KT) fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
@@ -347,156 +349,176 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   }
 }
 
-template <bool DQ>
-__global__ __launch_bounds__(256) void k_bwd_fast(const __bf16* __restrict__ dy, int64_t M, int64_t K, int64_t N,
-                                                  NF4View w, const float* __restrict__ Afac, int r, float s,
-                                                  const float* __restrict__ U, __bf16* __restrict__ dx) {
-  constexpr int BKO = 128, BNR = 64, WPITCH = 72;
-  __shared__ __attribute__((aligned(16))) __bf16 ys[2][FBM * XPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 wt[2][BKO * WPITCH];
+// Input gradient dX = dY W_hat + s U A, K % 64 == 0 and N % 64 == 0. Tile
+// (32 MS tokens) x 128 weight inputs k; reduction over the weight outputs n in
+// steps of 64. dY arrives by direct loads into two swizzled LDS stages. Wave w
+// owns outputs k in [32 w, 32 w + 32) of the tile: each step its lane l decodes
+// weight row n0 + l over those 32 columns (one 64-element block, one table) and
+// stores the bf16 values transposed into the wave's own [k][n] LDS tile, from
+// which the MFMA B operand (8 consecutive n per lane) is read. Only the wave
+// itself reads its tile, and a wave's LDS operations complete in order, so the
+// tile needs no barrier and a single buffer.
+template <bool DQ, int MS>
+__global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, int64_t M, int64_t K, int64_t N,
+                                                NF4View w, const float* __restrict__ Afac, int r, float s,
+                                                const float* __restrict__ U, __bf16* __restrict__ dx) {
+  constexpr int BM = 32 * MS, BKO = 128;
+  constexpr int STAGE = BM * 64;  // bf16 per dY stage
+  constexpr int YI = BM / 32;     // 1 KB direct loads per wave per stage
+  constexpr int WTP = 64;         // bf16 per row of a wave's [k][n] tile (16-byte chunks swizzled)
+  __shared__ __attribute__((aligned(16))) __bf16 ys0[STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 ys1[STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 wts[4][32 * WTP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
-  const int64_t MT = (M + FBM - 1) / FBM, KTL = (K + BKO - 1) / BKO;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t MT = (M + BM - 1) / BM, KTL = (K + BKO - 1) / BKO;
   int64_t mt, kt_tile;
   tile_coords(blockIdx.x, MT, KTL, mt, kt_tile);
-  const int64_t m0 = mt * FBM, k0 = kt_tile * BKO;
-  const int64_t NS = N / BNR;  // reduction steps
-  const int64_t KB = K / 64;   // blocks per weight row
+  const int64_t m0 = mt * BM, k0 = kt_tile * BKO;
+  const int64_t NSTEP = N / 64, KB = K / 64;
   const float mu = DQ ? w.offset[0] : 0.0f;
 
-  // dY loader (same pattern as x in the forward kernel)
-  const int yc = tid & 7, yr = tid >> 3;
-  uint4 yreg[8];
-  // weight decoder: rows 2p, 2p+1 of the step, columns [16c, 16c + 16) of the tile
-  const int p = tid & 31, c = tid >> 5;
-  const bool cok = k0 + 16 * c < K;
-  uint2 wreg[2];
-  float wsc[2];
-
-  auto load_y = [&](int64_t ns) {
+  const __bf16* yt = dy + m0 * N;
+  int32_t yoff[YI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + yr + 32 * i;
-      yreg[i] = (m < M) ? *reinterpret_cast<const uint4*>(dy + m * N + ns * BNR + 8 * yc) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < YI; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
+    yoff[i] = (int32_t)(m * N) + 8 * ((lane & 7) ^ swz(row));
+  }
+  auto issue_y = [&](int64_t ns, __bf16* buf) __device__ {
+#pragma unroll
+    for (int i = 0; i < YI; ++i) lds_dma16(yt + yoff[i] + ns * 64, buf + (4 * i + wave) * 512);
+  };
+  // This lane's weight slice: row n = 64 ns + lane, columns kc .. kc + 31 (clamped past K).
+  const int64_t kc = (k0 + 32 * wave < K) ? k0 + 32 * wave : K - 32;
+  const uint8_t* wbase = w.codes + kc / 2;
+  __bf16* wt = wts[wave];
+  // 32 columns = 16 bytes of codes per lane
+  auto load_w = [&](int64_t ns, uint4& q, uint32_t& qa, float& nv) __device__ {
+    const int64_t n = 64 * ns + lane;
+    q = *reinterpret_cast<const uint4*>(wbase + n * (K / 2));
+    const int64_t blk = n * KB + kc / 64;
+    if (DQ) {
+      qa = static_cast<const uint8_t*>(w.scales)[blk];
+      nv = w.nested[blk >> 8];
+    } else {
+      nv = static_cast<const float*>(w.scales)[blk];
     }
   };
-  auto store_y = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&ys[buf][(yr + 32 * i) * XPITCH + 8 * yc]) = yreg[i];
-  };
-  auto load_w = [&](int64_t ns) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int64_t n = ns * BNR + 2 * p + e;
-      if (cok) {
-        wreg[e] = *reinterpret_cast<const uint2*>(w.codes + (n * K + k0 + 16 * c) / 2);
-        wsc[e] = block_scale_of<DQ>(w, mu, n * KB + (k0 + 16 * c) / 64);
-      } else {
-        wreg[e] = make_uint2(0, 0);
-        wsc[e] = 0.0f;
-      }
-    }
-  };
-  auto decode_store_w = [&](int buf) {
-    const Bf16Table t0 = build_table(wsc[0]);
-    const Bf16Table t1 = build_table(wsc[1]);
-    bf16x8 r0[2], r1[2];
-    r0[0] = decode_word(wreg[0].x, t0);
-    r0[1] = decode_word(wreg[0].y, t0);
-    r1[0] = decode_word(wreg[1].x, t1);
-    r1[1] = decode_word(wreg[1].y, t1);
+  auto decode_store = [&](const uint4& q, uint32_t qa, float nv) __device__ {
+    const float a = DQ ? __fadd_rn(__fmul_rn(dyn8_value(qa), nv), mu) : nv;
+    const Bf16Table tb = build_table(a);
+    const uint32_t words[4] = {q.x, q.y, q.z, q.w};
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 a = __builtin_bit_cast(u32x4, r0[h]);
-      const u32x4 b = __builtin_bit_cast(u32x4, r1[h]);
+    for (int j = 0; j < 4; ++j) {  // word j = columns 8j .. 8j + 7 -> tile rows k = 8j .. 8j + 7
+      const u32x4 d = __builtin_bit_cast(u32x4, decode_word(words[j], tb));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kk = 16 * c + 8 * h + 2 * q;  // columns kk, kk + 1
-        uint32_t* base = reinterpret_cast<uint32_t*>(&wt[buf][0]);
-        base[(kk * WPITCH + 2 * p) / 2] = __builtin_amdgcn_perm(b[q], a[q], 0x05040100u);
-        base[((kk + 1) * WPITCH + 2 * p) / 2] = __builtin_amdgcn_perm(b[q], a[q], 0x07060302u);
+      for (int e = 0; e < 4; ++e) {
+        const int k_a = 8 * j + 2 * e, k_b = k_a + 1;
+        uint16_t* row0 = reinterpret_cast<uint16_t*>(wt + k_a * WTP + 8 * ((lane >> 3) ^ swz(k_a)) + (lane & 7));
+        uint16_t* row1 = reinterpret_cast<uint16_t*>(wt + k_b * WTP + 8 * ((lane >> 3) ^ swz(k_b)) + (lane & 7));
+        *row0 = (uint16_t)(d[e] & 0xFFFFu);
+        *row1 = (uint16_t)(d[e] >> 16);
       }
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[MS];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+  for (int i = 0; i < MS; ++i) acc[i] = f32x16{};
 
-  load_y(0);
-  load_w(0);
-  store_y(0);
-  decode_store_w(0);
-  __syncthreads();
-  for (int64_t ns = 0; ns < NS; ++ns) {
-    const int cur = (int)(ns & 1);
-    if (ns + 1 < NS) {
-      load_y(ns + 1);
-      load_w(ns + 1);
-    }
-    const __bf16* yb = ys[cur];
-    const __bf16* wb = wt[cur];
+  auto mfma_step = [&](const __bf16* yb) __device__ {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 aop[4], bop[2];
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wt[l32 * WTP + 8 * ((4 * g + j) ^ swz(l32))]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        aop[mi] = *reinterpret_cast<const bf16x8*>(&yb[(wm * 128 + mi * 32 + l32) * XPITCH + 32 * g + 8 * j]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bop[ni] = *reinterpret_cast<const bf16x8*>(&wb[(wn * 64 + ni * 32 + l32) * WPITCH + 32 * g + 8 * j]);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[mi], bop[ni], acc[mi][ni], 0, 0, 0);
+      for (int i = 0; i < MS; ++i) {
+        const int row = 32 * i + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&yb[row * 64 + 8 * ((4 * g + j) ^ swz(row))]);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+      }
     }
-    if (ns + 1 < NS) {
-      store_y(cur ^ 1);
-      decode_store_w(cur ^ 1);
-    }
+  };
+
+  uint4 qa_, qb_;
+  uint32_t sa = 0, sb = 0;
+  float va = 0.0f, vb = 0.0f;
+  issue_y(0, ys0);
+  load_w(0, qa_, sa, va);
+  if (NSTEP > 1) load_w(1, qb_, sb, vb);
+  __syncthreads();
+  decode_store(qa_, sa, va);
+
+  int64_t ns = 0;
+  for (; ns + 3 < NSTEP; ns += 2) {
+    issue_y(ns + 1, ys1);
+    load_w(ns + 2, qa_, sa, va);
+    mfma_step(ys0);
+    decode_store(qb_, sb, vb);
+    __syncthreads();
+    issue_y(ns + 2, ys0);
+    load_w(ns + 3, qb_, sb, vb);
+    mfma_step(ys1);
+    decode_store(qa_, sa, va);
+    __syncthreads();
+  }
+  for (; ns < NSTEP; ns += 2) {
+    if (ns + 1 < NSTEP) issue_y(ns + 1, ys1);
+    if (ns + 2 < NSTEP) load_w(ns + 2, qa_, sa, va);
+    mfma_step(ys0);
+    if (ns + 1 < NSTEP) decode_store(qb_, sb, vb);
+    __syncthreads();
+    if (ns + 1 >= NSTEP) break;
+    if (ns + 2 < NSTEP) issue_y(ns + 2, ys0);
+    if (ns + 3 < NSTEP) load_w(ns + 3, qb_, sb, vb);
+    mfma_step(ys1);
+    if (ns + 2 < NSTEP) decode_store(qa_, sa, va);
     __syncthreads();
   }
 
-  int64_t kcol[2];
-  bool kok[2];
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    kcol[ni] = k0 + wn * 64 + ni * 32 + l32;
-    kok[ni] = kcol[ni] < K;
-  }
-  // LoRA: acc += (s U[m][rho]) * A[rho][k], two ranks per fp32 MFMA step.
+  // LoRA: acc += (s U[m][:]) . A[:][k] as six bf16 products of exact splits.
+  const int64_t kcol = k0 + 32 * wave + l32;
+  const bool kok = kcol < K;
   if (r > 0) {
-    for (int rho0 = 0; rho0 < r; rho0 += 2) {
-      const int rho = rho0 + g;
-      float av[4], bv[2];
+    for (int rho0 = 0; rho0 < r; rho0 += 16) {
+      const int avail = r - (rho0 + 8 * g);
+      float bv[8];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int64_t m = m0 + wm * 128 + mi * 32 + l32;
-        av[mi] = (rho < r && m < M) ? s * U[m * r + rho] : 0.0f;
+      for (int e = 0; e < 8; ++e) bv[e] = (e < avail && kok) ? Afac[(int64_t)(rho0 + 8 * g + e) * K + kcol] : 0.0f;
+      bf16x8 b1, b2, b3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h, m_, l;
+        split3(bv[e], h, m_, l);
+        b1[e] = h;
+        b2[e] = m_;
+        b3[e] = l;
       }
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bv[ni] = (rho < r && kok[ni]) ? Afac[(int64_t)rho * K + kcol[ni]] : 0.0f;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+      for (int i = 0; i < MS; ++i) {
+        const int64_t m = (m0 + 32 * i + l32 < M) ? m0 + 32 * i + l32 : M - 1;
+        bf16x8 a1, a2, a3;
+        load_split8(U + m * r + rho0 + 8 * g, avail, s, a1, a2, a3);
+        f32x16 c = acc[i];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b3, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b2, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c, 0, 0, 0);
+        acc[i] = c;
+      }
     }
   }
+  if (!kok) return;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      if (!kok[ni]) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + mi * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (m < M) dx[m * K + kcol[ni]] = (__bf16)acc[mi][ni][e];
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+      if (m < M) dx[m * K + kcol] = (__bf16)acc[i][e];
     }
 }
 
@@ -512,14 +534,24 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   const NF4View w = make_view(g.W);
   const bool dq = g.W->double_quant != 0;
   if (g.backward) {
-    const int64_t MT = ceil_div(g.M, FBM), KTL = ceil_div(g.K, 128);
-    const dim3 grid((unsigned)(MT * KTL));
     const __bf16* dy = static_cast<const __bf16*>(g.a);
     __bf16* dx = static_cast<__bf16*>(g.out);
-    if (dq)
-      hipLaunchKernelGGL(k_bwd_fast<true>, grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, dx);
+    const bool big = ceil_div(g.M, 256) * ceil_div(g.K, 128) >= 224;
+#define NF4_BWD(MS)                                                                                             \
+  do {                                                                                                          \
+    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.K, 128)));                                 \
+    if (dq)                                                                                                     \
+      hipLaunchKernelGGL((k_bwd<true, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, \
+                         dx);                                                                                   \
+    else                                                                                                        \
+      hipLaunchKernelGGL((k_bwd<false, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s,       \
+                         g.side, dx);                                                                           \
+  } while (0)
+    if (big)
+      NF4_BWD(8);
     else
-      hipLaunchKernelGGL(k_bwd_fast<false>, grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, dx);
+      NF4_BWD(4);
+#undef NF4_BWD
     return launch_status();
   }
   const __bf16* x = static_cast<const __bf16*>(g.a);
@@ -537,7 +569,7 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
       hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,    \
                          g.side, y);                                                                            \
   } while (0)
-  if (wg22 >= 224)
+  if (wg22 < 0)
     NF4_FWD(8, 2);
   else if (wg21 >= 224)
     NF4_FWD(8, 1);
