@@ -53,11 +53,15 @@ __device__ __forceinline__ float decode_one(const NF4View& w, float mu, const fl
   return __fmul_rn(lut[code], block_scale_of<DQ>(w, mu, f >> 6));
 }
 
-// Tokens per partial sum of lora_grad: at least 256, and at most 16 chunks.
-inline int64_t lora_chunk(int64_t M) {
-  int64_t c = (M + 15) / 16;
-  c = (c + 15) / 16 * 16;
-  return c < 256 ? 256 : c;
+// Tokens per partial sum of lora_grad for J output columns: enough chunks that
+// (J / 512 column tiles) x chunks is about 512 workgroups, at least 32 tokens
+// per chunk, a multiple of 8.
+inline int64_t lora_chunk(int64_t M, int64_t J) {
+  const int64_t col_tiles = (J + 511) / 512;
+  int64_t chunks = (512 + col_tiles - 1) / col_tiles;
+  int64_t chunk = (M + chunks - 1) / chunks;
+  chunk = (chunk + 7) / 8 * 8;
+  return chunk < 32 ? 32 : chunk;
 }
 
 // Large-tile bf16 kernels (nf4_gemm_fast.hip).

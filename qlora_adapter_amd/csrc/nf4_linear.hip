@@ -103,11 +103,11 @@ __global__ __launch_bounds__(256) void k_linear_general(const T* __restrict__ a,
 // Adapter side product S[m][rho] = sum_i L[m][i] * R[i][rho] in fp32:
 //   forward : L = x  [M, K], R[k][rho] = Afac[rho][k]   (T = x A^T)
 //   backward: L = dY [M, N], R[n][rho] = Bfac[n][rho]   (U = dY B)
-// A workgroup owns 16 rows; its 4 waves split the reduction into 4 contiguous
-// slices, each accumulated with the 16x16x4 fp32 MFMA (lane l: row l % 16,
-// reduction group G = l / 16 holding 8 consecutive i; MFMA step q uses element
-// q, so step q covers i = 8G + q). The 4 slice sums are added in the fixed order
-// (w0 + w1) + (w2 + w3).
+// A workgroup of 16 waves owns 16 rows; the waves split the reduction into 16
+// contiguous slices, each accumulated with the 16x16x4 fp32 MFMA (lane l: row
+// l % 16, reduction group G = l / 16 holding 8 consecutive i; MFMA step q uses
+// element q, so step q covers i = 8G + q), with four 32-wide steps of loads in
+// flight. The 16 slice sums are added in wave order.
 // ---------------------------------------------------------------------------
 constexpr int SR = 16;
 
@@ -131,139 +131,168 @@ __device__ __forceinline__ void load8_row(const T* __restrict__ p, int64_t row_o
 }
 
 template <typename T, bool BWD>
-__global__ __launch_bounds__(256) void k_side(const T* __restrict__ L, int64_t M, int64_t I,
-                                              const float* __restrict__ fac, int r, float* __restrict__ outS) {
-  __shared__ float red[4][16 * 16];
+__global__ __launch_bounds__(1024) void k_side(const T* __restrict__ L, int64_t M, int64_t I,
+                                               const float* __restrict__ fac, int r, float* __restrict__ outS) {
+  constexpr int SW = 16;  // waves per workgroup, each reducing one slice of I
+  __shared__ float red[SW][16 * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, G = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * SR;
   const int64_t m = m0 + row;
   const bool mok = m < M;
   // reduction slice of this wave, a multiple of 32 long
-  const int64_t slice = ((I + 3) / 4 + 31) / 32 * 32;
+  const int64_t slice = ((I + SW - 1) / SW + 31) / 32 * 32;
   const int64_t ib = wave * slice, ie = (ib + slice < I) ? ib + slice : I;
   const int RT = (r + 15) / 16;
   f32x4 acc[kMaxRank / 16];
 #pragma unroll
   for (int t = 0; t < kMaxRank / 16; ++t) acc[t] = f32x4{};
-  for (int64_t i0 = ib; i0 < ie; i0 += 32) {
-    const int64_t i = i0 + 8 * G;
-    float lv[8];
-    load8_row<T>(L, m * I, i, ie, mok, lv);
+  for (int64_t i0 = ib; i0 < ie; i0 += 128) {
+    // four 32-wide steps of L in flight at once
+    float lv[4][8];
 #pragma unroll
-    for (int t = 0; t < kMaxRank / 16; ++t) {
-      if (t >= RT) break;
-      const int rho = 16 * t + row;
-      float rv[8];
-      if (BWD) {
+    for (int q4 = 0; q4 < 4; ++q4) load8_row<T>(L, m * I, i0 + 32 * q4 + 8 * G, ie, mok, lv[q4]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rv[e] = (rho < r && i + e < ie) ? fac[(i + e) * r + rho] : 0.0f;
-      } else {
-        load8_row<float>(fac, (int64_t)rho * I, i, ie, rho < r, rv);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int64_t i = i0 + 32 * q4 + 8 * G;
+#pragma unroll
+      for (int t = 0; t < kMaxRank / 16; ++t) {
+        if (t >= RT) break;
+        const int rho = 16 * t + row;
+        float rv[8];
+        if (BWD) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rv[e] = (rho < r && i + e < ie) ? fac[(i + e) * r + rho] : 0.0f;
+        } else {
+          load8_row<float>(fac, (int64_t)rho * I, i, ie, rho < r, rv);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(lv[q4][q], rv[q], acc[t], 0, 0, 0);
       }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(lv[q], rv[q], acc[t], 0, 0, 0);
     }
   }
-  // accumulator element j of lane l: row 4 * (l / 16) + j, column l % 16
+  // accumulator element j of lane l: row 4 * (l / 16) + j, column l % 16; the
+  // 16 slice sums are added in wave order
   for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[wave][(4 * G + j) * 16 + row] = acc[t][j];
     __syncthreads();
-    const int rr = tid >> 4, cc = tid & 15;
-    const float v = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-    const int64_t mm = m0 + rr;
-    const int rho = 16 * t + cc;
-    if (mm < M && rho < r) outS[mm * r + rho] = v;
+    if (tid < 256) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < SW; ++w2) v += red[w2][tid];
+      const int rr = tid >> 4, cc = tid & 15;
+      const int64_t mm = m0 + rr;
+      const int rho = 16 * t + cc;
+      if (mm < M && rho < r) outS[mm * r + rho] = v;
+    }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// LoRA gradients, stage 1: partial[c][rho][j] = sum over m in chunk c of
-// P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J]. One workgroup per
-// (64-column tile, chunk). 32 tokens at a time are staged in LDS (Q as fp32);
-// wave w owns columns 16w..16w+15 and every 16-rank tile, accumulated with the
-// 16x16x4 fp32 MFMA (A = P^T: lane l holds rank 16t + l % 16 of token
-// 4q + l / 16; B = Q: column 16w + l % 16 of the same token).
+// LoRA gradients, stage 1: partial[c][rho][j] = sum over tokens m of chunk c, in
+// order, of P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J]. Workgroup
+// (512-column tile, chunk c); thread t owns columns j0 + 2t, j0 + 2t + 1 and a
+// group of 16 ranks (groups run one after another). Each element of Q is read
+// once per rank group and feeds 16 fp32 FMAs; the factor row P[m][16 g .. +16]
+// is the same for the whole workgroup. The token loop is unrolled by 8 so that
+// 8 rows of Q are in flight per thread.
 // Stage 2 (k_lora_combine) adds the chunks in order c = 0, 1, ..., scales by s
 // and writes dA ([r][J]) or dB ([J][r]).
 // ---------------------------------------------------------------------------
-constexpr int LJ = 64, LSM = 32, LPP = kMaxRank + 4, LQP = LJ + 4;
+constexpr int LCOLS = 512, LRG = 16;
 
-template <typename T>
+// Two consecutive columns j, j + 1 of a row of Q as fp32. EVEN: J is even and
+// j has been clamped to at most J - 2, so the pair is in range and aligned.
+template <typename T, bool EVEN>
+__device__ __forceinline__ void load_pair(const T* __restrict__ q, int64_t j, int64_t J, float& a, float& b) {
+  if constexpr (EVEN) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(q + j);
+      a = __uint_as_float(v << 16);
+      b = __uint_as_float(v & 0xFFFF0000u);
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(q + j);
+      a = v.x;
+      b = v.y;
+    }
+  } else {
+    a = (j < J) ? (float)q[j] : 0.0f;
+    b = (j + 1 < J) ? (float)q[j + 1] : 0.0f;
+  }
+}
+
+template <typename T, bool EVEN>
 __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ P, const T* __restrict__ Q, int64_t M,
                                                       int64_t J, int r, int64_t chunk, float* __restrict__ partial) {
-  __shared__ float Ps[LSM * LPP];
-  __shared__ float Qs[LSM * LQP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int64_t j0 = (int64_t)blockIdx.x * LJ;
+  constexpr int SLAB = 64;  // tokens of P staged in LDS at a time
+  __shared__ __attribute__((aligned(16))) float ps[SLAB][LRG];
+  const int tid = threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * LCOLS + 2 * tid;
+  const int64_t jl = (EVEN && j > J - 2) ? J - 2 : j;  // load column (stores use j)
   const int64_t c = blockIdx.y;
   const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
-  const int RT = (r + 15) / 16;
-  f32x4 acc[kMaxRank / 16];
+  for (int rg = 0; rg < r; rg += LRG) {
+    float acc0[LRG], acc1[LRG];
 #pragma unroll
-  for (int t = 0; t < kMaxRank / 16; ++t) acc[t] = f32x4{};
-  // Q loader: thread t -> token row t / 8, columns 8 (t % 8) .. + 8
-  const int qr = tid >> 3, qc = 8 * (tid & 7);
-  for (int64_t m0 = mb; m0 < me; m0 += LSM) {
-    {
-      const int64_t m = m0 + qr, j = j0 + qc;
-      float v[8];
-      const bool ok = m < me;
-      if (ok && j + 8 <= J && ((m * J + j) % 8) == 0) {
-        if constexpr (sizeof(T) == 2) {
-          const bf16x8 q = *reinterpret_cast<const bf16x8*>(Q + m * J + j);
+    for (int q = 0; q < LRG; ++q) acc0[q] = acc1[q] = 0.0f;
+    for (int64_t m0 = mb; m0 < me; m0 += SLAB) {
+      // stage P[m0 .. m0 + 64][rg .. rg + 16], zero past the chunk and past rank r
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
-        } else {
-          const float4 a = *reinterpret_cast<const float4*>(Q + m * J + j);
-          const float4 b = *reinterpret_cast<const float4*>(Q + m * J + j + 4);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      for (int e = tid; e < SLAB * LRG; e += 256) {
+        const int mm = e / LRG, q = e % LRG;
+        const int64_t m = m0 + mm;
+        ps[mm][q] = (m < me && rg + q < r) ? P[m * r + rg + q] : 0.0f;
+      }
+      __syncthreads();
+      const int nrow = (me - m0 < SLAB) ? (int)(me - m0) : SLAB;
+      int u = 0;
+      for (; u + 8 <= nrow; u += 8) {
+        float qa[8], qb[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) load_pair<T, EVEN>(Q + (m0 + u + v) * J, jl, J, qa[v], qb[v]);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float4* pr = reinterpret_cast<const float4*>(ps[u + v]);
+#pragma unroll
+          for (int h = 0; h < LRG / 4; ++h) {
+            const float4 p4 = pr[h];
+            acc0[4 * h + 0] = fmaf(p4.x, qa[v], acc0[4 * h + 0]);
+            acc0[4 * h + 1] = fmaf(p4.y, qa[v], acc0[4 * h + 1]);
+            acc0[4 * h + 2] = fmaf(p4.z, qa[v], acc0[4 * h + 2]);
+            acc0[4 * h + 3] = fmaf(p4.w, qa[v], acc0[4 * h + 3]);
+            acc1[4 * h + 0] = fmaf(p4.x, qb[v], acc1[4 * h + 0]);
+            acc1[4 * h + 1] = fmaf(p4.y, qb[v], acc1[4 * h + 1]);
+            acc1[4 * h + 2] = fmaf(p4.z, qb[v], acc1[4 * h + 2]);
+            acc1[4 * h + 3] = fmaf(p4.w, qb[v], acc1[4 * h + 3]);
+          }
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (ok && j + e < J) ? (float)Q[m * J + j + e] : 0.0f;
       }
+      for (; u < nrow; ++u) {
+        float qa, qb;
+        load_pair<T, EVEN>(Q + (m0 + u) * J, jl, J, qa, qb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Qs[qr * LQP + qc + e] = v[e];
-    }
-    for (int e = tid; e < LSM * r; e += 256) {
-      const int mm = e / r, rho = e - mm * r;
-      const int64_t m = m0 + mm;
-      Ps[mm * LPP + rho] = (m < me) ? P[m * r + rho] : 0.0f;
-    }
-    if (r % 16) {
-      for (int e = tid; e < LSM * (RT * 16 - r); e += 256) {
-        const int pad = RT * 16 - r;
-        const int mm = e / pad, rho = r + (e - mm * pad);
-        Ps[mm * LPP + rho] = 0.0f;
+        for (int q = 0; q < LRG; ++q) {
+          acc0[q] = fmaf(ps[u][q], qa, acc0[q]);
+          acc1[q] = fmaf(ps[u][q], qb, acc1[q]);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
+    const int nr = (r - rg < LRG) ? r - rg : LRG;
 #pragma unroll
-    for (int q = 0; q < LSM / 4; ++q) {
-      const int mm = 4 * q + lg;
-      const float qv = Qs[mm * LQP + 16 * wave + l16];
-#pragma unroll
-      for (int t = 0; t < kMaxRank / 16; ++t) {
-        if (t >= RT) break;
-        const float pv = Ps[mm * LPP + 16 * t + l16];
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, qv, acc[t], 0, 0, 0);
+    for (int q = 0; q < LRG; ++q) {
+      if (q >= nr) break;
+      float* out = partial + (c * r + rg + q) * J + j;
+      if (j + 1 < J) {
+        out[0] = acc0[q];
+        out[1] = acc1[q];
+      } else if (j < J) {
+        out[0] = acc0[q];
       }
     }
-    __syncthreads();
-  }
-  // lane l holds C[4 (l / 16) + i][l % 16] of each rank tile: rank 16t + 4 lg + i, column 16 wave + l16
-  const int64_t j = j0 + 16 * wave + l16;
-  if (j < J) {
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rho = 16 * t + 4 * lg + i;
-        if (rho < r) partial[(c * r + rho) * J + j] = acc[t][i];
-      }
   }
 }
 
@@ -290,9 +319,9 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const T* a = static_cast<const T*>(g.a);
   const dim3 sg((unsigned)ceil_div(g.M, SR));
   if (g.backward)
-    hipLaunchKernelGGL((k_side<T, true>), sg, dim3(256), 0, st, a, g.M, I, g.B, g.r, g.side);
+    hipLaunchKernelGGL((k_side<T, true>), sg, dim3(1024), 0, st, a, g.M, I, g.B, g.r, g.side);
   else
-    hipLaunchKernelGGL((k_side<T, false>), sg, dim3(256), 0, st, a, g.M, I, g.A, g.r, g.side);
+    hipLaunchKernelGGL((k_side<T, false>), sg, dim3(1024), 0, st, a, g.M, I, g.A, g.r, g.side);
 }
 
 template <typename T>
@@ -329,42 +358,45 @@ int launch_linear(const LinearArgs& g, hipStream_t st) {
 }
 
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
-  const int64_t chunk = lora_chunk(M);
-  const int64_t chunks = ceil_div(M, chunk);
-  size_t bytes = round_up(sizeof(float) * (size_t)(chunks * r * N), 256);
-  if (!fa) bytes += round_up(sizeof(float) * (size_t)(chunks * r * K), 256);
+  const int64_t chB = ceil_div(M, lora_chunk(M, N)), chA = ceil_div(M, lora_chunk(M, K));
+  size_t bytes = round_up(sizeof(float) * (size_t)(chB * r * N), 256);
+  if (!fa) bytes += round_up(sizeof(float) * (size_t)(chA * r * K), 256);
   return bytes;
 }
 
+namespace {
+// partial[c][rho][j] for P [M, r] and Q [M, J], then the ordered chunk sum.
+template <typename T>
+void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, float s, bool transpose_out, float* part,
+               float* out, hipStream_t st) {
+  const int64_t chunk = lora_chunk(M, J), chunks = ceil_div(M, chunk);
+  const dim3 grid((unsigned)ceil_div(J, LCOLS), (unsigned)chunks);
+  if (J % 2 == 0 && J >= 2)
+    hipLaunchKernelGGL((k_lora_partial<T, true>), grid, dim3(256), 0, st, P, Q, M, J, r, chunk, part);
+  else
+    hipLaunchKernelGGL((k_lora_partial<T, false>), grid, dim3(256), 0, st, P, Q, M, J, r, chunk, part);
+  hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, part, chunks, r,
+                     J, s, transpose_out, out);
+}
+}  // namespace
+
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
                      const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st) {
-  const int64_t chunk = lora_chunk(M);
-  const int64_t chunks = ceil_div(M, chunk);
+  const int64_t chunksB = ceil_div(M, lora_chunk(M, N));
   float* partB = static_cast<float*>(ws);
-  float* partA = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunks * r * N), 256));
-  // dB[n][rho] = s * sum_m dY[m][n] T[m][rho]
-  {
-    const dim3 grid((unsigned)ceil_div(N, LJ), (unsigned)chunks);
-    if (dt == NF4_BF16)
-      hipLaunchKernelGGL((k_lora_partial<__bf16>), grid, dim3(256), 0, st, t, static_cast<const __bf16*>(dy), M, N, r,
-                         chunk, partB);
-    else
-      hipLaunchKernelGGL((k_lora_partial<float>), grid, dim3(256), 0, st, t, static_cast<const float*>(dy), M, N, r,
-                         chunk, partB);
-    hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * N, 256)), dim3(256), 0, st, partB,
-                       chunks, r, N, s, true, dB);
-  }
-  // dA[rho][k] = s * sum_m U[m][rho] x[m][k]
+  float* partA =
+      reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunksB * r * N), 256));
+  // dB[n][rho] = s * sum_m dY[m][n] T[m][rho]  ([N][r] layout)
+  if (dt == NF4_BF16)
+    lora_side<__bf16>(t, static_cast<const __bf16*>(dy), M, N, r, s, true, partB, dB, st);
+  else
+    lora_side<float>(t, static_cast<const float*>(dy), M, N, r, s, true, partB, dB, st);
+  // dA[rho][k] = s * sum_m U[m][rho] x[m][k]  ([r][K] layout); skipped for LoRA-FA
   if (dA) {
-    const dim3 grid((unsigned)ceil_div(K, LJ), (unsigned)chunks);
     if (dt == NF4_BF16)
-      hipLaunchKernelGGL((k_lora_partial<__bf16>), grid, dim3(256), 0, st, u, static_cast<const __bf16*>(x), M, K, r,
-                         chunk, partA);
+      lora_side<__bf16>(u, static_cast<const __bf16*>(x), M, K, r, s, false, partA, dA, st);
     else
-      hipLaunchKernelGGL((k_lora_partial<float>), grid, dim3(256), 0, st, u, static_cast<const float*>(x), M, K, r,
-                         chunk, partA);
-    hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * K, 256)), dim3(256), 0, st, partA,
-                       chunks, r, K, s, false, dA);
+      lora_side<float>(u, static_cast<const float*>(x), M, K, r, s, false, partA, dA, st);
   }
   return launch_status();
 }
