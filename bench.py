@@ -35,8 +35,82 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=48, help="token rows of the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=800, help="token rows of the oracle sample")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the same-session copy / library GEMM ceilings")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30  # 1 GiB read + 1 GiB written per copy
+
+
+def copy_probe():
+    """Plain device copies of a known size: under rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE they give the factor between counter KiB and true bytes."""
+    import torch
+    a = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3}), flush=True)
+
+
+def ceilings():
+    """Same-session ceilings (context, never the metric): a 2 GiB device copy
+    and torch's bf16 GEMM (hipBLASLt) at the gate_proj shape 4096x4096x14336."""
+    import torch
+    a = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    x = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    w = torch.randn(14336, 4096, dtype=torch.bfloat16, device="cuda").t().contiguous()
+    for _ in range(3):
+        x @ w
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        x @ w
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 10 * 2 * 4096 * 4096 * 14336 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"device_copy_GBps": round(copy_gbps, 1), "torch_bf16_gemm_TFLOPs_4096x4096x14336": round(gemm_tf, 1),
+            "note": "measured in this run; context only (torch's GEMM multiplies dense bf16 weights)"}
+
+
+def counter_traffic(kernel: str):
+    """HBM-side bytes per launch of the fused GEMM kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the copy-probe
+    calibration; None when the kernel source changed since the counters."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fused_gemm_counters_llama8b_layer.txt")
+    src = os.path.join(ROOT, "qlora_adapter_amd", "csrc", "nf4_gemm_fast.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    key = "fwd" if kernel == "nf4_linear_fwd" else "bwd"
+    try:
+        return float(kv[f"{key}_hbm_bytes_per_launch"])
+    except KeyError:
+        return None
 
 
 def layer_flops(M, N, K, r):
@@ -83,6 +157,9 @@ def cpu_baseline(layers, M, r, s, rows):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -198,6 +275,7 @@ def main():
     dq_gbps = dq_bytes / (dq_ms * 1e-3) / 1e9
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
 
+    ceil = None if args.no_ceilings else ceilings()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, M, r, s, args.cpu_rows)
@@ -221,7 +299,7 @@ def main():
                    "step": "quantize + fused fwd + fused bwd-input + lora_grad + dequantize, all 7 projections"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": counter_traffic(dominant)},
         "roofline_dequant": {"kernel": "nf4_dequantize (bf16 out)", "bound": "hbm", "achieved": round(dq_gbps, 1),
                              "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
                              "traffic": None},
@@ -231,6 +309,7 @@ def main():
                     "quantize_gbps": round(q_gbps, 1), "dequant_ms": round(dq_ms, 3),
                     "dequant_gbps": round(dq_gbps, 1),
                     "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds}},
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
