@@ -176,43 +176,52 @@ __global__ __launch_bounds__(256) void k_dq_nested(const float* __restrict__ abs
   if (lane == 0) nested[j] = m;
 }
 
-// Decode scale of block b (separately rounded multiply and add, no FMA).
-template <bool DQ>
-__device__ __forceinline__ float block_scale(const void* scales, const float* nested, float mu, int64_t b) {
-  if (DQ) {
-    const uint8_t q = static_cast<const uint8_t*>(scales)[b];
-    return __fadd_rn(__fmul_rn(__uint_as_float(c_dyn8[q]), nested[b >> 8]), mu);
-  }
-  return static_cast<const float*>(scales)[b];
-}
-
 // A unit is the 8 weights of one 32-bit code word (bytes 4u..4u+3). Wave w of
-// group g handles units 256*(4g+w) + l + 64q, q = 0..3: each code load is 256
-// contiguous bytes per wave and each bf16 store 1 KB. Units past the last full
-// one (n not a multiple of 8) are decoded element by element by group 0.
+// group g handles units 64*DQ_UNITS*(4g+w) + l + 64q, q < DQ_UNITS: each code
+// load is 256 contiguous bytes per wave and each bf16 store 1 KB. The group's
+// blocks get their scales computed once, one thread per block, into LDS. Units past the
+// last full one (n not a multiple of 8) are decoded element by element by
+// group 0.
+constexpr int DQ_UNITS = 8;
+
 template <bool DQ, bool BF16>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
                                                     const float* __restrict__ nested, const float* __restrict__ offset,
                                                     int64_t n, void* __restrict__ out) {
   __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = __uint_as_float(c_nf4[threadIdx.x]);
-  __syncthreads();
+  constexpr int BLOCKS = 4 * 64 * DQ_UNITS / 8;  // blocks covered by one workgroup
+  __shared__ float sc[BLOCKS];
+  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_value(threadIdx.x);
   const float mu = DQ ? offset[0] : 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t units = n / 8;
-  const int64_t ubase = ((int64_t)blockIdx.x * 4 + wave) * 256 + lane;
+  const int64_t units = n / 8, nb = (n + 63) / 64;
+  const int64_t ubase = ((int64_t)blockIdx.x * 4 + wave) * (64 * DQ_UNITS) + lane;
   const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
-  uint32_t word[4];
+  uint32_t word[DQ_UNITS];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < DQ_UNITS; ++q) {
     const int64_t u = ubase + 64 * q;
     word[q] = (u < units) ? words[u] : 0u;
   }
+  for (int t = threadIdx.x; t < BLOCKS; t += 256) {
+    const int64_t b = (int64_t)blockIdx.x * BLOCKS + t;  // block of the group's range
+    float a = 0.0f;
+    if (b < nb) {
+      if (DQ) {
+        const uint8_t qv = static_cast<const uint8_t*>(scales)[b];
+        a = __fadd_rn(__fmul_rn(dyn8_value(qv), nested[b >> 8]), mu);
+      } else {
+        a = static_cast<const float*>(scales)[b];
+      }
+    }
+    sc[t] = a;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < DQ_UNITS; ++q) {
     const int64_t u = ubase + 64 * q;
     if (u >= units) break;
-    const float a = block_scale<DQ>(scales, nested, mu, u >> 3);
+    const float a = sc[wave * 8 * DQ_UNITS + 8 * q + (lane >> 3)];
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -235,7 +244,9 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   }
   if (blockIdx.x == 0) {
     for (int64_t e = units * 8 + threadIdx.x; e < n; e += blockDim.x) {
-      const float a = block_scale<DQ>(scales, nested, mu, e >> 6);
+      const int64_t b = e >> 6;
+      const float a = DQ ? __fadd_rn(__fmul_rn(dyn8_value(static_cast<const uint8_t*>(scales)[b]), nested[b >> 8]), mu)
+                         : static_cast<const float*>(scales)[b];
       const uint8_t byte = codes[e >> 1];
       const float v = __fmul_rn(lut[(e & 1) ? (byte & 15) : (byte >> 4)], a);
       if (BF16)
@@ -272,7 +283,7 @@ int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, in
 
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s) {
   const int64_t units = t->n / 8;
-  const unsigned groups = (unsigned)(units > 0 ? ceil_div(units, 1024) : 1);
+  const unsigned groups = (unsigned)(units > 0 ? ceil_div(units, 4 * 64 * DQ_UNITS) : 1);
   const bool dq = t->double_quant != 0;
   if (dq && dt == NF4_BF16)
     hipLaunchKernelGGL((k_dequantize<true, true>), dim3(groups), dim3(256), 0, s, t->codes, t->scales, t->nested,
