@@ -1,34 +1,35 @@
-// Large-tile fused NF4 GEMM kernels for gfx950 (bf16 operands, fp32 accumulate).
+// Fused NF4 GEMM kernels for gfx950 (bf16 operands, fp32 accumulate): the
+// forward y = x W_hat^T + s T B^T and the input gradient dX = dY W_hat + s U A
+// with W_hat decoded from the packed NF4 weights on the fly, never stored as a
+// dense matrix (Aner docs "Native model adaptation and NF4", sections "Packed
+// NF4 and the portable QLoRA profile" and "Adapter API").
 //
-// Forward: y = x W_hat^T + s T B^T for K a multiple of 64. A workgroup owns a
-// 256 (tokens) x 128 (outputs) tile and walks K in steps of 64, which is exactly
-// one 64-element quantization block of every weight row. Four waves in a 2 x 2
-// arrangement each own 128 x 64 outputs as 4 x 2 accumulators of the 32x32x16
-// bf16 MFMA.
-//  - x is staged through LDS (double-buffered, rows padded to 144 bytes so that
-//    the 16-byte operand reads of 8 consecutive rows fall in distinct banks).
-//  - The packed weights never touch LDS: each lane loads the 16 bytes (32
-//    nibbles) of its weight row that its MFMA operands need, builds the 16-entry
-//    bf16 table {bf16(fl32(C4[c] * a'))} of that row's block once, and turns
-//    nibbles into bf16 with byte-select (v_perm_b32) lookups. The values are
-//    bit-identical to nf4_dequantize's bf16 output.
-//  - Lane group g = lane / 32 takes k in [32g, 32g + 32) of the block: MFMA step j
-//    uses k = 32g + 8j .. +8 for both operands, a fixed permutation of the
-//    reduction order.
-//  - The LoRA term s T B^T is added to the fp32 accumulators with the 32x32x2
-//    fp32 MFMA before the single bf16 rounding of the output.
+// Common to all kernels here:
+//  - A step of the reduction covers 64 weight inputs, exactly one quantization
+//    block of every weight row. Each decoding lane builds the 16-entry bf16
+//    table {bf16(fl32(C4[c] * a))} of its block once and turns nibbles into
+//    bf16 with byte-select (v_perm_b32) lookups; the values are bit-identical
+//    to nf4_dequantize's bf16 output.
+//  - Activations (x or dY) arrive by direct global->LDS loads into two
+//    double-buffered, XOR-swizzled stages.
+//  - MFMA step j of lane group g = lane / 32 uses reduction indices
+//    32 g + 8 j .. + 8 of the step for both operands (a fixed permutation of
+//    the reduction order).
+//  - The LoRA term is added to the fp32 accumulators with six bf16 MFMA
+//    products of exact three-part splits of both factors before the single
+//    bf16 rounding of the output.
 //  - Workgroups are numbered so that each XCD gets a contiguous run of tiles,
-//    and tiles are visited in groups of 4 token-tiles so that concurrently
-//    running workgroups share x and weight tiles in L2.
+//    visited in groups of 4 token tiles so that concurrently running
+//    workgroups share activation and weight tiles in L2.
 //
-// Input gradient: dX = dY W_hat + s U A for K and N multiples of 64. A
-// workgroup owns 256 (tokens) x 128 (weight inputs k) of dX and walks the
-// reduction over the weight outputs n in steps of 64. Here the weight operand
-// needs consecutive n per lane while the packed rows run along k, so each step
-// the workgroup decodes its 64 x 128 weight slice once, cooperatively, into an
-// LDS tile stored transposed ([k][n], rows padded to 144 bytes): thread t
-// decodes rows 2p, 2p+1 (p = t % 32) over 16 columns and pairs the two rows
-// into one 32-bit LDS word per column with a byte select.
+// k_gemm (problems with at least 128 tiles of 256 x 256): each step the
+// workgroup decodes its weight slice once into LDS, and every wave multiplies
+// 128 tokens x 64 outputs from the two stages (see the comment above k_gemm).
+//
+// k_fwd / k_bwd (smaller problems): 32 MS tokens per workgroup; in k_fwd each
+// lane decodes the 32 weights its own B operand needs straight into registers,
+// in k_bwd each wave decodes its 64 x 32 weight slice into a private
+// transposed LDS tile.
 #include "nf4_device.hpp"
 
 namespace nf4 {
@@ -42,9 +43,12 @@ struct Bf16Table {
   uint32_t lo[4], hi[4];
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16(a) | bf16(b) << 16, both rounded to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 __device__ __forceinline__ Bf16Table build_table(float a) {
@@ -72,27 +76,39 @@ __device__ __forceinline__ void lookup4(const Bf16Table& t, uint32_t sel, uint32
   hi = (hi8 & hi_b) | (~hi8 & hi_a);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Decode one 32-bit code word (8 weights; weight 2p in the high nibble of byte
-// p) into 8 bf16 values in weight order.
-__device__ __forceinline__ bf16x8 decode_word(uint32_t w, const Bf16Table& t) {
-  // selector bytes 0x0C -> 0x00 and 0x0D -> 0xFF turn bit 3 of each index into a byte mask
+// p) into 8 bf16 values in the order w0 w2 w4 w6 w1 w3 w5 w7.
+__device__ __forceinline__ u32x4 decode_word_eo(uint32_t w, const Bf16Table& t) {
+  // Bit 3 of each index becomes a byte mask through the sign-replicating
+  // selectors 8..11 of v_perm_b32 (bits 15, 31, 47, 63 of the 64-bit source
+  // {S0, S1}): for the even weights the index top bits are bits 7, 15, 23, 31
+  // of w, for the odd weights bits 3, 11, 19, 27.
   const uint32_t sel_e = (w >> 4) & 0x07070707u;
-  const uint32_t msk_e = __builtin_amdgcn_perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t msk_e = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
   const uint32_t sel_o = w & 0x07070707u;
-  const uint32_t msk_o = __builtin_amdgcn_perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t w4 = w << 4;
+  const uint32_t msk_o = __builtin_amdgcn_perm(w4 << 8, w4, 0x090B080Au);
   uint32_t el, eh, ol, oh;
   lookup4(t, sel_e, msk_e, el, eh);  // weights 0, 2, 4, 6
   lookup4(t, sel_o, msk_o, ol, oh);  // weights 1, 3, 5, 7
-  const uint32_t e01 = __builtin_amdgcn_perm(eh, el, 0x05010400u);  // bf16(w0) | bf16(w2) << 16
-  const uint32_t e23 = __builtin_amdgcn_perm(eh, el, 0x07030602u);  // bf16(w4) | bf16(w6) << 16
-  const uint32_t o01 = __builtin_amdgcn_perm(oh, ol, 0x05010400u);  // bf16(w1) | bf16(w3) << 16
-  const uint32_t o23 = __builtin_amdgcn_perm(oh, ol, 0x07030602u);  // bf16(w5) | bf16(w7) << 16
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 d;
-  d[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
-  d[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
-  d[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
-  d[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  d[0] = __builtin_amdgcn_perm(eh, el, 0x05010400u);  // bf16(w0) | bf16(w2) << 16
+  d[1] = __builtin_amdgcn_perm(eh, el, 0x07030602u);  // bf16(w4) | bf16(w6) << 16
+  d[2] = __builtin_amdgcn_perm(oh, ol, 0x05010400u);  // bf16(w1) | bf16(w3) << 16
+  d[3] = __builtin_amdgcn_perm(oh, ol, 0x07030602u);  // bf16(w5) | bf16(w7) << 16
+  return d;
+}
+
+// Decode one 32-bit code word into 8 bf16 values in weight order.
+__device__ __forceinline__ bf16x8 decode_word(uint32_t w, const Bf16Table& t) {
+  const u32x4 e = decode_word_eo(w, t);
+  u32x4 d;
+  d[0] = __builtin_amdgcn_perm(e[2], e[0], 0x05040100u);
+  d[1] = __builtin_amdgcn_perm(e[2], e[0], 0x07060302u);
+  d[2] = __builtin_amdgcn_perm(e[3], e[1], 0x05040100u);
+  d[3] = __builtin_amdgcn_perm(e[3], e[1], 0x07060302u);
   return __builtin_bit_cast(bf16x8, d);
 }
 
@@ -410,7 +426,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
     const float a = DQ ? __fadd_rn(__fmul_rn(dyn8_value(qa), nv), mu) : nv;
     const Bf16Table tb = build_table(a);
     const uint32_t words[4] = {q.x, q.y, q.z, q.w};
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // word j = columns 8j .. 8j + 7 -> tile rows k = 8j .. 8j + 7
       const u32x4 d = __builtin_bit_cast(u32x4, decode_word(words[j], tb));
@@ -522,6 +537,386 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Shared-decode GEMM for large problems: 256 x 256 output tiles, 256 threads
+// (4 waves, one per SIMD, each with the full 512-register file), reduction in
+// steps of 64. Each step the workgroup decodes its weight slice once into LDS
+// (every lane one 64-weight block, written as eight 16-byte chunks) while the
+// activation slice arrives by direct global->LDS loads; wave (wm, wn) =
+// (w % 2, w / 2) owns 128 x 128 outputs as 4 x 4 accumulators of the 32x32x16
+// bf16 MFMA (held in the accumulation registers).
+//  - Forward (BWD = false): activations x [M][K], output columns are weight rows
+//    n, the decoded slice is [256 n][64 k] and the B operand (8 consecutive k of
+//    one row n) is a plain 16-byte read.
+//  - Input gradient (BWD = true): activations dY [M][N], output columns are
+//    weight inputs k, the decoded slice is [64 n][256 k] in natural row order
+//    with each 8-column chunk stored in the order 0 2 4 6 1 3 5 7 (the decoder's
+//    natural output; only the output column of each accumulator lane changes),
+//    and the B operand (8 consecutive n for one k) is gathered with two
+//    transposing reads (ds_read_b64_tr_b16: within each 16-lane group, lane i
+//    receives element i % 4 of the 4-element pieces addressed by lanes
+//    4 e + i / 4, e = 0..3).
+//  - Operand k order: MFMA step j of lane group g uses reduction indices
+//    32 g + 8 j .. + 8 of the step for both operands.
+//  - The weight fragment is the MFMA's first operand, so each accumulator holds
+//    a transposed 32 x 32 tile: lane l (l % 32 = token row) holds output columns
+//    8 (e / 4) + 4 (l / 32) + e % 4 in element e, four consecutive columns per
+//    group of four elements, stored as one 8-byte write.
+//  - The decode of the next slice is spread over the MFMA steps (two code words
+//    after each group of sixteen MFMAs) so that it overlaps the matrix core.
+constexpr int GT = 256;          // output tile edge
+constexpr int GSTAGE = GT * 64;  // bf16 per activation stage (and per forward weight stage)
+
+// The [64][256] input-gradient weight slice has a row pitch of WPB = 288 bf16
+// (576 bytes: row r starts 4 r 16-byte bank groups further on) and keeps chunk c
+// of row r at c ^ xbb(r), which only permutes chunks within aligned groups of 4.
+// Sixteen consecutive rows put a given chunk in sixteen different bank groups
+// (conflict-free writes); four rows 4a .. 4a + 3 put four consecutive chunks in
+// sixteen different groups (conflict-free transposing reads); and the column
+// tile enters the read address as a constant offset.
+constexpr int WPB = 288;
+__device__ __forceinline__ int xbb(int r) { return (r >> 2) & 3; }
+
+// Codes of the DW code words (8 DW weights of one block) a lane decodes per
+// step, with the block's scale inputs.
+template <int DW>
+struct WCodes {
+  uint32_t q[DW];
+  uint32_t qa;  // dynamic8 code of the block (double quant)
+  float nv;     // nested max (double quant) or absmax
+};
+
+// The step-dependent parts of the code address and block index are uniform
+// across the wave (cstep, bstep), the lane parts 32-bit offsets (cofs bytes,
+// blane blocks).
+template <bool DQ, int DW>
+__device__ __forceinline__ void gemm_load_codes(const NF4View& w, const uint8_t* cstep, uint32_t cofs, int64_t bstep,
+                                                uint32_t blane, WCodes<DW>& c) {
+  const uint4* p = reinterpret_cast<const uint4*>(cstep + cofs);
+#pragma unroll
+  for (int u = 0; u < DW / 4; ++u) {
+    const uint4 v = p[u];
+    c.q[4 * u] = v.x;
+    c.q[4 * u + 1] = v.y;
+    c.q[4 * u + 2] = v.z;
+    c.q[4 * u + 3] = v.w;
+  }
+  if (DQ) {
+    c.qa = (static_cast<const uint8_t*>(w.scales) + bstep)[blane];
+    c.nv = w.nested[(bstep + blane) >> 8];
+  } else {
+    c.nv = (static_cast<const float*>(w.scales) + bstep)[blane];
+  }
+}
+
+template <bool DQ, int DW>
+__device__ __forceinline__ float gemm_block_scale(const WCodes<DW>& c, const float* d8s, float mu) {
+  return DQ ? __fadd_rn(__fmul_rn(d8s[c.qa], c.nv), mu) : c.nv;
+}
+
+// Decode one code word and store its 8 weights as one 16-byte chunk, in weight
+// order (EO = false) or in the order 0 2 4 6 1 3 5 7 (EO = true).
+template <bool EO>
+__device__ __forceinline__ void gemm_decode_word(uint32_t word, const Bf16Table& tb, __bf16* dst) {
+  if (EO)
+    *reinterpret_cast<u32x4*>(dst) = decode_word_eo(word, tb);
+  else
+    *reinterpret_cast<bf16x8*>(dst) = decode_word(word, tb);
+}
+
+// Weight column held at position p of an even/odd-ordered 8-column chunk.
+__device__ __forceinline__ int eo_col(int p) { return 2 * (p & 3) + (p >> 2); }
+
+// Activation loads of one step (NA per wave): `src` is the wave-uniform address
+// of the step's first column in the tile's first row, aoff the lanes' byte
+// offsets; instruction i of wave v fills stage rows 8 (NW i + v) .. + 7.
+template <int NA, int NW>
+__device__ __forceinline__ void gemm_issue_act(const char* src, const uint32_t (&aoff)[NA], __bf16* buf, int wave) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i) lds_dma16(src + aoff[i], buf + (NW * i + wave) * 512);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
+}
+
+// Operand fragments of MFMA step j: A for the wave's four 32-row tiles, B for
+// its NT 32-column tiles (the wave's columns start at stage column cw).
+template <bool BWD, int NT>
+__device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, int j, int lane, int wm, int cw,
+                                           bf16x8 (&a)[4], bf16x8 (&b)[NT]) {
+  const int g = lane >> 5, l32 = lane & 31;
+  const int q = 4 * g + j;  // reduction chunk of this lane at step j
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!BWD) {
+      const int row = cw + 32 * t + l32;
+      b[t] = *reinterpret_cast<const bf16x8*>(&ws[row * 64 + 8 * (q ^ swz(row))]);
+    } else {
+      const int col = cw + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      bf16x4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * q + 4 * h + ((lane & 15) >> 2);
+        v[h] = lds_read_tr16(&ws[row * WPB + 8 * ((col >> 3) ^ xbb(row)) + (col & 7)]);
+      }
+      b[t] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 128 * wm + 32 * i + l32;
+    a[i] = *reinterpret_cast<const bf16x8*>(&as[row * 64 + 8 * (q ^ swz(row))]);
+  }
+}
+
+// One 64-deep step of the wave's 128 x 32 NT tile from the activation stage
+// `as` and the decoded weight stage `ws`. With DEC, the lane's DW code words of
+// the next step (codes c, block scale sc) are decoded into `wdst` along the
+// way, DW / 4 words after each MFMA step: word u goes to element
+// wbase + 8 (u ^ wsx).
+template <bool BWD, bool DEC, int NT, int DW>
+__device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[4][NT], int lane, int wm,
+                                          int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
+  Bf16Table tb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 a[4], b[NT];
+    gemm_frags<BWD, NT>(as, ws, j, lane, wm, cw, a, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t], a[i], acc[i][t], 0, 0, 0);
+    if (DEC) {
+      if (j == 0) tb = build_table(sc);
+#pragma unroll
+      for (int u = j * DW / 4; u < (j + 1) * DW / 4; ++u)
+        gemm_decode_word<BWD>(c.q[u], tb, wdst + wbase + 8 * (u ^ wsx));
+    }
+  }
+}
+
+// LoRA part of the output tile: acc += (s S[m][:]) . F(:, c) as six bf16
+// products of exact three-part splits of both factors (the F split is the first
+// operand, like the weights). The column of lane l32 in the F fragment is a
+// stage column, mapped to its weight column for the input gradient.
+template <bool BWD, int NT>
+__device__ __forceinline__ void gemm_lora(f32x16 (&acc)[4][NT], int64_t M, int64_t K, int64_t N,
+                                          const float* __restrict__ F, int r, float s, const float* __restrict__ S,
+                                          int64_t m0, int64_t cc, int lane, int wm) {
+  const int g = lane >> 5, l32 = lane & 31;
+  for (int rho0 = 0; rho0 < r; rho0 += 16) {
+    const int avail = r - (rho0 + 8 * g);
+    bf16x8 f1[NT], f2[NT], f3[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t c = cc + 32 * t + (BWD ? (l32 & ~7) + eo_col(l32 & 7) : l32);
+      if (!BWD) {
+        const int64_t n = c < N ? c : N - 1;
+        load_split8(F + n * r + rho0 + 8 * g, avail, 1.0f, f1[t], f2[t], f3[t]);
+      } else {
+        const bool cok = c < K;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (e < avail && cok) ? F[(int64_t)(rho0 + 8 * g + e) * K + c] : 0.0f;
+          __bf16 x1, x2, x3;
+          split3(v, x1, x2, x3);
+          f1[t][e] = x1;
+          f2[t][e] = x2;
+          f3[t][e] = x3;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = (m0 + 128 * wm + 32 * i + l32 < M) ? m0 + 128 * wm + 32 * i + l32 : M - 1;
+      bf16x8 a1, a2, a3;
+      load_split8(S + m * r + rho0 + 8 * g, avail, s, a1, a2, a3);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16 c = acc[i][t];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[t], a3, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[t], a2, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3[t], a1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[t], a2, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[t], a1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[t], a1, c, 0, 0, 0);
+        acc[i][t] = c;
+      }
+    }
+  }
+}
+
+// Output tile store. Accumulator (i, t), elements 4k .. 4k + 3: token row
+// m0 + 128 wm + 32 i + l32, stage columns cc + 32 t + 8 k + 4 g + 0..3. In the
+// forward pass these are four consecutive output columns. In the input gradient
+// the even/odd chunk order puts weight columns 8 k + g + {0, 2, 4, 6} in lane
+// group g; the two lane groups swap half of their values so that each again
+// holds four consecutive columns (g = 0: 8 k .. 8 k + 3, g = 1: 8 k + 4 ..
+// 8 k + 7). Each group of four is one 8-byte buffer store (C % 4 == 0); stores
+// outside the output get an offset past the buffer's end, which the hardware
+// drops, so the epilogue has no branches.
+template <bool BWD, int NT>
+__device__ __forceinline__ void gemm_store(const f32x16 (&acc)[4][NT], __bf16* __restrict__ out, int64_t M, int64_t C,
+                                           int64_t m0, int64_t cc, int lane, int wm) {
+  const int g = lane >> 5, l32 = lane & 31;
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(2 * M * C), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + 128 * wm + 32 * i + l32;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v[4] = {acc[i][t][4 * k], acc[i][t][4 * k + 1], acc[i][t][4 * k + 2], acc[i][t][4 * k + 3]};
+        uint32_t lo, hi;
+        if (!BWD) {
+          lo = pack_bf16x2(v[0], v[1]);
+          hi = pack_bf16x2(v[2], v[3]);
+        } else {
+          const uint32_t p01 = pack_bf16x2(v[0], v[1]);  // g0: c0 c2  g1: c1 c3
+          const uint32_t p23 = pack_bf16x2(v[2], v[3]);  // g0: c4 c6  g1: c5 c7
+          const uint32_t recv = (uint32_t)__shfl_xor((int)(g ? p01 : p23), 32);
+          // g0: own c0 c2, received c1 c3; g1: own c5 c7, received c4 c6
+          const uint32_t ev = g ? recv : p01, od = g ? p23 : recv;
+          lo = __builtin_amdgcn_perm(od, ev, 0x05040100u);
+          hi = __builtin_amdgcn_perm(od, ev, 0x07060302u);
+        }
+        const int64_t c = cc + 32 * t + 8 * k + 4 * g;
+        const uint32_t off = (m < M && c < C) ? (uint32_t)(2 * (m * C + c)) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, orsrc, (int)off, 0, 0);
+      }
+    }
+  }
+}
+
+// out = act W_hat^T + s S F^T (forward: act = x [M][K], F = B [N][r], S = T [M][r])
+// or out = act W_hat + s S F (input gradient: act = dY [M][N], F = A [r][K],
+// S = U [M][r]) for a 256 x 256 output tile per workgroup of NW = 16 / NT waves;
+// wave w owns rows 128 (w % 2) .. + 128 and 32 NT columns from 32 NT (w / 2).
+// The reduction length (K or N) is a multiple of 64 and below 2^22, the packed
+// codes are under 4 GiB, the output has a multiple of 4 columns and is under
+// 2 GiB.
+template <bool BWD, bool DQ, int NT>
+__global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __restrict__ act, int64_t M, int64_t K,
+                                                            int64_t N, NF4View w, const float* __restrict__ F, int r,
+                                                            float s, const float* __restrict__ S,
+                                                            __bf16* __restrict__ out) {
+  constexpr int NW = 16 / NT;         // waves
+  constexpr int NA = 32 / NW;         // activation loads per wave per step
+  constexpr int DW = 2 * NT;          // code words decoded per lane per step
+  constexpr int LPR = 8 / DW;         // lanes per weight block
+  constexpr int WSTAGE = BWD ? 64 * WPB : GSTAGE;  // bf16 per decoded weight stage
+  __shared__ __attribute__((aligned(16))) __bf16 as0[GSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 as1[GSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 ws0[WSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 ws1[WSTAGE];
+  __shared__ float d8s[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, cw = 32 * NT * (wave >> 1);
+  const int64_t R = BWD ? N : K, C = BWD ? K : N;
+  const int64_t MT = (M + GT - 1) / GT, CT = (C + GT - 1) / GT;
+  int64_t mt, ct;
+  tile_coords(blockIdx.x, MT, CT, mt, ct);
+  const int64_t m0 = mt * GT, c0 = ct * GT;
+  const int64_t KT = R / 64, KB = K / 64;
+  if (DQ && tid < 256) d8s[tid] = dyn8_value((uint32_t)tid);
+  const float mu = DQ ? w.offset[0] : 0.0f;
+
+  // Activation loads: lane l of instruction i writes physical chunk l % 8 of
+  // stage row 8 (NW i + wave) + l / 8, i.e. logical chunk (l % 8) ^ swz(row).
+  // Rows past M are clamped (not stored).
+  const char* at = reinterpret_cast<const char*>(act + m0 * R);
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = 8 * (NW * i + wave) + (lane >> 3);
+    const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
+    aoff[i] = (uint32_t)(2 * m * R) + 16 * ((lane & 7) ^ swz(row));
+  }
+
+  // This lane's code words per step (at w.codes + kt * cstep + cofs, block
+  // kt * bstep + blane) and where its decoded chunks go: word u to element
+  // wbase + 8 (u ^ wsx) of the weight stage.
+  uint32_t cofs, blane;
+  int64_t cstep, bstep;
+  int wbase, wsx;
+  if (!BWD) {  // weight row c0 + tid / LPR (clamped past N), words h DW .. of block kt, h = tid % LPR
+    const int rl = tid / LPR, h = tid % LPR;
+    const int64_t n = (c0 + rl < N) ? c0 + rl : N - 1;
+    cofs = (uint32_t)(n * (K / 2) + 4 * DW * h);
+    blane = (uint32_t)(n * KB);
+    cstep = 32;
+    bstep = 1;
+    wbase = rl * 64;
+    wsx = swz(rl) ^ (DW * h);  // chunk (DW h + u) ^ swz(rl) = u ^ wsx for u < DW
+  } else {  // weight row 64 kt + lane, columns kc .. kc + 8 DW - 1 (clamped past K)
+    const int64_t kc = (c0 + 8 * DW * wave < K) ? c0 + 8 * DW * wave : K - 8 * DW;
+    cofs = (uint32_t)(lane * (K / 2) + kc / 2);
+    blane = (uint32_t)(lane * KB + kc / 64);
+    cstep = 64 * (K / 2);
+    bstep = 64 * KB;
+    wbase = lane * WPB + 8 * DW * wave;  // chunks DW wave .. + DW - 1 (xbb permutes within groups of 4)
+    wsx = xbb(lane);
+  }
+
+  f32x16 acc[4][NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = f32x16{};
+
+  // Step indices past the end are clamped to the last step: the surplus loads
+  // and decodes land in buffers that are not read again, and the loop body has
+  // a single path.
+  const int64_t last = KT - 1;
+  const int64_t second = last < 1 ? last : 1;
+  WCodes<DW> ca, cb;
+  gemm_issue_act<NA, NW>(at, aoff, as0, wave);
+  gemm_load_codes<DQ, DW>(w, w.codes, cofs, 0, blane, ca);
+  gemm_load_codes<DQ, DW>(w, w.codes + second * cstep, cofs, second * bstep, blane, cb);
+  __syncthreads();  // d8s
+  {
+    const Bf16Table tb = build_table(gemm_block_scale<DQ, DW>(ca, d8s, mu));
+#pragma unroll
+    for (int u = 0; u < DW; ++u) gemm_decode_word<BWD>(ca.q[u], tb, ws0 + wbase + 8 * (u ^ wsx));
+  }
+  __syncthreads();  // stage 0 complete
+
+  // Step kt multiplies stage kt % 2 while the activations of step kt + 1 land
+  // in the other stage, the codes of step kt + 2 are loaded and the codes of
+  // step kt + 1 are decoded into the other weight stage.
+  for (int64_t kt = 0; kt < KT; kt += 2) {
+    const int64_t k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
+                  k3 = kt + 3 < last ? kt + 3 : last;
+    float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
+    gemm_issue_act<NA, NW>(at + 128 * k1, aoff, as1, wave);
+    gemm_load_codes<DQ, DW>(w, w.codes + k2 * cstep, cofs, k2 * bstep, blane, ca);
+    gemm_step<BWD, true, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx);
+    __syncthreads();
+    if (kt + 1 >= KT) break;
+    sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
+    gemm_issue_act<NA, NW>(at + 128 * k2, aoff, as0, wave);
+    gemm_load_codes<DQ, DW>(w, w.codes + k3 * cstep, cofs, k3 * bstep, blane, cb);
+    gemm_step<BWD, true, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx);
+    __syncthreads();
+  }
+
+  // (The two paths store separately, so that no join merges the accumulators.)
+  const int64_t cc = c0 + cw;
+  if (r > 0) {
+    gemm_lora<BWD, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
+    gemm_store<BWD, NT>(acc, out, M, C, m0, cc, lane, wm);
+  } else {
+    gemm_store<BWD, NT>(acc, out, M, C, m0, cc, lane, wm);
+  }
+}
+
 }  // namespace
 
 bool fast_linear_applies(const LinearArgs& g) {
@@ -530,9 +925,43 @@ bool fast_linear_applies(const LinearArgs& g) {
   return g.K % FBK == 0;
 }
 
+#ifndef NF4_GEMM_MIN_TILES
+#define NF4_GEMM_MIN_TILES 128
+#endif
+
 int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   const NF4View w = make_view(g.W);
   const bool dq = g.W->double_quant != 0;
+  {
+    // 256 x 256 shared-decode kernel when there are enough tiles to fill the chip.
+    const int64_t R = g.backward ? g.N : g.K, C = g.backward ? g.K : g.N;
+    const int64_t tiles = ceil_div(g.M, GT) * ceil_div(C, GT);
+    // (lane offsets into the activations and codes are 32-bit, the output is
+    // written with 8-byte buffer stores at 31-bit offsets)
+    if (tiles >= NF4_GEMM_MIN_TILES && R < (int64_t(1) << 22) && g.N * (g.K / 2) < (int64_t(1) << 32) &&
+        C % 4 == 0 && 2 * g.M * C < (int64_t(1) << 31)) {
+      const __bf16* a = static_cast<const __bf16*>(g.a);
+      __bf16* o = static_cast<__bf16*>(g.out);
+      const float* F = g.backward ? g.A : g.B;
+#ifndef NF4_GEMM_NT
+#define NF4_GEMM_NT 2
+#endif
+      constexpr int NT = NF4_GEMM_NT;
+      const dim3 grid((unsigned)tiles), block(64 * (16 / NT));
+      if (g.backward) {
+        if (dq)
+          hipLaunchKernelGGL((k_gemm<true, true, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+        else
+          hipLaunchKernelGGL((k_gemm<true, false, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+      } else {
+        if (dq)
+          hipLaunchKernelGGL((k_gemm<false, true, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+        else
+          hipLaunchKernelGGL((k_gemm<false, false, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+      }
+      return launch_status();
+    }
+  }
   if (g.backward) {
     const __bf16* dy = static_cast<const __bf16*>(g.a);
     __bf16* dx = static_cast<__bf16*>(g.out);
@@ -556,8 +985,7 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   }
   const __bf16* x = static_cast<const __bf16*>(g.a);
   __bf16* y = static_cast<__bf16*>(g.out);
-  // Tile choice: 256 x 256 unless that leaves most of the 256 CUs idle.
-  const int64_t wg22 = ceil_div(g.M, 256) * ceil_div(g.N, 256);
+  // Tile choice: 256 x 128 unless that leaves most of the 256 CUs idle.
   const int64_t wg21 = ceil_div(g.M, 256) * ceil_div(g.N, 128);
 #define NF4_FWD(MS, NS)                                                                                         \
   do {                                                                                                          \
@@ -569,9 +997,7 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
       hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,    \
                          g.side, y);                                                                            \
   } while (0)
-  if (wg22 < 0)
-    NF4_FWD(8, 2);
-  else if (wg21 >= 224)
+  if (wg21 >= 224)
     NF4_FWD(8, 1);
   else
     NF4_FWD(4, 1);
