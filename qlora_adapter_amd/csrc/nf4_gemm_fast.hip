@@ -682,6 +682,21 @@ template <bool BWD, bool DEC, int NT, int DW>
 __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[4][NT], int lane, int wm,
                                           int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
   Bf16Table tb;
+#ifndef NF4_GEMM_PF
+#define NF4_GEMM_PF 1
+#endif
+#if NF4_GEMM_PF
+  bf16x8 a[2][4], b[2][NT];
+  gemm_frags<BWD, NT>(as, ws, 0, lane, wm, cw, a[0], b[0]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < 3) gemm_frags<BWD, NT>(as, ws, j + 1, lane, wm, cw, a[(j + 1) & 1], b[(j + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j & 1][t], a[j & 1][i], acc[i][t], 0, 0, 0);
+#else
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     bf16x8 a[4], b[NT];
@@ -691,6 +706,7 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t], a[i], acc[i][t], 0, 0, 0);
+#endif
     if (DEC) {
       if (j == 0) tb = build_table(sc);
 #pragma unroll

@@ -191,6 +191,104 @@ __global__ __launch_bounds__(1024) void k_side(const T* __restrict__ L, int64_t 
   }
 }
 
+// Side product for bf16 activations and rank r <= 32 (RT = ceil(r / 16) rank
+// tiles). Same work split as k_side (16 rows per workgroup, 16 waves each
+// reducing one slice of I, slice sums added in wave order), but on the bf16
+// 16x16x32 MFMA: the fp32 factor is split into three bf16 parts whose sum is
+// exact, so every product L * R_p is exact in fp32 and the sum keeps fp32
+// accuracy. Lane l handles row l % 16 of L, rank 16 t + l % 16 of the factor
+// and reduction indices 8 (l / 16) .. + 8 of each 32-wide chunk; four chunks
+// of loads are in flight before any arithmetic.
+template <bool BWD, int RT>
+__global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L, int64_t M, int64_t I,
+                                                    const float* __restrict__ fac, int r, float* __restrict__ outS) {
+  constexpr int SW = 16, PD = 4;
+  __shared__ float red[SW][RT][16 * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * SR;
+  const int64_t m = m0 + row;
+  const bool mok = m < M;
+  const int64_t mrow = mok ? m : M - 1;
+  const int64_t NC = (I + 31) / 32;
+  const int64_t cpw = (NC + SW - 1) / SW;
+  const int64_t cb = wave * cpw, ce = (cb + cpw < NC) ? cb + cpw : NC;
+  const bool vec_l = (I % 8) == 0;
+  const bool vec_f = !BWD && (I % 4) == 0 && (reinterpret_cast<uintptr_t>(fac) % 16) == 0;
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{};
+  for (int64_t c0 = cb; c0 < ce; c0 += PD) {
+    bf16x8 lv[PD];
+    float rv[PD][RT][8];
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const bool cok = c0 + u < ce;
+      const int64_t i = 32 * (cok ? c0 + u : ce - 1) + 8 * kg;
+      // L[m][i .. i + 7], zero past I, past M or for a chunk past the slice
+      if (vec_l && i + 8 <= I) {
+        lv[u] = *reinterpret_cast<const bf16x8*>(L + mrow * I + i);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lv[u][e] = (i + e < I) ? L[mrow * I + i + e] : (__bf16)0.0f;
+      }
+      if (!(cok && mok)) lv[u] = bf16x8{};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int rho = 16 * t + row;
+        if (BWD) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r && i + e < I) ? fac[(i + e) * r + rho] : 0.0f;
+        } else if (vec_f && i + 8 <= I && rho < r) {
+          const float4 a = *reinterpret_cast<const float4*>(fac + (int64_t)rho * I + i);
+          const float4 b = *reinterpret_cast<const float4*>(fac + (int64_t)rho * I + i + 4);
+          rv[u][t][0] = a.x; rv[u][t][1] = a.y; rv[u][t][2] = a.z; rv[u][t][3] = a.w;
+          rv[u][t][4] = b.x; rv[u][t][5] = b.y; rv[u][t][6] = b.z; rv[u][t][7] = b.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r && i + e < I) ? fac[(int64_t)rho * I + i + e] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        bf16x8 p1, p2, p3;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = rv[u][t][e];
+          const __bf16 h1 = (__bf16)v;
+          const float r1 = v - (float)h1;
+          const __bf16 h2 = (__bf16)r1;
+          p1[e] = h1;
+          p2[e] = h2;
+          p3[e] = (__bf16)(r1 - (float)h2);
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv[u], p3, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv[u], p2, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv[u], p1, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // accumulator element j of lane l: row 4 (l / 16) + j, column l % 16; the
+  // slice sums are added in wave order
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wave][t][(4 * kg + j) * 16 + row] = acc[t][j];
+  __syncthreads();
+  if (tid < 256 * RT) {
+    const int t = tid >> 8, e = tid & 255;
+    float v = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < SW; ++w2) v += red[w2][t][e];
+    const int64_t mm = m0 + (e >> 4);
+    const int rho = 16 * t + (e & 15);
+    if (mm < M && rho < r) outS[mm * r + rho] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LoRA gradients, stage 1: partial[c][rho][j] = sum over tokens m of chunk c, in
 // order, of P[m][rho] * Q[m][j]; P fp32 [M, r], Q of type T [M, J]. Workgroup
@@ -318,6 +416,21 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const int64_t I = g.backward ? g.N : g.K;
   const T* a = static_cast<const T*>(g.a);
   const dim3 sg((unsigned)ceil_div(g.M, SR));
+  if constexpr (sizeof(T) == 2) {
+    if (g.r <= 32) {
+      const float* fac = g.backward ? g.B : g.A;
+#define NF4_SIDE(BWD, RT) hipLaunchKernelGGL((k_side_bf16<BWD, RT>), sg, dim3(1024), 0, st, a, g.M, I, fac, g.r, g.side)
+      if (g.backward) {
+        if (g.r <= 16) NF4_SIDE(true, 1);
+        else NF4_SIDE(true, 2);
+      } else {
+        if (g.r <= 16) NF4_SIDE(false, 1);
+        else NF4_SIDE(false, 2);
+      }
+#undef NF4_SIDE
+      return;
+    }
+  }
   if (g.backward)
     hipLaunchKernelGGL((k_side<T, true>), sg, dim3(1024), 0, st, a, g.M, I, g.B, g.r, g.side);
   else
