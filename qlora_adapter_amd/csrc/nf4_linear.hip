@@ -400,8 +400,19 @@ __global__ __launch_bounds__(256) void k_lora_combine(const float* __restrict__ 
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)r * J) return;
   const int64_t rho = idx / J, j = idx % J;
+  const float* p = partial + rho * J + j;
+  const int64_t cs = (int64_t)r * J;  // stride between chunks
   float sum = 0.0f;
-  for (int64_t c = 0; c < chunks; ++c) sum += partial[(c * r + rho) * J + j];
+  int64_t c = 0;
+  // eight chunks of loads in flight; the sum stays in chunk order
+  for (; c + 8 <= chunks; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(c + u) * cs];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; c < chunks; ++c) sum += p[c * cs];
   const float v = s * sum;
   if (transpose_out)
     out[j * r + rho] = v;

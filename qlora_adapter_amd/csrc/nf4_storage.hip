@@ -47,12 +47,37 @@ __global__ void k_set_status(int32_t* status) {
 // 8 weights starting at 512*it + 8*l of the wave's range, so 8 lanes hold one
 // block. Writes codes, absmax (to `absmax`), and with DQ the group's pairwise
 // fp64 sum of its 256 maxima (zero beyond nb) to partials[blockIdx.x].
+//
+// The code of x = fl32(v / m) is found through a 256-bin table over [-1, 1]:
+// bin b = floor((x + 1) * 128) holds the threshold t_k nearest to its centre
+// and k, and code = k + (x > t_k). Thresholds are more than 0.07 apart and a bin
+// is 1/128 wide, so every x of the bin lies between t_(k-1) and t_(k+1) and the
+// count is exact. x is first taken as v * rcp(m) (within 3e-7 of v / m for
+// |v| <= m, m normal); only when it falls within 2^-14 |t_k| of t_k, or m is not
+// a normal number, is the correctly rounded quotient computed, so the decision
+// always matches fl32(v / m) > t_k.
 template <bool DQ>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, int64_t n,
                                                   uint8_t* __restrict__ codes, float* __restrict__ absmax,
                                                   double* __restrict__ partials, int32_t* __restrict__ status) {
   __shared__ float s_max[256];
+  __shared__ float2 s_bin[256];  // (t_k, k as bits) per bin
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {
+    const float centre = ((float)threadIdx.x + 0.5f) / 128.0f - 1.0f;
+    int best = 0;
+    float bd = fabsf(__uint_as_float(kNF4Thr[0]) - centre);
+#pragma unroll
+    for (int k = 1; k < NF4_THRESHOLDS_COUNT; ++k) {
+      const float d = fabsf(__uint_as_float(kNF4Thr[k]) - centre);
+      if (d < bd) {
+        bd = d;
+        best = k;
+      }
+    }
+    s_bin[threadIdx.x] = make_float2(__uint_as_float(kNF4Thr[best]), __uint_as_float((uint32_t)best));
+  }
+  __syncthreads();
   const int64_t nbytes = (n + 1) / 2;
   const int64_t base = (int64_t)blockIdx.x * 16384 + (int64_t)wave * 4096 + 8 * lane;
   bool bad = false;
@@ -78,10 +103,19 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, i
     m = fmaxf(m, __shfl_xor(m, 2));
     m = fmaxf(m, __shfl_xor(m, 4));
     uint32_t packed = 0;
+    const bool exact = !(m >= 1.17549435e-38f && m <= 3.40282347e38f);  // m zero, denormal or not finite
+    const float rm = __builtin_amdgcn_rcpf(m);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t c = (m > 0.0f) ? nf4_code(v[j] / m) : 7u;  // IEEE division
-      if (e0 + j >= n) c = 0;                             // padding nibble past the end
+      float x = v[j] * rm;
+      if (exact) x = v[j] / m;  // IEEE division
+      int b = (int)((x + 1.0f) * 128.0f);
+      b = b < 0 ? 0 : (b > 255 ? 255 : b);
+      const float2 e = s_bin[b];
+      uint32_t c = __float_as_uint(e.y) + ((x > e.x) ? 1u : 0u);
+      if (!exact && fabsf(x - e.x) < 6.103515625e-05f * fabsf(e.x)) c = __float_as_uint(e.y) + ((v[j] / m > e.x) ? 1u : 0u);
+      if (!(m > 0.0f)) c = 7u;
+      if (e0 + j >= n) c = 0;  // padding nibble past the end
       // element 2p -> high nibble of byte p, element 2p+1 -> low nibble
       packed |= c << (8 * (j >> 1) + ((j & 1) ? 0 : 4));
     }
