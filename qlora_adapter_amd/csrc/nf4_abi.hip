@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_device_cus[kMaxDevices];  // compute units, once known
 std::mutex g_device_mu;
 
 // The current device must be gfx950 (checked once per device).
@@ -29,6 +30,7 @@ int check_device() {
       hipDeviceProp_t prop;
       if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NF4_EDEVICE;
       state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+      g_device_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
       g_device_ok[dev].store(state, std::memory_order_release);
     }
   }
@@ -36,6 +38,18 @@ int check_device() {
 }
 
 bool valid_dtype(nf4_dtype d) { return d == NF4_F32 || d == NF4_BF16; }
+
+}  // namespace
+
+// Compute units of the current device (known once check_device has run on it).
+int64_t nf4::device_cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int n = g_device_cus[dev].load(std::memory_order_acquire);
+  return n > 0 ? n : 256;
+}
+
+namespace {
 
 // Structural checks of a packed tensor that holds n elements.
 int check_tensor(const nf4_tensor* t, int64_t n) {

@@ -115,10 +115,11 @@ __device__ __forceinline__ bf16x8 decode_word(uint32_t w, const Bf16Table& t) {
 // Tile coordinates of workgroup b: a contiguous run of tiles per XCD (workgroups
 // are dealt to the 8 XCDs round-robin), then groups of GM token-tiles walked
 // token-tile-fastest.
-__device__ __forceinline__ void tile_coords(int64_t b, int64_t MT, int64_t NT, int64_t& mt, int64_t& nt) {
-  const int64_t nwg = MT * NT;
-  int64_t t = b;
-  if (nwg % 8 == 0) t = (b % 8) * (nwg / 8) + b / 8;
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t nwg) {
+  return (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
+}
+
+__device__ __forceinline__ void group_map(int64_t t, int64_t MT, int64_t NT, int64_t& mt, int64_t& nt) {
   constexpr int64_t GM = 4;
   const int64_t group = t / (GM * NT);
   const int64_t first_m = group * GM;
@@ -126,6 +127,10 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t MT, int64_t NT, i
   const int64_t within = t - group * GM * NT;
   mt = first_m + within % gm;
   nt = within / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int64_t b, int64_t MT, int64_t NT, int64_t& mt, int64_t& nt) {
+  group_map(xcd_order(b, MT * NT), MT, NT, mt, nt);
 }
 
 constexpr int FBM = 256, FBN = 128, FBK = 64;
@@ -643,11 +648,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
 }
 
-// Operand fragments of MFMA step j: A for the wave's four 32-row tiles, B for
+// Operand fragments of MFMA step j: A for the wave's MS 32-row tiles, B for
 // its NT 32-column tiles (the wave's columns start at stage column cw).
-template <bool BWD, int NT>
+template <bool BWD, int MS, int NT>
 __device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, int j, int lane, int wm, int cw,
-                                           bf16x8 (&a)[4], bf16x8 (&b)[NT]) {
+                                           bf16x8 (&a)[MS], bf16x8 (&b)[NT]) {
   const int g = lane >> 5, l32 = lane & 31;
   const int q = 4 * g + j;  // reduction chunk of this lane at step j
 #pragma unroll
@@ -667,42 +672,42 @@ __device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, i
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 128 * wm + 32 * i + l32;
+  for (int i = 0; i < MS; ++i) {
+    const int row = 32 * MS * wm + 32 * i + l32;
     a[i] = *reinterpret_cast<const bf16x8*>(&as[row * 64 + 8 * (q ^ swz(row))]);
   }
 }
 
-// One 64-deep step of the wave's 128 x 32 NT tile from the activation stage
+// One 64-deep step of the wave's 32 MS x 32 NT tile from the activation stage
 // `as` and the decoded weight stage `ws`. With DEC, the lane's DW code words of
 // the next step (codes c, block scale sc) are decoded into `wdst` along the
 // way, DW / 4 words after each MFMA step: word u goes to element
 // wbase + 8 (u ^ wsx).
-template <bool BWD, bool DEC, int NT, int DW>
-__device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[4][NT], int lane, int wm,
+template <bool BWD, bool DEC, int MS, int NT, int DW>
+__device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[MS][NT], int lane, int wm,
                                           int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
   Bf16Table tb;
 #ifndef NF4_GEMM_PF
 #define NF4_GEMM_PF 1
 #endif
 #if NF4_GEMM_PF
-  bf16x8 a[2][4], b[2][NT];
-  gemm_frags<BWD, NT>(as, ws, 0, lane, wm, cw, a[0], b[0]);
+  bf16x8 a[2][MS], b[2][NT];
+  gemm_frags<BWD, MS, NT>(as, ws, 0, lane, wm, cw, a[0], b[0]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (j < 3) gemm_frags<BWD, NT>(as, ws, j + 1, lane, wm, cw, a[(j + 1) & 1], b[(j + 1) & 1]);
+    if (j < 3) gemm_frags<BWD, MS, NT>(as, ws, j + 1, lane, wm, cw, a[(j + 1) & 1], b[(j + 1) & 1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j & 1][t], a[j & 1][i], acc[i][t], 0, 0, 0);
 #else
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    bf16x8 a[4], b[NT];
-    gemm_frags<BWD, NT>(as, ws, j, lane, wm, cw, a, b);
+    bf16x8 a[MS], b[NT];
+    gemm_frags<BWD, MS, NT>(as, ws, j, lane, wm, cw, a, b);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t], a[i], acc[i][t], 0, 0, 0);
@@ -716,12 +721,25 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
   }
 }
 
+// Step barrier of k_gemm. Every wave issues its activation loads for the next
+// stage first and its NCL code/scale loads for a later step after them (a
+// scheduling barrier keeps that order), so vmcnt(NCL) means the activation
+// loads have landed in LDS while the code loads may still be in flight; they
+// are first used one step later. lgkmcnt(0) completes this wave's decoder
+// stores and operand reads before the other waves go on.
+template <int NCL>
+__device__ __forceinline__ void gemm_step_barrier() {
+  static_assert(NCL < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(NCL | (7 << 4));  // vmcnt(NCL) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 // LoRA part of the output tile: acc += (s S[m][:]) . F(:, c) as six bf16
 // products of exact three-part splits of both factors (the F split is the first
 // operand, like the weights). The column of lane l32 in the F fragment is a
 // stage column, mapped to its weight column for the input gradient.
-template <bool BWD, int NT>
-__device__ __forceinline__ void gemm_lora(f32x16 (&acc)[4][NT], int64_t M, int64_t K, int64_t N,
+template <bool BWD, int MS, int NT>
+__device__ __forceinline__ void gemm_lora(f32x16 (&acc)[MS][NT], int64_t M, int64_t K, int64_t N,
                                           const float* __restrict__ F, int r, float s, const float* __restrict__ S,
                                           int64_t m0, int64_t cc, int lane, int wm) {
   const int g = lane >> 5, l32 = lane & 31;
@@ -748,8 +766,9 @@ __device__ __forceinline__ void gemm_lora(f32x16 (&acc)[4][NT], int64_t M, int64
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = (m0 + 128 * wm + 32 * i + l32 < M) ? m0 + 128 * wm + 32 * i + l32 : M - 1;
+    for (int i = 0; i < MS; ++i) {
+      const int64_t mr = m0 + 32 * MS * wm + 32 * i + l32;
+      const int64_t m = mr < M ? mr : M - 1;
       bf16x8 a1, a2, a3;
       load_split8(S + m * r + rho0 + 8 * g, avail, s, a1, a2, a3);
 #pragma unroll
@@ -768,7 +787,7 @@ __device__ __forceinline__ void gemm_lora(f32x16 (&acc)[4][NT], int64_t M, int64
 }
 
 // Output tile store. Accumulator (i, t), elements 4k .. 4k + 3: token row
-// m0 + 128 wm + 32 i + l32, stage columns cc + 32 t + 8 k + 4 g + 0..3. In the
+// m0 + 32 MS wm + 32 i + l32, stage columns cc + 32 t + 8 k + 4 g + 0..3. In the
 // forward pass these are four consecutive output columns. In the input gradient
 // the even/odd chunk order puts weight columns 8 k + g + {0, 2, 4, 6} in lane
 // group g; the two lane groups swap half of their values so that each again
@@ -776,15 +795,15 @@ __device__ __forceinline__ void gemm_lora(f32x16 (&acc)[4][NT], int64_t M, int64
 // 8 k + 7). Each group of four is one 8-byte buffer store (C % 4 == 0); stores
 // outside the output get an offset past the buffer's end, which the hardware
 // drops, so the epilogue has no branches.
-template <bool BWD, int NT>
-__device__ __forceinline__ void gemm_store(const f32x16 (&acc)[4][NT], __bf16* __restrict__ out, int64_t M, int64_t C,
+template <bool BWD, int MS, int NT>
+__device__ __forceinline__ void gemm_store(const f32x16 (&acc)[MS][NT], __bf16* __restrict__ out, int64_t M, int64_t C,
                                            int64_t m0, int64_t cc, int lane, int wm) {
   const int g = lane >> 5, l32 = lane & 31;
   typedef int i32x2 __attribute__((ext_vector_type(2)));
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(2 * M * C), 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + 128 * wm + 32 * i + l32;
+  for (int i = 0; i < MS; ++i) {
+    const int64_t m = m0 + 32 * MS * wm + 32 * i + l32;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -813,23 +832,30 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[4][NT], __bf16* _
 
 // out = act W_hat^T + s S F^T (forward: act = x [M][K], F = B [N][r], S = T [M][r])
 // or out = act W_hat + s S F (input gradient: act = dY [M][N], F = A [r][K],
-// S = U [M][r]) for a 256 x 256 output tile per workgroup of NW = 16 / NT waves;
-// wave w owns rows 128 (w % 2) .. + 128 and 32 NT columns from 32 NT (w / 2).
-// The reduction length (K or N) is a multiple of 64 and below 2^22, the packed
+// S = U [M][r]) for a 64 MS x 256 output tile per workgroup of NW = 16 / NT
+// waves; wave w owns rows 32 MS (w % 2) .. + 32 MS and 32 NT columns from
+// 32 NT (w / 2). The 256 x 256 tiles of the problem are numbered as in
+// group_map; a workgroup of the MS = 4 kernel computes tile tbase +
+// xcd_order(b), one of the MS = 2 kernel the upper or lower half of tile
+// tbase + xcd_order(b) / 2 (so that a grid that does not fill its last round
+// of the chip with whole tiles can finish with half-height ones). The
+// reduction length (K or N) is a multiple of 64 and below 2^22, the packed
 // codes are under 4 GiB, the output has a multiple of 4 columns and is under
 // 2 GiB.
-template <bool BWD, bool DQ, int NT>
+template <bool BWD, bool DQ, int NT, int MS>
 __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __restrict__ act, int64_t M, int64_t K,
                                                             int64_t N, NF4View w, const float* __restrict__ F, int r,
                                                             float s, const float* __restrict__ S,
-                                                            __bf16* __restrict__ out) {
+                                                            __bf16* __restrict__ out, int64_t tbase) {
   constexpr int NW = 16 / NT;         // waves
-  constexpr int NA = 32 / NW;         // activation loads per wave per step
+  constexpr int BM = 64 * MS;         // tile rows
+  constexpr int NA = BM / (8 * NW);   // activation loads per wave per step
   constexpr int DW = 2 * NT;          // code words decoded per lane per step
   constexpr int LPR = 8 / DW;         // lanes per weight block
+  constexpr int NCL = DW / 4 + (DQ ? 2 : 1);  // code and scale loads per lane per step
   constexpr int WSTAGE = BWD ? 64 * WPB : GSTAGE;  // bf16 per decoded weight stage
-  __shared__ __attribute__((aligned(16))) __bf16 as0[GSTAGE];
-  __shared__ __attribute__((aligned(16))) __bf16 as1[GSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 as0[BM * 64];
+  __shared__ __attribute__((aligned(16))) __bf16 as1[BM * 64];
   __shared__ __attribute__((aligned(16))) __bf16 ws0[WSTAGE];
   __shared__ __attribute__((aligned(16))) __bf16 ws1[WSTAGE];
   __shared__ float d8s[256];
@@ -838,8 +864,9 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   const int64_t R = BWD ? N : K, C = BWD ? K : N;
   const int64_t MT = (M + GT - 1) / GT, CT = (C + GT - 1) / GT;
   int64_t mt, ct;
-  tile_coords(blockIdx.x, MT, CT, mt, ct);
-  const int64_t m0 = mt * GT, c0 = ct * GT;
+  const int64_t xb = xcd_order(blockIdx.x, gridDim.x);
+  group_map(tbase + (MS == 4 ? xb : xb >> 1), MT, CT, mt, ct);
+  const int64_t m0 = mt * GT + (MS == 4 ? 0 : BM * (xb & 1)), c0 = ct * GT;
   const int64_t KT = R / 64, KB = K / 64;
   if (DQ && tid < 256) d8s[tid] = dyn8_value((uint32_t)tid);
   const float mu = DQ ? w.offset[0] : 0.0f;
@@ -881,9 +908,9 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     wsx = xbb(lane);
   }
 
-  f32x16 acc[4][NT];
+  f32x16 acc[MS][NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x16{};
 
@@ -910,26 +937,32 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   for (int64_t kt = 0; kt < KT; kt += 2) {
     const int64_t k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
                   k3 = kt + 3 < last ? kt + 3 : last;
+    // (The scale's table read precedes the activation loads: an LDS read
+    // issued after them would wait for them.)
     float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_issue_act<NA, NW>(at + 128 * k1, aoff, as1, wave);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k2 * cstep, cofs, k2 * bstep, blane, ca);
-    gemm_step<BWD, true, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx);
-    __syncthreads();
+    gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx);
+    gemm_step_barrier<NCL>();
     if (kt + 1 >= KT) break;
     sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_issue_act<NA, NW>(at + 128 * k2, aoff, as0, wave);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k3 * cstep, cofs, k3 * bstep, blane, cb);
-    gemm_step<BWD, true, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx);
-    __syncthreads();
+    gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx);
+    gemm_step_barrier<NCL>();
   }
 
   // (The two paths store separately, so that no join merges the accumulators.)
   const int64_t cc = c0 + cw;
   if (r > 0) {
-    gemm_lora<BWD, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
-    gemm_store<BWD, NT>(acc, out, M, C, m0, cc, lane, wm);
+    gemm_lora<BWD, MS, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
+    gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
   } else {
-    gemm_store<BWD, NT>(acc, out, M, C, m0, cc, lane, wm);
+    gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
   }
 }
 
@@ -963,18 +996,33 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
 #define NF4_GEMM_NT 2
 #endif
       constexpr int NT = NF4_GEMM_NT;
-      const dim3 grid((unsigned)tiles), block(64 * (16 / NT));
+      const dim3 block(64 * (16 / NT));
+      // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
+      // last round of at most half the CUs is run as twice as many half tiles.
+      const int64_t cus = device_cu_count();
+      const int64_t tail = tiles > cus ? tiles % cus : 0;
+      const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
+#define NF4_GEMM(BWD, DQ, MS, NWG, TB)                                                                                 \
+  hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, MS>), dim3((unsigned)(NWG)), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, \
+                     g.side, o, (int64_t)(TB))
+#define NF4_GEMM_BOTH(BWD, DQ)                                          \
+  do {                                                                  \
+    NF4_GEMM(BWD, DQ, 4, whole, 0);                                     \
+    if (whole < tiles) NF4_GEMM(BWD, DQ, 2, 2 * (tiles - whole), whole); \
+  } while (0)
       if (g.backward) {
         if (dq)
-          hipLaunchKernelGGL((k_gemm<true, true, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+          NF4_GEMM_BOTH(true, true);
         else
-          hipLaunchKernelGGL((k_gemm<true, false, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+          NF4_GEMM_BOTH(true, false);
       } else {
         if (dq)
-          hipLaunchKernelGGL((k_gemm<false, true, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+          NF4_GEMM_BOTH(false, true);
         else
-          hipLaunchKernelGGL((k_gemm<false, false, NT>), grid, block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, g.side, o);
+          NF4_GEMM_BOTH(false, false);
       }
+#undef NF4_GEMM_BOTH
+#undef NF4_GEMM
       return launch_status();
     }
   }

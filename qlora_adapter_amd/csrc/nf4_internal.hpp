@@ -56,4 +56,7 @@ int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EDEVICE; }
 
+// Compute units of the current device (256 on MI355X).
+int64_t device_cu_count();
+
 }  // namespace nf4
