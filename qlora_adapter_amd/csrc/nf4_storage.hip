@@ -262,18 +262,21 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
       const uint32_t nib = (word[q] >> (8 * (j >> 1) + ((j & 1) ? 0 : 4))) & 15u;
       v[j] = __fmul_rn(lut[nib], a);
     }
+    // streaming stores: the decoded matrix is not read back by this kernel
     if (BF16) {
-      uint32_t o[4];
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+      u4v o;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const __bf16 lo = (__bf16)v[2 * p], hi = (__bf16)v[2 * p + 1];  // round to nearest even
-        o[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      reinterpret_cast<uint4*>(out)[u] = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int p = 0; p < 4; ++p)  // round to nearest even, one v_cvt_pk_bf16_f32 per pair
+        o[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{v[2 * p], v[2 * p + 1]}), b2));
+      __builtin_nontemporal_store(o, reinterpret_cast<u4v*>(out) + u);
     } else {
-      float4* o = reinterpret_cast<float4*>(out) + 2 * u;
-      o[0] = make_float4(v[0], v[1], v[2], v[3]);
-      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      f4v* o = reinterpret_cast<f4v*>(out) + 2 * u;
+      __builtin_nontemporal_store((f4v{v[0], v[1], v[2], v[3]}), o);
+      __builtin_nontemporal_store((f4v{v[4], v[5], v[6], v[7]}), o + 1);
     }
   }
   if (blockIdx.x == 0) {
