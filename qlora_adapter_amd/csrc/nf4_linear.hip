@@ -394,6 +394,131 @@ __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ 
   }
 }
 
+// Stage 1 on the bf16 MFMA for bf16 Q and r <= 32, same partial layout as
+// k_lora_partial. The fp32 factor P is split into three bf16 parts whose sum is
+// exact, so every product P_p[m][rho] * Q[m][j] is exact in fp32. Workgroup
+// (256-column tile, chunk c) of 4 waves; wave w owns columns 64 w .. + 64 as two
+// 32 x 32 accumulators D[rho][j] of the 32x32x16 MFMA (rank rows past r are
+// zero). The chunk is walked in steps of 32 tokens: the workgroup stages
+// Q[m .. m + 31][j0 .. j0 + 255] (rows padded to 576 bytes, so four consecutive
+// rows fall in four different quarters of the banks) and the three parts of
+// P[m .. m + 31][0 .. 31] (64-byte rows) in LDS; both MFMA operands need 8
+// consecutive tokens per lane and are gathered with ds_read_b64_tr_b16 (within
+// a 16-lane group, lane i receives element i % 4 of the 4-element pieces
+// addressed by lanes 4 e + i / 4). The next step's loads are in flight while
+// the current one multiplies.
+constexpr int LQP = 288;  // bf16 per staged Q row
+constexpr int LPP = 32;   // bf16 per staged P row
+
+typedef __bf16 bf16x4l __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4l lds_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4l __attribute__((address_space(3)))*)(p));
+}
+
+__global__ __launch_bounds__(256) void k_lora_mfma(const float* __restrict__ P, const __bf16* __restrict__ Q,
+                                                   int64_t M, int64_t J, int r, int64_t chunk,
+                                                   float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][32 * LQP];
+  __shared__ __attribute__((aligned(16))) __bf16 pls[2][3][32 * LPP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = lane >> 4, i16 = lane & 15, kg = G >> 1, hs = G & 1;
+  const int64_t j0 = (int64_t)blockIdx.x * 256;
+  const int64_t c = blockIdx.y;
+  const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
+  const bool vecq = (J % 8) == 0;
+  // staging roles: Q row 8 u + tid / 32 (u = 0..3), 16-byte chunk tid % 32;
+  // P row tid / 8, ranks 4 (tid % 8) .. + 3
+  const int qrow = tid >> 5, qch = tid & 31, prow = tid >> 3, prho = 4 * (tid & 7);
+  uint4 qv[4];
+  float pv[4];
+  auto load = [&](int64_t m) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t mm = m + 8 * u + qrow;
+      const int64_t j = j0 + 8 * qch;
+      if (mm < me && vecq && j + 8 <= J) {
+        qv[u] = *reinterpret_cast<const uint4*>(Q + mm * J + j);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h[e] = (mm < me && j + e < J) ? __builtin_bit_cast(uint16_t, Q[mm * J + j + e]) : (uint16_t)0;
+        qv[u] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16),
+                           h[6] | ((uint32_t)h[7] << 16));
+      }
+    }
+    const int64_t mm = m + prow;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = (mm < me && prho + e < r) ? P[mm * r + prho + e] : 0.0f;
+  };
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  int buf = 0;
+  if (mb < me) load(mb);
+  for (int64_t m = mb; m < me; m += 32, buf ^= 1) {
+    // stage this step
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&qs[buf][(8 * u + qrow) * LQP + 8 * qch]) = qv[u];
+    {
+      uint16_t h[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = pv[e];
+        const __bf16 a1 = (__bf16)v;
+        const float r1 = v - (float)a1;
+        const __bf16 a2 = (__bf16)r1;
+        const __bf16 a3 = (__bf16)(r1 - (float)a2);
+        h[0][e] = __builtin_bit_cast(uint16_t, a1);
+        h[1][e] = __builtin_bit_cast(uint16_t, a2);
+        h[2][e] = __builtin_bit_cast(uint16_t, a3);
+      }
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+        *reinterpret_cast<uint2*>(&pls[buf][pp][prow * LPP + prho]) =
+            make_uint2(h[pp][0] | ((uint32_t)h[pp][1] << 16), h[pp][2] | ((uint32_t)h[pp][3] << 16));
+    }
+    __syncthreads();
+    if (m + 32 < me) load(m + 32);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 a[3], b[2];
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) {
+        bf16x4l v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[h] = lds_tr16(&pls[buf][pp][(16 * s2 + 8 * kg + 4 * h + (i16 >> 2)) * LPP + 16 * hs + 4 * (i16 & 3)]);
+        a[pp] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x4l v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[h] = lds_tr16(&qs[buf][(16 * s2 + 8 * kg + 4 * h + (i16 >> 2)) * LQP + 64 * wave + 32 * t + 16 * hs +
+                                   4 * (i16 & 3)]);
+        b[t] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[t], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[t], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[t], acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // element e of accumulator t: rank 8 (e / 4) + 4 (lane / 32) + e % 4, column 64 wave + 32 t + lane % 32
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t j = j0 + 64 * wave + 32 * t + (lane & 31);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rho = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (rho < r && j < J) partial[(c * r + rho) * J + j] = acc[t][e];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_lora_combine(const float* __restrict__ partial, int64_t chunks, int r,
                                                       int64_t J, float s, bool transpose_out,
                                                       float* __restrict__ out) {
@@ -495,6 +620,15 @@ void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, floa
                float* out, hipStream_t st) {
   const int64_t chunk = lora_chunk(M, J), chunks = ceil_div(M, chunk);
   const dim3 grid((unsigned)ceil_div(J, LCOLS), (unsigned)chunks);
+  if constexpr (sizeof(T) == 2) {
+    if (r <= 32) {
+      hipLaunchKernelGGL(k_lora_mfma, dim3((unsigned)ceil_div(J, 256), (unsigned)chunks), dim3(256), 0, st, P, Q, M, J,
+                         r, chunk, part);
+      hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, part, chunks,
+                         r, J, s, transpose_out, out);
+      return;
+    }
+  }
   if (J % 2 == 0 && J >= 2)
     hipLaunchKernelGGL((k_lora_partial<T, true>), grid, dim3(256), 0, st, P, Q, M, J, r, chunk, part);
   else
