@@ -3,10 +3,15 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
 and by the benchmark's ``cpu_baseline`` leg, never by the GPU product path.
 
-The arithmetic lives in ``nf4_oracle.c`` (plain C, fp64 accumulation, no FMA
-contraction); this module builds it with gcc, loads it with ctypes and converts
-numpy arrays in and out. See the C file's header for the passages each function
-follows and for the readings taken where the pages are silent.
+The storage and linear-layer arithmetic lives in ``nf4_oracle.c`` (plain C,
+fp64 accumulation, no FMA contraction); this module builds it with gcc, loads
+it with ctypes and converts numpy arrays in and out. See the C file's header
+for the passages each function follows and for the readings taken where the
+pages are silent.
+
+The optimizer step after the LoRA gradients (the LoRA-FA preconditioner and
+AdamW) is written here in numpy fp64, in the order of its definition; see the
+section "LoRA-FA preconditioning and AdamW" below.
 """
 from __future__ import annotations
 
@@ -233,3 +238,97 @@ def lora_scale(alpha: float, r: int, rslora: bool = False) -> np.float32:
     """Resolved adapter scale s = alpha / r (LoRA) or alpha / sqrt(r) (rsLoRA),
     formed in fp64 and rounded once to fp32."""
     return np.float32(alpha / (np.sqrt(r) if rslora else r))
+
+
+# --------------------------------------------------------------------------- LoRA-FA preconditioning and AdamW
+#
+# Aner docs "Native model adaptation and NF4", section "LoRA FA includes
+# gradient preconditioning": A is frozen (no gradient, no moments) and the
+# gradient of B is replaced, before the Adam moments see it, by
+#     s^-2 g_B pinv(A A^T + 1e-8 I),   s = alpha / rank,
+# where the r x r matrix pinv(...) is computed once and stored with the adapter
+# (the qualification record "native_training_accelerated" lists 277,440 frozen
+# adapter bytes for 60 rank-2 targets of width 576: A plus a 2 x 2 fp32 matrix
+# per target).
+#
+# The optimizer is AdamW with FP32 masters and moments (same page, sections
+# "Explicit accelerated training profiles", "Mixed precision keeps stable state
+# in FP32" and "Paged AdamW uses real CUDA managed memory"; the paged variant
+# runs the same AdamW equations). The pages do not print those equations; they
+# are taken from the published AdamW definition (Loshchilov and Hutter,
+# decoupled weight decay) in the form the LibTorch optimizer uses (READING):
+# the decay multiplies the parameter by (1 - lr * wd), the moments are
+# bias-corrected by 1 - beta^t, and eps is added to the root of the corrected
+# second moment.
+#
+# Everything below is fp64. Inputs given as fp32 arrays are widened exactly;
+# scalar hyperparameters are taken at their fp32 values, since that is the
+# precision in which a caller hands them over.
+
+LORAFA_DAMPING = 1e-8
+
+
+def _f32val(x) -> float:
+    return float(np.float32(x))
+
+
+def lorafa_preconditioner(A: np.ndarray) -> np.ndarray:
+    """P = pinv(A A^T + 1e-8 I) in fp64 for a frozen A [r, K] (fp32 values).
+
+    A A^T + 1e-8 I is symmetric positive definite, so its Moore-Penrose inverse
+    is its inverse; the pseudo-inverse is taken with no singular-value cutoff
+    (READING: the damping term already makes the matrix nonsingular, and a
+    relative cutoff would silently drop the damped directions)."""
+    A64 = np.asarray(A, np.float32).astype(np.float64)
+    r = A64.shape[0]
+    G = A64 @ A64.T + LORAFA_DAMPING * np.eye(r)
+    return np.linalg.pinv(G, rcond=0.0)
+
+
+def lorafa_precondition(dB: np.ndarray, P: np.ndarray, s: float) -> np.ndarray:
+    """s^-2 dB P in fp64: dB [N, r] is the gradient of B, P [r, r] the stored
+    preconditioner, s the resolved adapter scale (its fp32 value)."""
+    s64 = _f32val(s)
+    return (np.asarray(dB, np.float64) @ np.asarray(P, np.float64)) / (s64 * s64)
+
+
+def adamw_step(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, *, lr: float, beta1: float,
+               beta2: float, eps: float, weight_decay: float, step: int, grad_scale: float = 1.0):
+    """One AdamW update of parameters p with gradient g and moments m, v (all
+    widened to fp64). `step` is the 1-based index t of this update. The
+    gradient is first multiplied by grad_scale (a clipping or unscaling
+    factor). Returns the new (p, m, v) in fp64."""
+    t = int(step)
+    if t < 1:
+        raise ValueError("step must be >= 1")
+    lr, b1, b2 = _f32val(lr), _f32val(beta1), _f32val(beta2)
+    eps, wd, gs = _f32val(eps), _f32val(weight_decay), _f32val(grad_scale)
+    g = np.asarray(g, np.float64) * gs
+    p = np.asarray(p, np.float64) * (1.0 - lr * wd)       # decoupled weight decay
+    m = b1 * np.asarray(m, np.float64) + (1.0 - b1) * g    # first moment
+    v = b2 * np.asarray(v, np.float64) + (1.0 - b2) * g * g  # second moment
+    m_hat = m / (1.0 - b1 ** t)
+    v_hat = v / (1.0 - b2 ** t)
+    p = p - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return p, m, v
+
+
+def lora_adamw_step(B, dB, mB, vB, *, A=None, dA=None, mA=None, vA=None, P=None, s=None, lr, beta1, beta2, eps,
+                    weight_decay, step, grad_scale=1.0) -> dict:
+    """The optimizer step of one adapter. LoRA: A and B each take an AdamW
+    update with their own gradients. LoRA-FA (A is None): only B is updated,
+    and with P given its gradient is first replaced by s^-2 (grad_scale dB) P.
+    Returns {"B", "mB", "vB"} (and {"A", "mA", "vA"} for LoRA) in fp64."""
+    hp = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, step=step)
+    out = {}
+    if A is not None:
+        if P is not None:
+            raise ValueError("the LoRA-FA preconditioner applies only with A frozen")
+        out["A"], out["mA"], out["vA"] = adamw_step(A, dA, mA, vA, grad_scale=grad_scale, **hp)
+    gB = np.asarray(dB, np.float64)
+    gs = grad_scale
+    if P is not None:
+        gB = lorafa_precondition(gB * _f32val(grad_scale), P, s)
+        gs = 1.0
+    out["B"], out["mB"], out["vB"] = adamw_step(B, gB, mB, vB, grad_scale=gs, **hp)
+    return out

@@ -19,8 +19,9 @@ from typing import Dict, List, Sequence, Tuple
 import numpy as np
 import torch
 
-# Seeds: weight matrix i uses 1000 + i; activations 1; A 2; B 3; dY 4; outlier mask 5.
-SEED_X, SEED_A, SEED_B, SEED_DY, SEED_OUTLIER = 1, 2, 3, 4, 5
+# Seeds: weight matrix i uses 1000 + i; activations 1; A 2; B 3; dY 4; outlier mask 5;
+# optimizer state (gradient, first and second moment) 6.
+SEED_X, SEED_A, SEED_B, SEED_DY, SEED_OUTLIER, SEED_OPT = 1, 2, 3, 4, 5, 6
 
 
 def weight_seed(i: int) -> int:
@@ -126,3 +127,14 @@ def lora_inputs(layer: Linear, tokens: int, seed_offset: int = 0, device: str = 
         out["A"] = normal_f32((r, layer.k_in), 1.0 / r, SEED_A + 10 * seed_offset, device)
         out["B"] = normal_f32((layer.n_out, r), 0.01, SEED_B + 10 * seed_offset, device)
     return out
+
+
+def adamw_state(shape: Sequence[int], seed_offset: int = 0, std: float = 1e-3, device: str = "cpu") -> dict:
+    """Seeded fp32 optimizer inputs of one tensor: a gradient g ~ N(0, std), a
+    first moment m ~ N(0, std) and a second moment v = (N(0, std))^2 >= 0, as
+    left by earlier updates."""
+    base = SEED_OPT + 10 * seed_offset
+    g = normal_f32(shape, std, base * 3 + 0, device)
+    m = normal_f32(shape, std, base * 3 + 1, device)
+    v = normal_f32(shape, std, base * 3 + 2, device) ** 2
+    return dict(g=g, m=m, v=v)
