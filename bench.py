@@ -7,8 +7,12 @@ LoRA r = 16, alpha = 32 on all 7 projections), per projection:
   nf4_linear_fwd (fused dequant-GEMM + LoRA side path)
   nf4_linear_bwd_input (fused dequant-GEMM through the frozen base + LoRA)
   lora_grad (dA, dB)
+  lora_adamw_step (fused AdamW update of A and B, fp32 masters and moments)
   nf4_dequantize (packed -> bf16)
 with every input already resident in device memory. Prints one JSON line.
+Outside the timed step it also times the LoRA-FA variant of the optimizer
+step (lorafa_preconditioner once per adapter, then the preconditioned update of
+B) on the rank-64 down_proj shape.
 
 value = algorithmic FLOPs of the step (4MNK + 6Mr(N+K) per projection) /
 step time: whole-step throughput including the quantize and dequantize work.
@@ -27,6 +31,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+ADAMW = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)  # adapter learning rate of the pages
+ADAMW_BYTES = 28  # per parameter: p, g, m, v read (16 B) and p, m, v written (12 B), fp32
 
 
 def parse():
@@ -126,8 +132,9 @@ def packed_bytes(n, nl):
 
 def cpu_baseline(layers, M, r, s, rows):
     """The oracle on the host cores over a bounded sample of the same step:
-    quantize + dequantize of all 7 weights, and forward, input gradient and
-    LoRA gradients for the first `rows` token rows of every projection."""
+    quantize + dequantize of all 7 weights, forward, input gradient and LoRA
+    gradients for the first `rows` token rows of every projection, and the
+    AdamW update of every adapter."""
     import numpy as np
     import oracle
     import workloads
@@ -145,14 +152,57 @@ def cpu_baseline(layers, M, r, s, rows):
         Wd = oracle.bf16_bits_to_f32(oracle.dequantize(q, "bf16")).reshape(W.shape)
         y, T = oracle.linear_fwd(x, Wd, A, B, s)
         dx, U = oracle.linear_bwd_input(dy, Wd, A, B, s)
-        oracle.lora_grad(x, dy, T, U, s)
+        dA, dB = oracle.lora_grad(x, dy, T, U, s)
+        oracle.lora_adamw_step(B, dB, np.zeros_like(B), np.zeros_like(B), A=A, dA=dA, mA=np.zeros_like(A),
+                               vA=np.zeros_like(A), step=1, **ADAMW)
         t_total += time.perf_counter() - t0
         b, l = layer_flops(rows, L.n_out, L.k_in, r)
         flops += b + l
     return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=f"all 7 weights quantized + dequantized, fwd/bwd-input/LoRA grads on {rows} of {M} "
-                       f"token rows per projection; {flops / 1e9:.1f} GFLOP in {t_total:.1f} s (fp64 accumulation)",
+                       f"token rows per projection, AdamW on all 7 adapters; {flops / 1e9:.1f} GFLOP in {t_total:.1f} s (fp64 accumulation)",
                 seconds=round(t_total, 2))
+
+
+def lorafa_measure(nl, dev, reps: int = 20):
+    """LoRA-FA optimizer step on the rank-64 down_proj adapter (A [64, 14336]
+    frozen, B [4096, 64]): the one-off preconditioner and the preconditioned
+    AdamW update of B, each timed with HIP events on the launch stream."""
+    import torch
+    import workloads
+    wl = workloads.WORKLOADS["down_proj_bwd"]
+    L = wl["layers"][0]
+    r, K, N = L.lora_rank, L.k_in, L.n_out
+    s = nl.lora_scale(wl["alpha"], r, wl["rslora"])
+    inp = workloads.lora_inputs(L, 1, device="cuda")
+    A, B = inp["A"], inp["B"]
+    st = workloads.adamw_state((N, r), 0, device="cuda")
+    Pm = torch.empty((r, r), dtype=torch.float32, device=dev)
+    ws = torch.empty(nl.lorafa_preconditioner_workspace_bytes(r, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    pre_ms = timed(lambda: nl.lorafa_preconditioner(A, out=Pm, workspace=ws))
+    k = [0]
+
+    def upd():
+        k[0] += 1
+        nl.lora_adamw_step(B, st["g"], st["m"], st["v"], step=k[0], precond=Pm, s=s, **ADAMW)
+    upd_ms = timed(upd)
+    upd_bytes = ADAMW_BYTES * N * r + 4 * r * r
+    return {"shape": f"A [{r}, {K}] frozen, B [{N}, {r}], s = {s}", "preconditioner_us": round(pre_ms * 1e3, 1),
+            "preconditioned_update_us": round(upd_ms * 1e3, 2),
+            "preconditioned_update_gbps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -196,12 +246,19 @@ def main():
             dA=torch.empty((r, L.k_in), dtype=torch.float32, device=dev),
             dB=torch.empty((L.n_out, r), dtype=torch.float32, device=dev),
             gws=torch.empty(nl.lora_grad_workspace_bytes(M, L.k_in, L.n_out, r), dtype=torch.uint8, device=dev),
+            mA=torch.zeros((r, L.k_in), dtype=torch.float32, device=dev),
+            vA=torch.zeros((r, L.k_in), dtype=torch.float32, device=dev),
+            mB=torch.zeros((L.n_out, r), dtype=torch.float32, device=dev),
+            vB=torch.zeros((L.n_out, r), dtype=torch.float32, device=dev),
             Wd=torch.empty(W.shape, dtype=torch.bfloat16, device=dev),
         ))
     stream = torch.cuda.current_stream(dev)
-    kinds = ["quantize", "fwd", "bwd", "grad", "dequant"]
+    kinds = ["quantize", "fwd", "bwd", "grad", "adamw", "dequant"]
+    opt_step = [0]
 
     def step(events=None):
+        opt_step[0] += 1
+        t = opt_step[0]
         def mark(kind, i, fn):
             if events is None:
                 fn()
@@ -223,6 +280,9 @@ def main():
         for i, p in enumerate(P):
             mark("grad", i, lambda p=p: nl.lora_grad(p["x"], p["dy"], p["T"], p["U"], s, dA=p["dA"], dB=p["dB"],
                                                      workspace=p["gws"]))
+        for i, p in enumerate(P):
+            mark("adamw", i, lambda p=p: nl.lora_adamw_step(p["B"], p["dB"], p["mB"], p["vB"], step=t, A=p["A"],
+                                                            dA=p["dA"], mA=p["mA"], vA=p["vA"], **ADAMW))
         for i, p in enumerate(P):
             mark("dequant", i, lambda p=p: nl.dequantize(p["Wq"], torch.bfloat16, out=p["Wd"]))
 
@@ -251,7 +311,7 @@ def main():
 
     flops_base = flops_lora = 0
     fwd_flops = fwd_ms = bwd_flops = bwd_ms = 0.0
-    dq_bytes = dq_ms = q_bytes = q_ms = 0.0
+    dq_bytes = dq_ms = q_bytes = q_ms = ad_bytes = ad_ms = 0.0
     for i, p in enumerate(P):
         L = p["L"]
         b, l = layer_flops(M, L.n_out, L.k_in, r)
@@ -267,6 +327,8 @@ def main():
         dq_ms += per["dequant"][i]
         q_bytes += 4 * n + pb
         q_ms += per["quantize"][i]
+        ad_bytes += ADAMW_BYTES * r * (L.k_in + L.n_out)
+        ad_ms += per["adamw"][i]
     total_flops = flops_base + flops_lora
     fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
@@ -274,6 +336,8 @@ def main():
     dom_tf = fwd_tf if fwd_ms >= bwd_ms else bwd_tf
     dq_gbps = dq_bytes / (dq_ms * 1e-3) / 1e9
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
+    ad_gbps = ad_bytes / (ad_ms * 1e-3) / 1e9
+    fa = lorafa_measure(nl, dev)
 
     ceil = None if args.no_ceilings else ceilings()
     cpu = None
@@ -296,7 +360,8 @@ def main():
         "config": {"workload": "llama8b_layer", "tokens": M, "hidden": 4096, "kv_dim": 1024,
                    "intermediate": 14336, "projections": 7, "lora_rank": r, "lora_alpha": wl["alpha"],
                    "double_quant": True, "block": 64, "nested_block": 256,
-                   "step": "quantize + fused fwd + fused bwd-input + lora_grad + dequantize, all 7 projections"},
+                   "step": "quantize + fused fwd + fused bwd-input + lora_grad + AdamW(A, B) + dequantize, "
+                           "all 7 projections"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic(dominant)},
@@ -307,8 +372,14 @@ def main():
                     "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
                     "grad_ms": round(sum(per["grad"]), 3), "quantize_ms": round(q_ms, 3),
                     "quantize_gbps": round(q_gbps, 1), "dequant_ms": round(dq_ms, 3),
-                    "dequant_gbps": round(dq_gbps, 1),
+                    "dequant_gbps": round(dq_gbps, 1), "adamw_ms": round(ad_ms, 4),
+                    "adamw_gbps": round(ad_gbps, 1),
                     "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds}},
+        "roofline_adamw": {"kernel": "lora_adamw_step (A and B, 7 adapters)", "bound": "hbm",
+                           "achieved": round(ad_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(ad_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                           "note": "28 B per parameter; 0.13-0.46 M parameters per launch, so launch-latency bound"},
+        "lorafa": fa,
         "ceilings": ceil,
         "cpu_baseline": cpu,
     }

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 1
+#define NF4LORA_ABI_VERSION 2
 
 enum nf4_status {
   NF4_OK = 0,
@@ -166,6 +166,55 @@ int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t
 /* Workspace bytes lora_grad needs for these sizes (fa != 0: LoRA-FA). Returns
  * a negative NF4_E* code for invalid sizes. Host-only. */
 int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
+
+/* Hyperparameters of one AdamW update (host struct, read during the call).
+ * The update is the decoupled-decay form with bias-corrected moments:
+ *   p <- p (1 - lr wd); m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+ *   p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * The bias corrections and 1 - lr wd are formed in fp64 on the host and
+ * rounded once to fp32; the per-entry arithmetic is fp32. */
+typedef struct nf4_adamw {
+  float lr;           /* learning rate, finite, >= 0 */
+  float beta1;        /* first-moment decay, in [0, 1) */
+  float beta2;        /* second-moment decay, in [0, 1) */
+  float eps;          /* added to the root of the corrected second moment, finite, > 0 */
+  float weight_decay; /* decoupled decay coefficient, finite, >= 0 */
+  int64_t step;       /* 1-based index t of this update */
+} nf4_adamw;
+
+/* Workspace bytes lorafa_preconditioner needs for A [r,K] (r in [1, 256],
+ * K >= 1); a negative NF4_E* code for invalid sizes. Host-only. */
+int64_t lorafa_preconditioner_workspace_bytes(int32_t r, int64_t K);
+
+/* LoRA-FA preconditioner (Aner docs "Native model adaptation and NF4", section
+ * "LoRA FA includes gradient preconditioning"): with A frozen, the gradient of
+ * B is multiplied by s^-2 pinv(A A^T + 1e-8 I) before the Adam moments, and
+ * that r x r matrix is computed once and stored with the adapter. This call
+ * computes P = (A A^T + 1e-8 I)^-1 (the damped Gram matrix is positive
+ * definite, so its pseudo-inverse is its inverse; no singular value is cut):
+ * A [r,K] fp32, P [r,r] fp32 (written), the Gram matrix accumulated and
+ * inverted in fp64. `workspace` (256-byte aligned) must hold
+ * lorafa_preconditioner_workspace_bytes(r, K) bytes. Deterministic. */
+int lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* workspace, size_t workspace_bytes,
+                          nf4_stream_t stream);
+
+/* One fused AdamW update of a LoRA adapter, in place (same page, sections
+ * "Adapter API", "LoRA FA includes gradient preconditioning" and "Mixed
+ * precision keeps stable state in FP32": FP32 parameters and moments).
+ *  - LoRA: A [r,K], dA, mA, vA and B [N,r], dB, mB, vB all given; both factors
+ *    take an AdamW update with their own gradients.
+ *  - LoRA-FA: A, dA, mA and vA all NULL (A is frozen and has no moments); only
+ *    B is updated. With `precond` (P [r,r] from lorafa_preconditioner) the
+ *    gradient of B is first replaced by s^-2 dB P, s the adapter scale
+ *    (finite, non-zero) used in the forward pass. `precond` requires LoRA-FA.
+ *  - grad_scale: optional device fp32 scalar that multiplies every gradient
+ *    first (a clipping or loss-scale factor); NULL means 1.
+ * Moments must hold zeros before step 1. Every array is a 16-byte aligned
+ * fp32 device array; gradients and P are read only. One kernel launch; entries
+ * are independent, so the result does not depend on the launch shape. */
+int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float* A, const float* dA, float* mA,
+                    float* vA, float* B, const float* dB, float* mB, float* vB, const float* precond, float s,
+                    const float* grad_scale, nf4_stream_t stream);
 
 /* Static text for a status code. */
 const char* nf4_status_string(int status);

@@ -177,4 +177,42 @@ int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t
   return launch_lora_grad(x, dy, dtype, M, K, N, t, fa ? nullptr : u, r, s, dA, dB, workspace, as_stream(stream));
 }
 
+int64_t lorafa_preconditioner_workspace_bytes(int32_t r, int64_t K) {
+  if (r < 1 || r > 256 || K < 1 || K > (INT64_MAX >> 8)) return NF4_EINVAL;
+  return (int64_t)lorafa_ws_bytes(r, K);
+}
+
+int lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* workspace, size_t workspace_bytes,
+                          nf4_stream_t stream) {
+  if (!A || !P || r < 1 || r > 256 || K < 1 || K > (INT64_MAX >> 8)) return NF4_EINVAL;
+  if (!aligned(A, 4) || !aligned(P, 4)) return NF4_EALIGN;
+  const size_t need = lorafa_ws_bytes(r, K);
+  if (!workspace || workspace_bytes < need) return NF4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_lorafa_preconditioner(A, r, K, P, workspace, as_stream(stream));
+}
+
+int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float* A, const float* dA, float* mA,
+                    float* vA, float* B, const float* dB, float* mB, float* vB, const float* precond, float s,
+                    const float* grad_scale, nf4_stream_t stream) {
+  constexpr int64_t kMaxEntries = int64_t(1) << 40;
+  if (!opt || r < 1 || r > 256 || K < 1 || N < 1) return NF4_EINVAL;
+  if (K > kMaxEntries / r || N > kMaxEntries / r) return NF4_EINVAL;
+  const float lr = opt->lr, b1 = opt->beta1, b2 = opt->beta2, eps = opt->eps, wd = opt->weight_decay;
+  if (!std::isfinite(lr) || lr < 0.0f || !(b1 >= 0.0f && b1 < 1.0f) || !(b2 >= 0.0f && b2 < 1.0f)) return NF4_EINVAL;
+  if (!std::isfinite(eps) || !(eps > 0.0f) || !std::isfinite(wd) || wd < 0.0f || opt->step < 1) return NF4_EINVAL;
+  if (!B || !dB || !mB || !vB) return NF4_EINVAL;
+  const int a_given = (A != nullptr) + (dA != nullptr) + (mA != nullptr) + (vA != nullptr);
+  if (a_given != 0 && a_given != 4) return NF4_EINVAL;
+  if (precond && (a_given != 0 || !std::isfinite(s) || s == 0.0f)) return NF4_EINVAL;
+  const void* arrays[] = {A, dA, mA, vA, B, dB, mB, vB, precond};
+  for (const void* p : arrays)
+    if (p && !aligned(p, 16)) return NF4_EALIGN;
+  if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  AdamwLaunch a{*opt, r, K, N, A, dA, mA, vA, B, dB, mB, vB, precond, s, grad_scale};
+  return launch_lora_adamw(a, as_stream(stream));
+}
+
 }  // extern "C"

@@ -54,6 +54,30 @@ size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
                      const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st);
 
+// LoRA-FA preconditioner P = pinv(A A^T + 1e-8 I): fp64 workspace of the
+// K-sliced Gram matrices, then one inversion.
+size_t lorafa_ws_bytes(int32_t r, int64_t K);
+int launch_lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* ws, hipStream_t st);
+
+// One AdamW update of an adapter (A-side pointers all null under LoRA-FA).
+struct AdamwLaunch {
+  nf4_adamw opt;
+  int32_t r;
+  int64_t K, N;
+  float* A;
+  const float* dA;
+  float* mA;
+  float* vA;
+  float* B;
+  const float* dB;
+  float* mB;
+  float* vB;
+  const float* precond;  // r x r or null
+  float s;
+  const float* grad_scale;  // device scalar or null
+};
+int launch_lora_adamw(const AdamwLaunch& a, hipStream_t st);
+
 inline int launch_status() { return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EDEVICE; }
 
 // Compute units of the current device (256 on MI355X).

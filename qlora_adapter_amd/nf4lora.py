@@ -23,8 +23,8 @@ NF4_F32, NF4_BF16 = 0, 1
 _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_linear_fwd",
-           "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "nf4_status_string",
-           "nf4lora_abi_version"]
+           "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
+           "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "nf4_status_string", "nf4lora_abi_version"]
 
 
 class NF4Error(RuntimeError):
@@ -43,6 +43,11 @@ class _Sizes(ctypes.Structure):
 class _Tensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("nested", ctypes.c_void_p),
                 ("offset", ctypes.c_void_p), ("n", ctypes.c_int64), ("double_quant", ctypes.c_int32)]
+
+
+class _Adamw(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
 _lib = None
@@ -70,11 +75,16 @@ def load() -> ctypes.CDLL:
             lib.lora_grad.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, P, I32, F, P, P, P, ctypes.c_size_t, P]
             lib.lora_grad_workspace_bytes.restype = I64
             lib.lora_grad_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int]
+            lib.lorafa_preconditioner_workspace_bytes.restype = I64
+            lib.lorafa_preconditioner_workspace_bytes.argtypes = [I32, I64]
+            lib.lorafa_preconditioner.argtypes = [P, I32, I64, P, P, ctypes.c_size_t, P]
+            lib.lora_adamw_step.argtypes = [ctypes.POINTER(_Adamw), I32, I64, I64, P, P, P, P, P, P, P, P, P, F, P, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
             lib.nf4_status_string.argtypes = [ctypes.c_int]
             for fn in EXPORTS:
                 getattr(lib, fn).restype = getattr(lib, fn).restype or ctypes.c_int
             lib.lora_grad_workspace_bytes.restype = I64
+            lib.lorafa_preconditioner_workspace_bytes.restype = I64
             lib.nf4_status_string.restype = ctypes.c_char_p
             _lib = lib
     return _lib
@@ -266,3 +276,59 @@ def lora_grad(x: Optional[torch.Tensor], dy: torch.Tensor, T: torch.Tensor, U: O
                                          r, float(s), _ptr(None if fa else dA), _ptr(dB), _ptr(workspace), need,
                                          _stream(dy.device)))
     return (None if fa else dA), dB
+
+
+# --------------------------------------------------------------------------- optimizer step
+
+def lorafa_preconditioner_workspace_bytes(r: int, K: int) -> int:
+    v = int(load().lorafa_preconditioner_workspace_bytes(int(r), int(K)))
+    if v < 0:
+        _check("lorafa_preconditioner_workspace_bytes", v)
+    return v
+
+
+def lorafa_preconditioner(A: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """P = pinv(A A^T + 1e-8 I) ([r, r] fp32) for a frozen LoRA-FA factor A [r, K]."""
+    _dev(A, "A", torch.float32)
+    r, K = A.shape
+    if out is None:
+        out = torch.empty((r, r), dtype=torch.float32, device=A.device)
+    _dev(out, "out", torch.float32)
+    need = lorafa_preconditioner_workspace_bytes(r, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    _check("lorafa_preconditioner", load().lorafa_preconditioner(_ptr(A), r, K, _ptr(out), _ptr(workspace), need,
+                                                                 _stream(A.device)))
+    return out
+
+
+def lora_adamw_step(B: torch.Tensor, dB: torch.Tensor, mB: torch.Tensor, vB: torch.Tensor, *, step: int,
+                    lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                    weight_decay: float = 0.01, A: Optional[torch.Tensor] = None, dA: Optional[torch.Tensor] = None,
+                    mA: Optional[torch.Tensor] = None, vA: Optional[torch.Tensor] = None,
+                    precond: Optional[torch.Tensor] = None, s: float = 0.0,
+                    grad_scale: Optional[torch.Tensor] = None) -> None:
+    """One in-place AdamW update of an adapter: A and B (LoRA) or B alone
+    (LoRA-FA: A, dA, mA, vA None), with B's gradient replaced by s^-2 dB P when
+    `precond` P is given. `grad_scale` is an optional one-element fp32 device
+    tensor that multiplies every gradient first."""
+    for name, t in (("B", B), ("dB", dB), ("mB", mB), ("vB", vB)):
+        _dev(t, name, torch.float32)
+    N, r = B.shape
+    K = 1
+    if A is not None:
+        for name, t in (("A", A), ("dA", dA), ("mA", mA), ("vA", vA)):
+            if t is None:
+                raise ValueError(f"{name} is required when A is trained")
+            _dev(t, name, torch.float32)
+        K = A.shape[1]
+    if precond is not None:
+        _dev(precond, "precond", torch.float32)
+    if grad_scale is not None:
+        _dev(grad_scale, "grad_scale", torch.float32)
+    opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    _check("lora_adamw_step", load().lora_adamw_step(ctypes.byref(opt), r, K, N, _ptr(A), _ptr(dA), _ptr(mA),
+                                                     _ptr(vA), _ptr(B), _ptr(dB), _ptr(mB), _ptr(vB),
+                                                     _ptr(precond), float(s), _ptr(grad_scale),
+                                                     _stream(B.device)))

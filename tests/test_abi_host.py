@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 1
+    assert lib[0].nf4lora_abi_version() == 2
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -110,3 +110,44 @@ def test_argument_errors_before_device(lib):
     assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 4, 1.0, 16, 16, None, 0, None) == EWS
     assert L.lora_grad_workspace_bytes(8, 64, 32, 0, 0) == EINVAL
     assert L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 0) > L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 1)
+
+
+def test_optimizer_argument_errors_before_device(lib):
+    """The LoRA-FA preconditioner and the AdamW step reject bad arguments on the
+    host (fake, 16-byte aligned addresses are never dereferenced)."""
+    L, m = lib
+    EINVAL, EALIGN, EWS = -1, -2, -6
+    assert L.lorafa_preconditioner_workspace_bytes(0, 64) == EINVAL
+    assert L.lorafa_preconditioner_workspace_bytes(257, 64) == EINVAL
+    assert L.lorafa_preconditioner_workspace_bytes(16, 0) == EINVAL
+    ws = L.lorafa_preconditioner_workspace_bytes(16, 4096)
+    assert ws >= 16 * 16 * 8
+    assert L.lorafa_preconditioner(None, 16, 4096, 256, 256, ws, None) == EINVAL
+    assert L.lorafa_preconditioner(256, 16, 4096, None, 256, ws, None) == EINVAL
+    assert L.lorafa_preconditioner(258, 16, 4096, 256, 256, ws, None) == EALIGN
+    assert L.lorafa_preconditioner(256, 16, 4096, 256, None, 0, None) == EWS
+    assert L.lorafa_preconditioner(256, 16, 4096, 256, 256, ws - 8, None) == EWS
+    assert L.lorafa_preconditioner(256, 16, 4096, 256, 272, ws, None) == EALIGN
+
+    def step(opt, r=16, K=64, N=32, A=(256, 256, 256, 256), Bp=(256, 256, 256, 256), P=None, s=2.0, gs=None):
+        return L.lora_adamw_step(ctypes.byref(opt) if opt is not None else None, r, K, N, *A, *Bp, P, s, gs, None)
+
+    good = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+    opt = m._Adamw(**good)
+    assert step(None) == EINVAL
+    assert step(opt, r=0) == EINVAL and step(opt, r=257) == EINVAL
+    assert step(opt, K=0) == EINVAL and step(opt, N=0) == EINVAL
+    for key, bad in [("lr", -1.0), ("lr", float("inf")), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0),
+                     ("eps", float("nan")), ("weight_decay", -0.5), ("step", 0)]:
+        assert step(m._Adamw(**{**good, key: bad})) == EINVAL, key
+    # A-side pointers all or none; B side required
+    assert step(opt, A=(256, None, 256, 256)) == EINVAL
+    assert step(opt, Bp=(256, 256, None, 256)) == EINVAL
+    # the preconditioner needs LoRA-FA and a finite non-zero scale
+    assert step(opt, P=256) == EINVAL
+    assert step(opt, A=(None,) * 4, P=256, s=0.0) == EINVAL
+    assert step(opt, A=(None,) * 4, P=256, s=float("inf")) == EINVAL
+    # 16-byte alignment of every array
+    assert step(opt, Bp=(256, 260, 256, 256)) == EALIGN
+    assert step(opt, A=(None,) * 4, P=264) == EALIGN
+    assert step(opt, gs=258) == EALIGN

@@ -1,0 +1,150 @@
+"""GPU parity of the adapter's optimizer step: lorafa_preconditioner and
+lora_adamw_step through the C ABI against the fp64 oracle on the same seeded
+fp32 inputs. Bounds: see tests/parity.py (derived from the fp32 rounding of
+each operation; the preconditioner from its conditioning)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import U32, U64, adamw_bounds, assert_within
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)  # the pages' adapter learning rate
+
+
+def _np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def _check_precond(P_gpu: np.ndarray, A: np.ndarray, what: str) -> float:
+    P = oracle.lorafa_preconditioner(A)
+    r, K = A.shape
+    A64 = A.astype(np.float64)
+    ev = np.linalg.eigvalsh(A64 @ A64.T + 1e-8 * np.eye(r))
+    kappa = ev.max() / ev.min()
+    bound = 1.01 * U32 * 2 * np.abs(P) + 4.0 * (K + r) * r * kappa * U64 * np.abs(P).max()
+    return assert_within(P_gpu, P, bound, what)
+
+
+@pytest.mark.parametrize("r,K", [(1, 576), (2, 576), (5, 333), (16, 4096), (16, 14336), (64, 14336), (100, 1000),
+                                 (128, 4096), (200, 4096), (256, 1024)])
+def test_preconditioner_matches_oracle(gpu, r, K):
+    print(f"[precond] r={r} K={K}", flush=True)
+    A = workloads.normal_f32((r, K), 1.0 / r, workloads.SEED_A + r, "cuda")
+    P = gpu.lorafa_preconditioner(A)
+    P2 = gpu.lorafa_preconditioner(A)
+    torch.cuda.synchronize()
+    _check_precond(_np(P), _np(A), f"P r={r} K={K}")
+    assert torch.equal(P, P2), "preconditioner not run-to-run identical"
+
+
+def test_preconditioner_degenerate_adapters(gpu):
+    """A = 0 (pure damping, P = 1e8 I) and duplicated rows (singular Gram
+    matrix made invertible only by the damping)."""
+    Z = torch.zeros((4, 300), dtype=torch.float32, device="cuda")
+    Pz = _np(gpu.lorafa_preconditioner(Z))
+    np.testing.assert_array_equal(Pz, np.eye(4, dtype=np.float32) * np.float32(1e8))
+    row = workloads.normal_f32((1, 640), 0.05, 91, "cuda")
+    A = torch.cat([row, row, workloads.normal_f32((6, 640), 0.05, 92, "cuda")])
+    _check_precond(_np(gpu.lorafa_preconditioner(A)), _np(A), "P duplicate rows")
+
+
+def _state(shape, seed, zero_moments: bool):
+    st = workloads.adamw_state(shape, seed, device="cuda")
+    if zero_moments:
+        st["m"].zero_()
+        st["v"].zero_()
+    st["p"] = workloads.normal_f32(shape, 0.02, 500 + seed, "cuda")
+    return st
+
+
+def _lora_case(gpu, r, K, N, step, gs_value, fa, precond, seed=0):
+    zero = step == 1
+    sA = None if fa else _state((r, K), seed, zero)
+    sB = _state((N, r), seed + 1, zero)
+    host = {k: {n: _np(t) for n, t in st.items()} for k, st in (("A", sA), ("B", sB)) if st is not None}
+    s = 2.0
+    P = None
+    if precond:
+        Af = workloads.normal_f32((r, K), 1.0 / r, workloads.SEED_A, "cuda")
+        P = gpu.lorafa_preconditioner(Af)
+    gs = None if gs_value is None else torch.full((1,), gs_value, dtype=torch.float32, device="cuda")
+    kw = {}
+    if sA is not None:
+        kw = dict(A=sA["p"], dA=sA["g"], mA=sA["m"], vA=sA["v"])
+    gpu.lora_adamw_step(sB["p"], sB["g"], sB["m"], sB["v"], step=step, precond=P, s=s, grad_scale=gs, **HP, **kw)
+    torch.cuda.synchronize()
+    gsv = 1.0 if gs_value is None else gs_value
+    Pn = None if P is None else _np(P)
+    hB = host["B"]
+    ref = oracle.lora_adamw_step(hB["p"], hB["g"], hB["m"], hB["v"], P=Pn, s=s, step=step, grad_scale=gsv,
+                                 **({} if fa else dict(A=host["A"]["p"], dA=host["A"]["g"], mA=host["A"]["m"],
+                                                       vA=host["A"]["v"])), **HP)
+    worst = 0.0
+    if not fa:
+        hA = host["A"]
+        g = hA["g"].astype(np.float64) * gsv
+        b = adamw_bounds(hA["p"], g, hA["m"], hA["v"], U32 * np.abs(g), HP, step)
+        for name, key, bd in zip(("A", "mA", "vA"), ("p", "m", "v"), b):
+            worst = max(worst, assert_within(_np(sA[key]), ref[name], bd, f"{name} r={r} K={K} t={step}"))
+    if P is not None:
+        g = oracle.lorafa_precondition(hB["g"].astype(np.float64) * gsv, Pn, s)
+        e_g = (r + 3) * U32 * (np.abs(hB["g"].astype(np.float64)) * gsv) @ np.abs(Pn.astype(np.float64)) / (s * s)
+    else:
+        g = hB["g"].astype(np.float64) * gsv
+        e_g = U32 * np.abs(g)
+    b = adamw_bounds(hB["p"], g, hB["m"], hB["v"], e_g, HP, step)
+    for name, key, bd in zip(("B", "mB", "vB"), ("p", "m", "v"), b):
+        worst = max(worst, assert_within(_np(sB[key]), ref[name], bd, f"{name} r={r} N={N} t={step}"))
+    return worst
+
+
+@pytest.mark.parametrize("r,K,N", [(16, 4096, 4096), (16, 4096, 14336), (5, 333, 77), (1, 3, 5), (64, 14336, 4096)])
+@pytest.mark.parametrize("step,gs", [(1, None), (7, 0.5), (100000, None)])
+def test_lora_adamw_matches_oracle(gpu, r, K, N, step, gs):
+    print(f"[adamw lora] r={r} K={K} N={N} step={step} gs={gs}", flush=True)
+    _lora_case(gpu, r, K, N, step, gs, fa=False, precond=False)
+
+
+@pytest.mark.parametrize("r,K,N", [(16, 4096, 4096), (2, 576, 576), (6, 100, 37), (64, 14336, 4096),
+                                   (256, 1024, 300), (3, 64, 1)])
+@pytest.mark.parametrize("step,gs", [(1, None), (9, 0.25)])
+def test_lorafa_preconditioned_step_matches_oracle(gpu, r, K, N, step, gs):
+    print(f"[adamw lorafa] r={r} K={K} N={N} step={step} gs={gs}", flush=True)
+    _lora_case(gpu, r, K, N, step, gs, fa=True, precond=True)
+
+
+def test_lorafa_without_preconditioner_updates_b_only(gpu):
+    _lora_case(gpu, 8, 256, 129, 3, None, fa=True, precond=False)
+
+
+def test_chained_steps_follow_the_oracle(gpu):
+    """Three updates in a row on the device; each is checked against the oracle
+    started from the device's previous fp32 state."""
+    r, K, N = 16, 1024, 768
+    sA, sB = _state((r, K), 40, True), _state((N, r), 41, True)
+    for t in range(1, 4):
+        dA = workloads.normal_f32((r, K), 1e-3, 700 + t, "cuda")
+        dB = workloads.normal_f32((N, r), 1e-3, 800 + t, "cuda")
+        before = {n: _np(x) for n, x in (("A", sA["p"]), ("mA", sA["m"]), ("vA", sA["v"]), ("B", sB["p"]),
+                                         ("mB", sB["m"]), ("vB", sB["v"]))}
+        gpu.lora_adamw_step(sB["p"], dB, sB["m"], sB["v"], step=t, A=sA["p"], dA=dA, mA=sA["m"], vA=sA["v"], **HP)
+        torch.cuda.synchronize()
+        ref = oracle.lora_adamw_step(before["B"], _np(dB), before["mB"], before["vB"], A=before["A"], dA=_np(dA),
+                                     mA=before["mA"], vA=before["vA"], step=t, **HP)
+        for side, g, st in (("A", _np(dA), sA), ("B", _np(dB), sB)):
+            g64 = g.astype(np.float64)
+            b = adamw_bounds(before[side], g64, before["m" + side], before["v" + side], U32 * np.abs(g64), HP, t)
+            for key, name, bd in zip(("p", "m", "v"), (side, "m" + side, "v" + side), b):
+                assert_within(_np(st[key]), ref[name], bd, f"{name} t={t}")
+
+
+def test_llama8b_layer_adapters_one_update(gpu):
+    """All seven rank-16 adapters of the Llama-8B-shaped layer, one update each,
+    in the shapes and launch configuration the benchmark times."""
+    for i, L in enumerate(workloads.WORKLOADS["llama8b_layer"]["layers"]):
+        print(f"[adamw llama8b] {L.name}", flush=True)
+        _lora_case(gpu, L.lora_rank, L.k_in, L.n_out, 5, None, fa=False, precond=False, seed=20 + 2 * i)
