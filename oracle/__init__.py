@@ -170,6 +170,28 @@ def dequantize(q: Dict[str, np.ndarray], out: str = "f32") -> np.ndarray:
     return f if out == "f32" else h
 
 
+def embedding_rows(q: Dict[str, np.ndarray], D: int, ids, out: str = "f32") -> np.ndarray:
+    """Decoded rows ids[0..T) of a packed [V, D] embedding table.
+
+    Aner docs "Native model adaptation and NF4", section "Packed NF4 and the
+    portable QLoRA profile" (embeddings decode only the selected rows) and
+    section "Fused GPU NF4 decodes inside the matrix kernel" (the selected-row
+    kernel decodes codes and nested scales on the device): row i of the result
+    is row ids[i] of the decoded table, so this is the full decode followed by
+    a row selection. out='f32' gives fp32 values, out='bf16' uint16 bf16 bits.
+    Raises IndexError for an id outside [0, V)."""
+    D = int(D)
+    n = int(q["n"])
+    if D < 1 or n % D:
+        raise ValueError("table size is not a multiple of the row width")
+    V = n // D
+    ids = np.asarray(ids, dtype=np.int64).ravel()
+    if ids.size and (ids.min() < 0 or ids.max() >= V):
+        raise IndexError("embedding id out of range")
+    table = dequantize(q, out).reshape(V, D)
+    return table[ids]
+
+
 # --------------------------------------------------------------------------- bf16 helpers
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

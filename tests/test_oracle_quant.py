@@ -234,3 +234,44 @@ def test_normalisation_is_true_division(orc):
     x = (w / a).astype(np.float32)
     want = np.argmin(np.abs(x[:, None].astype(np.float64) - c4[None, :]), axis=1)
     np.testing.assert_array_equal(codes, want)
+
+
+# --------------------------------------------------------------------------- selected-row embedding decode
+
+def _exact_table(V: int, D: int, seed: int, double_quant: bool) -> np.ndarray:
+    """A [V, D] fp32 table that NF4 stores exactly: every value is C4[k] * a with
+    one shared a, and every 64-block holds a +-a entry, so each block absmax is
+    a; then every centred absmax is 0 and double quantization is exact too."""
+    rng = np.random.default_rng(seed)
+    a = np.float32(0.03125)
+    import oracle
+    c4 = oracle.nf4_table()
+    codes = rng.integers(0, 16, size=V * D)
+    flat = (c4[codes] * a).astype(np.float32)
+    flat[::64] = np.where(rng.random(flat[::64].size) < 0.5, -a, a)
+    return flat.reshape(V, D)
+
+
+@pytest.mark.parametrize("V,D,dq", [(300, 576, True), (257, 77, True), (40, 64, False), (5, 3, True)])
+def test_embedding_rows_return_the_selected_rows(orc, V, D, dq):
+    """On a table NF4 represents exactly, the decoded rows are the table's rows:
+    ids in any order, repeated, first and last row."""
+    W = _exact_table(V, D, V + D, dq)
+    q = orc.quantize(W, dq)
+    ids = np.array([V - 1, 0, 7 % V, 7 % V, V // 2, 1 % V, V - 1], np.int64)
+    got = orc.embedding_rows(q, D, ids)
+    np.testing.assert_array_equal(got, W[ids])
+    bits = orc.embedding_rows(q, D, ids, out="bf16")
+    assert bits.dtype == np.uint16 and bits.shape == (ids.size, D)
+    want_bits = torch.from_numpy(W[ids]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, want_bits)  # torch's round-to-nearest-even of the exact rows
+
+
+def test_embedding_rows_reject_out_of_range(orc):
+    W = _exact_table(10, 64, 1, True)
+    q = orc.quantize(W, True)
+    with pytest.raises(IndexError):
+        orc.embedding_rows(q, 64, [0, 10])
+    with pytest.raises(IndexError):
+        orc.embedding_rows(q, 64, [-1])
+    assert orc.embedding_rows(q, 64, np.zeros(0, np.int64)).shape == (0, 64)
