@@ -135,6 +135,21 @@ int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* 
  * w_hat = fl32(C4[code] * a'_b), bf16 by round-to-nearest-even. */
 int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream);
 
+/* Selected rows of a packed embedding table (Aner docs "Native model
+ * adaptation and NF4": section "Packed NF4 and the portable QLoRA profile",
+ * embeddings decode only the selected rows; section "Fused GPU NF4 decodes
+ * inside the matrix kernel", the selected-row kernel decodes codes and nested
+ * scales on the device with no decoded copy of the table). E holds a [V, D]
+ * table (E->n == V*D, flattened row-major, so blocks may straddle rows); ids
+ * is a device int64 array of T token ids (8-byte aligned); out [T, D] of
+ * out_dtype receives out[t, :] = decoded row ids[t], bit-identical to those
+ * rows of nf4_dequantize. `status` (optional device int32) is set to 0 and then
+ * to NF4_EINVAL if an id is outside [0, V); that output row is written as
+ * zeros and nothing outside the table is read. T == 0 launches only the
+ * status reset. */
+int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype out_dtype,
+                       void* out, int32_t* status, nf4_stream_t stream);
+
 /* Fused forward: y = x W_hat^T + s (x A^T) B^T, W_hat decoded inside the
  * matrix kernel (no decoded copy of W is written to memory). x [M,K] and y
  * [M,N] are `dtype` (F32: fp32 weights; BF16: weights rounded to bf16 before
@@ -215,6 +230,35 @@ int lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* 
 int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float* A, const float* dA, float* mA,
                     float* vA, float* B, const float* dB, float* mB, float* vB, const float* precond, float s,
                     const float* grad_scale, nf4_stream_t stream);
+
+/* One adapter's tensors for lora_adamw_step_many; each field means what the
+ * argument of the same name means for lora_adamw_step. */
+typedef struct nf4_lora_state {
+  int32_t r;
+  int64_t K;
+  int64_t N;
+  float* A;
+  const float* dA;
+  float* mA;
+  float* vA;
+  float* B;
+  const float* dB;
+  float* mB;
+  float* vB;
+  const float* precond;
+  float s;
+} nf4_lora_state;
+
+#define NF4_MAX_ADAPTERS_PER_CALL 16
+
+/* lora_adamw_step for `count` adapters (1 to NF4_MAX_ADAPTERS_PER_CALL) with
+ * the same hyperparameters and grad_scale, in one kernel launch: the update of
+ * a layer's adapters at the cost of one launch. `adapters` is a host array read
+ * during the call; each entry is validated as lora_adamw_step validates its
+ * arguments, and no tensor may overlap another. Entries are independent, so the
+ * result equals `count` separate lora_adamw_step calls bit for bit. */
+int lora_adamw_step_many(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,
+                         const float* grad_scale, nf4_stream_t stream);
 
 /* Static text for a status code. */
 const char* nf4_status_string(int status);

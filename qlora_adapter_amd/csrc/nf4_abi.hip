@@ -142,6 +142,18 @@ int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stre
   return launch_dequantize(w, out_dtype, out, as_stream(stream));
 }
 
+int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype out_dtype,
+                       void* out, int32_t* status, nf4_stream_t stream) {
+  if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;
+  if (V < 1 || D < 1 || T < 0 || V > INT64_MAX / D) return NF4_EINVAL;
+  if (T > 0 && (T > (int64_t(1) << 40) / D || !ids || !out)) return NF4_EINVAL;
+  if (int rc = check_tensor(E, V * D)) return rc;
+  if (T > 0 && (!aligned(ids, 8) || !aligned(out, 16))) return NF4_EALIGN;
+  if (status && !aligned(status, 4)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_embedding_rows(E, V, D, ids, T, out_dtype, out, status, as_stream(stream));
+}
+
 int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
                    const float* A, const float* B, int32_t r, float s, void* y, float* t_out,
                    nf4_stream_t stream) {
@@ -193,26 +205,57 @@ int lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* 
   return launch_lorafa_preconditioner(A, r, K, P, workspace, as_stream(stream));
 }
 
-int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float* A, const float* dA, float* mA,
-                    float* vA, float* B, const float* dB, float* mB, float* vB, const float* precond, float s,
-                    const float* grad_scale, nf4_stream_t stream) {
-  constexpr int64_t kMaxEntries = int64_t(1) << 40;
-  if (!opt || r < 1 || r > 256 || K < 1 || N < 1) return NF4_EINVAL;
-  if (K > kMaxEntries / r || N > kMaxEntries / r) return NF4_EINVAL;
+}  // extern "C"
+
+namespace {
+
+int check_adamw(const nf4_adamw* opt) {
+  if (!opt) return NF4_EINVAL;
   const float lr = opt->lr, b1 = opt->beta1, b2 = opt->beta2, eps = opt->eps, wd = opt->weight_decay;
   if (!std::isfinite(lr) || lr < 0.0f || !(b1 >= 0.0f && b1 < 1.0f) || !(b2 >= 0.0f && b2 < 1.0f)) return NF4_EINVAL;
   if (!std::isfinite(eps) || !(eps > 0.0f) || !std::isfinite(wd) || wd < 0.0f || opt->step < 1) return NF4_EINVAL;
-  if (!B || !dB || !mB || !vB) return NF4_EINVAL;
-  const int a_given = (A != nullptr) + (dA != nullptr) + (mA != nullptr) + (vA != nullptr);
+  return NF4_OK;
+}
+
+int check_lora_state(const nf4_lora_state& a) {
+  constexpr int64_t kMaxEntries = int64_t(1) << 40;
+  const int32_t r = a.r;
+  if (r < 1 || r > 256 || a.K < 1 || a.N < 1) return NF4_EINVAL;
+  if (a.K > kMaxEntries / r || a.N > kMaxEntries / r) return NF4_EINVAL;
+  if (!a.B || !a.dB || !a.mB || !a.vB) return NF4_EINVAL;
+  const int a_given = (a.A != nullptr) + (a.dA != nullptr) + (a.mA != nullptr) + (a.vA != nullptr);
   if (a_given != 0 && a_given != 4) return NF4_EINVAL;
-  if (precond && (a_given != 0 || !std::isfinite(s) || s == 0.0f)) return NF4_EINVAL;
-  const void* arrays[] = {A, dA, mA, vA, B, dB, mB, vB, precond};
+  if (a.precond && (a_given != 0 || !std::isfinite(a.s) || a.s == 0.0f)) return NF4_EINVAL;
+  const void* arrays[] = {a.A, a.dA, a.mA, a.vA, a.B, a.dB, a.mB, a.vB, a.precond};
   for (const void* p : arrays)
     if (p && !aligned(p, 16)) return NF4_EALIGN;
+  return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float* A, const float* dA, float* mA,
+                    float* vA, float* B, const float* dB, float* mB, float* vB, const float* precond, float s,
+                    const float* grad_scale, nf4_stream_t stream) {
+  if (int rc = check_adamw(opt)) return rc;
+  const nf4_lora_state a{r, K, N, A, dA, mA, vA, B, dB, mB, vB, precond, s};
+  if (int rc = check_lora_state(a)) return rc;
   if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  AdamwLaunch a{*opt, r, K, N, A, dA, mA, vA, B, dB, mB, vB, precond, s, grad_scale};
-  return launch_lora_adamw(a, as_stream(stream));
+  return launch_lora_adamw(*opt, &a, 1, grad_scale, as_stream(stream));
+}
+
+int lora_adamw_step_many(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,
+                         const float* grad_scale, nf4_stream_t stream) {
+  if (int rc = check_adamw(opt)) return rc;
+  if (!adapters || count < 1 || count > NF4_MAX_ADAPTERS_PER_CALL) return NF4_EINVAL;
+  for (int32_t i = 0; i < count; ++i)
+    if (int rc = check_lora_state(adapters[i])) return rc;
+  if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_lora_adamw(*opt, adapters, count, grad_scale, as_stream(stream));
 }
 
 }  // extern "C"

@@ -32,6 +32,8 @@ inline size_t quantize_ws_bytes(int64_t n, int dq) {
 // Launchers (return NF4_OK or NF4_EDEVICE). Arguments are already validated.
 int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s);
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s);
+int launch_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype dt,
+                          void* out, int32_t* status, hipStream_t s);
 
 struct LinearArgs {
   const void* a;        // x (forward) or dY (input gradient): [M, Kred]
@@ -59,24 +61,9 @@ int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int
 size_t lorafa_ws_bytes(int32_t r, int64_t K);
 int launch_lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P, void* ws, hipStream_t st);
 
-// One AdamW update of an adapter (A-side pointers all null under LoRA-FA).
-struct AdamwLaunch {
-  nf4_adamw opt;
-  int32_t r;
-  int64_t K, N;
-  float* A;
-  const float* dA;
-  float* mA;
-  float* vA;
-  float* B;
-  const float* dB;
-  float* mB;
-  float* vB;
-  const float* precond;  // r x r or null
-  float s;
-  const float* grad_scale;  // device scalar or null
-};
-int launch_lora_adamw(const AdamwLaunch& a, hipStream_t st);
+// One AdamW update of `count` adapters (validated) in one launch.
+int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
+                      hipStream_t st);
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EDEVICE; }
 

@@ -26,8 +26,10 @@
 //                  column of each step pass through LDS (double-buffered, one
 //                  barrier per pivot). P is written in fp32.
 //  k_lora_adamw    one pass that reads p, g, m, v and writes p, m, v for every
-//                  entry of A and B (28 bytes per parameter, 16-byte accesses);
-//                  under LoRA-FA each thread forms its four entries of the
+//                  entry of A and B of up to 16 adapters (28 bytes per
+//                  parameter, 16-byte accesses); the tensors are described in
+//                  the kernel arguments and dealt out in workgroup ranges.
+//                  Under LoRA-FA each thread forms its four entries of the
 //                  preconditioned B gradient row from g_B and P on the fly.
 #include <cmath>
 
@@ -128,8 +130,17 @@ __global__ __launch_bounds__(1024) void k_spd_invert(double* __restrict__ ws, in
   for (int q = 0; q < EPT; ++q) {
     const int e = t + 1024 * q;
     if (e < rr) {
+      // slice order; eight loads in flight at a time
       double v = 0.0;
-      for (int64_t s = 0; s < slices; ++s) v += ws[s * rr + e];
+      int64_t s = 0;
+      for (; s + 8 <= slices; s += 8) {
+        double x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = ws[(s + u) * rr + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += x[u];
+      }
+      for (; s < slices; ++s) v += ws[s * rr + e];
       const int i = e / r, j = e - (e / r) * r;
       if (i == j) v += kDamping;
       st(q, e, v);
@@ -190,12 +201,28 @@ struct AdamwConst {
   float eps;
 };
 
+// One tensor of one update: A or B of an adapter. mode 0: plain AdamW over n
+// entries; 1: B with the preconditioned gradient, r % 4 == 0 (four entries of
+// one row per thread); 2: the same for any r (one entry per thread).
 struct AdamwSeg {
   float* p;
   const float* g;
   float* m;
   float* v;
-  int64_t n;
+  const float* P;  // r x r preconditioner (modes 1, 2)
+  int64_t n;       // entries
+  int64_t block0;  // first workgroup of this tensor
+  int32_t r;
+  int32_t mode;
+  float pscale;    // s^-2 (modes 1, 2)
+};
+
+constexpr int kMaxSegs = 2 * NF4_MAX_ADAPTERS_PER_CALL;
+
+// All tensors of one launch, passed by value in the kernel arguments.
+struct AdamwTable {
+  AdamwSeg seg[kMaxSegs];
+  int32_t count;
 };
 
 __device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v, const AdamwConst& c) {
@@ -225,65 +252,57 @@ __device__ __forceinline__ void adamw_four(const AdamwSeg& s, int64_t e, f4 gv, 
   *reinterpret_cast<f4*>(s.v + e) = v;
 }
 
-// Plain AdamW over entries [4 u, 4 u + 4) of a segment.
-__device__ __forceinline__ void adamw_plain(const AdamwSeg& s, int64_t u, float gs, const AdamwConst& c) {
-  const int64_t e = 4 * u;
-  if (e + 3 < s.n) {
-    f4 g = *reinterpret_cast<const f4*>(s.g + e);
-    adamw_four(s, e, g * gs, c);
-  } else {
-    for (int64_t x = e; x < s.n; ++x) {
-      float p = s.p[x], m = s.m[x], v = s.v[x];
-      adamw_one(p, s.g[x] * gs, m, v, c);
-      s.p[x] = p;
-      s.m[x] = m;
-      s.v[x] = v;
-    }
-  }
-}
-
-// MODE 0: B plain. MODE 1: B preconditioned, r % 4 == 0 (four entries of one
-// row per thread). MODE 2: B preconditioned, any r (one entry per thread).
-template <int MODE>
-__global__ __launch_bounds__(256) void k_lora_adamw(AdamwSeg sa, AdamwSeg sb, int64_t blocks_a,
-                                                   const float* __restrict__ P, int32_t r, float pscale,
-                                                   const float* __restrict__ gscale, AdamwConst c) {
+__global__ __launch_bounds__(256) void k_lora_adamw(AdamwTable tab, const float* __restrict__ gscale, AdamwConst c) {
   const float gs = gscale ? *gscale : 1.0f;
   const int64_t b = blockIdx.x;
-  if (b < blocks_a) {
-    adamw_plain(sa, b * 256 + threadIdx.x, gs, c);
-    return;
-  }
-  const int64_t u = (b - blocks_a) * 256 + threadIdx.x;
-  if constexpr (MODE == 0) {
-    adamw_plain(sb, u, gs, c);
-  } else if constexpr (MODE == 1) {
+  int k = 0;  // tensor of this workgroup (uniform)
+  while (k + 1 < tab.count && b >= tab.seg[k + 1].block0) ++k;
+  const AdamwSeg& s = tab.seg[k];
+  const int64_t u = (b - s.block0) * 256 + threadIdx.x;
+  if (s.mode == 0) {
     const int64_t e = 4 * u;
-    if (e >= sb.n) return;
+    if (e + 3 < s.n) {
+      const f4 g = *reinterpret_cast<const f4*>(s.g + e);
+      adamw_four(s, e, g * gs, c);
+    } else {
+      for (int64_t x = e; x < s.n; ++x) {
+        float p = s.p[x], m = s.m[x], v = s.v[x];
+        adamw_one(p, s.g[x] * gs, m, v, c);
+        s.p[x] = p;
+        s.m[x] = m;
+        s.v[x] = v;
+      }
+    }
+  } else if (s.mode == 1) {
+    const int64_t e = 4 * u;
+    if (e >= s.n) return;
+    const int r = s.r;
     const int64_t o = e / r;
     const int i0 = (int)(e - o * r);
-    const float* grow = sb.g + o * r;
+    const float* grow = s.g + o * r;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int j = 0; j < r; ++j) {
       const float gj = grow[j];
-      const f4 pj = *reinterpret_cast<const f4*>(P + (int64_t)j * r + i0);
+      const f4 pj = *reinterpret_cast<const f4*>(s.P + (int64_t)j * r + i0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(gj, pj[k], acc[k]);
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(gj, pj[q], acc[q]);
     }
-    adamw_four(sb, e, acc * (gs * pscale), c);
+    adamw_four(s, e, acc * (gs * s.pscale), c);
   } else {
     const int64_t e = u;
-    if (e >= sb.n) return;
+    if (e >= s.n) return;
+    const int r = s.r;
     const int64_t o = e / r;
     const int i = (int)(e - o * r);
-    const float* grow = sb.g + o * r;
+    const float* grow = s.g + o * r;
     float acc = 0.f;
-    for (int j = 0; j < r; ++j) acc = __builtin_fmaf(grow[j], P[(int64_t)j * r + i], acc);
-    float p = sb.p[e], m = sb.m[e], v = sb.v[e];
-    adamw_one(p, acc * (gs * pscale), m, v, c);
-    sb.p[e] = p;
-    sb.m[e] = m;
-    sb.v[e] = v;
+    for (int j = 0; j < r; ++j) acc = __builtin_fmaf(grow[j], s.P[(int64_t)j * r + i], acc);
+    float p = s.p[e], m = s.m[e], v = s.v[e];
+    adamw_one(p, acc * (gs * s.pscale), m, v, c);
+    s.p[e] = p;
+    s.m[e] = m;
+    s.v[e] = v;
   }
 }
 
@@ -312,41 +331,40 @@ int launch_lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P,
   return launch_status();
 }
 
-int launch_lora_adamw(const AdamwLaunch& a, hipStream_t st) {
-  const double lr = a.opt.lr, b1 = a.opt.beta1, b2 = a.opt.beta2, wd = a.opt.weight_decay;
-  const double t = (double)a.opt.step;
+int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
+                      hipStream_t st) {
+  const double lr = opt.lr, b1 = opt.beta1, b2 = opt.beta2, wd = opt.weight_decay;
+  const double t = (double)opt.step;
   const double bc1 = 1.0 - std::pow(b1, t), bc2 = 1.0 - std::pow(b2, t);
   AdamwConst c;
-  c.b1 = a.opt.beta1;
-  c.b2 = a.opt.beta2;
+  c.b1 = opt.beta1;
+  c.b2 = opt.beta2;
   c.omb1 = (float)(1.0 - b1);
   c.omb2 = (float)(1.0 - b2);
   c.dec = (float)(1.0 - lr * wd);
   c.stepsz = (float)(lr / bc1);
   c.rbc2 = (float)(1.0 / std::sqrt(bc2));
-  c.eps = a.opt.eps;
-  const double s = a.s;
-  const float pscale = a.precond ? (float)(1.0 / (s * s)) : 1.0f;
+  c.eps = opt.eps;
 
-  AdamwSeg sa{a.A, a.dA, a.mA, a.vA, a.A ? (int64_t)a.r * a.K : 0};
-  AdamwSeg sb{a.B, a.dB, a.mB, a.vB, a.N * a.r};
-  const int64_t blocks_a = ceil_div(ceil_div(sa.n, 4), 256);
-  int mode = 0;
-  int64_t blocks_b = ceil_div(ceil_div(sb.n, 4), 256);
-  if (a.precond) {
-    mode = (a.r % 4 == 0) ? 1 : 2;
-    if (mode == 2) blocks_b = ceil_div(sb.n, 256);
+  AdamwTable tab{};
+  int64_t blocks = 0;
+  auto add = [&](float* p, const float* g, float* m, float* v, int64_t n, const float* P, int32_t r, float s) {
+    AdamwSeg& q = tab.seg[tab.count++];
+    q = AdamwSeg{p, g, m, v, P, n, blocks, r, 0, 1.0f};
+    int64_t threads = ceil_div(n, 4);
+    if (P) {
+      q.mode = (r % 4 == 0) ? 1 : 2;
+      q.pscale = (float)(1.0 / ((double)s * (double)s));
+      if (q.mode == 2) threads = n;
+    }
+    blocks += ceil_div(threads, 256);
+  };
+  for (int32_t i = 0; i < count; ++i) {
+    const nf4_lora_state& a = ad[i];
+    if (a.A) add(a.A, a.dA, a.mA, a.vA, (int64_t)a.r * a.K, nullptr, a.r, a.s);
+    add(a.B, a.dB, a.mB, a.vB, a.N * a.r, a.precond, a.r, a.s);
   }
-  const dim3 grid((unsigned)(blocks_a + blocks_b));
-  if (mode == 0)
-    hipLaunchKernelGGL(k_lora_adamw<0>, grid, dim3(256), 0, st, sa, sb, blocks_a, a.precond, a.r, pscale,
-                       a.grad_scale, c);
-  else if (mode == 1)
-    hipLaunchKernelGGL(k_lora_adamw<1>, grid, dim3(256), 0, st, sa, sb, blocks_a, a.precond, a.r, pscale,
-                       a.grad_scale, c);
-  else
-    hipLaunchKernelGGL(k_lora_adamw<2>, grid, dim3(256), 0, st, sa, sb, blocks_a, a.precond, a.r, pscale,
-                       a.grad_scale, c);
+  hipLaunchKernelGGL(k_lora_adamw, dim3((unsigned)blocks), dim3(256), 0, st, tab, grad_scale, c);
   return launch_status();
 }
 

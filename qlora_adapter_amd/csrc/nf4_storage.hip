@@ -294,7 +294,117 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   }
 }
 
+// Selected rows of a packed [V, D] table: out[t, :] = decoded row ids[t], the
+// same values nf4_dequantize gives for those rows. VEC (D % 8 == 0): 8-element
+// units, i.e. one 4-byte code word inside one block and one 16-byte bf16 (or
+// two 16-byte fp32) stores; each thread takes EMB_UPT units 256 apart so that
+// their dependent loads (id, then code word and scale) overlap. Otherwise one
+// thread per element. An id outside [0, V) yields a zero row and NF4_EINVAL in
+// the status word; no packed byte outside the table is read.
+constexpr int EMB_UPT = 4;
+
+template <bool DQ, bool BF16>
+__device__ __forceinline__ void store_unit(void* out, int64_t o, const float (&v)[8]) {
+  if (BF16) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v q;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      q[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{v[2 * p], v[2 * p + 1]}), b2));
+    *reinterpret_cast<u4v*>(static_cast<__bf16*>(out) + o) = q;
+  } else {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    f4v* dst = reinterpret_cast<f4v*>(static_cast<float*>(out) + o);
+    dst[0] = f4v{v[0], v[1], v[2], v[3]};
+    dst[1] = f4v{v[4], v[5], v[6], v[7]};
+  }
+}
+
+template <bool DQ, bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void k_embed_rows(NF4View w, int64_t V, int64_t D, const int64_t* __restrict__ ids,
+                                                   int64_t units, void* __restrict__ out,
+                                                   int32_t* __restrict__ status) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_value(threadIdx.x);
+  __syncthreads();
+  const float mu = DQ ? w.offset[0] : 0.0f;
+  if constexpr (VEC) {
+    const int64_t per_row = D / 8;
+    const int64_t base = (int64_t)blockIdx.x * (256 * EMB_UPT) + threadIdx.x;
+    int64_t t[EMB_UPT], c[EMB_UPT], id[EMB_UPT];
+    bool live[EMB_UPT], ok[EMB_UPT];
+#pragma unroll
+    for (int q = 0; q < EMB_UPT; ++q) {
+      const int64_t u = base + 256 * q;
+      live[q] = u < units;
+      t[q] = live[q] ? u / per_row : 0;
+      c[q] = u - t[q] * per_row;
+      id[q] = live[q] ? ids[t[q]] : 0;
+    }
+    uint32_t word[EMB_UPT];
+    float a[EMB_UPT];
+#pragma unroll
+    for (int q = 0; q < EMB_UPT; ++q) {
+      ok[q] = live[q] && id[q] >= 0 && id[q] < V;
+      const int64_t f = ok[q] ? id[q] * D + 8 * c[q] : 0;
+      word[q] = ok[q] ? reinterpret_cast<const uint32_t*>(w.codes)[f >> 3] : 0u;
+      a[q] = ok[q] ? block_scale_of<DQ>(w, mu, f >> 6) : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < EMB_UPT; ++q) {
+      if (!live[q]) continue;
+      if (!ok[q] && status && c[q] == 0) *status = NF4_EINVAL;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = __fmul_rn(lut[(word[q] >> (8 * (j >> 1) + ((j & 1) ? 0 : 4))) & 15u], a[q]);
+      store_unit<DQ, BF16>(out, t[q] * D + 8 * c[q], v);
+    }
+  } else {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const int64_t t = u / D, c = u - t * D;
+    const int64_t id = ids[t];
+    const bool ok = id >= 0 && id < V;
+    if (!ok && status && c == 0) *status = NF4_EINVAL;
+    const float v = ok ? decode_one<DQ>(w, mu, lut, id * D + c) : 0.0f;
+    if (BF16)
+      static_cast<__bf16*>(out)[u] = (__bf16)v;
+    else
+      static_cast<float*>(out)[u] = v;
+  }
+}
+
 }  // namespace
+
+int launch_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype dt,
+                          void* out, int32_t* status, hipStream_t s) {
+  if (status) hipLaunchKernelGGL(k_set_status, dim3(1), dim3(64), 0, s, status);
+  if (T == 0) return launch_status();
+  const bool vec = (D % 8) == 0, dq = E->double_quant != 0, bf = dt == NF4_BF16;
+  const int64_t units = T * (vec ? D / 8 : D);
+  const dim3 grid((unsigned)ceil_div(units, vec ? 256 * EMB_UPT : 256));
+  const NF4View w = make_view(E);
+#define NF4_EMBED(DQ_, BF_, VEC_) \
+  hipLaunchKernelGGL((k_embed_rows<DQ_, BF_, VEC_>), grid, dim3(256), 0, s, w, V, D, ids, units, out, status)
+  if (dq) {
+    if (bf) {
+      if (vec) NF4_EMBED(true, true, true); else NF4_EMBED(true, true, false);
+    } else {
+      if (vec) NF4_EMBED(true, false, true); else NF4_EMBED(true, false, false);
+    }
+  } else {
+    if (bf) {
+      if (vec) NF4_EMBED(false, true, true); else NF4_EMBED(false, true, false);
+    } else {
+      if (vec) NF4_EMBED(false, false, true); else NF4_EMBED(false, false, false);
+    }
+  }
+#undef NF4_EMBED
+  return launch_status();
+}
 
 int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s) {
   const int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);

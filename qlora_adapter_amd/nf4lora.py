@@ -22,9 +22,12 @@ LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
 NF4_F32, NF4_BF16 = 0, 1
 _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
-EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_linear_fwd",
+EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
-           "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "nf4_status_string", "nf4lora_abi_version"]
+           "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "nf4_status_string",
+           "nf4lora_abi_version"]
+
+MAX_ADAPTERS_PER_CALL = 16
 
 
 class NF4Error(RuntimeError):
@@ -50,6 +53,13 @@ class _Adamw(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class _LoraState(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int32), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("mA", ctypes.c_void_p), ("vA", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("dB", ctypes.c_void_p), ("mB", ctypes.c_void_p), ("vB", ctypes.c_void_p),
+                ("precond", ctypes.c_void_p), ("s", ctypes.c_float)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -68,6 +78,7 @@ def load() -> ctypes.CDLL:
             lib.nf4_code_tables.argtypes = [P, P]
             lib.nf4_quantize.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, ctypes.c_size_t, P, P]
             lib.nf4_dequantize.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, P, P]
+            lib.nf4_embedding_rows.argtypes = [ctypes.POINTER(_Tensor), I64, I64, P, I64, ctypes.c_int, P, P, P]
             lib.nf4_linear_fwd.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32, F, P,
                                            P, P]
             lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
@@ -79,6 +90,7 @@ def load() -> ctypes.CDLL:
             lib.lorafa_preconditioner_workspace_bytes.argtypes = [I32, I64]
             lib.lorafa_preconditioner.argtypes = [P, I32, I64, P, P, ctypes.c_size_t, P]
             lib.lora_adamw_step.argtypes = [ctypes.POINTER(_Adamw), I32, I64, I64, P, P, P, P, P, P, P, P, P, F, P, P]
+            lib.lora_adamw_step_many.argtypes = [ctypes.POINTER(_Adamw), ctypes.POINTER(_LoraState), I32, P, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
             lib.nf4_status_string.argtypes = [ctypes.c_int]
             for fn in EXPORTS:
@@ -210,6 +222,24 @@ def dequantize(t: NF4Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] =
     return out
 
 
+def embedding_rows(E: NF4Tensor, ids: torch.Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                   status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decoded rows ids of a packed [V, D] table: out[t] = dequantize(E)[ids[t]].
+    An id outside [0, V) gives a zero row and NF4_EINVAL (-1) in `status`."""
+    if len(E.shape) != 2:
+        raise ValueError("the embedding table must be 2-D [V, D]")
+    V, D = E.shape
+    _dev(ids, "ids", torch.int64)
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, D), dtype=dtype, device=E.device)
+    _dev(out, "out", dtype)
+    st = E.c_struct()
+    _check("nf4_embedding_rows", load().nf4_embedding_rows(ctypes.byref(st), V, D, _ptr(ids), T, _DT[dtype],
+                                                           _ptr(out), _ptr(status), _stream(E.device)))
+    return out
+
+
 def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
                s: float = 0.0, y: Optional[torch.Tensor] = None,
                t_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -301,6 +331,44 @@ def lorafa_preconditioner(A: torch.Tensor, out: Optional[torch.Tensor] = None,
     _check("lorafa_preconditioner", load().lorafa_preconditioner(_ptr(A), r, K, _ptr(out), _ptr(workspace), need,
                                                                  _stream(A.device)))
     return out
+
+
+def _state(ad: dict) -> _LoraState:
+    B = ad["B"]
+    for name in ("B", "dB", "mB", "vB"):
+        _dev(ad[name], name, torch.float32)
+    N, r = B.shape
+    A = ad.get("A")
+    K = 1
+    if A is not None:
+        for name in ("A", "dA", "mA", "vA"):
+            if ad.get(name) is None:
+                raise ValueError(f"{name} is required when A is trained")
+            _dev(ad[name], name, torch.float32)
+        K = A.shape[1]
+    P = ad.get("precond")
+    if P is not None:
+        _dev(P, "precond", torch.float32)
+    g = lambda k: None if ad.get(k) is None else ad[k].data_ptr()
+    return _LoraState(r, K, N, g("A"), g("dA"), g("mA"), g("vA"), g("B"), g("dB"), g("mB"), g("vB"), g("precond"),
+                      float(ad.get("s", 0.0)))
+
+
+def lora_adamw_step_many(adapters, *, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                         eps: float = 1e-8, weight_decay: float = 0.01,
+                         grad_scale: Optional[torch.Tensor] = None) -> None:
+    """lora_adamw_step for up to 16 adapters in one launch. Each adapter is a
+    dict with B, dB, mB, vB and, for LoRA, A, dA, mA, vA; for LoRA-FA optionally
+    precond and s."""
+    adapters = list(adapters)
+    if not adapters:
+        return
+    if grad_scale is not None:
+        _dev(grad_scale, "grad_scale", torch.float32)
+    arr = (_LoraState * len(adapters))(*[_state(a) for a in adapters])
+    opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    _check("lora_adamw_step_many", load().lora_adamw_step_many(ctypes.byref(opt), arr, len(adapters),
+                                                               _ptr(grad_scale), _stream(adapters[0]["B"].device)))
 
 
 def lora_adamw_step(B: torch.Tensor, dB: torch.Tensor, mB: torch.Tensor, vB: torch.Tensor, *, step: int,

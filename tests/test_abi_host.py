@@ -151,3 +151,36 @@ def test_optimizer_argument_errors_before_device(lib):
     assert step(opt, Bp=(256, 260, 256, 256)) == EALIGN
     assert step(opt, A=(None,) * 4, P=264) == EALIGN
     assert step(opt, gs=258) == EALIGN
+
+
+def test_embedding_argument_errors_before_device(lib):
+    L, m = lib
+    EINVAL, EALIGN, EUNSUP = -1, -2, -3
+    E = m._Tensor(16, 16, 16, 16, 100 * 64, 1)
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 256, 10, 9, 256, None, None) == EUNSUP
+    assert L.nf4_embedding_rows(ctypes.byref(E), 0, 64, 256, 10, 1, 256, None, None) == EINVAL
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 63, 256, 10, 1, 256, None, None) == EINVAL  # n != V*D
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, None, 10, 1, 256, None, None) == EINVAL
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 256, 10, 1, None, None, None) == EINVAL
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 256, -1, 1, 256, None, None) == EINVAL
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 260, 10, 1, 256, None, None) == EALIGN
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 256, 10, 1, 264, None, None) == EALIGN
+    assert L.nf4_embedding_rows(ctypes.byref(E), 100, 64, 256, 10, 1, 256, 258, None) == EALIGN
+    assert L.nf4_embedding_rows(None, 100, 64, 256, 10, 1, 256, None, None) == EINVAL
+
+
+def test_many_adapter_step_argument_errors(lib):
+    L, m = lib
+    EINVAL, EALIGN = -1, -2
+    opt = m._Adamw(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    good = dict(r=16, K=64, N=32, A=256, dA=256, mA=256, vA=256, B=256, dB=256, mB=256, vB=256, precond=None,
+                s=2.0)
+    arr = lambda *ds: (m._LoraState * len(ds))(*[m._LoraState(**d) for d in ds])
+    assert L.lora_adamw_step_many(ctypes.byref(opt), None, 1, None, None) == EINVAL
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good), 0, None, None) == EINVAL
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(*[good] * 17), 17, None, None) == EINVAL
+    assert L.lora_adamw_step_many(None, arr(good), 1, None, None) == EINVAL
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good, {**good, "r": 0}), 2, None, None) == EINVAL
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good, {**good, "precond": 256}), 2, None, None) == EINVAL
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good, {**good, "vB": 264}), 2, None, None) == EALIGN
+    assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good), 1, 258, None) == EALIGN

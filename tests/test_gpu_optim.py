@@ -143,8 +143,70 @@ def test_chained_steps_follow_the_oracle(gpu):
 
 
 def test_llama8b_layer_adapters_one_update(gpu):
-    """All seven rank-16 adapters of the Llama-8B-shaped layer, one update each,
-    in the shapes and launch configuration the benchmark times."""
+    """All seven rank-16 adapters of the Llama-8B-shaped layer, one
+    lora_adamw_step call each."""
     for i, L in enumerate(workloads.WORKLOADS["llama8b_layer"]["layers"]):
         print(f"[adamw llama8b] {L.name}", flush=True)
         _lora_case(gpu, L.lora_rank, L.k_in, L.n_out, 5, None, fa=False, precond=False, seed=20 + 2 * i)
+
+
+def _adapter(r, K, N, fa, precond, seed):
+    d = {}
+    st = _state((N, r), seed, False)
+    d.update(B=st["p"], dB=st["g"], mB=st["m"], vB=st["v"])
+    if not fa:
+        sa = _state((r, K), seed + 1, False)
+        d.update(A=sa["p"], dA=sa["g"], mA=sa["m"], vA=sa["v"])
+    if precond:
+        d.update(precond=gpu_precond(r, K, seed), s=2.0)
+    return d
+
+
+def gpu_precond(r, K, seed):
+    from qlora_adapter_amd import nf4lora
+    return nf4lora.lorafa_preconditioner(workloads.normal_f32((r, K), 1.0 / r, 900 + seed, "cuda"))
+
+
+def test_many_adapters_in_one_launch_equal_separate_calls(gpu):
+    """lora_adamw_step_many over a mixed set (LoRA, LoRA-FA with and without
+    the preconditioner, r % 4 != 0, ragged sizes) is bit-identical to one
+    lora_adamw_step call per adapter."""
+    specs = [(16, 4096, 4096, False, False), (5, 333, 77, False, False), (16, 1024, 512, True, True),
+             (6, 100, 37, True, True), (8, 256, 129, True, False), (64, 14336, 4096, False, False),
+             (1, 3, 5, False, False)]
+    many = [_adapter(*sp, seed=10 * i) for i, sp in enumerate(specs)]
+    single = [{k: v.clone() for k, v in ad.items() if isinstance(v, torch.Tensor)} | {"s": ad.get("s", 0.0)}
+              for ad in many]
+    gs = torch.full((1,), 0.75, dtype=torch.float32, device="cuda")
+    gpu.lora_adamw_step_many(many, step=4, grad_scale=gs, **HP)
+    for ad in single:
+        kw = {k: ad[k] for k in ("A", "dA", "mA", "vA") if k in ad}
+        gpu.lora_adamw_step(ad["B"], ad["dB"], ad["mB"], ad["vB"], step=4, precond=ad.get("precond"), s=ad["s"],
+                            grad_scale=gs, **kw, **HP)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(many, single)):
+        for k in ("A", "mA", "vA", "B", "mB", "vB"):
+            if k in a:
+                assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), (i, k)
+
+
+def test_llama8b_layer_adapters_one_launch(gpu):
+    """The seven rank-16 adapters of the Llama-8B-shaped layer in one launch
+    (the benchmark's call), each checked against the oracle."""
+    layers = workloads.WORKLOADS["llama8b_layer"]["layers"]
+    ads, host = [], []
+    for i, L in enumerate(layers):
+        ad = _adapter(L.lora_rank, L.k_in, L.n_out, False, False, seed=300 + 10 * i)
+        ads.append(ad)
+        host.append({k: _np(v) for k, v in ad.items()})
+    gpu.lora_adamw_step_many(ads, step=3, **HP)
+    torch.cuda.synchronize()
+    for L, ad, h in zip(layers, ads, host):
+        print(f"[adamw many] {L.name}", flush=True)
+        ref = oracle.lora_adamw_step(h["B"], h["dB"], h["mB"], h["vB"], A=h["A"], dA=h["dA"], mA=h["mA"],
+                                     vA=h["vA"], step=3, **HP)
+        for side in ("A", "B"):
+            g = h["d" + side].astype(np.float64)
+            b = adamw_bounds(h[side], g, h["m" + side], h["v" + side], U32 * np.abs(g), HP, 3)
+            for key, name, bd in zip((side, "m" + side, "v" + side), (side, "m" + side, "v" + side), b):
+                assert_within(_np(ad[key]), ref[name], bd, f"{L.name} {name}")
