@@ -46,7 +46,8 @@ __global__ void k_set_status(int32_t* status) {
 // Wave w owns blocks [64w, 64w+64) of the group; in pass `it` lane l holds the
 // 8 weights starting at 512*it + 8*l of the wave's range, so 8 lanes hold one
 // block. Writes codes, absmax (to `absmax`), and with DQ the group's pairwise
-// fp64 sum of its 256 maxima (zero beyond nb) to partials[blockIdx.x].
+// fp64 sum of its 256 maxima (zero beyond nb) to partials[blockIdx.x], NaN if
+// the group holds a non-finite weight.
 //
 // The code of x = fl32(v / m) is found through a 256-bin table over [-1, 1]:
 // bin b = floor((x + 1) * 128) holds the threshold t_k nearest to its centre
@@ -99,21 +100,47 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, i
       bad |= !isfinite(v[j]);
       m = fmaxf(m, fabsf(v[j]));
     }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    uint32_t packed = 0;
+    // maximum over the 8 lanes of the block with DPP moves (no LDS round trip):
+    // quad lanes [1,0,3,2], then [2,3,0,1], then the mirror inside each 8-lane
+    // half-row pairs the two quads
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x141, 0xF, 0xF, false)));
     const bool exact = !(m >= 1.17549435e-38f && m <= 3.40282347e38f);  // m zero, denormal or not finite
     const float rm = __builtin_amdgcn_rcpf(m);
+    // all eight table reads first, then the decisions
+    float x[8];
+    float2 e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float x = v[j] * rm;
-      if (exact) x = v[j] / m;  // IEEE division
-      int b = (int)((x + 1.0f) * 128.0f);
+      x[j] = v[j] * rm;
+      int b = (int)((x[j] + 1.0f) * 128.0f);
       b = b < 0 ? 0 : (b > 255 ? 255 : b);
-      const float2 e = s_bin[b];
-      uint32_t c = __float_as_uint(e.y) + ((x > e.x) ? 1u : 0u);
-      if (!exact && fabsf(x - e.x) < 6.103515625e-05f * fabsf(e.x)) c = __float_as_uint(e.y) + ((v[j] / m > e.x) ? 1u : 0u);
+      e[j] = s_bin[b];
+    }
+    uint32_t cj[8];
+    uint32_t slow = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cj[j] = __float_as_uint(e[j].y) + ((x[j] > e[j].x) ? 1u : 0u);
+      slow |= (exact || fabsf(x[j] - e[j].x) < 6.103515625e-05f * fabsf(e[j].x)) ? (1u << j) : 0u;
+    }
+    // Rare: the correctly rounded quotient decides (kept behind a branch so the
+    // division is not evaluated on the common path).
+    if (__builtin_expect(slow != 0, 0)) {
+      for (int j = 0; j < 8; ++j) {
+        if (!((slow >> j) & 1u)) continue;
+        const float xe = v[j] / m;  // IEEE division
+        int be = (int)((xe + 1.0f) * 128.0f);
+        be = be < 0 ? 0 : (be > 255 ? 255 : be);
+        const float2 ee = s_bin[be];
+        cj[j] = __float_as_uint(ee.y) + ((xe > ee.x) ? 1u : 0u);
+      }
+    }
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c = cj[j];
       if (!(m > 0.0f)) c = 7u;
       if (e0 + j >= n) c = 0;  // padding nibble past the end
       // element 2p -> high nibble of byte p, element 2p+1 -> low nibble
@@ -131,9 +158,13 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, i
       if (e0 < n) absmax[e0 / 64] = m;
     }
   }
-  if (bad && status) *status = NF4_ENONFINITE;
-  if (!DQ) return;
-  __syncthreads();
+  if (!DQ) {
+    if (bad && status) *status = NF4_ENONFINITE;
+    return;
+  }
+  // With double quantization the status word is written after the mean: a
+  // group with a non-finite weight reports a NaN partial sum instead.
+  const bool group_bad = __syncthreads_or(bad);
   if (wave == 0) {
     // Leaves 4l..4l+3 in tree order, then a butterfly that pairs lane l with
     // l^1, l^2, ...: every step adds two adjacent, equally sized subtrees.
@@ -141,73 +172,108 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ w, i
                ((double)s_max[4 * lane + 2] + (double)s_max[4 * lane + 3]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) t = t + __shfl_xor(t, off);
-    if (lane == 0) partials[blockIdx.x] = t;
+    if (lane == 0) partials[blockIdx.x] = group_bad ? __builtin_nan("") : t;
   }
 }
 
-// One workgroup. Pairwise fp64 sum of partials[0..C) zero-padded to a power
-// of two, then offset = fp32(sum / nb). Thread t sums an aligned run of L
-// leaves with a binary-counter stack (left + right at every level); the 256
-// thread sums are then combined by a butterfly inside each wave and by
-// (w0 + w1) + (w2 + w3) across the four waves.
-__global__ __launch_bounds__(256) void k_dq_mean(const double* __restrict__ partials, int64_t C, int64_t nb,
-                                                 float* __restrict__ offset) {
-  __shared__ double s_wave[4];
+// Pairwise fp64 sum of partials[0..C) zero-padded to a power of two, by the
+// whole workgroup (256 threads): thread t sums an aligned run of L leaves with
+// a binary-counter stack (left + right at every level); the 256 thread sums are
+// then combined by a butterfly inside each wave and by (w0 + w1) + (w2 + w3)
+// across the four waves. Every thread returns the same value.
+__device__ double pairwise_sum_wg(const double* __restrict__ partials, int64_t C, double* s_wave) {
   int64_t P = 1;
   while (P < C) P <<= 1;
   const int64_t L = P >= 256 ? P / 256 : 1;
   const int64_t first = (int64_t)threadIdx.x * L;
-  double stack[48];
-  int top = 0;
-  for (int64_t i = 0; i < L; ++i) {
-    double v = (first + i < C) ? partials[first + i] : 0.0;
-    int lv = 0;
-    for (int64_t idx = i; idx & 1; idx >>= 1, ++lv) v = stack[lv] + v;
-    stack[lv] = v;
-    top = lv;
+  double t;
+  if (L <= 16) {
+    // the run's tree in registers: 16 slots, the L leaves first and zeros after
+    // (x + 0 is exact, so the padded tree gives the L-leaf tree's value)
+    double v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (i < L && first + i < C) ? partials[first + i] : 0.0;
+#pragma unroll
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * w) v[i] = v[i] + v[i + w];
+    t = v[0];
+  } else {
+    double stack[48];
+    int top = 0;
+    for (int64_t i = 0; i < L; ++i) {
+      double v = (first + i < C) ? partials[first + i] : 0.0;
+      int lv = 0;
+      for (int64_t idx = i; idx & 1; idx >>= 1, ++lv) v = stack[lv] + v;
+      stack[lv] = v;
+      top = lv;
+    }
+    t = stack[top];
   }
-  double t = stack[top];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) t = t + __shfl_xor(t, off);
   if (lane == 0) s_wave[wave] = t;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const double S = (s_wave[0] + s_wave[1]) + (s_wave[2] + s_wave[3]);
-    offset[0] = (float)(S / (double)nb);
-  }
+  return (s_wave[0] + s_wave[1]) + (s_wave[2] + s_wave[3]);
 }
 
-// One wave per nested block j: lane l holds maxima 4l..4l+3 of the block.
-// c = fl32(absmax - mu); nested[j] = max |c|; qabs = dynamic8 code of c / m.
-__global__ __launch_bounds__(256) void k_dq_nested(const float* __restrict__ absmax, int64_t nb,
-                                                   const float* __restrict__ offset, uint8_t* __restrict__ qabs,
-                                                   float* __restrict__ nested) {
+// Double quantization after k_quantize. Every workgroup forms the matrix mean
+// mu = fp32(S / nb) from the group partial sums itself (the same code and order
+// in every workgroup, so the same value), then each wave handles nested blocks
+// j = 16 g + 4 i + w, i < 4: lane l holds maxima 4l..4l+3 of the block,
+// c = fl32(absmax - mu), nested[j] = max |c|, qabs = dynamic8 code of c / m.
+// Workgroup 0 also writes the offset and the status word (NF4_ENONFINITE when
+// S is not finite, i.e. some weight was not finite, else 0).
+constexpr int DQN_PER_WG = 4;
+
+__global__ __launch_bounds__(256) void k_dq_nested(const double* __restrict__ partials, int64_t C,
+                                                   const float* __restrict__ absmax, int64_t nb,
+                                                   float* __restrict__ offset, uint8_t* __restrict__ qabs,
+                                                   float* __restrict__ nested, int32_t* __restrict__ status) {
+  __shared__ double s_wave[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 4 + wave;
   const int64_t nn = (nb + 255) / 256;
-  if (j >= nn) return;
-  const float mu = offset[0];
-  const int64_t b0 = j * 256 + 4 * lane;
-  float c[4];
-  float m = 0.0f;
+  constexpr int IT = DQN_PER_WG / 4;
+  // the maxima do not depend on the mean: their loads go out before it
+  float am[IT][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c[q] = (b0 + q < nb) ? __fsub_rn(absmax[b0 + q], mu) : 0.0f;
-    m = fmaxf(m, fabsf(c[q]));
+  for (int i = 0; i < IT; ++i) {
+    const int64_t b0 = ((int64_t)blockIdx.x * DQN_PER_WG + 4 * i + wave) * 256 + 4 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) am[i][q] = (b0 + q < nb) ? absmax[b0 + q] : 0.0f;
+  }
+  const double S = pairwise_sum_wg(partials, C, s_wave);
+  const float mu = (float)(S / (double)nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    offset[0] = mu;
+    if (status) *status = isfinite(S) ? 0 : NF4_ENONFINITE;
   }
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-  uint32_t packed = 0;
+  for (int i = 0; i < IT; ++i) {
+    const int64_t j = (int64_t)blockIdx.x * DQN_PER_WG + 4 * i + wave;
+    if (j >= nn) break;
+    const int64_t b0 = j * 256 + 4 * lane;
+    float c[4];
+    float m = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) packed |= ((m > 0.0f) ? dyn8_code(c[q] / m) : 127u) << (8 * q);
-  if (b0 + 4 <= nb) {
-    *reinterpret_cast<uint32_t*>(qabs + b0) = packed;
-  } else {
-    for (int q = 0; q < 4; ++q)
-      if (b0 + q < nb) qabs[b0 + q] = (uint8_t)(packed >> (8 * q));
+    for (int q = 0; q < 4; ++q) {
+      c[q] = (b0 + q < nb) ? __fsub_rn(am[i][q], mu) : 0.0f;
+      m = fmaxf(m, fabsf(c[q]));
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    uint32_t packed = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) packed |= ((m > 0.0f) ? dyn8_code(c[q] / m) : 127u) << (8 * q);
+    if (b0 + 4 <= nb) {
+      *reinterpret_cast<uint32_t*>(qabs + b0) = packed;
+    } else {
+      for (int q = 0; q < 4; ++q)
+        if (b0 + q < nb) qabs[b0 + q] = (uint8_t)(packed >> (8 * q));
+    }
+    if (lane == 0) nested[j] = m;
   }
-  if (lane == 0) nested[j] = m;
 }
 
 // A unit is the 8 weights of one 32-bit code word (bytes 4u..4u+3). Wave w of
@@ -410,21 +476,19 @@ int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, in
   const int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);
   const int64_t groups = nn;  // one workgroup per 16384 weights
   int32_t* st = status;
-  if (st) {
-    hipLaunchKernelGGL(k_set_status, dim3(1), dim3(64), 0, s, st);
-  }
-  // The quantize kernels write the status word only on a non-finite weight.
   if (!t->double_quant) {
+    // reset first; k_quantize writes the status word only on a non-finite weight
+    if (st) hipLaunchKernelGGL(k_set_status, dim3(1), dim3(64), 0, s, st);
     hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes,
                        static_cast<float*>(t->scales), nullptr, st);
     return launch_status();
   }
   float* absmax = static_cast<float*>(ws);
   double* partials = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)nb, 256));
-  hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes, absmax, partials, st);
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, partials, nn, nb, t->offset);
-  hipLaunchKernelGGL(k_dq_nested, dim3((unsigned)ceil_div(nn, 4)), dim3(256), 0, s, absmax, nb, t->offset,
-                     static_cast<uint8_t*>(t->scales), t->nested);
+  hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes, absmax, partials,
+                     nullptr);
+  hipLaunchKernelGGL(k_dq_nested, dim3((unsigned)ceil_div(nn, DQN_PER_WG)), dim3(256), 0, s, partials, nn, absmax, nb,
+                     t->offset, static_cast<uint8_t*>(t->scales), t->nested, st);
   return launch_status();
 }
 
