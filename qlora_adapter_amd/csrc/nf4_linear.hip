@@ -416,15 +416,34 @@ __device__ __forceinline__ bf16x4l lds_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4l __attribute__((address_space(3)))*)(p));
 }
 
-__global__ __launch_bounds__(256) void k_lora_mfma(const float* __restrict__ P, const __bf16* __restrict__ Q,
-                                                   int64_t M, int64_t J, int r, int64_t chunk,
-                                                   float* __restrict__ partial) {
+// One token reduction of lora_grad: partial[c][rho][j] = sum over the tokens
+// of chunk c of P[m][rho] Q[m][j].
+struct LoraProb {
+  const float* P;
+  const __bf16* Q;
+  int64_t J;
+  int64_t chunk;
+  int64_t col_tiles;  // ceil(J / 256)
+  float* partial;
+};
+
+// Both reductions of one lora_grad call (dB's and dA's) share the grid:
+// workgroups [0, blocks0) take problem 0, the rest problem 1; inside a problem
+// workgroup b covers column tile b % col_tiles of chunk b / col_tiles.
+__global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int64_t blocks0, int64_t M, int r) {
   __shared__ __attribute__((aligned(16))) __bf16 qs[2][32 * LQP];
   __shared__ __attribute__((aligned(16))) __bf16 pls[2][3][32 * LPP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 4, i16 = lane & 15, kg = G >> 1, hs = G & 1;
-  const int64_t j0 = (int64_t)blockIdx.x * 256;
-  const int64_t c = blockIdx.y;
+  const bool second = (int64_t)blockIdx.x >= blocks0;
+  const LoraProb& pr = second ? p1 : p0;
+  const float* __restrict__ P = pr.P;
+  const __bf16* __restrict__ Q = pr.Q;
+  const int64_t J = pr.J, chunk = pr.chunk;
+  float* __restrict__ partial = pr.partial;
+  const int64_t b = (int64_t)blockIdx.x - (second ? blocks0 : 0);
+  const int64_t j0 = (b % pr.col_tiles) * 256;
+  const int64_t c = b / pr.col_tiles;
   const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
   const bool vecq = (J % 8) == 0;
   // staging roles: Q row 8 u + tid / 32 (u = 0..3), 16-byte chunk tid % 32;
@@ -519,10 +538,26 @@ __global__ __launch_bounds__(256) void k_lora_mfma(const float* __restrict__ P, 
   }
 }
 
-__global__ __launch_bounds__(256) void k_lora_combine(const float* __restrict__ partial, int64_t chunks, int r,
-                                                      int64_t J, float s, bool transpose_out,
-                                                      float* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Stage 2 of one or two reductions: out = s * (sum of the chunks in order), in
+// [J][r] (transpose_out) or [r][J] layout. Threads [0, r J0) take problem 0,
+// the next r J1 problem 1.
+struct LoraSum {
+  const float* partial;
+  int64_t chunks;
+  int64_t J;
+  bool transpose_out;
+  float* out;
+};
+
+__global__ __launch_bounds__(256) void k_lora_combine(LoraSum q0, LoraSum q1, int r, float s) {
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool second = idx >= (int64_t)r * q0.J;
+  if (second) idx -= (int64_t)r * q0.J;
+  const LoraSum& q = second ? q1 : q0;
+  const float* __restrict__ partial = q.partial;
+  const int64_t chunks = q.chunks, J = q.J;
+  const bool transpose_out = q.transpose_out;
+  float* __restrict__ out = q.out;
   if (idx >= (int64_t)r * J) return;
   const int64_t rho = idx / J, j = idx % J;
   const float* p = partial + rho * J + j;
@@ -606,8 +641,25 @@ int launch_linear(const LinearArgs& g, hipStream_t st) {
   return run_linear_general<float>(g, st);
 }
 
+// Tokens per chunk of the bf16 MFMA reduction: about 256 workgroups of 256
+// columns per problem, a multiple of the 32-token step. Fewer, longer chunks
+// than the general path keep the partial sums small next to the input.
+int64_t lora_chunk_mfma(int64_t M, int64_t J) {
+  const int64_t tiles = ceil_div(J, 256);
+  int64_t chunks = 256 / tiles;
+  if (chunks < 1) chunks = 1;
+  return ceil_div(ceil_div(M, chunks), 32) * 32;
+}
+
+// Chunks of either path (the query does not know the dtype, so the workspace
+// covers the larger).
+int64_t lora_chunks_max(int64_t M, int64_t J) {
+  const int64_t a = ceil_div(M, lora_chunk(M, J)), b = ceil_div(M, lora_chunk_mfma(M, J));
+  return a > b ? a : b;
+}
+
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
-  const int64_t chB = ceil_div(M, lora_chunk(M, N)), chA = ceil_div(M, lora_chunk(M, K));
+  const int64_t chB = lora_chunks_max(M, N), chA = lora_chunks_max(M, K);
   size_t bytes = round_up(sizeof(float) * (size_t)(chB * r * N), 256);
   if (!fa) bytes += round_up(sizeof(float) * (size_t)(chA * r * K), 256);
   return bytes;
@@ -620,30 +672,44 @@ void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, floa
                float* out, hipStream_t st) {
   const int64_t chunk = lora_chunk(M, J), chunks = ceil_div(M, chunk);
   const dim3 grid((unsigned)ceil_div(J, LCOLS), (unsigned)chunks);
-  if constexpr (sizeof(T) == 2) {
-    if (r <= 32) {
-      hipLaunchKernelGGL(k_lora_mfma, dim3((unsigned)ceil_div(J, 256), (unsigned)chunks), dim3(256), 0, st, P, Q, M, J,
-                         r, chunk, part);
-      hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, part, chunks,
-                         r, J, s, transpose_out, out);
-      return;
-    }
-  }
   if (J % 2 == 0 && J >= 2)
     hipLaunchKernelGGL((k_lora_partial<T, true>), grid, dim3(256), 0, st, P, Q, M, J, r, chunk, part);
   else
     hipLaunchKernelGGL((k_lora_partial<T, false>), grid, dim3(256), 0, st, P, Q, M, J, r, chunk, part);
-  hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, part, chunks, r,
-                     J, s, transpose_out, out);
+  const LoraSum q{part, chunks, J, transpose_out, out};
+  hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, q, q, r, s);
+}
+
+// bf16 activations, r <= 32: dB's reduction (P = T, Q = dY) and, unless
+// LoRA-FA, dA's (P = U, Q = x) in one MFMA launch and one combine launch.
+void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int64_t N, const float* t,
+                    const float* u, int32_t r, float s, float* dA, float* dB, float* partA, float* partB,
+                    hipStream_t st) {
+  const int64_t chB = lora_chunk_mfma(M, N), chA = lora_chunk_mfma(M, K);
+  const LoraProb pb{t, dy, N, chB, ceil_div(N, 256), partB};
+  const LoraProb pa{u, x, K, chA, ceil_div(K, 256), partA};
+  const int64_t blocksB = pb.col_tiles * ceil_div(M, chB);
+  const int64_t blocksA = dA ? pa.col_tiles * ceil_div(M, chA) : 0;
+  hipLaunchKernelGGL(k_lora_mfma, dim3((unsigned)(blocksB + blocksA)), dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M,
+                     r);
+  const LoraSum qb{partB, ceil_div(M, chB), N, true, dB};
+  const LoraSum qa{partA, ceil_div(M, chA), K, false, dA};
+  const int64_t outs = (int64_t)r * N + (dA ? (int64_t)r * K : 0);
+  hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div(outs, 256)), dim3(256), 0, st, qb, dA ? qa : qb, r, s);
 }
 }  // namespace
 
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
                      const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st) {
-  const int64_t chunksB = ceil_div(M, lora_chunk(M, N));
+  const int64_t chunksB = lora_chunks_max(M, N);
   float* partB = static_cast<float*>(ws);
   float* partA =
       reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunksB * r * N), 256));
+  if (dt == NF4_BF16 && r <= 32) {
+    lora_grad_mfma(static_cast<const __bf16*>(x), static_cast<const __bf16*>(dy), M, K, N, t, u, r, s, dA, dB, partA,
+                   partB, st);
+    return launch_status();
+  }
   // dB[n][rho] = s * sum_m dY[m][n] T[m][rho]  ([N][r] layout)
   if (dt == NF4_BF16)
     lora_side<__bf16>(t, static_cast<const __bf16*>(dy), M, N, r, s, true, partB, dB, st);

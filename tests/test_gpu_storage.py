@@ -80,6 +80,9 @@ def test_repeat_identical_and_nonfinite(gpu):
         gpu.quantize(v, True, status=st)
         torch.cuda.synchronize()
         assert int(st.item()) == -5  # NF4_ENONFINITE
+        gpu.quantize(w, True, status=st)  # a finite call clears it again
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
 
 
 def test_dequantize_from_oracle_packed(gpu, orc):
@@ -104,3 +107,16 @@ def test_full_size_matrix(gpu, orc, shape):
     ref = orc.quantize(w.cpu().numpy(), True)
     _compare_packed(q, ref, True)
     np.testing.assert_array_equal(bits(d).ravel(), orc.dequantize(ref, "bf16"))
+
+
+@pytest.mark.parametrize("n", [4096 * 16384, 4096 * 16384 + 7, (1 << 27) + 12345])
+def test_mean_over_many_groups(gpu, orc, n):
+    """Matrices with 4096, 4097 and 8193 groups of 16384 weights: the per-thread
+    runs of the mean's pairwise tree hold 16, 32 and 64 group sums (the
+    register form and the stack form of the tree)."""
+    print(f"[storage] mean tree n={n}", flush=True)
+    w = workloads.weight_with_outliers((n,), seed=n % 1000, device="cuda")
+    q = gpu.quantize(w, True)
+    torch.cuda.synchronize()
+    ref = orc.quantize(w.cpu().numpy(), True)
+    _compare_packed(q, ref, True)
