@@ -11,9 +11,11 @@ LoRA r = 16, alpha = 32 on all 7 projections), per projection:
   one launch, fp32 masters and moments)
   nf4_dequantize (packed -> bf16)
 with every input already resident in device memory. Prints one JSON line.
-Outside the timed step it also times the LoRA-FA variant of the optimizer
+Outside the timed step it also runs the standalone quantize/dequantize
+throughput workload (7.5e9 parameters, cold passes; its dequant rate is the
+reported dequant roofline), times the LoRA-FA variant of the optimizer
 step (lorafa_preconditioner once per adapter, then the preconditioned update of
-B) on the rank-64 down_proj shape, and the selected-row decode of packed
+B) on the rank-64 down_proj shape, and times the selected-row decode of packed
 embedding tables (nf4_embedding_rows).
 
 value = algorithmic FLOPs of the step (4MNK + 6Mr(N+K) per projection) /
@@ -45,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=800, help="token rows of the oracle sample")
     p.add_argument("--no-ceilings", action="store_true", help="skip the same-session copy / library GEMM ceilings")
+    p.add_argument("--no-throughput", action="store_true",
+                   help="skip the 7.5e9-parameter quantize/dequantize throughput pass")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
@@ -239,6 +243,60 @@ def embedding_measure(nl, dev, reps: int = 20):
     return res
 
 
+def quant_dequant_throughput(nl, dev, passes: int = 3):
+    """The standalone quantize + dequantize workload: 7,499,415,552 fp32
+    parameters (96 matrices of 4096 x 14336 and 111 of 4096 x 4096, N(0, 0.02)
+    with 1% outliers at 10x), all resident. One pass quantizes (or decodes)
+    every matrix once, back to back, so each pass walks 3.87 GB of packed
+    weights: far more than the 256 MB last-level cache. Each matrix decodes
+    into its own output. HIP events around whole passes on the launch stream."""
+    import torch
+    import workloads
+    mats = workloads.quant_throughput_matrices()
+    W, Q, OUT = [], [], []
+    for i, shape in enumerate(mats):
+        w = workloads.weight_with_outliers(shape, seed=workloads.weight_seed(i), device="cuda")
+        W.append(w)
+        Q.append(nl.NF4Tensor.empty(shape, True, dev))
+        OUT.append(torch.empty(shape, dtype=torch.bfloat16, device=dev))
+    lay = {sh: nl.layout(sh[0] * sh[1], True) for sh in set(mats)}
+    ws = torch.empty(max(l["quantize_workspace_bytes"] for l in lay.values()), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    n_total = sum(a * b for a, b in mats)
+    packed = sum(lay[sh]["codes_bytes"] + lay[sh]["scales_bytes"] + lay[sh]["nested_bytes"] + lay[sh]["offset_bytes"]
+                 for sh in mats)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(fn):
+        fn()  # warm-up pass
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / passes
+
+    def quant_pass():
+        for w, q in zip(W, Q):
+            nl.quantize(w, True, out=q, workspace=ws, status=status)
+
+    def deq_pass():
+        for q, o in zip(Q, OUT):
+            nl.dequantize(q, torch.bfloat16, out=o)
+
+    q_ms = run(quant_pass)
+    assert int(status.item()) == 0
+    d_ms = run(deq_pass)
+    del W, Q, OUT
+    torch.cuda.empty_cache()
+    q_bytes, d_bytes = 4 * n_total + packed, packed + 2 * n_total
+    return {"params": n_total, "matrices": len(mats), "packed_bytes": packed,
+            "dequant_bf16_ms": round(d_ms, 3), "dequant_bf16_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+            "quantize_ms": round(q_ms, 3), "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -372,6 +430,7 @@ def main():
     dq_gbps = dq_bytes / (dq_ms * 1e-3) / 1e9
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
     ad_gbps = ad_bytes / (ad_ms * 1e-3) / 1e9
+    qd = None if args.no_throughput else quant_dequant_throughput(nl, dev)
     fa = lorafa_measure(nl, dev)
     emb = embedding_measure(nl, dev)
 
@@ -401,9 +460,16 @@ def main():
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic(dominant)},
-        "roofline_dequant": {"kernel": "nf4_dequantize (bf16 out)", "bound": "hbm", "achieved": round(dq_gbps, 1),
-                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
-                             "traffic": None},
+        "roofline_dequant": (
+            {"kernel": "nf4_dequantize (bf16 out)", "workload": "7.5e9-parameter quantize/dequantize throughput "
+             "(96 x 4096x14336 + 111 x 4096x4096, cold passes)", "bound": "hbm",
+             "achieved": qd["dequant_bf16_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(qd["dequant_bf16_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
+             "in_layer_step_gbps": round(dq_gbps, 1)} if qd else
+            {"kernel": "nf4_dequantize (bf16 out)", "workload": "the layer step's seven matrices", "bound": "hbm",
+             "achieved": round(dq_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(dq_gbps / PEAK_HBM_GBPS, 4), "traffic": None}),
+        "quant_dequant_throughput": qd,
         "kernels": {"fwd_tflops": round(fwd_tf, 1), "bwd_tflops": round(bwd_tf, 1),
                     "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
                     "grad_ms": round(sum(per["grad"]), 3), "quantize_ms": round(q_ms, 3),
