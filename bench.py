@@ -9,7 +9,7 @@ LoRA r = 16, alpha = 32 on all 7 projections), per projection:
   lora_grad (dA, dB)
   lora_adamw_step_many (fused AdamW update of A and B of all seven adapters in
   one launch, fp32 masters and moments)
-  nf4_dequantize (packed -> bf16)
+  nf4_dequantize_many (packed -> bf16, all seven matrices in one launch)
 with every input already resident in device memory. Prints one JSON line.
 Outside the timed step it also runs the standalone quantize/dequantize
 throughput workload (7.5e9 parameters, cold passes; its dequant rate is the
@@ -243,13 +243,15 @@ def embedding_measure(nl, dev, reps: int = 20):
     return res
 
 
-def quant_dequant_throughput(nl, dev, passes: int = 3):
+def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
     """The standalone quantize + dequantize workload: 7,499,415,552 fp32
     parameters (96 matrices of 4096 x 14336 and 111 of 4096 x 4096, N(0, 0.02)
     with 1% outliers at 10x), all resident. One pass quantizes (or decodes)
     every matrix once, back to back, so each pass walks 3.87 GB of packed
     weights: far more than the 256 MB last-level cache. Each matrix decodes
-    into its own output. HIP events around whole passes on the launch stream."""
+    into its own output. With batch > 1, nf4_dequantize_many decodes that many
+    matrices per launch (slower on matrices this large: one launch per matrix
+    measured 5.70 TB/s against 5.36-5.57 with 16 per launch). HIP events around whole passes on the launch stream."""
     import torch
     import workloads
     mats = workloads.quant_throughput_matrices()
@@ -282,9 +284,12 @@ def quant_dequant_throughput(nl, dev, passes: int = 3):
         for w, q in zip(W, Q):
             nl.quantize(w, True, out=q, workspace=ws, status=status)
 
-    def deq_pass():
-        for q, o in zip(Q, OUT):
-            nl.dequantize(q, torch.bfloat16, out=o)
+    def deq_pass():  # `batch` matrices per launch
+        for i in range(0, len(Q), batch):
+            if batch == 1:
+                nl.dequantize(Q[i], torch.bfloat16, out=OUT[i])
+            else:
+                nl.dequantize_many(Q[i:i + batch], torch.bfloat16, outs=OUT[i:i + batch])
 
     q_ms = run(quant_pass)
     assert int(status.item()) == 0
@@ -347,6 +352,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     adapters = [dict(A=p["A"], dA=p["dA"], mA=p["mA"], vA=p["vA"], B=p["B"], dB=p["dB"], mB=p["mB"], vB=p["vB"])
                 for p in P]
+    wq_all, wd_all = [p["Wq"] for p in P], [p["Wd"] for p in P]
     kinds = ["quantize", "fwd", "bwd", "grad", "adamw", "dequant"]
     opt_step = [0]
 
@@ -376,8 +382,8 @@ def main():
                                                      workspace=p["gws"]))
         # one launch updates all seven adapters
         mark("adamw", 0, lambda: nl.lora_adamw_step_many(adapters, step=t, **ADAMW))
-        for i, p in enumerate(P):
-            mark("dequant", i, lambda p=p: nl.dequantize(p["Wq"], torch.bfloat16, out=p["Wd"]))
+        # one launch decodes all seven matrices
+        mark("dequant", 0, lambda: nl.dequantize_many(wq_all, torch.bfloat16, outs=wd_all))
 
     for _ in range(args.warmup):
         step()
@@ -417,7 +423,7 @@ def main():
         n = L.n_out * L.k_in
         pb = packed_bytes(n, nl)
         dq_bytes += pb + 2 * n
-        dq_ms += per["dequant"][i]
+        dq_ms += per["dequant"][i]  # the whole decode is recorded at index 0
         q_bytes += 4 * n + pb
         q_ms += per["quantize"][i]
         ad_bytes += ADAMW_BYTES * r * (L.k_in + L.n_out)
@@ -461,12 +467,13 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic(dominant)},
         "roofline_dequant": (
-            {"kernel": "nf4_dequantize (bf16 out)", "workload": "7.5e9-parameter quantize/dequantize throughput "
+            {"kernel": "nf4_dequantize (bf16 out, one launch per matrix)",
+             "workload": "7.5e9-parameter quantize/dequantize throughput "
              "(96 x 4096x14336 + 111 x 4096x4096, cold passes)", "bound": "hbm",
              "achieved": qd["dequant_bf16_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
              "frac": round(qd["dequant_bf16_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
              "in_layer_step_gbps": round(dq_gbps, 1)} if qd else
-            {"kernel": "nf4_dequantize (bf16 out)", "workload": "the layer step's seven matrices", "bound": "hbm",
+            {"kernel": "nf4_dequantize_many (bf16 out)", "workload": "the layer step's seven matrices", "bound": "hbm",
              "achieved": round(dq_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
              "frac": round(dq_gbps / PEAK_HBM_GBPS, 4), "traffic": None}),
         "quant_dequant_throughput": qd,
@@ -476,7 +483,8 @@ def main():
                     "quantize_gbps": round(q_gbps, 1), "dequant_ms": round(dq_ms, 3),
                     "dequant_gbps": round(dq_gbps, 1), "adamw_ms": round(ad_ms, 4),
                     "adamw_gbps": round(ad_gbps, 1),
-                    "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds if k != "adamw"}},
+                    "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds
+                                          if k not in ("adamw", "dequant")}},
         "roofline_adamw": {"kernel": "lora_adamw_step_many (A and B of all 7 adapters, one launch)",
                            "bound": "hbm", "achieved": round(ad_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                            "frac": round(ad_gbps / PEAK_HBM_GBPS, 4), "traffic": None,

@@ -135,6 +135,19 @@ int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* 
  * w_hat = fl32(C4[code] * a'_b), bf16 by round-to-nearest-even. */
 int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream);
 
+#define NF4_MAX_TENSORS_PER_CALL 16
+
+/* nf4_dequantize for `count` (1 to NF4_MAX_TENSORS_PER_CALL) packed matrices
+ * in one kernel launch, all to out_dtype: outs[i] (device, 16-byte aligned)
+ * receives the tensors[i].n decoded weights of tensors[i]. `tensors` and `outs`
+ * are host arrays read during the call; each tensor is validated as
+ * nf4_dequantize validates its argument, single and double quantization may
+ * be mixed, and the outputs must not overlap. The results equal `count`
+ * separate nf4_dequantize calls bit for bit; one launch decodes a layer's
+ * matrices without a launch tail per matrix. */
+int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t count, nf4_dtype out_dtype,
+                        nf4_stream_t stream);
+
 /* Selected rows of a packed embedding table (Aner docs "Native model
  * adaptation and NF4": section "Packed NF4 and the portable QLoRA profile",
  * embeddings decode only the selected rows; section "Fused GPU NF4 decodes

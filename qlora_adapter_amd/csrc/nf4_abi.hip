@@ -142,6 +142,22 @@ int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stre
   return launch_dequantize(w, out_dtype, out, as_stream(stream));
 }
 
+int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t count, nf4_dtype out_dtype,
+                        nf4_stream_t stream) {
+  if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;
+  if (!tensors || !outs || count < 1 || count > NF4_MAX_TENSORS_PER_CALL) return NF4_EINVAL;
+  int64_t groups = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (!outs[i]) return NF4_EINVAL;
+    if (int rc = check_tensor(&tensors[i], tensors[i].n)) return rc;
+    if (!aligned(outs[i], 16)) return NF4_EALIGN;
+    groups += ceil_div(tensors[i].n / 8 > 0 ? tensors[i].n / 8 : 1, 2048);
+  }
+  if (groups >= (int64_t(1) << 31)) return NF4_EINVAL;
+  if (int rc = check_device()) return rc;
+  return launch_dequantize_many(tensors, outs, count, out_dtype, as_stream(stream));
+}
+
 int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype out_dtype,
                        void* out, int32_t* status, nf4_stream_t stream) {
   if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;

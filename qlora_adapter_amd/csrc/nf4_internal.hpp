@@ -32,6 +32,7 @@ inline size_t quantize_ws_bytes(int64_t n, int dq) {
 // Launchers (return NF4_OK or NF4_EDEVICE). Arguments are already validated.
 int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s);
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s);
+int launch_dequantize_many(const nf4_tensor* t, void* const* outs, int32_t count, nf4_dtype dt, hipStream_t s);
 int launch_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype dt,
                           void* out, int32_t* status, hipStream_t s);
 

@@ -284,27 +284,27 @@ __global__ __launch_bounds__(256) void k_dq_nested(const double* __restrict__ pa
 // group 0.
 constexpr int DQ_UNITS = 8;
 
+// Workgroup `group` of one matrix's decode (the grid of k_dequantize, or a
+// range of k_dequantize_many's). The LDS arrays are the caller's.
 template <bool DQ, bool BF16>
-__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
-                                                    const float* __restrict__ nested, const float* __restrict__ offset,
-                                                    int64_t n, void* __restrict__ out) {
-  __shared__ float lut[16];
+__device__ __forceinline__ void dequant_group(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                              const float* __restrict__ nested, const float* __restrict__ offset,
+                                              int64_t n, void* __restrict__ out, int64_t group, float* lut, float* sc) {
   constexpr int BLOCKS = 4 * 64 * DQ_UNITS / 8;  // blocks covered by one workgroup
-  __shared__ float sc[BLOCKS];
   if (threadIdx.x < 16) lut[threadIdx.x] = nf4_value(threadIdx.x);
   const float mu = DQ ? offset[0] : 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t units = n / 8, nb = (n + 63) / 64;
-  const int64_t ubase = ((int64_t)blockIdx.x * 4 + wave) * (64 * DQ_UNITS) + lane;
+  const int64_t ubase = (group * 4 + wave) * (64 * DQ_UNITS) + lane;
   const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
   uint32_t word[DQ_UNITS];
 #pragma unroll
   for (int q = 0; q < DQ_UNITS; ++q) {
     const int64_t u = ubase + 64 * q;
-    word[q] = (u < units) ? words[u] : 0u;
+    word[q] = (u < units) ? __builtin_nontemporal_load(&words[u]) : 0u;  // codes are read once
   }
   for (int t = threadIdx.x; t < BLOCKS; t += 256) {
-    const int64_t b = (int64_t)blockIdx.x * BLOCKS + t;  // block of the group's range
+    const int64_t b = group * BLOCKS + t;  // block of the group's range
     float a = 0.0f;
     if (b < nb) {
       if (DQ) {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
       __builtin_nontemporal_store((f4v{v[4], v[5], v[6], v[7]}), o + 1);
     }
   }
-  if (blockIdx.x == 0) {
+  if (group == 0) {
     for (int64_t e = units * 8 + threadIdx.x; e < n; e += blockDim.x) {
       const int64_t b = e >> 6;
       const float a = DQ ? __fadd_rn(__fmul_rn(dyn8_value(static_cast<const uint8_t*>(scales)[b]), nested[b >> 8]), mu)
@@ -358,6 +358,46 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
         static_cast<float*>(out)[e] = v;
     }
   }
+}
+
+template <bool DQ, bool BF16>
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                                    const float* __restrict__ nested, const float* __restrict__ offset,
+                                                    int64_t n, void* __restrict__ out) {
+  __shared__ float lut[16];
+  __shared__ float sc[4 * 64 * DQ_UNITS / 8];
+  dequant_group<DQ, BF16>(codes, scales, nested, offset, n, out, blockIdx.x, lut, sc);
+}
+
+// Up to NF4_MAX_TENSORS_PER_CALL matrices in one grid; the table travels in the
+// kernel arguments and matrix k owns workgroups [group0, next group0).
+struct DequantItem {
+  const uint8_t* codes;
+  const void* scales;
+  const float* nested;
+  const float* offset;
+  void* out;
+  int64_t n;
+  int64_t group0;
+  int32_t dq;
+};
+struct DequantTable {
+  DequantItem item[NF4_MAX_TENSORS_PER_CALL];
+  int32_t count;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequantize_many(DequantTable tab) {
+  __shared__ float lut[16];
+  __shared__ float sc[4 * 64 * DQ_UNITS / 8];
+  const int64_t b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < tab.count && b >= tab.item[k + 1].group0) ++k;
+  const DequantItem& it = tab.item[k];
+  if (it.dq)
+    dequant_group<true, BF16>(it.codes, it.scales, it.nested, it.offset, it.n, it.out, b - it.group0, lut, sc);
+  else
+    dequant_group<false, BF16>(it.codes, it.scales, it.nested, it.offset, it.n, it.out, b - it.group0, lut, sc);
 }
 
 // Selected rows of a packed [V, D] table: out[t, :] = decoded row ids[t], the
@@ -492,9 +532,29 @@ int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, in
   return launch_status();
 }
 
+static int64_t dequant_groups(int64_t n) {
+  const int64_t units = n / 8;
+  return units > 0 ? ceil_div(units, 4 * 64 * DQ_UNITS) : 1;
+}
+
+int launch_dequantize_many(const nf4_tensor* t, void* const* outs, int32_t count, nf4_dtype dt, hipStream_t s) {
+  DequantTable tab{};
+  int64_t groups = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    tab.item[i] = DequantItem{t[i].codes, t[i].scales, t[i].nested, t[i].offset, outs[i], t[i].n, groups,
+                              t[i].double_quant};
+    groups += dequant_groups(t[i].n);
+  }
+  tab.count = count;
+  if (dt == NF4_BF16)
+    hipLaunchKernelGGL(k_dequantize_many<true>, dim3((unsigned)groups), dim3(256), 0, s, tab);
+  else
+    hipLaunchKernelGGL(k_dequantize_many<false>, dim3((unsigned)groups), dim3(256), 0, s, tab);
+  return launch_status();
+}
+
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s) {
-  const int64_t units = t->n / 8;
-  const unsigned groups = (unsigned)(units > 0 ? ceil_div(units, 4 * 64 * DQ_UNITS) : 1);
+  const unsigned groups = (unsigned)dequant_groups(t->n);
   const bool dq = t->double_quant != 0;
   if (dq && dt == NF4_BF16)
     hipLaunchKernelGGL((k_dequantize<true, true>), dim3(groups), dim3(256), 0, s, t->codes, t->scales, t->nested,

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
 NF4_F32, NF4_BF16 = 0, 1
 _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
-EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_embedding_rows", "nf4_linear_fwd",
+EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_dequantize_many",
+           "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "nf4_status_string",
            "nf4lora_abi_version"]
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
             lib.nf4_code_tables.argtypes = [P, P]
             lib.nf4_quantize.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, ctypes.c_size_t, P, P]
             lib.nf4_dequantize.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, P, P]
+            lib.nf4_dequantize_many.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(ctypes.c_void_p), I32,
+                                                ctypes.c_int, P]
             lib.nf4_embedding_rows.argtypes = [ctypes.POINTER(_Tensor), I64, I64, P, I64, ctypes.c_int, P, P, P]
             lib.nf4_linear_fwd.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32, F, P,
                                            P, P]
@@ -220,6 +223,23 @@ def dequantize(t: NF4Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] =
     st = t.c_struct()
     _check("nf4_dequantize", load().nf4_dequantize(ctypes.byref(st), _DT[dtype], _ptr(out), _stream(t.device)))
     return out
+
+
+MAX_TENSORS_PER_CALL = 16
+
+
+def dequantize_many(tensors, dtype=torch.bfloat16, outs=None):
+    """nf4_dequantize of up to 16 packed tensors in one launch; returns the outputs."""
+    tensors = list(tensors)
+    if outs is None:
+        outs = [torch.empty(t.shape, dtype=dtype, device=t.device) for t in tensors]
+    for o in outs:
+        _dev(o, "out", dtype)
+    arr = (_Tensor * len(tensors))(*[t.c_struct() for t in tensors])
+    ptrs = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    _check("nf4_dequantize_many", load().nf4_dequantize_many(arr, ptrs, len(tensors), _DT[dtype],
+                                                             _stream(tensors[0].device)))
+    return outs
 
 
 def embedding_rows(E: NF4Tensor, ids: torch.Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,

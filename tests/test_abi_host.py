@@ -184,3 +184,20 @@ def test_many_adapter_step_argument_errors(lib):
     assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good, {**good, "precond": 256}), 2, None, None) == EINVAL
     assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good, {**good, "vB": 264}), 2, None, None) == EALIGN
     assert L.lora_adamw_step_many(ctypes.byref(opt), arr(good), 1, 258, None) == EALIGN
+
+
+def test_dequantize_many_argument_errors(lib):
+    L, m = lib
+    EINVAL, EALIGN, EUNSUP = -1, -2, -3
+    arr = lambda *ts: (m._Tensor * len(ts))(*ts)
+    outs = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    good = m._Tensor(16, 16, 16, 16, 100, 1)
+    assert L.nf4_dequantize_many(arr(good), outs(256), 1, 9, None) == EUNSUP
+    assert L.nf4_dequantize_many(None, outs(256), 1, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(good), None, 1, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(good), outs(256), 0, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(*[good] * 17), outs(*[256] * 17), 17, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(good, good), outs(256, None), 2, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(good, m._Tensor(16, 16, 16, 16, 0, 1)), outs(256, 256), 2, 1, None) == EINVAL
+    assert L.nf4_dequantize_many(arr(good, m._Tensor(17, 16, 16, 16, 64, 1)), outs(256, 256), 2, 1, None) == EALIGN
+    assert L.nf4_dequantize_many(arr(good), outs(264), 1, 1, None) == EALIGN

@@ -120,3 +120,23 @@ def test_mean_over_many_groups(gpu, orc, n):
     torch.cuda.synchronize()
     ref = orc.quantize(w.cpu().numpy(), True)
     _compare_packed(q, ref, True)
+
+
+def test_dequantize_many_equals_single_calls(gpu, orc):
+    """One launch over mixed tensors (double and single quantization, sizes with
+    tails, one tiny) equals per-tensor nf4_dequantize bit for bit, and the
+    oracle for two of them."""
+    sizes = [(64 * 5000 + 3, True), (1, True), (4096 * 37 + 5, False), (16384 * 3, True), (127, False),
+             (1536 * 576, True)]
+    ws = [workloads.weight_with_outliers((n,), seed=i + 11).numpy() for i, (n, _) in enumerate(sizes)]
+    qs = [gpu.quantize(torch.from_numpy(w).cuda(), dq) for w, (_, dq) in zip(ws, sizes)]
+    for dtype in (torch.bfloat16, torch.float32):
+        many = gpu.dequantize_many(qs, dtype)
+        single = [gpu.dequantize(q, dtype) for q in qs]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(many, single)):
+            assert torch.equal(a.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                               b.view(torch.int16 if dtype == torch.bfloat16 else torch.int32)), (i, dtype)
+    for i in (0, 2):
+        ref = orc.quantize(ws[i], sizes[i][1])
+        np.testing.assert_array_equal(bits(many[i]), orc.dequantize(ref, "f32").view(np.uint32))
