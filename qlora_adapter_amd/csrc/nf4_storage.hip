@@ -218,15 +218,31 @@ __device__ double pairwise_sum_wg(const double* __restrict__ partials, int64_t C
   return (s_wave[0] + s_wave[1]) + (s_wave[2] + s_wave[3]);
 }
 
-// Double quantization after k_quantize. Every workgroup forms the matrix mean
-// mu = fp32(S / nb) from the group partial sums itself (the same code and order
-// in every workgroup, so the same value), then each wave handles nested blocks
-// j = 16 g + 4 i + w, i < 4: lane l holds maxima 4l..4l+3 of the block,
-// c = fl32(absmax - mu), nested[j] = max |c|, qabs = dynamic8 code of c / m.
-// Workgroup 0 also writes the offset and the status word (NF4_ENONFINITE when
-// S is not finite, i.e. some weight was not finite, else 0).
-constexpr int DQN_PER_WG = 4;
+// The matrix mean for large matrices: one workgroup forms mu = fp32(S / nb)
+// from the group partial sums and writes the offset and the status word
+// (NF4_ENONFINITE when S is not finite, i.e. some weight was not finite).
+__global__ __launch_bounds__(256) void k_dq_mean(const double* __restrict__ partials, int64_t C, int64_t nb,
+                                                 float* __restrict__ offset, int32_t* __restrict__ status) {
+  __shared__ double s_wave[4];
+  const double S = pairwise_sum_wg(partials, C, s_wave);
+  if (threadIdx.x == 0) {
+    offset[0] = (float)(S / (double)nb);
+    if (status) *status = isfinite(S) ? 0 : NF4_ENONFINITE;
+  }
+}
 
+// Double quantization after k_quantize. With FUSED_MEAN (matrices of at most
+// kFusedMeanGroups groups) every workgroup forms the matrix mean from the group
+// partial sums itself (the same code and order as k_dq_mean, so the same
+// value) and workgroup 0 writes the offset and the status word; otherwise the
+// mean comes from k_dq_mean through `offset`. Each wave handles nested blocks
+// j = 16 g + 4 i + w, i < DQN_PER_WG / 4: lane l holds maxima 4l..4l+3 of the
+// block, c = fl32(absmax - mu), nested[j] = max |c|, qabs = dynamic8 code of
+// c / m.
+constexpr int DQN_PER_WG = 4;
+constexpr int64_t kFusedMeanGroups = 1024;
+
+template <bool FUSED_MEAN>
 __global__ __launch_bounds__(256) void k_dq_nested(const double* __restrict__ partials, int64_t C,
                                                    const float* __restrict__ absmax, int64_t nb,
                                                    float* __restrict__ offset, uint8_t* __restrict__ qabs,
@@ -243,11 +259,16 @@ __global__ __launch_bounds__(256) void k_dq_nested(const double* __restrict__ pa
 #pragma unroll
     for (int q = 0; q < 4; ++q) am[i][q] = (b0 + q < nb) ? absmax[b0 + q] : 0.0f;
   }
-  const double S = pairwise_sum_wg(partials, C, s_wave);
-  const float mu = (float)(S / (double)nb);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    offset[0] = mu;
-    if (status) *status = isfinite(S) ? 0 : NF4_ENONFINITE;
+  float mu;
+  if constexpr (FUSED_MEAN) {
+    const double S = pairwise_sum_wg(partials, C, s_wave);
+    mu = (float)(S / (double)nb);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      offset[0] = mu;
+      if (status) *status = isfinite(S) ? 0 : NF4_ENONFINITE;
+    }
+  } else {
+    mu = offset[0];
   }
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
@@ -527,8 +548,15 @@ int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, in
   double* partials = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)nb, 256));
   hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)groups), dim3(256), 0, s, w, n, t->codes, absmax, partials,
                      nullptr);
-  hipLaunchKernelGGL(k_dq_nested, dim3((unsigned)ceil_div(nn, DQN_PER_WG)), dim3(256), 0, s, partials, nn, absmax, nb,
-                     t->offset, static_cast<uint8_t*>(t->scales), t->nested, st);
+  const dim3 ng((unsigned)ceil_div(nn, DQN_PER_WG));
+  if (nn <= kFusedMeanGroups) {
+    hipLaunchKernelGGL(k_dq_nested<true>, ng, dim3(256), 0, s, partials, nn, absmax, nb, t->offset,
+                       static_cast<uint8_t*>(t->scales), t->nested, st);
+  } else {
+    hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, partials, nn, nb, t->offset, st);
+    hipLaunchKernelGGL(k_dq_nested<false>, ng, dim3(256), 0, s, partials, nn, absmax, nb, t->offset,
+                       static_cast<uint8_t*>(t->scales), t->nested, st);
+  }
   return launch_status();
 }
 

@@ -109,9 +109,11 @@ def test_full_size_matrix(gpu, orc, shape):
     np.testing.assert_array_equal(bits(d).ravel(), orc.dequantize(ref, "bf16"))
 
 
-@pytest.mark.parametrize("n", [4096 * 16384, 4096 * 16384 + 7, (1 << 27) + 12345])
+@pytest.mark.parametrize("n", [1024 * 16384, 1024 * 16384 + 1, 4096 * 16384, 4096 * 16384 + 7, (1 << 27) + 12345])
 def test_mean_over_many_groups(gpu, orc, n):
-    """Matrices with 4096, 4097 and 8193 groups of 16384 weights: the per-thread
+    """Matrices with 1024 and 1025 groups of 16384 weights (the largest with
+    the mean formed in every nested-block workgroup, the smallest with the
+    separate mean kernel), and with 4096, 4097 and 8193 groups: the per-thread
     runs of the mean's pairwise tree hold 16, 32 and 64 group sums (the
     register form and the stack form of the tree)."""
     print(f"[storage] mean tree n={n}", flush=True)
