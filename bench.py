@@ -15,8 +15,10 @@ Outside the timed step it also runs the standalone quantize/dequantize
 throughput workload (7.5e9 parameters, cold passes; its dequant rate is the
 reported dequant roofline), times the LoRA-FA variant of the optimizer
 step (lorafa_preconditioner once per adapter, then the preconditioned update of
-B) on the rank-64 down_proj shape, and times the selected-row decode of packed
-embedding tables (nf4_embedding_rows).
+B) on the rank-64 down_proj shape, times the selected-row decode of packed
+embedding tables (nf4_embedding_rows), and reports the other configurations of
+the workload table (the 576x576 layer, the SmolLM2 stack, the backward-heavy
+rank-64 down_proj).
 
 value = algorithmic FLOPs of the step (4MNK + 6Mr(N+K) per projection) /
 step time: whole-step throughput including the quantize and dequantize work.
@@ -170,11 +172,11 @@ def cpu_baseline(layers, M, r, s, rows):
                 seconds=round(t_total, 2))
 
 
-def gpu_time_ms(fn, dev, reps: int = 20) -> float:
-    """Mean device time of fn() over `reps` back-to-back calls. A ~1 ms bf16
-    GEMM is queued first, so the calls are all enqueued before the GPU reaches
-    the start event and host-side call overhead does not leave gaps in the
-    measured region. HIP events on the launch stream."""
+def gpu_time_ms(fn, dev, reps: int = 20, block: int = 1) -> float:
+    """Mean device time of fn() over `reps` back-to-back calls. `block` bf16
+    GEMMs of ~1 ms each are queued first, so the calls are all enqueued before
+    the GPU reaches the start event and host-side call overhead does not leave
+    gaps in the measured region. HIP events on the launch stream."""
     import torch
     for _ in range(3):
         fn()
@@ -182,7 +184,8 @@ def gpu_time_ms(fn, dev, reps: int = 20) -> float:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.matmul(a, a)
+    for _ in range(block):
+        torch.matmul(a, a)
     e0.record(stream)
     for _ in range(reps):
         fn()
@@ -300,6 +303,89 @@ def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
     return {"params": n_total, "matrices": len(mats), "packed_bytes": packed,
             "dequant_bf16_ms": round(d_ms, 3), "dequant_bf16_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
             "quantize_ms": round(q_ms, 3), "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
+
+
+def other_configs(nl, dev):
+    """The other configurations of the workload table, each timed with
+    gpu_time_ms (device time of back-to-back calls):
+      single_576: one 576x576 layer, 512 tokens, r = 16: latency of the forward,
+        the input gradient and the LoRA gradients;
+      smollm2_stack: 30 SmolLM2-shaped layers (7 linears each, LoRA r = 8 on q
+        and v), 512 tokens: one forward + input-gradient + LoRA-gradient pass
+        over all 210 linears, as TFLOP/s and microseconds per layer (device time
+        with the launches queued back to back, as a captured graph would run);
+      down_proj_bwd: down_proj [4096, 14336], 8192 tokens, rank-64 rsLoRA: the
+        input gradient (with U), the LoRA gradients and the LoRA-FA dB alone."""
+    import torch
+    import workloads
+
+    def setup(layers, M, alpha, rslora, dy_std=1.0, seed0=0):
+        out = []
+        for i, L in enumerate(layers):
+            inp = workloads.lora_inputs(L, M, seed_offset=seed0 + i, device="cuda", dy_std=dy_std)
+            W = workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(seed0 + i), "cuda")
+            r = L.lora_rank
+            s = nl.lora_scale(alpha, r, rslora) if r else 0.0
+            e = dict(L=L, x=inp["x"], dy=inp["dy"], Wq=nl.quantize(W, True), s=s, r=r,
+                     A=inp.get("A"), B=inp.get("B"))
+            e["y"], e["T"] = nl.linear_fwd(e["x"], e["Wq"], e["A"], e["B"], s)
+            e["dx"], e["U"] = nl.linear_bwd_input(e["dy"], e["Wq"], e["A"], e["B"], s)
+            if r:
+                e["dA"], e["dB"] = nl.lora_grad(e["x"], e["dy"], e["T"], e["U"], s)
+                e["ws"] = torch.empty(nl.lora_grad_workspace_bytes(M, L.k_in, L.n_out, r), dtype=torch.uint8,
+                                      device=dev)
+            out.append(e)
+        return out
+
+    fwd = lambda e: nl.linear_fwd(e["x"], e["Wq"], e["A"], e["B"], e["s"], y=e["y"], t_out=e["T"])
+    bwd = lambda e: nl.linear_bwd_input(e["dy"], e["Wq"], e["A"], e["B"], e["s"], dx=e["dx"], u_out=e["U"])
+    grad = lambda e: nl.lora_grad(e["x"], e["dy"], e["T"], e["U"], e["s"], dA=e["dA"], dB=e["dB"],
+                                  workspace=e["ws"])
+    res = {}
+
+    wl = workloads.WORKLOADS["single_576"]
+    (e,) = setup(wl["layers"], wl["tokens"], wl["alpha"], wl["rslora"])
+    tf, tb, tg = gpu_time_ms(lambda: fwd(e), dev), gpu_time_ms(lambda: bwd(e), dev), gpu_time_ms(lambda: grad(e), dev)
+    res["single_576"] = {"tokens": wl["tokens"], "rank": 16, "fwd_us": round(tf * 1e3, 2), "bwd_input_us": round(tb * 1e3, 2),
+                         "lora_grad_us": round(tg * 1e3, 2), "total_us": round((tf + tb + tg) * 1e3, 2)}
+
+    wl = workloads.WORKLOADS["smollm2_stack"]
+    M = wl["tokens"]
+    E = setup(wl["layers"], M, wl["alpha"], wl["rslora"])
+
+    def stack_pass():
+        for e in E:
+            fwd(e)
+        for e in reversed(E):
+            bwd(e)
+            if e["r"]:
+                grad(e)
+    # 480 calls per pass: queue ~70 ms of GEMMs first so that all five passes are enqueued before timing starts
+    ms = gpu_time_ms(stack_pass, dev, reps=5, block=70)
+    flops = sum(4 * M * e["L"].n_out * e["L"].k_in + (6 * M * e["r"] * (e["L"].n_out + e["L"].k_in) if e["r"] else 0)
+                for e in E)
+    res["smollm2_stack"] = {"tokens": M, "linears": len(E), "pass_ms": round(ms, 3),
+                            "us_per_layer": round(ms * 1e3 / 30, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                            "gflop": round(flops / 1e9, 1)}
+    del E
+
+    wl = workloads.WORKLOADS["down_proj_bwd"]
+    M = wl["tokens"]
+    (e,) = setup(wl["layers"], M, wl["alpha"], wl["rslora"], dy_std=wl.get("dy_std", 1.0))
+    L, r = e["L"], e["r"]
+    ws_fa = torch.empty(nl.lora_grad_workspace_bytes(M, L.k_in, L.n_out, r, fa=True), dtype=torch.uint8, device=dev)
+    tb = gpu_time_ms(lambda: bwd(e), dev, reps=10)
+    tg = gpu_time_ms(lambda: grad(e), dev, reps=10)
+    tfa = gpu_time_ms(lambda: nl.lora_grad(e["x"], e["dy"], e["T"], None, e["s"], fa=True, dB=e["dB"], workspace=ws_fa),
+                      dev, reps=10)
+    bwd_flops = 2 * M * L.n_out * L.k_in + 2 * M * r * (L.n_out + L.k_in)
+    res["down_proj_bwd"] = {"tokens": M, "rank": r, "scale": e["s"], "bwd_input_ms": round(tb, 3),
+                            "bwd_input_tflops": round(bwd_flops / (tb * 1e-3) / 1e12, 1),
+                            "lora_grad_ms": round(tg, 3), "lora_fa_dB_ms": round(tfa, 3),
+                            "lora_grad_gbps": round(2 * M * (L.k_in + L.n_out) / (tg * 1e-3) / 1e9, 1)}
+    del e
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -439,6 +525,7 @@ def main():
     qd = None if args.no_throughput else quant_dequant_throughput(nl, dev)
     fa = lorafa_measure(nl, dev)
     emb = embedding_measure(nl, dev)
+    others = other_configs(nl, dev)
 
     ceil = None if args.no_ceilings else ceilings()
     cpu = None
@@ -491,6 +578,7 @@ def main():
                            "note": "28 B per parameter, 1.31 M parameters (36.7 MB) per launch"},
         "lorafa": fa,
         "embedding_rows": emb,
+        "other_configs": others,
         "ceilings": ceil,
         "cpu_baseline": cpu,
     }

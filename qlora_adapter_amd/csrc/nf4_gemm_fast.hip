@@ -1040,10 +1040,17 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
       hipLaunchKernelGGL((k_bwd<false, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s,       \
                          g.side, dx);                                                                           \
   } while (0)
+    // Smaller token tiles when the 128-token tiles would leave most CUs idle
+    // (short sequences): more workgroups, each with the same K loop.
+    const int64_t kt = ceil_div(g.K, 128);
     if (big)
       NF4_BWD(8);
-    else
+    else if (ceil_div(g.M, 128) * kt >= 200)
       NF4_BWD(4);
+    else if (ceil_div(g.M, 64) * kt >= 200)
+      NF4_BWD(2);
+    else
+      NF4_BWD(1);
 #undef NF4_BWD
     return launch_status();
   }
@@ -1061,10 +1068,15 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
       hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,    \
                          g.side, y);                                                                            \
   } while (0)
+  const int64_t nt = ceil_div(g.N, 128);
   if (wg21 >= 224)
     NF4_FWD(8, 1);
-  else
+  else if (ceil_div(g.M, 128) * nt >= 200)
     NF4_FWD(4, 1);
+  else if (ceil_div(g.M, 64) * nt >= 200)
+    NF4_FWD(2, 1);
+  else
+    NF4_FWD(1, 1);
 #undef NF4_FWD
   return launch_status();
 }

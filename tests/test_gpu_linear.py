@@ -188,3 +188,31 @@ def test_fused_decode_bitexact_bwd(gpu, K, N, dq):
     d = gpu.dequantize(Wq, torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(dx, d)
+
+
+def test_backward_heavy_down_proj(gpu, orc):
+    """The backward-heavy configuration: down_proj W [4096, 14336], 8192 tokens,
+    dY ~ N(0, 0.01), rank-64 rsLoRA with alpha 16, in the launch configuration
+    the benchmark times. dX and U on 24 sampled token rows; dA and dB in full,
+    then the LoRA-FA variant (dB only, bit-identical to the full call's dB)."""
+    print("[linear] backward-heavy down_proj 8192 tokens r=64", flush=True)
+    wl = workloads.WORKLOADS["down_proj_bwd"]
+    L = wl["layers"][0]
+    M, r = wl["tokens"], L.lora_rank
+    s = gpu.lora_scale(wl["alpha"], r, rslora=wl["rslora"])
+    c = make_case(M, L.k_in, L.n_out, r, torch.bfloat16, seed=21, dy_std=wl["dy_std"])
+    Wq, y, T, dx, U, (dA, dB) = run_all(gpu, c, s)
+    _, dB_fa = gpu.lora_grad(c["x"], c["dy"], T, None, s, fa=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dB.view(torch.int32), dB_fa.view(torch.int32))
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16)
+    rows = np.sort(np.random.default_rng(5).choice(M, 24, replace=False))
+    dy = to_np(c["dy"])
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    dx_ref, U_ref = orc.linear_bwd_input(dy[rows], Wref, A, B, s)
+    assert_close(to_np(dx)[rows], dx_ref, "bf16", "dx rows")
+    assert_close(U.cpu().numpy()[rows], U_ref, "f32", "U rows")
+    dA_ref, dB_ref = orc.lora_grad(to_np(c["x"]), dy, T.cpu().numpy().astype(np.float64),
+                                   U.cpu().numpy().astype(np.float64), s)
+    assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
+    assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
