@@ -16,7 +16,8 @@ throughput workload (7.5e9 parameters, cold passes; its dequant rate is the
 reported dequant roofline), times the LoRA-FA variant of the optimizer
 step (lorafa_preconditioner once per adapter, then the preconditioned update of
 B) on the rank-64 down_proj shape, times the selected-row decode of packed
-embedding tables (nf4_embedding_rows), and reports the other configurations of
+embedding tables (nf4_embedding_rows) and the AdamW update with paged host
+moments (lora_adamw_step_paged), and reports the other configurations of
 the workload table (the 576x576 layer, the SmolLM2 stack, the backward-heavy
 rank-64 down_proj).
 
@@ -220,6 +221,45 @@ def lorafa_measure(nl, dev, reps: int = 20):
     return {"shape": f"A [{r}, {K}] frozen, B [{N}, {r}], s = {s}", "preconditioner_us": round(pre_ms * 1e3, 1),
             "preconditioned_update_us": round(upd_ms * 1e3, 2),
             "preconditioned_update_gbps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1)}
+
+
+def paged_adamw_measure(nl, dev, reps: int = 10):
+    """The AdamW update of the seven Llama-8B adapters (r = 16) with the moments
+    in pinned host memory, moved in 2 MiB pages (lora_adamw_step_paged), against
+    the same update with device-resident moments. Per update 16 bytes of moments
+    per parameter cross PCIe (m and v, in and out)."""
+    import torch
+    import workloads
+    ads_dev, ads_host = [], []
+    for i, L in enumerate(workloads.llama8b_layer()):
+        r = L.lora_rank
+        d = dict(A=workloads.normal_f32((r, L.k_in), 1.0 / r, 2 + 10 * i, "cuda"),
+                 B=workloads.normal_f32((L.n_out, r), 0.01, 3 + 10 * i, "cuda"))
+        d["dA"] = workloads.normal_f32((r, L.k_in), 1e-3, 70 + i, "cuda")
+        d["dB"] = workloads.normal_f32((L.n_out, r), 1e-3, 80 + i, "cuda")
+        for k, shape in (("mA", (r, L.k_in)), ("vA", (r, L.k_in)), ("mB", (L.n_out, r)), ("vB", (L.n_out, r))):
+            d[k] = torch.zeros(shape, dtype=torch.float32, device=dev)
+        h = dict(d)
+        for k in ("mA", "vA", "mB", "vB"):
+            h[k] = torch.zeros(d[k].shape, dtype=torch.float32, pin_memory=True)
+        ads_dev.append(d)
+        ads_host.append(h)
+    page = 2 << 20
+    staging = torch.empty(2 * page, dtype=torch.uint8, device=dev)
+    k = [0]
+
+    def paged():
+        k[0] += 1
+        nl.lora_adamw_step_paged(ads_host, step=k[0], staging=staging, page_bytes=page, **ADAMW)
+
+    def resident():
+        k[0] += 1
+        nl.lora_adamw_step_many(ads_dev, step=k[0], **ADAMW)
+    t_p = gpu_time_ms(paged, dev, reps)
+    t_d = gpu_time_ms(resident, dev, reps)
+    params = sum(a["A"].numel() + a["B"].numel() for a in ads_dev)
+    return {"params": params, "page_bytes": page, "paged_ms": round(t_p, 3), "resident_ms": round(t_d, 4),
+            "pcie_gbps": round(16 * params / (t_p * 1e-3) / 1e9, 1)}
 
 
 def embedding_measure(nl, dev, reps: int = 20):
@@ -525,6 +565,7 @@ def main():
     qd = None if args.no_throughput else quant_dequant_throughput(nl, dev)
     fa = lorafa_measure(nl, dev)
     emb = embedding_measure(nl, dev)
+    paged = paged_adamw_measure(nl, dev)
     others = other_configs(nl, dev)
 
     ceil = None if args.no_ceilings else ceilings()
@@ -578,6 +619,7 @@ def main():
                            "note": "28 B per parameter, 1.31 M parameters (36.7 MB) per launch"},
         "lorafa": fa,
         "embedding_rows": emb,
+        "paged_adamw": paged,
         "other_configs": others,
         "ceilings": ceil,
         "cpu_baseline": cpu,

@@ -233,6 +233,15 @@ int check_adamw(const nf4_adamw* opt) {
   return NF4_OK;
 }
 
+bool is_pinned_host(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error an unknown (pageable) pointer leaves
+    return false;
+  }
+  return at.type == hipMemoryTypeHost;
+}
+
 int check_lora_state(const nf4_lora_state& a) {
   constexpr int64_t kMaxEntries = int64_t(1) << 40;
   const int32_t r = a.r;
@@ -261,6 +270,27 @@ int lora_adamw_step(const nf4_adamw* opt, int32_t r, int64_t K, int64_t N, float
   if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
   return launch_lora_adamw(*opt, &a, 1, grad_scale, as_stream(stream));
+}
+
+int lora_adamw_step_paged(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,
+                          const float* grad_scale, void* staging, size_t staging_bytes, size_t page_bytes,
+                          nf4_stream_t stream) {
+  if (int rc = check_adamw(opt)) return rc;
+  if (!adapters || count < 1 || count > NF4_MAX_ADAPTERS_PER_CALL) return NF4_EINVAL;
+  if (page_bytes < 4096 || page_bytes > (size_t(64) << 20) || page_bytes % 4096 != 0) return NF4_EINVAL;
+  if (!staging || staging_bytes < 2 * page_bytes) return NF4_EWORKSPACE;
+  if (!aligned(staging, 16)) return NF4_EALIGN;
+  for (int32_t i = 0; i < count; ++i)
+    if (int rc = check_lora_state(adapters[i])) return rc;
+  if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  for (int32_t i = 0; i < count; ++i) {
+    const nf4_lora_state& a = adapters[i];
+    const void* host[] = {a.mA, a.vA, a.mB, a.vB};
+    for (const void* p : host)
+      if (p && !is_pinned_host(p)) return NF4_EINVAL;
+  }
+  return launch_lora_adamw_paged(*opt, adapters, count, grad_scale, staging, page_bytes, as_stream(stream));
 }
 
 int lora_adamw_step_many(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,

@@ -331,8 +331,10 @@ int launch_lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P,
   return launch_status();
 }
 
-int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
-                      hipStream_t st) {
+namespace {
+
+// Per-update constants, formed in fp64 and rounded once to fp32.
+AdamwConst make_adamw_const(const nf4_adamw& opt) {
   const double lr = opt.lr, b1 = opt.beta1, b2 = opt.beta2, wd = opt.weight_decay;
   const double t = (double)opt.step;
   const double bc1 = 1.0 - std::pow(b1, t), bc2 = 1.0 - std::pow(b2, t);
@@ -345,19 +347,25 @@ int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t co
   c.stepsz = (float)(lr / bc1);
   c.rbc2 = (float)(1.0 / std::sqrt(bc2));
   c.eps = opt.eps;
+  return c;
+}
 
+// Mode of a tensor (see AdamwSeg) and the s^-2 factor.
+int seg_mode(const float* P, int32_t r) { return P ? ((r % 4 == 0) ? 1 : 2) : 0; }
+float seg_pscale(const float* P, float s) { return P ? (float)(1.0 / ((double)s * (double)s)) : 1.0f; }
+int64_t seg_blocks(int mode, int64_t n) { return ceil_div(mode == 2 ? n : ceil_div(n, 4), 256); }
+
+}  // namespace
+
+int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
+                      hipStream_t st) {
+  const AdamwConst c = make_adamw_const(opt);
   AdamwTable tab{};
   int64_t blocks = 0;
   auto add = [&](float* p, const float* g, float* m, float* v, int64_t n, const float* P, int32_t r, float s) {
-    AdamwSeg& q = tab.seg[tab.count++];
-    q = AdamwSeg{p, g, m, v, P, n, blocks, r, 0, 1.0f};
-    int64_t threads = ceil_div(n, 4);
-    if (P) {
-      q.mode = (r % 4 == 0) ? 1 : 2;
-      q.pscale = (float)(1.0 / ((double)s * (double)s));
-      if (q.mode == 2) threads = n;
-    }
-    blocks += ceil_div(threads, 256);
+    const int mode = seg_mode(P, r);
+    tab.seg[tab.count++] = AdamwSeg{p, g, m, v, P, n, blocks, r, mode, seg_pscale(P, s)};
+    blocks += seg_blocks(mode, n);
   };
   for (int32_t i = 0; i < count; ++i) {
     const nf4_lora_state& a = ad[i];
@@ -366,6 +374,44 @@ int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t co
   }
   hipLaunchKernelGGL(k_lora_adamw, dim3((unsigned)blocks), dim3(256), 0, st, tab, grad_scale, c);
   return launch_status();
+}
+
+int launch_lora_adamw_paged(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
+                            void* staging, size_t page_bytes, hipStream_t st) {
+  const AdamwConst c = make_adamw_const(opt);
+  const int64_t page = (int64_t)(page_bytes / sizeof(float));
+  float* ms = static_cast<float*>(staging);
+  float* vs = ms + page;
+  // One tensor in pages: moments in, update, moments out, all in stream order.
+  auto run = [&](float* p, const float* g, float* mh, float* vh, int64_t n, const float* P, int32_t r,
+                 float s) -> int {
+    const int mode = seg_mode(P, r);
+    const int64_t unit = mode == 0 ? 4 : 4 * (int64_t)r;  // a page holds whole rows of a preconditioned B
+    const int64_t chunk = page / unit * unit;
+    for (int64_t off = 0; off < n; off += chunk) {
+      const int64_t len = (n - off < chunk) ? n - off : chunk;
+      const size_t bytes = sizeof(float) * (size_t)len;
+      if (hipMemcpyAsync(ms, mh + off, bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+          hipMemcpyAsync(vs, vh + off, bytes, hipMemcpyHostToDevice, st) != hipSuccess)
+        return NF4_EDEVICE;
+      AdamwTable tab{};
+      tab.seg[0] = AdamwSeg{p + off, g + off, ms, vs, P, len, 0, r, mode, seg_pscale(P, s)};
+      tab.count = 1;
+      hipLaunchKernelGGL(k_lora_adamw, dim3((unsigned)seg_blocks(mode, len)), dim3(256), 0, st, tab, grad_scale, c);
+      if (int rc = launch_status()) return rc;
+      if (hipMemcpyAsync(mh + off, ms, bytes, hipMemcpyDeviceToHost, st) != hipSuccess ||
+          hipMemcpyAsync(vh + off, vs, bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return NF4_EDEVICE;
+    }
+    return NF4_OK;
+  };
+  for (int32_t i = 0; i < count; ++i) {
+    const nf4_lora_state& a = ad[i];
+    if (a.A)
+      if (int rc = run(a.A, a.dA, a.mA, a.vA, (int64_t)a.r * a.K, nullptr, a.r, a.s)) return rc;
+    if (int rc = run(a.B, a.dB, a.mB, a.vB, a.N * a.r, a.precond, a.r, a.s)) return rc;
+  }
+  return NF4_OK;
 }
 
 }  // namespace nf4

@@ -25,8 +25,8 @@ _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_dequantize_many",
            "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
-           "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "nf4_status_string",
-           "nf4lora_abi_version"]
+           "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
+           "nf4_status_string", "nf4lora_abi_version"]
 
 MAX_ADAPTERS_PER_CALL = 16
 
@@ -94,6 +94,8 @@ def load() -> ctypes.CDLL:
             lib.lorafa_preconditioner.argtypes = [P, I32, I64, P, P, ctypes.c_size_t, P]
             lib.lora_adamw_step.argtypes = [ctypes.POINTER(_Adamw), I32, I64, I64, P, P, P, P, P, P, P, P, P, F, P, P]
             lib.lora_adamw_step_many.argtypes = [ctypes.POINTER(_Adamw), ctypes.POINTER(_LoraState), I32, P, P]
+            lib.lora_adamw_step_paged.argtypes = [ctypes.POINTER(_Adamw), ctypes.POINTER(_LoraState), I32, P, P,
+                                                  ctypes.c_size_t, ctypes.c_size_t, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
             lib.nf4_status_string.argtypes = [ctypes.c_int]
             for fn in EXPORTS:
@@ -353,10 +355,19 @@ def lorafa_preconditioner(A: torch.Tensor, out: Optional[torch.Tensor] = None,
     return out
 
 
-def _state(ad: dict) -> _LoraState:
+def _host_pinned(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.is_cuda or not t.is_pinned() or not t.is_contiguous() or t.dtype != torch.float32:
+        raise ValueError(f"{name} must be a contiguous pinned fp32 host tensor")
+    return t
+
+
+def _state(ad: dict, paged: bool = False) -> _LoraState:
     B = ad["B"]
     for name in ("B", "dB", "mB", "vB"):
-        _dev(ad[name], name, torch.float32)
+        if paged and name in ("mB", "vB"):
+            _host_pinned(ad[name], name)
+        else:
+            _dev(ad[name], name, torch.float32)
     N, r = B.shape
     A = ad.get("A")
     K = 1
@@ -364,7 +375,10 @@ def _state(ad: dict) -> _LoraState:
         for name in ("A", "dA", "mA", "vA"):
             if ad.get(name) is None:
                 raise ValueError(f"{name} is required when A is trained")
-            _dev(ad[name], name, torch.float32)
+            if paged and name in ("mA", "vA"):
+                _host_pinned(ad[name], name)
+            else:
+                _dev(ad[name], name, torch.float32)
         K = A.shape[1]
     P = ad.get("precond")
     if P is not None:
@@ -389,6 +403,26 @@ def lora_adamw_step_many(adapters, *, step: int, lr: float, beta1: float = 0.9, 
     opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
     _check("lora_adamw_step_many", load().lora_adamw_step_many(ctypes.byref(opt), arr, len(adapters),
                                                                _ptr(grad_scale), _stream(adapters[0]["B"].device)))
+
+
+def lora_adamw_step_paged(adapters, *, step: int, lr: float, staging: torch.Tensor, page_bytes: int = 2 << 20,
+                          beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01,
+                          grad_scale: Optional[torch.Tensor] = None) -> None:
+    """lora_adamw_step_many with every moment tensor in pinned host memory,
+    moved page by page through `staging` (a device uint8 tensor of at least
+    2 * page_bytes). Synchronize the stream before reading the moments."""
+    adapters = list(adapters)
+    if not adapters:
+        return
+    if grad_scale is not None:
+        _dev(grad_scale, "grad_scale", torch.float32)
+    _dev(staging, "staging")
+    arr = (_LoraState * len(adapters))(*[_state(a, paged=True) for a in adapters])
+    opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    _check("lora_adamw_step_paged",
+           load().lora_adamw_step_paged(ctypes.byref(opt), arr, len(adapters), _ptr(grad_scale), _ptr(staging),
+                                        staging.numel() * staging.element_size(), int(page_bytes),
+                                        _stream(adapters[0]["B"].device)))
 
 
 def lora_adamw_step(B: torch.Tensor, dB: torch.Tensor, mB: torch.Tensor, vB: torch.Tensor, *, step: int,

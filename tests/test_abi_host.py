@@ -201,3 +201,18 @@ def test_dequantize_many_argument_errors(lib):
     assert L.nf4_dequantize_many(arr(good, m._Tensor(16, 16, 16, 16, 0, 1)), outs(256, 256), 2, 1, None) == EINVAL
     assert L.nf4_dequantize_many(arr(good, m._Tensor(17, 16, 16, 16, 64, 1)), outs(256, 256), 2, 1, None) == EALIGN
     assert L.nf4_dequantize_many(arr(good), outs(264), 1, 1, None) == EALIGN
+
+
+def test_paged_step_argument_errors(lib):
+    L, m = lib
+    EINVAL, EALIGN, EWS = -1, -2, -6
+    opt = m._Adamw(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    st = (m._LoraState * 1)(m._LoraState(r=16, K=64, N=32, A=256, dA=256, mA=256, vA=256, B=256, dB=256, mB=256,
+                                         vB=256, precond=None, s=2.0))
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 8192, 4095, None) == EINVAL
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 8192, 2048, None) == EINVAL
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 1 << 28, 128 << 20, None) == EINVAL
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 4096, 4096, None) == EWS
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, None, 8192, 4096, None) == EWS
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 264, 8192, 4096, None) == EALIGN
+    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 0, None, 256, 8192, 4096, None) == EINVAL

@@ -210,3 +210,47 @@ def test_llama8b_layer_adapters_one_launch(gpu):
             b = adamw_bounds(h[side], g, h["m" + side], h["v" + side], U32 * np.abs(g), HP, 3)
             for key, name, bd in zip((side, "m" + side, "v" + side), (side, "m" + side, "v" + side), b):
                 assert_within(_np(ad[key]), ref[name], bd, f"{L.name} {name}")
+
+
+def _to_pinned(t: torch.Tensor) -> torch.Tensor:
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+@pytest.mark.parametrize("page_bytes", [4096, 2 << 20])
+def test_paged_moments_equal_device_moments(gpu, page_bytes):
+    """lora_adamw_step_paged with the moments in pinned host memory, moved page
+    by page, gives the same parameters and moments as lora_adamw_step_many, bit
+    for bit: LoRA, LoRA-FA with the preconditioner (r % 4 == 0 and r = 6), and
+    tensors spanning many 4 KiB pages."""
+    specs = [(16, 4096, 4096, False, False), (5, 333, 77, False, False), (16, 1024, 512, True, True),
+             (6, 100, 37, True, True), (64, 14336, 4096, False, False)]
+    dev_ads = [_adapter(*sp, seed=40 + 10 * i) for i, sp in enumerate(specs)]
+    paged = []
+    for ad in dev_ads:
+        q = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in ad.items()}
+        for k in ("mA", "vA", "mB", "vB"):
+            if k in q:
+                q[k] = _to_pinned(q[k])
+        paged.append(q)
+    staging = torch.empty(2 * page_bytes, dtype=torch.uint8, device="cuda")
+    gs = torch.full((1,), 0.5, dtype=torch.float32, device="cuda")
+    for step in (1, 2):
+        gpu.lora_adamw_step_many(dev_ads, step=step, grad_scale=gs, **HP)
+        gpu.lora_adamw_step_paged(paged, step=step, grad_scale=gs, staging=staging, page_bytes=page_bytes, **HP)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(dev_ads, paged)):
+            for k in ("A", "mA", "vA", "B", "mB", "vB"):
+                if k in a:
+                    assert torch.equal(a[k].cpu().view(torch.int32), b[k].cpu().view(torch.int32)), (i, k, step)
+
+
+def test_paged_moments_reject_pageable_memory(gpu):
+    ad = _adapter(8, 64, 32, False, False, seed=3)
+    ad["mB"] = ad["mB"].cpu()  # pageable host memory
+    ad["vB"] = _to_pinned(ad["vB"])
+    ad["mA"], ad["vA"] = _to_pinned(ad["mA"]), _to_pinned(ad["vA"])
+    staging = torch.empty(8192, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        gpu.lora_adamw_step_paged([ad], step=1, staging=staging, page_bytes=4096, **HP)
