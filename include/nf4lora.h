@@ -291,6 +291,66 @@ int lora_adamw_step_paged(const nf4_adamw* opt, const nf4_lora_state* adapters, 
                           const float* grad_scale, void* staging, size_t staging_bytes, size_t page_bytes,
                           nf4_stream_t stream);
 
+/* ---- Decoder-layer operations around the NF4 linears (a Llama-shaped layer).
+ * Soup, "NF4 Layer Streaming - Gate results": the pages measure a full
+ * training step of a checkpointed Llama-3.1-8B-shaped model on a frozen NF4
+ * base; they name the model but print no layer equations, so these are the
+ * standard Llama definitions. Activations are [rows, width] row-major arrays
+ * of `dtype` (bf16 or fp32); all arithmetic is fp32; gamma, rstd, lse and
+ * delta are fp32. Device pointers, caller-owned, 16-byte aligned
+ * (NF4_EALIGN), enqueued on `stream`; argument errors are returned first. */
+
+/* y = s / sqrt(mean(s^2) + eps) * gamma per row, s = x + res (res may be NULL:
+ * s = x). With res, s is stored to `sum` in `dtype` and normalized as stored.
+ * rstd [rows] receives 1 / sqrt(mean(s^2) + eps). */
+int nf4_add_rmsnorm(const void* x, const void* res, nf4_dtype dtype, int64_t rows, int64_t width, const float* gamma,
+                    float eps, void* sum, void* y, float* rstd, nf4_stream_t stream);
+
+/* Input gradient of RMSNorm with gamma frozen: dx = rstd (g - n mean(g n)),
+ * g = dy gamma, n = x rstd (x is the normalized input, rstd from the forward),
+ * plus dres when it is not NULL (the residual path's gradient). */
+int nf4_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dtype, int64_t rows, int64_t width,
+                    const float* gamma, const void* dres, void* dx, nf4_stream_t stream);
+
+/* Rotary embedding in place on x [S, heads*d]: for every head and i < d/2 the
+ * pair (x_i, x_{i+d/2}) of the row at position pos is rotated by
+ * pos * theta^(-2 i / d) (inverse != 0: by the negative angle, which is the
+ * input gradient of the forward rotation). Angles in fp64, cos/sin in fp32.
+ * d even, d <= 256. */
+int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+             nf4_stream_t stream);
+
+/* Causal grouped-query attention: o = softmax(q k^T / sqrt(d), causal) v per
+ * query head h, which reads key/value head h / (hq / hkv). q, o [S, hq*d];
+ * k, v [S, hkv*d]; lse [hq, S] receives each row's log-sum-exp (scaled
+ * scores). d a multiple of 16 up to 128; hq a multiple of hkv. */
+int nf4_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dtype, int64_t S, int32_t hq,
+                      int32_t hkv, int32_t d, void* o, float* lse, nf4_stream_t stream);
+
+/* Input gradients of nf4_attention_fwd from dout, the forward's q, k, v, o and
+ * lse: dq [S, hq*d], dk and dv [S, hkv*d] (key/value gradients summed over the
+ * query heads of their group). delta [hq, S] is scratch that receives
+ * rowsum(dout * o). No atomics; repeated calls are bitwise identical. */
+int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
+                      void* dk, void* dv, nf4_stream_t stream);
+
+/* a = silu(g) * u elementwise over n entries, silu(z) = z / (1 + exp(-z)). */
+int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream);
+
+/* Input gradients of nf4_swiglu: dg = da u s (1 + g (1 - s)), du = da g s with
+ * s = 1 / (1 + exp(-g)). */
+int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t n, void* dg, void* du,
+                   nf4_stream_t stream);
+
+/* Token cross-entropy of logits z [T, V] against int64 targets [T]:
+ * tok_loss[t] = logsumexp(z_t) - z_t[target_t] (fp32, [T]), loss[0] = their
+ * mean, and, unless dz is NULL, dz = (softmax(z_t) - onehot) / T in `dtype`.
+ * `status` (optional device int32) is set to 0, then to NF4_EINVAL if a
+ * target is outside [0, V) (that token's loss is 0). */
+int nf4_cross_entropy(const void* z, nf4_dtype dtype, int64_t T, int64_t V, const int64_t* target, float* tok_loss,
+                      float* loss, void* dz, int32_t* status, nf4_stream_t stream);
+
 /* Static text for a status code. */
 const char* nf4_status_string(int status);
 

@@ -142,6 +142,102 @@ int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stre
   return launch_dequantize(w, out_dtype, out, as_stream(stream));
 }
 
+int nf4_add_rmsnorm(const void* x, const void* res, nf4_dtype dtype, int64_t rows, int64_t width, const float* gamma,
+                    float eps, void* sum, void* y, float* rstd, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!x || !gamma || !y || !rstd || rows < 1 || width < 1 || (res && !sum)) return NF4_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f || rows >= (int64_t(1) << 31)) return NF4_EINVAL;
+  const void* arrays[] = {x, res, sum, y, gamma, rstd};
+  for (const void* p : arrays)
+    if (p && !aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_add_rmsnorm(x, res, dtype, rows, width, gamma, eps, sum, y, rstd, as_stream(stream));
+}
+
+int nf4_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dtype, int64_t rows, int64_t width,
+                    const float* gamma, const void* dres, void* dx, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!dy || !x || !rstd || !gamma || !dx || rows < 1 || width < 1 || rows >= (int64_t(1) << 31)) return NF4_EINVAL;
+  const void* arrays[] = {dy, x, rstd, gamma, dres, dx};
+  for (const void* p : arrays)
+    if (p && !aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_rmsnorm_bwd(dy, x, rstd, dtype, rows, width, gamma, dres, dx, as_stream(stream));
+}
+
+int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+             nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!x || S < 1 || S >= (int64_t(1) << 31) || heads < 1 || d < 2 || d > 256 || d % 2 != 0) return NF4_EINVAL;
+  if (!std::isfinite(theta) || theta <= 1.0 || (inverse != 0 && inverse != 1)) return NF4_EINVAL;
+  if (!aligned(x, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_rope(x, dtype, S, heads, d, theta, inverse, as_stream(stream));
+}
+
+namespace {
+int check_attention(nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (S < 1 || S >= (int64_t(1) << 31) || hq < 1 || hkv < 1 || hq % hkv != 0 || hq > 65535) return NF4_EINVAL;
+  if (d < 16 || d > 128 || d % 16 != 0) return NF4_EINVAL;
+  return NF4_OK;
+}
+}  // namespace
+
+int nf4_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dtype, int64_t S, int32_t hq,
+                      int32_t hkv, int32_t d, void* o, float* lse, nf4_stream_t stream) {
+  if (int rc = check_attention(dtype, S, hq, hkv, d)) return rc;
+  if (!q || !k || !v || !o || !lse) return NF4_EINVAL;
+  const void* arrays[] = {q, k, v, o, lse};
+  for (const void* p : arrays)
+    if (!aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_attention_fwd(q, k, v, dtype, S, hq, hkv, d, o, lse, as_stream(stream));
+}
+
+int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
+                      void* dk, void* dv, nf4_stream_t stream) {
+  if (int rc = check_attention(dtype, S, hq, hkv, d)) return rc;
+  if (!dout || !q || !k || !v || !o || !lse || !delta || !dq || !dk || !dv) return NF4_EINVAL;
+  const void* arrays[] = {dout, q, k, v, o, lse, delta, dq, dk, dv};
+  for (const void* p : arrays)
+    if (!aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_attention_bwd(dout, q, k, v, o, lse, dtype, S, hq, hkv, d, delta, dq, dk, dv, as_stream(stream));
+}
+
+int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!g || !u || !a || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;
+  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(a, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_swiglu(g, u, dtype, n, a, as_stream(stream));
+}
+
+int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t n, void* dg, void* du,
+                   nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!da || !g || !u || !dg || !du || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;
+  const void* arrays[] = {da, g, u, dg, du};
+  for (const void* p : arrays)
+    if (!aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_swiglu_bwd(da, g, u, dtype, n, dg, du, as_stream(stream));
+}
+
+int nf4_cross_entropy(const void* z, nf4_dtype dtype, int64_t T, int64_t V, const int64_t* target, float* tok_loss,
+                      float* loss, void* dz, int32_t* status, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!z || !target || !tok_loss || !loss || T < 1 || V < 1 || T >= (int64_t(1) << 31)) return NF4_EINVAL;
+  const void* arrays[] = {z, target, tok_loss, loss, dz};
+  for (const void* p : arrays)
+    if (p && !aligned(p, 16)) return NF4_EALIGN;
+  if (status && !aligned(status, 4)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_cross_entropy(z, dtype, T, V, target, tok_loss, loss, dz, status, as_stream(stream));
+}
+
 int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t count, nf4_dtype out_dtype,
                         nf4_stream_t stream) {
   if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;

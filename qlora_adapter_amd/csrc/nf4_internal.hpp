@@ -70,6 +70,24 @@ int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t co
 int launch_lora_adamw_paged(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
                             void* staging, size_t page_bytes, hipStream_t st);
 
+// Decoder-layer operations (nf4_decoder.hip).
+int launch_add_rmsnorm(const void* x, const void* res, nf4_dtype dt, int64_t rows, int64_t D, const float* gamma,
+                       float eps, void* sum, void* y, float* rstd, hipStream_t st);
+int launch_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dt, int64_t rows, int64_t D,
+                       const float* gamma, const void* dres, void* dx, hipStream_t st);
+int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+                hipStream_t st);
+int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dt, int64_t S, int32_t hq,
+                         int32_t hkv, int32_t d, void* o, float* lse, hipStream_t st);
+int launch_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta,
+                         void* dq, void* dk, void* dv, hipStream_t st);
+int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t n, void* a, hipStream_t st);
+int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t n, void* dg, void* du,
+                      hipStream_t st);
+int launch_cross_entropy(const void* z, nf4_dtype dt, int64_t T, int64_t V, const int64_t* target, float* tok_loss,
+                         float* loss, void* dz, int32_t* status, hipStream_t st);
+
 inline int launch_status() { return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EDEVICE; }
 
 // Compute units of the current device (256 on MI355X).

@@ -26,7 +26,8 @@ EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "n
            "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
-           "nf4_status_string", "nf4lora_abi_version"]
+           "nf4_add_rmsnorm", "nf4_rmsnorm_bwd", "nf4_rope", "nf4_attention_fwd", "nf4_attention_bwd", "nf4_swiglu",
+           "nf4_swiglu_bwd", "nf4_cross_entropy", "nf4_status_string", "nf4lora_abi_version"]
 
 MAX_ADAPTERS_PER_CALL = 16
 
@@ -96,6 +97,15 @@ def load() -> ctypes.CDLL:
             lib.lora_adamw_step_many.argtypes = [ctypes.POINTER(_Adamw), ctypes.POINTER(_LoraState), I32, P, P]
             lib.lora_adamw_step_paged.argtypes = [ctypes.POINTER(_Adamw), ctypes.POINTER(_LoraState), I32, P, P,
                                                   ctypes.c_size_t, ctypes.c_size_t, P]
+            C = ctypes.c_int
+            lib.nf4_add_rmsnorm.argtypes = [P, P, C, I64, I64, P, F, P, P, P, P]
+            lib.nf4_rmsnorm_bwd.argtypes = [P, P, P, C, I64, I64, P, P, P, P]
+            lib.nf4_rope.argtypes = [P, C, I64, I32, I32, ctypes.c_double, C, P]
+            lib.nf4_attention_fwd.argtypes = [P, P, P, C, I64, I32, I32, I32, P, P, P]
+            lib.nf4_attention_bwd.argtypes = [P, P, P, P, P, P, C, I64, I32, I32, I32, P, P, P, P, P]
+            lib.nf4_swiglu.argtypes = [P, P, C, I64, P, P]
+            lib.nf4_swiglu_bwd.argtypes = [P, P, P, C, I64, P, P, P]
+            lib.nf4_cross_entropy.argtypes = [P, C, I64, I64, P, P, P, P, P, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
             lib.nf4_status_string.argtypes = [ctypes.c_int]
             for fn in EXPORTS:
@@ -454,3 +464,100 @@ def lora_adamw_step(B: torch.Tensor, dB: torch.Tensor, mB: torch.Tensor, vB: tor
                                                      _ptr(vA), _ptr(B), _ptr(dB), _ptr(mB), _ptr(vB),
                                                      _ptr(precond), float(s), _ptr(grad_scale),
                                                      _stream(B.device)))
+
+
+# --------------------------------------------------------------------------- decoder-layer operations
+
+def add_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, res: Optional[torch.Tensor] = None,
+                sum_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                rstd: Optional[torch.Tensor] = None):
+    """(sum, y, rstd): sum = x + res (None without res), y = RMSNorm(sum or x) * gamma."""
+    _dev(x, "x")
+    _dev(gamma, "gamma", torch.float32)
+    rows, width = x.shape
+    if res is not None:
+        _dev(res, "res", x.dtype)
+        if sum_out is None:
+            sum_out = torch.empty_like(x)
+    if y is None:
+        y = torch.empty_like(x)
+    if rstd is None:
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check("nf4_add_rmsnorm", load().nf4_add_rmsnorm(_ptr(x), _ptr(res), _DT[x.dtype], rows, width, _ptr(gamma),
+                                                     float(eps), _ptr(sum_out), _ptr(y), _ptr(rstd),
+                                                     _stream(x.device)))
+    return sum_out, y, rstd
+
+
+def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, gamma: torch.Tensor,
+                dres: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(dy, "dy")
+    rows, width = dy.shape
+    if dx is None:
+        dx = torch.empty_like(dy)
+    _check("nf4_rmsnorm_bwd", load().nf4_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _DT[dy.dtype], rows, width,
+                                                     _ptr(gamma), _ptr(dres), _ptr(dx), _stream(dy.device)))
+    return dx
+
+
+def rope_(x: torch.Tensor, heads: int, d: int, theta: float, inverse: bool = False) -> torch.Tensor:
+    """Rotary embedding of x [S, heads*d] in place."""
+    _dev(x, "x")
+    _check("nf4_rope", load().nf4_rope(_ptr(x), _DT[x.dtype], x.shape[0], int(heads), int(d), float(theta),
+                                       int(bool(inverse)), _stream(x.device)))
+    return x
+
+
+def attention_fwd(q, k, v, hq: int, hkv: int, d: int, o=None, lse=None):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, n, q.dtype)
+    S = q.shape[0]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, S), dtype=torch.float32, device=q.device)
+    _check("nf4_attention_fwd", load().nf4_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], S, hq, hkv, d,
+                                                         _ptr(o), _ptr(lse), _stream(q.device)))
+    return o, lse
+
+
+def attention_bwd(dout, q, k, v, o, lse, hq: int, hkv: int, d: int, dq=None, dk=None, dv=None, delta=None):
+    S = q.shape[0]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((hq, S), dtype=torch.float32, device=q.device)
+    _check("nf4_attention_bwd", load().nf4_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                         _DT[q.dtype], S, hq, hkv, d, _ptr(delta), _ptr(dq), _ptr(dk),
+                                                         _ptr(dv), _stream(q.device)))
+    return dq, dk, dv
+
+
+def swiglu(g, u, a=None):
+    a = torch.empty_like(g) if a is None else a
+    _check("nf4_swiglu", load().nf4_swiglu(_ptr(g), _ptr(u), _DT[g.dtype], g.numel(), _ptr(a), _stream(g.device)))
+    return a
+
+
+def swiglu_bwd(da, g, u, dg=None, du=None):
+    dg = torch.empty_like(g) if dg is None else dg
+    du = torch.empty_like(u) if du is None else du
+    _check("nf4_swiglu_bwd", load().nf4_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), _DT[g.dtype], g.numel(), _ptr(dg),
+                                                   _ptr(du), _stream(g.device)))
+    return dg, du
+
+
+def cross_entropy(z, target, dz=None, want_grad: bool = True, tok_loss=None, loss=None, status=None):
+    """(loss [1], tok_loss [T], dz or None) for logits z [T, V] and int64 targets [T]."""
+    _dev(z, "z")
+    _dev(target, "target", torch.int64)
+    T, V = z.shape
+    tok_loss = torch.empty(T, dtype=torch.float32, device=z.device) if tok_loss is None else tok_loss
+    loss = torch.empty(1, dtype=torch.float32, device=z.device) if loss is None else loss
+    if want_grad and dz is None:
+        dz = torch.empty_like(z)
+    _check("nf4_cross_entropy", load().nf4_cross_entropy(_ptr(z), _DT[z.dtype], T, V, _ptr(target), _ptr(tok_loss),
+                                                         _ptr(loss), _ptr(dz if want_grad else None), _ptr(status),
+                                                         _stream(z.device)))
+    return loss, tok_loss, (dz if want_grad else None)

@@ -1,0 +1,122 @@
+"""GPU parity of the decoder-layer operations (RMSNorm, rotary embedding,
+causal grouped-query attention, SwiGLU, cross-entropy, with input gradients)
+against the fp64 oracle in oracle/llama.py on the same seeded inputs. bf16
+outputs: tests/parity.py's bf16 bar; fp32 outputs: relative Frobenius 1e-5
+(fp32 arithmetic throughout)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import llama as OL
+from tests.parity import assert_close, bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def rnd(shape, std, seed, dt):
+    return workloads.normal_f32(shape, std, seed, "cuda").to(DT[dt])
+
+
+@pytest.mark.parametrize("rows,width", [(512, 4096), (3, 100), (1, 16)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_add_rmsnorm_and_backward(gpu, rows, width, dt):
+    x, res = rnd((rows, width), 1.0, 1, dt), rnd((rows, width), 0.5, 2, dt)
+    gamma = workloads.normal_f32((width,), 1.0, 3, "cuda")
+    eps = 1e-5
+    s, y, rstd = gpu.add_rmsnorm(x, gamma, eps, res=res)
+    _, y0, rstd0 = gpu.add_rmsnorm(x, gamma, eps)
+    dy = rnd((rows, width), 1.0, 4, dt)
+    dres = rnd((rows, width), 1.0, 5, dt)
+    dx = gpu.rmsnorm_bwd(dy, s, rstd, gamma, dres=dres)
+    torch.cuda.synchronize()
+    # the stored sum is the activation-type rounding of x + res
+    np.testing.assert_array_equal(bits(s), bits((x.float() + res.float()).to(DT[dt])))
+    g = gamma.cpu().numpy()
+    y_ref, r_ref = OL.rmsnorm(to_np(s), g, eps)
+    assert_close(to_np(y), y_ref, dt, "y")
+    assert_close(rstd.cpu().numpy(), r_ref, "f32", "rstd")
+    y0_ref, _ = OL.rmsnorm(to_np(x), g, eps)
+    assert_close(to_np(y0), y0_ref, dt, "y without residual")
+    dx_ref = OL.rmsnorm_bwd(to_np(dy), to_np(s), g, eps) + to_np(dres)
+    assert_close(to_np(dx), dx_ref, dt, "dx")
+
+
+@pytest.mark.parametrize("S,heads,d", [(512, 32, 128), (37, 3, 64), (5, 1, 2)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rope(gpu, S, heads, d, dt):
+    x = rnd((S, heads * d), 1.0, 7, dt)
+    y = gpu.rope_(x.clone(), heads, d, 500000.0)
+    z = gpu.rope_(y.clone(), heads, d, 500000.0, inverse=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), OL.rope(to_np(x), heads, d, 500000.0), dt, "rope")
+    assert_close(to_np(z), OL.rope(to_np(y), heads, d, 500000.0, inverse=True), dt, "inverse rope")
+
+
+@pytest.mark.parametrize("S,hq,hkv,d", [(512, 32, 8, 128), (100, 8, 2, 64), (17, 4, 4, 16), (1, 2, 1, 32),
+                                        (130, 4, 1, 128)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_attention_forward_backward(gpu, S, hq, hkv, d, dt):
+    print(f"[attention] S={S} hq={hq} hkv={hkv} d={d} {dt}", flush=True)
+    q, k, v = rnd((S, hq * d), 1.0, 11, dt), rnd((S, hkv * d), 1.0, 12, dt), rnd((S, hkv * d), 1.0, 13, dt)
+    do = rnd((S, hq * d), 1.0, 14, dt)
+    o, lse = gpu.attention_fwd(q, k, v, hq, hkv, d)
+    dq, dk, dv = gpu.attention_bwd(do, q, k, v, o, lse, hq, hkv, d)
+    dq2, dk2, dv2 = gpu.attention_bwd(do, q, k, v, o, lse, hq, hkv, d)
+    torch.cuda.synchronize()
+    qn, kn, vn, don = to_np(q), to_np(k), to_np(v), to_np(do)
+    o_ref, lse_ref = OL.attention(qn, kn, vn, hq, hkv, d)
+    assert_close(to_np(o), o_ref, dt, "o")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-4)
+    dq_ref, dk_ref, dv_ref = OL.attention_bwd(don, qn, kn, vn, hq, hkv, d)
+    if S == 1:
+        # one key: dS = P (dP - rowsum(dO * O)) = 0 exactly, so dQ and dK are 0 up to the
+        # cancellation of two equal sums of d products
+        bound = 64 * np.finfo(np.float32).eps * np.abs(don).max() * np.abs(vn).max() * d * np.abs(kn).max()
+        assert np.abs(to_np(dq)).max() <= bound and np.abs(to_np(dk)).max() <= bound
+    else:
+        assert_close(to_np(dq), dq_ref, dt, "dq")
+        assert_close(to_np(dk), dk_ref, dt, "dk")
+    assert_close(to_np(dv), dv_ref, dt, "dv")
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b), "attention backward not run-to-run identical"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_swiglu(gpu, dt):
+    n = (512, 14336)
+    g, u, da = rnd(n, 2.0, 21, dt), rnd(n, 1.0, 22, dt), rnd(n, 1.0, 23, dt)
+    a = gpu.swiglu(g, u)
+    dg, du = gpu.swiglu_bwd(da, g, u)
+    torch.cuda.synchronize()
+    gn, un, dan = to_np(g), to_np(u), to_np(da)
+    assert_close(to_np(a), OL.swiglu(gn, un), dt, "a")
+    dg_ref, du_ref = OL.swiglu_bwd(dan, gn, un)
+    assert_close(to_np(dg), dg_ref, dt, "dg")
+    assert_close(to_np(du), du_ref, dt, "du")
+
+
+@pytest.mark.parametrize("T,V,dt", [(512, 128256, "bf16"), (7, 1000, "f32"), (1, 3, "bf16")])
+def test_cross_entropy(gpu, T, V, dt):
+    z = rnd((T, V), 2.0, 31, dt)
+    t = torch.from_numpy(np.random.default_rng(T).integers(0, V, size=T, dtype=np.int64)).cuda()
+    st = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+    loss, tok, dz = gpu.cross_entropy(z, t, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    l_ref, g_ref = OL.cross_entropy(to_np(z), t.cpu().numpy())
+    assert abs(float(loss.item()) - l_ref) <= 1e-5 * abs(l_ref) + 1e-6
+    assert_close(to_np(dz), g_ref, dt, "dz")
+
+
+def test_cross_entropy_bad_target(gpu):
+    z = rnd((4, 50), 1.0, 32, "f32")
+    t = torch.tensor([0, 50, -1, 49], dtype=torch.int64, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loss, tok, _ = gpu.cross_entropy(z, t, status=st, want_grad=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == -1
+    tk = tok.cpu().numpy()
+    assert tk[1] == 0.0 and tk[2] == 0.0 and tk[0] > 0 and tk[3] > 0
