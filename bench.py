@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--no-ceilings", action="store_true", help="skip the same-session copy / library GEMM ceilings")
     p.add_argument("--no-throughput", action="store_true",
                    help="skip the 7.5e9-parameter quantize/dequantize throughput pass")
+    p.add_argument("--no-decoder-step", action="store_true",
+                   help="skip the 32-layer Llama-8B-shaped training step (tokens/s)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
@@ -284,6 +286,50 @@ def embedding_measure(nl, dev, reps: int = 20):
                      "gbps": round(T * row_bytes / (ms * 1e-3) / 1e9, 1)}
         del E
     return res
+
+
+def decoder_step_measure(dev, steps: int = 3, warmup: int = 1, seq: int = 512):
+    """The full checkpointed training step of a Llama-3.1-8B-shaped model on the
+    NF4 base (32 layers, hidden 4096, GQA 32/8 heads of 128, FFN 14336, vocab
+    128256; LoRA r = 16, alpha 32 on q_proj and v_proj; 512 tokens, batch 1):
+    embedding rows, 32 layers, final norm, lm_head, cross-entropy, the
+    lm_head backward, 32 recomputed layers with their backward, and the AdamW
+    update of the 64 adapters. Synthetic seeded weights and token ids. Work is
+    counted as the pages do: 6 flops per decoder projection parameter and 4 per
+    lm_head parameter per token (43.98 GFLOP/token)."""
+    import torch
+    from qlora_adapter_amd import llama
+    cfg = llama.LlamaConfig()
+    t0 = time.perf_counter()
+    m = llama.LlamaNF4(cfg, seq, device=dev)
+    torch.cuda.synchronize(dev)
+    build_s = time.perf_counter() - t0
+    g = torch.Generator().manual_seed(31)
+    ids = torch.randint(0, cfg.vocab, (seq + 1,), generator=g).to(dev)
+    x, y = ids[:-1].clone(), ids[1:].clone()
+    losses = []
+    for _ in range(warmup):
+        losses.append(m.train_step(x, y))
+    torch.cuda.synchronize(dev)
+    st = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        losses.append(m.train_step(x, y))
+    e1.record(st)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    fpt = cfg.flops_per_token()
+    peak_gb = torch.cuda.max_memory_allocated(dev) / 2 ** 30
+    out = {"model": "Llama-3.1-8B shape, NF4 + double quantization, random init", "seq": seq, "batch": 1,
+           "layers": cfg.layers, "lora": "r=16 alpha=32 on q_proj, v_proj", "steps": steps, "warmup": warmup,
+           "ms_per_step": round(ms, 2), "tokens_per_s": round(seq / (ms * 1e-3), 1),
+           "gflop_per_token": round(fpt / 1e9, 2), "effective_tflops": round(fpt * seq / (ms * 1e-3) / 1e12, 1),
+           "loss_first_last": [round(float(losses[0].item()), 4), round(float(losses[-1].item()), 4)],
+           "peak_allocated_gib": round(peak_gb, 2), "build_s": round(build_s, 1)}
+    del m
+    torch.cuda.empty_cache()
+    return out
 
 
 def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
@@ -567,6 +613,7 @@ def main():
     emb = embedding_measure(nl, dev)
     paged = paged_adamw_measure(nl, dev)
     others = other_configs(nl, dev)
+    decoder = None if args.no_decoder_step else decoder_step_measure(dev)
 
     ceil = None if args.no_ceilings else ceilings()
     cpu = None
@@ -621,6 +668,7 @@ def main():
         "embedding_rows": emb,
         "paged_adamw": paged,
         "other_configs": others,
+        "decoder_step": decoder,
         "ceilings": ceil,
         "cpu_baseline": cpu,
     }

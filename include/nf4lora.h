@@ -335,6 +335,11 @@ int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void
                       nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
                       void* dk, void* dv, nf4_stream_t stream);
 
+/* out = a + b (+ c when c is not NULL) over n entries, summed in fp32 and
+ * rounded once: the input gradient of a layer input that feeds several
+ * projections. out may alias a. */
+int nf4_add(const void* a, const void* b, const void* c, nf4_dtype dtype, int64_t n, void* out, nf4_stream_t stream);
+
 /* a = silu(g) * u elementwise over n entries, silu(z) = z / (1 + exp(-z)). */
 int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream);
 

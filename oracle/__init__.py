@@ -239,6 +239,16 @@ def linear_bwd_input(dy: np.ndarray, W: np.ndarray, A: Optional[np.ndarray] = No
     return dx, U
 
 
+def lora_down(x: np.ndarray, A: np.ndarray) -> np.ndarray:
+    """T = x A^T in fp64: the rank-r projection the forward keeps for dB."""
+    return np.asarray(x, np.float64) @ np.asarray(A, np.float64).T
+
+
+def lora_up_grad(dy: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """U = dY B in fp64: the rank-r projection the backward keeps for dA."""
+    return np.asarray(dy, np.float64) @ np.asarray(B, np.float64)
+
+
 def lora_grad(x: np.ndarray, dy: np.ndarray, T: np.ndarray, U: Optional[np.ndarray], s: float,
               fa: bool = False):
     """dA = s U^T x (None when fa, LoRA-FA) and dB = s dY^T T, in fp64."""

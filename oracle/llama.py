@@ -168,3 +168,88 @@ def cross_entropy(logits, target):
     grad = np.exp(z - lse[:, None])
     grad[np.arange(T), t] -= 1.0
     return loss, grad / T
+
+
+# --------------------------------------------------------------------------- one decoder layer
+
+def _bf16(a) -> np.ndarray:
+    """Round to bf16 (nearest even) and back to fp64: the activation storage of
+    the layer, applied where the GPU stores an activation."""
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float64)).to(torch.bfloat16).double().numpy()
+
+
+def decoder_layer(p: dict, xin, res, dx3, cfg: dict, bf16: bool = True) -> dict:
+    """Forward and input/adapter gradients of one pre-norm Llama layer:
+        x = xin + res; h1 = rmsnorm(x); q, k, v = linears(h1) (+ LoRA on the
+        adapted ones); q, k rotated; a = attention(q, k, v); x2 = x + o(a);
+        h2 = rmsnorm(x2); out = x2 + down(swiglu(gate(h2), up(h2))),
+    then, for the upstream gradient dx3 of out: dx (gradient of x) and dA, dB
+    of every adapted projection. Returns out, x2, dn (so out = x2 + dn), dx
+    and grads[name] = (dA, dB). p holds the decoded weights W_<name> [N, K]
+    (fp32 values, already rounded as the GPU multiplies them), gamma1, gamma2,
+    and A_<name>, B_<name> for adapted names; cfg holds heads, kv_heads,
+    head_dim, eps, theta, s and targets. With bf16=True every stored
+    activation is rounded to bf16 where the GPU path stores one. Uses the
+    NF4-linear oracle for the projections."""
+    import oracle as O
+    rb = _bf16 if bf16 else (lambda a: _f64(a))
+    H, Hkv, d, eps, th, s = cfg["heads"], cfg["kv_heads"], cfg["head_dim"], cfg["eps"], cfg["theta"], cfg["s"]
+    tg = cfg["targets"]
+
+    def lin(name, inp):
+        if name in tg:
+            y, T = O.linear_fwd(inp, p["W_" + name], p["A_" + name], p["B_" + name], s)
+            return rb(y), T
+        y, _ = O.linear_fwd(inp, p["W_" + name])
+        return rb(y), None
+
+    def lin_bwd(name, dy):
+        if name in tg:
+            dxx, U = O.linear_bwd_input(dy, p["W_" + name], p["A_" + name], p["B_" + name], s)
+            return rb(dxx), U
+        dxx, _ = O.linear_bwd_input(dy, p["W_" + name])
+        return rb(dxx), None
+
+    x = rb(_f64(xin) + _f64(res)) if res is not None else _f64(xin)
+    h1 = rb(rmsnorm(x, p["gamma1"], eps)[0])
+    q, Tq = lin("q_proj", h1)
+    k, Tk = lin("k_proj", h1)
+    v, Tv = lin("v_proj", h1)
+    q, k = rb(rope(q, H, d, th)), rb(rope(k, Hkv, d, th))
+    a = rb(attention(q, k, v, H, Hkv, d)[0])
+    o, To = lin("o_proj", a)
+    x2 = rb(x + o)
+    h2 = rb(rmsnorm(x2, p["gamma2"], eps)[0])
+    g, Tg = lin("gate_proj", h2)
+    u, Tu = lin("up_proj", h2)
+    sw = rb(swiglu(g, u))
+    dn, Td = lin("down_proj", sw)
+    out = rb(x2 + dn)
+    T = {"q_proj": Tq, "k_proj": Tk, "v_proj": Tv, "o_proj": To, "gate_proj": Tg, "up_proj": Tu, "down_proj": Td}
+
+    dx3 = _f64(dx3)
+    dsw, Ud = lin_bwd("down_proj", dx3)
+    dg, du = swiglu_bwd(dsw, g, u)
+    dg, du = rb(dg), rb(du)
+    dh2a, Ug = lin_bwd("gate_proj", dg)
+    dh2b, Uu = lin_bwd("up_proj", du)
+    dh2 = rb(dh2a + dh2b)
+    dx2 = rb(rmsnorm_bwd(dh2, x2, p["gamma2"], eps) + dx3)
+    da, Uo = lin_bwd("o_proj", dx2)
+    dq, dk, dv = attention_bwd(da, q, k, v, H, Hkv, d)
+    dq, dk, dv = rb(dq), rb(dk), rb(dv)
+    dq, dk = rb(rope(dq, H, d, th, inverse=True)), rb(rope(dk, Hkv, d, th, inverse=True))
+    dh1q, Uq = lin_bwd("q_proj", dq)
+    dh1k, Uk = lin_bwd("k_proj", dk)
+    dh1v, Uv = lin_bwd("v_proj", dv)
+    dh1 = rb(dh1q + dh1k + dh1v)
+    dx = rb(rmsnorm_bwd(dh1, x, p["gamma1"], eps) + dx2)
+    U = {"q_proj": Uq, "k_proj": Uk, "v_proj": Uv, "o_proj": Uo, "gate_proj": Ug, "up_proj": Uu, "down_proj": Ud}
+    ins = {"q_proj": (h1, dq), "k_proj": (h1, dk), "v_proj": (h1, dv), "o_proj": (a, dx2), "gate_proj": (h2, dg),
+           "up_proj": (h2, du), "down_proj": (sw, dx3)}
+    grads = {}
+    for name in tg:
+        xi, dyi = ins[name]
+        grads[name] = O.lora_grad(xi, dyi, T[name], U[name], s)
+    return {"out": out, "dx": dx, "grads": grads, "x2": x2, "dn": dn}

@@ -16,7 +16,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnf4lora.so")
 ARCH = "gfx950"
 
-SOURCES = ["nf4_storage.hip", "nf4_linear.hip", "nf4_gemm_fast.hip", "nf4_optim.hip", "nf4_decoder.hip", "nf4_abi.hip"]
+SOURCES = ["nf4_storage.hip", "nf4_linear.hip", "nf4_gemm_fast.hip", "nf4_optim.hip", "nf4_decoder.hip", "nf4_attention.hip",
+           "nf4_abi.hip"]
 
 # -ffp-contract=off: decoding and every scalar fp32 step is separately rounded
 # (no fused multiply-add); matrix products run on MFMA and are unaffected.

@@ -207,6 +207,16 @@ int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void
   return launch_attention_bwd(dout, q, k, v, o, lse, dtype, S, hq, hkv, d, delta, dq, dk, dv, as_stream(stream));
 }
 
+int nf4_add(const void* a, const void* b, const void* c, nf4_dtype dtype, int64_t n, void* out, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (!a || !b || !out || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;
+  const void* arrays[] = {a, b, c, out};
+  for (const void* p : arrays)
+    if (p && !aligned(p, 16)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_add3(a, b, c, dtype, n, out, as_stream(stream));
+}
+
 int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream) {
   if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
   if (!g || !u || !a || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;

@@ -23,6 +23,9 @@
 //                  gradient.
 //  k_rope          one workgroup per token: the row's d/2 angles in fp64,
 //                  cos/sin rounded to fp32, applied to every head in place.
+//  Attention in bf16 with a head dim that is a multiple of 32 (up to 128)
+//  runs on the matrix cores (nf4_attention.hip); the kernels below serve fp32
+//  and the other head dims.
 //  k_attn_fwd      workgroup = (head, 16 query rows); 16 threads per row.
 //                  Keys and values pass through LDS in blocks of 64 with an
 //                  online softmax; writes O and the row log-sum-exp.
@@ -32,7 +35,7 @@
 //                  query heads of the group and the query blocks at or after
 //                  the keys; dV = sum_i P_ij dO_i, dK = scale sum_i dS_ij q_i.
 //                  No atomics: every output row has one owner.
-//  k_swiglu / k_swiglu_bwd   elementwise.
+//  k_swiglu / k_swiglu_bwd / k_add3   elementwise.
 //  k_xent          one workgroup per token: max, sum of exponentials, the
 //                  token loss, and the logit gradient (softmax - onehot) / T;
 //                  k_xent_mean adds the token losses in index order.
@@ -359,6 +362,20 @@ __global__ __launch_bounds__(256) void k_attn_dkv(const T* __restrict__ dout, co
     }
 }
 
+// ---------------------------------------------------------------- sums
+
+// out = a + b (+ c), fp32 sum rounded once to the activation type. No
+// restrict qualifiers: out may alias an input (each entry is read, then
+// written, by the same lane).
+template <typename T>
+__global__ __launch_bounds__(256) void k_add3(const T* a, const T* b, const T* c, int64_t n, T* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = ldf(a, i) + ldf(b, i);
+  if (c) v += ldf(c, i);
+  stf(out, i, v);
+}
+
 // ---------------------------------------------------------------- SwiGLU
 
 template <typename T>
@@ -459,6 +476,7 @@ int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, doub
 
 int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dt, int64_t S, int32_t hq,
                          int32_t hkv, int32_t d, void* o, float* lse, hipStream_t st) {
+  if (attention_mfma_supported(dt, d)) return launch_attention_fwd_mfma(q, k, v, S, hq, hkv, d, o, lse, st);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const dim3 grid((unsigned)ceil_div(S, AQ), (unsigned)hq);
   NF4_DISPATCH(dt, hipLaunchKernelGGL(k_attn_fwd<T>, grid, dim3(256), 0, st, static_cast<const T*>(q),
@@ -470,6 +488,8 @@ int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype 
 int launch_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta,
                          void* dq, void* dk, void* dv, hipStream_t st) {
+  if (attention_mfma_supported(dt, d))
+    return launch_attention_bwd_mfma(dout, q, k, v, o, lse, S, hq, hkv, d, delta, dq, dk, dv, st);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   NF4_DISPATCH(dt, {
     hipLaunchKernelGGL(k_attn_dq<T>, dim3((unsigned)ceil_div(S, AQ), (unsigned)hq), dim3(256), 0, st,
@@ -481,6 +501,13 @@ int launch_attention_bwd(const void* dout, const void* q, const void* k, const v
                        static_cast<const T*>(v), lse, delta, S, hq, hkv, d, scale, static_cast<T*>(dk),
                        static_cast<T*>(dv));
   });
+  return launch_status();
+}
+
+int launch_add3(const void* a, const void* b, const void* c, nf4_dtype dt, int64_t n, void* out, hipStream_t st) {
+  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_add3<T>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
+                                      static_cast<const T*>(a), static_cast<const T*>(b), static_cast<const T*>(c), n,
+                                      static_cast<T*>(out)));
   return launch_status();
 }
 

@@ -82,6 +82,14 @@ int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype 
 int launch_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta,
                          void* dq, void* dk, void* dv, hipStream_t st);
+// Matrix-core attention (nf4_attention.hip): bf16 with head dim 32, 64, 96 or 128.
+bool attention_mfma_supported(nf4_dtype dt, int32_t d);
+int launch_attention_fwd_mfma(const void* q, const void* k, const void* v, int64_t S, int32_t hq, int32_t hkv,
+                              int32_t d, void* o, float* lse, hipStream_t st);
+int launch_attention_bwd_mfma(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
+                              void* dk, void* dv, hipStream_t st);
+int launch_add3(const void* a, const void* b, const void* c, nf4_dtype dt, int64_t n, void* out, hipStream_t st);
 int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t n, void* a, hipStream_t st);
 int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t n, void* dg, void* du,
                       hipStream_t st);

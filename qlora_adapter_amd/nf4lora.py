@@ -27,7 +27,7 @@ EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "n
            "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
            "nf4_add_rmsnorm", "nf4_rmsnorm_bwd", "nf4_rope", "nf4_attention_fwd", "nf4_attention_bwd", "nf4_swiglu",
-           "nf4_swiglu_bwd", "nf4_cross_entropy", "nf4_status_string", "nf4lora_abi_version"]
+           "nf4_swiglu_bwd", "nf4_cross_entropy", "nf4_add", "nf4_status_string", "nf4lora_abi_version"]
 
 MAX_ADAPTERS_PER_CALL = 16
 
@@ -106,6 +106,7 @@ def load() -> ctypes.CDLL:
             lib.nf4_swiglu.argtypes = [P, P, C, I64, P, P]
             lib.nf4_swiglu_bwd.argtypes = [P, P, P, C, I64, P, P, P]
             lib.nf4_cross_entropy.argtypes = [P, C, I64, I64, P, P, P, P, P, P]
+            lib.nf4_add.argtypes = [P, P, P, C, I64, P, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
             lib.nf4_status_string.argtypes = [ctypes.c_int]
             for fn in EXPORTS:
@@ -561,3 +562,11 @@ def cross_entropy(z, target, dz=None, want_grad: bool = True, tok_loss=None, los
                                                          _ptr(loss), _ptr(dz if want_grad else None), _ptr(status),
                                                          _stream(z.device)))
     return loss, tok_loss, (dz if want_grad else None)
+
+
+def add(a, b, c=None, out=None):
+    """out = a + b (+ c), one fp32 sum rounded once."""
+    out = torch.empty_like(a) if out is None else out
+    _check("nf4_add", load().nf4_add(_ptr(a), _ptr(b), _ptr(c), _DT[a.dtype], a.numel(), _ptr(out),
+                                     _stream(a.device)))
+    return out

@@ -216,3 +216,40 @@ def test_paged_step_argument_errors(lib):
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, None, 8192, 4096, None) == EWS
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 264, 8192, 4096, None) == EALIGN
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 0, None, 256, 8192, 4096, None) == EINVAL
+
+
+def test_decoder_op_argument_errors(lib):
+    L, _ = lib
+    EINVAL, EALIGN, EUNSUP = -1, -2, -3
+    c = ctypes.c_float
+    # fused residual add + RMSNorm and its backward
+    assert L.nf4_add_rmsnorm(256, None, 9, 4, 64, 256, c(1e-5), None, 256, 256, None) == EUNSUP
+    assert L.nf4_add_rmsnorm(256, 256, 1, 4, 64, 256, c(1e-5), None, 256, 256, None) == EINVAL  # res without sum
+    assert L.nf4_add_rmsnorm(256, None, 1, 4, 64, 256, c(-1.0), None, 256, 256, None) == EINVAL
+    assert L.nf4_add_rmsnorm(256, None, 1, 0, 64, 256, c(1e-5), None, 256, 256, None) == EINVAL
+    assert L.nf4_add_rmsnorm(258, None, 1, 4, 64, 256, c(1e-5), None, 256, 256, None) == EALIGN
+    assert L.nf4_rmsnorm_bwd(256, 256, 256, 1, 4, 64, None, None, 256, None) == EINVAL
+    assert L.nf4_rmsnorm_bwd(256, 256, 256, 1, 4, 64, 256, 264, 256, None) == EALIGN
+    # rotary embedding
+    assert L.nf4_rope(256, 1, 8, 2, 3, ctypes.c_double(1e4), 0, None) == EINVAL  # odd head dim
+    assert L.nf4_rope(256, 1, 8, 2, 64, ctypes.c_double(1.0), 0, None) == EINVAL
+    assert L.nf4_rope(256, 1, 8, 2, 64, ctypes.c_double(1e4), 2, None) == EINVAL
+    assert L.nf4_rope(260, 1, 8, 2, 64, ctypes.c_double(1e4), 0, None) == EALIGN
+    # attention: head dim a multiple of 16 up to 128, whole groups of query heads
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 72, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 144, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 3, 64, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 64, 256, None, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 264, 256, 1, 8, 4, 2, 64, 256, 256, None) == EALIGN
+    assert L.nf4_attention_bwd(256, 256, 256, 256, 256, 256, 1, 8, 4, 2, 64, None, 256, 256, 256, None) == EINVAL
+    # elementwise
+    assert L.nf4_add(256, 256, None, 9, 10, 256, None) == EUNSUP
+    assert L.nf4_add(256, None, None, 1, 10, 256, None) == EINVAL
+    assert L.nf4_add(256, 256, None, 1, 0, 256, None) == EINVAL
+    assert L.nf4_add(256, 256, 258, 1, 10, 256, None) == EALIGN
+    assert L.nf4_swiglu(256, 256, 1, 0, 256, None) == EINVAL
+    assert L.nf4_swiglu_bwd(256, 256, 256, 1, 10, 256, 264, None) == EALIGN
+    # cross-entropy
+    assert L.nf4_cross_entropy(256, 1, 4, 0, 256, 256, 256, None, None, None) == EINVAL
+    assert L.nf4_cross_entropy(256, 1, 4, 10, None, 256, 256, None, None, None) == EINVAL
+    assert L.nf4_cross_entropy(256, 1, 4, 10, 256, 256, 256, None, 258, None) == EALIGN

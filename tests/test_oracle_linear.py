@@ -86,6 +86,9 @@ def test_gradients_match_torch_autograd(orc, rslora):
     dA_fa, dB_fa = orc.lora_grad(x, dy, T, None, s, fa=True)
     assert dA_fa is None
     np.testing.assert_array_equal(dB_fa, dB)
+    # the rank-r side products on their own are the same T and U
+    np.testing.assert_allclose(orc.lora_down(x, A), T, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(orc.lora_up_grad(dy, B), U, rtol=1e-12, atol=1e-13)
 
 
 def test_adjoint_identity(orc):

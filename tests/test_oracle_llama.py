@@ -144,3 +144,71 @@ def test_cross_entropy():
     loss, grad = L.cross_entropy(z, t)
     assert abs(loss - lt.item()) < 1e-12
     np.testing.assert_allclose(grad, zt.grad.numpy(), rtol=1e-11, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- the assembled layer
+
+def _torch_rope(x, heads, d, theta):
+    """Half-split rotation, built from torch.polar (a complex phase per pair)."""
+    S = x.shape[0]
+    pos = torch.arange(S, dtype=torch.float64)[:, None]
+    inv = torch.tensor(theta, dtype=torch.float64) ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(S, d // 2, dtype=torch.float64), pos * inv[None, :])
+    xh = x.view(S, heads, 2, d // 2)
+    z = torch.complex(xh[:, :, 0], xh[:, :, 1]) * rot[:, None, :]
+    return torch.stack((z.real, z.imag), dim=2).reshape(S, heads * d)
+
+
+@pytest.mark.parametrize("targets", [("q_proj", "v_proj"),
+                                     ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")])
+def test_decoder_layer_against_torch_autograd(orc, targets):
+    """The oracle's layer (fp64 between the linears, fp32 linear inputs) against
+    the same pre-norm Llama layer written with torch library routines
+    (rms_norm, scaled_dot_product_attention, silu) and differentiated by
+    autograd: output, input gradient and every adapter's dA, dB. Catches a
+    missing residual, a wrong operand in an adapter gradient or a head
+    mapping error."""
+    S, D, H, Hkv, d, F_, r = 11, 32, 4, 2, 8, 48, 3
+    rng = np.random.default_rng(21)
+    f32 = lambda *sh, std=1.0: (rng.standard_normal(sh) * std).astype(np.float32)
+    names = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+    shapes = dict(q_proj=(H * d, D), k_proj=(Hkv * d, D), v_proj=(Hkv * d, D), o_proj=(D, H * d),
+                  gate_proj=(F_, D), up_proj=(F_, D), down_proj=(D, F_))
+    p = {"W_" + n: f32(*shapes[n], std=0.3) for n in names}
+    for n in targets:
+        p["A_" + n], p["B_" + n] = f32(r, shapes[n][1], std=0.3), f32(shapes[n][0], r, std=0.3)
+    p["gamma1"], p["gamma2"] = 1 + f32(D, std=0.2), 1 + f32(D, std=0.2)
+    s, eps, theta = 0.75, 1e-5, 10000.0
+    cfg = dict(heads=H, kv_heads=Hkv, head_dim=d, eps=eps, theta=theta, s=s, targets=targets)
+    xin, res, dx3 = f32(S, D), f32(S, D), f32(S, D)
+    ref = L.decoder_layer(p, xin, res, dx3, cfg, bf16=False)
+
+    T = {k: torch.tensor(v, dtype=torch.float64, requires_grad=k.startswith(("A_", "B_"))) for k, v in p.items()}
+    tx = torch.tensor(xin, dtype=torch.float64, requires_grad=True)
+    fn = torch.nn.functional
+
+    def lin(n, a):
+        y = a @ T["W_" + n].T
+        return y + s * (a @ T["A_" + n].T) @ T["B_" + n].T if n in targets else y
+
+    x = tx + torch.tensor(res, dtype=torch.float64)
+    h1 = fn.rms_norm(x, (D,), T["gamma1"], eps=eps)
+    q = _torch_rope(lin("q_proj", h1), H, d, theta).view(S, H, d).transpose(0, 1)
+    k = _torch_rope(lin("k_proj", h1), Hkv, d, theta).view(S, Hkv, d).transpose(0, 1)
+    v = lin("v_proj", h1).view(S, Hkv, d).transpose(0, 1)
+    k, v = k.repeat_interleave(H // Hkv, 0), v.repeat_interleave(H // Hkv, 0)
+    a = fn.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)[0]
+    x2 = x + lin("o_proj", a.transpose(0, 1).reshape(S, H * d))
+    h2 = fn.rms_norm(x2, (D,), T["gamma2"], eps=eps)
+    out = x2 + lin("down_proj", fn.silu(lin("gate_proj", h2)) * lin("up_proj", h2))
+    out.backward(torch.tensor(dx3, dtype=torch.float64))
+    # fp32 inputs of every linear on the oracle side bound the agreement
+    tol = dict(rtol=2e-5, atol=2e-5)
+    np.testing.assert_allclose(ref["out"], out.detach().numpy(), **tol)
+    np.testing.assert_allclose(ref["x2"], x2.detach().numpy(), **tol)
+    np.testing.assert_allclose(ref["dx"], tx.grad.numpy(), **tol)
+    for n in targets:
+        dA, dB = ref["grads"][n]
+        gA, gB = T["A_" + n].grad.numpy(), T["B_" + n].grad.numpy()
+        np.testing.assert_allclose(dA, gA, rtol=2e-5, atol=2e-5 * np.abs(gA).max())
+        np.testing.assert_allclose(dB, gB, rtol=2e-5, atol=2e-5 * np.abs(gB).max())
