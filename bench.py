@@ -54,6 +54,8 @@ def parse():
                    help="skip the 7.5e9-parameter quantize/dequantize throughput pass")
     p.add_argument("--no-decoder-step", action="store_true",
                    help="skip the 32-layer Llama-8B-shaped training step (tokens/s)")
+    p.add_argument("--decoder-step-only", action="store_true",
+                   help="only the Llama-8B-shaped training step (--steps timed after --warmup), for profiling")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
@@ -478,6 +480,13 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.decoder_step_only:
+        import torch
+        from qlora_adapter_amd import nf4lora as nl
+        nl.load()
+        print(json.dumps(decoder_step_measure(torch.device("cuda:0"), steps=args.steps, warmup=args.warmup)),
+              flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",

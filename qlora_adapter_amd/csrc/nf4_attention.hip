@@ -24,18 +24,20 @@
 // every accumulator stay fp32. Exponentials run in base 2 on log2(e)-scaled
 // scores.
 //
-// Kernels (one wave per workgroup unless noted):
-//  k_attn_fwd_mfma  32 queries of one head, key blocks up to the diagonal,
-//                   online softmax; V tiles staged in LDS. Query blocks are
-//                   numbered longest-first.
+// Kernels (workgroups of 4 waves; the next block's tiles are prefetched into
+// registers while the current one is multiplied):
+//  k_attn_fwd_mfma  32 queries of one head; wave w takes key blocks w, w + 4,
+//                   ... up to the diagonal with its own online softmax and V
+//                   tile in LDS; the four (max, sum, O) are merged in LDS.
+//                   Query blocks are numbered longest-first.
 //  k_attn_dq_mfma   32 queries of one head: delta = rowsum(dO * O) (written
-//                   for the dK/dV kernel), then dQ = scale sum_j dS_ij k_j over
-//                   the key blocks up to the diagonal; K tiles staged in LDS.
-//  k_attn_dkv_mfma  4 waves, 32 keys of one key/value head: wave w takes the
-//                   query blocks at or after the keys with index = w mod 4,
-//                   for every query head of the group, staging its own Q and
-//                   dO tiles; the four partial dK, dV are added in LDS in a
-//                   fixed order. No atomics: every output has one owner.
+//                   for the dK/dV kernel), then dQ = scale sum_j dS_ij k_j with
+//                   the key blocks split over the waves as in the forward.
+//  k_attn_dkv_mfma  32 keys of one key/value head: the (query head of the
+//                   group, query block at or after the keys) items are split
+//                   over the waves, each staging its own Q and dO tiles.
+// Partial results of the waves are added in LDS in the fixed order 3, 2, 1, 0,
+// so every output is deterministic; no atomics.
 #include <cmath>
 
 #include "nf4_device.hpp"
@@ -81,17 +83,33 @@ __device__ __forceinline__ void store4(__bf16* dst, const f32x16& a, int i, floa
   *reinterpret_cast<u32x2*>(dst) = r;
 }
 
-// Rows r0 .. r0 + 31 (clamped to S - 1) of columns col0 .. col0 + D - 1 of a
-// [S, ld] bf16 matrix into an LDS tile with row pitch TP, by lanes lane,
-// lane + nl, ... in 16-byte chunks.
-template <int D, int TP>
-__device__ __forceinline__ void stage_tile(__bf16* dst, const __bf16* src, int64_t ld, int64_t r0, int64_t S,
-                                           int64_t col0, int lane, int nl) {
+// A 32-row tile of columns col0 .. col0 + D - 1 of a [S, ld] bf16 matrix held
+// in registers on its way to LDS: chunk c = lane + 64 i (i < D / 16) is row
+// c / (D / 8), 16-byte column chunk c % (D / 8); rows past S - 1 are clamped.
+template <int D>
+struct TileRegs {
+  bf16x8 c[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D>& t, const __bf16* src, int64_t ld, int64_t r0, int64_t S,
+                                          int64_t col0, int lane) {
   constexpr int CPR = D / 8;
-  for (int c = lane; c < AB * CPR; c += nl) {
-    const int row = c / CPR, ch = c - row * CPR;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int c = lane + 64 * i, row = c / CPR, ch = c - row * CPR;
     const int64_t gr = (r0 + row < S) ? r0 + row : S - 1;
-    *reinterpret_cast<bf16x8*>(dst + row * TP + 8 * ch) = ld16(src + gr * ld + col0 + 8 * ch);
+    t.c[i] = ld16(src + gr * ld + col0 + 8 * ch);
+  }
+}
+
+template <int D, int TP>
+__device__ __forceinline__ void tile_store(const TileRegs<D>& t, __bf16* dst, int lane) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int c = lane + 64 * i, row = c / CPR, ch = c - row * CPR;
+    *reinterpret_cast<bf16x8*>(dst + row * TP + 8 * ch) = t.c[i];
   }
 }
 
@@ -110,15 +128,26 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+template <int ND>
+constexpr int tiles_bytes(int per_wave) {
+  return 4 * per_wave * AB * (32 * ND + 16) * 2;
+}
+
 // ---------------------------------------------------------------- forward
 
+// Workgroup = 4 waves on 32 queries of one head; wave w takes key blocks
+// w, w + 4, ... up to the diagonal (next block's K fragments and V tile
+// prefetched into registers), and the four (max, sum, O) triples are merged in
+// LDS in the order 3, 2, 1, 0.
 template <int ND>
-__global__ __launch_bounds__(64) void k_attn_fwd_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                      const __bf16* __restrict__ v, int64_t S, int hq, int hkv,
-                                                      float sl2, __bf16* __restrict__ o, float* __restrict__ lse) {
-  constexpr int D = 32 * ND, TP = D + 16;
-  __shared__ __attribute__((aligned(16))) __bf16 vs[AB * TP];
-  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+__global__ __launch_bounds__(256) void k_attn_fwd_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                       const __bf16* __restrict__ v, int64_t S, int hq, int hkv,
+                                                       float sl2, __bf16* __restrict__ o, float* __restrict__ lse) {
+  constexpr int D = 32 * ND, TP = D + 16, NE = ND * 16 + 2;
+  constexpr int SMEM = tiles_bytes<ND>(1) > NE * 64 * 4 ? tiles_bytes<ND>(1) : NE * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int h = blockIdx.y, kh = h / (hq / hkv);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t q0 = (nqb - 1 - (int64_t)blockIdx.x) * AB;
@@ -132,13 +161,32 @@ __global__ __launch_bounds__(64) void k_attn_fwd_mfma(const __bf16* __restrict__
 #pragma unroll
   for (int tt = 0; tt < ND; ++tt) acc[tt] = f32x16{};
   const int64_t kend = (q0 + AB < S) ? q0 + AB : S;
-  for (int64_t k0 = 0; k0 < kend; k0 += AB) {
-    __syncthreads();
-    stage_tile<D, TP>(vs, v, ldk, k0, S, (int64_t)kh * D, lane, 64);
-    const int64_t kr = (k0 + l32 < S) ? k0 + l32 : S - 1;
+  const int64_t nkb = (kend + AB - 1) / AB;
+  __bf16* vt = reinterpret_cast<__bf16*>(smem) + wave * AB * TP;
+  const __bf16* kcol = k + (int64_t)kh * D + 8 * g;
+  bf16x8 kc[2 * ND];
+  TileRegs<D> vr;
+  if (wave < nkb) {
+    const int64_t kr = (wave * AB + l32 < S) ? wave * AB + l32 : S - 1;
+#pragma unroll
+    for (int st = 0; st < 2 * ND; ++st) kc[st] = ld16(kcol + kr * ldk + 16 * st);
+    tile_load<D>(vr, v, ldk, wave * AB, S, (int64_t)kh * D, lane);
+  }
+  for (int64_t b = wave; b < nkb; b += 4) {
+    const int64_t k0 = b * AB;
+    tile_store<D, TP>(vr, vt, lane);
+    const bool more = b + 4 < nkb;
+    bf16x8 kn[2 * ND];
+    if (more) {
+      const int64_t k1 = k0 + 4 * AB;
+      const int64_t kr = (k1 + l32 < S) ? k1 + l32 : S - 1;
+#pragma unroll
+      for (int st = 0; st < 2 * ND; ++st) kn[st] = ld16(kcol + kr * ldk + 16 * st);
+      tile_load<D>(vr, v, ldk, k1, S, (int64_t)kh * D, lane);
+    }
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int st = 0; st < 2 * ND; ++st) s = mfma(ld16(k + kr * ldk + (int64_t)kh * D + 16 * st + 8 * g), qf[st], s);
+    for (int st = 0; st < 2 * ND; ++st) s = mfma(kc[st], qf[st], s);
     float x[16];
     float bm = -INFINITY;
 #pragma unroll
@@ -148,7 +196,7 @@ __global__ __launch_bounds__(64) void k_attn_fwd_mfma(const __bf16* __restrict__
       bm = fmaxf(bm, x[e]);
     }
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    // every query row of the block sees key k0 <= q0, so mn is finite
+    // every query row sees a key of the block (keys k0 <= q0), so mn is finite
     const float mn = fmaxf(m, bm);
     const float alpha = exp2f(m - mn);
     float rs = 0.0f;
@@ -161,15 +209,57 @@ __global__ __launch_bounds__(64) void k_attn_fwd_mfma(const __bf16* __restrict__
     lsum = lsum * alpha + rs;
     m = mn;
     const bf16x8 pb0 = pack_half(x, 0), pb1 = pack_half(x, 1);
-    __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < ND; ++tt) {
       acc[tt] *= alpha;
-      acc[tt] = mfma(tr_operand<TP>(vs, lane, tt, 0), pb0, acc[tt]);
-      acc[tt] = mfma(tr_operand<TP>(vs, lane, tt, 1), pb1, acc[tt]);
+      acc[tt] = mfma(tr_operand<TP>(vt, lane, tt, 0), pb0, acc[tt]);
+      acc[tt] = mfma(tr_operand<TP>(vt, lane, tt, 1), pb1, acc[tt]);
+    }
+    if (more) {
+#pragma unroll
+      for (int st = 0; st < 2 * ND; ++st) kc[st] = kn[st];
     }
   }
-  if (qi < S) {
+  // merge: cb[e][lane] holds acc elements (e < 16 ND), then max and sum
+  float* cb = reinterpret_cast<float*>(smem);
+  __syncthreads();
+  if (wave == 3) {
+#pragma unroll
+    for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cb[(16 * tt + e) * 64 + lane] = acc[tt][e];
+    cb[(NE - 2) * 64 + lane] = m;
+    cb[(NE - 1) * 64 + lane] = lsum;
+  }
+#pragma unroll
+  for (int w = 2; w >= 0; --w) {
+    __syncthreads();
+    if (wave == w) {
+      const float mb = cb[(NE - 2) * 64 + lane], lb = cb[(NE - 1) * 64 + lane];
+      const float M = fmaxf(mb, m);
+      const float fb = (mb == -INFINITY) ? 0.0f : exp2f(mb - M);
+      const float fw = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+      if (w > 0) {
+#pragma unroll
+        for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float* c = &cb[(16 * tt + e) * 64 + lane];
+            *c = *c * fb + acc[tt][e] * fw;
+          }
+        cb[(NE - 2) * 64 + lane] = M;
+        cb[(NE - 1) * 64 + lane] = lb * fb + lsum * fw;
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[tt][e] = cb[(16 * tt + e) * 64 + lane] * fb + acc[tt][e] * fw;
+        lsum = lb * fb + lsum * fw;
+        m = M;
+      }
+    }
+  }
+  if (wave == 0 && qi < S) {
     const float inv = 1.0f / lsum;
     __bf16* orow = o + qi * ldq + (int64_t)h * D;
 #pragma unroll
@@ -180,17 +270,53 @@ __global__ __launch_bounds__(64) void k_attn_fwd_mfma(const __bf16* __restrict__
   }
 }
 
+// Adds the ND accumulator tiles of the four waves in the order 3, 2, 1, 0 through
+// LDS (`buf`: 16 ND floats x 64 lanes); wave 0 ends with the sum. `wave` must
+// be wave-uniform.
+template <int ND>
+__device__ __forceinline__ void wave_sum(f32x16 (&acc)[ND], float* buf, int wave, int lane) {
+  __syncthreads();
+  if (wave == 3) {
+#pragma unroll
+    for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) buf[(16 * tt + e) * 64 + lane] = acc[tt][e];
+  }
+#pragma unroll
+  for (int w = 2; w >= 1; --w) {
+    __syncthreads();
+    if (wave == w) {
+#pragma unroll
+      for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) buf[(16 * tt + e) * 64 + lane] += acc[tt][e];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int tt = 0; tt < ND; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tt][e] += buf[(16 * tt + e) * 64 + lane];
+  }
+}
+
 // ---------------------------------------------------------------- dQ
 
+// Workgroup = 4 waves on 32 queries of one head; wave w takes key blocks
+// w, w + 4, ... up to the diagonal with the next K and V tiles prefetched into
+// registers; the four partial dQ are added in LDS.
 template <int ND>
-__global__ __launch_bounds__(64) void k_attn_dq_mfma(const __bf16* __restrict__ dout, const __bf16* __restrict__ q,
-                                                     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-                                                     const __bf16* __restrict__ o, const float* __restrict__ lse,
-                                                     int64_t S, int hq, int hkv, float sl2, float scale,
-                                                     float* __restrict__ delta, __bf16* __restrict__ dq) {
+__global__ __launch_bounds__(256) void k_attn_dq_mfma(const __bf16* __restrict__ dout, const __bf16* __restrict__ q,
+                                                      const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                                      const __bf16* __restrict__ o, const float* __restrict__ lse,
+                                                      int64_t S, int hq, int hkv, float sl2, float scale,
+                                                      float* __restrict__ delta, __bf16* __restrict__ dq) {
   constexpr int D = 32 * ND, TP = D + 16;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[AB * TP];
-  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+  constexpr int SMEM = tiles_bytes<ND>(2) > ND * 16 * 64 * 4 ? tiles_bytes<ND>(2) : ND * 16 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int h = blockIdx.y, kh = h / (hq / hkv);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t q0 = (nqb - 1 - (int64_t)blockIdx.x) * AB;
@@ -210,21 +336,33 @@ __global__ __launch_bounds__(64) void k_attn_dq_mfma(const __bf16* __restrict__ 
     for (int u = 0; u < 8; ++u) dl += (float)df[st][u] * (float)ov[u];
   }
   dl += __shfl_xor(dl, 32);
-  if (qi < S && g == 0) delta[(int64_t)h * S + qi] = dl;
+  if (wave == 0 && qi < S && g == 0) delta[(int64_t)h * S + qi] = dl;
   const float L2 = lse[(int64_t)h * S + qr] * kLog2e;
   f32x16 acc[ND];
 #pragma unroll
   for (int tt = 0; tt < ND; ++tt) acc[tt] = f32x16{};
   const int64_t kend = (q0 + AB < S) ? q0 + AB : S;
-  for (int64_t k0 = 0; k0 < kend; k0 += AB) {
-    __syncthreads();
-    stage_tile<D, TP>(ks, k, ldk, k0, S, (int64_t)kh * D, lane, 64);
-    const int64_t kr = (k0 + l32 < S) ? k0 + l32 : S - 1;
+  const int64_t nkb = (kend + AB - 1) / AB;
+  __bf16* kt = reinterpret_cast<__bf16*>(smem) + (2 * wave) * AB * TP;
+  __bf16* vt = kt + AB * TP;
+  TileRegs<D> kr, vr;
+  if (wave < nkb) {
+    tile_load<D>(kr, k, ldk, wave * AB, S, (int64_t)kh * D, lane);
+    tile_load<D>(vr, v, ldk, wave * AB, S, (int64_t)kh * D, lane);
+  }
+  for (int64_t b = wave; b < nkb; b += 4) {
+    const int64_t k0 = b * AB;
+    tile_store<D, TP>(kr, kt, lane);
+    tile_store<D, TP>(vr, vt, lane);
+    if (b + 4 < nkb) {
+      tile_load<D>(kr, k, ldk, k0 + 4 * AB, S, (int64_t)kh * D, lane);
+      tile_load<D>(vr, v, ldk, k0 + 4 * AB, S, (int64_t)kh * D, lane);
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < 2 * ND; ++st) {
-      s = mfma(ld16(k + kr * ldk + (int64_t)kh * D + 16 * st + 8 * g), qf[st], s);
-      dp = mfma(ld16(v + kr * ldk + (int64_t)kh * D + 16 * st + 8 * g), df[st], dp);
+      s = mfma(ld16(kt + l32 * TP + 16 * st + 8 * g), qf[st], s);
+      dp = mfma(ld16(vt + l32 * TP + 16 * st + 8 * g), df[st], dp);
     }
     float x[16];
 #pragma unroll
@@ -233,14 +371,14 @@ __global__ __launch_bounds__(64) void k_attn_dq_mfma(const __bf16* __restrict__ 
       x[e] = key <= qi ? exp2f(s[e] * sl2 - L2) * (dp[e] - dl) : 0.0f;
     }
     const bf16x8 b0 = pack_half(x, 0), b1 = pack_half(x, 1);
-    __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < ND; ++tt) {
-      acc[tt] = mfma(tr_operand<TP>(ks, lane, tt, 0), b0, acc[tt]);
-      acc[tt] = mfma(tr_operand<TP>(ks, lane, tt, 1), b1, acc[tt]);
+      acc[tt] = mfma(tr_operand<TP>(kt, lane, tt, 0), b0, acc[tt]);
+      acc[tt] = mfma(tr_operand<TP>(kt, lane, tt, 1), b1, acc[tt]);
     }
   }
-  if (qi < S) {
+  wave_sum<ND>(acc, reinterpret_cast<float*>(smem), wave, lane);
+  if (wave == 0 && qi < S) {
     __bf16* out = dq + qi * ldq + (int64_t)h * D;
 #pragma unroll
     for (int tt = 0; tt < ND; ++tt)
@@ -251,6 +389,11 @@ __global__ __launch_bounds__(64) void k_attn_dq_mfma(const __bf16* __restrict__ 
 
 // ---------------------------------------------------------------- dK, dV
 
+// Workgroup = 4 waves on 32 keys of one key/value head. The work items are
+// the (query head of the group, query block at or after the keys) pairs,
+// numbered head-major; wave w takes items w, w + 4, ... with the next item's
+// Q and dO tiles, log-sum-exp and delta prefetched into registers. The four
+// partial dK, dV are added in LDS.
 template <int ND>
 __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict__ dout, const __bf16* __restrict__ q,
                                                        const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -259,11 +402,11 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
                                                        float sl2, float scale, __bf16* __restrict__ dk,
                                                        __bf16* __restrict__ dv) {
   constexpr int D = 32 * ND, TP = D + 16;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[4][AB * TP];
-  __shared__ __attribute__((aligned(16))) __bf16 dos[4][AB * TP];
+  constexpr int SMEM = tiles_bytes<ND>(2) > 2 * ND * 16 * 64 * 4 ? tiles_bytes<ND>(2) : 2 * ND * 16 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ float ls[4][AB], dls[4][AB];
-  __shared__ float red[2 * ND * 16 * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int kh = blockIdx.y, grp = hq / hkv;
   const int64_t k0 = (int64_t)blockIdx.x * AB;
   const int64_t ldq = (int64_t)hq * D, ldk = (int64_t)hkv * D;
@@ -277,73 +420,59 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
   f32x16 ak[ND], av[ND];
 #pragma unroll
   for (int tt = 0; tt < ND; ++tt) ak[tt] = av[tt] = f32x16{};
-  const int64_t nqb = (S + AB - 1) / AB;
-  __bf16* qt = qs[wave];
-  __bf16* dt = dos[wave];
-  for (int hh = 0; hh < grp; ++hh) {
-    const int h = kh * grp + hh;
-    for (int64_t qb = k0 / AB + wave; qb < nqb; qb += 4) {
-      const int64_t q0 = qb * AB;
-      // this wave's own tiles: the wave's LDS operations complete in order,
-      // so the previous iteration's reads are done before these writes land
-      stage_tile<D, TP>(qt, q, ldq, q0, S, (int64_t)h * D, lane, 64);
-      stage_tile<D, TP>(dt, dout, ldq, q0, S, (int64_t)h * D, lane, 64);
-      if (lane < AB) {
-        const int64_t qq = (q0 + lane < S) ? q0 + lane : S - 1;
-        ls[wave][lane] = lse[(int64_t)h * S + qq] * kLog2e;
-        dls[wave][lane] = delta[(int64_t)h * S + qq];
-      }
-      __builtin_amdgcn_wave_barrier();
-      f32x16 s = f32x16{}, dp = f32x16{};
+  const int64_t nqb = (S + AB - 1) / AB, qb0 = k0 / AB, nq = nqb - qb0;
+  const int64_t items = nq * grp;
+  __bf16* qt = reinterpret_cast<__bf16*>(smem) + (2 * wave) * AB * TP;
+  __bf16* dt = qt + AB * TP;
+  TileRegs<D> qr_, dr_;
+  float lr_ = 0.0f, dlr_ = 0.0f;
+  auto fetch = [&](int64_t it) {
+    const int h = kh * grp + (int)(it / nq);
+    const int64_t q0 = (qb0 + it % nq) * AB;
+    tile_load<D>(qr_, q, ldq, q0, S, (int64_t)h * D, lane);
+    tile_load<D>(dr_, dout, ldq, q0, S, (int64_t)h * D, lane);
+    const int64_t qq = (q0 + l32 < S) ? q0 + l32 : S - 1;
+    lr_ = lse[(int64_t)h * S + qq] * kLog2e;
+    dlr_ = delta[(int64_t)h * S + qq];
+  };
+  if (wave < items) fetch(wave);
+  for (int64_t it = wave; it < items; it += 4) {
+    const int64_t q0 = (qb0 + it % nq) * AB;
+    tile_store<D, TP>(qr_, qt, lane);
+    tile_store<D, TP>(dr_, dt, lane);
+    if (lane < AB) {
+      ls[wave][lane] = lr_;
+      dls[wave][lane] = dlr_;
+    }
+    if (it + 4 < items) fetch(it + 4);
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < 2 * ND; ++st) {
-        s = mfma(ld16(qt + l32 * TP + 16 * st + 8 * g), kf[st], s);
-        dp = mfma(ld16(dt + l32 * TP + 16 * st + 8 * g), vf[st], dp);
-      }
-      float p[16], ds[16];
+    for (int st = 0; st < 2 * ND; ++st) {
+      s = mfma(ld16(qt + l32 * TP + 16 * st + 8 * g), kf[st], s);
+      dp = mfma(ld16(dt + l32 * TP + 16 * st + 8 * g), vf[st], dp);
+    }
+    float p[16], ds[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qrel = 8 * (e >> 2) + 4 * g + (e & 3);
-        const int64_t qidx = q0 + qrel;
-        const bool ok = qidx < S && kj <= qidx;
-        p[e] = ok ? exp2f(s[e] * sl2 - ls[wave][qrel]) : 0.0f;
-        ds[e] = p[e] * (dp[e] - dls[wave][qrel]);
-      }
-      const bf16x8 p0 = pack_half(p, 0), p1 = pack_half(p, 1);
-      const bf16x8 d0 = pack_half(ds, 0), d1 = pack_half(ds, 1);
+    for (int e = 0; e < 16; ++e) {
+      const int qrel = 8 * (e >> 2) + 4 * g + (e & 3);
+      const int64_t qidx = q0 + qrel;
+      const bool ok = qidx < S && kj <= qidx;
+      p[e] = ok ? exp2f(s[e] * sl2 - ls[wave][qrel]) : 0.0f;
+      ds[e] = p[e] * (dp[e] - dls[wave][qrel]);
+    }
+    const bf16x8 p0 = pack_half(p, 0), p1 = pack_half(p, 1);
+    const bf16x8 d0 = pack_half(ds, 0), d1 = pack_half(ds, 1);
 #pragma unroll
-      for (int tt = 0; tt < ND; ++tt) {
-        av[tt] = mfma(tr_operand<TP>(dt, lane, tt, 0), p0, av[tt]);
-        av[tt] = mfma(tr_operand<TP>(dt, lane, tt, 1), p1, av[tt]);
-        ak[tt] = mfma(tr_operand<TP>(qt, lane, tt, 0), d0, ak[tt]);
-        ak[tt] = mfma(tr_operand<TP>(qt, lane, tt, 1), d1, ak[tt]);
-      }
-      __builtin_amdgcn_wave_barrier();
+    for (int tt = 0; tt < ND; ++tt) {
+      av[tt] = mfma(tr_operand<TP>(dt, lane, tt, 0), p0, av[tt]);
+      av[tt] = mfma(tr_operand<TP>(dt, lane, tt, 1), p1, av[tt]);
+      ak[tt] = mfma(tr_operand<TP>(qt, lane, tt, 0), d0, ak[tt]);
+      ak[tt] = mfma(tr_operand<TP>(qt, lane, tt, 1), d1, ak[tt]);
     }
   }
-  // partial sums of waves 3, 2, 1 into LDS, then wave 0 adds them and stores
-  for (int w = 3; w >= 0; --w) {
-    __syncthreads();
-    if (wave == w) {
-#pragma unroll
-      for (int tt = 0; tt < ND; ++tt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float* rk = &red[((0 * ND + tt) * 16 + e) * 64 + lane];
-          float* rv = &red[((1 * ND + tt) * 16 + e) * 64 + lane];
-          if (w == 3) {
-            *rk = ak[tt][e];
-            *rv = av[tt][e];
-          } else if (w > 0) {
-            *rk += ak[tt][e];
-            *rv += av[tt][e];
-          } else {
-            ak[tt][e] += *rk;
-            av[tt][e] += *rv;
-          }
-        }
-    }
-  }
+  float* red = reinterpret_cast<float*>(smem);
+  wave_sum<ND>(ak, red, wave, lane);
+  wave_sum<ND>(av, red + ND * 16 * 64, wave, lane);
   if (wave == 0 && kj < S) {
     __bf16* krow = dk + kj * ldk + (int64_t)kh * D;
     __bf16* vrow = dv + kj * ldk + (int64_t)kh * D;
@@ -361,7 +490,7 @@ template <int ND>
 void fwd_nd(const void* q, const void* k, const void* v, int64_t S, int hq, int hkv, float sl2, void* o, float* lse,
             hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(S, AB), (unsigned)hq);
-  hipLaunchKernelGGL(k_attn_fwd_mfma<ND>, grid, dim3(64), 0, st, static_cast<const __bf16*>(q),
+  hipLaunchKernelGGL(k_attn_fwd_mfma<ND>, grid, dim3(256), 0, st, static_cast<const __bf16*>(q),
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), S, hq, hkv, sl2,
                      static_cast<__bf16*>(o), lse);
 }
@@ -369,7 +498,7 @@ void fwd_nd(const void* q, const void* k, const void* v, int64_t S, int hq, int 
 template <int ND>
 void bwd_nd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t S,
             int hq, int hkv, float sl2, float scale, float* delta, void* dq, void* dk, void* dv, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_dq_mfma<ND>, dim3((unsigned)ceil_div(S, AB), (unsigned)hq), dim3(64), 0, st,
+  hipLaunchKernelGGL(k_attn_dq_mfma<ND>, dim3((unsigned)ceil_div(S, AB), (unsigned)hq), dim3(256), 0, st,
                      static_cast<const __bf16*>(dout), static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<const __bf16*>(o), lse, S, hq, hkv, sl2, scale, delta,
                      static_cast<__bf16*>(dq));
