@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 2
+#define NF4LORA_ABI_VERSION 3
 
 enum nf4_status {
   NF4_OK = 0,
@@ -168,18 +168,32 @@ int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t*
  * [M,N] are `dtype` (F32: fp32 weights; BF16: weights rounded to bf16 before
  * the multiply); accumulation is fp32. r == 0 disables the adapter (A, B,
  * t_out may be NULL); r in [1, 256] requires A [r,K], B [N,r] and t_out [M,r]
- * (receives T = x A^T in fp32, kept for lora_grad). W->n must equal N*K. */
+ * (receives T = x A^T in fp32, kept for lora_grad). W->n must equal N*K.
+ * `workspace` holds nf4_linear_workspace_bytes(M, K, N, 0) bytes (NULL when
+ * that is 0). */
 int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
-                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out,
-                   nf4_stream_t stream);
+                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out, void* workspace,
+                   size_t workspace_bytes, nf4_stream_t stream);
 
 /* Fused input gradient through the frozen base: dX = dY W_hat + s (dY B) A.
  * dY [M,N] and dX [M,K] are `dtype`. r == 0 disables the adapter; r >= 1
  * requires A, B and u_out [M,r] (receives U = dY B in fp32). No weight
- * gradient is produced for W. */
+ * gradient is produced for W. `workspace` holds
+ * nf4_linear_workspace_bytes(M, K, N, 1) bytes (NULL when that is 0). */
 int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W,
                          int64_t K, const float* A, const float* B, int32_t r, float s, void* dx,
-                         float* u_out, nf4_stream_t stream);
+                         float* u_out, void* workspace, size_t workspace_bytes, nf4_stream_t stream);
+
+/* Device workspace (bytes, 16-byte aligned) that nf4_linear_fwd (backward = 0)
+ * or nf4_linear_bwd_input (backward = 1) needs in bf16 for these sizes; 0
+ * for most shapes. A long reduction over few output tiles (short sequences
+ * through a wide layer, e.g. 512 tokens through a 4096 x 14336 projection) is
+ * split in parts whose fp32 partial sums the workspace holds; they are added
+ * in a fixed order, so results stay run-to-run identical. When the value is
+ * positive, a call with a NULL or smaller workspace fails with
+ * NF4_EWORKSPACE; fp32 calls ignore the workspace. Host-only; a negative
+ * NF4_E* code for invalid sizes. */
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int backward);
 
 /* LoRA factor gradients: dA = s U^T x [r,K] and dB = s dY^T T [N,r] (fp32),
  * sums over the M tokens in a fixed order (no atomics, run-to-run identical).

@@ -65,7 +65,8 @@ int check_tensor(const nf4_tensor* t, int64_t n) {
 hipStream_t as_stream(nf4_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const nf4_tensor* W, const float* A,
-                  const float* B, int32_t r, float s, void* out, float* side, bool backward, nf4_stream_t stream) {
+                  const float* B, int32_t r, float s, void* out, float* side, void* ws, size_t ws_bytes, bool backward,
+                  nf4_stream_t stream) {
   if (!valid_dtype(dt)) return NF4_EUNSUPPORTED;
   if (!a || !out || M < 1 || K < 1 || N < 1) return NF4_EINVAL;
   if (K > INT64_MAX / N) return NF4_EINVAL;
@@ -75,8 +76,13 @@ int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, 
   if (r > 0 && !std::isfinite(s)) return NF4_EINVAL;
   if (!aligned(a, 16) || !aligned(out, 16)) return NF4_EALIGN;
   if (r > 0 && (!aligned(A, 4) || !aligned(B, 4) || !aligned(side, 4))) return NF4_EALIGN;
+  if (ws && !aligned(ws, 16)) return NF4_EALIGN;
+  if (dt == NF4_BF16) {
+    const int64_t need = linear_fast_workspace_bytes(M, K, N, backward);
+    if (need > 0 && (!ws || ws_bytes < (size_t)need)) return NF4_EWORKSPACE;
+  }
   if (int rc = check_device()) return rc;
-  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward};
+  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward, ws, ws_bytes};
   return launch_linear(g, as_stream(stream));
 }
 
@@ -277,15 +283,20 @@ int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t*
 }
 
 int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
-                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out,
-                   nf4_stream_t stream) {
-  return linear_common(x, dtype, M, K, N, W, A, B, r, s, y, t_out, false, stream);
+                   const float* A, const float* B, int32_t r, float s, void* y, float* t_out, void* workspace,
+                   size_t workspace_bytes, nf4_stream_t stream) {
+  return linear_common(x, dtype, M, K, N, W, A, B, r, s, y, t_out, workspace, workspace_bytes, false, stream);
 }
 
 int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W, int64_t K,
-                         const float* A, const float* B, int32_t r, float s, void* dx, float* u_out,
-                         nf4_stream_t stream) {
-  return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, true, stream);
+                         const float* A, const float* B, int32_t r, float s, void* dx, float* u_out, void* workspace,
+                         size_t workspace_bytes, nf4_stream_t stream) {
+  return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, workspace, workspace_bytes, true, stream);
+}
+
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int backward) {
+  if (M < 1 || K < 1 || N < 1 || K > INT64_MAX / N || (backward != 0 && backward != 1)) return NF4_EINVAL;
+  return linear_fast_workspace_bytes(M, K, N, backward != 0);
 }
 
 int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {

@@ -29,7 +29,10 @@
 // k_fwd / k_bwd (smaller problems): 32 MS tokens per workgroup; in k_fwd each
 // lane decodes the 32 weights its own B operand needs straight into registers,
 // in k_bwd each wave decodes its 64 x 32 weight slice into a private
-// transposed LDS tile.
+// transposed LDS tile. A long reduction over few output tiles (short
+// sequences through a wide layer) is split in parts: each workgroup writes the
+// fp32 partial sum of its part to a caller-provided workspace and k_split_sum
+// adds the parts in order, adds the LoRA term and rounds once.
 #include "nf4_device.hpp"
 
 namespace nf4 {
@@ -133,6 +136,24 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t MT, int64_t NT, i
   group_map(xcd_order(b, MT * NT), MT, NT, mt, nt);
 }
 
+// Tile and reduction range of workgroup b when the reduction of S steps is
+// split in `nsplit` parts: split index b % nsplit (the slice of the partial
+// sums it writes), output tile from b / nsplit as in tile_coords, steps
+// [kbeg, kbeg + nk) of ceil(S / nsplit) each.
+__device__ __forceinline__ void split_coords(int64_t b, int64_t MT, int64_t NT, int nsplit, int64_t S, int64_t& mt,
+                                             int64_t& nt, int64_t& sp, int64_t& kbeg, int64_t& nk) {
+  const int64_t per = (S + nsplit - 1) / nsplit;
+  const int64_t bb = xcd_order(b, MT * NT * nsplit);
+  sp = bb % nsplit;
+  group_map(bb / nsplit, MT, NT, mt, nt);
+  kbeg = sp * per;
+  nk = (S - kbeg) < per ? (S - kbeg) : per;
+  if (nk < 1) {  // an empty part (the launcher never makes one): a zero partial sum
+    kbeg = 0;
+    nk = 0;
+  }
+}
+
 constexpr int FBM = 256, FBN = 128, FBK = 64;
 constexpr int XPITCH = 72;  // bf16 per padded LDS row (64 + 8) of the input-gradient kernel
 
@@ -189,11 +210,11 @@ __device__ __forceinline__ void fwd_issue_x(const __bf16* __restrict__ x, const 
 
 template <bool DQ, int NS>
 __device__ __forceinline__ void fwd_load_w(const NF4View& w, const uint8_t* const (&wp)[NS],
-                                           const int64_t (&nrow)[NS], int64_t KT, int64_t kt, WStep<NS>& st) {
+                                           const int64_t (&blk0)[NS], int64_t kt, WStep<NS>& st) {
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     st.q[t] = *reinterpret_cast<const uint4*>(wp[t] + 32 * kt);
-    const int64_t blk = nrow[t] * KT + kt;
+    const int64_t blk = blk0[t] + kt;
     if (DQ) {
       st.qa[t] = static_cast<const uint8_t*>(w.scales)[blk];
       st.nv[t] = w.nested[blk >> 8];
@@ -240,7 +261,7 @@ __device__ __forceinline__ void fwd_mfma(const __bf16* xb, const bf16x8 (&bop)[N
 template <bool DQ, int MS, int NS>
 __global__ __launch_bounds__(256, NS == 1 ? 2 : 1)
 void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4View w, const float* __restrict__ Bfac,
-           int r, float s, const float* __restrict__ T, __bf16* __restrict__ y) {
+           int r, float s, const float* __restrict__ T, __bf16* __restrict__ y, int nsplit, float* __restrict__ part) {
   constexpr int BM = 32 * MS, WN = 32 * NS, BN = 4 * WN;
   constexpr int STAGE = BM * 64;   // bf16 per x stage
   constexpr int XI = BM / 32;      // 1 KB direct loads per wave per stage
@@ -250,10 +271,9 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t MT = (M + BM - 1) / BM, NT = (N + BN - 1) / BN;
-  int64_t mt, nt;
-  tile_coords(blockIdx.x, MT, NT, mt, nt);
+  int64_t mt, nt, sp, kbeg, KT;
+  split_coords(blockIdx.x, MT, NT, nsplit, K / 64, mt, nt, sp, kbeg, KT);
   const int64_t m0 = mt * BM, n0 = nt * BN;
-  const int64_t KT = K / 64;
   if (DQ) d8s[tid] = dyn8_value((uint32_t)tid);
   const float mu = DQ ? w.offset[0] : 0.0f;
 
@@ -261,7 +281,7 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // lane l writes physical chunk l % 8 of row 8G + l / 8, i.e. logical chunk
   // (l % 8) ^ swz(row). Rows past M are clamped (their outputs are not stored).
   // (offsets relative to row m0, so they fit in 32 bits: rows < 256, K < 2^22)
-  const __bf16* xt = x + m0 * K;
+  const __bf16* xt = x + m0 * K + kbeg * 64;
   int32_t xoff[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
@@ -270,13 +290,14 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
     xoff[i] = (int32_t)(m * K) + 8 * ((lane & 7) ^ swz(row));
   }
   // weight rows of this lane (clamped past N)
-  int64_t nrow[NS];
+  int64_t nrow[NS], blk0[NS];
   const uint8_t* wp[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     const int64_t n = n0 + wave * WN + 32 * t + l32;
     nrow[t] = n < N ? n : N - 1;
-    wp[t] = w.codes + nrow[t] * (K / 2) + 16 * g;
+    wp[t] = w.codes + nrow[t] * (K / 2) + 32 * kbeg + 16 * g;
+    blk0[t] = nrow[t] * (K / 64) + kbeg;
   }
 
   f32x16 acc[MS][NS];
@@ -288,8 +309,8 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   WStep<NS> wa, wb;
   bf16x8 bopa[NS][4], bopb[NS][4];
   fwd_issue_x<XI>(xt, xoff, 0, xs0, wave);
-  fwd_load_w<DQ, NS>(w, wp, nrow, KT, 0, wb);
-  if (KT > 1) fwd_load_w<DQ, NS>(w, wp, nrow, KT, 1, wa);
+  fwd_load_w<DQ, NS>(w, wp, blk0, 0, wb);
+  if (KT > 1) fwd_load_w<DQ, NS>(w, wp, blk0, 1, wa);
   __syncthreads();
   fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
 
@@ -302,12 +323,12 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // body has no branches (keeps the accumulators in place across iterations).
   for (; kt + 3 < KT; kt += 2) {
     fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
-    fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
+    fwd_load_w<DQ, NS>(w, wp, blk0, kt + 2, wb);
     fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     __syncthreads();
     fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
-    fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
+    fwd_load_w<DQ, NS>(w, wp, blk0, kt + 3, wa);
     fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
     __syncthreads();
@@ -315,16 +336,35 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // Last one to three steps.
   for (; kt < KT; kt += 2) {
     if (kt + 1 < KT) fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
-    if (kt + 2 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 2, wb);
+    if (kt + 2 < KT) fwd_load_w<DQ, NS>(w, wp, blk0, kt + 2, wb);
     if (kt + 1 < KT) fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     __syncthreads();
     if (kt + 1 >= KT) break;
     if (kt + 2 < KT) fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
-    if (kt + 3 < KT) fwd_load_w<DQ, NS>(w, wp, nrow, KT, kt + 3, wa);
+    if (kt + 3 < KT) fwd_load_w<DQ, NS>(w, wp, blk0, kt + 3, wa);
     if (kt + 2 < KT) fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
     __syncthreads();
+  }
+
+  // Split reduction: this workgroup's fp32 partial sum goes to its slice of
+  // `part`; k_split_sum adds the slices, the LoRA term and rounds once.
+  if (part) {
+    float* pz = part + (sp * M) * N;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int64_t n = n0 + wave * WN + 32 * t + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+          if (m < M) pz[m * N + n] = acc[i][t][e];
+        }
+    }
+    return;
   }
 
   // LoRA: acc += (s T[m][:]) . B[n][:], as six bf16 MFMA products of three-part
@@ -382,7 +422,8 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
 template <bool DQ, int MS>
 __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, int64_t M, int64_t K, int64_t N,
                                                 NF4View w, const float* __restrict__ Afac, int r, float s,
-                                                const float* __restrict__ U, __bf16* __restrict__ dx) {
+                                                const float* __restrict__ U, __bf16* __restrict__ dx, int nsplit,
+                                                float* __restrict__ part) {
   constexpr int BM = 32 * MS, BKO = 128;
   constexpr int STAGE = BM * 64;  // bf16 per dY stage
   constexpr int YI = BM / 32;     // 1 KB direct loads per wave per stage
@@ -393,13 +434,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t MT = (M + BM - 1) / BM, KTL = (K + BKO - 1) / BKO;
-  int64_t mt, kt_tile;
-  tile_coords(blockIdx.x, MT, KTL, mt, kt_tile);
+  int64_t mt, kt_tile, sp, nbeg, NSTEP;
+  split_coords(blockIdx.x, MT, KTL, nsplit, N / 64, mt, kt_tile, sp, nbeg, NSTEP);
   const int64_t m0 = mt * BM, k0 = kt_tile * BKO;
-  const int64_t NSTEP = N / 64, KB = K / 64;
+  const int64_t KB = K / 64;
   const float mu = DQ ? w.offset[0] : 0.0f;
 
-  const __bf16* yt = dy + m0 * N;
+  const __bf16* yt = dy + m0 * N + nbeg * 64;
   int32_t yoff[YI];
 #pragma unroll
   for (int i = 0; i < YI; ++i) {
@@ -417,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   __bf16* wt = wts[wave];
   // 32 columns = 16 bytes of codes per lane
   auto load_w = [&](int64_t ns, uint4& q, uint32_t& qa, float& nv) __device__ {
-    const int64_t n = 64 * ns + lane;
+    const int64_t n = 64 * (nbeg + ns) + lane;
     q = *reinterpret_cast<const uint4*>(wbase + n * (K / 2));
     const int64_t blk = n * KB + kc / 64;
     if (DQ) {
@@ -498,9 +539,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
     __syncthreads();
   }
 
-  // LoRA: acc += (s U[m][:]) . A[:][k] as six bf16 products of exact splits.
   const int64_t kcol = k0 + 32 * wave + l32;
   const bool kok = kcol < K;
+  // Split reduction: fp32 partial sums to this workgroup's slice of `part`.
+  if (part) {
+    if (!kok) return;
+    float* pz = part + (sp * M) * K;
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (m < M) pz[m * K + kcol] = acc[i][e];
+      }
+    return;
+  }
+  // LoRA: acc += (s U[m][:]) . A[:][k] as six bf16 products of exact splits.
   if (r > 0) {
     for (int rho0 = 0; rho0 < r; rho0 += 16) {
       const int avail = r - (rho0 + 8 * g);
@@ -977,31 +1031,134 @@ bool fast_linear_applies(const LinearArgs& g) {
 #ifndef NF4_GEMM_MIN_TILES
 #define NF4_GEMM_MIN_TILES 128
 #endif
+#ifndef NF4_SPLIT_MS
+#define NF4_SPLIT_MS 8
+#endif
+
+namespace {
+
+// Output width C (y columns or dX columns) and reduction length R of a call.
+inline void out_red(int64_t K, int64_t N, bool backward, int64_t& C, int64_t& R) {
+  C = backward ? K : N;
+  R = backward ? N : K;
+}
+
+bool use_gemm256(int64_t M, int64_t K, int64_t N, bool backward) {
+  int64_t C, R;
+  out_red(K, N, backward, C, R);
+  const int64_t tiles = ceil_div(M, GT) * ceil_div(C, GT);
+  // (lane offsets into the activations and codes are 32-bit, the output is
+  // written with 8-byte buffer stores at 31-bit offsets)
+  return tiles >= NF4_GEMM_MIN_TILES && R < (int64_t(1) << 22) && N * (K / 2) < (int64_t(1) << 32) && C % 4 == 0 &&
+         2 * M * C < (int64_t(1) << 31);
+}
+
+// Token tile (32 MS rows) and reduction split of the k_fwd / k_bwd path. Tiles
+// of 256 or 128 tokens when they still give enough workgroups, smaller ones
+// for short sequences. A long reduction (at least 128 steps of 64) whose
+// 256-token tiles would not fill the chip is instead split in parts of at
+// least 32 steps over 256-token tiles (each weight slice decoded for 256
+// tokens, not 64), the parts' fp32 partial sums added by k_split_sum.
+struct SmallPlan {
+  int ms;
+  int nsplit;
+};
+
+SmallPlan small_plan(int64_t M, int64_t K, int64_t N, bool backward) {
+  int64_t C, R;
+  out_red(K, N, backward, C, R);
+  const int64_t ct = ceil_div(C, 128), steps = R / 64;
+  auto wg = [&](int ms) { return ceil_div(M, 32 * ms) * ct; };
+  SmallPlan p{1, 1};
+  if (wg(8) >= 448)
+    p.ms = 8;
+  else if (wg(4) >= 200)
+    p.ms = 4;
+  else if (wg(2) >= 200)
+    p.ms = 2;
+  if (steps >= 128 && wg(NF4_SPLIT_MS) < 200 && C % 4 == 0) {
+    const int ms = NF4_SPLIT_MS;
+    int64_t ns = ceil_div(256, wg(ms));
+    if (ns > steps / 32) ns = steps / 32;
+    if (ns > 8) ns = 8;
+    if (ns >= 2) {
+      ns = ceil_div(steps, ceil_div(steps, ns));  // every part non-empty
+      p.ms = ms;
+      p.nsplit = (int)ns;
+    }
+  }
+  return p;
+}
+
+// out[m][c] = bf16(sum_p part[p][m][c] + s sum_rho side[m][rho] F(rho, c)) with
+// F = B[c][rho] (forward) or A[rho][c] (input gradient); parts added in index
+// order. Four consecutive columns per thread (C % 4 == 0).
+template <bool BWD>
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int nsplit, int64_t M, int64_t C,
+                                                   const float* __restrict__ side, const float* __restrict__ F, int r,
+                                                   float s, __bf16* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q * 4 >= M * C) return;
+  const int64_t m = (q * 4) / C, c0 = q * 4 - m * C;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + q * 4);
+  for (int p = 1; p < nsplit; ++p) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(part + (int64_t)p * M * C + q * 4);
+    v[0] += u[0];
+    v[1] += u[1];
+    v[2] += u[2];
+    v[3] += u[3];
+  }
+  if (r > 0) {
+    float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rho = 0; rho < r; ++rho) {
+      const float sv = s * side[m * r + rho];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] += sv * (BWD ? F[(int64_t)rho * C + c0 + j] : F[(c0 + j) * r + rho]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] += t[j];
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 o;
+  o[0] = pack_bf16x2(v[0], v[1]);
+  o[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(out + q * 4) = o;
+}
+
+}  // namespace
+
+int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward) {
+  if (backward ? (K % 64 != 0 || N % 64 != 0) : (K % FBK != 0)) return 0;
+  if (use_gemm256(M, K, N, backward)) return 0;
+  const SmallPlan p = small_plan(M, K, N, backward);
+  if (p.nsplit < 2) return 0;
+  int64_t C, R;
+  out_red(K, N, backward, C, R);
+  if (C % 4 != 0) return 0;
+  return (int64_t)p.nsplit * M * C * (int64_t)sizeof(float);
+}
 
 int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   const NF4View w = make_view(g.W);
   const bool dq = g.W->double_quant != 0;
-  {
+  if (use_gemm256(g.M, g.K, g.N, g.backward)) {
     // 256 x 256 shared-decode kernel when there are enough tiles to fill the chip.
-    const int64_t R = g.backward ? g.N : g.K, C = g.backward ? g.K : g.N;
+    int64_t C, R;
+    out_red(g.K, g.N, g.backward, C, R);
     const int64_t tiles = ceil_div(g.M, GT) * ceil_div(C, GT);
-    // (lane offsets into the activations and codes are 32-bit, the output is
-    // written with 8-byte buffer stores at 31-bit offsets)
-    if (tiles >= NF4_GEMM_MIN_TILES && R < (int64_t(1) << 22) && g.N * (g.K / 2) < (int64_t(1) << 32) &&
-        C % 4 == 0 && 2 * g.M * C < (int64_t(1) << 31)) {
-      const __bf16* a = static_cast<const __bf16*>(g.a);
-      __bf16* o = static_cast<__bf16*>(g.out);
-      const float* F = g.backward ? g.A : g.B;
+    const __bf16* a = static_cast<const __bf16*>(g.a);
+    __bf16* o = static_cast<__bf16*>(g.out);
+    const float* F = g.backward ? g.A : g.B;
 #ifndef NF4_GEMM_NT
 #define NF4_GEMM_NT 2
 #endif
-      constexpr int NT = NF4_GEMM_NT;
-      const dim3 block(64 * (16 / NT));
-      // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
-      // last round of at most half the CUs is run as twice as many half tiles.
-      const int64_t cus = device_cu_count();
-      const int64_t tail = tiles > cus ? tiles % cus : 0;
-      const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
+    constexpr int NT = NF4_GEMM_NT;
+    const dim3 block(64 * (16 / NT));
+    // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
+    // last round of at most half the CUs is run as twice as many half tiles.
+    const int64_t cus = device_cu_count();
+    const int64_t tail = tiles > cus ? tiles % cus : 0;
+    const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
 #define NF4_GEMM(BWD, DQ, MS, NWG, TB)                                                                                 \
   hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, MS>), dim3((unsigned)(NWG)), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, \
                      g.side, o, (int64_t)(TB))
@@ -1010,74 +1167,75 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
     NF4_GEMM(BWD, DQ, 4, whole, 0);                                     \
     if (whole < tiles) NF4_GEMM(BWD, DQ, 2, 2 * (tiles - whole), whole); \
   } while (0)
-      if (g.backward) {
-        if (dq)
-          NF4_GEMM_BOTH(true, true);
-        else
-          NF4_GEMM_BOTH(true, false);
-      } else {
-        if (dq)
-          NF4_GEMM_BOTH(false, true);
-        else
-          NF4_GEMM_BOTH(false, false);
-      }
+    if (g.backward) {
+      if (dq)
+        NF4_GEMM_BOTH(true, true);
+      else
+        NF4_GEMM_BOTH(true, false);
+    } else {
+      if (dq)
+        NF4_GEMM_BOTH(false, true);
+      else
+        NF4_GEMM_BOTH(false, false);
+    }
 #undef NF4_GEMM_BOTH
 #undef NF4_GEMM
-      return launch_status();
-    }
+    return launch_status();
+  }
+  SmallPlan p = small_plan(g.M, g.K, g.N, g.backward);
+  float* part = nullptr;
+  if (p.nsplit > 1) {
+    const int64_t need = linear_fast_workspace_bytes(g.M, g.K, g.N, g.backward);
+    if (need <= 0 || !g.ws || g.ws_bytes < (size_t)need) return NF4_EWORKSPACE;
+    part = static_cast<float*>(g.ws);
   }
   if (g.backward) {
     const __bf16* dy = static_cast<const __bf16*>(g.a);
     __bf16* dx = static_cast<__bf16*>(g.out);
-    const bool big = ceil_div(g.M, 256) * ceil_div(g.K, 128) >= 224;
-#define NF4_BWD(MS)                                                                                             \
-  do {                                                                                                          \
-    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.K, 128)));                                 \
-    if (dq)                                                                                                     \
-      hipLaunchKernelGGL((k_bwd<true, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, \
-                         dx);                                                                                   \
-    else                                                                                                        \
-      hipLaunchKernelGGL((k_bwd<false, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s,       \
-                         g.side, dx);                                                                           \
+#define NF4_BWD(MS)                                                                                               \
+  do {                                                                                                            \
+    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.K, 128) * p.nsplit));                        \
+    if (dq)                                                                                                       \
+      hipLaunchKernelGGL((k_bwd<true, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side,  \
+                         dx, p.nsplit, part);                                                                     \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_bwd<false, MS>), grid, dim3(256), 0, st, dy, g.M, g.K, g.N, w, g.A, g.r, g.s, g.side, \
+                         dx, p.nsplit, part);                                                                     \
   } while (0)
-    // Smaller token tiles when the 128-token tiles would leave most CUs idle
-    // (short sequences): more workgroups, each with the same K loop.
-    const int64_t kt = ceil_div(g.K, 128);
-    if (big)
-      NF4_BWD(8);
-    else if (ceil_div(g.M, 128) * kt >= 200)
-      NF4_BWD(4);
-    else if (ceil_div(g.M, 64) * kt >= 200)
-      NF4_BWD(2);
-    else
-      NF4_BWD(1);
+    switch (p.ms) {
+      case 8: NF4_BWD(8); break;
+      case 4: NF4_BWD(4); break;
+      case 2: NF4_BWD(2); break;
+      default: NF4_BWD(1); break;
+    }
 #undef NF4_BWD
+    if (part)
+      hipLaunchKernelGGL(k_split_sum<true>, dim3((unsigned)ceil_div(g.M * g.K / 4, 256)), dim3(256), 0, st, part,
+                         p.nsplit, g.M, g.K, g.side, g.A, g.r, g.s, dx);
     return launch_status();
   }
   const __bf16* x = static_cast<const __bf16*>(g.a);
   __bf16* y = static_cast<__bf16*>(g.out);
-  // Tile choice: 256 x 128 unless that leaves most of the 256 CUs idle.
-  const int64_t wg21 = ceil_div(g.M, 256) * ceil_div(g.N, 128);
-#define NF4_FWD(MS, NS)                                                                                         \
-  do {                                                                                                          \
-    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.N, 128 * NS)));                            \
-    if (dq)                                                                                                     \
-      hipLaunchKernelGGL((k_fwd<true, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,     \
-                         g.side, y);                                                                            \
-    else                                                                                                        \
-      hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,    \
-                         g.side, y);                                                                            \
+#define NF4_FWD(MS, NS)                                                                                           \
+  do {                                                                                                            \
+    const dim3 grid((unsigned)(ceil_div(g.M, 32 * MS) * ceil_div(g.N, 128 * NS) * p.nsplit));                   \
+    if (dq)                                                                                                       \
+      hipLaunchKernelGGL((k_fwd<true, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,       \
+                         g.side, y, p.nsplit, part);                                                              \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_fwd<false, MS, NS>), grid, dim3(256), 0, st, x, g.M, g.K, g.N, w, g.B, g.r, g.s,      \
+                         g.side, y, p.nsplit, part);                                                              \
   } while (0)
-  const int64_t nt = ceil_div(g.N, 128);
-  if (wg21 >= 224)
-    NF4_FWD(8, 1);
-  else if (ceil_div(g.M, 128) * nt >= 200)
-    NF4_FWD(4, 1);
-  else if (ceil_div(g.M, 64) * nt >= 200)
-    NF4_FWD(2, 1);
-  else
-    NF4_FWD(1, 1);
+  switch (p.ms) {
+    case 8: NF4_FWD(8, 1); break;
+    case 4: NF4_FWD(4, 1); break;
+    case 2: NF4_FWD(2, 1); break;
+    default: NF4_FWD(1, 1); break;
+  }
 #undef NF4_FWD
+  if (part)
+    hipLaunchKernelGGL(k_split_sum<false>, dim3((unsigned)ceil_div(g.M * g.N / 4, 256)), dim3(256), 0, st, part,
+                       p.nsplit, g.M, g.N, g.side, g.B, g.r, g.s, y);
   return launch_status();
 }
 

@@ -50,7 +50,11 @@ struct LinearArgs {
   void* out;            // y [M, N] or dX [M, K]
   float* side;          // T = x A^T or U = dY B, [M, r]
   bool backward;        // false: y = x W^T + s T B^T; true: dX = dY W + s U A
+  void* ws;             // split-reduction partial sums (linear_fast_workspace_bytes), may be null
+  size_t ws_bytes;
 };
+// Workspace the bf16 fused path needs for these sizes (0 for most shapes).
+int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward);
 int launch_linear(const LinearArgs& a, hipStream_t s);
 
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa);

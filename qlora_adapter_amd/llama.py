@@ -138,6 +138,11 @@ class LlamaNF4:
         self.U = {n: f(S, r) for n in c.lora_targets}
         self.gws = {n: torch.empty(nl.lora_grad_workspace_bytes(S, c.shape(n)[1], c.shape(n)[0], r),
                                    dtype=torch.uint8, device=self.dev) for n in c.lora_targets}
+        shapes = [(c.shape(n)[1], c.shape(n)[0]) for n in PROJ]
+        if self.with_head:
+            shapes.append((c.hidden, c.vocab))
+        need = max(nl.linear_workspace_bytes(S, k, n, bwd) for k, n in shapes for bwd in (False, True))
+        self.lws = torch.empty(need, dtype=torch.uint8, device=self.dev) if need else None
         self.cur_x = None
         if self.with_head:
             self.saved: List[torch.Tensor] = [e(S, D) for _ in range(c.layers)]
@@ -148,16 +153,17 @@ class LlamaNF4:
     def _lin(self, L: Layer, name: str, inp, out):
         ad = L.lora.get(name)
         if ad is None:
-            nl.linear_fwd(inp, L.W[name], y=out)
+            nl.linear_fwd(inp, L.W[name], y=out, workspace=self.lws)
         else:
-            nl.linear_fwd(inp, L.W[name], ad["A"], ad["B"], self.s, y=out, t_out=self.T[name])
+            nl.linear_fwd(inp, L.W[name], ad["A"], ad["B"], self.s, y=out, t_out=self.T[name], workspace=self.lws)
 
     def _lin_bwd(self, L: Layer, name: str, dy, out):
         ad = L.lora.get(name)
         if ad is None:
-            nl.linear_bwd_input(dy, L.W[name], dx=out)
+            nl.linear_bwd_input(dy, L.W[name], dx=out, workspace=self.lws)
         else:
-            nl.linear_bwd_input(dy, L.W[name], ad["A"], ad["B"], self.s, dx=out, u_out=self.U[name])
+            nl.linear_bwd_input(dy, L.W[name], ad["A"], ad["B"], self.s, dx=out, u_out=self.U[name],
+                                workspace=self.lws)
 
     def layer_forward(self, L: Layer, xin, res=None, x_out=None):
         """Runs the layer on x = xin + res (written to x_out) or on x = xin when
@@ -228,9 +234,9 @@ class LlamaNF4:
         for i in range(1, c.layers):
             x2, dn = self.layer_forward(self.layers[i], x2, dn, x_out=self.saved[i])
         nl.add_rmsnorm(x2, self.gamma_f, c.eps, res=dn, sum_out=hb["xf"], y=hb["hf"], rstd=hb["rf"])
-        nl.linear_fwd(hb["hf"], self.lm_head, y=hb["logits"])
+        nl.linear_fwd(hb["hf"], self.lm_head, y=hb["logits"], workspace=self.lws)
         nl.cross_entropy(hb["logits"], targets, dz=hb["dlogits"], tok_loss=hb["tok_loss"], loss=hb["loss"])
-        nl.linear_bwd_input(hb["dlogits"], self.lm_head, dx=hb["dhf"])
+        nl.linear_bwd_input(hb["dlogits"], self.lm_head, dx=hb["dhf"], workspace=self.lws)
         grad = [self.b["gA"], self.b["gB"]]
         nl.rmsnorm_bwd(hb["dhf"], hb["xf"], hb["rf"], self.gamma_f, dx=grad[0])
         for i in reversed(range(c.layers)):

@@ -24,7 +24,7 @@ _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_dequantize_many",
            "nf4_embedding_rows", "nf4_linear_fwd",
-           "nf4_linear_bwd_input", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
+           "nf4_linear_bwd_input", "nf4_linear_workspace_bytes", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
            "nf4_add_rmsnorm", "nf4_rmsnorm_bwd", "nf4_rope", "nf4_attention_fwd", "nf4_attention_bwd", "nf4_swiglu",
            "nf4_swiglu_bwd", "nf4_cross_entropy", "nf4_add", "nf4_status_string", "nf4lora_abi_version"]
@@ -84,9 +84,11 @@ def load() -> ctypes.CDLL:
                                                 ctypes.c_int, P]
             lib.nf4_embedding_rows.argtypes = [ctypes.POINTER(_Tensor), I64, I64, P, I64, ctypes.c_int, P, P, P]
             lib.nf4_linear_fwd.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32, F, P,
-                                           P, P]
+                                           P, P, ctypes.c_size_t, P]
             lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
-                                                 F, P, P, P]
+                                                 F, P, P, P, ctypes.c_size_t, P]
+            lib.nf4_linear_workspace_bytes.restype = I64
+            lib.nf4_linear_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
             lib.lora_grad.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, P, I32, F, P, P, P, ctypes.c_size_t, P]
             lib.lora_grad_workspace_bytes.restype = I64
             lib.lora_grad_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int]
@@ -273,10 +275,30 @@ def embedding_rows(E: NF4Tensor, ids: torch.Tensor, dtype=torch.bfloat16, out: O
     return out
 
 
+def linear_workspace_bytes(M: int, K: int, N: int, backward: bool = False) -> int:
+    """Device workspace the bf16 linear needs for these sizes (0 for most)."""
+    v = int(load().nf4_linear_workspace_bytes(int(M), int(K), int(N), int(bool(backward))))
+    if v < 0:
+        _check("nf4_linear_workspace_bytes", v)
+    return v
+
+
+def _linear_ws(workspace, M, K, N, backward, dtype, device):
+    need = linear_workspace_bytes(M, K, N, backward) if dtype == torch.bfloat16 else 0
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
-               s: float = 0.0, y: Optional[torch.Tensor] = None,
-               t_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """y = x W^T + s (x A^T) B^T; returns (y, T) with T = x A^T (fp32) or None."""
+               s: float = 0.0, y: Optional[torch.Tensor] = None, t_out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """y = x W^T + s (x A^T) B^T; returns (y, T) with T = x A^T (fp32) or None.
+    `workspace` (device bytes, linear_workspace_bytes(M, K, N)) is allocated
+    here when needed and not given."""
     _dev(x, "x")
     M, K = x.shape
     N = W.shape[0]
@@ -289,15 +311,19 @@ def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, 
         _dev(A, "A", torch.float32)
         _dev(B, "B", torch.float32)
     st = W.c_struct()
+    ws, wsb = _linear_ws(workspace, M, K, N, False, x.dtype, x.device)
     _check("nf4_linear_fwd", load().nf4_linear_fwd(_ptr(x), _DT[x.dtype], M, K, ctypes.byref(st), N, _ptr(A),
-                                                   _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _stream(x.device)))
+                                                   _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _ptr(ws), wsb,
+                                                   _stream(x.device)))
     return y, t_out
 
 
 def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None,
                      B: Optional[torch.Tensor] = None, s: float = 0.0, dx: Optional[torch.Tensor] = None,
-                     u_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """dX = dY W + s (dY B) A; returns (dX, U) with U = dY B (fp32) or None."""
+                     u_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dX = dY W + s (dY B) A; returns (dX, U) with U = dY B (fp32) or None.
+    `workspace`: as for linear_fwd, linear_workspace_bytes(M, K, N, True)."""
     _dev(dy, "dy")
     M, N = dy.shape
     K = W.shape[1]
@@ -307,9 +333,10 @@ def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] =
     if r and u_out is None:
         u_out = torch.empty((M, r), dtype=torch.float32, device=dy.device)
     st = W.c_struct()
+    ws, wsb = _linear_ws(workspace, M, K, N, True, dy.dtype, dy.device)
     _check("nf4_linear_bwd_input",
            load().nf4_linear_bwd_input(_ptr(dy), _DT[dy.dtype], M, N, ctypes.byref(st), K, _ptr(A), _ptr(B), r,
-                                       float(s), _ptr(dx), _ptr(u_out), _stream(dy.device)))
+                                       float(s), _ptr(dx), _ptr(u_out), _ptr(ws), wsb, _stream(dy.device)))
     return dx, u_out
 
 

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 2
+    assert lib[0].nf4lora_abi_version() == 3
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -99,12 +99,27 @@ def test_argument_errors_before_device(lib):
     assert L.nf4_dequantize(ctypes.byref(t), 7, 16, None) == EUNSUP
     # linear: bad rank, missing adapter buffers, size mismatch
     w = m._Tensor(16, 16, 16, 16, 64 * 32, 1)
-    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, None, None, 4, 1.0, 16, None, None) == EINVAL
-    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 257, 1.0, 16, 16, None) == EINVAL
-    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 33, None, None, 0, 0.0, 16, None, None) == EINVAL
-    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 4, float("nan"), 16, 16, None) == EINVAL
-    assert L.nf4_linear_fwd(24, 1, 8, 64, ctypes.byref(w), 32, None, None, 0, 0.0, 16, None, None) == EALIGN
-    assert L.nf4_linear_bwd_input(16, 5, 8, 32, ctypes.byref(w), 64, None, None, 0, 0.0, 16, None, None) == EUNSUP
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, None, None, 4, 1.0, 16, None, None, 0, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 257, 1.0, 16, 16, None, 0, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 33, None, None, 0, 0.0, 16, None, None, 0, None) == EINVAL
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, 16, 16, 4, float("nan"), 16, 16, None, 0,
+                            None) == EINVAL
+    assert L.nf4_linear_fwd(24, 1, 8, 64, ctypes.byref(w), 32, None, None, 0, 0.0, 16, None, None, 0, None) == EALIGN
+    assert L.nf4_linear_fwd(16, 1, 8, 64, ctypes.byref(w), 32, None, None, 0, 0.0, 16, None, 24, 64, None) == EALIGN
+    assert L.nf4_linear_bwd_input(16, 5, 8, 32, ctypes.byref(w), 64, None, None, 0, 0.0, 16, None, None, 0,
+                                  None) == EUNSUP
+    # split-reduction workspace: 512 tokens through a 4096 x 14336 projection need one in bf16
+    assert L.nf4_linear_workspace_bytes(0, 64, 64, 0) == EINVAL
+    assert L.nf4_linear_workspace_bytes(8, 64, 64, 2) == EINVAL
+    assert L.nf4_linear_workspace_bytes(4096, 4096, 4096, 0) == 0   # large problems: no split
+    need = L.nf4_linear_workspace_bytes(512, 14336, 4096, 0)
+    assert need > 0 and need % (512 * 4096 * 4) == 0
+    assert L.nf4_linear_workspace_bytes(512, 4096, 14336, 1) > 0
+    wd = m._Tensor(16, 16, 16, 16, 4096 * 14336, 1)
+    assert L.nf4_linear_fwd(16, 1, 512, 14336, ctypes.byref(wd), 4096, None, None, 0, 0.0, 16, None, None, 0,
+                            None) == EWS
+    assert L.nf4_linear_fwd(16, 1, 512, 14336, ctypes.byref(wd), 4096, None, None, 0, 0.0, 16, None, 256, need - 16,
+                            None) == EWS
     # lora_grad: rank bounds, workspace
     assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 0, 1.0, 16, 16, 256, 1 << 20, None) == EINVAL
     assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 4, 1.0, 16, 16, None, 0, None) == EWS

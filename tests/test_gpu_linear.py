@@ -216,3 +216,42 @@ def test_backward_heavy_down_proj(gpu, orc):
     dA_ref, dB_ref = orc.lora_grad(x, dy, orc.lora_down(x, A), orc.lora_up_grad(dy, B), s)
     assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
     assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
+
+
+SPLIT = [
+    # (M, K, N, r, backward): long reductions over few output tiles, which the
+    # bf16 path splits in parts whose fp32 partial sums are added in order
+    (512, 14336, 4096, 16, False),   # down_proj forward at 512 tokens
+    (512, 4096, 14336, 16, True),    # gate/up input gradient at 512 tokens
+    (300, 8320, 1000, 5, False),     # ragged tokens, 130 steps in 4 unequal parts, partial column tile
+    (300, 1024, 8320, 5, True),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,bwd", SPLIT)
+def test_split_reduction(gpu, orc, M, K, N, r, bwd):
+    """The split path on 32 sampled token rows against the oracle, the run-to-run
+    identity of the fixed-order sum, and B = 0 giving the base result bit for
+    bit (the LoRA term is added in the final sum)."""
+    print(f"[linear] split M={M} K={K} N={N} r={r} bwd={bwd}", flush=True)
+    assert gpu.linear_workspace_bytes(M, K, N, bwd) > 0
+    c = make_case(M, K, N, r, torch.bfloat16, seed=M + N)
+    s = gpu.lora_scale(32.0, r)
+    Wq = gpu.quantize(c["W"], True)
+    fn = gpu.linear_bwd_input if bwd else gpu.linear_fwd
+    a = c["dy"] if bwd else c["x"]
+    out, side = fn(a, Wq, c["A"], c["B"], s)
+    out2, _ = fn(a, Wq, c["A"], c["B"], s)
+    base, _ = fn(a, Wq)
+    zero, _ = fn(a, Wq, c["A"], torch.zeros_like(c["B"]), s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(zero, base)
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16)
+    rows = np.sort(np.random.default_rng(M + K).choice(M, 32, replace=False))
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    if bwd:
+        ref, U_ref = orc.linear_bwd_input(to_np(a)[rows], Wref, A, B, s)
+    else:
+        ref, U_ref = orc.linear_fwd(to_np(a)[rows], Wref, A, B, s)
+    assert_close(to_np(out)[rows], ref, "bf16", "split output rows")
+    assert_close(side.cpu().numpy()[rows], U_ref, "f32", "side product rows")
