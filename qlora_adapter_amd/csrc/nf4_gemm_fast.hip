@@ -1031,9 +1031,6 @@ bool fast_linear_applies(const LinearArgs& g) {
 #ifndef NF4_GEMM_MIN_TILES
 #define NF4_GEMM_MIN_TILES 128
 #endif
-#ifndef NF4_SPLIT_MS
-#define NF4_SPLIT_MS 8
-#endif
 
 namespace {
 
@@ -1053,12 +1050,18 @@ bool use_gemm256(int64_t M, int64_t K, int64_t N, bool backward) {
          2 * M * C < (int64_t(1) << 31);
 }
 
-// Token tile (32 MS rows) and reduction split of the k_fwd / k_bwd path. Tiles
-// of 256 or 128 tokens when they still give enough workgroups, smaller ones
-// for short sequences. A long reduction (at least 128 steps of 64) whose
-// 256-token tiles would not fill the chip is instead split in parts of at
-// least 32 steps over 256-token tiles (each weight slice decoded for 256
-// tokens, not 64), the parts' fp32 partial sums added by k_split_sum.
+// Token tile (32 MS rows) and reduction split of the k_fwd / k_bwd path
+// (measured at 512 tokens over the Llama-8B projection shapes):
+//  - forward: 256-token tiles when they give >= 448 workgroups, else 128- or
+//    64-token tiles when those give >= 200, else 32. A long reduction (>= 128
+//    steps of 64) runs on 256-token tiles split in parts (about 512
+//    workgroups); a shorter one (>= 32 steps) whose tiles give < 200
+//    workgroups is split over 64-token tiles (about 256 workgroups).
+//  - input gradient: the weight slice is decoded transposed into LDS, so
+//    256-token tiles split to about 512 workgroups whenever the reduction has
+//    >= 32 steps; the forward rule for shorter ones.
+// Parts are a power of two, at most 8, of at least 8 steps; their fp32 partial
+// sums are added by k_split_sum.
 struct SmallPlan {
   int ms;
   int nsplit;
@@ -1069,6 +1072,11 @@ SmallPlan small_plan(int64_t M, int64_t K, int64_t N, bool backward) {
   out_red(K, N, backward, C, R);
   const int64_t ct = ceil_div(C, 128), steps = R / 64;
   auto wg = [&](int ms) { return ceil_div(M, 32 * ms) * ct; };
+  auto parts = [&](int64_t target, int ms) {
+    int64_t ns = 1;
+    while (2 * ns <= 8 && 2 * ns * wg(ms) <= target && steps / (2 * ns) >= 8) ns *= 2;
+    return ns;
+  };
   SmallPlan p{1, 1};
   if (wg(8) >= 448)
     p.ms = 8;
@@ -1076,17 +1084,16 @@ SmallPlan small_plan(int64_t M, int64_t K, int64_t N, bool backward) {
     p.ms = 4;
   else if (wg(2) >= 200)
     p.ms = 2;
-  if (steps >= 128 && wg(NF4_SPLIT_MS) < 200 && C % 4 == 0) {
-    const int ms = NF4_SPLIT_MS;
-    int64_t ns = ceil_div(256, wg(ms));
-    if (ns > steps / 32) ns = steps / 32;
-    if (ns > 8) ns = 8;
-    if (ns >= 2) {
-      ns = ceil_div(steps, ceil_div(steps, ns));  // every part non-empty
-      p.ms = ms;
-      p.nsplit = (int)ns;
-    }
+  if (C % 4 != 0) return p;
+  int64_t ns = 1;
+  if ((backward && steps >= 32) || steps >= 128) {
+    p.ms = 8;
+    ns = parts(512, 8);
+  } else if (steps >= 32 && wg(p.ms) < 200) {
+    if (p.ms < 2) p.ms = 2;
+    ns = parts(256, p.ms);
   }
+  if (ns >= 2) p.nsplit = (int)ceil_div(steps, ceil_div(steps, ns));  // every part non-empty
   return p;
 }
 
