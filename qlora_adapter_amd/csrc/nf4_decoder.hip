@@ -36,6 +36,9 @@
 //                  the keys; dV = sum_i P_ij dO_i, dK = scale sum_i dS_ij q_i.
 //                  No atomics: every output row has one owner.
 //  k_swiglu / k_swiglu_bwd / k_add3   elementwise.
+//  bf16 rows with a width that is a multiple of 8 use vectorized forms
+//  (k_add_rmsnorm_v, k_rmsnorm_bwd_v: the row in registers between the two
+//  phases; k_xent_v: one pass for max and sum).
 //  k_xent          one workgroup per token: max, sum of exponentials, the
 //                  token loss, and the logit gradient (softmax - onehot) / T;
 //                  k_xent_mean adds the token losses in index order.
@@ -54,6 +57,8 @@ template <typename T>
 __device__ __forceinline__ void stf(T* p, int64_t i, float v) {
   p[i] = (T)v;
 }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Sum over the 256 threads of a workgroup, the same value returned to all.
 __device__ __forceinline__ float block_sum256(float v, float* sh) {
@@ -117,6 +122,106 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const T* __restrict__ dy, c
     float v = r * (g - ldf(x + row * D, i) * r * mgn);
     if (dres) v += ldf(dres + row * D, i);
     stf(dx + row * D, i, v);
+  }
+}
+
+// bf16 rows of width D % 8 == 0, D <= 2048 CPT: each thread keeps its CPT
+// 8-element chunks (chunk c = thread + 256 j) in registers between the sum of
+// squares and the scaling, with 16-byte loads and stores. Same arithmetic as
+// the general kernels; only the order of the per-thread partial sums differs.
+typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void load_gamma8(const float* __restrict__ gamma, int64_t i, float g[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(gamma + i);
+  const float4 b = *reinterpret_cast<const float4*>(gamma + i + 4);
+  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+}
+
+template <int CPT>
+__global__ __launch_bounds__(256) void k_add_rmsnorm_v(const __bf16* __restrict__ x, const __bf16* __restrict__ res,
+                                                       int64_t D, const float* __restrict__ gamma, float eps,
+                                                       __bf16* __restrict__ sum, __bf16* __restrict__ y,
+                                                       float* __restrict__ rstd) {
+  __shared__ float sh[4];
+  const int64_t row = blockIdx.x, nch = D / 8;
+  float v[CPT][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = threadIdx.x + 256 * j;
+    if (c >= nch) break;
+    const bf16x8d xv = *reinterpret_cast<const bf16x8d*>(x + row * D + 8 * c);
+    if (res) {
+      const bf16x8d rv = *reinterpret_cast<const bf16x8d*>(res + row * D + 8 * c);
+      bf16x8d sv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[e] = (__bf16)((float)xv[e] + (float)rv[e]);  // stored in bf16, normalized as stored
+        v[j][e] = (float)sv[e];
+      }
+      *reinterpret_cast<bf16x8d*>(sum + row * D + 8 * c) = sv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = (float)xv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+  }
+  const float r = 1.0f / sqrtf(block_sum256(ss, sh) / (float)D + eps);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = threadIdx.x + 256 * j;
+    if (c >= nch) break;
+    float g[8];
+    load_gamma8(gamma, 8 * c, g);
+    bf16x8d o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)(v[j][e] * r * g[e]);
+    *reinterpret_cast<bf16x8d*>(y + row * D + 8 * c) = o;
+  }
+  if (threadIdx.x == 0) rstd[row] = r;
+}
+
+template <int CPT>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const __bf16* __restrict__ dy, const __bf16* __restrict__ x,
+                                                       const float* __restrict__ rstd, int64_t D,
+                                                       const float* __restrict__ gamma,
+                                                       const __bf16* __restrict__ dres, __bf16* __restrict__ dx) {
+  __shared__ float sh[4];
+  const int64_t row = blockIdx.x, nch = D / 8;
+  const float r = rstd[row];
+  float gv[CPT][8], xv[CPT][8];
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = threadIdx.x + 256 * j;
+    if (c >= nch) break;
+    const bf16x8d a = *reinterpret_cast<const bf16x8d*>(dy + row * D + 8 * c);
+    const bf16x8d b = *reinterpret_cast<const bf16x8d*>(x + row * D + 8 * c);
+    float g[8];
+    load_gamma8(gamma, 8 * c, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gv[j][e] = (float)a[e] * g[e];
+      xv[j][e] = (float)b[e];
+      acc += gv[j][e] * (xv[j][e] * r);
+    }
+  }
+  const float mgn = block_sum256(acc, sh) / (float)D;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = threadIdx.x + 256 * j;
+    if (c >= nch) break;
+    bf16x8d o;
+    if (dres) {
+      const bf16x8d d = *reinterpret_cast<const bf16x8d*>(dres + row * D + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)(r * (gv[j][e] - xv[j][e] * r * mgn) + (float)d[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)(r * (gv[j][e] - xv[j][e] * r * mgn));
+    }
+    *reinterpret_cast<bf16x8d*>(dx + row * D + 8 * c) = o;
   }
 }
 
@@ -426,6 +531,68 @@ __global__ __launch_bounds__(256) void k_xent(const T* __restrict__ z, const int
       stf(dz + row * V, i, (expf(ldf(zr, i) - lse) - (i == tg ? 1.0f : 0.0f)) * inv_tokens);
 }
 
+// bf16 logits with V % 8 == 0: one pass for the maximum and the sum of
+// exponentials (each thread keeps a running (max, sum) pair, rescaled when its
+// maximum grows; the pairs are merged across the workgroup), then one pass for
+// the gradient; 16-byte loads and stores.
+__global__ __launch_bounds__(256) void k_xent_v(const __bf16* __restrict__ z, const int64_t* __restrict__ target,
+                                                int64_t V, float inv_tokens, float* __restrict__ tok_loss,
+                                                __bf16* __restrict__ dz, int32_t* __restrict__ status) {
+  __shared__ float shm[4], shs[4];
+  const int64_t row = blockIdx.x, nch = V / 8;
+  const __bf16* zr = z + row * V;
+  float m = -INFINITY, se = 0.0f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    const bf16x8d v = *reinterpret_cast<const bf16x8d*>(zr + 8 * c);
+    float cm = (float)v[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, (float)v[e]);
+    if (cm > m) {
+      se *= expf(m - cm);  // 0 while m is -inf
+      m = cm;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) se += expf((float)v[e] - m);
+  }
+  // merge the (max, sum) pairs: wave shuffles, then the four waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float om = __shfl_xor(m, off), os = __shfl_xor(se, off);
+    const float nm = fmaxf(m, om);
+    se = (m == -INFINITY ? 0.0f : se * expf(m - nm)) + (om == -INFINITY ? 0.0f : os * expf(om - nm));
+    m = nm;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    shm[wave] = m;
+    shs[wave] = se;
+  }
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(shm[0], shm[1]), fmaxf(shm[2], shm[3]));
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) tot += shm[w] == -INFINITY ? 0.0f : shs[w] * expf(shm[w] - mx);
+  const float lse = mx + logf(tot);
+  const int64_t tg = target[row];
+  const bool ok = tg >= 0 && tg < V;
+  if (threadIdx.x == 0) {
+    const float zt = (float)zr[ok ? tg : 0];  // never indexes outside the row
+    tok_loss[row] = ok ? lse - zt : 0.0f;
+    if (!ok && status) *status = NF4_EINVAL;
+  }
+  if (!dz) return;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    const bf16x8d v = *reinterpret_cast<const bf16x8d*>(zr + 8 * c);
+    bf16x8d o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t i = 8 * c + e;
+      o[e] = (__bf16)((expf((float)v[e] - lse) - (i == tg ? 1.0f : 0.0f)) * inv_tokens);
+    }
+    *reinterpret_cast<bf16x8d*>(dz + row * V + 8 * c) = o;
+  }
+}
+
 __global__ __launch_bounds__(64) void k_xent_mean(const float* __restrict__ tok_loss, int64_t T,
                                                   float* __restrict__ loss) {
   if (threadIdx.x != 0) return;
@@ -453,6 +620,19 @@ __global__ void k_status_zero(int32_t* status) {
 
 int launch_add_rmsnorm(const void* x, const void* res, nf4_dtype dt, int64_t rows, int64_t D, const float* gamma,
                        float eps, void* sum, void* y, float* rstd, hipStream_t st) {
+  const bool vec = dt == NF4_BF16 && D % 8 == 0 && D <= 8192 && aligned16(gamma);
+  if (vec) {
+    const __bf16* xb = static_cast<const __bf16*>(x);
+    const __bf16* rb = static_cast<const __bf16*>(res);
+#define NF4_ARN(CPT)                                                                                          \
+  hipLaunchKernelGGL(k_add_rmsnorm_v<CPT>, dim3((unsigned)rows), dim3(256), 0, st, xb, rb, D, gamma, eps,   \
+                     static_cast<__bf16*>(sum), static_cast<__bf16*>(y), rstd)
+    if (D <= 2048) NF4_ARN(1);
+    else if (D <= 4096) NF4_ARN(2);
+    else NF4_ARN(4);
+#undef NF4_ARN
+    return launch_status();
+  }
   NF4_DISPATCH(dt, hipLaunchKernelGGL(k_add_rmsnorm<T>, dim3((unsigned)rows), dim3(256), 0, st,
                                       static_cast<const T*>(x), static_cast<const T*>(res), D, gamma, eps,
                                       static_cast<T*>(sum), static_cast<T*>(y), rstd));
@@ -461,6 +641,18 @@ int launch_add_rmsnorm(const void* x, const void* res, nf4_dtype dt, int64_t row
 
 int launch_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dt, int64_t rows, int64_t D,
                        const float* gamma, const void* dres, void* dx, hipStream_t st) {
+  const bool vec = dt == NF4_BF16 && D % 8 == 0 && D <= 8192 && aligned16(gamma);
+  if (vec) {
+#define NF4_RNB(CPT)                                                                                               \
+  hipLaunchKernelGGL(k_rmsnorm_bwd_v<CPT>, dim3((unsigned)rows), dim3(256), 0, st, static_cast<const __bf16*>(dy), \
+                     static_cast<const __bf16*>(x), rstd, D, gamma, static_cast<const __bf16*>(dres),             \
+                     static_cast<__bf16*>(dx))
+    if (D <= 2048) NF4_RNB(1);
+    else if (D <= 4096) NF4_RNB(2);
+    else NF4_RNB(4);
+#undef NF4_RNB
+    return launch_status();
+  }
   NF4_DISPATCH(dt, hipLaunchKernelGGL(k_rmsnorm_bwd<T>, dim3((unsigned)rows), dim3(256), 0, st,
                                       static_cast<const T*>(dy), static_cast<const T*>(x), rstd, D, gamma,
                                       static_cast<const T*>(dres), static_cast<T*>(dx)));
@@ -528,6 +720,12 @@ int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt
 int launch_cross_entropy(const void* z, nf4_dtype dt, int64_t tokens, int64_t V, const int64_t* target,
                          float* tok_loss, float* loss, void* dz, int32_t* status, hipStream_t st) {
   if (status) hipLaunchKernelGGL(k_status_zero, dim3(1), dim3(64), 0, st, status);
+  if (dt == NF4_BF16 && V % 8 == 0) {
+    hipLaunchKernelGGL(k_xent_v, dim3((unsigned)tokens), dim3(256), 0, st, static_cast<const __bf16*>(z), target, V,
+                       (float)(1.0 / (double)tokens), tok_loss, static_cast<__bf16*>(dz), status);
+    hipLaunchKernelGGL(k_xent_mean, dim3(1), dim3(64), 0, st, tok_loss, tokens, loss);
+    return launch_status();
+  }
   NF4_DISPATCH(dt, hipLaunchKernelGGL(k_xent<T>, dim3((unsigned)tokens), dim3(256), 0, st, static_cast<const T*>(z),
                                       target, V, (float)(1.0 / (double)tokens), tok_loss, static_cast<T*>(dz),
                                       status));
