@@ -224,6 +224,26 @@ __device__ __forceinline__ void fwd_load_w(const NF4View& w, const uint8_t* cons
   }
 }
 
+// Block scales of a loaded step (the D8 lookup is an LDS read, issued before
+// the step's direct activation loads: an LDS read after them would wait for them).
+template <bool DQ, int NS>
+__device__ __forceinline__ void fwd_scales(const WStep<NS>& st, const float* d8s, float mu, float (&a)[NS]) {
+#pragma unroll
+  for (int t = 0; t < NS; ++t) a[t] = DQ ? __fadd_rn(__fmul_rn(d8s[st.qa[t]], st.nv[t]), mu) : st.nv[t];
+}
+
+template <int NS>
+__device__ __forceinline__ void fwd_decode_scaled(const WStep<NS>& st, const float (&sa)[NS], bf16x8 (&bop)[NS][4]) {
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const Bf16Table tb = build_table(sa[t]);
+    bop[t][0] = decode_word(st.q[t].x, tb);
+    bop[t][1] = decode_word(st.q[t].y, tb);
+    bop[t][2] = decode_word(st.q[t].z, tb);
+    bop[t][3] = decode_word(st.q[t].w, tb);
+  }
+}
+
 template <bool DQ, int NS>
 __device__ __forceinline__ void fwd_decode(const WStep<NS>& st, const float* d8s, float mu, bf16x8 (&bop)[NS][4]) {
 #pragma unroll
@@ -251,6 +271,19 @@ __device__ __forceinline__ void fwd_mfma(const __bf16* xb, const bf16x8 (&bop)[N
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[t][j], acc[i][t], 0, 0, 0);
     }
   }
+}
+
+// Half-step barrier of k_fwd / k_bwd. Each wave issues the next activation
+// stage's direct loads first and its NCL code/scale loads for a later step
+// after them (scheduling barriers keep that order), so vmcnt(NCL) means the
+// activation stage has landed in LDS while the code loads may still be in
+// flight; lgkmcnt(0) completes the wave's LDS reads and writes before the
+// other waves go on. (A plain __syncthreads would wait for every load.)
+template <int NCL>
+__device__ __forceinline__ void small_step_barrier() {
+  static_assert(NCL < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(NCL | (7 << 4));  // vmcnt(NCL) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
 }
 
 // Forward y = x W_hat^T + s T B^T, K % 64 == 0. Tile (32 MS) x (128 NS): each of
@@ -321,18 +354,29 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   int64_t kt = 0;
   // Steady state: every load and decode of both half-steps is in range, so the
   // body has no branches (keeps the accumulators in place across iterations).
+  // (The barriers wait only for the activation loads: the code loads issued
+  // after them stay in flight into the next half-step, see small_step_barrier.)
+  constexpr int NCL = NS * (DQ ? 3 : 2);
   for (; kt + 3 < KT; kt += 2) {
+    float sc[NS];
+    fwd_scales<DQ, NS>(wa, d8s, mu, sc);
+    __builtin_amdgcn_sched_barrier(0);
     fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
+    __builtin_amdgcn_sched_barrier(0);
     fwd_load_w<DQ, NS>(w, wp, blk0, kt + 2, wb);
-    fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
+    fwd_decode_scaled<NS>(wa, sc, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
-    __syncthreads();
+    small_step_barrier<NCL>();
+    fwd_scales<DQ, NS>(wb, d8s, mu, sc);
+    __builtin_amdgcn_sched_barrier(0);
     fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
+    __builtin_amdgcn_sched_barrier(0);
     fwd_load_w<DQ, NS>(w, wp, blk0, kt + 3, wa);
-    fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
+    fwd_decode_scaled<NS>(wb, sc, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
-    __syncthreads();
+    small_step_barrier<NCL>();
   }
+  __syncthreads();
   // Last one to three steps.
   for (; kt < KT; kt += 2) {
     if (kt + 1 < KT) fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
@@ -468,8 +512,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
       nv = static_cast<const float*>(w.scales)[blk];
     }
   };
-  auto decode_store = [&](const uint4& q, uint32_t qa, float nv) __device__ {
-    const float a = DQ ? __fadd_rn(__fmul_rn(dyn8_value(qa), nv), mu) : nv;
+  // Block scale a' = fl32(fl32(D8[qa] nv) + mu). The D8 value is a gather from
+  // the constant table (a memory load), issued at the start of the half-step
+  // that decodes the block, ahead of that half-step's other loads, so its
+  // latency overlaps the MFMAs. (An LDS copy of the table would take the
+  // 256-token tile's LDS past two workgroups per CU.)
+  auto d8_of = [&](uint32_t qa) __device__ { return DQ ? dyn8_value(qa) : 0.0f; };
+  auto scale_of = [&](float d8, float nv) __device__ { return DQ ? __fadd_rn(__fmul_rn(d8, nv), mu) : nv; };
+  auto decode_store = [&](const uint4& q, float a) __device__ {
     const Bf16Table tb = build_table(a);
     const uint32_t words[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -490,15 +540,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
 #pragma unroll
   for (int i = 0; i < MS; ++i) acc[i] = f32x16{};
 
+  // operand reads are issued in groups of up to four before their MFMAs (more
+  // would cost the 256-token tile its second wave per SIMD)
+  constexpr int RG = MS < 4 ? MS : 4;
   auto mfma_step = [&](const __bf16* yb) __device__ {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wt[l32 * WTP + 8 * ((4 * g + j) ^ swz(l32))]);
 #pragma unroll
-      for (int i = 0; i < MS; ++i) {
-        const int row = 32 * i + l32;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&yb[row * 64 + 8 * ((4 * g + j) ^ swz(row))]);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+      for (int i0 = 0; i0 < MS; i0 += RG) {
+        bf16x8 a[RG];
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+          const int row = 32 * (i0 + i) + l32;
+          a[i] = *reinterpret_cast<const bf16x8*>(&yb[row * 64 + 8 * ((4 * g + j) ^ swz(row))]);
+        }
+#pragma unroll
+        for (int i = 0; i < RG; ++i)
+          acc[i0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i0 + i], 0, 0, 0);
       }
     }
   };
@@ -510,32 +569,40 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   load_w(0, qa_, sa, va);
   if (NSTEP > 1) load_w(1, qb_, sb, vb);
   __syncthreads();
-  decode_store(qa_, sa, va);
+  decode_store(qa_, scale_of(d8_of(sa), va));
 
   int64_t ns = 0;
+  constexpr int NCL = DQ ? 3 : 2;
   for (; ns + 3 < NSTEP; ns += 2) {
+    float d8 = d8_of(sb);
+    __builtin_amdgcn_sched_barrier(0);
     issue_y(ns + 1, ys1);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(ns + 2, qa_, sa, va);
     mfma_step(ys0);
-    decode_store(qb_, sb, vb);
-    __syncthreads();
+    decode_store(qb_, scale_of(d8, vb));
+    small_step_barrier<NCL>();
+    d8 = d8_of(sa);
+    __builtin_amdgcn_sched_barrier(0);
     issue_y(ns + 2, ys0);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(ns + 3, qb_, sb, vb);
     mfma_step(ys1);
-    decode_store(qa_, sa, va);
-    __syncthreads();
+    decode_store(qa_, scale_of(d8, va));
+    small_step_barrier<NCL>();
   }
+  __syncthreads();
   for (; ns < NSTEP; ns += 2) {
     if (ns + 1 < NSTEP) issue_y(ns + 1, ys1);
     if (ns + 2 < NSTEP) load_w(ns + 2, qa_, sa, va);
     mfma_step(ys0);
-    if (ns + 1 < NSTEP) decode_store(qb_, sb, vb);
+    if (ns + 1 < NSTEP) decode_store(qb_, scale_of(d8_of(sb), vb));
     __syncthreads();
     if (ns + 1 >= NSTEP) break;
     if (ns + 2 < NSTEP) issue_y(ns + 2, ys0);
     if (ns + 3 < NSTEP) load_w(ns + 3, qb_, sb, vb);
     mfma_step(ys1);
-    if (ns + 2 < NSTEP) decode_store(qa_, sa, va);
+    if (ns + 2 < NSTEP) decode_store(qa_, scale_of(d8_of(sa), va));
     __syncthreads();
   }
 
