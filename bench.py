@@ -302,6 +302,9 @@ def decoder_step_measure(dev, steps: int = 3, warmup: int = 1, seq: int = 512):
     import torch
     from qlora_adapter_amd import llama
     cfg = llama.LlamaConfig()
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
     t0 = time.perf_counter()
     m = llama.LlamaNF4(cfg, seq, device=dev)
     torch.cuda.synchronize(dev)
@@ -328,7 +331,7 @@ def decoder_step_measure(dev, steps: int = 3, warmup: int = 1, seq: int = 512):
            "ms_per_step": round(ms, 2), "tokens_per_s": round(seq / (ms * 1e-3), 1),
            "gflop_per_token": round(fpt / 1e9, 2), "effective_tflops": round(fpt * seq / (ms * 1e-3) / 1e12, 1),
            "loss_first_last": [round(float(losses[0].item()), 4), round(float(losses[-1].item()), 4)],
-           "peak_allocated_gib": round(peak_gb, 2), "build_s": round(build_s, 1)}
+           "peak_allocated_gib": round(peak_gb, 2), "build_s": round(build_s, 2)}
     del m
     torch.cuda.empty_cache()
     return out
