@@ -392,28 +392,10 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
     __syncthreads();
   }
 
-  // Split reduction: this workgroup's fp32 partial sum goes to its slice of
-  // `part`; k_split_sum adds the slices, the LoRA term and rounds once.
-  if (part) {
-    float* pz = part + (sp * M) * N;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const int64_t n = n0 + wave * WN + 32 * t + l32;
-      if (n >= N) continue;
-#pragma unroll
-      for (int i = 0; i < MS; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (m < M) pz[m * N + n] = acc[i][t][e];
-        }
-    }
-    return;
-  }
-
   // LoRA: acc += (s T[m][:]) . B[n][:], as six bf16 MFMA products of three-part
-  // splits of both factors (the products that reach fp32 precision).
-  if (r > 0) {
+  // splits of both factors (the products that reach fp32 precision). In a
+  // split reduction only part 0 adds it.
+  if (r > 0 && sp == 0) {
     for (int rho0 = 0; rho0 < r; rho0 += 16) {
       const int avail = r - (rho0 + 8 * g);
       bf16x8 b1[NS], b2[NS], b3[NS];
@@ -437,6 +419,25 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
         }
       }
     }
+  }
+
+  // Split reduction: this workgroup's fp32 partial sum goes to its slice of
+  // `part`; k_split_sum adds the slices in order and rounds once.
+  if (part) {
+    float* pz = part + (sp * M) * N;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int64_t n = n0 + wave * WN + 32 * t + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+          if (m < M) pz[m * N + n] = acc[i][t][e];
+        }
+    }
+    return;
   }
 
   // Store: element e of accumulator (i, t) is row 32 i + 8 (e / 4) + 4 g + e % 4, column l32.
@@ -608,21 +609,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
 
   const int64_t kcol = k0 + 32 * wave + l32;
   const bool kok = kcol < K;
-  // Split reduction: fp32 partial sums to this workgroup's slice of `part`.
-  if (part) {
-    if (!kok) return;
-    float* pz = part + (sp * M) * K;
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (m < M) pz[m * K + kcol] = acc[i][e];
-      }
-    return;
-  }
-  // LoRA: acc += (s U[m][:]) . A[:][k] as six bf16 products of exact splits.
-  if (r > 0) {
+  // LoRA: acc += (s U[m][:]) . A[:][k] as six bf16 products of exact splits (in
+  // a split reduction, part 0 only).
+  if (r > 0 && sp == 0) {
     for (int rho0 = 0; rho0 < r; rho0 += 16) {
       const int avail = r - (rho0 + 8 * g);
       float bv[8];
@@ -654,6 +643,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
     }
   }
   if (!kok) return;
+  // Split reduction: fp32 partial sums to this workgroup's slice of `part`.
+  if (part) {
+    float* pz = part + (sp * M) * K;
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * i + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (m < M) pz[m * K + kcol] = acc[i][e];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -1117,18 +1118,17 @@ bool use_gemm256(int64_t M, int64_t K, int64_t N, bool backward) {
          2 * M * C < (int64_t(1) << 31);
 }
 
-// Token tile (32 MS rows) and reduction split of the k_fwd / k_bwd path
-// (measured at 512 tokens over the Llama-8B projection shapes):
-//  - forward: 256-token tiles when they give >= 448 workgroups, else 128- or
-//    64-token tiles when those give >= 200, else 32. A long reduction (>= 128
-//    steps of 64) runs on 256-token tiles split in parts (about 512
-//    workgroups); a shorter one (>= 32 steps) whose tiles give < 200
-//    workgroups is split over 64-token tiles (about 256 workgroups).
-//  - input gradient: the weight slice is decoded transposed into LDS, so
-//    256-token tiles split to about 512 workgroups whenever the reduction has
-//    >= 32 steps; the forward rule for shorter ones.
-// Parts are a power of two, at most 8, of at least 8 steps; their fp32 partial
-// sums are added by k_split_sum.
+// Token tile (32 MS rows) and reduction split of the k_fwd / k_bwd path, from a
+// sweep at 512 tokens over the Llama-8B shapes. The per-lane weight decode
+// costs about as many VALU cycles per step as a 128-token tile's MFMAs, so
+// small tiles are VALU-bound: a reduction of >= 32 steps of 64 whose 128-token
+// tiles give fewer than 256 workgroups is split in parts over 128-token tiles
+// (256-token tiles when the reduction is long, >= 128 steps, or when they
+// alone give >= 200 workgroups in an input gradient), for about 512
+// workgroups. Otherwise: 256-token tiles when they give >= 448 workgroups,
+// else 128 or 64 when those give >= 200, else 32. Parts are a power of two, at
+// most 8, of at least 8 steps; their fp32 partial sums are added by
+// k_split_sum (part 0 carries the LoRA term).
 struct SmallPlan {
   int ms;
   int nsplit;
@@ -1151,29 +1151,25 @@ SmallPlan small_plan(int64_t M, int64_t K, int64_t N, bool backward) {
     p.ms = 4;
   else if (wg(2) >= 200)
     p.ms = 2;
-  if (C % 4 != 0) return p;
+  if (C % 4 != 0 || steps < 32) return p;
   int64_t ns = 1;
-  if ((backward && steps >= 32) || steps >= 128) {
+  if (steps >= 128 || (backward && wg(8) >= 200)) {
     p.ms = 8;
     ns = parts(512, 8);
-  } else if (steps >= 32 && wg(p.ms) < 200) {
-    if (p.ms < 2) p.ms = 2;
-    ns = parts(256, p.ms);
+  } else if (wg(4) < 256) {
+    p.ms = 4;
+    ns = parts(512, 4);
   }
   if (ns >= 2) p.nsplit = (int)ceil_div(steps, ceil_div(steps, ns));  // every part non-empty
   return p;
 }
 
-// out[m][c] = bf16(sum_p part[p][m][c] + s sum_rho side[m][rho] F(rho, c)) with
-// F = B[c][rho] (forward) or A[rho][c] (input gradient); parts added in index
-// order. Four consecutive columns per thread (C % 4 == 0).
-template <bool BWD>
+// out[m][c] = bf16(sum_p part[p][m][c]), parts added in index order (part 0
+// already holds the LoRA term). Four consecutive columns per thread (C % 4 == 0).
 __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int nsplit, int64_t M, int64_t C,
-                                                   const float* __restrict__ side, const float* __restrict__ F, int r,
-                                                   float s, __bf16* __restrict__ out) {
+                                                   __bf16* __restrict__ out) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q * 4 >= M * C) return;
-  const int64_t m = (q * 4) / C, c0 = q * 4 - m * C;
   f32x4 v = *reinterpret_cast<const f32x4*>(part + q * 4);
   for (int p = 1; p < nsplit; ++p) {
     const f32x4 u = *reinterpret_cast<const f32x4*>(part + (int64_t)p * M * C + q * 4);
@@ -1181,16 +1177,6 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
     v[1] += u[1];
     v[2] += u[2];
     v[3] += u[3];
-  }
-  if (r > 0) {
-    float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int rho = 0; rho < r; ++rho) {
-      const float sv = s * side[m * r + rho];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) t[j] += sv * (BWD ? F[(int64_t)rho * C + c0 + j] : F[(c0 + j) * r + rho]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] += t[j];
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   u32x2 o;
@@ -1284,8 +1270,8 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
     }
 #undef NF4_BWD
     if (part)
-      hipLaunchKernelGGL(k_split_sum<true>, dim3((unsigned)ceil_div(g.M * g.K / 4, 256)), dim3(256), 0, st, part,
-                         p.nsplit, g.M, g.K, g.side, g.A, g.r, g.s, dx);
+      hipLaunchKernelGGL(k_split_sum, dim3((unsigned)ceil_div(g.M * g.K / 4, 256)), dim3(256), 0, st, part,
+                         p.nsplit, g.M, g.K, dx);
     return launch_status();
   }
   const __bf16* x = static_cast<const __bf16*>(g.a);
@@ -1308,8 +1294,8 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   }
 #undef NF4_FWD
   if (part)
-    hipLaunchKernelGGL(k_split_sum<false>, dim3((unsigned)ceil_div(g.M * g.N / 4, 256)), dim3(256), 0, st, part,
-                       p.nsplit, g.M, g.N, g.side, g.B, g.r, g.s, y);
+    hipLaunchKernelGGL(k_split_sum, dim3((unsigned)ceil_div(g.M * g.N / 4, 256)), dim3(256), 0, st, part,
+                       p.nsplit, g.M, g.N, y);
   return launch_status();
 }
 
