@@ -219,12 +219,15 @@ def test_backward_heavy_down_proj(gpu, orc):
 
 
 SPLIT = [
-    # (M, K, N, r, backward): long reductions over few output tiles, which the
-    # bf16 path splits in parts whose fp32 partial sums are added in order
+    # (M, K, N, r, backward): reductions over few output tiles, which the bf16
+    # path splits in parts whose fp32 partial sums are added in order
     (512, 14336, 4096, 16, False),   # down_proj forward at 512 tokens
     (512, 4096, 14336, 16, True),    # gate/up input gradient at 512 tokens
-    (300, 8320, 1000, 5, False),     # ragged tokens, 130 steps in 4 unequal parts, partial column tile
+    (300, 8320, 1000, 5, False),     # ragged tokens, 130 steps in unequal parts, partial column tile
     (300, 1024, 8320, 5, True),
+    (128, 4096, 1024, 16, False),    # too few tiles for the large kernel: small tiles in parts
+    (128, 1024, 4096, 16, True),
+    (100, 4096, 1024, 3, False),
 ]
 
 
