@@ -62,25 +62,28 @@ U32 = 2.0 ** -24  # unit roundoff of fp32
 U64 = 2.0 ** -53
 
 
-def adamw_bounds(p0, g, m0, v0, e_g, hp, step: int, safety: float = 2.0):
+def adamw_bounds(p0, g, m0, v0, e_g, hp, step: int, safety: float = 2.0, e_state=(0.0, 0.0, 0.0)):
     """Entrywise bounds on |gpu - oracle| for p, m, v after one AdamW update
     computed with separately rounded fp32 operations.
 
-    p0, m0, v0: fp32 inputs; g: the exact (fp64) gradient the update uses; e_g:
-    a bound on the error of the gradient the GPU forms (0 when it is an input
-    used as is). Every fp32 operation and every host constant (1 - b, 1 - lr wd,
-    lr / (1 - b1^t), 1 / sqrt(1 - b2^t)) contributes one rounding of its
-    result; errors are propagated to first order."""
+    p0, m0, v0: the oracle's inputs; g: the exact (fp64) gradient the update
+    uses; e_g: a bound on the error of the gradient the GPU forms (0 when it is
+    an input used as is); e_state: bounds on how far the GPU's own p, m, v
+    inputs already are from p0, m0, v0 (nonzero when both sides run a chain of
+    updates each on its own state). Every fp32 operation and every host
+    constant (1 - b, 1 - lr wd, lr / (1 - b1^t), 1 / sqrt(1 - b2^t)) contributes
+    one rounding of its result; errors are propagated to first order."""
     f = lambda a: np.abs(np.asarray(a, np.float64))
     m0s = np.asarray(m0, np.float64)
     p0, g, m0, v0, e_g = f(p0), np.asarray(g, np.float64), f(m0), np.asarray(v0, np.float64), f(e_g)
+    e_p0, e_m0, e_v0 = (f(e) for e in e_state)
     b1, b2 = float(np.float32(hp["beta1"])), float(np.float32(hp["beta2"]))
     lr, wd, eps = float(np.float32(hp["lr"])), float(np.float32(hp["weight_decay"])), float(np.float32(hp["eps"]))
     ag = np.abs(g)
     m1 = b1 * m0s + (1 - b1) * g
     v1 = b2 * v0 + (1 - b2) * g * g
-    e_m = (1 - b1) * e_g + 4 * U32 * (b1 * m0 + (1 - b1) * ag)
-    e_v = (1 - b2) * 2 * ag * e_g + 5 * U32 * (b2 * v0 + (1 - b2) * g * g)
+    e_m = (1 - b1) * e_g + b1 * e_m0 + 4 * U32 * (b1 * m0 + (1 - b1) * ag)
+    e_v = (1 - b2) * 2 * ag * e_g + b2 * e_v0 + 5 * U32 * (b2 * v0 + (1 - b2) * g * g)
     bc1, bc2 = 1 - b1 ** step, 1 - b2 ** step
     rb = 1 / np.sqrt(bc2)
     sv = np.sqrt(v1)
@@ -92,7 +95,7 @@ def adamw_bounds(p0, g, m0, v0, e_g, hp, step: int, safety: float = 2.0):
     e_q = e_m / den + np.abs(m1) * e_den / den ** 2 + U32 * q
     stepsz = lr / bc1
     p1 = np.abs(p0 * (1 - lr * wd)) + stepsz * q
-    e_p = 2 * U32 * p0 + stepsz * e_q + 2 * U32 * stepsz * q + U32 * p1
+    e_p = (1 - lr * wd) * e_p0 + 2 * U32 * p0 + stepsz * e_q + 2 * U32 * stepsz * q + U32 * p1
     return safety * e_p, safety * e_m, safety * e_v
 
 

@@ -67,10 +67,13 @@ def _lora_case(gpu, r, K, N, step, gs_value, fa, precond, seed=0):
     sB = _state((N, r), seed + 1, zero)
     host = {k: {n: _np(t) for n, t in st.items()} for k, st in (("A", sA), ("B", sB)) if st is not None}
     s = 2.0
-    P = None
+    P = Pn = None
     if precond:
-        Af = workloads.normal_f32((r, K), 1.0 / r, workloads.SEED_A, "cuda")
-        P = gpu.lorafa_preconditioner(Af)
+        # The oracle's preconditioner, rounded to fp32, is the input of both
+        # sides (the device's own preconditioner is checked on its own above).
+        Af = workloads.normal_f32((r, K), 1.0 / r, workloads.SEED_A, "cpu")
+        Pn = oracle.lorafa_preconditioner(_np(Af)).astype(np.float32)
+        P = torch.from_numpy(Pn).to("cuda")
     gs = None if gs_value is None else torch.full((1,), gs_value, dtype=torch.float32, device="cuda")
     kw = {}
     if sA is not None:
@@ -78,7 +81,6 @@ def _lora_case(gpu, r, K, N, step, gs_value, fa, precond, seed=0):
     gpu.lora_adamw_step(sB["p"], sB["g"], sB["m"], sB["v"], step=step, precond=P, s=s, grad_scale=gs, **HP, **kw)
     torch.cuda.synchronize()
     gsv = 1.0 if gs_value is None else gs_value
-    Pn = None if P is None else _np(P)
     hB = host["B"]
     ref = oracle.lora_adamw_step(hB["p"], hB["g"], hB["m"], hB["v"], P=Pn, s=s, step=step, grad_scale=gsv,
                                  **({} if fa else dict(A=host["A"]["p"], dA=host["A"]["g"], mA=host["A"]["m"],
@@ -122,24 +124,29 @@ def test_lorafa_without_preconditioner_updates_b_only(gpu):
 
 
 def test_chained_steps_follow_the_oracle(gpu):
-    """Three updates in a row on the device; each is checked against the oracle
-    started from the device's previous fp32 state."""
+    """Three updates in a row: the device chains its fp32 state, the oracle
+    chains its own fp64 state from the same seeded start, and each step's
+    bound carries the previous step's bound forward."""
     r, K, N = 16, 1024, 768
     sA, sB = _state((r, K), 40, True), _state((N, r), 41, True)
+    ref = {n: _np(x).astype(np.float64) for n, x in (("A", sA["p"]), ("mA", sA["m"]), ("vA", sA["v"]),
+                                                      ("B", sB["p"]), ("mB", sB["m"]), ("vB", sB["v"]))}
+    carried = {"A": (0.0, 0.0, 0.0), "B": (0.0, 0.0, 0.0)}
     for t in range(1, 4):
         dA = workloads.normal_f32((r, K), 1e-3, 700 + t, "cuda")
         dB = workloads.normal_f32((N, r), 1e-3, 800 + t, "cuda")
-        before = {n: _np(x) for n, x in (("A", sA["p"]), ("mA", sA["m"]), ("vA", sA["v"]), ("B", sB["p"]),
-                                         ("mB", sB["m"]), ("vB", sB["v"]))}
         gpu.lora_adamw_step(sB["p"], dB, sB["m"], sB["v"], step=t, A=sA["p"], dA=dA, mA=sA["m"], vA=sA["v"], **HP)
         torch.cuda.synchronize()
-        ref = oracle.lora_adamw_step(before["B"], _np(dB), before["mB"], before["vB"], A=before["A"], dA=_np(dA),
-                                     mA=before["mA"], vA=before["vA"], step=t, **HP)
+        new = oracle.lora_adamw_step(ref["B"], _np(dB), ref["mB"], ref["vB"], A=ref["A"], dA=_np(dA),
+                                     mA=ref["mA"], vA=ref["vA"], step=t, **HP)
         for side, g, st in (("A", _np(dA), sA), ("B", _np(dB), sB)):
             g64 = g.astype(np.float64)
-            b = adamw_bounds(before[side], g64, before["m" + side], before["v" + side], U32 * np.abs(g64), HP, t)
+            b = adamw_bounds(ref[side], g64, ref["m" + side], ref["v" + side], U32 * np.abs(g64), HP, t,
+                             e_state=carried[side])
             for key, name, bd in zip(("p", "m", "v"), (side, "m" + side, "v" + side), b):
-                assert_within(_np(st[key]), ref[name], bd, f"{name} t={t}")
+                assert_within(_np(st[key]), new[name], bd, f"{name} t={t}")
+            carried[side] = b
+        ref = new
 
 
 def test_llama8b_layer_adapters_one_update(gpu):
