@@ -696,12 +696,11 @@ constexpr int GT = 256;          // output tile edge
 constexpr int GSTAGE = GT * 64;  // bf16 per activation stage (and per forward weight stage)
 
 // The [64][256] input-gradient weight slice has a row pitch of WPB = 288 bf16
-// (576 bytes: row r starts 4 r 16-byte bank groups further on) and keeps chunk c
-// of row r at c ^ xbb(r), which only permutes chunks within aligned groups of 4.
-// Sixteen consecutive rows put a given chunk in sixteen different bank groups
-// (conflict-free writes); four rows 4a .. 4a + 3 put four consecutive chunks in
-// sixteen different groups (conflict-free transposing reads); and the column
-// tile enters the read address as a constant offset.
+// (576 bytes) and keeps chunk c of row r at c ^ xbb(r), which only permutes
+// chunks within aligned groups of 4, so the column tile enters the read address
+// as a constant offset. (Counters still show LDS bank conflicts on this
+// kernel's transposing reads, about a fifth of its LDS cycles; a 544-byte pitch
+// and plain reads at the same addresses measured the same.)
 constexpr int WPB = 288;
 __device__ __forceinline__ int xbb(int r) { return (r >> 2) & 3; }
 
@@ -755,13 +754,21 @@ __device__ __forceinline__ void gemm_decode_word(uint32_t word, const Bf16Table&
 // Weight column held at position p of an even/odd-ordered 8-column chunk.
 __device__ __forceinline__ int eo_col(int p) { return 2 * (p & 3) + (p >> 2); }
 
-// Activation loads of one step (NA per wave): `src` is the wave-uniform address
-// of the step's first column in the tile's first row, aoff the lanes' byte
-// offsets; instruction i of wave v fills stage rows 8 (NW i + v) .. + 7.
+// Activation loads of one step (NA per wave) through a buffer resource based at
+// the tile's first row: aoff holds the lanes' byte offsets, soff the step's
+// column offset (wave-uniform, so no per-lane address arithmetic); instruction i
+// of wave v fills stage rows 8 (NW i + v) .. + 7.
+__device__ __forceinline__ void lds_buffer_load16(const __bf16* base, int nbytes, uint32_t voff, uint32_t soff,
+                                                  __bf16* dst) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
 template <int NA, int NW>
-__device__ __forceinline__ void gemm_issue_act(const char* src, const uint32_t (&aoff)[NA], __bf16* buf, int wave) {
+__device__ __forceinline__ void gemm_issue_act(const __bf16* base, int nbytes, uint32_t soff,
+                                               const uint32_t (&aoff)[NA], __bf16* buf, int wave) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) lds_dma16(src + aoff[i], buf + (NW * i + wave) * 512);
+  for (int i = 0; i < NA; ++i) lds_buffer_load16(base, nbytes, aoff[i], soff, buf + (NW * i + wave) * 512);
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -981,7 +988,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   __shared__ __attribute__((aligned(16))) __bf16 ws0[WSTAGE];
   __shared__ __attribute__((aligned(16))) __bf16 ws1[WSTAGE];
   __shared__ float d8s[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, cw = 32 * NT * (wave >> 1);
   const int64_t R = BWD ? N : K, C = BWD ? K : N;
   const int64_t MT = (M + GT - 1) / GT, CT = (C + GT - 1) / GT;
@@ -996,7 +1003,10 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   // Activation loads: lane l of instruction i writes physical chunk l % 8 of
   // stage row 8 (NW i + wave) + l / 8, i.e. logical chunk (l % 8) ^ swz(row).
   // Rows past M are clamped (not stored).
-  const char* at = reinterpret_cast<const char*>(act + m0 * R);
+  // (every offset used stays below 256 rows x 2^23 bytes = 2^31)
+  const int64_t abytes = 2 * (M - m0) * R;
+  const __bf16* at = act + m0 * R;
+  const int an = (int)(abytes < 0x7fffffff ? abytes : 0x7fffffff);
   uint32_t aoff[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -1011,8 +1021,11 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   uint32_t cofs, blane;
   int64_t cstep, bstep;
   int wbase, wsx;
-  if (!BWD) {  // weight row c0 + tid / LPR (clamped past N), words h DW .. of block kt, h = tid % LPR
-    const int rl = tid / LPR, h = tid % LPR;
+  if (!BWD) {  // weight row c0 + rl (clamped past N), words h DW .. of block kt, h = tid % LPR
+    // Within each group of 8 rows, lane pairs take rows 0 2 4 6 1 3 5 7: the 8
+    // lanes of one 128-byte store phase then write 8 different bank groups.
+    const int t = tid / LPR, h = tid % LPR;
+    const int rl = (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1);
     const int64_t n = (c0 + rl < N) ? c0 + rl : N - 1;
     cofs = (uint32_t)(n * (K / 2) + 4 * DW * h);
     blane = (uint32_t)(n * KB);
@@ -1042,7 +1055,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   const int64_t last = KT - 1;
   const int64_t second = last < 1 ? last : 1;
   WCodes<DW> ca, cb;
-  gemm_issue_act<NA, NW>(at, aoff, as0, wave);
+  gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
   gemm_load_codes<DQ, DW>(w, w.codes, cofs, 0, blane, ca);
   gemm_load_codes<DQ, DW>(w, w.codes + second * cstep, cofs, second * bstep, blane, cb);
   __syncthreads();  // d8s
@@ -1063,7 +1076,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     // issued after them would wait for them.)
     float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_issue_act<NA, NW>(at + 128 * k1, aoff, as1, wave);
+    gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k1), aoff, as1, wave);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k2 * cstep, cofs, k2 * bstep, blane, ca);
     gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx);
@@ -1071,7 +1084,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     if (kt + 1 >= KT) break;
     sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_issue_act<NA, NW>(at + 128 * k2, aoff, as0, wave);
+    gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k2), aoff, as0, wave);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k3 * cstep, cofs, k3 * bstep, blane, cb);
     gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx);
