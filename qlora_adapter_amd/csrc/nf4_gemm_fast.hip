@@ -455,15 +455,30 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   }
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane i receives element i % 4 of the 4-element pieces addressed by lanes
+// 4 e + i / 4, e = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
+}
+
+// Chunk swizzle of the small input-gradient kernel's [64 n][32 k] weight tile
+// (four 16-byte chunks per 64-byte row, chunk c of row n at c ^ wsw(n)): the 8
+// rows of one 128-byte store phase hit 8 different bank groups, and so do the
+// two-chunk pieces of rows 4a .. 4a + 3 that one transposing read phase covers.
+__device__ __forceinline__ int wsw(int n) { return (n & 2) | ((n >> 2) & 1); }
+
 // Input gradient dX = dY W_hat + s U A, K % 64 == 0 and N % 64 == 0. Tile
 // (32 MS tokens) x 128 weight inputs k; reduction over the weight outputs n in
 // steps of 64. dY arrives by direct loads into two swizzled LDS stages. Wave w
 // owns outputs k in [32 w, 32 w + 32) of the tile: each step its lane l decodes
-// weight row n0 + l over those 32 columns (one 64-element block, one table) and
-// stores the bf16 values transposed into the wave's own [k][n] LDS tile, from
-// which the MFMA B operand (8 consecutive n per lane) is read. Only the wave
-// itself reads its tile, and a wave's LDS operations complete in order, so the
-// tile needs no barrier and a single buffer.
+// weight row n0 + l over those 32 columns (half a 64-element block, one table)
+// into the wave's own [n][k] LDS tile as four 16-byte chunks, and the MFMA B
+// operand (8 consecutive n for one k) is gathered with two transposing reads.
+// Only the wave itself reads its tile, and a wave's LDS operations complete in
+// order, so the tile needs no barrier and a single buffer.
 template <bool DQ, int MS>
 __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, int64_t M, int64_t K, int64_t N,
                                                 NF4View w, const float* __restrict__ Afac, int r, float s,
@@ -472,10 +487,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   constexpr int BM = 32 * MS, BKO = 128;
   constexpr int STAGE = BM * 64;  // bf16 per dY stage
   constexpr int YI = BM / 32;     // 1 KB direct loads per wave per stage
-  constexpr int WTP = 64;         // bf16 per row of a wave's [k][n] tile (16-byte chunks swizzled)
+  constexpr int WTP = 32;         // bf16 per row n of a wave's [n][k] tile
   __shared__ __attribute__((aligned(16))) __bf16 ys0[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 ys1[STAGE];
-  __shared__ __attribute__((aligned(16))) __bf16 wts[4][32 * WTP];
+  __shared__ __attribute__((aligned(16))) __bf16 wts[4][64 * WTP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t MT = (M + BM - 1) / BM, KTL = (K + BKO - 1) / BKO;
@@ -520,22 +535,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   // 256-token tile's LDS past two workgroups per CU.)
   auto d8_of = [&](uint32_t qa) __device__ { return DQ ? dyn8_value(qa) : 0.0f; };
   auto scale_of = [&](float d8, float nv) __device__ { return DQ ? __fadd_rn(__fmul_rn(d8, nv), mu) : nv; };
+  const int wsl = wsw(lane);
   auto decode_store = [&](const uint4& q, float a) __device__ {
     const Bf16Table tb = build_table(a);
     const uint32_t words[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // word j = columns 8j .. 8j + 7 -> tile rows k = 8j .. 8j + 7
-      const u32x4 d = __builtin_bit_cast(u32x4, decode_word(words[j], tb));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k_a = 8 * j + 2 * e, k_b = k_a + 1;
-        uint16_t* row0 = reinterpret_cast<uint16_t*>(wt + k_a * WTP + 8 * ((lane >> 3) ^ swz(k_a)) + (lane & 7));
-        uint16_t* row1 = reinterpret_cast<uint16_t*>(wt + k_b * WTP + 8 * ((lane >> 3) ^ swz(k_b)) + (lane & 7));
-        *row0 = (uint16_t)(d[e] & 0xFFFFu);
-        *row1 = (uint16_t)(d[e] >> 16);
-      }
-    }
+    for (int j = 0; j < 4; ++j)  // word j = columns 8 j .. 8 j + 7 of row n = lane
+      *reinterpret_cast<bf16x8*>(wt + lane * WTP + 8 * (j ^ wsl)) = decode_word(words[j], tb);
   };
+  // B operand of MFMA step j: lane (g, k = l32) takes n = 32 g + 8 j + 4 h + e,
+  // e = 0..3, from transposing read h; the lane's own piece is row
+  // 32 g + 8 j + 4 h + (lane % 16) / 4, columns kq .. kq + 3.
+  const int kq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 acc[MS];
 #pragma unroll
@@ -547,7 +558,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   auto mfma_step = [&](const __bf16* yb) __device__ {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wt[l32 * WTP + 8 * ((4 * g + j) ^ swz(l32))]);
+      bf16x4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = 32 * g + 8 * j + 4 * h + ((lane & 15) >> 2);
+        v[h] = lds_read_tr16(&wt[n * WTP + 8 * ((kq >> 3) ^ wsw(n)) + (kq & 7)]);
+      }
+      const bf16x8 b = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
 #pragma unroll
       for (int i0 = 0; i0 < MS; i0 += RG) {
         bf16x8 a[RG];
@@ -769,12 +786,6 @@ __device__ __forceinline__ void gemm_issue_act(const __bf16* base, int nbytes, u
                                                const uint32_t (&aoff)[NA], __bf16* buf, int wave) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) lds_buffer_load16(base, nbytes, aoff[i], soff, buf + (NW * i + wave) * 512);
-}
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
 }
 
 // Operand fragments of MFMA step j: A for the wave's MS 32-row tiles, B for
