@@ -683,13 +683,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
 
 
 // ---------------------------------------------------------------------------
-// Shared-decode GEMM for large problems: 256 x 256 output tiles, 256 threads
-// (4 waves, one per SIMD, each with the full 512-register file), reduction in
-// steps of 64. Each step the workgroup decodes its weight slice once into LDS
-// (every lane one 64-weight block, written as eight 16-byte chunks) while the
-// activation slice arrives by direct global->LDS loads; wave (wm, wn) =
-// (w % 2, w / 2) owns 128 x 128 outputs as 4 x 4 accumulators of the 32x32x16
-// bf16 MFMA (held in the accumulation registers).
+// Shared-decode GEMM for large problems: 256 x 256 output tiles, 512 threads
+// (8 waves, two per SIMD), reduction in steps of 64. Each step the workgroup
+// decodes its weight slice once into LDS (two lanes per 64-weight block, each
+// writing four 16-byte chunks) while the activation slice arrives by direct
+// global->LDS loads; wave (wm, wn) = (w % 2, w / 2) owns 128 x 64 outputs as
+// 4 x 2 accumulators of the 32x32x16 bf16 MFMA.
 //  - Forward (BWD = false): activations x [M][K], output columns are weight rows
 //    n, the decoded slice is [256 n][64 k] and the B operand (8 consecutive k of
 //    one row n) is a plain 16-byte read.
@@ -707,8 +706,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
 //    a transposed 32 x 32 tile: lane l (l % 32 = token row) holds output columns
 //    8 (e / 4) + 4 (l / 32) + e % 4 in element e, four consecutive columns per
 //    group of four elements, stored as one 8-byte write.
-//  - The decode of the next slice is spread over the MFMA steps (two code words
-//    after each group of sixteen MFMAs) so that it overlaps the matrix core.
+//  - The decode of the next slice is spread over the MFMA steps (one code word
+//    after each group of eight MFMAs) so that it overlaps the matrix core.
 constexpr int GT = 256;          // output tile edge
 constexpr int GSTAGE = GT * 64;  // bf16 per activation stage (and per forward weight stage)
 
