@@ -177,6 +177,38 @@ def test_llama8b_shapes_sampled(gpu, orc, name, N, K):
     assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
 
 
+RAGGED_LARGE = [
+    # (M, K, N): enough 256 x 256 tiles for the shared-decode kernel, with a
+    # part-filled last token tile and (first case) a part-filled column tile;
+    # the second leaves a last round of 16 tiles, run as half-height tiles
+    (2000, 1024, 4160),
+    (4000, 4096, 4352),
+]
+
+
+@pytest.mark.parametrize("M,K,N", RAGGED_LARGE)
+def test_large_ragged_sampled(gpu, orc, M, K, N):
+    """The shared-decode kernel at ragged sizes: y and dX on 24 sampled token
+    rows (always including the last few rows of the part-filled token tile)
+    against the oracle, r = 8."""
+    print(f"[linear] large ragged M={M} K={K} N={N}", flush=True)
+    r = 8
+    c = make_case(M, K, N, r, torch.bfloat16, seed=M + N)
+    s = gpu.lora_scale(16.0, r)
+    Wq = gpu.quantize(c["W"], True)
+    y, _ = gpu.linear_fwd(c["x"], Wq, c["A"], c["B"], s)
+    dx, _ = gpu.linear_bwd_input(c["dy"], Wq, c["A"], c["B"], s)
+    torch.cuda.synchronize()
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16)
+    rng = np.random.default_rng(M + K)
+    rows = np.unique(np.concatenate([rng.choice(M - 4, 20, replace=False), np.arange(M - 4, M)]))
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    y_ref, _ = orc.linear_fwd(to_np(c["x"])[rows], Wref, A, B, s)
+    dx_ref, _ = orc.linear_bwd_input(to_np(c["dy"])[rows], Wref, A, B, s)
+    assert_close(to_np(y)[rows], y_ref, "bf16", "y rows")
+    assert_close(to_np(dx)[rows], dx_ref, "bf16", "dx rows")
+
+
 @pytest.mark.parametrize("K,N,dq", [(576, 192, True), (4096, 1024, True), (640, 4096, False), (576, 1536, True)])
 def test_fused_decode_bitexact_bwd(gpu, K, N, dq):
     """With dY = I (M = N), dX[m][k] = W_hat[m][k] exactly: the weights the input
