@@ -180,9 +180,11 @@ def test_llama8b_shapes_sampled(gpu, orc, name, N, K):
 RAGGED_LARGE = [
     # (M, K, N): enough 256 x 256 tiles for the shared-decode kernel, with a
     # part-filled last token tile and (first case) a part-filled column tile;
-    # the second leaves a last round of 16 tiles, run as half-height tiles
+    # the second leaves a last round of 16 tiles, run as half-height tiles; the
+    # third (128 tiles, half the CUs) runs entirely as half-height tiles
     (2000, 1024, 4160),
     (4000, 4096, 4352),
+    (2047, 2048, 4096),
 ]
 
 
