@@ -1119,8 +1119,11 @@ bool fast_linear_applies(const LinearArgs& g) {
   return g.K % FBK == 0;
 }
 
+// Problems of more than half a round of 256 x 256 tiles (on 256 CUs) take the
+// shared-decode kernel; up to 128 tiles the small-tile kernels measured faster
+// (a 128-tile problem by 5-13% against the kernel's half-height tiles).
 #ifndef NF4_GEMM_MIN_TILES
-#define NF4_GEMM_MIN_TILES 128
+#define NF4_GEMM_MIN_TILES 129
 #endif
 
 namespace {
@@ -1240,15 +1243,14 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
     // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
     // last round of at most half the CUs is run as twice as many half tiles.
     const int64_t cus = device_cu_count();
-    // (A problem of at most half the CUs in tiles runs entirely as half tiles.)
-    const int64_t tail = tiles % cus;
+    const int64_t tail = tiles > cus ? tiles % cus : 0;
     const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
 #define NF4_GEMM(BWD, DQ, MS, NWG, TB)                                                                                 \
   hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, MS>), dim3((unsigned)(NWG)), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, \
                      g.side, o, (int64_t)(TB))
 #define NF4_GEMM_BOTH(BWD, DQ)                                          \
   do {                                                                  \
-    if (whole > 0) NF4_GEMM(BWD, DQ, 4, whole, 0);                      \
+    NF4_GEMM(BWD, DQ, 4, whole, 0);                                     \
     if (whole < tiles) NF4_GEMM(BWD, DQ, 2, 2 * (tiles - whole), whole); \
   } while (0)
     if (g.backward) {

@@ -181,7 +181,7 @@ RAGGED_LARGE = [
     # (M, K, N): enough 256 x 256 tiles for the shared-decode kernel, with a
     # part-filled last token tile and (first case) a part-filled column tile;
     # the second leaves a last round of 16 tiles, run as half-height tiles; the
-    # third (128 tiles, half the CUs) runs entirely as half-height tiles
+    # third (128 tiles) is the largest problem left to the small-tile kernels
     (2000, 1024, 4160),
     (4000, 4096, 4352),
     (2047, 2048, 4096),
@@ -190,7 +190,7 @@ RAGGED_LARGE = [
 
 @pytest.mark.parametrize("M,K,N", RAGGED_LARGE)
 def test_large_ragged_sampled(gpu, orc, M, K, N):
-    """The shared-decode kernel at ragged sizes: y and dX on 24 sampled token
+    """Large problems at ragged sizes: y and dX on 24 sampled token
     rows (always including the last few rows of the part-filled token tile)
     against the oracle, r = 8."""
     print(f"[linear] large ragged M={M} K={K} N={N}", flush=True)
