@@ -312,16 +312,21 @@ def decoder_step_measure(dev, steps: int = 3, warmup: int = 1, seq: int = 512):
     g = torch.Generator().manual_seed(31)
     ids = torch.randint(0, cfg.vocab, (seq + 1,), generator=g).to(dev)
     x, y = ids[:-1].clone(), ids[1:].clone()
+    # train_step returns the model's one loss buffer, so the first loss is copied
+    # out before the next step overwrites it (outside the timed region)
     losses = []
-    for _ in range(warmup):
-        losses.append(m.train_step(x, y))
+    for i in range(warmup):
+        loss = m.train_step(x, y)
+        if i == 0:
+            losses.append(loss.clone())
     torch.cuda.synchronize(dev)
     st = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(steps):
-        losses.append(m.train_step(x, y))
+        loss = m.train_step(x, y)
     e1.record(st)
+    losses.append(loss)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     fpt = cfg.flops_per_token()

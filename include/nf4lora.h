@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 3
+#define NF4LORA_ABI_VERSION 4
 
 enum nf4_status {
   NF4_OK = 0,
@@ -117,22 +117,38 @@ typedef struct nf4_tensor {
  * device needed. Returns NF4_EINVAL for n < 1, a bad flag or out == NULL. */
 int nf4_layout(int64_t n, int double_quant, nf4_sizes* out);
 
-/* Host copies of the library's constant code tables: nf4[16] (QLoRA normal
- * float, ascending, nf4[7] == 0) and dyn8[256] (signed dynamic tree,
- * ascending, dyn8[127] == 0, dyn8[255] == +1). Host-only. */
+/* Host copies of the library's constant code tables (Aner native adaptation
+ * qualification, key nf4: the exact 16-value NF4 codebook and the signed
+ * dynamic8 nested codebook; Soup gate results "P3 is solved": the two tables
+ * are the same for every weight): nf4[16] (QLoRA normal float, ascending,
+ * nf4[7] == 0) and dyn8[256] (signed dynamic tree, ascending, dyn8[127] == 0,
+ * dyn8[255] == +1). Both are host arrays the caller owns. Host-only; NF4_EINVAL
+ * for a NULL argument. */
 int nf4_code_tables(float nf4[16], float dyn8[256]);
 
-/* Quantize n fp32 weights `w` (device) into `out` (buffers sized by
- * nf4_layout; out->n and out->double_quant must equal n and double_quant).
- * `workspace` must hold quantize_workspace_bytes (may be NULL when that is 0).
- * `status` (optional device int32) is set to 0 and then to NF4_ENONFINITE if
- * any weight is NaN or infinite; the outputs are then unspecified.
- * Deterministic: repeated calls give identical bytes. */
+/* Quantize n fp32 weights (Aner docs "Native model adaptation and NF4",
+ * section "Packed NF4 and the portable QLoRA profile": 64-element blocks with
+ * an absolute maximum each, nearest NF4 index per element, and with double
+ * quantization the block maxima centred by their FP32 mean and coded with
+ * dynamic8 in blocks of 256). `w` is a device fp32 array of n elements, the
+ * flattened row-major matrix; `out` is a host struct whose device buffers are
+ * sized by nf4_layout (out->n and out->double_quant must equal n and
+ * double_quant). `workspace` (device, 256-byte aligned) must hold
+ * quantize_workspace_bytes (may be NULL when that is 0). `status` (optional
+ * device int32) is set to 0 and then to NF4_ENONFINITE if any weight is NaN or
+ * infinite; the outputs are then unspecified. Argument errors (NULL, n < 1,
+ * sizes that disagree, misalignment, small workspace) return before any
+ * launch. Deterministic: repeated calls give identical bytes. */
 int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* out, void* workspace,
                  size_t workspace_bytes, int32_t* status, nf4_stream_t stream);
 
-/* Decode all n weights of `w` into `out` (device, fp32 or bf16, n elements):
- * w_hat = fl32(C4[code] * a'_b), bf16 by round-to-nearest-even. */
+/* Decode all n weights of `w` into `out` (Aner native training accelerated
+ * qualification, key jit.kernel_identity: separately rounded fp32 decode
+ * steps, no fused multiply-add): w_hat = fl32(C4[code] * a'_b), bf16 output
+ * by round-to-nearest-even of w_hat. `w` is a host struct of device buffers;
+ * `out` a device array of n elements of out_dtype (F32 or BF16, else
+ * NF4_EUNSUPPORTED), 16-byte aligned. Argument errors return before any
+ * launch. */
 int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream);
 
 #define NF4_MAX_TENSORS_PER_CALL 16
@@ -163,51 +179,78 @@ int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t co
 int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype out_dtype,
                        void* out, int32_t* status, nf4_stream_t stream);
 
-/* Fused forward: y = x W_hat^T + s (x A^T) B^T, W_hat decoded inside the
- * matrix kernel (no decoded copy of W is written to memory). x [M,K] and y
- * [M,N] are `dtype` (F32: fp32 weights; BF16: weights rounded to bf16 before
- * the multiply); accumulation is fp32. r == 0 disables the adapter (A, B,
- * t_out may be NULL); r in [1, 256] requires A [r,K], B [N,r] and t_out [M,r]
- * (receives T = x A^T in fp32, kept for lora_grad). W->n must equal N*K.
- * `workspace` holds nf4_linear_workspace_bytes(M, K, N, 0) bytes (NULL when
- * that is 0). */
+/* Fused forward (Aner docs "Native model adaptation and NF4", sections
+ * "Adapter API" and "Fused GPU NF4 decodes inside the matrix kernel"):
+ * y = x W_hat^T + s (x A^T) B^T, W_hat decoded inside the matrix kernel (no
+ * decoded copy of W is written to memory). x [M,K] and y [M,N] are `dtype`
+ * (F32: fp32 weights; BF16: weights rounded to bf16 before the multiply,
+ * section "Mixed precision keeps stable state in FP32"); accumulation is fp32.
+ * W->n must equal N*K. r == 0 disables the adapter (A, B, t_out may be NULL);
+ * r in [1, min(256, K, N)] requires A [r,K] and B [N,r] (fp32). t_out [M,r]
+ * (fp32) is optional: when given it receives T = x A^T, kept for lora_grad;
+ * when NULL, T lives in the workspace for the duration of the call.
+ * `workspace` (device; a non-NULL workspace must be 256-byte aligned, else
+ * NF4_EALIGN) holds
+ * nf4_linear_workspace_bytes(M, K, N, t_out ? 0 : r, 0) bytes (NULL when that
+ * is 0), else NF4_EWORKSPACE. Every argument error is returned before any
+ * launch. */
 int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
                    const float* A, const float* B, int32_t r, float s, void* y, float* t_out, void* workspace,
                    size_t workspace_bytes, nf4_stream_t stream);
 
-/* Fused input gradient through the frozen base: dX = dY W_hat + s (dY B) A.
- * dY [M,N] and dX [M,K] are `dtype`. r == 0 disables the adapter; r >= 1
- * requires A, B and u_out [M,r] (receives U = dY B in fp32). No weight
- * gradient is produced for W. `workspace` holds
- * nf4_linear_workspace_bytes(M, K, N, 1) bytes (NULL when that is 0). */
+/* Fused input gradient through the frozen base (same page, sections "Adapter
+ * API" and "LoRA FA includes gradient preconditioning": the base weight gets
+ * no gradient): dX = dY W_hat + s (dY B) A. dY [M,N] and dX [M,K] are `dtype`.
+ * r == 0 disables the adapter; r >= 1 requires A [r,K] and B [N,r]. u_out
+ * [M,r] (fp32) is optional: when given it receives U = dY B; when NULL, U
+ * lives in the workspace. `workspace` holds
+ * nf4_linear_workspace_bytes(M, K, N, u_out ? 0 : r, 1) bytes (NULL when that
+ * is 0). */
 int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W,
                          int64_t K, const float* A, const float* B, int32_t r, float s, void* dx,
                          float* u_out, void* workspace, size_t workspace_bytes, nf4_stream_t stream);
 
-/* Device workspace (bytes, 16-byte aligned) that nf4_linear_fwd (backward = 0)
- * or nf4_linear_bwd_input (backward = 1) needs in bf16 for these sizes; 0
- * for most shapes. A long reduction over few output tiles (short sequences
- * through a wide layer, e.g. 512 tokens through a 4096 x 14336 projection) is
- * split in parts whose fp32 partial sums the workspace holds; they are added
- * in a fixed order, so results stay run-to-run identical. When the value is
- * positive, a call with a NULL or smaller workspace fails with
- * NF4_EWORKSPACE; fp32 calls ignore the workspace. Host-only; a negative
- * NF4_E* code for invalid sizes. */
-int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int backward);
+/* Device workspace (bytes; pass it 256-byte aligned) that nf4_linear_fwd
+ * (backward = 0) or nf4_linear_bwd_input (backward = 1) needs for these sizes
+ * when `r_side` rank columns of the side product (T or U) are NOT returned to
+ * the caller: pass r_side = 0 when t_out / u_out is given, r_side = r when it
+ * is NULL. Two parts, each rounded up to 256 bytes: (1) bf16 only: a long
+ * reduction over few output tiles (short sequences through a wide layer, e.g.
+ * 512 tokens through a 4096 x 14336 projection) is split in parts whose fp32
+ * partial sums the workspace holds; they are added in a fixed order, so
+ * results stay run-to-run identical (0 for most shapes); (2) M * r_side fp32
+ * for the side product. A call with a NULL or smaller workspace than it needs
+ * fails with NF4_EWORKSPACE. Host-only; a negative NF4_E* code for invalid
+ * sizes. */
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r_side, int backward);
 
-/* LoRA factor gradients: dA = s U^T x [r,K] and dB = s dY^T T [N,r] (fp32),
- * sums over the M tokens in a fixed order (no atomics, run-to-run identical).
- * LoRA-FA (A frozen): pass dA == NULL and u == NULL; only dB is computed.
- * x [M,K] and dY [M,N] are `dtype`; t [M,r] and u [M,r] fp32 as produced by
- * nf4_linear_fwd / nf4_linear_bwd_input. `workspace` must hold
- * lora_grad_workspace_bytes(M, K, N, r, fa) bytes. */
-int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* t,
-              const float* u, int32_t r, float s, float* dA, float* dB, void* workspace, size_t workspace_bytes,
-              nf4_stream_t stream);
+/* LoRA factor gradients (Aner docs "Native model adaptation and NF4", sections
+ * "Adapter API" and "LoRA FA includes gradient preconditioning"):
+ * dA = s U^T x [r,K] and dB = s dY^T T [N,r] (fp32), with T = x A^T and
+ * U = dY B, sums over the M tokens in a fixed order (no atomics, run-to-run
+ * identical). x [M,K] and dY [M,N] are `dtype`; A [r,K], B [N,r], t and u
+ * [M,r] are fp32.
+ *  - LoRA-FA (A frozen): dA == NULL; only dB is computed and u, B are unused.
+ *  - t (from nf4_linear_fwd) may be NULL: T is then recomputed from x and A.
+ *  - u (from nf4_linear_bwd_input) may be NULL when dA is wanted: U is then
+ *    recomputed from dY and B.
+ *  - x is required unless LoRA-FA with t given; A is required when t is NULL;
+ *    B when u is NULL and dA is wanted (NF4_EINVAL otherwise).
+ * `workspace` (device, 256-byte aligned) must hold
+ * lora_grad_workspace_bytes(M, K, N, r, dA == NULL, recompute) bytes, where
+ * recompute has NF4_RECOMPUTE_T set when t is NULL and NF4_RECOMPUTE_U when u
+ * is NULL and dA is wanted. Every argument error is returned before any
+ * launch. */
+#define NF4_RECOMPUTE_T 1
+#define NF4_RECOMPUTE_U 2
+int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* A,
+              const float* B, const float* t, const float* u, int32_t r, float s, float* dA, float* dB,
+              void* workspace, size_t workspace_bytes, nf4_stream_t stream);
 
-/* Workspace bytes lora_grad needs for these sizes (fa != 0: LoRA-FA). Returns
- * a negative NF4_E* code for invalid sizes. Host-only. */
-int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
+/* Workspace bytes lora_grad needs for these sizes (fa != 0: LoRA-FA;
+ * recompute: NF4_RECOMPUTE_T | NF4_RECOMPUTE_U as above). Returns a negative
+ * NF4_E* code for invalid sizes. Host-only. */
+int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa, int recompute);
 
 /* Hyperparameters of one AdamW update (host struct, read during the call).
  * The update is the decoupled-decay form with bias-corrected moments:

@@ -64,25 +64,49 @@ int check_tensor(const nf4_tensor* t, int64_t n) {
 
 hipStream_t as_stream(nf4_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Bytes of an M x r fp32 side product carved from a workspace (0 when r == 0).
+int64_t side_ws_bytes(int64_t M, int32_t r) { return r > 0 ? (int64_t)round_up(sizeof(float) * (size_t)(M * r), 256) : 0; }
+
+// Sizes every linear call accepts: positive, and small enough that M * max(K, N)
+// and N * K (elements) stay below 2^62.
+bool linear_sizes_ok(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || K < 1 || N < 1) return false;
+  constexpr int64_t kLim = int64_t(1) << 62;
+  const int64_t W = K > N ? K : N;
+  return K <= kLim / N && M <= kLim / W;
+}
+
+int64_t linear_ws_bytes(nf4_dtype dt, int64_t M, int64_t K, int64_t N, int32_t r_side, bool backward) {
+  const int64_t split = dt == NF4_BF16 ? linear_fast_workspace_bytes(M, K, N, backward) : 0;
+  const int64_t split_part = split > 0 ? (int64_t)round_up((size_t)split, 256) : 0;
+  return split_part + side_ws_bytes(M, r_side);
+}
+
 int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const nf4_tensor* W, const float* A,
                   const float* B, int32_t r, float s, void* out, float* side, void* ws, size_t ws_bytes, bool backward,
                   nf4_stream_t stream) {
   if (!valid_dtype(dt)) return NF4_EUNSUPPORTED;
-  if (!a || !out || M < 1 || K < 1 || N < 1) return NF4_EINVAL;
-  if (K > INT64_MAX / N) return NF4_EINVAL;
+  if (!a || !out || !linear_sizes_ok(M, K, N)) return NF4_EINVAL;
   if (int rc = check_tensor(W, N * K)) return rc;
   if (r < 0 || r > 256) return NF4_EINVAL;
-  if (r > 0 && (!A || !B || !side || r > (K < N ? K : N))) return NF4_EINVAL;
+  if (r > 0 && (!A || !B || r > (K < N ? K : N))) return NF4_EINVAL;
   if (r > 0 && !std::isfinite(s)) return NF4_EINVAL;
   if (!aligned(a, 16) || !aligned(out, 16)) return NF4_EALIGN;
-  if (r > 0 && (!aligned(A, 4) || !aligned(B, 4) || !aligned(side, 4))) return NF4_EALIGN;
-  if (ws && !aligned(ws, 16)) return NF4_EALIGN;
-  if (dt == NF4_BF16) {
-    const int64_t need = linear_fast_workspace_bytes(M, K, N, backward);
-    if (need > 0 && (!ws || ws_bytes < (size_t)need)) return NF4_EWORKSPACE;
-  }
+  if (r > 0 && (!aligned(A, 4) || !aligned(B, 4) || (side && !aligned(side, 4)))) return NF4_EALIGN;
+  // The workspace holds the split-reduction partial sums (bf16) and, when the
+  // caller does not take the side product, that product (in its last part).
+  const int32_t r_side = (r > 0 && !side) ? r : 0;
+  const int64_t need = linear_ws_bytes(dt, M, K, N, r_side, backward);
+  if (ws && !aligned(ws, 256)) return NF4_EALIGN;
+  if (need > 0 && (!ws || ws_bytes < (size_t)need)) return NF4_EWORKSPACE;
   if (int rc = check_device()) return rc;
-  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward, ws, ws_bytes};
+  size_t split_bytes = ws_bytes;
+  if (r_side > 0) {
+    const int64_t sb = side_ws_bytes(M, r_side);
+    split_bytes = (size_t)(need - sb);
+    side = reinterpret_cast<float*>(static_cast<char*>(ws) + (need - sb));
+  }
+  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward, ws, split_bytes};
   return launch_linear(g, as_stream(stream));
 }
 
@@ -294,32 +318,56 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
   return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, workspace, workspace_bytes, true, stream);
 }
 
-int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int backward) {
-  if (M < 1 || K < 1 || N < 1 || K > INT64_MAX / N || (backward != 0 && backward != 1)) return NF4_EINVAL;
-  return linear_fast_workspace_bytes(M, K, N, backward != 0);
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r_side, int backward) {
+  if (!linear_sizes_ok(M, K, N) || r_side < 0 || r_side > 256 || (backward != 0 && backward != 1)) return NF4_EINVAL;
+  return linear_ws_bytes(NF4_BF16, M, K, N, r_side, backward != 0);
 }
 
-int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
-  if (M < 1 || K < 1 || N < 1 || r < 1 || r > 256) return NF4_EINVAL;
-  return (int64_t)lora_grad_ws(M, K, N, r, fa);
+int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa, int recompute) {
+  if (!linear_sizes_ok(M, K, N) || r < 1 || r > 256 || (fa != 0 && fa != 1)) return NF4_EINVAL;
+  if (recompute < 0 || recompute > (NF4_RECOMPUTE_T | NF4_RECOMPUTE_U)) return NF4_EINVAL;
+  int64_t bytes = (int64_t)lora_grad_ws(M, K, N, r, fa);
+  if (recompute & NF4_RECOMPUTE_T) bytes += side_ws_bytes(M, r);
+  if (!fa && (recompute & NF4_RECOMPUTE_U)) bytes += side_ws_bytes(M, r);
+  return bytes;
 }
 
-int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* t,
-              const float* u, int32_t r, float s, float* dA, float* dB, void* workspace, size_t workspace_bytes,
-              nf4_stream_t stream) {
+int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* A,
+              const float* B, const float* t, const float* u, int32_t r, float s, float* dA, float* dB,
+              void* workspace, size_t workspace_bytes, nf4_stream_t stream) {
   if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
-  if (M < 1 || K < 1 || N < 1 || r < 1 || r > 256) return NF4_EINVAL;
+  if (!linear_sizes_ok(M, K, N) || r < 1 || r > 256) return NF4_EINVAL;
   const bool fa = (dA == nullptr);
-  if (!dy || !t || !dB) return NF4_EINVAL;
-  if (!fa && (!x || !u)) return NF4_EINVAL;
-  if (!std::isfinite(s)) return NF4_EINVAL;
-  if (!aligned(dy, 16) || !aligned(t, 4) || !aligned(dB, 4)) return NF4_EALIGN;
-  if (!fa && (!aligned(x, 16) || !aligned(u, 4) || !aligned(dA, 4))) return NF4_EALIGN;
-  const size_t need = lora_grad_ws(M, K, N, r, fa);
+  const bool need_t = (t == nullptr), need_u = !fa && (u == nullptr);
+  if (!dy || !dB || !std::isfinite(s)) return NF4_EINVAL;
+  if ((!fa || need_t) && !x) return NF4_EINVAL;  // dA and a recomputed T read x
+  if ((need_t && !A) || (need_u && !B)) return NF4_EINVAL;
+  if (need_t && r > K) return NF4_EINVAL;
+  if (!aligned(dy, 16) || !aligned(dB, 4) || (t && !aligned(t, 4))) return NF4_EALIGN;
+  if (x && !aligned(x, 16)) return NF4_EALIGN;
+  if (!fa && (!aligned(dA, 4) || (u && !aligned(u, 4)))) return NF4_EALIGN;
+  if ((need_t && !aligned(A, 4)) || (need_u && !aligned(B, 4))) return NF4_EALIGN;
+  const size_t base = lora_grad_ws(M, K, N, r, fa);
+  const size_t side = (size_t)side_ws_bytes(M, r);
+  const size_t need = base + (need_t ? side : 0) + (need_u ? side : 0);
   if (!workspace || workspace_bytes < need) return NF4_EWORKSPACE;
   if (!aligned(workspace, 256)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_lora_grad(x, dy, dtype, M, K, N, t, fa ? nullptr : u, r, s, dA, dB, workspace, as_stream(stream));
+  // Recomputed side products follow the reduction partial sums in the workspace.
+  char* extra = static_cast<char*>(workspace) + base;
+  if (need_t) {  // T = x A^T
+    float* tt = reinterpret_cast<float*>(extra);
+    extra += side;
+    if (int rc = launch_side_product(x, dtype, M, K, A, r, false, tt, as_stream(stream))) return rc;
+    t = tt;
+  }
+  if (need_u) {  // U = dY B
+    float* uu = reinterpret_cast<float*>(extra);
+    if (int rc = launch_side_product(dy, dtype, M, N, B, r, true, uu, as_stream(stream))) return rc;
+    u = uu;
+  }
+  return launch_lora_grad(fa ? nullptr : x, dy, dtype, M, K, N, t, fa ? nullptr : u, r, s, dA, dB, workspace,
+                          as_stream(stream));
 }
 
 int64_t lorafa_preconditioner_workspace_bytes(int32_t r, int64_t K) {

@@ -826,10 +826,7 @@ template <bool BWD, bool DEC, int MS, int NT, int DW>
 __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[MS][NT], int lane, int wm,
                                           int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
   Bf16Table tb;
-#ifndef NF4_GEMM_PF
-#define NF4_GEMM_PF 1
-#endif
-#if NF4_GEMM_PF
+  // The operands of MFMA step j + 1 are read while step j multiplies.
   bf16x8 a[2][MS], b[2][NT];
   gemm_frags<BWD, MS, NT>(as, ws, 0, lane, wm, cw, a[0], b[0]);
 #pragma unroll
@@ -840,17 +837,6 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j & 1][t], a[j & 1][i], acc[i][t], 0, 0, 0);
-#else
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf16x8 a[MS], b[NT];
-    gemm_frags<BWD, MS, NT>(as, ws, j, lane, wm, cw, a, b);
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t], a[i], acc[i][t], 0, 0, 0);
-#endif
     if (DEC) {
       if (j == 0) tb = build_table(sc);
 #pragma unroll
@@ -1113,18 +1099,22 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
 
 }  // namespace
 
-bool fast_linear_applies(const LinearArgs& g) {
-  if (g.dtype != NF4_BF16) return false;
-  if (g.backward) return g.K % 64 == 0 && g.N % 64 == 0;
-  return g.K % FBK == 0;
+// Shapes the bf16 kernels of this file take: the reduction (K forward, N input
+// gradient) and, in the input gradient, the output width in whole 64-wide
+// blocks; k_fwd and k_bwd keep per-lane activation offsets (rows < 256 of the
+// tile times the reduction length) in 32 bits, so the reduction stays below
+// 2^22. Other shapes go to the general kernel.
+bool fast_shape_ok(int64_t K, int64_t N, bool backward) {
+  if (backward) return K % 64 == 0 && N % 64 == 0 && N < (int64_t(1) << 22);
+  return K % FBK == 0 && K < (int64_t(1) << 22);
 }
+
+bool fast_linear_applies(const LinearArgs& g) { return g.dtype == NF4_BF16 && fast_shape_ok(g.K, g.N, g.backward); }
 
 // Problems of more than half a round of 256 x 256 tiles (on 256 CUs) take the
 // shared-decode kernel; up to 128 tiles the small-tile kernels measured faster
 // (a 128-tile problem by 5-13% against the kernel's half-height tiles).
-#ifndef NF4_GEMM_MIN_TILES
-#define NF4_GEMM_MIN_TILES 129
-#endif
+constexpr int64_t kGemmMinTiles = 129;
 
 namespace {
 
@@ -1140,7 +1130,7 @@ bool use_gemm256(int64_t M, int64_t K, int64_t N, bool backward) {
   const int64_t tiles = ceil_div(M, GT) * ceil_div(C, GT);
   // (lane offsets into the activations and codes are 32-bit, the output is
   // written with 8-byte buffer stores at 31-bit offsets)
-  return tiles >= NF4_GEMM_MIN_TILES && R < (int64_t(1) << 22) && N * (K / 2) < (int64_t(1) << 32) && C % 4 == 0 &&
+  return tiles >= kGemmMinTiles && R < (int64_t(1) << 22) && N * (K / 2) < (int64_t(1) << 32) && C % 4 == 0 &&
          2 * M * C < (int64_t(1) << 31);
 }
 
@@ -1214,7 +1204,7 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
 }  // namespace
 
 int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward) {
-  if (backward ? (K % 64 != 0 || N % 64 != 0) : (K % FBK != 0)) return 0;
+  if (!fast_shape_ok(K, N, backward)) return 0;
   if (use_gemm256(M, K, N, backward)) return 0;
   const SmallPlan p = small_plan(M, K, N, backward);
   if (p.nsplit < 2) return 0;
@@ -1235,10 +1225,7 @@ int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
     const __bf16* a = static_cast<const __bf16*>(g.a);
     __bf16* o = static_cast<__bf16*>(g.out);
     const float* F = g.backward ? g.A : g.B;
-#ifndef NF4_GEMM_NT
-#define NF4_GEMM_NT 2
-#endif
-    constexpr int NT = NF4_GEMM_NT;
+    constexpr int NT = 2;  // 32x32 column tiles per wave (two waves per SIMD)
     const dim3 block(64 * (16 / NT));
     // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
     // last round of at most half the CUs is run as twice as many half tiles.

@@ -56,6 +56,11 @@ struct LinearArgs {
 // Workspace the bf16 fused path needs for these sizes (0 for most shapes).
 int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward);
 int launch_linear(const LinearArgs& a, hipStream_t s);
+// Side product alone: out[m][rho] = sum_i L[m][i] R[i][rho] (fp32 [M, r]), with
+// R[i][rho] = fac[rho][i] (backward = false: T = x A^T, I = K) or fac[i][rho]
+// (backward = true: U = dY B, I = N). Arguments are already validated.
+int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const float* fac, int32_t r, bool backward,
+                        float* out, hipStream_t s);
 
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,

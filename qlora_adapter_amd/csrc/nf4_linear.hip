@@ -630,6 +630,27 @@ int run_linear_general(const LinearArgs& g, hipStream_t st) {
 
 }  // namespace
 
+int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const float* fac, int32_t r, bool backward,
+                        float* out, hipStream_t st) {
+  // A LinearArgs that carries only what launch_side reads.
+  LinearArgs g{};
+  g.a = L;
+  g.dtype = dt;
+  g.M = M;
+  g.K = backward ? 1 : I;
+  g.N = backward ? I : 1;
+  g.A = backward ? nullptr : fac;
+  g.B = backward ? fac : nullptr;
+  g.r = r;
+  g.side = out;
+  g.backward = backward;
+  if (dt == NF4_BF16)
+    launch_side<__bf16>(g, st);
+  else
+    launch_side<float>(g, st);
+  return launch_status();
+}
+
 int launch_linear(const LinearArgs& g, hipStream_t st) {
   if (g.dtype == NF4_BF16) {
     if (fast_linear_applies(g)) {

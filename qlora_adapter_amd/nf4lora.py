@@ -88,10 +88,11 @@ def load() -> ctypes.CDLL:
             lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
                                                  F, P, P, P, ctypes.c_size_t, P]
             lib.nf4_linear_workspace_bytes.restype = I64
-            lib.nf4_linear_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
-            lib.lora_grad.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, P, I32, F, P, P, P, ctypes.c_size_t, P]
+            lib.nf4_linear_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int]
+            lib.lora_grad.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, P, P, P, I32, F, P, P, P,
+                                      ctypes.c_size_t, P]
             lib.lora_grad_workspace_bytes.restype = I64
-            lib.lora_grad_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int]
+            lib.lora_grad_workspace_bytes.argtypes = [I64, I64, I64, I32, ctypes.c_int, ctypes.c_int]
             lib.lorafa_preconditioner_workspace_bytes.restype = I64
             lib.lorafa_preconditioner_workspace_bytes.argtypes = [I32, I64]
             lib.lorafa_preconditioner.argtypes = [P, I32, I64, P, P, ctypes.c_size_t, P]
@@ -134,13 +135,30 @@ def _stream(device: torch.device):
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t
+
+
+def _arrays(*specs) -> None:
+    """Check (tensor, name, dtype, shape) specs: every dtype and exact shape
+    first, then device and contiguity, so that a wrong size is reported as such
+    before anything reaches the library (which sees only pointers and could not
+    tell). A None tensor or a None dtype/shape is skipped."""
+    for t, name, dtype, shape in specs:
+        if t is None:
+            continue
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    for t, name, _, _ in specs:
+        if t is not None:
+            _dev(t, name)
 
 
 # --------------------------------------------------------------------------- layout and tables
@@ -275,16 +293,21 @@ def embedding_rows(E: NF4Tensor, ids: torch.Tensor, dtype=torch.bfloat16, out: O
     return out
 
 
-def linear_workspace_bytes(M: int, K: int, N: int, backward: bool = False) -> int:
-    """Device workspace the bf16 linear needs for these sizes (0 for most)."""
-    v = int(load().nf4_linear_workspace_bytes(int(M), int(K), int(N), int(bool(backward))))
+def linear_workspace_bytes(M: int, K: int, N: int, backward: bool = False, r_side: int = 0) -> int:
+    """Device workspace the linear call needs for these sizes: the bf16 split
+    partial sums (0 for most shapes) plus, with r_side > 0, room for the M x
+    r_side fp32 side product when the caller does not take it (t_out / u_out
+    None)."""
+    v = int(load().nf4_linear_workspace_bytes(int(M), int(K), int(N), int(r_side), int(bool(backward))))
     if v < 0:
         _check("nf4_linear_workspace_bytes", v)
     return v
 
 
-def _linear_ws(workspace, M, K, N, backward, dtype, device):
-    need = linear_workspace_bytes(M, K, N, backward) if dtype == torch.bfloat16 else 0
+def _linear_ws(workspace, M, K, N, backward, dtype, device, r_side):
+    need = linear_workspace_bytes(M, K, N, backward, r_side)
+    if dtype != torch.bfloat16:  # no split reduction in fp32: only the side-product part
+        need -= linear_workspace_bytes(M, K, N, backward, 0)
     if workspace is None:
         if need == 0:
             return None, 0
@@ -293,25 +316,38 @@ def _linear_ws(workspace, M, K, N, backward, dtype, device):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _lora_rank(A, B, what):
+    if (A is None) != (B is None):
+        raise ValueError(f"{what}: A and B are given together or not at all")
+    return 0 if A is None else int(A.shape[0])
+
+
 def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
                s: float = 0.0, y: Optional[torch.Tensor] = None, t_out: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """y = x W^T + s (x A^T) B^T; returns (y, T) with T = x A^T (fp32) or None.
-    `workspace` (device bytes, linear_workspace_bytes(M, K, N)) is allocated
-    here when needed and not given."""
-    _dev(x, "x")
+               workspace: Optional[torch.Tensor] = None,
+               want_t: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """y = x W^T + s (x A^T) B^T; returns (y, T) with T = x A^T (fp32), or None
+    without an adapter or with want_t=False (T then stays in the workspace).
+    `workspace` (device bytes, linear_workspace_bytes) is allocated here when
+    needed and not given."""
+    if x.dim() != 2 or len(W.shape) != 2:
+        raise ValueError("x must be [M, K] and W [N, K]")
     M, K = x.shape
     N = W.shape[0]
-    r = 0 if A is None else A.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W is {tuple(W.shape)} but x has {K} columns")
+    r = _lora_rank(A, B, "linear_fwd")
+    _arrays((x, "x", None, None), (A, "A", torch.float32, (r, K) if r else None),
+            (B, "B", torch.float32, (N, r) if r else None), (y, "y", x.dtype, (M, N)),
+            (t_out, "t_out", torch.float32, (M, r)))
+    if x.dtype not in _DT:
+        raise ValueError(f"x must be bfloat16 or float32, got {x.dtype}")
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    if r and t_out is None:
+    if r and t_out is None and want_t:
         t_out = torch.empty((M, r), dtype=torch.float32, device=x.device)
-    if r:
-        _dev(A, "A", torch.float32)
-        _dev(B, "B", torch.float32)
     st = W.c_struct()
-    ws, wsb = _linear_ws(workspace, M, K, N, False, x.dtype, x.device)
+    ws, wsb = _linear_ws(workspace, M, K, N, False, x.dtype, x.device, r if (r and t_out is None) else 0)
     _check("nf4_linear_fwd", load().nf4_linear_fwd(_ptr(x), _DT[x.dtype], M, K, ctypes.byref(st), N, _ptr(A),
                                                    _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _ptr(ws), wsb,
                                                    _stream(x.device)))
@@ -320,50 +356,84 @@ def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, 
 
 def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None,
                      B: Optional[torch.Tensor] = None, s: float = 0.0, dx: Optional[torch.Tensor] = None,
-                     u_out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """dX = dY W + s (dY B) A; returns (dX, U) with U = dY B (fp32) or None.
-    `workspace`: as for linear_fwd, linear_workspace_bytes(M, K, N, True)."""
-    _dev(dy, "dy")
+                     u_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     want_u: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dX = dY W + s (dY B) A; returns (dX, U) with U = dY B (fp32), or None
+    without an adapter or with want_u=False. `workspace`: as for linear_fwd."""
+    if dy.dim() != 2 or len(W.shape) != 2:
+        raise ValueError("dy must be [M, N] and W [N, K]")
     M, N = dy.shape
     K = W.shape[1]
-    r = 0 if A is None else A.shape[0]
+    if W.shape[0] != N:
+        raise ValueError(f"W is {tuple(W.shape)} but dy has {N} columns")
+    r = _lora_rank(A, B, "linear_bwd_input")
+    _arrays((dy, "dy", None, None), (A, "A", torch.float32, (r, K) if r else None),
+            (B, "B", torch.float32, (N, r) if r else None), (dx, "dx", dy.dtype, (M, K)),
+            (u_out, "u_out", torch.float32, (M, r)))
+    if dy.dtype not in _DT:
+        raise ValueError(f"dy must be bfloat16 or float32, got {dy.dtype}")
     if dx is None:
         dx = torch.empty((M, K), dtype=dy.dtype, device=dy.device)
-    if r and u_out is None:
+    if r and u_out is None and want_u:
         u_out = torch.empty((M, r), dtype=torch.float32, device=dy.device)
     st = W.c_struct()
-    ws, wsb = _linear_ws(workspace, M, K, N, True, dy.dtype, dy.device)
+    ws, wsb = _linear_ws(workspace, M, K, N, True, dy.dtype, dy.device, r if (r and u_out is None) else 0)
     _check("nf4_linear_bwd_input",
            load().nf4_linear_bwd_input(_ptr(dy), _DT[dy.dtype], M, N, ctypes.byref(st), K, _ptr(A), _ptr(B), r,
                                        float(s), _ptr(dx), _ptr(u_out), _ptr(ws), wsb, _stream(dy.device)))
     return dx, u_out
 
 
-def lora_grad_workspace_bytes(M: int, K: int, N: int, r: int, fa: bool = False) -> int:
-    v = int(load().lora_grad_workspace_bytes(M, K, N, r, int(fa)))
+RECOMPUTE_T, RECOMPUTE_U = 1, 2
+
+
+def lora_grad_workspace_bytes(M: int, K: int, N: int, r: int, fa: bool = False, recompute: int = 0) -> int:
+    v = int(load().lora_grad_workspace_bytes(M, K, N, r, int(fa), int(recompute)))
     if v < 0:
         _check("lora_grad_workspace_bytes", v)
     return v
 
 
-def lora_grad(x: Optional[torch.Tensor], dy: torch.Tensor, T: torch.Tensor, U: Optional[torch.Tensor], s: float,
-              fa: bool = False, dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
-    """dA = s U^T x ([r,K], None for LoRA-FA) and dB = s dY^T T ([N,r])."""
-    _dev(dy, "dy")
+def lora_grad(x: Optional[torch.Tensor], dy: torch.Tensor, T: Optional[torch.Tensor], U: Optional[torch.Tensor],
+              s: float, fa: bool = False, dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+              B: Optional[torch.Tensor] = None, K: Optional[int] = None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """dA = s U^T x ([r,K], None for LoRA-FA) and dB = s dY^T T ([N,r]).
+    T (or U) may be None: it is then recomputed from x and A (or dY and B)."""
+    if dy.dim() != 2:
+        raise ValueError("dy must be [M, N]")
     M, N = dy.shape
-    r = T.shape[1]
-    K = x.shape[1] if x is not None else 1
+    r = next((int(t.shape[1]) for t in (T, U) if t is not None), None)
+    if r is None:
+        r = int(A.shape[0]) if A is not None else (int(B.shape[1]) if B is not None else 0)
+    if r < 1:
+        raise ValueError("lora_grad: the rank comes from T, U, A or B; none was given")
+    if K is None:
+        K = int(x.shape[1]) if x is not None else (int(A.shape[1]) if A is not None else 1)
+    need_t, need_u = T is None, (not fa) and U is None
+    if (not fa or need_t) and x is None:
+        raise ValueError("lora_grad: x is required for dA or to recompute T")
+    if need_t and A is None:
+        raise ValueError("lora_grad: A is required when T is None")
+    if need_u and B is None:
+        raise ValueError("lora_grad: B is required when U is None and dA is wanted")
+    _arrays((dy, "dy", None, None), (x, "x", dy.dtype, (M, K)), (T, "T", torch.float32, (M, r)),
+            (None if fa else U, "U", torch.float32, (M, r)), (A, "A", torch.float32, (r, K)),
+            (B, "B", torch.float32, (N, r)), (None if fa else dA, "dA", torch.float32, (r, K)),
+            (dB, "dB", torch.float32, (N, r)))
     if not fa and dA is None:
         dA = torch.empty((r, K), dtype=torch.float32, device=dy.device)
     if dB is None:
         dB = torch.empty((N, r), dtype=torch.float32, device=dy.device)
-    need = lora_grad_workspace_bytes(M, K, N, r, fa)
+    recompute = (RECOMPUTE_T if need_t else 0) | (RECOMPUTE_U if need_u else 0)
+    need = lora_grad_workspace_bytes(M, K, N, r, fa, recompute)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
-    _check("lora_grad", load().lora_grad(_ptr(x), _ptr(dy), _DT[dy.dtype], M, K, N, _ptr(T), _ptr(None if fa else U),
-                                         r, float(s), _ptr(None if fa else dA), _ptr(dB), _ptr(workspace), need,
+    _dev(workspace, "workspace")
+    wsb = workspace.numel() * workspace.element_size()
+    _check("lora_grad", load().lora_grad(_ptr(x), _ptr(dy), _DT[dy.dtype], M, K, N, _ptr(A if need_t else None),
+                                         _ptr(B if need_u else None), _ptr(T), _ptr(None if fa else U), r, float(s),
+                                         _ptr(None if fa else dA), _ptr(dB), _ptr(workspace), wsb,
                                          _stream(dy.device)))
     return (None if fa else dA), dB
 
@@ -399,30 +469,52 @@ def _host_pinned(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
-def _state(ad: dict, paged: bool = False) -> _LoraState:
-    B = ad["B"]
-    for name in ("B", "dB", "mB", "vB"):
-        if paged and name in ("mB", "vB"):
-            _host_pinned(ad[name], name)
-        else:
-            _dev(ad[name], name, torch.float32)
+def _grad_scale(g: Optional[torch.Tensor]) -> None:
+    if g is not None:
+        if g.numel() != 1:
+            raise ValueError(f"grad_scale must hold one element, got {g.numel()}")
+        _dev(g, "grad_scale", torch.float32)
+
+
+def _adapter_specs(B, dB, mB, vB, A, dA, mA, vA, precond, paged: bool) -> None:
+    """Shape and dtype of every adapter tensor (moments and gradients the shape
+    of their factor, P [r, r]); then device, or pinned host for paged moments."""
+    if B is None or B.dim() != 2:
+        raise ValueError("B must be a 2-D [N, r] tensor")
     N, r = B.shape
-    A = ad.get("A")
-    K = 1
+    if A is not None and (A.dim() != 2 or A.shape[0] != r):
+        raise ValueError(f"A must be [{r}, K], got {tuple(A.shape)}")
+    if A is None and any(t is not None for t in (dA, mA, vA)):
+        raise ValueError("dA, mA and vA need A")
     if A is not None:
-        for name in ("A", "dA", "mA", "vA"):
-            if ad.get(name) is None:
+        for name, t in (("dA", dA), ("mA", mA), ("vA", vA)):
+            if t is None:
                 raise ValueError(f"{name} is required when A is trained")
-            if paged and name in ("mA", "vA"):
-                _host_pinned(ad[name], name)
-            else:
-                _dev(ad[name], name, torch.float32)
-        K = A.shape[1]
-    P = ad.get("precond")
-    if P is not None:
-        _dev(P, "precond", torch.float32)
-    g = lambda k: None if ad.get(k) is None else ad[k].data_ptr()
-    return _LoraState(r, K, N, g("A"), g("dA"), g("mA"), g("vA"), g("B"), g("dB"), g("mB"), g("vB"), g("precond"),
+    shpA = None if A is None else tuple(A.shape)
+    specs = [(B, "B", torch.float32, (N, r)), (dB, "dB", torch.float32, (N, r)),
+             (A, "A", torch.float32, shpA), (dA, "dA", torch.float32, shpA),
+             (precond, "precond", torch.float32, (r, r))]
+    moments = [(mB, "mB", (N, r)), (vB, "vB", (N, r)), (mA, "mA", shpA), (vA, "vA", shpA)]
+    for t, name, shp in moments:
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shp):
+            raise ValueError(f"{name} must be float32 of shape {shp}, got {t.dtype} {tuple(t.shape)}")
+    _arrays(*specs)
+    for t, name, _ in moments:
+        if t is None:
+            continue
+        if paged:
+            _host_pinned(t, name)
+        else:
+            _dev(t, name)
+
+
+def _state(ad: dict, paged: bool = False) -> _LoraState:
+    g = lambda k: ad.get(k)
+    _adapter_specs(g("B"), g("dB"), g("mB"), g("vB"), g("A"), g("dA"), g("mA"), g("vA"), g("precond"), paged)
+    N, r = ad["B"].shape
+    K = ad["A"].shape[1] if ad.get("A") is not None else 1
+    p = lambda k: None if ad.get(k) is None else ad[k].data_ptr()
+    return _LoraState(r, K, N, p("A"), p("dA"), p("mA"), p("vA"), p("B"), p("dB"), p("mB"), p("vB"), p("precond"),
                       float(ad.get("s", 0.0)))
 
 
@@ -435,8 +527,7 @@ def lora_adamw_step_many(adapters, *, step: int, lr: float, beta1: float = 0.9, 
     adapters = list(adapters)
     if not adapters:
         return
-    if grad_scale is not None:
-        _dev(grad_scale, "grad_scale", torch.float32)
+    _grad_scale(grad_scale)
     arr = (_LoraState * len(adapters))(*[_state(a) for a in adapters])
     opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
     _check("lora_adamw_step_many", load().lora_adamw_step_many(ctypes.byref(opt), arr, len(adapters),
@@ -452,8 +543,7 @@ def lora_adamw_step_paged(adapters, *, step: int, lr: float, staging: torch.Tens
     adapters = list(adapters)
     if not adapters:
         return
-    if grad_scale is not None:
-        _dev(grad_scale, "grad_scale", torch.float32)
+    _grad_scale(grad_scale)
     _dev(staging, "staging")
     arr = (_LoraState * len(adapters))(*[_state(a, paged=True) for a in adapters])
     opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
@@ -473,20 +563,12 @@ def lora_adamw_step(B: torch.Tensor, dB: torch.Tensor, mB: torch.Tensor, vB: tor
     (LoRA-FA: A, dA, mA, vA None), with B's gradient replaced by s^-2 dB P when
     `precond` P is given. `grad_scale` is an optional one-element fp32 device
     tensor that multiplies every gradient first."""
-    for name, t in (("B", B), ("dB", dB), ("mB", mB), ("vB", vB)):
-        _dev(t, name, torch.float32)
+    if grad_scale is not None and grad_scale.numel() != 1:
+        raise ValueError(f"grad_scale must hold one element, got {grad_scale.numel()}")
+    _adapter_specs(B, dB, mB, vB, A, dA, mA, vA, precond, paged=False)
     N, r = B.shape
-    K = 1
-    if A is not None:
-        for name, t in (("A", A), ("dA", dA), ("mA", mA), ("vA", vA)):
-            if t is None:
-                raise ValueError(f"{name} is required when A is trained")
-            _dev(t, name, torch.float32)
-        K = A.shape[1]
-    if precond is not None:
-        _dev(precond, "precond", torch.float32)
-    if grad_scale is not None:
-        _dev(grad_scale, "grad_scale", torch.float32)
+    K = 1 if A is None else A.shape[1]
+    _grad_scale(grad_scale)
     opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
     _check("lora_adamw_step", load().lora_adamw_step(ctypes.byref(opt), r, K, N, _ptr(A), _ptr(dA), _ptr(mA),
                                                      _ptr(vA), _ptr(B), _ptr(dB), _ptr(mB), _ptr(vB),

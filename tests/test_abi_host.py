@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 3
+    assert lib[0].nf4lora_abi_version() == 4
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -109,22 +109,129 @@ def test_argument_errors_before_device(lib):
     assert L.nf4_linear_bwd_input(16, 5, 8, 32, ctypes.byref(w), 64, None, None, 0, 0.0, 16, None, None, 0,
                                   None) == EUNSUP
     # split-reduction workspace: 512 tokens through a 4096 x 14336 projection need one in bf16
-    assert L.nf4_linear_workspace_bytes(0, 64, 64, 0) == EINVAL
-    assert L.nf4_linear_workspace_bytes(8, 64, 64, 2) == EINVAL
-    assert L.nf4_linear_workspace_bytes(4096, 4096, 4096, 0) == 0   # large problems: no split
-    need = L.nf4_linear_workspace_bytes(512, 14336, 4096, 0)
+    assert L.nf4_linear_workspace_bytes(0, 64, 64, 0, 0) == EINVAL
+    assert L.nf4_linear_workspace_bytes(8, 64, 64, 0, 2) == EINVAL
+    assert L.nf4_linear_workspace_bytes(8, 64, 64, 257, 0) == EINVAL
+    assert L.nf4_linear_workspace_bytes(4096, 4096, 4096, 0, 0) == 0   # large problems: no split
+    need = L.nf4_linear_workspace_bytes(512, 14336, 4096, 0, 0)
     assert need > 0 and need % (512 * 4096 * 4) == 0
-    assert L.nf4_linear_workspace_bytes(512, 4096, 14336, 1) > 0
+    assert L.nf4_linear_workspace_bytes(512, 4096, 14336, 0, 1) > 0
     wd = m._Tensor(16, 16, 16, 16, 4096 * 14336, 1)
     assert L.nf4_linear_fwd(16, 1, 512, 14336, ctypes.byref(wd), 4096, None, None, 0, 0.0, 16, None, None, 0,
                             None) == EWS
     assert L.nf4_linear_fwd(16, 1, 512, 14336, ctypes.byref(wd), 4096, None, None, 0, 0.0, 16, None, 256, need - 16,
                             None) == EWS
-    # lora_grad: rank bounds, workspace
-    assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 0, 1.0, 16, 16, 256, 1 << 20, None) == EINVAL
-    assert L.lora_grad(16, 16, 1, 8, 64, 32, 16, 16, 4, 1.0, 16, 16, None, 0, None) == EWS
-    assert L.lora_grad_workspace_bytes(8, 64, 32, 0, 0) == EINVAL
-    assert L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 0) > L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 1)
+    # lora_grad(x, dy, dt, M, K, N, A, B, t, u, r, s, dA, dB, ws, ws_bytes, stream): rank bounds, workspace
+    assert L.lora_grad(16, 16, 1, 8, 64, 32, None, None, 16, 16, 0, 1.0, 16, 16, 256, 1 << 20, None) == EINVAL
+    assert L.lora_grad(16, 16, 1, 8, 64, 32, None, None, 16, 16, 4, 1.0, 16, 16, None, 0, None) == EWS
+    assert L.lora_grad_workspace_bytes(8, 64, 32, 0, 0, 0) == EINVAL
+    assert L.lora_grad_workspace_bytes(8, 64, 32, 4, 0, 4) == EINVAL
+    assert L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 0, 0) > L.lora_grad_workspace_bytes(4096, 4096, 4096,
+                                                                                                  16, 1, 0)
+
+
+def test_optional_side_products_and_recompute(lib):
+    """t_out / u_out may be NULL (the side product then lives in the workspace),
+    and lora_grad recomputes T from x and A, or U from dY and B, when they are
+    NULL; the required buffers and workspace are checked before any launch."""
+    L, m = lib
+    EINVAL, EWS = -1, -6
+    M, K, N, r = 64, 576, 192, 8
+    side = ((M * r * 4 + 255) // 256) * 256
+    # the side product adds M r fp32 (256-byte rounded) to the linear workspace
+    for bwd in (0, 1):
+        assert L.nf4_linear_workspace_bytes(M, K, N, r, bwd) == L.nf4_linear_workspace_bytes(M, K, N, 0, bwd) + side
+    w = m._Tensor(16, 16, 16, 16, K * N, 1)
+    # no t_out and no workspace: the side product has nowhere to go
+    assert L.nf4_linear_fwd(16, 1, M, K, ctypes.byref(w), N, 16, 16, r, 1.0, 16, None, None, 0, None) == EWS
+    assert L.nf4_linear_fwd(16, 1, M, K, ctypes.byref(w), N, 16, 16, r, 1.0, 16, None, 256, side - 4, None) == EWS
+    assert L.nf4_linear_bwd_input(16, 1, M, N, ctypes.byref(w), K, 16, 16, r, 1.0, 16, None, None, 0, None) == EWS
+    base = L.lora_grad_workspace_bytes(M, K, N, r, 0, 0)
+    assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 1) == base + side
+    assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 3) == base + 2 * side
+    fa = L.lora_grad_workspace_bytes(M, K, N, r, 1, 0)
+    assert L.lora_grad_workspace_bytes(M, K, N, r, 1, 3) == fa + side   # LoRA-FA never needs U
+    # T NULL needs A and x; U NULL (with dA) needs B
+    assert L.lora_grad(16, 16, 1, M, K, N, None, 16, None, 16, r, 1.0, 16, 16, 256, 1 << 24, None) == EINVAL
+    assert L.lora_grad(None, 16, 1, M, K, N, 16, 16, None, None, r, 1.0, None, 16, 256, 1 << 24, None) == EINVAL
+    assert L.lora_grad(16, 16, 1, M, K, N, 16, None, 16, None, r, 1.0, 16, 16, 256, 1 << 24, None) == EINVAL
+    # LoRA-FA with T given needs neither x nor U nor the factors
+    assert L.lora_grad(None, 16, 1, M, K, N, None, None, 16, None, r, 1.0, None, 16, None, 0, None) == EWS
+    # recomputing needs the larger workspace
+    assert L.lora_grad(16, 16, 1, M, K, N, 16, 16, None, None, r, 1.0, 16, 16, 256, base + side, None) == EWS
+
+
+def test_small_kernel_offsets_stay_32_bit(lib):
+    """The small-tile kernels keep per-lane activation offsets (tile row times
+    reduction length) in 32 bits, so a reduction of 2^22 or more leaves the fast
+    path: such shapes then need no split-reduction workspace (the general kernel
+    has none), while the longest accepted reduction still splits."""
+    L, _ = lib
+    assert L.nf4_linear_workspace_bytes(512, (1 << 22) - 64, 128, 0, 0) > 0
+    assert L.nf4_linear_workspace_bytes(512, 1 << 22, 128, 0, 0) == 0
+    assert L.nf4_linear_workspace_bytes(512, 128, (1 << 22) - 64, 0, 1) > 0
+    assert L.nf4_linear_workspace_bytes(512, 128, 1 << 22, 0, 1) == 0
+
+
+def test_binding_rejects_bad_shapes_and_dtypes(lib):
+    """The ctypes binding checks dtype and exact shape of every fp32 factor,
+    side product, gradient, output and moment before calling the library (which
+    sees only pointers): a wrong shape or dtype is a ValueError, never an
+    out-of-bounds access. Tensors here are host tensors, so a well-formed call
+    stops at the device check."""
+    import torch
+    _, m = lib
+    M, K, N, r = 8, 64, 32, 4
+    W = m.NF4Tensor(torch.zeros(K * N // 2, dtype=torch.uint8), torch.zeros(K * N // 64, dtype=torch.uint8),
+                    torch.zeros(1), torch.zeros(1), (N, K), True)
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    dy = torch.zeros(M, N, dtype=torch.bfloat16)
+    A, B = torch.zeros(r, K), torch.zeros(N, r)
+    T, U = torch.zeros(M, r), torch.zeros(M, r)
+
+    def raises(fn, *a, match, **k):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **k)
+
+    raises(m.linear_fwd, x, W, torch.zeros(r, K + 1), B, 1.0, match="A must have shape")
+    raises(m.linear_fwd, x, W, A, torch.zeros(N, r + 1), 1.0, match="B must have shape")
+    raises(m.linear_fwd, x, W, A.double(), B, 1.0, match="A must be torch.float32")
+    raises(m.linear_fwd, x, W, A, B, 1.0, y=torch.zeros(M, N + 1, dtype=torch.bfloat16), match="y must have shape")
+    raises(m.linear_fwd, x, W, A, B, 1.0, y=torch.zeros(M, N), match="y must be torch.bfloat16")
+    raises(m.linear_fwd, x, W, A, B, 1.0, t_out=torch.zeros(M, r + 1), match="t_out must have shape")
+    raises(m.linear_fwd, x, W, A, None, 1.0, match="A and B")
+    raises(m.linear_fwd, x, W, A, B, 1.0, match="x must be a device tensor")
+    raises(m.linear_bwd_input, dy, W, torch.zeros(r, K - 1), B, 1.0, match="A must have shape")
+    raises(m.linear_bwd_input, dy, W, A, B.bfloat16(), 1.0, match="B must be torch.float32")
+    raises(m.linear_bwd_input, dy, W, A, B, 1.0, dx=torch.zeros(M + 1, K, dtype=torch.bfloat16),
+           match="dx must have shape")
+    raises(m.linear_bwd_input, dy, W, A, B, 1.0, u_out=torch.zeros(M, r, dtype=torch.bfloat16),
+           match="u_out must be torch.float32")
+    raises(m.linear_bwd_input, dy, W, A, B, 1.0, match="dy must be a device tensor")
+    raises(m.lora_grad, x, dy, torch.zeros(M + 1, r), U, 1.0, match="T must have shape")
+    raises(m.lora_grad, x, dy, T, torch.zeros(M, r + 1), 1.0, match="U must have shape")
+    raises(m.lora_grad, x, dy, T, U, 1.0, dA=torch.zeros(r, K + 1), match="dA must have shape")
+    raises(m.lora_grad, x, dy, T, U, 1.0, dB=torch.zeros(N, r, dtype=torch.bfloat16), match="dB must be")
+    raises(m.lora_grad, x, dy, None, U, 1.0, match="A is required")
+    raises(m.lora_grad, x, dy, T, None, 1.0, match="B is required")
+    raises(m.lora_grad, None, dy, T, U, 1.0, match="x is required")
+    raises(m.lora_grad, x, dy, None, U, 1.0, A=torch.zeros(r + 1, K), match="A must have shape")
+    raises(m.lora_grad, x, dy, T, U, 1.0, match="dy must be a device tensor")
+    # optimizer: every gradient and moment has its factor's shape, P is [r, r]
+    g = lambda *s: torch.zeros(*s)
+    raises(m.lora_adamw_step, g(N, r), g(N, r + 1), g(N, r), g(N, r), step=1, lr=1e-3, match="dB must have shape")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N - 1, r), g(N, r), step=1, lr=1e-3, match="mB must be float32")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N, r), g(N, r), step=1, lr=1e-3, A=g(r, K), dA=g(r, K),
+           mA=g(r, K), vA=g(r, K + 1), match="vA must be float32")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N, r), g(N, r), step=1, lr=1e-3, A=g(r + 1, K), dA=g(r, K),
+           mA=g(r, K), vA=g(r, K), match="A must be")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N, r), g(N, r), step=1, lr=1e-3, precond=g(r, r + 1), s=1.0,
+           match="precond must have shape")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N, r), g(N, r), step=1, lr=1e-3, grad_scale=g(2),
+           match="grad_scale must hold one element")
+    raises(m.lora_adamw_step_many, [dict(B=g(N, r), dB=g(N, r), mB=g(N, r), vB=g(N, r + 2))], step=1, lr=1e-3,
+           match="vB must be float32")
+    raises(m.lora_adamw_step, g(N, r), g(N, r), g(N, r), g(N, r), step=1, lr=1e-3, match="B must be a device tensor")
 
 
 def test_optimizer_argument_errors_before_device(lib):

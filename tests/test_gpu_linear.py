@@ -148,7 +148,7 @@ def test_fused_decode_bitexact(gpu, K, N, dq):
     assert torch.equal(y, d.T.contiguous())
 
 
-FULL = [("q_proj", 4096, 4096), ("gate_proj", 14336, 4096), ("down_proj", 4096, 14336)]
+FULL = [("q_proj", 4096, 4096), ("k_proj", 1024, 4096), ("gate_proj", 14336, 4096), ("down_proj", 4096, 14336)]
 
 
 @pytest.mark.parametrize("name,N,K", FULL)
@@ -185,6 +185,14 @@ RAGGED_LARGE = [
     (2000, 1024, 4160),
     (4000, 4096, 4352),
     (2047, 2048, 4096),
+    # odd and single reduction-step counts on the shared-decode kernel: the
+    # forward of a 576-wide input (9 steps of 64) and of a 64-wide input (one
+    # step), the input gradient of a 576-wide output (9 steps) and of a 64-wide
+    # output (one step), each with 256 whole tiles
+    (4096, 576, 4096),
+    (4096, 64, 4096),
+    (4096, 4096, 576),
+    (4096, 4096, 64),
 ]
 
 
@@ -269,7 +277,8 @@ SPLIT = [
 def test_split_reduction(gpu, orc, M, K, N, r, bwd):
     """The split path on 32 sampled token rows against the oracle, the run-to-run
     identity of the fixed-order sum, and B = 0 giving the base result bit for
-    bit (the LoRA term is added in the final sum)."""
+    bit (part 0 of the split adds the LoRA term to its partial sum before the
+    parts are summed)."""
     print(f"[linear] split M={M} K={K} N={N} r={r} bwd={bwd}", flush=True)
     assert gpu.linear_workspace_bytes(M, K, N, bwd) > 0
     c = make_case(M, K, N, r, torch.bfloat16, seed=M + N)
@@ -292,3 +301,38 @@ def test_split_reduction(gpu, orc, M, K, N, r, bwd):
         ref, U_ref = orc.linear_fwd(to_np(a)[rows], Wref, A, B, s)
     assert_close(to_np(out)[rows], ref, "bf16", "split output rows")
     assert_close(side.cpu().numpy()[rows], U_ref, "f32", "side product rows")
+
+
+@pytest.mark.parametrize("M,K,N,r", [(512, 576, 576, 16), (4096, 4096, 1024, 16), (300, 1024, 8320, 5)])
+def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
+    """t_out / u_out may be omitted (the side product then lives in the
+    workspace): y and dX are bit-identical to the calls that return T and U.
+    lora_grad recomputes T from x and A, and U from dY and B, when they are not
+    given: bit-identical to the calls that pass them (the same kernels form
+    them), and dA, dB against the oracle; LoRA-FA recomputing T gives the same
+    dB."""
+    print(f"[linear] optional side products M={M} K={K} N={N} r={r}", flush=True)
+    c = make_case(M, K, N, r, torch.bfloat16, seed=M + 7)
+    s = gpu.lora_scale(32.0, r)
+    Wq = gpu.quantize(c["W"], True)
+    y, T = gpu.linear_fwd(c["x"], Wq, c["A"], c["B"], s)
+    y2, T2 = gpu.linear_fwd(c["x"], Wq, c["A"], c["B"], s, want_t=False)
+    dx, U = gpu.linear_bwd_input(c["dy"], Wq, c["A"], c["B"], s)
+    dx2, U2 = gpu.linear_bwd_input(c["dy"], Wq, c["A"], c["B"], s, want_u=False)
+    dA, dB = gpu.lora_grad(c["x"], c["dy"], T, U, s)
+    dA_t, dB_t = gpu.lora_grad(c["x"], c["dy"], None, U, s, A=c["A"])
+    dA_u, dB_u = gpu.lora_grad(c["x"], c["dy"], T, None, s, B=c["B"])
+    dA_tu, dB_tu = gpu.lora_grad(c["x"], c["dy"], None, None, s, A=c["A"], B=c["B"])
+    _, dB_fa = gpu.lora_grad(c["x"], c["dy"], None, None, s, fa=True, A=c["A"])
+    torch.cuda.synchronize()
+    assert T2 is None and U2 is None
+    assert torch.equal(y, y2) and torch.equal(dx, dx2)
+    for a in (dA_t, dA_u, dA_tu):
+        assert torch.equal(a.view(torch.int32), dA.view(torch.int32))
+    for b in (dB_t, dB_u, dB_tu, dB_fa):
+        assert torch.equal(b.view(torch.int32), dB.view(torch.int32))
+    x, dy = to_np(c["x"]), to_np(c["dy"])
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    dA_ref, dB_ref = orc.lora_grad(x, dy, orc.lora_down(x, A), orc.lora_up_grad(dy, B), s)
+    assert_close(dA_tu.cpu().numpy(), dA_ref, "f32", "dA (T, U recomputed)")
+    assert_close(dB_tu.cpu().numpy(), dB_ref, "f32", "dB (T, U recomputed)")

@@ -253,6 +253,63 @@ def test_paged_moments_equal_device_moments(gpu, page_bytes):
                     assert torch.equal(a[k].cpu().view(torch.int32), b[k].cpu().view(torch.int32)), (i, k, step)
 
 
+@pytest.mark.parametrize("page_bytes", [4096, 2 << 20])
+def test_paged_chain_follows_oracle(gpu, page_bytes):
+    """Two chained lora_adamw_step_paged updates (moments in pinned host
+    memory, page by page) against the fp64 oracle chaining its own state from
+    the same start: a LoRA adapter (A and B) and a LoRA-FA adapter with the
+    preconditioner (B only), with a gradient scale; each step's bound carries
+    the previous step's forward (e_state)."""
+    print(f"[adamw paged chain] page_bytes={page_bytes}", flush=True)
+    r, K, N = 16, 1024, 768
+    rf, Kf, Nf, sf = 6, 100, 37, 2.0
+    sA, sB = _state((r, K), 60, True), _state((N, r), 61, True)
+    sF = _state((Nf, rf), 62, True)
+    Af = workloads.normal_f32((rf, Kf), 1.0 / rf, workloads.SEED_A + 7, "cpu")
+    Pn = oracle.lorafa_preconditioner(_np(Af)).astype(np.float32)
+    P = torch.from_numpy(Pn).to("cuda")
+    ref = {n: _np(x).astype(np.float64) for n, x in (("A", sA["p"]), ("mA", sA["m"]), ("vA", sA["v"]),
+                                                      ("B", sB["p"]), ("mB", sB["m"]), ("vB", sB["v"]),
+                                                      ("F", sF["p"]), ("mF", sF["m"]), ("vF", sF["v"]))}
+    host = {k: _to_pinned(st["m" if k[0] == "m" else "v"]) for k, st in (("mA", sA), ("vA", sA), ("mB", sB),
+                                                                          ("vB", sB), ("mF", sF), ("vF", sF))}
+    staging = torch.empty(2 * page_bytes, dtype=torch.uint8, device="cuda")
+    gsv = 0.5
+    gs = torch.full((1,), gsv, dtype=torch.float32, device="cuda")
+    carried = {k: (0.0, 0.0, 0.0) for k in ("A", "B", "F")}
+    for t in (1, 2):
+        dA = workloads.normal_f32((r, K), 1e-3, 710 + t, "cuda")
+        dB = workloads.normal_f32((N, r), 1e-3, 810 + t, "cuda")
+        dF = workloads.normal_f32((Nf, rf), 1e-3, 910 + t, "cuda")
+        ads = [dict(A=sA["p"], dA=dA, mA=host["mA"], vA=host["vA"], B=sB["p"], dB=dB, mB=host["mB"], vB=host["vB"]),
+               dict(B=sF["p"], dB=dF, mB=host["mF"], vB=host["vF"], precond=P, s=sf)]
+        gpu.lora_adamw_step_paged(ads, step=t, grad_scale=gs, staging=staging, page_bytes=page_bytes, **HP)
+        torch.cuda.synchronize()
+        new = oracle.lora_adamw_step(ref["B"], _np(dB), ref["mB"], ref["vB"], A=ref["A"], dA=_np(dA), mA=ref["mA"],
+                                     vA=ref["vA"], step=t, grad_scale=gsv, **HP)
+        newf = oracle.lora_adamw_step(ref["F"], _np(dF), ref["mF"], ref["vF"], P=Pn, s=sf, step=t, grad_scale=gsv,
+                                      **HP)
+        got = {"A": _np(sA["p"]), "mA": host["mA"].numpy(), "vA": host["vA"].numpy(), "B": _np(sB["p"]),
+               "mB": host["mB"].numpy(), "vB": host["vB"].numpy(), "F": _np(sF["p"]), "mF": host["mF"].numpy(),
+               "vF": host["vF"].numpy()}
+        grads = {"A": _np(dA).astype(np.float64) * gsv, "B": _np(dB).astype(np.float64) * gsv}
+        for side in ("A", "B"):
+            g = grads[side]
+            b = adamw_bounds(ref[side], g, ref["m" + side], ref["v" + side], U32 * np.abs(g), HP, t,
+                             e_state=carried[side])
+            for name, bd in zip((side, "m" + side, "v" + side), b):
+                assert_within(got[name], new[name], bd, f"paged {name} t={t}")
+            carried[side] = b
+        gF = _np(dF).astype(np.float64) * gsv
+        g = oracle.lorafa_precondition(gF, Pn, sf)
+        e_g = (rf + 3) * U32 * np.abs(gF) @ np.abs(Pn.astype(np.float64)) / (sf * sf)
+        b = adamw_bounds(ref["F"], g, ref["mF"], ref["vF"], e_g, HP, t, e_state=carried["F"])
+        for name, key, bd in zip(("F", "mF", "vF"), ("B", "mB", "vB"), b):
+            assert_within(got[name], newf[key], bd, f"paged LoRA-FA {name} t={t}")
+        carried["F"] = b
+        ref = dict(new, F=newf["B"], mF=newf["mB"], vF=newf["vB"])
+
+
 def test_paged_moments_reject_pageable_memory(gpu):
     ad = _adapter(8, 64, 32, False, False, seed=3)
     ad["mB"] = ad["mB"].cpu()  # pageable host memory

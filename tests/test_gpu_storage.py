@@ -142,3 +142,53 @@ def test_dequantize_many_equals_single_calls(gpu, orc):
     for i in (0, 2):
         ref = orc.quantize(ws[i], sizes[i][1])
         np.testing.assert_array_equal(bits(many[i]), orc.dequantize(ref, "f32").view(np.uint32))
+
+
+def test_quantizer_decision_boundaries(gpu, orc):
+    """Inputs on the decision boundaries, where a reciprocal multiply and the
+    correctly rounded division pick different codes: NF4 codes of elements
+    within a few ulps of the midpoints between adjacent codes (single and
+    double quantization), and dynamic8 codes of centred block maxima within a
+    few ulps of the dynamic8 midpoints (exact mean and nested maxima by
+    construction). The GPU packs them bit for bit like the oracle, whose codes
+    the CPU tests pin to an exact nearest search with true division."""
+    from tests import boundary_sets
+    w, dis = boundary_sets.nf4_division_boundary(orc.nf4_table())
+    assert dis > 20
+    for dq in (False, True):
+        print(f"[storage] NF4 division boundaries n={w.size} dq={dq}", flush=True)
+        q, status = _gpu_quant(gpu, w, dq)
+        assert status == 0
+        _compare_packed(q, orc.quantize(w, dq), dq)
+    w, mu0, nested, dis = boundary_sets.dyn8_midpoint_maxima(orc.dyn8_table())
+    assert dis > 20
+    print(f"[storage] dynamic8 midpoint maxima n={w.size}", flush=True)
+    q, status = _gpu_quant(gpu, w, True)
+    assert status == 0
+    ref = orc.quantize(w, True)
+    assert ref["offset"][0] == mu0
+    np.testing.assert_array_equal(ref["nested"], nested)
+    _compare_packed(q, ref, True)
+    np.testing.assert_array_equal(bits(gpu.dequantize(q, torch.float32)), orc.dequantize(ref, "f32").view(np.uint32))
+
+
+def test_double_quant_decode_golden(gpu):
+    """The hand-built double-quantized matrix of tests/golden/dq_decode_golden.json,
+    whose block scales a fused multiply-add would round differently: both
+    nf4_dequantize outputs, and the weights the fused forward GEMM decodes
+    (x = I, so y = W_hat^T exactly), equal the stored bits."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "dq_decode_golden.json")))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    u32 = lambda v: np.asarray(v, np.uint32).view(np.float32)
+    W = gpu.NF4Tensor(dev(np.frombuffer(bytes.fromhex(g["codes_hex"]), np.uint8).copy()),
+                      dev(np.array(g["qabs"], np.uint8)), dev(u32([g["nested_f32_bits"]])),
+                      dev(u32([g["offset_f32_bits"]])), (5, 64), True)
+    f32 = gpu.dequantize(W, torch.float32)
+    b16 = gpu.dequantize(W, torch.bfloat16)
+    y, _ = gpu.linear_fwd(torch.eye(64, dtype=torch.bfloat16, device="cuda"), W)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(f32).ravel(), np.array(g["expected_f32_bits"], np.uint32))
+    np.testing.assert_array_equal(bits(b16).ravel(), np.array(g["expected_bf16_bits"], np.uint16))
+    np.testing.assert_array_equal(bits(y.T.contiguous()).ravel(), np.array(g["expected_bf16_bits"], np.uint16))

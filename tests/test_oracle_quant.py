@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import workloads
+from tests import boundary_sets
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "nf4_worked_example.json")))
 
@@ -201,39 +202,34 @@ def test_normalisation_is_true_division(orc):
     w * (1/a) and the correctly rounded w / a fall on different sides; the codes
     must follow w / a (reading: IEEE division, round to nearest)."""
     c4 = orc.nf4_table().astype(np.float64)
-    mids = (c4[:-1] + c4[1:]) / 2
-    rng = np.random.default_rng(123)
-    blocks_out, disagreements = [], 0
-    for a in rng.uniform(0.01, 0.1, 400).astype(np.float32):
-        cand = []
-        for mid in mids:
-            w0 = np.float32(mid * float(a))
-            for d in range(-6, 7):
-                w = np.float32(w0)
-                for _ in range(abs(d)):
-                    w = np.nextafter(w, np.float32(np.inf if d > 0 else -np.inf))
-                if abs(w) < a:
-                    cand.append(w)
-        cand = np.array(cand, np.float32)
-        x_div = (cand / a).astype(np.float32)
-        x_rcp = (cand * np.float32(np.float32(1) / a)).astype(np.float32)
-        code_div = np.argmin(np.abs(x_div[:, None].astype(np.float64) - c4[None, :]), axis=1)
-        code_rcp = np.argmin(np.abs(x_rcp[:, None].astype(np.float64) - c4[None, :]), axis=1)
-        pick = cand[code_div != code_rcp][:63]
-        disagreements += pick.size
-        if pick.size:
-            blk = np.zeros(64, np.float32)
-            blk[0] = a
-            blk[1:1 + pick.size] = pick
-            blocks_out.append(blk)
+    w, disagreements = boundary_sets.nf4_division_boundary(orc.nf4_table())
     assert disagreements > 20
-    w = np.concatenate(blocks_out)
     q = orc.quantize(w, False)
     codes = unpack(q["codes"], w.size)
     a = np.repeat(q["absmax"], 64)
     x = (w / a).astype(np.float32)
     want = np.argmin(np.abs(x[:, None].astype(np.float64) - c4[None, :]), axis=1)
     np.testing.assert_array_equal(codes, want)
+
+
+def test_nested_codes_at_dynamic8_midpoints(orc):
+    """Block maxima whose centred values sit within a few ulps of the midpoints
+    between dynamic8 codes (the mean and nested maximum are exact by
+    construction): the mean is the construction's, the nested maxima are
+    exact, and every nested code is the argmin (ties to the lower index) of
+    |D8[k] - fl32(c / m)| with true division, which differs from the
+    reciprocal-multiply code on some of them."""
+    d8 = orc.dyn8_table().astype(np.float64)
+    w, mu0, nested, disagreements = boundary_sets.dyn8_midpoint_maxima(orc.dyn8_table())
+    assert disagreements > 20
+    q = orc.quantize(w, True)
+    assert q["offset"][0] == mu0
+    np.testing.assert_array_equal(q["nested"], nested)
+    c = (q["absmax"] - mu0).astype(np.float32)       # exact: the maxima are mu0 +- d
+    m = np.repeat(nested, 256)[:c.size]
+    x = (c / m).astype(np.float32).astype(np.float64)
+    want = np.argmin(np.abs(x[:, None] - d8[None, :]), axis=1)
+    np.testing.assert_array_equal(q["qabs"], want)
 
 
 # --------------------------------------------------------------------------- selected-row embedding decode
@@ -275,3 +271,43 @@ def test_embedding_rows_reject_out_of_range(orc):
     with pytest.raises(IndexError):
         orc.embedding_rows(q, 64, [-1])
     assert orc.embedding_rows(q, 64, np.zeros(0, np.int64)).shape == (0, 64)
+
+
+# --------------------------------------------------------------------------- double-quant decode rounding
+
+DQG = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "dq_decode_golden.json")))
+
+
+def _f32(bits):
+    return np.asarray(bits, np.uint32).view(np.float32)
+
+
+def test_double_quant_decode_golden(orc):
+    """The hand-built double-quantized matrix of tests/golden/dq_decode_golden.json
+    (decode rule: separately rounded fp32 steps, no fused multiply-add). The
+    block-0 derivation is checked in integers, every stored value against exact
+    rational arithmetic on the tables (not the oracle's decoder), and the oracle's
+    dequantize against the stored bits; a fused multiply-add for the block scale
+    would change the first three blocks."""
+    from fractions import Fraction as F
+    from tests.golden import make_dq_decode_golden as gen
+    # block 0 by hand: D8[7] = -229/256, m = 13421773 * 2^-29, mu = 2^-5
+    assert F(float(orc.dyn8_table()[7])) == F(-229, 256)
+    assert F(float(_f32(DQG["nested_f32_bits"]))) == F(13421773, 2 ** 29)
+    assert -229 * 13421773 == -3073586017 and round(3073586017 / 2 ** 8 - 0.5) == 12006195
+    assert F(float(_f32(DQG["block_scale_f32_bits"][0]))) == F(16777216 - 12006195, 2 ** 29) == F(4771021, 2 ** 29)
+    assert F(float(_f32(DQG["block_scale_if_fused_f32_bits"][0]))) == F(9542041, 2 ** 30)
+    # every stored value from exact arithmetic on the two tables
+    m, blocks = gen.derive(orc.nf4_table(), orc.dyn8_table())
+    assert [gen.f32_bits(b["a_sep"]) for b in blocks] == DQG["block_scale_f32_bits"]
+    assert [gen.f32_bits(b["w"][i % 16]) for b in blocks for i in range(64)] == DQG["expected_f32_bits"]
+    assert [gen.bf16_bits(b["w"][i % 16]) for b in blocks for i in range(64)] == DQG["expected_bf16_bits"]
+    sep, fused = DQG["block_scale_f32_bits"], DQG["block_scale_if_fused_f32_bits"]
+    assert all(sep[b] != fused[b] for b in range(3)) and sep[3:] == fused[3:]
+    # the oracle decodes the packed fields to the stored bits
+    q = dict(codes=np.frombuffer(bytes.fromhex(DQG["codes_hex"]), np.uint8), qabs=np.array(DQG["qabs"], np.uint8),
+             nested=_f32([DQG["nested_f32_bits"]]), offset=_f32([DQG["offset_f32_bits"]]), n=DQG["n"],
+             double_quant=True)
+    np.testing.assert_array_equal(orc.dequantize(q, "f32").view(np.uint32), np.array(DQG["expected_f32_bits"],
+                                                                                      np.uint32))
+    np.testing.assert_array_equal(orc.dequantize(q, "bf16"), np.array(DQG["expected_bf16_bits"], np.uint16))
