@@ -706,8 +706,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
 //    a transposed 32 x 32 tile: lane l (l % 32 = token row) holds output columns
 //    8 (e / 4) + 4 (l / 32) + e % 4 in element e, four consecutive columns per
 //    group of four elements, stored as one 8-byte write.
-//  - The decode of the next slice is spread over the MFMA steps (one code word
-//    after each group of eight MFMAs) so that it overlaps the matrix core.
+//  - The decode of the next slice is spread over the first two MFMA steps (two
+//    code words after each group of eight MFMAs), so that it overlaps the
+//    matrix core and its LDS stores complete before the step barrier.
 constexpr int GT = 256;          // output tile edge
 constexpr int GSTAGE = GT * 64;  // bf16 per activation stage (and per forward weight stage)
 
@@ -820,8 +821,8 @@ __device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, i
 // One 64-deep step of the wave's 32 MS x 32 NT tile from the activation stage
 // `as` and the decoded weight stage `ws`. With DEC, the lane's DW code words of
 // the next step (codes c, block scale sc) are decoded into `wdst` along the
-// way, DW / 4 words after each MFMA step: word u goes to element
-// wbase + 8 (u ^ wsx).
+// way, DW / 2 words after each of the first two MFMA steps: word u goes to
+// element wbase + 8 (u ^ wsx).
 template <bool BWD, bool DEC, int MS, int NT, int DW>
 __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[MS][NT], int lane, int wm,
                                           int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
@@ -837,10 +838,13 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j & 1][t], a[j & 1][i], acc[i][t], 0, 0, 0);
-    if (DEC) {
+    // The decode runs in the first two MFMA steps, so that its LDS stores are
+    // issued early and complete well before the step barrier waits for them
+    // (measured faster than one word after each of the four steps).
+    if (DEC && j < 2) {
       if (j == 0) tb = build_table(sc);
 #pragma unroll
-      for (int u = j * DW / 4; u < (j + 1) * DW / 4; ++u)
+      for (int u = j * DW / 2; u < (j + 1) * DW / 2; ++u)
         gemm_decode_word<BWD>(c.q[u], tb, wdst + wbase + 8 * (u ^ wsx));
     }
   }
@@ -1096,6 +1100,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
   }
 }
+
 
 }  // namespace
 
