@@ -142,6 +142,24 @@ int nf4_code_tables(float nf4[16], float dyn8[256]);
 int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* out, void* workspace,
                  size_t workspace_bytes, int32_t* status, nf4_stream_t stream);
 
+/* nf4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same operation, arguments and results as nf4_quantize (bit for bit),
+ * without the workspace argument. Double quantization uses a fixed scratch
+ * array in device memory that the library holds on each device it runs on
+ * until the process ends (16 MiB); an n whose scratch would not fit
+ * (n > nf4_quantize_noalloc_max_elements(), about 2.66e8 weights with double
+ * quantization; single quantization needs none) returns NF4_EWORKSPACE before
+ * any launch. The call allocates nothing. Every call on one device shares the
+ * scratch: calls that overlap on a device (concurrent streams or threads) race
+ * and must be serialized by the caller. */
+int nf4_quantize_noalloc(const float* w, int64_t n, int double_quant, const nf4_tensor* out, int32_t* status,
+                         nf4_stream_t stream);
+
+/* Largest n that nf4_quantize_noalloc accepts with double quantization.
+ * Host-only. */
+int64_t nf4_quantize_noalloc_max_elements(void);
+
 /* Decode all n weights of `w` into `out` (Aner native training accelerated
  * qualification, key jit.kernel_identity: separately rounded fp32 decode
  * steps, no fused multiply-add): w_hat = fl32(C4[code] * a'_b), bf16 output

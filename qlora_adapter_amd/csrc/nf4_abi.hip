@@ -163,6 +163,36 @@ int nf4_quantize(const float* w, int64_t n, int double_quant, const nf4_tensor* 
   return launch_quantize(w, n, out, workspace, status, as_stream(stream));
 }
 
+int nf4_quantize_noalloc(const float* w, int64_t n, int double_quant, const nf4_tensor* out, int32_t* status,
+                         nf4_stream_t stream) {
+  if (!w || n < 1 || (double_quant != 0 && double_quant != 1)) return NF4_EINVAL;
+  if (int rc = check_tensor(out, n)) return rc;
+  if (out->double_quant != double_quant) return NF4_EINVAL;
+  if (!aligned(w, 16)) return NF4_EALIGN;
+  if (status && !aligned(status, 4)) return NF4_EALIGN;
+  const size_t need = quantize_ws_bytes(n, double_quant);
+  if (need > kQuantizeScratchBytes) return NF4_EWORKSPACE;
+  if (int rc = check_device()) return rc;
+  void* ws = nullptr;
+  if (need > 0) {
+    if (int rc = quantize_scratch(&ws)) return rc;
+  }
+  return launch_quantize(w, n, out, ws, status, as_stream(stream));
+}
+
+int64_t nf4_quantize_noalloc_max_elements(void) {
+  // the largest n whose double-quantization scratch fits (the need grows with n)
+  int64_t lo = 1, hi = int64_t(1) << 40;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (quantize_ws_bytes(mid, 1) <= kQuantizeScratchBytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stream_t stream) {
   if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;
   if (!w || !out) return NF4_EINVAL;

@@ -29,6 +29,11 @@ inline size_t quantize_ws_bytes(int64_t n, int dq) {
   return round_up(sizeof(float) * (size_t)nb, 256) + sizeof(double) * (size_t)nn;
 }
 
+// Size of the fixed device scratch behind nf4_quantize_noalloc, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kQuantizeScratchBytes = size_t(16) << 20;
+int quantize_scratch(void** ptr);
+
 // Launchers (return NF4_OK or NF4_EDEVICE). Arguments are already validated.
 int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s);
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s);

@@ -8,6 +8,9 @@
 // instruction; block maxima are reduced across the 8 lanes that hold one block,
 // and the fp64 sum behind the double-quantization mean is formed as a fixed
 // pairwise tree so that it is identical on every run.
+#include <atomic>
+#include <mutex>
+
 #include "nf4_device.hpp"
 
 namespace nf4 {
@@ -558,6 +561,42 @@ int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, in
                        static_cast<uint8_t*>(t->scales), t->nested, st);
   }
   return launch_status();
+}
+
+// Fixed device scratch of nf4_quantize_noalloc (the block maxima and the
+// per-group partial sums that nf4_quantize keeps in its workspace): callers
+// that cannot allocate pass no workspace, and every call on a device shares
+// this array, which stays allocated on each device the library runs on until
+// the process ends. k_quantize writes every entry a call reads before any
+// kernel reads it, so nothing needs clearing between calls; calls that overlap
+// on one device race on it.
+static __device__ __align__(256) unsigned char scratch[kQuantizeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+int quantize_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return NF4_EDEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // the device address of this device's copy of the array (the host-side
+      // name is only a stand-in and must not reach a kernel)
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return NF4_EDEVICE;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return NF4_OK;
 }
 
 static int64_t dequant_groups(int64_t n) {

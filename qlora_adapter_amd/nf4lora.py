@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
 NF4_F32, NF4_BF16 = 0, 1
 _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
-EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_dequantize", "nf4_dequantize_many",
+EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noalloc", "nf4_quantize_noalloc_max_elements",
+           "nf4_dequantize", "nf4_dequantize_many",
            "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "nf4_linear_workspace_bytes", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
             lib.nf4_layout.argtypes = [I64, ctypes.c_int, ctypes.POINTER(_Sizes)]
             lib.nf4_code_tables.argtypes = [P, P]
             lib.nf4_quantize.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, ctypes.c_size_t, P, P]
+            lib.nf4_quantize_noalloc.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, P]
+            lib.nf4_quantize_noalloc_max_elements.restype = I64
+            lib.nf4_quantize_noalloc_max_elements.argtypes = []
             lib.nf4_dequantize.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, P, P]
             lib.nf4_dequantize_many.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(ctypes.c_void_p), I32,
                                                 ctypes.c_int, P]
@@ -116,6 +120,7 @@ def load() -> ctypes.CDLL:
                 getattr(lib, fn).restype = getattr(lib, fn).restype or ctypes.c_int
             lib.lora_grad_workspace_bytes.restype = I64
             lib.lorafa_preconditioner_workspace_bytes.restype = I64
+            lib.nf4_quantize_noalloc_max_elements.restype = I64
             lib.nf4_status_string.restype = ctypes.c_char_p
             _lib = lib
     return _lib
@@ -247,6 +252,24 @@ def quantize(w: torch.Tensor, double_quant: bool = True, out: Optional[NF4Tensor
     _check("nf4_quantize", load().nf4_quantize(_ptr(w), n, int(bool(double_quant)), ctypes.byref(st),
                                                _ptr(workspace), need, _ptr(status), _stream(w.device)))
     return out
+
+
+def quantize_noalloc(w: torch.Tensor, out: NF4Tensor, status: Optional[torch.Tensor] = None) -> NF4Tensor:
+    """nf4_quantize into a caller-allocated `out` with no workspace (the library's
+    fixed device scratch): allocates nothing. Calls that overlap on one device
+    race on that scratch."""
+    _dev(w, "w", torch.float32)
+    n = w.numel()
+    if out.n != n:
+        raise ValueError(f"out holds {out.n} elements, w has {n}")
+    st = out.c_struct()
+    _check("nf4_quantize_noalloc", load().nf4_quantize_noalloc(_ptr(w), n, int(out.double_quant), ctypes.byref(st),
+                                                               _ptr(status), _stream(w.device)))
+    return out
+
+
+def quantize_noalloc_max_elements() -> int:
+    return int(load().nf4_quantize_noalloc_max_elements())
 
 
 def dequantize(t: NF4Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:

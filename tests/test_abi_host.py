@@ -375,3 +375,20 @@ def test_decoder_op_argument_errors(lib):
     assert L.nf4_cross_entropy(256, 1, 4, 0, 256, 256, 256, None, None, None) == EINVAL
     assert L.nf4_cross_entropy(256, 1, 4, 10, None, 256, 256, None, None, None) == EINVAL
     assert L.nf4_cross_entropy(256, 1, 4, 10, 256, 256, 256, None, 258, None) == EALIGN
+
+
+def test_quantize_noalloc_arguments_before_device(lib):
+    """nf4_quantize_noalloc validates as nf4_quantize does, and a matrix whose
+    double-quantization scratch exceeds the fixed device array is refused with
+    NF4_EWORKSPACE before anything touches a device."""
+    L, m = lib
+    EINVAL, EALIGN, EWS = -1, -2, -6
+    nmax = L.nf4_quantize_noalloc_max_elements()
+    assert m.layout(nmax)["quantize_workspace_bytes"] <= 16 << 20 < m.layout(nmax + 1)["quantize_workspace_bytes"]
+    t = m._Tensor(16, 16, 16, 16, nmax + 1, 1)
+    assert L.nf4_quantize_noalloc(16, nmax + 1, 1, ctypes.byref(t), None, None) == EWS
+    t = m._Tensor(16, 16, 16, 16, 64, 1)
+    assert L.nf4_quantize_noalloc(None, 64, 1, ctypes.byref(t), None, None) == EINVAL
+    assert L.nf4_quantize_noalloc(16, 64, 0, ctypes.byref(t), None, None) == EINVAL   # flag disagrees with out
+    assert L.nf4_quantize_noalloc(24, 64, 1, ctypes.byref(t), None, None) == EALIGN
+    assert L.nf4_quantize_noalloc(16, 65, 1, ctypes.byref(t), None, None) == EINVAL   # n disagrees with out
