@@ -191,19 +191,24 @@ __global__ __launch_bounds__(1024) void k_side(const T* __restrict__ L, int64_t 
   }
 }
 
-// Side product for bf16 activations and rank r <= 32 (RT = ceil(r / 16) rank
-// tiles). Same work split as k_side (16 rows per workgroup, 16 waves each
-// reducing one slice of I, slice sums added in wave order), but on the bf16
-// 16x16x32 MFMA: the fp32 factor is split into three bf16 parts whose sum is
-// exact, so every product L * R_p is exact in fp32 and the sum keeps fp32
-// accuracy. Lane l handles row l % 16 of L, rank 16 t + l % 16 of the factor
-// and reduction indices 8 (l / 16) .. + 8 of each 32-wide chunk; four chunks
-// of loads are in flight before any arithmetic.
+// Side product for bf16 activations: ranks rho0 .. rho0 + 16 RT - 1 of the r
+// (RT <= 4 rank tiles per launch; larger ranks take one launch per 64). Same
+// work split as k_side (16 rows per workgroup, 16 waves each reducing one
+// slice of I, slice sums added in wave order), but on the bf16 16x16x32 MFMA:
+// the fp32 factor is split into three bf16 parts whose sum is exact, so every
+// product L * R_p is exact in fp32 and the sum keeps fp32 accuracy. Lane l
+// handles row l % 16 of L, rank 16 t + l % 16 of the factor and reduction
+// indices 8 (l / 16) .. + 8 of each 32-wide chunk; PD chunks of loads are in
+// flight before any arithmetic (fewer for many rank tiles, to bound registers).
+// The slice sums are reduced through LDS four rank tiles at a time.
 template <bool BWD, int RT>
 __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L, int64_t M, int64_t I,
-                                                    const float* __restrict__ fac, int r, float* __restrict__ outS) {
-  constexpr int SW = 16, PD = 4;
-  __shared__ float red[SW][RT][16 * 16];
+                                                    const float* __restrict__ fac, int r, int rho0,
+                                                    float* __restrict__ outS) {
+  static_assert(RT <= 4, "rank tiles per launch");
+  constexpr int SW = 16, PD = RT <= 2 ? 4 : 2;
+  constexpr int RR = RT < 4 ? RT : 4;  // rank tiles per reduction round
+  __shared__ float red[SW][RR][16 * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * SR;
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
       if (!(cok && mok)) lv[u] = bf16x8{};
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const int rho = 16 * t + row;
+        const int rho = rho0 + 16 * t + row;
         if (BWD) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r && i + e < I) ? fac[(i + e) * r + rho] : 0.0f;
@@ -272,20 +277,24 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
     }
   }
   // accumulator element j of lane l: row 4 (l / 16) + j, column l % 16; the
-  // slice sums are added in wave order
+  // slice sums are added in wave order, RR rank tiles per round
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+  for (int t0 = 0; t0 < RT; t0 += RR) {
+    if (t0 > 0) __syncthreads();  // the previous round's sums are read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wave][t][(4 * kg + j) * 16 + row] = acc[t][j];
-  __syncthreads();
-  if (tid < 256 * RT) {
-    const int t = tid >> 8, e = tid & 255;
-    float v = 0.0f;
+    for (int q = 0; q < RR; ++q)
 #pragma unroll
-    for (int w2 = 0; w2 < SW; ++w2) v += red[w2][t][e];
-    const int64_t mm = m0 + (e >> 4);
-    const int rho = 16 * t + (e & 15);
-    if (mm < M && rho < r) outS[mm * r + rho] = v;
+      for (int j = 0; j < 4; ++j) red[wave][q][(4 * kg + j) * 16 + row] = acc[t0 + q][j];
+    __syncthreads();
+    if (tid < 256 * RR) {
+      const int q = tid >> 8, e = tid & 255;
+      float v = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < SW; ++w2) v += red[w2][q][e];
+      const int64_t mm = m0 + (e >> 4);
+      const int rho = rho0 + 16 * (t0 + q) + (e & 15);
+      if (mm < M && rho < r) outS[mm * r + rho] = v;
+    }
   }
 }
 
@@ -394,12 +403,13 @@ __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ 
   }
 }
 
-// Stage 1 on the bf16 MFMA for bf16 Q and r <= 32, same partial layout as
-// k_lora_partial. The fp32 factor P is split into three bf16 parts whose sum is
-// exact, so every product P_p[m][rho] * Q[m][j] is exact in fp32. Workgroup
-// (256-column tile, chunk c) of 4 waves; wave w owns columns 64 w .. + 64 as two
-// 32 x 32 accumulators D[rho][j] of the 32x32x16 MFMA (rank rows past r are
-// zero). The chunk is walked in steps of 32 tokens: the workgroup stages
+// Stage 1 on the bf16 MFMA for bf16 Q, same partial layout as k_lora_partial.
+// The fp32 factor P is split into three bf16 parts whose sum is exact, so every
+// product P_p[m][rho] * Q[m][j] is exact in fp32. Workgroup (256-column tile,
+// chunk c) of 4 waves; wave w owns columns 64 w .. + 64 as 2 RB accumulators
+// D[rho][j] of the 32x32x16 MFMA for the RB blocks of 32 ranks rho0 + 32 b ..
+// (rank rows past r are zero); ranks beyond 32 RB take further launches over
+// the same Q (RB = 4 covers 128 ranks). The chunk is walked in steps of 32 tokens: the workgroup stages
 // Q[m .. m + 31][j0 .. j0 + 255] (rows padded to 576 bytes, so four consecutive
 // rows fall in four different quarters of the banks) and the three parts of
 // P[m .. m + 31][0 .. 31] (64-byte rows) in LDS; both MFMA operands need 8
@@ -430,9 +440,11 @@ struct LoraProb {
 // Both reductions of one lora_grad call (dB's and dA's) share the grid:
 // workgroups [0, blocks0) take problem 0, the rest problem 1; inside a problem
 // workgroup b covers column tile b % col_tiles of chunk b / col_tiles.
-__global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int64_t blocks0, int64_t M, int r) {
+template <int RB>
+__global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int64_t blocks0, int64_t M, int r,
+                                                   int rho0) {
   __shared__ __attribute__((aligned(16))) __bf16 qs[2][32 * LQP];
-  __shared__ __attribute__((aligned(16))) __bf16 pls[2][3][32 * LPP];
+  __shared__ __attribute__((aligned(16))) __bf16 pls[2][RB][3][32 * LPP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 4, i16 = lane & 15, kg = G >> 1, hs = G & 1;
   const bool second = (int64_t)blockIdx.x >= blocks0;
@@ -450,7 +462,7 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
   // P row tid / 8, ranks 4 (tid % 8) .. + 3
   const int qrow = tid >> 5, qch = tid & 31, prow = tid >> 3, prho = 4 * (tid & 7);
   uint4 qv[4];
-  float pv[4];
+  float pv[RB][4];
   auto load = [&](int64_t m) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -469,20 +481,28 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
     }
     const int64_t mm = m + prow;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = (mm < me && prho + e < r) ? P[mm * r + prho + e] : 0.0f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rho = rho0 + 32 * rb + prho + e;
+        pv[rb][e] = (mm < me && rho < r) ? P[mm * r + rho] : 0.0f;
+      }
   };
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
   int buf = 0;
   if (mb < me) load(mb);
   for (int64_t m = mb; m < me; m += 32, buf ^= 1) {
     // stage this step
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&qs[buf][(8 * u + qrow) * LQP + 8 * qch]) = qv[u];
-    {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       uint16_t h[3][4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = pv[e];
+        const float v = pv[rb][e];
         const __bf16 a1 = (__bf16)v;
         const float r1 = v - (float)a1;
         const __bf16 a2 = (__bf16)r1;
@@ -493,22 +513,14 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
       }
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp)
-        *reinterpret_cast<uint2*>(&pls[buf][pp][prow * LPP + prho]) =
+        *reinterpret_cast<uint2*>(&pls[buf][rb][pp][prow * LPP + prho]) =
             make_uint2(h[pp][0] | ((uint32_t)h[pp][1] << 16), h[pp][2] | ((uint32_t)h[pp][3] << 16));
     }
     __syncthreads();
     if (m + 32 < me) load(m + 32);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 a[3], b[2];
-#pragma unroll
-      for (int pp = 0; pp < 3; ++pp) {
-        bf16x4l v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          v[h] = lds_tr16(&pls[buf][pp][(16 * s2 + 8 * kg + 4 * h + (i16 >> 2)) * LPP + 16 * hs + 4 * (i16 & 3)]);
-        a[pp] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-      }
+      bf16x8 b[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bf16x4l v[2];
@@ -519,23 +531,39 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
         b[t] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[t], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[t], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[t], acc[t], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb) {
+        bf16x8 a[3];
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+          bf16x4l v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v[h] = lds_tr16(
+                &pls[buf][rb][pp][(16 * s2 + 8 * kg + 4 * h + (i16 >> 2)) * LPP + 16 * hs + 4 * (i16 & 3)]);
+          a[pp] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[t], acc[rb][t], 0, 0, 0);
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[t], acc[rb][t], 0, 0, 0);
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[t], acc[rb][t], 0, 0, 0);
+        }
       }
     }
   }
-  // element e of accumulator t: rank 8 (e / 4) + 4 (lane / 32) + e % 4, column 64 wave + 32 t + lane % 32
+  // element e of accumulator (rb, t): rank rho0 + 32 rb + 8 (e / 4) + 4 (lane / 32) + e % 4, column
+  // 64 wave + 32 t + lane % 32
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int64_t j = j0 + 64 * wave + 32 * t + (lane & 31);
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rho = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (rho < r && j < J) partial[(c * r + rho) * J + j] = acc[t][e];
+    for (int t = 0; t < 2; ++t) {
+      const int64_t j = j0 + 64 * wave + 32 * t + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rho = rho0 + 32 * rb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (rho < r && j < J) partial[(c * r + rho) * J + j] = acc[rb][t][e];
+      }
     }
-  }
 }
 
 // Stage 2 of one or two reductions: out = s * (sum of the chunks in order), in
@@ -588,19 +616,22 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const T* a = static_cast<const T*>(g.a);
   const dim3 sg((unsigned)ceil_div(g.M, SR));
   if constexpr (sizeof(T) == 2) {
-    if (g.r <= 32) {
-      const float* fac = g.backward ? g.B : g.A;
-#define NF4_SIDE(BWD, RT) hipLaunchKernelGGL((k_side_bf16<BWD, RT>), sg, dim3(1024), 0, st, a, g.M, I, fac, g.r, g.side)
-      if (g.backward) {
-        if (g.r <= 16) NF4_SIDE(true, 1);
-        else NF4_SIDE(true, 2);
-      } else {
-        if (g.r <= 16) NF4_SIDE(false, 1);
-        else NF4_SIDE(false, 2);
-      }
+    const float* fac = g.backward ? g.B : g.A;
+#define NF4_SIDE(BWD, RT, R0) \
+  hipLaunchKernelGGL((k_side_bf16<BWD, RT>), sg, dim3(1024), 0, st, a, g.M, I, fac, g.r, R0, g.side)
+#define NF4_SIDE_RT(BWD)                                          \
+  do {                                                            \
+    if (g.r <= 16) NF4_SIDE(BWD, 1, 0);                           \
+    else if (g.r <= 32) NF4_SIDE(BWD, 2, 0);                      \
+    else for (int r0 = 0; r0 < g.r; r0 += 64) NF4_SIDE(BWD, 4, r0); \
+  } while (0)
+    if (g.backward)
+      NF4_SIDE_RT(true);
+    else
+      NF4_SIDE_RT(false);
+#undef NF4_SIDE_RT
 #undef NF4_SIDE
-      return;
-    }
+    return;
   }
   if (g.backward)
     hipLaunchKernelGGL((k_side<T, true>), sg, dim3(1024), 0, st, a, g.M, I, g.B, g.r, g.side);
@@ -701,8 +732,8 @@ void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, floa
   hipLaunchKernelGGL(k_lora_combine, dim3((unsigned)ceil_div((int64_t)r * J, 256)), dim3(256), 0, st, q, q, r, s);
 }
 
-// bf16 activations, r <= 32: dB's reduction (P = T, Q = dY) and, unless
-// LoRA-FA, dA's (P = U, Q = x) in one MFMA launch and one combine launch.
+// bf16 activations: dB's reduction (P = T, Q = dY) and, unless LoRA-FA, dA's
+// (P = U, Q = x) in one MFMA launch per 128 ranks and one combine launch.
 void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int64_t N, const float* t,
                     const float* u, int32_t r, float s, float* dA, float* dB, float* partA, float* partB,
                     hipStream_t st) {
@@ -711,8 +742,17 @@ void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int
   const LoraProb pa{u, x, K, chA, ceil_div(K, 256), partA};
   const int64_t blocksB = pb.col_tiles * ceil_div(M, chB);
   const int64_t blocksA = dA ? pa.col_tiles * ceil_div(M, chA) : 0;
-  hipLaunchKernelGGL(k_lora_mfma, dim3((unsigned)(blocksB + blocksA)), dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M,
-                     r);
+  // 32, 64 or 128 ranks per launch (further launches for the ranks past 128)
+  for (int r0 = 0; r0 < r; r0 += 128) {
+    const int left = r - r0;
+    const dim3 grid((unsigned)(blocksB + blocksA));
+    if (left <= 32)
+      hipLaunchKernelGGL(k_lora_mfma<1>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+    else if (left <= 64)
+      hipLaunchKernelGGL(k_lora_mfma<2>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+    else
+      hipLaunchKernelGGL(k_lora_mfma<4>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+  }
   const LoraSum qb{partB, ceil_div(M, chB), N, true, dB};
   const LoraSum qa{partA, ceil_div(M, chA), K, false, dA};
   const int64_t outs = (int64_t)r * N + (dA ? (int64_t)r * K : 0);
@@ -726,7 +766,7 @@ int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int
   float* partB = static_cast<float*>(ws);
   float* partA =
       reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunksB * r * N), 256));
-  if (dt == NF4_BF16 && r <= 32) {
+  if (dt == NF4_BF16) {
     lora_grad_mfma(static_cast<const __bf16*>(x), static_cast<const __bf16*>(dy), M, K, N, t, u, r, s, dA, dB, partA,
                    partB, st);
     return launch_status();

@@ -336,3 +336,31 @@ def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
     dA_ref, dB_ref = orc.lora_grad(x, dy, orc.lora_down(x, A), orc.lora_up_grad(dy, B), s)
     assert_close(dA_tu.cpu().numpy(), dA_ref, "f32", "dA (T, U recomputed)")
     assert_close(dB_tu.cpu().numpy(), dB_ref, "f32", "dB (T, U recomputed)")
+
+
+@pytest.mark.parametrize("M,K,N,r", [(300, 1024, 576, 64), (129, 576, 1536, 100), (200, 640, 512, 256),
+                                     (64, 256, 320, 33), (40, 448, 192, 128)])
+def test_large_ranks(gpu, orc, M, K, N, r):
+    """Ranks past 32 on the bf16 path (the side products in slices of 64 ranks,
+    the LoRA-gradient reduction in blocks of 32, 64 or 128 ranks per launch):
+    y, dX against the oracle at the bf16 bar, T, U, dA, dB at the fp32 bar, and
+    LoRA-FA's dB equal to the full call's."""
+    print(f"[linear] large rank M={M} K={K} N={N} r={r}", flush=True)
+    c = make_case(M, K, N, r, torch.bfloat16, seed=M + r)
+    s = gpu.lora_scale(16.0, r, rslora=True)
+    Wq, y, T, dx, U, (dA, dB) = run_all(gpu, c, s)
+    _, dB_fa = gpu.lora_grad(c["x"], c["dy"], T, None, s, fa=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dB.view(torch.int32), dB_fa.view(torch.int32))
+    Wref = oracle_weight(orc, c["W"], torch.bfloat16)
+    x, dy = to_np(c["x"]), to_np(c["dy"])
+    A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
+    y_ref, T_ref = orc.linear_fwd(x, Wref, A, B, s)
+    dx_ref, U_ref = orc.linear_bwd_input(dy, Wref, A, B, s)
+    assert_close(to_np(y), y_ref, "bf16", "y")
+    assert_close(to_np(dx), dx_ref, "bf16", "dx")
+    assert_close(T.cpu().numpy(), T_ref, "f32", "T")
+    assert_close(U.cpu().numpy(), U_ref, "f32", "U")
+    dA_ref, dB_ref = orc.lora_grad(x, dy, T_ref, U_ref, s)
+    assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
+    assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
