@@ -311,3 +311,42 @@ def test_double_quant_decode_golden(orc):
     np.testing.assert_array_equal(orc.dequantize(q, "f32").view(np.uint32), np.array(DQG["expected_f32_bits"],
                                                                                       np.uint32))
     np.testing.assert_array_equal(orc.dequantize(q, "bf16"), np.array(DQG["expected_bf16_bits"], np.uint16))
+
+
+# --------------------------------------------------------------------------- property test over odd sizes
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=40, deadline=None)
+@given(half=st.integers(min_value=0, max_value=49_999), seed=st.integers(min_value=0, max_value=2**31 - 1),
+       dq=st.booleans())
+def test_odd_sizes_property(orc, half, seed, dq):
+    """For any odd n in [1, 1e5] (format: Aner docs "Packed NF4 and the portable
+    QLoRA profile"): the layout sizes, a zero low nibble in the last byte,
+    codes equal to the exact nearest search, repeat quantization byte-identical,
+    and every decoded weight within the nearest-code round-trip bound."""
+    n = 2 * half + 1
+    w = workloads.weight_with_outliers((n,), seed=seed % 100_000).numpy()
+    q = orc.quantize(w, dq)
+    nb = (n + 63) // 64
+    assert q["codes"].size == (n + 1) // 2 and q["absmax"].size == nb
+    if dq:
+        assert q["qabs"].size == nb and q["nested"].size == (nb + 255) // 256 and q["offset"].size == 1
+    assert q["codes"][-1] & 0x0F == 0
+    q2 = orc.quantize(w, dq)
+    assert all(np.array_equal(q[k], q2[k]) for k in q if isinstance(q[k], np.ndarray))
+    c4 = orc.nf4_table().astype(np.float64)
+    codes = unpack(q["codes"], n)
+    a = np.repeat(q["absmax"], 64)[:n]
+    x = np.where(a > 0, (w / np.where(a > 0, a, 1)).astype(np.float32), 0).astype(np.float64)
+    want = np.where(a > 0, np.argmin(np.abs(x[:, None] - c4[None, :]), axis=1), 7)
+    np.testing.assert_array_equal(codes, want)
+    r = orc.dequantize(q).astype(np.float64)
+    eps = 2.0 ** -23
+    bound = a.astype(np.float64) * (_half_gaps(c4)[codes] + eps) + np.abs(r) * eps
+    if dq:
+        d8 = orc.dyn8_table()
+        m = np.repeat(q["nested"].astype(np.float64), 256)[:nb]
+        bound += np.abs(c4[codes]) * np.repeat(m * (_half_gaps(d8).max() + 4 * eps) + q["absmax"] * 4 * eps, 64)[:n]
+    assert np.all(np.abs(w.astype(np.float64) - r) <= bound)
