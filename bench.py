@@ -350,7 +350,11 @@ def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
     weights: far more than the 256 MB last-level cache. Each matrix decodes
     into its own output. With batch > 1, nf4_dequantize_many decodes that many
     matrices per launch (slower on matrices this large: one launch per matrix
-    measured 5.70 TB/s against 5.36-5.57 with 16 per launch). HIP events around whole passes on the launch stream."""
+    measured 5.70 TB/s against 5.36-5.57 with 16 per launch). Quantize is timed
+    both ways: one nf4_quantize call per matrix, and nf4_quantize_many over 16
+    matrices per call (three launches per call, so the double-quantization
+    tail is paid per call, not per matrix). HIP events around whole passes on
+    the launch stream."""
     import torch
     import workloads
     mats = workloads.quant_throughput_matrices()
@@ -383,6 +387,14 @@ def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
         for w, q in zip(W, Q):
             nl.quantize(w, True, out=q, workspace=ws, status=status)
 
+    many = nl.MAX_TENSORS_PER_CALL
+    ws_many = torch.empty(max(nl.quantize_many_workspace_bytes(Q[i:i + many]) for i in range(0, len(Q), many)),
+                          dtype=torch.uint8, device=dev)
+
+    def quant_many_pass():  # 16 matrices per nf4_quantize_many call
+        for i in range(0, len(W), many):
+            nl.quantize_many(W[i:i + many], True, outs=Q[i:i + many], workspace=ws_many, status=status)
+
     def deq_pass():  # `batch` matrices per launch
         for i in range(0, len(Q), batch):
             if batch == 1:
@@ -392,13 +404,16 @@ def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
 
     q_ms = run(quant_pass)
     assert int(status.item()) == 0
+    qm_ms = run(quant_many_pass)
+    assert int(status.item()) == 0
     d_ms = run(deq_pass)
     del W, Q, OUT
     torch.cuda.empty_cache()
     q_bytes, d_bytes = 4 * n_total + packed, packed + 2 * n_total
     return {"params": n_total, "matrices": len(mats), "packed_bytes": packed,
             "dequant_bf16_ms": round(d_ms, 3), "dequant_bf16_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
-            "quantize_ms": round(q_ms, 3), "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
+            "quantize_ms": round(q_ms, 3), "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_many_ms": round(qm_ms, 3), "quantize_many_gbps": round(q_bytes / (qm_ms * 1e-3) / 1e9, 1)}
 
 
 def other_configs(nl, dev):

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 4
+#define NF4LORA_ABI_VERSION 5
 
 enum nf4_status {
   NF4_OK = 0,
@@ -181,6 +181,30 @@ int nf4_dequantize(const nf4_tensor* w, nf4_dtype out_dtype, void* out, nf4_stre
  * matrices without a launch tail per matrix. */
 int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t count, nf4_dtype out_dtype,
                         nf4_stream_t stream);
+
+/* nf4_quantize for `count` (1 to NF4_MAX_TENSORS_PER_CALL) matrices in three
+ * kernel launches (Aner docs "Native model adaptation and NF4", section
+ * "Packed NF4 and the portable QLoRA profile", as for nf4_quantize): w[i]
+ * (device fp32, 16-byte aligned) holds the out[i].n weights of matrix i and
+ * out[i] (host struct of device buffers sized by nf4_layout) receives them
+ * with out[i].double_quant; single and double quantization may be mixed.
+ * `w` and `out` are host arrays read during the call; the outputs must not
+ * overlap each other or the inputs. `workspace` (device, 256-byte aligned)
+ * must hold nf4_quantize_many_workspace_bytes(out, count). `status` (optional
+ * device int32) is set to 0, or to NF4_ENONFINITE if any weight of any matrix
+ * is NaN or infinite (that matrix's outputs are then unspecified). Each
+ * matrix's bytes equal those of a separate nf4_quantize call; the launches
+ * cover all matrices at once, so a layer's weights are packed without a
+ * launch tail per matrix. Argument errors return before any launch. */
+int nf4_quantize_many(const float* const* w, const nf4_tensor* out, int32_t count, void* workspace,
+                      size_t workspace_bytes, int32_t* status, nf4_stream_t stream);
+
+/* Workspace bytes nf4_quantize_many needs for these outputs (their n and
+ * double_quant): per matrix the fp32 block maxima (double quantization only)
+ * and one fp64 partial sum per 4096 weights, each rounded up to 256 bytes,
+ * plus 256. Host-only; NF4_EINVAL (negative) for a NULL array, a count
+ * outside 1..NF4_MAX_TENSORS_PER_CALL or an n < 1. */
+int64_t nf4_quantize_many_workspace_bytes(const nf4_tensor* out, int32_t count);
 
 /* Selected rows of a packed embedding table (Aner docs "Native model
  * adaptation and NF4": section "Packed NF4 and the portable QLoRA profile",

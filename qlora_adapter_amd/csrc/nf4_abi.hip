@@ -324,6 +324,31 @@ int nf4_dequantize_many(const nf4_tensor* tensors, void* const* outs, int32_t co
   return launch_dequantize_many(tensors, outs, count, out_dtype, as_stream(stream));
 }
 
+int64_t nf4_quantize_many_workspace_bytes(const nf4_tensor* out, int32_t count) {
+  if (!out || count < 1 || count > NF4_MAX_TENSORS_PER_CALL) return NF4_EINVAL;
+  for (int32_t i = 0; i < count; ++i)
+    if (out[i].n < 1 || (out[i].double_quant != 0 && out[i].double_quant != 1)) return NF4_EINVAL;
+  return (int64_t)quantize_many_ws_bytes(out, count);
+}
+
+int nf4_quantize_many(const float* const* w, const nf4_tensor* out, int32_t count, void* workspace,
+                      size_t workspace_bytes, int32_t* status, nf4_stream_t stream) {
+  if (!w || !out || count < 1 || count > NF4_MAX_TENSORS_PER_CALL) return NF4_EINVAL;
+  int64_t groups = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (!w[i]) return NF4_EINVAL;
+    if (int rc = check_tensor(&out[i], out[i].n)) return rc;
+    if (!aligned(w[i], 16)) return NF4_EALIGN;
+    groups += quant_groups(out[i].n);
+  }
+  if (groups >= (int64_t(1) << 31)) return NF4_EINVAL;
+  if (status && !aligned(status, 4)) return NF4_EALIGN;
+  if (!workspace || workspace_bytes < quantize_many_ws_bytes(out, count)) return NF4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NF4_EALIGN;
+  if (int rc = check_device()) return rc;
+  return launch_quantize_many(w, out, count, workspace, status, as_stream(stream));
+}
+
 int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype out_dtype,
                        void* out, int32_t* status, nf4_stream_t stream) {
   if (!valid_dtype(out_dtype)) return NF4_EUNSUPPORTED;

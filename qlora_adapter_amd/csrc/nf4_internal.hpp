@@ -21,12 +21,17 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The quantizer's workgroups each code 64 blocks (4096 weights) and leave one
+// fp64 partial sum of their block maxima.
+constexpr int64_t kQuantGroupBlocks = 64;
+inline int64_t quant_groups(int64_t n) { return ceil_div(ceil_div(n, kBlock), kQuantGroupBlocks); }
+
 // Scratch layout of nf4_quantize with double quantization: fp32 absmax[nb]
-// (256-byte aligned) followed by fp64 partial sums[nn].
+// (256-byte aligned) followed by the fp64 partial sums, one per 4096 weights.
 inline size_t quantize_ws_bytes(int64_t n, int dq) {
   if (!dq) return 0;
-  int64_t nb = ceil_div(n, kBlock), nn = ceil_div(nb, kNested);
-  return round_up(sizeof(float) * (size_t)nb, 256) + sizeof(double) * (size_t)nn;
+  const int64_t nb = ceil_div(n, kBlock);
+  return round_up(sizeof(float) * (size_t)nb, 256) + sizeof(double) * (size_t)quant_groups(n);
 }
 
 // Size of the fixed device scratch behind nf4_quantize_noalloc, and its device
@@ -36,6 +41,12 @@ int quantize_scratch(void** ptr);
 
 // Launchers (return NF4_OK or NF4_EDEVICE). Arguments are already validated.
 int launch_quantize(const float* w, int64_t n, const nf4_tensor* t, void* ws, int32_t* status, hipStream_t s);
+// Workspace of nf4_quantize_many: per tensor the fp32 block maxima (double
+// quantization only) and one fp64 partial per 4096 weights, each 256-byte
+// aligned, then the per-tensor non-finite flags.
+size_t quantize_many_ws_bytes(const nf4_tensor* t, int32_t count);
+int launch_quantize_many(const float* const* w, const nf4_tensor* t, int32_t count, void* ws, int32_t* status,
+                         hipStream_t s);
 int launch_dequantize(const nf4_tensor* t, nf4_dtype dt, void* out, hipStream_t s);
 int launch_dequantize_many(const nf4_tensor* t, void* const* outs, int32_t count, nf4_dtype dt, hipStream_t s);
 int launch_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t* ids, int64_t T, nf4_dtype dt,

@@ -7,6 +7,7 @@ library is missing or the device is not gfx950, calls raise.
 from __future__ import annotations
 
 import ctypes
+import functools
 import dataclasses
 import math
 import os
@@ -23,7 +24,7 @@ NF4_F32, NF4_BF16 = 0, 1
 _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noalloc", "nf4_quantize_noalloc_max_elements",
-           "nf4_dequantize", "nf4_dequantize_many",
+           "nf4_quantize_many", "nf4_quantize_many_workspace_bytes", "nf4_dequantize", "nf4_dequantize_many",
            "nf4_embedding_rows", "nf4_linear_fwd",
            "nf4_linear_bwd_input", "nf4_linear_workspace_bytes", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
@@ -31,6 +32,7 @@ EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noallo
            "nf4_swiglu_bwd", "nf4_cross_entropy", "nf4_add", "nf4_status_string", "nf4lora_abi_version"]
 
 MAX_ADAPTERS_PER_CALL = 16
+MAX_TENSORS_PER_CALL = 16
 
 
 class NF4Error(RuntimeError):
@@ -83,6 +85,10 @@ def load() -> ctypes.CDLL:
             lib.nf4_quantize_noalloc.argtypes = [P, I64, ctypes.c_int, ctypes.POINTER(_Tensor), P, P]
             lib.nf4_quantize_noalloc_max_elements.restype = I64
             lib.nf4_quantize_noalloc_max_elements.argtypes = []
+            lib.nf4_quantize_many.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(_Tensor), I32, P,
+                                              ctypes.c_size_t, P, P]
+            lib.nf4_quantize_many_workspace_bytes.restype = I64
+            lib.nf4_quantize_many_workspace_bytes.argtypes = [ctypes.POINTER(_Tensor), I32]
             lib.nf4_dequantize.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, P, P]
             lib.nf4_dequantize_many.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(ctypes.c_void_p), I32,
                                                 ctypes.c_int, P]
@@ -121,6 +127,7 @@ def load() -> ctypes.CDLL:
             lib.lora_grad_workspace_bytes.restype = I64
             lib.lorafa_preconditioner_workspace_bytes.restype = I64
             lib.nf4_quantize_noalloc_max_elements.restype = I64
+            lib.nf4_quantize_many_workspace_bytes.restype = I64
             lib.nf4_status_string.restype = ctypes.c_char_p
             _lib = lib
     return _lib
@@ -168,10 +175,15 @@ def _arrays(*specs) -> None:
 
 # --------------------------------------------------------------------------- layout and tables
 
-def layout(n: int, double_quant: bool = True) -> dict:
+@functools.lru_cache(maxsize=1024)
+def _layout(n: int, dq: int) -> Tuple[Tuple[str, int], ...]:
     s = _Sizes()
-    _check("nf4_layout", load().nf4_layout(int(n), int(bool(double_quant)), ctypes.byref(s)))
-    return {f: int(getattr(s, f)) for f, _ in _Sizes._fields_}
+    _check("nf4_layout", load().nf4_layout(n, dq, ctypes.byref(s)))
+    return tuple((f, int(getattr(s, f))) for f, _ in _Sizes._fields_)
+
+
+def layout(n: int, double_quant: bool = True) -> dict:
+    return dict(_layout(int(n), int(bool(double_quant))))
 
 
 def code_tables() -> Tuple[np.ndarray, np.ndarray]:
@@ -254,6 +266,50 @@ def quantize(w: torch.Tensor, double_quant: bool = True, out: Optional[NF4Tensor
     return out
 
 
+def quantize_many_workspace_bytes(outs) -> int:
+    """Device workspace nf4_quantize_many needs for these packed outputs."""
+    outs = list(outs)
+    arr = (_Tensor * len(outs))(*[o.c_struct() for o in outs])
+    v = int(load().nf4_quantize_many_workspace_bytes(arr, len(outs)))
+    if v < 0:
+        _check("nf4_quantize_many_workspace_bytes", v)
+    return v
+
+
+def quantize_many(ws, double_quant=True, outs=None, workspace: Optional[torch.Tensor] = None,
+                  status: Optional[torch.Tensor] = None):
+    """Pack up to 16 fp32 device tensors in one nf4_quantize_many call (three
+    launches for all of them); double_quant is one flag or one per tensor.
+    Returns the packed tensors; each equals a separate quantize() bit for bit."""
+    ws = list(ws)
+    if not 1 <= len(ws) <= MAX_TENSORS_PER_CALL:
+        raise ValueError(f"quantize_many takes 1 to {MAX_TENSORS_PER_CALL} tensors, got {len(ws)}")
+    dqs = list(double_quant) if isinstance(double_quant, (list, tuple)) else [double_quant] * len(ws)
+    if len(dqs) != len(ws):
+        raise ValueError("one double_quant flag per tensor")
+    for i, w in enumerate(ws):
+        _dev(w, f"ws[{i}]", torch.float32)
+    if outs is None:
+        outs = [NF4Tensor.empty(tuple(w.shape), bool(dq), w.device) for w, dq in zip(ws, dqs)]
+    outs = list(outs)
+    if len(outs) != len(ws):
+        raise ValueError("one output per input")
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        if o.n != w.numel() or o.double_quant != bool(dqs[i]):
+            raise ValueError(f"outs[{i}] does not match ws[{i}] (size or double_quant)")
+    arr = (_Tensor * len(outs))(*[o.c_struct() for o in outs])
+    need = int(load().nf4_quantize_many_workspace_bytes(arr, len(outs)))
+    if need < 0:
+        _check("nf4_quantize_many_workspace_bytes", need)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=ws[0].device)
+    ptrs = (ctypes.c_void_p * len(ws))(*[w.data_ptr() for w in ws])
+    _check("nf4_quantize_many", load().nf4_quantize_many(ptrs, arr, len(ws), _ptr(workspace),
+                                                         workspace.numel() * workspace.element_size(), _ptr(status),
+                                                         _stream(ws[0].device)))
+    return outs
+
+
 def quantize_noalloc(w: torch.Tensor, out: NF4Tensor, status: Optional[torch.Tensor] = None) -> NF4Tensor:
     """nf4_quantize into a caller-allocated `out` with no workspace (the library's
     fixed device scratch): allocates nothing. Calls that overlap on one device
@@ -280,8 +336,6 @@ def dequantize(t: NF4Tensor, dtype=torch.bfloat16, out: Optional[torch.Tensor] =
     _check("nf4_dequantize", load().nf4_dequantize(ctypes.byref(st), _DT[dtype], _ptr(out), _stream(t.device)))
     return out
 
-
-MAX_TENSORS_PER_CALL = 16
 
 
 def dequantize_many(tensors, dtype=torch.bfloat16, outs=None):

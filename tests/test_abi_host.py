@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 4
+    assert lib[0].nf4lora_abi_version() == 5
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -323,6 +323,42 @@ def test_dequantize_many_argument_errors(lib):
     assert L.nf4_dequantize_many(arr(good, m._Tensor(16, 16, 16, 16, 0, 1)), outs(256, 256), 2, 1, None) == EINVAL
     assert L.nf4_dequantize_many(arr(good, m._Tensor(17, 16, 16, 16, 64, 1)), outs(256, 256), 2, 1, None) == EALIGN
     assert L.nf4_dequantize_many(arr(good), outs(264), 1, 1, None) == EALIGN
+
+
+def test_quantize_many_argument_errors(lib):
+    """nf4_quantize_many sizes its workspace per tensor (maxima with double
+    quantization, one fp64 partial per 16384 weights, each rounded to 256
+    bytes, plus 256 for the flags) and rejects bad arguments before any
+    device work."""
+    L, m = lib
+    EINVAL, EALIGN, EWS = -1, -2, -6
+    arr = lambda *ts: (m._Tensor * len(ts))(*ts)
+    ptrs = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    good = m._Tensor(16, 16, 16, 16, 100, 1)          # nb 2, one group
+    single = m._Tensor(16, 16, None, None, 5000, 0)   # no maxima in the workspace
+    big = m._Tensor(16, 16, 16, 16, 16384 * 3 + 1, 1)  # nb 769 (3076 B -> 3328), 4 groups
+    assert L.nf4_quantize_many_workspace_bytes(arr(good), 1) == 256 + 256 + 256
+    assert L.nf4_quantize_many_workspace_bytes(arr(good, single, big), 3) == (512 + 256 + 3328 + 256) + 256
+    assert L.nf4_quantize_many_workspace_bytes(None, 1) == EINVAL
+    assert L.nf4_quantize_many_workspace_bytes(arr(good), 0) == EINVAL
+    assert L.nf4_quantize_many_workspace_bytes(arr(*[good] * 17), 17) == EINVAL
+    assert L.nf4_quantize_many_workspace_bytes(arr(m._Tensor(16, 16, 16, 16, 0, 1)), 1) == EINVAL
+    need = L.nf4_quantize_many_workspace_bytes(arr(good, single), 2)
+    W = ptrs(16, 32)
+    assert L.nf4_quantize_many(None, arr(good, single), 2, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(W, None, 2, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(W, arr(good, single), 0, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(ptrs(*[16] * 17), arr(*[good] * 17), 17, 256, 1 << 20, None, None) == EINVAL
+    assert L.nf4_quantize_many(ptrs(16, None), arr(good, single), 2, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(W, arr(good, m._Tensor(16, 16, 16, 16, 0, 1)), 2, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(W, arr(good, m._Tensor(16, 16, None, None, 64, 1)), 2, 256, need, None, None) == EINVAL
+    assert L.nf4_quantize_many(ptrs(16, 40), arr(good, single), 2, 256, need, None, None) == EALIGN
+    assert L.nf4_quantize_many(W, arr(good, single), 2, 256, need, 2, None) == EALIGN      # status
+    assert L.nf4_quantize_many(W, arr(good, single), 2, None, need, None, None) == EWS
+    assert L.nf4_quantize_many(W, arr(good, single), 2, 256, need - 1, None, None) == EWS
+    assert L.nf4_quantize_many(W, arr(good, single), 2, 264, need, None, None) == EALIGN
+    with pytest.raises(ValueError):
+        m.quantize_many([])
 
 
 def test_paged_step_argument_errors(lib):

@@ -66,6 +66,34 @@ def test_special_blocks(gpu, orc):
         np.testing.assert_array_equal(bits(gpu.dequantize(q, torch.float32)), orc.dequantize(ref).view(np.uint32))
 
 
+def test_extreme_block_maxima(gpu, orc):
+    """Blocks whose maximum lies above 2^126 (so 1/m is subnormal), at 2^126
+    exactly, between it and the largest float, in [2^-126, 2^-120) (where
+    128 / m overflows), at 2^-120, subnormal, and at 1 and 2^-1, with subnormal
+    weights beside normal maxima: every weight's code is that of the correctly
+    rounded w / m (each block holds +-m itself, so the quotients reach +-1)."""
+    rng = np.random.default_rng(17)
+
+    def block(m):
+        b = (rng.uniform(-1.0, 1.0, 64) * m).astype(np.float32)
+        b[rng.integers(64)] = np.float32(m) * np.float32(rng.choice([-1.0, 1.0]))
+        return b
+
+    maxima = [3.0e38, 1.5e38, 2.0 ** 126, 1.5 * 2.0 ** 126, 1.0e38, 3.4e38, 2.0 ** -126, 3 * 2.0 ** -126,
+              1.5 * 2.0 ** -121, 2.0 ** -120, 1.25 * 2.0 ** -120, 1.0e-40, 5.0e-45, 1.0, 0.5, 2.0 ** 100]
+    parts = [block(m) for m in maxima]
+    parts.append(workloads.normal_f32((64 * 700 + 9,), 0.02, 5).numpy())
+    w = np.concatenate(parts).astype(np.float32)
+    assert np.all(np.isfinite(w))
+    for dq in (True, False):
+        print(f"[storage] extreme maxima dq={dq}", flush=True)
+        q, status = _gpu_quant(gpu, w, dq)
+        assert status == 0
+        ref = orc.quantize(w, dq)
+        _compare_packed(q, ref, dq)
+        np.testing.assert_array_equal(bits(gpu.dequantize(q, torch.float32)), orc.dequantize(ref).view(np.uint32))
+
+
 def test_repeat_identical_and_nonfinite(gpu):
     w = workloads.weight_with_outliers((64 * 5000 + 3,), seed=8).cuda()
     a = gpu.quantize(w, True)
@@ -111,11 +139,11 @@ def test_full_size_matrix(gpu, orc, shape):
 
 @pytest.mark.parametrize("n", [1024 * 16384, 1024 * 16384 + 1, 4096 * 16384, 4096 * 16384 + 7, (1 << 27) + 12345])
 def test_mean_over_many_groups(gpu, orc, n):
-    """Matrices with 1024 and 1025 groups of 16384 weights (the largest with
-    the mean formed in every nested-block workgroup, the smallest with the
-    separate mean kernel), and with 4096, 4097 and 8193 groups: the per-thread
-    runs of the mean's pairwise tree hold 16, 32 and 64 group sums (the
-    register form and the stack form of the tree)."""
+    """The mean's pairwise tree over the quantizer's partial sums (one per
+    4096 weights): 4096 partials (the mean formed in every nested-block
+    workgroup, one full round), 4097 (the separate 1024-thread mean kernel, one
+    zero-padded round of 16384), 16384 (one full round), 16385 and 32772 (two
+    and four rounds joined by the binary counter)."""
     print(f"[storage] mean tree n={n}", flush=True)
     w = workloads.weight_with_outliers((n,), seed=n % 1000, device="cuda")
     q = gpu.quantize(w, True)
@@ -142,6 +170,51 @@ def test_dequantize_many_equals_single_calls(gpu, orc):
     for i in (0, 2):
         ref = orc.quantize(ws[i], sizes[i][1])
         np.testing.assert_array_equal(bits(many[i]), orc.dequantize(ref, "f32").view(np.uint32))
+
+
+def _same_packed(a, b):
+    assert torch.equal(a.codes, b.codes)
+    assert torch.equal(a.scales.view(torch.uint8), b.scales.view(torch.uint8))
+    if a.double_quant:
+        assert torch.equal(a.nested.view(torch.int32), b.nested.view(torch.int32))
+        assert torch.equal(a.offset.view(torch.int32), b.offset.view(torch.int32))
+
+
+def test_quantize_many_equals_single_calls(gpu, orc):
+    """One nf4_quantize_many call over mixed tensors (double and single
+    quantization, sizes with tails, tiny ones, one past 4096 groups whose mean
+    a single call forms in its own kernel) equals per-tensor nf4_quantize bit
+    for bit, and the oracle for three of them; the status word reports a
+    non-finite weight in any tensor and is cleared by the next finite call."""
+    sizes = [(64 * 5000 + 3, True), (1, True), (4096 * 37 + 5, False), (16384 * 3, True), (127, False),
+             (1536 * 576, True), (4097 * 16384 + 5, True), (64, False)]
+    ws = [workloads.weight_with_outliers((n,), seed=i + 21, device="cuda") for i, (n, _) in enumerate(sizes)]
+    dqs = [dq for _, dq in sizes]
+    st = torch.full((1,), 77, dtype=torch.int32, device="cuda")
+    many = gpu.quantize_many(ws, dqs, status=st)
+    single = [gpu.quantize(w, dq) for w, dq in zip(ws, dqs)]
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i, (a, b) in enumerate(zip(many, single)):
+        print(f"[storage] many item {i} n={sizes[i][0]}", flush=True)
+        _same_packed(a, b)
+    for i in (0, 2, 5):
+        _compare_packed(many[i], orc.quantize(ws[i].cpu().numpy(), dqs[i]), dqs[i])
+    for bad_item in (2, 6):  # single, then double quantization
+        v = [w.clone() for w in ws]
+        v[bad_item][sizes[bad_item][0] // 2] = float("nan")
+        gpu.quantize_many(v, dqs, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == -5  # NF4_ENONFINITE
+        gpu.quantize_many(ws, dqs, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+    # single quantization only: no nested blocks, one workgroup writes the status
+    outs = gpu.quantize_many([ws[2], ws[4]], False, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    _same_packed(outs[0], single[2])
+    _same_packed(outs[1], single[4])
 
 
 def test_quantizer_decision_boundaries(gpu, orc):
