@@ -56,6 +56,8 @@ def parse():
                    help="skip the 32-layer Llama-8B-shaped training step (tokens/s)")
     p.add_argument("--decoder-step-only", action="store_true",
                    help="only the Llama-8B-shaped training step (--steps timed after --warmup), for profiling")
+    p.add_argument("--throughput-only", action="store_true",
+                   help="only the 7.5e9-parameter quantize/dequantize pass (one timed pass; for counter runs)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
@@ -109,13 +111,11 @@ def ceilings():
             "note": "measured in this run; context only (torch's GEMM multiplies dense bf16 weights)"}
 
 
-def counter_traffic(kernel: str):
-    """HBM-side bytes per launch of the fused GEMM kernel, from the rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the copy-probe
-    calibration; None when the kernel source changed since the counters."""
+def _counter_summary(name: str, sources):
+    """key = value lines of a rocprofv3 counter summary under profiles/, or None
+    when the kernel sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "fused_gemm_counters_llama8b_layer.txt")
-    src = os.path.join(ROOT, "qlora_adapter_amd", "csrc", "nf4_gemm_fast.hip")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -123,11 +123,31 @@ def counter_traffic(kernel: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
-        return None
+    h = hashlib.sha256()
+    for s in sources:
+        h.update(open(os.path.join(ROOT, "qlora_adapter_amd", "csrc", s), "rb").read())
+    return kv if kv.get("kernel_source_sha256") == h.hexdigest() else None
+
+
+def counter_traffic(kernel: str):
+    """HBM-side bytes per nf4_linear_fwd / nf4_linear_bwd_input call (all its
+    dispatches, averaged over the layer's 7 projections) from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the copy-probe
+    calibration; None when the kernel sources changed since the counters."""
+    kv = _counter_summary("fused_gemm_counters_llama8b_layer.txt", ("nf4_gemm_fast.hip", "nf4_linear.hip"))
     key = "fwd" if kernel == "nf4_linear_fwd" else "bwd"
     try:
-        return float(kv[f"{key}_hbm_bytes_per_launch"])
+        return float(kv[f"{key}_hbm_bytes_per_launch"]) if kv else None
+    except KeyError:
+        return None
+
+
+def dequant_counter_traffic():
+    """Calibrated HBM-side bytes of one decode pass of the 7.5e9-parameter
+    workload (207 launches), or None when nf4_storage.hip changed since."""
+    kv = _counter_summary("dequant_quantize_counters_7p5e9.txt", ("nf4_storage.hip",))
+    try:
+        return float(kv["dequant_pass_hbm_bytes"]) if kv else None
     except KeyError:
         return None
 
@@ -410,7 +430,7 @@ def quant_dequant_throughput(nl, dev, passes: int = 3, batch: int = 1):
     del W, Q, OUT
     torch.cuda.empty_cache()
     q_bytes, d_bytes = 4 * n_total + packed, packed + 2 * n_total
-    return {"params": n_total, "matrices": len(mats), "packed_bytes": packed,
+    return {"params": n_total, "matrices": len(mats), "packed_bytes": packed, "dequant_bf16_bytes": d_bytes,
             "dequant_bf16_ms": round(d_ms, 3), "dequant_bf16_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
             "quantize_ms": round(q_ms, 3), "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
             "quantize_many_ms": round(qm_ms, 3), "quantize_many_gbps": round(q_bytes / (qm_ms * 1e-3) / 1e9, 1)}
@@ -503,6 +523,12 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.throughput_only:
+        import torch
+        from qlora_adapter_amd import nf4lora as nl
+        nl.load()
+        print(json.dumps(quant_dequant_throughput(nl, torch.device("cuda:0"), passes=1)), flush=True)
         return
     if args.decoder_step_only:
         import torch
@@ -678,7 +704,8 @@ def main():
              "workload": "7.5e9-parameter quantize/dequantize throughput "
              "(96 x 4096x14336 + 111 x 4096x4096, cold passes)", "bound": "hbm",
              "achieved": qd["dequant_bf16_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-             "frac": round(qd["dequant_bf16_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
+             "frac": round(qd["dequant_bf16_gbps"] / PEAK_HBM_GBPS, 4), "traffic": dequant_counter_traffic(),
+             "traffic_per": "pass of 207 launches (algorithmic bytes per pass: %d)" % qd["dequant_bf16_bytes"],
              "in_layer_step_gbps": round(dq_gbps, 1)} if qd else
             {"kernel": "nf4_dequantize_many (bf16 out)", "workload": "the layer step's seven matrices", "bound": "hbm",
              "achieved": round(dq_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
