@@ -232,10 +232,9 @@ int nf4_embedding_rows(const nf4_tensor* E, int64_t V, int64_t D, const int64_t*
  * (fp32) is optional: when given it receives T = x A^T, kept for lora_grad;
  * when NULL, T lives in the workspace for the duration of the call.
  * `workspace` (device; a non-NULL workspace must be 256-byte aligned, else
- * NF4_EALIGN) holds
- * nf4_linear_workspace_bytes(M, K, N, t_out ? 0 : r, 0) bytes (NULL when that
- * is 0), else NF4_EWORKSPACE. Every argument error is returned before any
- * launch. */
+ * NF4_EALIGN) holds nf4_linear_workspace_bytes(M, K, N, r, t_out ? 0 :
+ * NF4_WS_NO_SIDE_OUT) bytes (NULL when that is 0), else NF4_EWORKSPACE. Every
+ * argument error is returned before any launch. */
 int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const nf4_tensor* W, int64_t N,
                    const float* A, const float* B, int32_t r, float s, void* y, float* t_out, void* workspace,
                    size_t workspace_bytes, nf4_stream_t stream);
@@ -245,26 +244,30 @@ int nf4_linear_fwd(const void* x, nf4_dtype dtype, int64_t M, int64_t K, const n
  * no gradient): dX = dY W_hat + s (dY B) A. dY [M,N] and dX [M,K] are `dtype`.
  * r == 0 disables the adapter; r >= 1 requires A [r,K] and B [N,r]. u_out
  * [M,r] (fp32) is optional: when given it receives U = dY B; when NULL, U
- * lives in the workspace. `workspace` holds
- * nf4_linear_workspace_bytes(M, K, N, u_out ? 0 : r, 1) bytes (NULL when that
- * is 0). */
+ * lives in the workspace. `workspace` holds nf4_linear_workspace_bytes(M, K,
+ * N, r, NF4_WS_BACKWARD | (u_out ? 0 : NF4_WS_NO_SIDE_OUT)) bytes (NULL when
+ * that is 0). */
 int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, const nf4_tensor* W,
                          int64_t K, const float* A, const float* B, int32_t r, float s, void* dx,
                          float* u_out, void* workspace, size_t workspace_bytes, nf4_stream_t stream);
 
-/* Device workspace (bytes; pass it 256-byte aligned) that nf4_linear_fwd
- * (backward = 0) or nf4_linear_bwd_input (backward = 1) needs for these sizes
- * when `r_side` rank columns of the side product (T or U) are NOT returned to
- * the caller: pass r_side = 0 when t_out / u_out is given, r_side = r when it
- * is NULL. Two parts, each rounded up to 256 bytes: (1) bf16 only: a long
- * reduction over few output tiles (short sequences through a wide layer, e.g.
- * 512 tokens through a 4096 x 14336 projection) is split in parts whose fp32
- * partial sums the workspace holds; they are added in a fixed order, so
- * results stay run-to-run identical (0 for most shapes); (2) M * r_side fp32
- * for the side product. A call with a NULL or smaller workspace than it needs
- * fails with NF4_EWORKSPACE. Host-only; a negative NF4_E* code for invalid
- * sizes. */
-int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r_side, int backward);
+/* Flags of nf4_linear_workspace_bytes. */
+#define NF4_WS_BACKWARD 1     /* the call is nf4_linear_bwd_input (else nf4_linear_fwd) */
+#define NF4_WS_NO_SIDE_OUT 2  /* the call passes no t_out / u_out */
+
+/* Device workspace (bytes; pass it 256-byte aligned) that nf4_linear_fwd or
+ * nf4_linear_bwd_input (NF4_WS_BACKWARD) needs for these sizes and adapter
+ * rank r (0: no adapter). Three parts, each rounded up to 256 bytes: (1) bf16
+ * only: a long reduction over few output tiles (short sequences through a
+ * wide layer, e.g. 512 tokens through a 4096 x 14336 projection) is split in
+ * parts whose fp32 partial sums the workspace holds; (2) r > 32: the side
+ * product's reduction (over K forward, N backward) is split in parts whose
+ * fp32 partial sums of the M x r product the workspace holds; (3) with
+ * NF4_WS_NO_SIDE_OUT, M * r fp32 for the side product itself. Partial sums are
+ * added in a fixed order, so results stay run-to-run identical. A call with a
+ * NULL or smaller workspace than it needs fails with NF4_EWORKSPACE.
+ * Host-only; a negative NF4_E* code for invalid sizes or flags. */
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int flags);
 
 /* LoRA factor gradients (Aner docs "Native model adaptation and NF4", sections
  * "Adapter API" and "LoRA FA includes gradient preconditioning"):

@@ -67,6 +67,15 @@ hipStream_t as_stream(nf4_stream_t s) { return reinterpret_cast<hipStream_t>(s);
 // Bytes of an M x r fp32 side product carved from a workspace (0 when r == 0).
 int64_t side_ws_bytes(int64_t M, int32_t r) { return r > 0 ? (int64_t)round_up(sizeof(float) * (size_t)(M * r), 256) : 0; }
 
+// Workspace of lora_grad: the reduction partial sums, the recomputed side
+// products, and the partial sums of a split recomputation (the larger of the
+// two, as they run one after the other).
+size_t lora_grad_need(int64_t M, int64_t K, int64_t N, int32_t r, bool fa, bool need_t, bool need_u) {
+  const size_t side = (size_t)side_ws_bytes(M, r);
+  const int64_t pt = need_t ? side_split_ws_bytes(M, K, r) : 0, pu = need_u ? side_split_ws_bytes(M, N, r) : 0;
+  return lora_grad_ws(M, K, N, r, fa) + (need_t ? side : 0) + (need_u ? side : 0) + (size_t)(pt > pu ? pt : pu);
+}
+
 // Sizes every linear call accepts: positive, and small enough that M * max(K, N)
 // and N * K (elements) stay below 2^62.
 bool linear_sizes_ok(int64_t M, int64_t K, int64_t N) {
@@ -76,10 +85,19 @@ bool linear_sizes_ok(int64_t M, int64_t K, int64_t N) {
   return K <= kLim / N && M <= kLim / W;
 }
 
-int64_t linear_ws_bytes(nf4_dtype dt, int64_t M, int64_t K, int64_t N, int32_t r_side, bool backward) {
+// Workspace of a linear call: [split-reduction partial sums (bf16)][split side
+// product partial sums (bf16, r > 32)][side product when the caller takes none].
+struct LinearWs {
+  int64_t split, side_part, side;
+  int64_t total() const { return split + side_part + side; }
+};
+LinearWs linear_ws(nf4_dtype dt, int64_t M, int64_t K, int64_t N, int32_t r, bool own_side, bool backward) {
   const int64_t split = dt == NF4_BF16 ? linear_fast_workspace_bytes(M, K, N, backward) : 0;
-  const int64_t split_part = split > 0 ? (int64_t)round_up((size_t)split, 256) : 0;
-  return split_part + side_ws_bytes(M, r_side);
+  LinearWs w;
+  w.split = split > 0 ? (int64_t)round_up((size_t)split, 256) : 0;
+  w.side_part = (dt == NF4_BF16 && r > 0) ? side_split_ws_bytes(M, backward ? N : K, r) : 0;
+  w.side = own_side ? side_ws_bytes(M, r) : 0;
+  return w;
 }
 
 int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const nf4_tensor* W, const float* A,
@@ -93,20 +111,15 @@ int linear_common(const void* a, nf4_dtype dt, int64_t M, int64_t K, int64_t N, 
   if (r > 0 && !std::isfinite(s)) return NF4_EINVAL;
   if (!aligned(a, 16) || !aligned(out, 16)) return NF4_EALIGN;
   if (r > 0 && (!aligned(A, 4) || !aligned(B, 4) || (side && !aligned(side, 4)))) return NF4_EALIGN;
-  // The workspace holds the split-reduction partial sums (bf16) and, when the
-  // caller does not take the side product, that product (in its last part).
-  const int32_t r_side = (r > 0 && !side) ? r : 0;
-  const int64_t need = linear_ws_bytes(dt, M, K, N, r_side, backward);
+  const LinearWs w = linear_ws(dt, M, K, N, r, r > 0 && !side, backward);
+  const int64_t need = w.total();
   if (ws && !aligned(ws, 256)) return NF4_EALIGN;
   if (need > 0 && (!ws || ws_bytes < (size_t)need)) return NF4_EWORKSPACE;
   if (int rc = check_device()) return rc;
-  size_t split_bytes = ws_bytes;
-  if (r_side > 0) {
-    const int64_t sb = side_ws_bytes(M, r_side);
-    split_bytes = (size_t)(need - sb);
-    side = reinterpret_cast<float*>(static_cast<char*>(ws) + (need - sb));
-  }
-  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward, ws, split_bytes};
+  char* base = static_cast<char*>(ws);
+  float* side_part = w.side_part > 0 ? reinterpret_cast<float*>(base + w.split) : nullptr;
+  if (w.side > 0) side = reinterpret_cast<float*>(base + w.split + w.side_part);
+  LinearArgs g{a, dt, M, K, N, W, A, B, r, s, out, side, backward, ws, (size_t)w.split, side_part};
   return launch_linear(g, as_stream(stream));
 }
 
@@ -373,18 +386,17 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
   return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, workspace, workspace_bytes, true, stream);
 }
 
-int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r_side, int backward) {
-  if (!linear_sizes_ok(M, K, N) || r_side < 0 || r_side > 256 || (backward != 0 && backward != 1)) return NF4_EINVAL;
-  return linear_ws_bytes(NF4_BF16, M, K, N, r_side, backward != 0);
+int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int flags) {
+  if (!linear_sizes_ok(M, K, N) || r < 0 || r > 256) return NF4_EINVAL;
+  if (flags & ~(NF4_WS_BACKWARD | NF4_WS_NO_SIDE_OUT)) return NF4_EINVAL;
+  return linear_ws(NF4_BF16, M, K, N, r, r > 0 && (flags & NF4_WS_NO_SIDE_OUT), (flags & NF4_WS_BACKWARD) != 0)
+      .total();
 }
 
 int64_t lora_grad_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int fa, int recompute) {
   if (!linear_sizes_ok(M, K, N) || r < 1 || r > 256 || (fa != 0 && fa != 1)) return NF4_EINVAL;
   if (recompute < 0 || recompute > (NF4_RECOMPUTE_T | NF4_RECOMPUTE_U)) return NF4_EINVAL;
-  int64_t bytes = (int64_t)lora_grad_ws(M, K, N, r, fa);
-  if (recompute & NF4_RECOMPUTE_T) bytes += side_ws_bytes(M, r);
-  if (!fa && (recompute & NF4_RECOMPUTE_U)) bytes += side_ws_bytes(M, r);
-  return bytes;
+  return (int64_t)lora_grad_need(M, K, N, r, fa != 0, recompute & NF4_RECOMPUTE_T, !fa && (recompute & NF4_RECOMPUTE_U));
 }
 
 int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t K, int64_t N, const float* A,
@@ -404,21 +416,24 @@ int lora_grad(const void* x, const void* dy, nf4_dtype dtype, int64_t M, int64_t
   if ((need_t && !aligned(A, 4)) || (need_u && !aligned(B, 4))) return NF4_EALIGN;
   const size_t base = lora_grad_ws(M, K, N, r, fa);
   const size_t side = (size_t)side_ws_bytes(M, r);
-  const size_t need = base + (need_t ? side : 0) + (need_u ? side : 0);
+  const size_t need = lora_grad_need(M, K, N, r, fa, need_t, need_u);
   if (!workspace || workspace_bytes < need) return NF4_EWORKSPACE;
   if (!aligned(workspace, 256)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  // Recomputed side products follow the reduction partial sums in the workspace.
+  // Recomputed side products follow the reduction partial sums in the
+  // workspace, then the partial sums of a split side product (shared: the two
+  // recomputations run one after the other on the stream).
   char* extra = static_cast<char*>(workspace) + base;
+  float* part = reinterpret_cast<float*>(extra + (need_t ? side : 0) + (need_u ? side : 0));
   if (need_t) {  // T = x A^T
     float* tt = reinterpret_cast<float*>(extra);
     extra += side;
-    if (int rc = launch_side_product(x, dtype, M, K, A, r, false, tt, as_stream(stream))) return rc;
+    if (int rc = launch_side_product(x, dtype, M, K, A, r, false, tt, part, as_stream(stream))) return rc;
     t = tt;
   }
   if (need_u) {  // U = dY B
     float* uu = reinterpret_cast<float*>(extra);
-    if (int rc = launch_side_product(dy, dtype, M, N, B, r, true, uu, as_stream(stream))) return rc;
+    if (int rc = launch_side_product(dy, dtype, M, N, B, r, true, uu, part, as_stream(stream))) return rc;
     u = uu;
   }
   return launch_lora_grad(fa ? nullptr : x, dy, dtype, M, K, N, t, fa ? nullptr : u, r, s, dA, dB, workspace,

@@ -68,15 +68,20 @@ struct LinearArgs {
   bool backward;        // false: y = x W^T + s T B^T; true: dX = dY W + s U A
   void* ws;             // split-reduction partial sums (linear_fast_workspace_bytes), may be null
   size_t ws_bytes;
+  float* side_part;     // partial sums of a split side product (side_split_ws_bytes), may be null
 };
 // Workspace the bf16 fused path needs for these sizes (0 for most shapes).
 int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward);
 int launch_linear(const LinearArgs& a, hipStream_t s);
 // Side product alone: out[m][rho] = sum_i L[m][i] R[i][rho] (fp32 [M, r]), with
 // R[i][rho] = fac[rho][i] (backward = false: T = x A^T, I = K) or fac[i][rho]
-// (backward = true: U = dY B, I = N). Arguments are already validated.
+// (backward = true: U = dY B, I = N). `part` holds side_split_ws_bytes(M, I, r)
+// (bf16, r > 32). Arguments are already validated.
 int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const float* fac, int32_t r, bool backward,
-                        float* out, hipStream_t s);
+                        float* out, float* part, hipStream_t s);
+// Workspace of the split bf16 side product for ranks beyond 32 (0 when the
+// reduction over I is not split).
+int64_t side_split_ws_bytes(int64_t M, int64_t I, int32_t r);
 
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa);
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,

@@ -191,8 +191,18 @@ __global__ __launch_bounds__(1024) void k_side(const T* __restrict__ L, int64_t 
   }
 }
 
-// Side product for bf16 activations: ranks rho0 .. rho0 + 16 RT - 1 of the r
-// (RT <= 4 rank tiles per launch; larger ranks take one launch per 64). Same
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): within a 16-lane group,
+// lane i receives element i % 4 of the 4-element pieces addressed by lanes
+// 4 e + i / 4, e = 0..3.
+typedef __bf16 bf16x4l __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4l lds_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4l __attribute__((address_space(3)))*)(p));
+}
+
+// Side product for bf16 activations and r <= 32: ranks rho0 .. rho0 + 16 RT - 1
+// (ranks beyond 32 take k_side_wide, which shares each factor block between
+// 128 rows). Same
 // work split as k_side (16 rows per workgroup, 16 waves each reducing one
 // slice of I, slice sums added in wave order), but on the bf16 16x16x32 MFMA:
 // the fp32 factor is split into three bf16 parts whose sum is exact, so every
@@ -295,6 +305,181 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
       const int rho = rho0 + 16 * (t0 + q) + (e & 15);
       if (mm < M && rho < r) outS[mm * r + rho] = v;
     }
+  }
+}
+
+// Side product for bf16 activations and ranks beyond 32, as a skinny GEMM
+// with the reduction split: workgroup (b, ks, z) covers rows 128 b .. + 127,
+// reduction indices [ks kc, ks kc + kc) and ranks 64 z .. 64 z + 63. Per
+// 32-wide reduction step the whole workgroup stages the factor block (64 ranks
+// x 32 indices, fp32) once: each thread loads 8 values with 16-byte loads,
+// splits each into three bf16 parts whose sum is exact and stores the parts in
+// LDS, where all four waves read them (so the split and the factor traffic are
+// paid once per 128 rows). Forward (A [r][I]) the parts are stored [rank][i]
+// and read with 16-byte loads; backward (B [I][r]) they are stored [i][rank]
+// and gathered with transposing reads. Wave w multiplies rows 32 w .. + 31 (two
+// 16-row tiles, its activations loaded directly as 8 consecutive indices per
+// lane) on the 16x16x32 bf16 MFMA. The loads of steps s + 1 and s + 2 are in
+// flight while step s multiplies. Each split writes its sums to out + ks *
+// part_stride; with more than one split k_side_sum adds them in split order.
+constexpr int SW_FP = 40;  // bf16 pitch of a staged forward factor row (32 indices + 8)
+constexpr int SW_BP = 72;  // bf16 pitch of a staged backward factor row (64 ranks + 8)
+
+template <bool BWD, bool FAST>
+__global__ __launch_bounds__(256) void k_side_wide(const __bf16* __restrict__ L, int64_t M, int64_t I,
+                                                   const float* __restrict__ fac, int r, int64_t kc,
+                                                   float* __restrict__ out, int64_t part_stride) {
+  constexpr int FSZ = BWD ? 32 * SW_BP : 64 * SW_FP;  // bf16 per part and stage
+  __shared__ __attribute__((aligned(16))) __bf16 fp[2][3][FSZ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t mw = (int64_t)blockIdx.x * 128 + 32 * wave;  // first row of this wave
+  const int64_t kb = (int64_t)blockIdx.y * kc, ke = (kb + kc < I) ? kb + kc : I;
+  const int rho0 = 64 * (int)blockIdx.z;
+  const int64_t steps = (ke - kb + 31) / 32;
+  // staging role: forward, rank sr = tid / 4 and indices 8 (tid % 4) .. + 7;
+  // backward, index sr = tid / 8 and ranks 8 (tid % 8) .. + 7
+  const int sr = BWD ? (tid >> 3) : (tid >> 2), sq = BWD ? (tid & 7) : (tid & 3);
+  // one step's loads: the activations of the wave's two row tiles and the
+  // thread's 8 factor values, with their in-range flags
+  struct Set {
+    bf16x8 lv[2];
+    float fv[8];
+    bool lok[2], fok;
+  };
+  // FAST (I % 8 == 0, r % 8 == 0, 16-byte aligned arrays): every 8-element
+  // piece is wholly in range or wholly out, so each is one unconditional
+  // 16-byte load from a clamped address, zeroed at its use when out of range
+  // (a step past the last loads in-range data that is never used); no load
+  // sits behind a branch and none waits on another. Otherwise element-wise
+  // guards.
+  auto load = [&](int64_t k0, Set& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t m = mw + 16 * rt + row, i = k0 + 8 * kg;
+      if constexpr (FAST) {
+        S.lok[rt] = m < M && i < ke;
+        S.lv[rt] = *reinterpret_cast<const bf16x8*>(L + (m < M ? m : M - 1) * I + (i < ke ? i : kb));
+      } else {
+        S.lok[rt] = true;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S.lv[rt][e] = (m < M && i + e < ke) ? L[m * I + i + e] : (__bf16)0.0f;
+      }
+    }
+    // BWD: B[i][rho], i = k0 + sr, rho = rho0 + 8 sq + e
+    // FWD: A[rho][i], rho = rho0 + sr, i = k0 + 8 sq + e
+    const int64_t i = BWD ? k0 + sr : k0 + 8 * sq;
+    const int rho = BWD ? rho0 + 8 * sq : rho0 + sr;
+    if constexpr (FAST) {
+      S.fok = i < ke && rho < r;
+      const float* q = BWD ? fac + (i < ke ? i : kb) * r + (rho < r ? rho : 0)
+                           : fac + (int64_t)(rho < r ? rho : 0) * I + (i < ke ? i : kb);
+      const float4 a = *reinterpret_cast<const float4*>(q), b = *reinterpret_cast<const float4*>(q + 4);
+      S.fv[0] = a.x; S.fv[1] = a.y; S.fv[2] = a.z; S.fv[3] = a.w;
+      S.fv[4] = b.x; S.fv[5] = b.y; S.fv[6] = b.z; S.fv[7] = b.w;
+    } else {
+      S.fok = true;
+      if (BWD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S.fv[e] = (i < ke && rho + e < r) ? fac[i * r + rho + e] : 0.0f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S.fv[e] = (rho < r && i + e < ke) ? fac[(int64_t)rho * I + i + e] : 0.0f;
+      }
+    }
+  };
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[rt][t] = f32x4{};
+  // one step from register set S into LDS stage buf: stage the factor's three
+  // exact bf16 parts, then (after the barrier) load step `next` into S and
+  // multiply
+  auto step = [&](int buf, Set& S, int64_t next) __attribute__((always_inline)) {
+    {
+      bf16x8 h[3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = S.fok ? S.fv[e] : 0.0f;
+        const __bf16 a1 = (__bf16)v;
+        const float r1 = v - (float)a1;
+        const __bf16 a2 = (__bf16)r1;
+        h[0][e] = a1;
+        h[1][e] = a2;
+        h[2][e] = (__bf16)(r1 - (float)a2);
+      }
+      const int off = BWD ? sr * SW_BP + 8 * sq : sr * SW_FP + 8 * sq;
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) *reinterpret_cast<bf16x8*>(&fp[buf][pp][off]) = h[pp];
+    }
+    const bf16x8 l0 = S.lok[0] ? S.lv[0] : bf16x8{}, l1 = S.lok[1] ? S.lv[1] : bf16x8{};
+    __syncthreads();
+    load(next, S);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int pp = 2; pp >= 0; --pp) {
+        bf16x8 f;
+        if (BWD) {
+          bf16x4l v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v[h] = lds_tr16(&fp[buf][pp][(8 * kg + 4 * h + (row >> 2)) * SW_BP + 16 * t + 4 * (row & 3)]);
+          f = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        } else {
+          f = *reinterpret_cast<const bf16x8*>(&fp[buf][pp][(16 * t + row) * SW_FP + 8 * kg]);
+        }
+        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l0, f, acc[0][t], 0, 0, 0);
+        acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l1, f, acc[1][t], 0, 0, 0);
+      }
+    }
+  };
+  // two register sets in turn: steps s + 1 and s + 2 are loading while step s
+  // multiplies. The loop body has no branch (so the load waits stay exact):
+  // an odd step count gets one more step past the end, all of whose values
+  // are zeroed, and adding zero products leaves the sums unchanged.
+  Set A, B;
+  load(kb, A);
+  load(kb + 32, B);
+  for (int64_t s = 0; s < steps; s += 2) {
+    step(0, A, kb + 32 * (s + 2));
+    step(1, B, kb + 32 * (s + 3));
+  }
+  // accumulator element j of lane l: row 4 (l / 16) + j of the tile, rank 16 t + l % 16
+  float* o = out + (int64_t)blockIdx.y * part_stride;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rho = rho0 + 16 * t + row;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = mw + 16 * rt + 4 * kg + j;
+        if (m < M && rho < r) o[m * r + rho] = acc[rt][t][j];
+      }
+    }
+}
+
+// out[e] = sum over splits ks = 0, 1, ... in order of part[ks * n + e]; four
+// consecutive elements per thread (n % 4 == 0 and 16-byte aligned arrays: the
+// caller checks) or one.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void k_side_sum(const float* __restrict__ part, int64_t n, int splits,
+                                                  float* __restrict__ out) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC4 ? 4 : 1);
+  if (e >= n) return;
+  if constexpr (VEC4) {
+    float4 v = *reinterpret_cast<const float4*>(part + e);
+    for (int ks = 1; ks < splits; ++ks) {
+      const float4 w = *reinterpret_cast<const float4*>(part + (int64_t)ks * n + e);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    *reinterpret_cast<float4*>(out + e) = v;
+  } else {
+    float v = part[e];
+    for (int ks = 1; ks < splits; ++ks) v += part[(int64_t)ks * n + e];
+    out[e] = v;
   }
 }
 
@@ -420,11 +605,6 @@ __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ 
 constexpr int LQP = 288;  // bf16 per staged Q row
 constexpr int LPP = 32;   // bf16 per staged P row
 
-typedef __bf16 bf16x4l __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x4l lds_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4l __attribute__((address_space(3)))*)(p));
-}
 
 // One token reduction of lora_grad: partial[c][rho][j] = sum over the tokens
 // of chunk c of P[m][rho] Q[m][j].
@@ -463,7 +643,16 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
   const int qrow = tid >> 5, qch = tid & 31, prow = tid >> 3, prho = 4 * (tid & 7);
   uint4 qv[4];
   float pv[RB][4];
+  // full steps (32 tokens in the chunk, 256 columns in range, 16-byte rows)
+  // load without per-lane guards, so no load waits on another
+  const bool fullq = vecq && j0 + 256 <= J;
+  const bool fullp = (r % 4) == 0 && rho0 + 32 * RB <= r && (reinterpret_cast<uintptr_t>(P) % 16) == 0;
   auto load = [&](int64_t m) __attribute__((always_inline)) {
+    if (m + 32 <= me && fullq) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        qv[u] = *reinterpret_cast<const uint4*>(Q + (m + 8 * u + qrow) * J + j0 + 8 * qch);
+    } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t mm = m + 8 * u + qrow;
@@ -479,7 +668,15 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
                            h[6] | ((uint32_t)h[7] << 16));
       }
     }
+    }
     const int64_t mm = m + prow;
+    if (m + 32 <= me && fullp) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float4 v = *reinterpret_cast<const float4*>(P + mm * r + rho0 + 32 * rb + prho);
+        pv[rb][0] = v.x; pv[rb][1] = v.y; pv[rb][2] = v.z; pv[rb][3] = v.w;
+      }
+    } else {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -487,6 +684,7 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
         const int rho = rho0 + 32 * rb + prho + e;
         pv[rb][e] = (mm < me && rho < r) ? P[mm * r + rho] : 0.0f;
       }
+    }
   };
   f32x16 acc[RB][2];
 #pragma unroll
@@ -608,6 +806,21 @@ __global__ __launch_bounds__(256) void k_lora_combine(LoraSum q0, LoraSum q1, in
     out[rho * J + j] = v;
 }
 
+// Split of the wide side product's reduction: about 512 workgroups of 128
+// rows x 64 ranks, at least 4 steps of 32 per split.
+struct SideSplit {
+  int64_t splits;
+  int64_t kc;  // reduction indices per split, a multiple of 32
+};
+SideSplit side_split_plan(int64_t M, int64_t I, int32_t r) {
+  const int64_t tiles = ceil_div(M, 128) * ceil_div((int64_t)r, 64), steps = ceil_div(I, 32);
+  int64_t ks = ceil_div(512, tiles);
+  const int64_t maxks = steps / 4 > 1 ? steps / 4 : 1;
+  if (ks > maxks) ks = maxks;
+  const int64_t kc = ceil_div(steps, ks) * 32;
+  return {ceil_div(I, kc), kc};
+}
+
 // Adapter side product (T = x A^T or U = dY B), needed by the main kernel's epilogue.
 template <typename T>
 void launch_side(const LinearArgs& g, hipStream_t st) {
@@ -617,19 +830,38 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const dim3 sg((unsigned)ceil_div(g.M, SR));
   if constexpr (sizeof(T) == 2) {
     const float* fac = g.backward ? g.B : g.A;
-#define NF4_SIDE(BWD, RT, R0) \
-  hipLaunchKernelGGL((k_side_bf16<BWD, RT>), sg, dim3(1024), 0, st, a, g.M, I, fac, g.r, R0, g.side)
-#define NF4_SIDE_RT(BWD)                                          \
-  do {                                                            \
-    if (g.r <= 16) NF4_SIDE(BWD, 1, 0);                           \
-    else if (g.r <= 32) NF4_SIDE(BWD, 2, 0);                      \
-    else for (int r0 = 0; r0 < g.r; r0 += 64) NF4_SIDE(BWD, 4, r0); \
-  } while (0)
-    if (g.backward)
-      NF4_SIDE_RT(true);
-    else
-      NF4_SIDE_RT(false);
-#undef NF4_SIDE_RT
+    if (g.r > 32) {
+      const SideSplit sp = side_split_plan(g.M, I, g.r);
+      const dim3 grid((unsigned)ceil_div(g.M, 128), (unsigned)sp.splits, (unsigned)ceil_div((int64_t)g.r, 64));
+      float* dst = sp.splits > 1 ? g.side_part : g.side;
+      const int64_t stride = g.M * (int64_t)g.r;
+      const bool fast = I % 8 == 0 && g.r % 8 == 0 && aligned(a, 16) && aligned(fac, 16);
+#define NF4_WIDE(BWD, FAST) \
+  hipLaunchKernelGGL((k_side_wide<BWD, FAST>), grid, dim3(256), 0, st, a, g.M, I, fac, g.r, sp.kc, dst, stride)
+      if (g.backward && fast) NF4_WIDE(true, true);
+      else if (g.backward) NF4_WIDE(true, false);
+      else if (fast) NF4_WIDE(false, true);
+      else NF4_WIDE(false, false);
+#undef NF4_WIDE
+      if (sp.splits > 1) {
+        if (stride % 4 == 0 && aligned(g.side, 16) && aligned(g.side_part, 16))
+          hipLaunchKernelGGL(k_side_sum<true>, dim3((unsigned)ceil_div(stride / 4, 256)), dim3(256), 0, st,
+                             g.side_part, stride, (int)sp.splits, g.side);
+        else
+          hipLaunchKernelGGL(k_side_sum<false>, dim3((unsigned)ceil_div(stride, 256)), dim3(256), 0, st, g.side_part,
+                             stride, (int)sp.splits, g.side);
+      }
+      return;
+    }
+#define NF4_SIDE(BWD, RT) \
+  hipLaunchKernelGGL((k_side_bf16<BWD, RT>), sg, dim3(1024), 0, st, a, g.M, I, fac, g.r, 0, g.side)
+    if (g.backward) {
+      if (g.r <= 16) NF4_SIDE(true, 1);
+      else NF4_SIDE(true, 2);
+    } else {
+      if (g.r <= 16) NF4_SIDE(false, 1);
+      else NF4_SIDE(false, 2);
+    }
 #undef NF4_SIDE
     return;
   }
@@ -661,8 +893,14 @@ int run_linear_general(const LinearArgs& g, hipStream_t st) {
 
 }  // namespace
 
+int64_t side_split_ws_bytes(int64_t M, int64_t I, int32_t r) {
+  if (r <= 32) return 0;
+  const SideSplit sp = side_split_plan(M, I, r);
+  return sp.splits > 1 ? (int64_t)round_up(sizeof(float) * (size_t)(sp.splits * M * r), 256) : 0;
+}
+
 int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const float* fac, int32_t r, bool backward,
-                        float* out, hipStream_t st) {
+                        float* out, float* part, hipStream_t st) {
   // A LinearArgs that carries only what launch_side reads.
   LinearArgs g{};
   g.a = L;
@@ -674,6 +912,7 @@ int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const
   g.B = backward ? fac : nullptr;
   g.r = r;
   g.side = out;
+  g.side_part = part;
   g.backward = backward;
   if (dt == NF4_BF16)
     launch_side<__bf16>(g, st);
@@ -693,25 +932,38 @@ int launch_linear(const LinearArgs& g, hipStream_t st) {
   return run_linear_general<float>(g, st);
 }
 
-// Tokens per chunk of the bf16 MFMA reduction: about 256 workgroups of 256
-// columns per problem, a multiple of the 32-token step. Fewer, longer chunks
-// than the general path keep the partial sums small next to the input.
-int64_t lora_chunk_mfma(int64_t M, int64_t J) {
-  const int64_t tiles = ceil_div(J, 256);
-  int64_t chunks = 256 / tiles;
+// Tokens per chunk of the bf16 MFMA reduction (a multiple of the 32-token
+// step), for about 512 workgroups of 256 columns (two per CU):
+//  - dB (N columns): 512 / tiles(N) chunks, the same with or without dA, so
+//    that LoRA-FA's dB sums in the same order as the full call's;
+//  - dA (K columns): 512 / (tiles(K) + tiles(N)) chunks, so that a dA
+//    workgroup walks about as many steps as the whole call's work spread over
+//    512 slots; dA's workgroups come first in the grid and the short dB ones
+//    cycle through the remaining slots.
+// Fewer, longer chunks than the general path keep the partial sums small next
+// to the input.
+int64_t lora_chunk_steps(int64_t M, int64_t tiles) {
+  int64_t chunks = 512 / tiles;
+  const int64_t steps = ceil_div(M, 32);
+  if (chunks > steps) chunks = steps;
   if (chunks < 1) chunks = 1;
   return ceil_div(ceil_div(M, chunks), 32) * 32;
+}
+int64_t lora_chunk_mfma_b(int64_t M, int64_t N) { return lora_chunk_steps(M, ceil_div(N, 256)); }
+int64_t lora_chunk_mfma_a(int64_t M, int64_t K, int64_t N) {
+  return lora_chunk_steps(M, ceil_div(K, 256) + ceil_div(N, 256));
 }
 
 // Chunks of either path (the query does not know the dtype, so the workspace
 // covers the larger).
-int64_t lora_chunks_max(int64_t M, int64_t J) {
-  const int64_t a = ceil_div(M, lora_chunk(M, J)), b = ceil_div(M, lora_chunk_mfma(M, J));
+int64_t lora_chunks_max(int64_t M, int64_t J, int64_t mfma_chunk) {
+  const int64_t a = ceil_div(M, lora_chunk(M, J)), b = ceil_div(M, mfma_chunk);
   return a > b ? a : b;
 }
 
 size_t lora_grad_ws(int64_t M, int64_t K, int64_t N, int32_t r, int fa) {
-  const int64_t chB = lora_chunks_max(M, N), chA = lora_chunks_max(M, K);
+  const int64_t chB = lora_chunks_max(M, N, lora_chunk_mfma_b(M, N));
+  const int64_t chA = lora_chunks_max(M, K, lora_chunk_mfma_a(M, K, N));
   size_t bytes = round_up(sizeof(float) * (size_t)(chB * r * N), 256);
   if (!fa) bytes += round_up(sizeof(float) * (size_t)(chA * r * K), 256);
   return bytes;
@@ -737,21 +989,24 @@ void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, floa
 void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int64_t N, const float* t,
                     const float* u, int32_t r, float s, float* dA, float* dB, float* partA, float* partB,
                     hipStream_t st) {
-  const int64_t chB = lora_chunk_mfma(M, N), chA = lora_chunk_mfma(M, K);
+  const int64_t chB = lora_chunk_mfma_b(M, N), chA = lora_chunk_mfma_a(M, K, N);
   const LoraProb pb{t, dy, N, chB, ceil_div(N, 256), partB};
   const LoraProb pa{u, x, K, chA, ceil_div(K, 256), partA};
   const int64_t blocksB = pb.col_tiles * ceil_div(M, chB);
   const int64_t blocksA = dA ? pa.col_tiles * ceil_div(M, chA) : 0;
-  // 32, 64 or 128 ranks per launch (further launches for the ranks past 128)
+  // dA's (longer) workgroups first; 32, 64 or 128 ranks per launch (further
+  // launches for the ranks past 128)
+  const LoraProb& p0 = dA ? pa : pb;
+  const int64_t blocks0 = dA ? blocksA : blocksB;
   for (int r0 = 0; r0 < r; r0 += 128) {
     const int left = r - r0;
     const dim3 grid((unsigned)(blocksB + blocksA));
     if (left <= 32)
-      hipLaunchKernelGGL(k_lora_mfma<1>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+      hipLaunchKernelGGL(k_lora_mfma<1>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
     else if (left <= 64)
-      hipLaunchKernelGGL(k_lora_mfma<2>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+      hipLaunchKernelGGL(k_lora_mfma<2>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
     else
-      hipLaunchKernelGGL(k_lora_mfma<4>, grid, dim3(256), 0, st, pb, dA ? pa : pb, blocksB, M, r, r0);
+      hipLaunchKernelGGL(k_lora_mfma<4>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
   }
   const LoraSum qb{partB, ceil_div(M, chB), N, true, dB};
   const LoraSum qa{partA, ceil_div(M, chA), K, false, dA};
@@ -762,7 +1017,7 @@ void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int
 
 int launch_lora_grad(const void* x, const void* dy, nf4_dtype dt, int64_t M, int64_t K, int64_t N, const float* t,
                      const float* u, int32_t r, float s, float* dA, float* dB, void* ws, hipStream_t st) {
-  const int64_t chunksB = lora_chunks_max(M, N);
+  const int64_t chunksB = lora_chunks_max(M, N, lora_chunk_mfma_b(M, N));
   float* partB = static_cast<float*>(ws);
   float* partA =
       reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(float) * (size_t)(chunksB * r * N), 256));

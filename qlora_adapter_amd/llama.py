@@ -141,7 +141,7 @@ class LlamaNF4:
         shapes = [(c.shape(n)[1], c.shape(n)[0]) for n in PROJ]
         if self.with_head:
             shapes.append((c.hidden, c.vocab))
-        need = max(nl.linear_workspace_bytes(S, k, n, bwd) for k, n in shapes for bwd in (False, True))
+        need = max(nl.linear_workspace_bytes(S, k, n, r, backward=bwd) for k, n in shapes for bwd in (False, True))
         self.lws = torch.empty(need, dtype=torch.uint8, device=self.dev) if need else None
         self.cur_x = None
         if self.with_head:

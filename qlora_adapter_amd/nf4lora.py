@@ -370,21 +370,26 @@ def embedding_rows(E: NF4Tensor, ids: torch.Tensor, dtype=torch.bfloat16, out: O
     return out
 
 
-def linear_workspace_bytes(M: int, K: int, N: int, backward: bool = False, r_side: int = 0) -> int:
-    """Device workspace the linear call needs for these sizes: the bf16 split
-    partial sums (0 for most shapes) plus, with r_side > 0, room for the M x
-    r_side fp32 side product when the caller does not take it (t_out / u_out
-    None)."""
-    v = int(load().nf4_linear_workspace_bytes(int(M), int(K), int(N), int(r_side), int(bool(backward))))
+WS_BACKWARD, WS_NO_SIDE_OUT = 1, 2
+
+
+def linear_workspace_bytes(M: int, K: int, N: int, r: int = 0, backward: bool = False, side_out: bool = True) -> int:
+    """Device workspace the linear call needs for these sizes and adapter rank
+    r: the bf16 split partial sums (0 for most shapes), the partial sums of a
+    split side product (bf16, r > 32) and, with side_out=False (no t_out /
+    u_out), room for the M x r fp32 side product itself."""
+    flags = (WS_BACKWARD if backward else 0) | (0 if side_out else WS_NO_SIDE_OUT)
+    v = int(load().nf4_linear_workspace_bytes(int(M), int(K), int(N), int(r), flags))
     if v < 0:
         _check("nf4_linear_workspace_bytes", v)
     return v
 
 
-def _linear_ws(workspace, M, K, N, backward, dtype, device, r_side):
-    need = linear_workspace_bytes(M, K, N, backward, r_side)
-    if dtype != torch.bfloat16:  # no split reduction in fp32: only the side-product part
-        need -= linear_workspace_bytes(M, K, N, backward, 0)
+def _linear_ws(workspace, M, K, N, backward, dtype, device, r, side_out):
+    if dtype == torch.bfloat16:
+        need = linear_workspace_bytes(M, K, N, r, backward, side_out)
+    else:  # fp32: neither reduction is split; only the side product itself
+        need = 0 if (side_out or not r) else (M * r * 4 + 255) // 256 * 256
     if workspace is None:
         if need == 0:
             return None, 0
@@ -424,7 +429,7 @@ def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, 
     if r and t_out is None and want_t:
         t_out = torch.empty((M, r), dtype=torch.float32, device=x.device)
     st = W.c_struct()
-    ws, wsb = _linear_ws(workspace, M, K, N, False, x.dtype, x.device, r if (r and t_out is None) else 0)
+    ws, wsb = _linear_ws(workspace, M, K, N, False, x.dtype, x.device, r, t_out is not None)
     _check("nf4_linear_fwd", load().nf4_linear_fwd(_ptr(x), _DT[x.dtype], M, K, ctypes.byref(st), N, _ptr(A),
                                                    _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _ptr(ws), wsb,
                                                    _stream(x.device)))
@@ -454,7 +459,7 @@ def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] =
     if r and u_out is None and want_u:
         u_out = torch.empty((M, r), dtype=torch.float32, device=dy.device)
     st = W.c_struct()
-    ws, wsb = _linear_ws(workspace, M, K, N, True, dy.dtype, dy.device, r if (r and u_out is None) else 0)
+    ws, wsb = _linear_ws(workspace, M, K, N, True, dy.dtype, dy.device, r, u_out is not None)
     _check("nf4_linear_bwd_input",
            load().nf4_linear_bwd_input(_ptr(dy), _DT[dy.dtype], M, N, ctypes.byref(st), K, _ptr(A), _ptr(B), r,
                                        float(s), _ptr(dx), _ptr(u_out), _ptr(ws), wsb, _stream(dy.device)))

@@ -110,7 +110,7 @@ def test_argument_errors_before_device(lib):
                                   None) == EUNSUP
     # split-reduction workspace: 512 tokens through a 4096 x 14336 projection need one in bf16
     assert L.nf4_linear_workspace_bytes(0, 64, 64, 0, 0) == EINVAL
-    assert L.nf4_linear_workspace_bytes(8, 64, 64, 0, 2) == EINVAL
+    assert L.nf4_linear_workspace_bytes(8, 64, 64, 0, 4) == EINVAL    # unknown flag
     assert L.nf4_linear_workspace_bytes(8, 64, 64, 257, 0) == EINVAL
     assert L.nf4_linear_workspace_bytes(4096, 4096, 4096, 0, 0) == 0   # large problems: no split
     need = L.nf4_linear_workspace_bytes(512, 14336, 4096, 0, 0)
@@ -138,9 +138,11 @@ def test_optional_side_products_and_recompute(lib):
     EINVAL, EWS = -1, -6
     M, K, N, r = 64, 576, 192, 8
     side = ((M * r * 4 + 255) // 256) * 256
-    # the side product adds M r fp32 (256-byte rounded) to the linear workspace
+    # without t_out / u_out the side product adds M r fp32 (256-byte rounded) to
+    # the linear workspace (NF4_WS_NO_SIDE_OUT = 2; NF4_WS_BACKWARD = 1)
     for bwd in (0, 1):
-        assert L.nf4_linear_workspace_bytes(M, K, N, r, bwd) == L.nf4_linear_workspace_bytes(M, K, N, 0, bwd) + side
+        assert L.nf4_linear_workspace_bytes(M, K, N, r, bwd | 2) == L.nf4_linear_workspace_bytes(M, K, N, r, bwd) + side
+        assert L.nf4_linear_workspace_bytes(M, K, N, r, bwd) == L.nf4_linear_workspace_bytes(M, K, N, 0, bwd)
     w = m._Tensor(16, 16, 16, 16, K * N, 1)
     # no t_out and no workspace: the side product has nowhere to go
     assert L.nf4_linear_fwd(16, 1, M, K, ctypes.byref(w), N, 16, 16, r, 1.0, 16, None, None, 0, None) == EWS
@@ -159,6 +161,35 @@ def test_optional_side_products_and_recompute(lib):
     assert L.lora_grad(None, 16, 1, M, K, N, None, None, 16, None, r, 1.0, None, 16, None, 0, None) == EWS
     # recomputing needs the larger workspace
     assert L.lora_grad(16, 16, 1, M, K, N, 16, 16, None, None, r, 1.0, 16, 16, 256, base + side, None) == EWS
+
+
+def test_wide_rank_side_product_workspace(lib):
+    """Ranks beyond 32 split the side product's reduction (over K forward, N
+    backward) into parts of at least 128 indices, about 512 workgroups of 128
+    rows x 64 ranks in all; the workspace holds one M x r fp32 partial product
+    per part, and lora_grad's recomputation takes the larger of its two."""
+    L, _ = lib
+    def parts(M, I, r):
+        tiles = -(-M // 128) * -(-r // 64)
+        steps = -(-I // 32)
+        ks = min(-(-512 // tiles), max(steps // 4, 1))
+        kc = -(-steps // ks) * 32
+        return -(-I // kc)
+    rnd = lambda b: (b + 255) // 256 * 256
+    for M, K, N, r in ((8192, 14336, 4096, 64), (4096, 4096, 4096, 100), (512, 4096, 14336, 256), (64, 576, 192, 33)):
+        for bwd in (0, 1):
+            I = N if bwd else K
+            ks = parts(M, I, r)
+            extra = rnd(ks * M * r * 4) if ks > 1 else 0
+            assert L.nf4_linear_workspace_bytes(M, K, N, r, bwd) == L.nf4_linear_workspace_bytes(M, K, N, 0, bwd) + extra
+        side = rnd(M * r * 4)
+        pt = rnd(parts(M, K, r) * M * r * 4) if parts(M, K, r) > 1 else 0
+        pu = rnd(parts(M, N, r) * M * r * 4) if parts(M, N, r) > 1 else 0
+        base = L.lora_grad_workspace_bytes(M, K, N, r, 0, 0)
+        assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 3) == base + 2 * side + max(pt, pu)
+        assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 1) == base + side + pt
+    # 32 and below: no split
+    assert L.nf4_linear_workspace_bytes(8192, 14336, 4096, 32, 1) == L.nf4_linear_workspace_bytes(8192, 14336, 4096, 0, 1)
 
 
 def test_small_kernel_offsets_stay_32_bit(lib):

@@ -280,7 +280,7 @@ def test_split_reduction(gpu, orc, M, K, N, r, bwd):
     bit (part 0 of the split adds the LoRA term to its partial sum before the
     parts are summed)."""
     print(f"[linear] split M={M} K={K} N={N} r={r} bwd={bwd}", flush=True)
-    assert gpu.linear_workspace_bytes(M, K, N, bwd) > 0
+    assert gpu.linear_workspace_bytes(M, K, N, backward=bwd) > 0
     c = make_case(M, K, N, r, torch.bfloat16, seed=M + N)
     s = gpu.lora_scale(32.0, r)
     Wq = gpu.quantize(c["W"], True)
@@ -341,10 +341,11 @@ def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
 @pytest.mark.parametrize("M,K,N,r", [(300, 1024, 576, 64), (129, 576, 1536, 100), (200, 640, 512, 256),
                                      (64, 256, 320, 33), (40, 448, 192, 128)])
 def test_large_ranks(gpu, orc, M, K, N, r):
-    """Ranks past 32 on the bf16 path (the side products in slices of 64 ranks,
-    the LoRA-gradient reduction in blocks of 32, 64 or 128 ranks per launch):
-    y, dX against the oracle at the bf16 bar, T, U, dA, dB at the fp32 bar, and
-    LoRA-FA's dB equal to the full call's."""
+    """Ranks past 32 on the bf16 path (the side products in workgroups of 64
+    ranks with a split reduction, the LoRA-gradient reduction in blocks of 32,
+    64 or 128 ranks per launch): y, dX against the oracle at the bf16 bar, T, U,
+    dA, dB at the fp32 bar, LoRA-FA's dB equal to the full call's, and the
+    workspace-held and recomputed side products equal to the returned ones."""
     print(f"[linear] large rank M={M} K={K} N={N} r={r}", flush=True)
     c = make_case(M, K, N, r, torch.bfloat16, seed=M + r)
     s = gpu.lora_scale(16.0, r, rslora=True)
@@ -364,3 +365,13 @@ def test_large_ranks(gpu, orc, M, K, N, r):
     dA_ref, dB_ref = orc.lora_grad(x, dy, T_ref, U_ref, s)
     assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
     assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
+    # side products left in the workspace, and T, U recomputed inside lora_grad:
+    # the same kernels and split, so the same bits
+    y2, _ = gpu.linear_fwd(c["x"], Wq, c["A"], c["B"], s, want_t=False)
+    dx2, _ = gpu.linear_bwd_input(c["dy"], Wq, c["A"], c["B"], s, want_u=False)
+    dA2, dB2 = gpu.lora_grad(c["x"], c["dy"], None, None, s, A=c["A"], B=c["B"])
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(dA2.view(torch.int32), dA.view(torch.int32))
+    assert torch.equal(dB2.view(torch.int32), dB.view(torch.int32))
