@@ -915,15 +915,32 @@ __device__ __forceinline__ void gemm_lora(f32x16 (&acc)[MS][NT], int64_t M, int6
   }
 }
 
-// Output tile store. Accumulator (i, t), elements 4k .. 4k + 3: token row
-// m0 + 32 MS wm + 32 i + l32, stage columns cc + 32 t + 8 k + 4 g + 0..3. In the
-// forward pass these are four consecutive output columns. In the input gradient
-// the even/odd chunk order puts weight columns 8 k + g + {0, 2, 4, 6} in lane
-// group g; the two lane groups swap half of their values so that each again
-// holds four consecutive columns (g = 0: 8 k .. 8 k + 3, g = 1: 8 k + 4 ..
-// 8 k + 7). Each group of four is one 8-byte buffer store (C % 4 == 0); stores
-// outside the output get an offset past the buffer's end, which the hardware
-// drops, so the epilogue has no branches.
+// Four bf16 output values of accumulator elements 4k .. 4k + 3 (token row
+// m0 + 32 MS wm + 32 i + l32, stage columns cc + 32 t + 8 k + 4 g + 0..3): in
+// the forward pass four consecutive output columns. In the input gradient the
+// even/odd chunk order puts weight columns 8 k + g + {0, 2, 4, 6} in lane group
+// g; the two lane groups swap half of their values so that each again holds
+// four consecutive columns (g = 0: 8 k .. 8 k + 3, g = 1: 8 k + 4 .. 8 k + 7).
+template <bool BWD>
+__device__ __forceinline__ void gemm_pack4(const f32x16& a, int k, int g, uint32_t& lo, uint32_t& hi) {
+  if (!BWD) {
+    lo = pack_bf16x2(a[4 * k], a[4 * k + 1]);
+    hi = pack_bf16x2(a[4 * k + 2], a[4 * k + 3]);
+  } else {
+    const uint32_t p01 = pack_bf16x2(a[4 * k], a[4 * k + 1]);      // g0: c0 c2  g1: c1 c3
+    const uint32_t p23 = pack_bf16x2(a[4 * k + 2], a[4 * k + 3]);  // g0: c4 c6  g1: c5 c7
+    const uint32_t recv = (uint32_t)__shfl_xor((int)(g ? p01 : p23), 32);
+    // g0: own c0 c2, received c1 c3; g1: own c5 c7, received c4 c6
+    const uint32_t ev = g ? recv : p01, od = g ? p23 : recv;
+    lo = __builtin_amdgcn_perm(od, ev, 0x05040100u);
+    hi = __builtin_amdgcn_perm(od, ev, 0x07060302u);
+  }
+}
+
+// Output tile store for C % 4 == 4 (8 bytes per lane): each group of four
+// columns is one 8-byte buffer store; stores outside the output get an offset
+// past the buffer's end, which the hardware drops, so the epilogue has no
+// branches.
 template <bool BWD, int MS, int NT>
 __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[MS][NT], __bf16* __restrict__ out, int64_t M, int64_t C,
                                            int64_t m0, int64_t cc, int lane, int wm) {
@@ -937,25 +954,62 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[MS][NT], __bf16* 
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float v[4] = {acc[i][t][4 * k], acc[i][t][4 * k + 1], acc[i][t][4 * k + 2], acc[i][t][4 * k + 3]};
         uint32_t lo, hi;
-        if (!BWD) {
-          lo = pack_bf16x2(v[0], v[1]);
-          hi = pack_bf16x2(v[2], v[3]);
-        } else {
-          const uint32_t p01 = pack_bf16x2(v[0], v[1]);  // g0: c0 c2  g1: c1 c3
-          const uint32_t p23 = pack_bf16x2(v[2], v[3]);  // g0: c4 c6  g1: c5 c7
-          const uint32_t recv = (uint32_t)__shfl_xor((int)(g ? p01 : p23), 32);
-          // g0: own c0 c2, received c1 c3; g1: own c5 c7, received c4 c6
-          const uint32_t ev = g ? recv : p01, od = g ? p23 : recv;
-          lo = __builtin_amdgcn_perm(od, ev, 0x05040100u);
-          hi = __builtin_amdgcn_perm(od, ev, 0x07060302u);
-        }
+        gemm_pack4<BWD>(acc[i][t], k, g, lo, hi);
         const int64_t c = cc + 32 * t + 8 * k + 4 * g;
         const uint32_t off = (m < M && c < C) ? (uint32_t)(2 * (m * C + c)) : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, orsrc, (int)off, 0, 0);
       }
     }
+  }
+}
+
+// Output tile store for C % 8 == 0, through LDS: the tile's 64 MS rows x 256
+// columns of bf16 are written into the (no longer needed) stage buffers, rows
+// 64 q .. + 63 into region q (ws0, ws1, as0, as1), 16-byte chunk c of row r at
+// chunk position c ^ (r % 32); then every thread stores whole 16-byte chunks,
+// 32 lanes per 512-byte row, so each store instruction writes full cache lines
+// (the accumulator layout itself would scatter 8 bytes over 32 rows per
+// instruction). Chunks outside the output are dropped as in gemm_store.
+template <bool BWD, int MS, int NT>
+__device__ __forceinline__ void gemm_store_tile(const f32x16 (&acc)[MS][NT], __bf16* __restrict__ out, int64_t M,
+                                                int64_t C, int64_t m0, int64_t c0, int cw, int tid, int wm,
+                                                __bf16* q0, __bf16* q1, __bf16* q2, __bf16* q3) {
+  constexpr int NW = 16 / NT, BM = 64 * MS;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  // every wave's LDS reads and every activation load into the stages are done
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int q = (32 * MS * wm + 32 * i) >> 6;  // wave-uniform region
+    __bf16* reg = q == 0 ? q0 : q == 1 ? q1 : q == 2 ? q2 : q3;
+    const int lr = (32 * i + l32) & 63;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t lo, hi;
+        gemm_pack4<BWD>(acc[i][t], k, g, lo, hi);
+        const int c = cw + 32 * t + 8 * k + 4 * g;
+        *reinterpret_cast<uint2*>(&reg[lr * 256 + 8 * ((c >> 3) ^ (lr & 31)) + (c & 7)]) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(2 * M * C), 0x00020000);
+  const int ch = tid & 31;
+  const int64_t col = c0 + 8 * ch;
+#pragma unroll
+  for (int it = 0; it < BM / (2 * NW); ++it) {
+    const int row = 2 * NW * it + (tid >> 5);
+    const int q = (2 * NW * it) >> 6;  // the iteration's rows lie in one region
+    const __bf16* reg = q == 0 ? q0 : q == 1 ? q1 : q == 2 ? q2 : q3;
+    const int lr = row & 63;
+    const uint4 v = *reinterpret_cast<const uint4*>(&reg[lr * 256 + 8 * (ch ^ (lr & 31))]);
+    const int64_t m = m0 + row;
+    const uint32_t off = (m < M && col < C) ? (uint32_t)(2 * (m * C + col)) : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, orsrc, (int)off, 0, 0);
   }
 }
 
@@ -1093,11 +1147,18 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
 
   // (The two paths store separately, so that no join merges the accumulators.)
   const int64_t cc = c0 + cw;
+  const bool whole = C % 8 == 0;
   if (r > 0) {
     gemm_lora<BWD, MS, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
-    gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
+    if (whole)
+      gemm_store_tile<BWD, MS, NT>(acc, out, M, C, m0, c0, cw, tid, wm, ws0, ws1, as0, as1);
+    else
+      gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
   } else {
-    gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
+    if (whole)
+      gemm_store_tile<BWD, MS, NT>(acc, out, M, C, m0, c0, cw, tid, wm, ws0, ws1, as0, as1);
+    else
+      gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
   }
 }
 
