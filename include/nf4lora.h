@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 5
+#define NF4LORA_ABI_VERSION 6
 
 enum nf4_status {
   NF4_OK = 0,
@@ -260,9 +260,10 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
  * rank r (0: no adapter). Three parts, each rounded up to 256 bytes: (1) bf16
  * only: a long reduction over few output tiles (short sequences through a
  * wide layer, e.g. 512 tokens through a 4096 x 14336 projection) is split in
- * parts whose fp32 partial sums the workspace holds; (2) r > 32: the side
- * product's reduction (over K forward, N backward) is split in parts whose
- * fp32 partial sums of the M x r product the workspace holds; (3) with
+ * parts whose fp32 partial sums the workspace holds; (2) r > 32, or fewer
+ * than 4096 token rows with a reduction of at least 2048: the side product's
+ * reduction (over K forward, N backward) is split in parts whose fp32 partial
+ * sums of the M x r product the workspace holds; (3) with
  * NF4_WS_NO_SIDE_OUT, M * r fp32 for the side product itself. Partial sums are
  * added in a fixed order, so results stay run-to-run identical. A call with a
  * NULL or smaller workspace than it needs fails with NF4_EWORKSPACE.
@@ -414,41 +415,53 @@ int nf4_add_rmsnorm(const void* x, const void* res, nf4_dtype dtype, int64_t row
 int nf4_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dtype, int64_t rows, int64_t width,
                     const float* gamma, const void* dres, void* dx, nf4_stream_t stream);
 
-/* Rotary embedding in place on x [S, heads*d]: for every head and i < d/2 the
- * pair (x_i, x_{i+d/2}) of the row at position pos is rotated by
- * pos * theta^(-2 i / d) (inverse != 0: by the negative angle, which is the
+/* Row strides: an `ld` argument of 0 (or the row's width) means rows are
+ * dense; otherwise it is the distance between rows in elements, larger than
+ * the row's width and a multiple of 16 bytes (NF4_EALIGN), so a caller can
+ * keep several activations side by side in one wider array (for example q, k
+ * and v as column blocks of one [S, (hq + 2 hkv) d] projection output). */
+
+/* Rotary embedding in place on x [S, heads*d] (rows ld apart): for every head
+ * and i < d/2 the pair (x_i, x_{i+d/2}) of the row at position pos is rotated
+ * by pos * theta^(-2 i / d) (inverse != 0: by the negative angle, which is the
  * input gradient of the forward rotation). Angles in fp64, cos/sin in fp32.
  * d even, d <= 256. */
-int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, int64_t ld, double theta, int inverse,
              nf4_stream_t stream);
 
 /* Causal grouped-query attention: o = softmax(q k^T / sqrt(d), causal) v per
- * query head h, which reads key/value head h / (hq / hkv). q, o [S, hq*d];
- * k, v [S, hkv*d]; lse [hq, S] receives each row's log-sum-exp (scaled
- * scores). d a multiple of 16 up to 128; hq a multiple of hkv. */
+ * query head h, which reads key/value head h / (hq / hkv). q [S, hq*d], k and
+ * v [S, hkv*d], with rows ld_qkv apart (0: each dense); o [S, hq*d] dense;
+ * lse [hq, S] receives each row's log-sum-exp (scaled scores). d a multiple of
+ * 16 up to 128; hq a multiple of hkv. */
 int nf4_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dtype, int64_t S, int32_t hq,
-                      int32_t hkv, int32_t d, void* o, float* lse, nf4_stream_t stream);
+                      int32_t hkv, int32_t d, int64_t ld_qkv, void* o, float* lse, nf4_stream_t stream);
 
 /* Input gradients of nf4_attention_fwd from dout, the forward's q, k, v, o and
  * lse: dq [S, hq*d], dk and dv [S, hkv*d] (key/value gradients summed over the
- * query heads of their group). delta [hq, S] is scratch that receives
- * rowsum(dout * o). No atomics; repeated calls are bitwise identical. */
+ * query heads of their group). q, k, v, dq, dk and dv have rows ld_qkv apart
+ * (0: each dense); dout and o are dense. delta [hq, S] is scratch that
+ * receives rowsum(dout * o). No atomics; repeated calls are bitwise
+ * identical. */
 int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
-                      void* dk, void* dv, nf4_stream_t stream);
+                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t ld_qkv, float* delta,
+                      void* dq, void* dk, void* dv, nf4_stream_t stream);
 
 /* out = a + b (+ c when c is not NULL) over n entries, summed in fp32 and
  * rounded once: the input gradient of a layer input that feeds several
  * projections. out may alias a. */
 int nf4_add(const void* a, const void* b, const void* c, nf4_dtype dtype, int64_t n, void* out, nf4_stream_t stream);
 
-/* a = silu(g) * u elementwise over n entries, silu(z) = z / (1 + exp(-z)). */
-int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream);
+/* a = silu(g) * u elementwise over rows x width entries, silu(z) =
+ * z / (1 + exp(-z)); g and u have rows ld apart (0: dense), a is dense. */
+int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t rows, int64_t width, int64_t ld, void* a,
+               nf4_stream_t stream);
 
 /* Input gradients of nf4_swiglu: dg = da u s (1 + g (1 - s)), du = da g s with
- * s = 1 / (1 + exp(-g)). */
-int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t n, void* dg, void* du,
-                   nf4_stream_t stream);
+ * s = 1 / (1 + exp(-g)); g, u, dg and du have rows ld apart (0: dense), da is
+ * dense. */
+int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t rows, int64_t width,
+                   int64_t ld, void* dg, void* du, nf4_stream_t stream);
 
 /* Token cross-entropy of logits z [T, V] against int64 targets [T]:
  * tok_loss[t] = logsumexp(z_t) - z_t[target_t] (fp32, [T]), loss[0] = their

@@ -238,14 +238,28 @@ int nf4_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype 
   return launch_rmsnorm_bwd(dy, x, rstd, dtype, rows, width, gamma, dres, dx, as_stream(stream));
 }
 
-int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+namespace {
+// Row stride of a strided activation: 0 (or `width`) means dense; a larger
+// stride must be a whole number of 16-byte units (NF4_EALIGN).
+int row_stride(nf4_dtype dtype, int64_t width, int64_t ld, int64_t* out) {
+  if (ld == 0) ld = width;
+  if (ld < width || ld > (int64_t(1) << 40)) return NF4_EINVAL;
+  if (ld > width && (ld * (dtype == NF4_BF16 ? 2 : 4)) % 16 != 0) return NF4_EALIGN;
+  *out = ld;
+  return NF4_OK;
+}
+}  // namespace
+
+int nf4_rope(void* x, nf4_dtype dtype, int64_t S, int32_t heads, int32_t d, int64_t ld, double theta, int inverse,
              nf4_stream_t stream) {
   if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
   if (!x || S < 1 || S >= (int64_t(1) << 31) || heads < 1 || d < 2 || d > 256 || d % 2 != 0) return NF4_EINVAL;
   if (!std::isfinite(theta) || theta <= 1.0 || (inverse != 0 && inverse != 1)) return NF4_EINVAL;
+  int64_t lx = 0;
+  if (int rc = row_stride(dtype, (int64_t)heads * d, ld, &lx)) return rc;
   if (!aligned(x, 16)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_rope(x, dtype, S, heads, d, theta, inverse, as_stream(stream));
+  return launch_rope(x, dtype, S, heads, d, lx, theta, inverse, as_stream(stream));
 }
 
 namespace {
@@ -258,26 +272,33 @@ int check_attention(nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t
 }  // namespace
 
 int nf4_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dtype, int64_t S, int32_t hq,
-                      int32_t hkv, int32_t d, void* o, float* lse, nf4_stream_t stream) {
+                      int32_t hkv, int32_t d, int64_t ld_qkv, void* o, float* lse, nf4_stream_t stream) {
   if (int rc = check_attention(dtype, S, hq, hkv, d)) return rc;
   if (!q || !k || !v || !o || !lse) return NF4_EINVAL;
+  int64_t lq = 0, lk = 0;
+  if (int rc = row_stride(dtype, (int64_t)hq * d, ld_qkv, &lq)) return rc;
+  if (int rc = row_stride(dtype, (int64_t)hkv * d, ld_qkv, &lk)) return rc;
   const void* arrays[] = {q, k, v, o, lse};
   for (const void* p : arrays)
     if (!aligned(p, 16)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_attention_fwd(q, k, v, dtype, S, hq, hkv, d, o, lse, as_stream(stream));
+  return launch_attention_fwd(q, k, v, dtype, S, hq, hkv, d, lq, lk, o, lse, as_stream(stream));
 }
 
 int nf4_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
-                      void* dk, void* dv, nf4_stream_t stream) {
+                      nf4_dtype dtype, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t ld_qkv, float* delta,
+                      void* dq, void* dk, void* dv, nf4_stream_t stream) {
   if (int rc = check_attention(dtype, S, hq, hkv, d)) return rc;
   if (!dout || !q || !k || !v || !o || !lse || !delta || !dq || !dk || !dv) return NF4_EINVAL;
+  int64_t lq = 0, lk = 0;
+  if (int rc = row_stride(dtype, (int64_t)hq * d, ld_qkv, &lq)) return rc;
+  if (int rc = row_stride(dtype, (int64_t)hkv * d, ld_qkv, &lk)) return rc;
   const void* arrays[] = {dout, q, k, v, o, lse, delta, dq, dk, dv};
   for (const void* p : arrays)
     if (!aligned(p, 16)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_attention_bwd(dout, q, k, v, o, lse, dtype, S, hq, hkv, d, delta, dq, dk, dv, as_stream(stream));
+  return launch_attention_bwd(dout, q, k, v, o, lse, dtype, S, hq, hkv, d, lq, lk, delta, dq, dk, dv,
+                              as_stream(stream));
 }
 
 int nf4_add(const void* a, const void* b, const void* c, nf4_dtype dtype, int64_t n, void* out, nf4_stream_t stream) {
@@ -290,23 +311,28 @@ int nf4_add(const void* a, const void* b, const void* c, nf4_dtype dtype, int64_
   return launch_add3(a, b, c, dtype, n, out, as_stream(stream));
 }
 
-int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t n, void* a, nf4_stream_t stream) {
+int nf4_swiglu(const void* g, const void* u, nf4_dtype dtype, int64_t rows, int64_t width, int64_t ld, void* a,
+               nf4_stream_t stream) {
   if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
-  if (!g || !u || !a || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;
+  if (!g || !u || !a || rows < 1 || width < 1 || rows > (int64_t(1) << 40) / width) return NF4_EINVAL;
+  int64_t lg = 0;
+  if (int rc = row_stride(dtype, width, ld, &lg)) return rc;
   if (!aligned(g, 16) || !aligned(u, 16) || !aligned(a, 16)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_swiglu(g, u, dtype, n, a, as_stream(stream));
+  return launch_swiglu(g, u, dtype, rows, width, lg, a, as_stream(stream));
 }
 
-int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t n, void* dg, void* du,
-                   nf4_stream_t stream) {
+int nf4_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dtype, int64_t rows, int64_t width,
+                   int64_t ld, void* dg, void* du, nf4_stream_t stream) {
   if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
-  if (!da || !g || !u || !dg || !du || n < 1 || n > (int64_t(1) << 40)) return NF4_EINVAL;
+  if (!da || !g || !u || !dg || !du || rows < 1 || width < 1 || rows > (int64_t(1) << 40) / width) return NF4_EINVAL;
+  int64_t lg = 0;
+  if (int rc = row_stride(dtype, width, ld, &lg)) return rc;
   const void* arrays[] = {da, g, u, dg, du};
   for (const void* p : arrays)
     if (!aligned(p, 16)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
-  return launch_swiglu_bwd(da, g, u, dtype, n, dg, du, as_stream(stream));
+  return launch_swiglu_bwd(da, g, u, dtype, rows, width, lg, dg, du, as_stream(stream));
 }
 
 int nf4_cross_entropy(const void* z, nf4_dtype dtype, int64_t T, int64_t V, const int64_t* target, float* tok_loss,

@@ -142,7 +142,8 @@ constexpr int tiles_bytes(int per_wave) {
 template <int ND>
 __global__ __launch_bounds__(256) void k_attn_fwd_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                        const __bf16* __restrict__ v, int64_t S, int hq, int hkv,
-                                                       float sl2, __bf16* __restrict__ o, float* __restrict__ lse) {
+                                                       int64_t lq, int64_t lk, float sl2, __bf16* __restrict__ o,
+                                                       float* __restrict__ lse) {
   constexpr int D = 32 * ND, TP = D + 16, NE = ND * 16 + 2;
   constexpr int SMEM = tiles_bytes<ND>(1) > NE * 64 * 4 ? tiles_bytes<ND>(1) : NE * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_mfma(const __bf16* __restrict_
   const int h = blockIdx.y, kh = h / (hq / hkv);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t q0 = (nqb - 1 - (int64_t)blockIdx.x) * AB;
-  const int64_t ldq = (int64_t)hq * D, ldk = (int64_t)hkv * D;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * D;  // q rows, k and v rows, o rows
   const int64_t qi = q0 + l32, qr = qi < S ? qi : S - 1;
   bf16x8 qf[2 * ND];
 #pragma unroll
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_mfma(const __bf16* __restrict_
   }
   if (wave == 0 && qi < S) {
     const float inv = 1.0f / lsum;
-    __bf16* orow = o + qi * ldq + (int64_t)h * D;
+    __bf16* orow = o + qi * ldo + (int64_t)h * D;
 #pragma unroll
     for (int tt = 0; tt < ND; ++tt)
 #pragma unroll
@@ -310,8 +311,9 @@ template <int ND>
 __global__ __launch_bounds__(256) void k_attn_dq_mfma(const __bf16* __restrict__ dout, const __bf16* __restrict__ q,
                                                       const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ o, const float* __restrict__ lse,
-                                                      int64_t S, int hq, int hkv, float sl2, float scale,
-                                                      float* __restrict__ delta, __bf16* __restrict__ dq) {
+                                                      int64_t S, int hq, int hkv, int64_t lq, int64_t lk, float sl2,
+                                                      float scale, float* __restrict__ delta,
+                                                      __bf16* __restrict__ dq) {
   constexpr int D = 32 * ND, TP = D + 16;
   constexpr int SMEM = tiles_bytes<ND>(2) > ND * 16 * 64 * 4 ? tiles_bytes<ND>(2) : ND * 16 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -320,11 +322,11 @@ __global__ __launch_bounds__(256) void k_attn_dq_mfma(const __bf16* __restrict__
   const int h = blockIdx.y, kh = h / (hq / hkv);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t q0 = (nqb - 1 - (int64_t)blockIdx.x) * AB;
-  const int64_t ldq = (int64_t)hq * D, ldk = (int64_t)hkv * D;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * D;  // q and dq rows, k and v rows, o and dO rows
   const int64_t qi = q0 + l32, qr = qi < S ? qi : S - 1;
   const __bf16* qrow = q + qr * ldq + (int64_t)h * D;
-  const __bf16* drow = dout + qr * ldq + (int64_t)h * D;
-  const __bf16* orow = o + qr * ldq + (int64_t)h * D;
+  const __bf16* drow = dout + qr * ldo + (int64_t)h * D;
+  const __bf16* orow = o + qr * ldo + (int64_t)h * D;
   bf16x8 qf[2 * ND], df[2 * ND];
   float dl = 0.0f;
 #pragma unroll
@@ -399,8 +401,8 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
                                                        const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ delta, int64_t S, int hq, int hkv,
-                                                       float sl2, float scale, __bf16* __restrict__ dk,
-                                                       __bf16* __restrict__ dv) {
+                                                       int64_t lq, int64_t lk, float sl2, float scale,
+                                                       __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int D = 32 * ND, TP = D + 16;
   constexpr int SMEM = tiles_bytes<ND>(2) > 2 * ND * 16 * 64 * 4 ? tiles_bytes<ND>(2) : 2 * ND * 16 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int kh = blockIdx.y, grp = hq / hkv;
   const int64_t k0 = (int64_t)blockIdx.x * AB;
-  const int64_t ldq = (int64_t)hq * D, ldk = (int64_t)hkv * D;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * D;  // q rows, k v dk dv rows, dO rows
   const int64_t kj = k0 + l32, kr = kj < S ? kj : S - 1;
   bf16x8 kf[2 * ND], vf[2 * ND];
 #pragma unroll
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
     const int h = kh * grp + (int)(it / nq);
     const int64_t q0 = (qb0 + it % nq) * AB;
     tile_load<D>(qr_, q, ldq, q0, S, (int64_t)h * D, lane);
-    tile_load<D>(dr_, dout, ldq, q0, S, (int64_t)h * D, lane);
+    tile_load<D>(dr_, dout, ldo, q0, S, (int64_t)h * D, lane);
     const int64_t qq = (q0 + l32 < S) ? q0 + l32 : S - 1;
     lr_ = lse[(int64_t)h * S + qq] * kLog2e;
     dlr_ = delta[(int64_t)h * S + qq];
@@ -487,24 +489,25 @@ __global__ __launch_bounds__(256) void k_attn_dkv_mfma(const __bf16* __restrict_
 }
 
 template <int ND>
-void fwd_nd(const void* q, const void* k, const void* v, int64_t S, int hq, int hkv, float sl2, void* o, float* lse,
-            hipStream_t st) {
+void fwd_nd(const void* q, const void* k, const void* v, int64_t S, int hq, int hkv, int64_t lq, int64_t lk, float sl2,
+            void* o, float* lse, hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(S, AB), (unsigned)hq);
   hipLaunchKernelGGL(k_attn_fwd_mfma<ND>, grid, dim3(256), 0, st, static_cast<const __bf16*>(q),
-                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), S, hq, hkv, sl2,
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), S, hq, hkv, lq, lk, sl2,
                      static_cast<__bf16*>(o), lse);
 }
 
 template <int ND>
 void bwd_nd(const void* dout, const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t S,
-            int hq, int hkv, float sl2, float scale, float* delta, void* dq, void* dk, void* dv, hipStream_t st) {
+            int hq, int hkv, int64_t lq, int64_t lk, float sl2, float scale, float* delta, void* dq, void* dk, void* dv,
+            hipStream_t st) {
   hipLaunchKernelGGL(k_attn_dq_mfma<ND>, dim3((unsigned)ceil_div(S, AB), (unsigned)hq), dim3(256), 0, st,
                      static_cast<const __bf16*>(dout), static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(o), lse, S, hq, hkv, sl2, scale, delta,
-                     static_cast<__bf16*>(dq));
+                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(o), lse, S, hq, hkv, lq, lk, sl2, scale,
+                     delta, static_cast<__bf16*>(dq));
   hipLaunchKernelGGL(k_attn_dkv_mfma<ND>, dim3((unsigned)ceil_div(S, AB), (unsigned)hkv), dim3(256), 0, st,
                      static_cast<const __bf16*>(dout), static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), lse, delta, S, hq, hkv, sl2, scale, static_cast<__bf16*>(dk),
+                     static_cast<const __bf16*>(v), lse, delta, S, hq, hkv, lq, lk, sl2, scale, static_cast<__bf16*>(dk),
                      static_cast<__bf16*>(dv));
 }
 
@@ -513,28 +516,28 @@ void bwd_nd(const void* dout, const void* q, const void* k, const void* v, const
 bool attention_mfma_supported(nf4_dtype dt, int32_t d) { return dt == NF4_BF16 && d % 32 == 0 && d <= 128; }
 
 int launch_attention_fwd_mfma(const void* q, const void* k, const void* v, int64_t S, int32_t hq, int32_t hkv,
-                              int32_t d, void* o, float* lse, hipStream_t st) {
+                              int32_t d, int64_t lq, int64_t lk, void* o, float* lse, hipStream_t st) {
   const float sl2 = (float)(kLog2e / std::sqrt((double)d));
   switch (d / 32) {
-    case 1: fwd_nd<1>(q, k, v, S, hq, hkv, sl2, o, lse, st); break;
-    case 2: fwd_nd<2>(q, k, v, S, hq, hkv, sl2, o, lse, st); break;
-    case 3: fwd_nd<3>(q, k, v, S, hq, hkv, sl2, o, lse, st); break;
-    case 4: fwd_nd<4>(q, k, v, S, hq, hkv, sl2, o, lse, st); break;
+    case 1: fwd_nd<1>(q, k, v, S, hq, hkv, lq, lk, sl2, o, lse, st); break;
+    case 2: fwd_nd<2>(q, k, v, S, hq, hkv, lq, lk, sl2, o, lse, st); break;
+    case 3: fwd_nd<3>(q, k, v, S, hq, hkv, lq, lk, sl2, o, lse, st); break;
+    case 4: fwd_nd<4>(q, k, v, S, hq, hkv, lq, lk, sl2, o, lse, st); break;
     default: return NF4_EUNSUPPORTED;
   }
   return launch_status();
 }
 
 int launch_attention_bwd_mfma(const void* dout, const void* q, const void* k, const void* v, const void* o,
-                              const float* lse, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
-                              void* dk, void* dv, hipStream_t st) {
+                              const float* lse, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t lq, int64_t lk,
+                              float* delta, void* dq, void* dk, void* dv, hipStream_t st) {
   const double sc = 1.0 / std::sqrt((double)d);
   const float sl2 = (float)(kLog2e * sc), scale = (float)sc;
   switch (d / 32) {
-    case 1: bwd_nd<1>(dout, q, k, v, o, lse, S, hq, hkv, sl2, scale, delta, dq, dk, dv, st); break;
-    case 2: bwd_nd<2>(dout, q, k, v, o, lse, S, hq, hkv, sl2, scale, delta, dq, dk, dv, st); break;
-    case 3: bwd_nd<3>(dout, q, k, v, o, lse, S, hq, hkv, sl2, scale, delta, dq, dk, dv, st); break;
-    case 4: bwd_nd<4>(dout, q, k, v, o, lse, S, hq, hkv, sl2, scale, delta, dq, dk, dv, st); break;
+    case 1: bwd_nd<1>(dout, q, k, v, o, lse, S, hq, hkv, lq, lk, sl2, scale, delta, dq, dk, dv, st); break;
+    case 2: bwd_nd<2>(dout, q, k, v, o, lse, S, hq, hkv, lq, lk, sl2, scale, delta, dq, dk, dv, st); break;
+    case 3: bwd_nd<3>(dout, q, k, v, o, lse, S, hq, hkv, lq, lk, sl2, scale, delta, dq, dk, dv, st); break;
+    case 4: bwd_nd<4>(dout, q, k, v, o, lse, S, hq, hkv, lq, lk, sl2, scale, delta, dq, dk, dv, st); break;
     default: return NF4_EUNSUPPORTED;
   }
   return launch_status();

@@ -272,7 +272,8 @@ __device__ __forceinline__ void load_rows(float* s, const T* src, int64_t ld, in
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, int64_t S, int hq, int hkv, int d,
-                                                  float scale, T* __restrict__ o, float* __restrict__ lse) {
+                                                  int64_t lq, int64_t lk, float scale, T* __restrict__ o,
+                                                  float* __restrict__ lse) {
   __shared__ float qs[AQ * ADMAX];
   __shared__ float ks[AKB * ADMAX];
   __shared__ float vs[AKB * ADMAX];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
   const int64_t q0 = (int64_t)blockIdx.x * AQ;
   const int t = threadIdx.x, r = t >> 4, c = t & 15;
   const int64_t qi = q0 + r;
-  const int64_t ldq = (int64_t)hq * d, ldk = (int64_t)hkv * d;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * d;
   load_rows(qs, q, ldq, q0, AQ, S, h, d);
   float m = -INFINITY, l = 0.0f;
   float acc[ADMAX / 16];
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
   }
   if (qi < S) {
     const float inv = 1.0f / l;
-    for (int j = 0; j < nd; ++j) stf(o, qi * ldq + (int64_t)h * d + c + 16 * j, acc[j] * inv);
+    for (int j = 0; j < nd; ++j) stf(o, qi * ldo + (int64_t)h * d + c + 16 * j, acc[j] * inv);
     if (c == 0) lse[(int64_t)h * S + qi] = m + logf(l);
   }
 }
@@ -338,8 +339,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_attn_dq(const T* __restrict__ dout, const T* __restrict__ q,
                                                  const T* __restrict__ k, const T* __restrict__ v,
                                                  const T* __restrict__ o, const float* __restrict__ lse, int64_t S,
-                                                 int hq, int hkv, int d, float scale, float* __restrict__ delta,
-                                                 T* __restrict__ dq) {
+                                                 int hq, int hkv, int d, int64_t lq, int64_t lk, float scale,
+                                                 float* __restrict__ delta, T* __restrict__ dq) {
   __shared__ float qs[AQ * ADMAX];
   __shared__ float dos[AQ * ADMAX];
   __shared__ float ks[AKB * ADMAX];
@@ -349,15 +350,15 @@ __global__ __launch_bounds__(256) void k_attn_dq(const T* __restrict__ dout, con
   const int64_t q0 = (int64_t)blockIdx.x * AQ;
   const int t = threadIdx.x, r = t >> 4, c = t & 15;
   const int64_t qi = q0 + r;
-  const int64_t ldq = (int64_t)hq * d, ldk = (int64_t)hkv * d;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * d;
   load_rows(qs, q, ldq, q0, AQ, S, h, d);
-  load_rows(dos, dout, ldq, q0, AQ, S, h, d);
+  load_rows(dos, dout, ldo, q0, AQ, S, h, d);
   const int nd = d / 16;
   // delta of this row (16 threads, d / 16 products each)
   float dl = 0.0f;
   for (int j = 0; j < nd; ++j) {
     const int e = c + 16 * j;
-    dl += (qi < S) ? ldf(dout, qi * ldq + (int64_t)h * d + e) * ldf(o, qi * ldq + (int64_t)h * d + e) : 0.0f;
+    dl += (qi < S) ? ldf(dout, qi * ldo + (int64_t)h * d + e) * ldf(o, qi * ldo + (int64_t)h * d + e) : 0.0f;
   }
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) dl += __shfl_xor(dl, off);
@@ -401,8 +402,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_attn_dkv(const T* __restrict__ dout, const T* __restrict__ q,
                                                   const T* __restrict__ k, const T* __restrict__ v,
                                                   const float* __restrict__ lse, const float* __restrict__ delta,
-                                                  int64_t S, int hq, int hkv, int d, float scale, T* __restrict__ dk,
-                                                  T* __restrict__ dv) {
+                                                  int64_t S, int hq, int hkv, int d, int64_t lq, int64_t lk,
+                                                  float scale, T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float ks[AQ * ADMAX];
   __shared__ float vs[AQ * ADMAX];
   __shared__ float qs[AKB * ADMAX];
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void k_attn_dkv(const T* __restrict__ dout, co
   const int64_t k0 = (int64_t)blockIdx.x * AQ;
   const int t = threadIdx.x, r = t >> 4, c = t & 15;
   const int64_t kj = k0 + r;
-  const int64_t ldq = (int64_t)hq * d, ldk = (int64_t)hkv * d;
+  const int64_t ldq = lq, ldk = lk, ldo = (int64_t)hq * d;
   load_rows(ks, k, ldk, k0, AQ, S, kh, d);
   load_rows(vs, v, ldk, k0, AQ, S, kh, d);
   const int nd = d / 16;
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(256) void k_attn_dkv(const T* __restrict__ dout, co
     for (int64_t q0 = qstart; q0 < S; q0 += AKB) {
       __syncthreads();
       load_rows(qs, q, ldq, q0, AKB, S, h, d);
-      load_rows(dos, dout, ldq, q0, AKB, S, h, d);
+      load_rows(dos, dout, ldo, q0, AKB, S, h, d);
       for (int e = threadIdx.x; e < AKB; e += 256) {
         const int64_t qi = q0 + e;
         ls[e] = qi < S ? lse[(int64_t)h * S + qi] : 0.0f;
@@ -483,24 +484,31 @@ __global__ __launch_bounds__(256) void k_add3(const T* a, const T* b, const T* c
 
 // ---------------------------------------------------------------- SwiGLU
 
+// Rows of `width` entries; g, u (and dg, du) are rows ld apart, a and da dense.
+// Workgroup (x, y): columns 256 x .. + 255 of rows y, y + gridDim.y, ...
 template <typename T>
-__global__ __launch_bounds__(256) void k_swiglu(const T* __restrict__ g, const T* __restrict__ u, int64_t n,
-                                                T* __restrict__ a) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float z = ldf(g, i);
-  stf(a, i, z / (1.0f + expf(-z)) * ldf(u, i));
+__global__ __launch_bounds__(256) void k_swiglu(const T* __restrict__ g, const T* __restrict__ u, int64_t rows,
+                                                int64_t width, int64_t ld, T* __restrict__ a) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= width) return;
+  for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
+    const float z = ldf(g, m * ld + j);
+    stf(a, m * width + j, z / (1.0f + expf(-z)) * ldf(u, m * ld + j));
+  }
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const T* __restrict__ da, const T* __restrict__ g,
-                                                    const T* __restrict__ u, int64_t n, T* __restrict__ dg,
-                                                    T* __restrict__ du) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float z = ldf(g, i), s = 1.0f / (1.0f + expf(-z)), dav = ldf(da, i);
-  stf(dg, i, dav * ldf(u, i) * s * (1.0f + z * (1.0f - s)));
-  stf(du, i, dav * z * s);
+                                                    const T* __restrict__ u, int64_t rows, int64_t width, int64_t ld,
+                                                    T* __restrict__ dg, T* __restrict__ du) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= width) return;
+  for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
+    const int64_t e = m * ld + j;
+    const float z = ldf(g, e), s = 1.0f / (1.0f + expf(-z)), dav = ldf(da, m * width + j);
+    stf(dg, e, dav * ldf(u, e) * s * (1.0f + z * (1.0f - s)));
+    stf(du, e, dav * z * s);
+  }
 }
 
 // ---------------------------------------------------------------- cross-entropy
@@ -659,38 +667,38 @@ int launch_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dty
   return launch_status();
 }
 
-int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, int64_t ld, double theta, int inverse,
                 hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)S), dim3(256), 0, st, static_cast<T*>(x),
-                                      (int64_t)heads * d, heads, d, theta, inverse));
+  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)S), dim3(256), 0, st, static_cast<T*>(x), ld, heads,
+                                      d, theta, inverse));
   return launch_status();
 }
 
 int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dt, int64_t S, int32_t hq,
-                         int32_t hkv, int32_t d, void* o, float* lse, hipStream_t st) {
-  if (attention_mfma_supported(dt, d)) return launch_attention_fwd_mfma(q, k, v, S, hq, hkv, d, o, lse, st);
+                         int32_t hkv, int32_t d, int64_t lq, int64_t lk, void* o, float* lse, hipStream_t st) {
+  if (attention_mfma_supported(dt, d)) return launch_attention_fwd_mfma(q, k, v, S, hq, hkv, d, lq, lk, o, lse, st);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const dim3 grid((unsigned)ceil_div(S, AQ), (unsigned)hq);
   NF4_DISPATCH(dt, hipLaunchKernelGGL(k_attn_fwd<T>, grid, dim3(256), 0, st, static_cast<const T*>(q),
-                                      static_cast<const T*>(k), static_cast<const T*>(v), S, hq, hkv, d, scale,
-                                      static_cast<T*>(o), lse));
+                                      static_cast<const T*>(k), static_cast<const T*>(v), S, hq, hkv, d, lq, lk,
+                                      scale, static_cast<T*>(o), lse));
   return launch_status();
 }
 
 int launch_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
-                         const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta,
-                         void* dq, void* dk, void* dv, hipStream_t st) {
+                         const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t lq,
+                         int64_t lk, float* delta, void* dq, void* dk, void* dv, hipStream_t st) {
   if (attention_mfma_supported(dt, d))
-    return launch_attention_bwd_mfma(dout, q, k, v, o, lse, S, hq, hkv, d, delta, dq, dk, dv, st);
+    return launch_attention_bwd_mfma(dout, q, k, v, o, lse, S, hq, hkv, d, lq, lk, delta, dq, dk, dv, st);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   NF4_DISPATCH(dt, {
     hipLaunchKernelGGL(k_attn_dq<T>, dim3((unsigned)ceil_div(S, AQ), (unsigned)hq), dim3(256), 0, st,
                        static_cast<const T*>(dout), static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), static_cast<const T*>(o), lse, S, hq, hkv, d, scale, delta,
+                       static_cast<const T*>(v), static_cast<const T*>(o), lse, S, hq, hkv, d, lq, lk, scale, delta,
                        static_cast<T*>(dq));
     hipLaunchKernelGGL(k_attn_dkv<T>, dim3((unsigned)ceil_div(S, AQ), (unsigned)hkv), dim3(256), 0, st,
                        static_cast<const T*>(dout), static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), lse, delta, S, hq, hkv, d, scale, static_cast<T*>(dk),
+                       static_cast<const T*>(v), lse, delta, S, hq, hkv, d, lq, lk, scale, static_cast<T*>(dk),
                        static_cast<T*>(dv));
   });
   return launch_status();
@@ -703,17 +711,25 @@ int launch_add3(const void* a, const void* b, const void* c, nf4_dtype dt, int64
   return launch_status();
 }
 
-int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t n, void* a, hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu<T>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
-                                      static_cast<const T*>(g), static_cast<const T*>(u), n, static_cast<T*>(a)));
+// Grid of the row-wise SwiGLU kernels: column blocks of 256 times up to 65535
+// row groups (rows beyond loop).
+dim3 swiglu_grid(int64_t rows, int64_t width) {
+  return dim3((unsigned)ceil_div(width, 256), (unsigned)(rows < 65535 ? rows : 65535));
+}
+
+int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width, int64_t ld, void* a,
+                  hipStream_t st) {
+  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu<T>, swiglu_grid(rows, width), dim3(256), 0, st,
+                                      static_cast<const T*>(g), static_cast<const T*>(u), rows, width, ld,
+                                      static_cast<T*>(a)));
   return launch_status();
 }
 
-int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t n, void* dg, void* du,
-                      hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu_bwd<T>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
+int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width,
+                      int64_t ld, void* dg, void* du, hipStream_t st) {
+  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu_bwd<T>, swiglu_grid(rows, width), dim3(256), 0, st,
                                       static_cast<const T*>(da), static_cast<const T*>(g), static_cast<const T*>(u),
-                                      n, static_cast<T*>(dg), static_cast<T*>(du)));
+                                      rows, width, ld, static_cast<T*>(dg), static_cast<T*>(du)));
   return launch_status();
 }
 

@@ -105,24 +105,28 @@ int launch_add_rmsnorm(const void* x, const void* res, nf4_dtype dt, int64_t row
                        float eps, void* sum, void* y, float* rstd, hipStream_t st);
 int launch_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dtype dt, int64_t rows, int64_t D,
                        const float* gamma, const void* dres, void* dx, hipStream_t st);
-int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, double theta, int inverse,
+// Row strides (elements): rope's ld for x; attention's lq for q and dq, lk for
+// k, v, dk and dv (o and dO are dense, hq d per row).
+int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, int64_t ld, double theta, int inverse,
                 hipStream_t st);
 int launch_attention_fwd(const void* q, const void* k, const void* v, nf4_dtype dt, int64_t S, int32_t hq,
-                         int32_t hkv, int32_t d, void* o, float* lse, hipStream_t st);
+                         int32_t hkv, int32_t d, int64_t lq, int64_t lk, void* o, float* lse, hipStream_t st);
 int launch_attention_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
-                         const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta,
-                         void* dq, void* dk, void* dv, hipStream_t st);
+                         const float* lse, nf4_dtype dt, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t lq,
+                         int64_t lk, float* delta, void* dq, void* dk, void* dv, hipStream_t st);
 // Matrix-core attention (nf4_attention.hip): bf16 with head dim 32, 64, 96 or 128.
 bool attention_mfma_supported(nf4_dtype dt, int32_t d);
 int launch_attention_fwd_mfma(const void* q, const void* k, const void* v, int64_t S, int32_t hq, int32_t hkv,
-                              int32_t d, void* o, float* lse, hipStream_t st);
+                              int32_t d, int64_t lq, int64_t lk, void* o, float* lse, hipStream_t st);
 int launch_attention_bwd_mfma(const void* dout, const void* q, const void* k, const void* v, const void* o,
-                              const float* lse, int64_t S, int32_t hq, int32_t hkv, int32_t d, float* delta, void* dq,
-                              void* dk, void* dv, hipStream_t st);
+                              const float* lse, int64_t S, int32_t hq, int32_t hkv, int32_t d, int64_t lq, int64_t lk,
+                              float* delta, void* dq, void* dk, void* dv, hipStream_t st);
 int launch_add3(const void* a, const void* b, const void* c, nf4_dtype dt, int64_t n, void* out, hipStream_t st);
-int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t n, void* a, hipStream_t st);
-int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t n, void* dg, void* du,
-                      hipStream_t st);
+// SwiGLU over rows of `width`: g, u, dg, du rows ld apart; a and da dense.
+int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width, int64_t ld, void* a,
+                  hipStream_t st);
+int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width,
+                      int64_t ld, void* dg, void* du, hipStream_t st);
 int launch_cross_entropy(const void* z, nf4_dtype dt, int64_t T, int64_t V, const int64_t* target, float* tok_loss,
                          float* loss, void* dz, int32_t* status, hipStream_t st);
 

@@ -463,24 +463,28 @@ __global__ __launch_bounds__(256) void k_side_wide(const __bf16* __restrict__ L,
 
 // out[e] = sum over splits ks = 0, 1, ... in order of part[ks * n + e]; four
 // consecutive elements per thread (n % 4 == 0 and 16-byte aligned arrays: the
-// caller checks) or one.
+// caller checks) or one. The parts are loaded eight at a time before they are
+// added (in split order), so a short sum over many splits is not a chain of
+// dependent loads.
 template <bool VEC4>
 __global__ __launch_bounds__(256) void k_side_sum(const float* __restrict__ part, int64_t n, int splits,
                                                   float* __restrict__ out) {
+  typedef float vec __attribute__((ext_vector_type(VEC4 ? 4 : 1)));
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC4 ? 4 : 1);
   if (e >= n) return;
-  if constexpr (VEC4) {
-    float4 v = *reinterpret_cast<const float4*>(part + e);
-    for (int ks = 1; ks < splits; ++ks) {
-      const float4 w = *reinterpret_cast<const float4*>(part + (int64_t)ks * n + e);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
-    *reinterpret_cast<float4*>(out + e) = v;
-  } else {
-    float v = part[e];
-    for (int ks = 1; ks < splits; ++ks) v += part[(int64_t)ks * n + e];
-    out[e] = v;
+  const vec* p = reinterpret_cast<const vec*>(part + e);
+  const int64_t nv = n / (VEC4 ? 4 : 1);  // parts apart, in vectors
+  vec v = p[0];
+  int ks = 1;
+  for (; ks + 8 <= splits; ks += 8) {
+    vec w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = p[(int64_t)(ks + u) * nv];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += w[u];
   }
+  for (; ks < splits; ++ks) v += p[(int64_t)ks * nv];
+  *reinterpret_cast<vec*>(out + e) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -806,6 +810,15 @@ __global__ __launch_bounds__(256) void k_lora_combine(LoraSum q0, LoraSum q1, in
     out[rho * J + j] = v;
 }
 
+// The side product takes the split skinny GEMM (k_side_wide, then k_side_sum
+// over the parts) for ranks beyond 32, and for ranks up to 32 when k_side_bf16
+// (16 rows per workgroup) would leave most of the chip idle: fewer than 256
+// workgroups over a reduction of at least 2048 (a 512-token step through a
+// 4096-wide layer: 32 workgroups of k_side_bf16).
+bool side_split_path(int64_t M, int64_t I, int32_t r) {
+  return r > 32 || (ceil_div(M, SR) < 256 && I >= 2048);
+}
+
 // Split of the wide side product's reduction: about 512 workgroups of 128
 // rows x 64 ranks, at least 4 steps of 32 per split.
 struct SideSplit {
@@ -830,7 +843,7 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const dim3 sg((unsigned)ceil_div(g.M, SR));
   if constexpr (sizeof(T) == 2) {
     const float* fac = g.backward ? g.B : g.A;
-    if (g.r > 32) {
+    if (side_split_path(g.M, I, g.r)) {
       const SideSplit sp = side_split_plan(g.M, I, g.r);
       const dim3 grid((unsigned)ceil_div(g.M, 128), (unsigned)sp.splits, (unsigned)ceil_div((int64_t)g.r, 64));
       float* dst = sp.splits > 1 ? g.side_part : g.side;
@@ -894,7 +907,7 @@ int run_linear_general(const LinearArgs& g, hipStream_t st) {
 }  // namespace
 
 int64_t side_split_ws_bytes(int64_t M, int64_t I, int32_t r) {
-  if (r <= 32) return 0;
+  if (r <= 0 || !side_split_path(M, I, r)) return 0;
   const SideSplit sp = side_split_plan(M, I, r);
   return sp.splits > 1 ? (int64_t)round_up(sizeof(float) * (size_t)(sp.splits * M * r), 256) : 0;
 }

@@ -15,6 +15,16 @@ cross-entropy. Backward: lm_head and final norm, then per layer in reverse:
 recompute its forward from the saved x, run its backward. Last: one AdamW
 update of every adapter. The only activation kept per layer is x (one [S, D]
 tensor); everything else lives in buffers shared by all layers.
+
+Projections that read the same input are stored as one packed NF4 matrix
+(q, k, v stacked as [(hq + 2 hkv) d, D]; gate, up as [2 F, D]) and run as one
+linear call each way: the forward writes q, k, v (or gate, up) as column
+blocks of one output whose row stride the rotary, attention and SwiGLU calls
+take, and the input gradient of the stacked matrix is the sum over its members
+in one reduction. Adapters on members of a stack become one adapter of the
+stack: A stacked along the rank, B block-diagonal (member j's B in its rows and
+its rank block, zeros elsewhere); the zero blocks add exact zeros, and their
+gradients are cleared after every lora_grad, so they stay zero under AdamW.
 """
 from __future__ import annotations
 
@@ -26,6 +36,9 @@ import torch
 from . import nf4lora as nl
 
 PROJ = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+# Stacked matrices (one packed NF4 tensor each) and their members, in row order.
+STACKS = {"qkv": ("q_proj", "k_proj", "v_proj"), "o_proj": ("o_proj",), "gate_up": ("gate_proj", "up_proj"),
+          "down_proj": ("down_proj",)}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -64,17 +77,45 @@ def synthetic_normal(shape, std: float, seed: int, device) -> torch.Tensor:
 
 
 class Layer:
-    """One decoder layer: packed NF4 projections, fp32 norm weights, fp32
-    adapters with their gradients and AdamW moments."""
+    """One decoder layer: packed NF4 stacked projections (STACKS), fp32 norm
+    weights, fp32 adapters with their gradients and AdamW moments.
+
+    lora[stack] is the adapter of a stack (A [R, K], B [N, R] block-diagonal,
+    R = r times its adapted members); lora[name] holds views of one member's
+    A, B, dA and dB inside it (dB's view is that member's block)."""
 
     def __init__(self, cfg: LlamaConfig, weights: Dict[str, torch.Tensor], gamma1: torch.Tensor,
                  gamma2: torch.Tensor, adapters: Dict[str, tuple]):
-        self.W: Dict[str, nl.NF4Tensor] = {name: nl.quantize(weights[name], True) for name in PROJ}
+        self.W: Dict[str, nl.NF4Tensor] = {
+            st: nl.quantize(torch.cat([weights[n] for n in mem]) if len(mem) > 1 else weights[mem[0]], True)
+            for st, mem in STACKS.items()}
         self.gamma1, self.gamma2 = gamma1, gamma2
         self.lora: Dict[str, dict] = {}
-        for name, (A, B) in adapters.items():
-            self.lora[name] = dict(A=A, B=B, dA=torch.zeros_like(A), dB=torch.zeros_like(B), mA=torch.zeros_like(A),
-                                   vA=torch.zeros_like(A), mB=torch.zeros_like(B), vB=torch.zeros_like(B))
+        self.stack_lora: Dict[str, dict] = {}
+        for st, mem in STACKS.items():
+            ad = [n for n in mem if n in adapters]
+            if not ad:
+                continue
+            r = adapters[ad[0]][0].shape[0]
+            rows = [cfg.shape(n)[0] for n in mem]
+            K = cfg.shape(mem[0])[1]
+            dev = adapters[ad[0]][0].device
+            A = torch.cat([adapters[n][0] for n in ad]).contiguous()
+            B = torch.zeros((sum(rows), r * len(ad)), dtype=torch.float32, device=dev)
+            mask = torch.zeros_like(B)
+            for j, n in enumerate(ad):
+                off = sum(rows[:mem.index(n)])
+                B[off:off + rows[mem.index(n)], r * j:r * (j + 1)] = adapters[n][1]
+                mask[off:off + rows[mem.index(n)], r * j:r * (j + 1)] = 1.0
+            full = dict(A=A, B=B, dA=torch.zeros_like(A), dB=torch.zeros_like(B), mA=torch.zeros_like(A),
+                        vA=torch.zeros_like(A), mB=torch.zeros_like(B), vB=torch.zeros_like(B),
+                        mask=None if len(mem) == 1 else mask, K=K)
+            self.stack_lora[st] = full
+            for j, n in enumerate(ad):
+                off, nr = sum(rows[:mem.index(n)]), rows[mem.index(n)]
+                blk = (slice(off, off + nr), slice(r * j, r * (j + 1)))
+                self.lora[n] = dict(A=A[r * j:r * (j + 1)], B=B[blk], dA=full["dA"][r * j:r * (j + 1)],
+                                    dB=full["dB"][blk])
 
     @staticmethod
     def synthetic(cfg: LlamaConfig, idx: int, device, w_std: float = 0.02) -> "Layer":
@@ -123,25 +164,39 @@ class LlamaNF4:
         self._alloc()
         self.step_count = 0
 
+    def _stack_shape(self, st: str):
+        """[N, K] of a stacked matrix."""
+        mem = STACKS[st]
+        return sum(self.cfg.shape(n)[0] for n in mem), self.cfg.shape(mem[0])[1]
+
     def _alloc(self):
         c, S = self.cfg, self.S
         e = lambda *sh: torch.empty(sh, dtype=self.dt, device=self.dev)
         f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=self.dev)
-        H, Hkv, d, D, F, r = c.heads, c.kv_heads, c.head_dim, c.hidden, c.ffn, c.lora_rank
-        self.b = dict(x=e(S, D), h1=e(S, D), q=e(S, H * d), k=e(S, Hkv * d), v=e(S, Hkv * d), a=e(S, H * d),
-                      o=e(S, D), x2=e(S, D), h2=e(S, D), g=e(S, F), u=e(S, F), sw=e(S, F), dn=e(S, D),
-                      lse=f(H, S), r1=f(S), r2=f(S), delta=f(H, S),
-                      dsw=e(S, F), dg=e(S, F), du=e(S, F), dh2a=e(S, D), dh2b=e(S, D), dx2=e(S, D), da=e(S, H * d),
-                      dq=e(S, H * d), dk=e(S, Hkv * d), dv=e(S, Hkv * d), dh1q=e(S, D), dh1k=e(S, D),
-                      dh1v=e(S, D), gA=e(S, D), gB=e(S, D))
-        self.T = {n: f(S, r) for n in c.lora_targets}
-        self.U = {n: f(S, r) for n in c.lora_targets}
-        self.gws = {n: torch.empty(nl.lora_grad_workspace_bytes(S, c.shape(n)[1], c.shape(n)[0], r),
-                                   dtype=torch.uint8, device=self.dev) for n in c.lora_targets}
-        shapes = [(c.shape(n)[1], c.shape(n)[0]) for n in PROJ]
+        H, Hkv, d, D, F = c.heads, c.kv_heads, c.head_dim, c.hidden, c.ffn
+        QKV = (H + 2 * Hkv) * d
+        self.b = dict(x=e(S, D), h1=e(S, D), qkv=e(S, QKV), a=e(S, H * d), o=e(S, D), x2=e(S, D), h2=e(S, D),
+                      gu=e(S, 2 * F), sw=e(S, F), dn=e(S, D), lse=f(H, S), r1=f(S), r2=f(S), delta=f(H, S),
+                      dsw=e(S, F), dgu=e(S, 2 * F), dh2=e(S, D), dx2=e(S, D), da=e(S, H * d), dqkv=e(S, QKV),
+                      dh1=e(S, D), gA=e(S, D), gB=e(S, D))
+        # column blocks of the stacked outputs (and of their gradients)
+        cols = lambda t, a, b: t[:, a:b]
+        self.v_ = dict(q=cols(self.b["qkv"], 0, H * d), k=cols(self.b["qkv"], H * d, (H + Hkv) * d),
+                       v=cols(self.b["qkv"], (H + Hkv) * d, QKV), qk=cols(self.b["qkv"], 0, (H + Hkv) * d),
+                       dq=cols(self.b["dqkv"], 0, H * d), dk=cols(self.b["dqkv"], H * d, (H + Hkv) * d),
+                       dv=cols(self.b["dqkv"], (H + Hkv) * d, QKV), dqk=cols(self.b["dqkv"], 0, (H + Hkv) * d),
+                       g=cols(self.b["gu"], 0, F), u=cols(self.b["gu"], F, 2 * F),
+                       dg=cols(self.b["dgu"], 0, F), du=cols(self.b["dgu"], F, 2 * F))
+        ranks = {st: c.lora_rank * sum(n in c.lora_targets for n in mem) for st, mem in STACKS.items()}
+        self.T = {st: f(S, R) for st, R in ranks.items() if R}
+        self.U = {st: f(S, R) for st, R in ranks.items() if R}
+        self.gws = {st: torch.empty(nl.lora_grad_workspace_bytes(S, self._stack_shape(st)[1], self._stack_shape(st)[0],
+                                                                 R), dtype=torch.uint8, device=self.dev)
+                    for st, R in ranks.items() if R}
+        shapes = [(self._stack_shape(st)[1], self._stack_shape(st)[0], ranks[st]) for st in STACKS]
         if self.with_head:
-            shapes.append((c.hidden, c.vocab))
-        need = max(nl.linear_workspace_bytes(S, k, n, r, backward=bwd) for k, n in shapes for bwd in (False, True))
+            shapes.append((c.hidden, c.vocab, 0))
+        need = max(nl.linear_workspace_bytes(S, k, n, r, backward=bwd) for k, n, r in shapes for bwd in (False, True))
         self.lws = torch.empty(need, dtype=torch.uint8, device=self.dev) if need else None
         self.cur_x = None
         if self.with_head:
@@ -150,19 +205,19 @@ class LlamaNF4:
                            dhf=e(S, D), loss=f(1), tok_loss=f(S))
 
     # ---------------------------------------------------------------- one layer
-    def _lin(self, L: Layer, name: str, inp, out):
-        ad = L.lora.get(name)
+    def _lin(self, L: Layer, st: str, inp, out):
+        ad = L.stack_lora.get(st)
         if ad is None:
-            nl.linear_fwd(inp, L.W[name], y=out, workspace=self.lws)
+            nl.linear_fwd(inp, L.W[st], y=out, workspace=self.lws)
         else:
-            nl.linear_fwd(inp, L.W[name], ad["A"], ad["B"], self.s, y=out, t_out=self.T[name], workspace=self.lws)
+            nl.linear_fwd(inp, L.W[st], ad["A"], ad["B"], self.s, y=out, t_out=self.T[st], workspace=self.lws)
 
-    def _lin_bwd(self, L: Layer, name: str, dy, out):
-        ad = L.lora.get(name)
+    def _lin_bwd(self, L: Layer, st: str, dy, out):
+        ad = L.stack_lora.get(st)
         if ad is None:
-            nl.linear_bwd_input(dy, L.W[name], dx=out, workspace=self.lws)
+            nl.linear_bwd_input(dy, L.W[st], dx=out, workspace=self.lws)
         else:
-            nl.linear_bwd_input(dy, L.W[name], ad["A"], ad["B"], self.s, dx=out, u_out=self.U[name],
+            nl.linear_bwd_input(dy, L.W[st], ad["A"], ad["B"], self.s, dx=out, u_out=self.U[st],
                                 workspace=self.lws)
 
     def layer_forward(self, L: Layer, xin, res=None, x_out=None):
@@ -170,7 +225,7 @@ class LlamaNF4:
         res is None. Returns (x2, dn): the layer output is x2 + dn, which the
         next layer's fused add + RMSNorm forms. Everything the backward needs
         stays in the shared buffers until the next call."""
-        c, b = self.cfg, self.b
+        c, b, v = self.cfg, self.b, self.v_
         if res is None:
             x = xin
             nl.add_rmsnorm(x, L.gamma1, c.eps, y=b["h1"], rstd=b["r1"])
@@ -178,17 +233,13 @@ class LlamaNF4:
             x = b["x"] if x_out is None else x_out
             nl.add_rmsnorm(xin, L.gamma1, c.eps, res=res, sum_out=x, y=b["h1"], rstd=b["r1"])
         self.cur_x = x
-        self._lin(L, "q_proj", b["h1"], b["q"])
-        self._lin(L, "k_proj", b["h1"], b["k"])
-        self._lin(L, "v_proj", b["h1"], b["v"])
-        nl.rope_(b["q"], c.heads, c.head_dim, c.theta)
-        nl.rope_(b["k"], c.kv_heads, c.head_dim, c.theta)
-        nl.attention_fwd(b["q"], b["k"], b["v"], c.heads, c.kv_heads, c.head_dim, o=b["a"], lse=b["lse"])
+        self._lin(L, "qkv", b["h1"], b["qkv"])
+        nl.rope_(v["qk"], c.heads + c.kv_heads, c.head_dim, c.theta)  # the q and k heads in one call
+        nl.attention_fwd(v["q"], v["k"], v["v"], c.heads, c.kv_heads, c.head_dim, o=b["a"], lse=b["lse"])
         self._lin(L, "o_proj", b["a"], b["o"])
         nl.add_rmsnorm(x, L.gamma2, c.eps, res=b["o"], sum_out=b["x2"], y=b["h2"], rstd=b["r2"])
-        self._lin(L, "gate_proj", b["h2"], b["g"])
-        self._lin(L, "up_proj", b["h2"], b["u"])
-        nl.swiglu(b["g"], b["u"], a=b["sw"])
+        self._lin(L, "gate_up", b["h2"], b["gu"])
+        nl.swiglu(v["g"], v["u"], a=b["sw"])
         self._lin(L, "down_proj", b["sw"], b["dn"])
         return b["x2"], b["dn"]
 
@@ -196,30 +247,24 @@ class LlamaNF4:
         """Backward of the layer whose forward ran last: dout is the gradient
         of its output x2 + dn. Writes the gradient of its input x into dx_out
         (which must not alias dout) and every adapter's dA, dB."""
-        c, b = self.cfg, self.b
+        c, b, v = self.cfg, self.b, self.v_
         self._lin_bwd(L, "down_proj", dout, b["dsw"])
-        nl.swiglu_bwd(b["dsw"], b["g"], b["u"], dg=b["dg"], du=b["du"])
-        self._lin_bwd(L, "gate_proj", b["dg"], b["dh2a"])
-        self._lin_bwd(L, "up_proj", b["du"], b["dh2b"])
-        nl.add(b["dh2a"], b["dh2b"], out=b["dh2a"])
-        nl.rmsnorm_bwd(b["dh2a"], b["x2"], b["r2"], L.gamma2, dres=dout, dx=b["dx2"])
+        nl.swiglu_bwd(b["dsw"], v["g"], v["u"], dg=v["dg"], du=v["du"])
+        self._lin_bwd(L, "gate_up", b["dgu"], b["dh2"])  # gate's and up's input gradients, summed
+        nl.rmsnorm_bwd(b["dh2"], b["x2"], b["r2"], L.gamma2, dres=dout, dx=b["dx2"])
         self._lin_bwd(L, "o_proj", b["dx2"], b["da"])
-        nl.attention_bwd(b["da"], b["q"], b["k"], b["v"], b["a"], b["lse"], c.heads, c.kv_heads, c.head_dim,
-                         dq=b["dq"], dk=b["dk"], dv=b["dv"], delta=b["delta"])
-        nl.rope_(b["dq"], c.heads, c.head_dim, c.theta, inverse=True)
-        nl.rope_(b["dk"], c.kv_heads, c.head_dim, c.theta, inverse=True)
-        self._lin_bwd(L, "q_proj", b["dq"], b["dh1q"])
-        self._lin_bwd(L, "k_proj", b["dk"], b["dh1k"])
-        self._lin_bwd(L, "v_proj", b["dv"], b["dh1v"])
-        nl.add(b["dh1q"], b["dh1k"], b["dh1v"], out=b["dh1q"])
-        nl.rmsnorm_bwd(b["dh1q"], self.cur_x, b["r1"], L.gamma1, dres=b["dx2"], dx=dx_out)
-        ins = {"q_proj": (b["h1"], b["dq"]), "k_proj": (b["h1"], b["dk"]), "v_proj": (b["h1"], b["dv"]),
-               "o_proj": (b["a"], b["dx2"]), "gate_proj": (b["h2"], b["dg"]), "up_proj": (b["h2"], b["du"]),
+        nl.attention_bwd(b["da"], v["q"], v["k"], v["v"], b["a"], b["lse"], c.heads, c.kv_heads, c.head_dim,
+                         dq=v["dq"], dk=v["dk"], dv=v["dv"], delta=b["delta"])
+        nl.rope_(v["dqk"], c.heads + c.kv_heads, c.head_dim, c.theta, inverse=True)
+        self._lin_bwd(L, "qkv", b["dqkv"], b["dh1"])  # q's, k's and v's input gradients, summed
+        nl.rmsnorm_bwd(b["dh1"], self.cur_x, b["r1"], L.gamma1, dres=b["dx2"], dx=dx_out)
+        ins = {"qkv": (b["h1"], b["dqkv"]), "o_proj": (b["a"], b["dx2"]), "gate_up": (b["h2"], b["dgu"]),
                "down_proj": (b["sw"], dout)}
-        for name, ad in L.lora.items():
-            xi, dyi = ins[name]
-            nl.lora_grad(xi, dyi, self.T[name], self.U[name], self.s, dA=ad["dA"], dB=ad["dB"],
-                         workspace=self.gws[name])
+        for st, ad in L.stack_lora.items():
+            xi, dyi = ins[st]
+            nl.lora_grad(xi, dyi, self.T[st], self.U[st], self.s, dA=ad["dA"], dB=ad["dB"], workspace=self.gws[st])
+            if ad["mask"] is not None:
+                ad["dB"].mul_(ad["mask"])  # only the members' own blocks of B are parameters
         return dx_out
 
     # ---------------------------------------------------------------- the step
@@ -247,7 +292,8 @@ class LlamaNF4:
         return hb["loss"]
 
     def adapters(self) -> List[dict]:
-        return [ad for L in self.layers for ad in L.lora.values()]
+        return [dict((k, ad[k]) for k in ("A", "dA", "mA", "vA", "B", "dB", "mB", "vB"))
+                for L in self.layers for ad in L.stack_lora.values()]
 
     def optimizer_step(self, lr: float = 2e-4, weight_decay: float = 0.0) -> None:
         self.step_count += 1

@@ -113,11 +113,11 @@ def load() -> ctypes.CDLL:
             C = ctypes.c_int
             lib.nf4_add_rmsnorm.argtypes = [P, P, C, I64, I64, P, F, P, P, P, P]
             lib.nf4_rmsnorm_bwd.argtypes = [P, P, P, C, I64, I64, P, P, P, P]
-            lib.nf4_rope.argtypes = [P, C, I64, I32, I32, ctypes.c_double, C, P]
-            lib.nf4_attention_fwd.argtypes = [P, P, P, C, I64, I32, I32, I32, P, P, P]
-            lib.nf4_attention_bwd.argtypes = [P, P, P, P, P, P, C, I64, I32, I32, I32, P, P, P, P, P]
-            lib.nf4_swiglu.argtypes = [P, P, C, I64, P, P]
-            lib.nf4_swiglu_bwd.argtypes = [P, P, P, C, I64, P, P, P]
+            lib.nf4_rope.argtypes = [P, C, I64, I32, I32, I64, ctypes.c_double, C, P]
+            lib.nf4_attention_fwd.argtypes = [P, P, P, C, I64, I32, I32, I32, I64, P, P, P]
+            lib.nf4_attention_bwd.argtypes = [P, P, P, P, P, P, C, I64, I32, I32, I32, I64, P, P, P, P, P]
+            lib.nf4_swiglu.argtypes = [P, P, C, I64, I64, I64, P, P]
+            lib.nf4_swiglu_bwd.argtypes = [P, P, P, C, I64, I64, I64, P, P, P]
             lib.nf4_cross_entropy.argtypes = [P, C, I64, I64, P, P, P, P, P, P]
             lib.nf4_add.argtypes = [P, P, P, C, I64, P, P]
             lib.nf4_status_string.restype = ctypes.c_char_p
@@ -692,51 +692,115 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, gamma: to
     return dx
 
 
+def _rows(t: torch.Tensor, name: str, width: int) -> int:
+    """Row stride (elements) of a 2-D activation whose rows hold `width`
+    contiguous entries: a dense array or a column block of a wider one."""
+    if t.dim() != 2 or t.shape[1] != width or (t.shape[0] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be [rows, {width}] with contiguous rows")
+    return int(t.stride(0)) if t.shape[0] > 1 else width
+
+
+def _dev_rows(t: torch.Tensor, name: str, dtype=None) -> None:
+    """Device, dtype and alignment checks of a possibly strided activation."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
 def rope_(x: torch.Tensor, heads: int, d: int, theta: float, inverse: bool = False) -> torch.Tensor:
-    """Rotary embedding of x [S, heads*d] in place."""
-    _dev(x, "x")
-    _check("nf4_rope", load().nf4_rope(_ptr(x), _DT[x.dtype], x.shape[0], int(heads), int(d), float(theta),
+    """Rotary embedding of x [S, heads*d] in place (x may be a column block of a
+    wider array: its row stride is passed on)."""
+    _dev_rows(x, "x")
+    ld = _rows(x, "x", int(heads) * int(d))
+    _check("nf4_rope", load().nf4_rope(_ptr(x), _DT[x.dtype], x.shape[0], int(heads), int(d), ld, float(theta),
                                        int(bool(inverse)), _stream(x.device)))
     return x
 
 
+def _qkv_stride(q, k, v, hq: int, hkv: int, d: int) -> int:
+    """Common row stride of q, k, v (0 when all three are dense)."""
+    lq, lk, lv = _rows(q, "q", hq * d), _rows(k, "k", hkv * d), _rows(v, "v", hkv * d)
+    if lq == hq * d and lk == hkv * d and lv == hkv * d:
+        return 0
+    if not (lq == lk == lv):
+        raise ValueError("q, k and v must be dense or share one row stride")
+    return lq
+
+
 def attention_fwd(q, k, v, hq: int, hkv: int, d: int, o=None, lse=None):
+    """Causal GQA attention; q, k, v may be column blocks of one wider array."""
     for n, t in (("q", q), ("k", k), ("v", v)):
-        _dev(t, n, q.dtype)
+        _dev_rows(t, n, q.dtype)
+    ld = _qkv_stride(q, k, v, hq, hkv, d)
     S = q.shape[0]
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty((S, hq * d), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((hq, S), dtype=torch.float32, device=q.device)
-    _check("nf4_attention_fwd", load().nf4_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], S, hq, hkv, d,
+    _check("nf4_attention_fwd", load().nf4_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], S, hq, hkv, d, ld,
                                                          _ptr(o), _ptr(lse), _stream(q.device)))
     return o, lse
 
 
 def attention_bwd(dout, q, k, v, o, lse, hq: int, hkv: int, d: int, dq=None, dk=None, dv=None, delta=None):
+    """Input gradients of attention_fwd. q, k, v and dq, dk, dv may be column
+    blocks of wider arrays, all with one row stride."""
     S = q.shape[0]
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    ld = _qkv_stride(q, k, v, hq, hkv, d)
+    if ld and (dq is None or dk is None or dv is None):
+        raise ValueError("with strided q, k, v pass dq, dk, dv of the same row stride")
+    dq = torch.empty((S, hq * d), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((S, hkv * d), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((S, hkv * d), dtype=q.dtype, device=q.device) if dv is None else dv
+    if _qkv_stride(dq, dk, dv, hq, hkv, d) != ld:
+        raise ValueError("dq, dk, dv must have the row stride of q, k, v")
     if delta is None:
         delta = torch.empty((hq, S), dtype=torch.float32, device=q.device)
     _check("nf4_attention_bwd", load().nf4_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                                         _DT[q.dtype], S, hq, hkv, d, _ptr(delta), _ptr(dq), _ptr(dk),
-                                                         _ptr(dv), _stream(q.device)))
+                                                         _DT[q.dtype], S, hq, hkv, d, ld, _ptr(delta), _ptr(dq),
+                                                         _ptr(dk), _ptr(dv), _stream(q.device)))
     return dq, dk, dv
 
 
+def _gu_stride(g, u) -> Tuple[int, int, int]:
+    """(rows, width, row stride) of the SwiGLU inputs, which share one stride."""
+    if g.dim() != 2 or u.shape != g.shape:
+        raise ValueError("g and u must be [rows, width] of one shape")
+    rows, width = g.shape
+    lg, lu = _rows(g, "g", width), _rows(u, "u", width)
+    if lg != lu:
+        raise ValueError("g and u must share one row stride")
+    return rows, width, lg
+
+
 def swiglu(g, u, a=None):
-    a = torch.empty_like(g) if a is None else a
-    _check("nf4_swiglu", load().nf4_swiglu(_ptr(g), _ptr(u), _DT[g.dtype], g.numel(), _ptr(a), _stream(g.device)))
+    """a = silu(g) * u for [rows, width] g, u (which may be column blocks of one
+    wider array); a is dense."""
+    rows, width, ld = _gu_stride(g, u)
+    a = torch.empty((rows, width), dtype=g.dtype, device=g.device) if a is None else a
+    if not a.is_contiguous() or a.shape != g.shape:
+        raise ValueError("a must be a dense [rows, width] array")
+    _check("nf4_swiglu", load().nf4_swiglu(_ptr(g), _ptr(u), _DT[g.dtype], rows, width, ld, _ptr(a),
+                                           _stream(g.device)))
     return a
 
 
 def swiglu_bwd(da, g, u, dg=None, du=None):
-    dg = torch.empty_like(g) if dg is None else dg
-    du = torch.empty_like(u) if du is None else du
-    _check("nf4_swiglu_bwd", load().nf4_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), _DT[g.dtype], g.numel(), _ptr(dg),
-                                                   _ptr(du), _stream(g.device)))
+    """Input gradients of swiglu; dg, du take the row stride of g, u (given
+    together, as column blocks with that stride, or allocated dense when g, u
+    are dense)."""
+    rows, width, ld = _gu_stride(g, u)
+    if dg is None and du is None:
+        if ld != width:
+            raise ValueError("dg and du must be given when g and u are strided")
+        dg, du = torch.empty_like(g), torch.empty_like(u)
+    if _gu_stride(dg, du)[2] != ld:
+        raise ValueError("dg, du must have the row stride of g, u")
+    if not da.is_contiguous() or da.shape != g.shape:
+        raise ValueError("da must be a dense [rows, width] array")
+    _check("nf4_swiglu_bwd", load().nf4_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), _DT[g.dtype], rows, width, ld,
+                                                   _ptr(dg), _ptr(du), _stream(g.device)))
     return dg, du
 
 

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 5
+    assert lib[0].nf4lora_abi_version() == 6
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -164,19 +164,26 @@ def test_optional_side_products_and_recompute(lib):
 
 
 def test_wide_rank_side_product_workspace(lib):
-    """Ranks beyond 32 split the side product's reduction (over K forward, N
-    backward) into parts of at least 128 indices, about 512 workgroups of 128
+    """The side product's reduction (over K forward, N backward) is split for
+    ranks beyond 32, and for ranks up to 32 when fewer than 4096 token rows
+    meet a reduction of at least 2048 (16-row workgroups would leave most of
+    the chip idle): parts of at least 128 indices, about 512 workgroups of 128
     rows x 64 ranks in all; the workspace holds one M x r fp32 partial product
     per part, and lora_grad's recomputation takes the larger of its two."""
     L, _ = lib
     def parts(M, I, r):
+        if not (r > 32 or (-(-M // 16) < 256 and I >= 2048)):
+            return 1
         tiles = -(-M // 128) * -(-r // 64)
         steps = -(-I // 32)
         ks = min(-(-512 // tiles), max(steps // 4, 1))
         kc = -(-steps // ks) * 32
         return -(-I // kc)
     rnd = lambda b: (b + 255) // 256 * 256
-    for M, K, N, r in ((8192, 14336, 4096, 64), (4096, 4096, 4096, 100), (512, 4096, 14336, 256), (64, 576, 192, 33)):
+    cases = ((8192, 14336, 4096, 64), (4096, 4096, 4096, 100), (512, 4096, 14336, 256), (64, 576, 192, 33),
+             (512, 4096, 1024, 16), (512, 14336, 4096, 8), (4080, 4096, 4096, 32), (512, 576, 1536, 8),
+             (4096, 4096, 4096, 16))
+    for M, K, N, r in cases:
         for bwd in (0, 1):
             I = N if bwd else K
             ks = parts(M, I, r)
@@ -188,7 +195,9 @@ def test_wide_rank_side_product_workspace(lib):
         base = L.lora_grad_workspace_bytes(M, K, N, r, 0, 0)
         assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 3) == base + 2 * side + max(pt, pu)
         assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 1) == base + side + pt
-    # 32 and below: no split
+    # the split engages where the model says it does
+    assert parts(512, 4096, 16) > 1 and parts(512, 1024, 16) == 1 and parts(4096, 4096, 16) == 1
+    # 32 and below at 4096 or more tokens: no split
     assert L.nf4_linear_workspace_bytes(8192, 14336, 4096, 32, 1) == L.nf4_linear_workspace_bytes(8192, 14336, 4096, 0, 1)
 
 
@@ -420,24 +429,37 @@ def test_decoder_op_argument_errors(lib):
     assert L.nf4_rmsnorm_bwd(256, 256, 256, 1, 4, 64, None, None, 256, None) == EINVAL
     assert L.nf4_rmsnorm_bwd(256, 256, 256, 1, 4, 64, 256, 264, 256, None) == EALIGN
     # rotary embedding
-    assert L.nf4_rope(256, 1, 8, 2, 3, ctypes.c_double(1e4), 0, None) == EINVAL  # odd head dim
-    assert L.nf4_rope(256, 1, 8, 2, 64, ctypes.c_double(1.0), 0, None) == EINVAL
-    assert L.nf4_rope(256, 1, 8, 2, 64, ctypes.c_double(1e4), 2, None) == EINVAL
-    assert L.nf4_rope(260, 1, 8, 2, 64, ctypes.c_double(1e4), 0, None) == EALIGN
+    assert L.nf4_rope(256, 1, 8, 2, 3, 0, ctypes.c_double(1e4), 0, None) == EINVAL  # odd head dim
+    assert L.nf4_rope(256, 1, 8, 2, 64, 0, ctypes.c_double(1.0), 0, None) == EINVAL
+    assert L.nf4_rope(256, 1, 8, 2, 64, 0, ctypes.c_double(1e4), 2, None) == EINVAL
+    assert L.nf4_rope(260, 1, 8, 2, 64, 0, ctypes.c_double(1e4), 0, None) == EALIGN
+    # row strides: at least the row width, whole 16-byte units
+    assert L.nf4_rope(256, 1, 8, 2, 64, 120, ctypes.c_double(1e4), 0, None) == EINVAL  # below 2 * 64
+    assert L.nf4_rope(256, 1, 8, 2, 64, 132, ctypes.c_double(1e4), 0, None) == EALIGN  # 264 bytes
+    assert L.nf4_rope(256, 0, 8, 2, 64, 130, ctypes.c_double(1e4), 0, None) == EALIGN  # fp32: 520 bytes
+    assert L.nf4_rope(256, 0, 8, 2, 64, 126, ctypes.c_double(1e4), 0, None) == EINVAL
     # attention: head dim a multiple of 16 up to 128, whole groups of query heads
-    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 72, 256, 256, None) == EINVAL
-    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 144, 256, 256, None) == EINVAL
-    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 3, 64, 256, 256, None) == EINVAL
-    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 64, 256, None, None) == EINVAL
-    assert L.nf4_attention_fwd(256, 264, 256, 1, 8, 4, 2, 64, 256, 256, None) == EALIGN
-    assert L.nf4_attention_bwd(256, 256, 256, 256, 256, 256, 1, 8, 4, 2, 64, None, 256, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 72, 0, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 144, 0, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 3, 64, 0, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 64, 0, 256, None, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 264, 256, 1, 8, 4, 2, 64, 0, 256, 256, None) == EALIGN
+    # a shared q/k/v row stride must hold the 4 query heads' 256 entries
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 64, 200, 256, 256, None) == EINVAL
+    assert L.nf4_attention_fwd(256, 256, 256, 1, 8, 4, 2, 64, 260, 256, 256, None) == EALIGN
+    assert L.nf4_attention_bwd(256, 256, 256, 256, 256, 256, 1, 8, 4, 2, 64, 0, None, 256, 256, 256, None) == EINVAL
+    assert L.nf4_attention_bwd(256, 256, 256, 256, 256, 256, 1, 8, 4, 2, 64, 136, 256, 256, 256, 256,
+                               None) == EINVAL
     # elementwise
     assert L.nf4_add(256, 256, None, 9, 10, 256, None) == EUNSUP
     assert L.nf4_add(256, None, None, 1, 10, 256, None) == EINVAL
     assert L.nf4_add(256, 256, None, 1, 0, 256, None) == EINVAL
     assert L.nf4_add(256, 256, 258, 1, 10, 256, None) == EALIGN
-    assert L.nf4_swiglu(256, 256, 1, 0, 256, None) == EINVAL
-    assert L.nf4_swiglu_bwd(256, 256, 256, 1, 10, 256, 264, None) == EALIGN
+    assert L.nf4_swiglu(256, 256, 1, 0, 8, 0, 256, None) == EINVAL
+    assert L.nf4_swiglu(256, 256, 1, 4, 0, 0, 256, None) == EINVAL
+    assert L.nf4_swiglu(256, 256, 1, 4, 16, 12, 256, None) == EINVAL  # stride below the width
+    assert L.nf4_swiglu(256, 256, 1, 4, 16, 20, 256, None) == EALIGN  # 40-byte rows
+    assert L.nf4_swiglu_bwd(256, 256, 256, 1, 2, 5, 0, 256, 264, None) == EALIGN
     # cross-entropy
     assert L.nf4_cross_entropy(256, 1, 4, 0, 256, 256, 256, None, None, None) == EINVAL
     assert L.nf4_cross_entropy(256, 1, 4, 10, None, 256, 256, None, None, None) == EINVAL

@@ -101,6 +101,56 @@ def test_swiglu(gpu, dt):
     assert_close(to_np(du), du_ref, dt, "du")
 
 
+@pytest.mark.parametrize("S,hq,hkv,d", [(512, 32, 8, 128), (100, 8, 2, 64), (37, 4, 2, 16)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_strided_qkv_matches_dense(gpu, S, hq, hkv, d, dt):
+    """q, k, v as column blocks of one [S, (hq + 2 hkv) d] projection output
+    (rows one stride apart): rope on the q and k blocks together, attention
+    forward and backward with dq, dk, dv written into the same blocks of a
+    second such array; every result equals the dense calls' bit for bit (the
+    stride only moves the addresses)."""
+    print(f"[strided] S={S} hq={hq} hkv={hkv} d={d} {dt}", flush=True)
+    w = (hq + 2 * hkv) * d
+    qkv = rnd((S, w), 1.0, 31, dt)
+    do = rnd((S, hq * d), 1.0, 32, dt)
+    q, k, v = qkv[:, :hq * d], qkv[:, hq * d:(hq + hkv) * d], qkv[:, (hq + hkv) * d:]
+    dense = [t.contiguous() for t in (q, k, v)]
+    gpu.rope_(qkv[:, :(hq + hkv) * d], hq + hkv, d, 500000.0)  # q and k heads in one call
+    gpu.rope_(dense[0], hq, d, 500000.0)
+    gpu.rope_(dense[1], hkv, d, 500000.0)
+    o, lse = gpu.attention_fwd(q, k, v, hq, hkv, d)
+    o_d, lse_d = gpu.attention_fwd(*dense, hq, hkv, d)
+    g = torch.full((S, w), 7.0, dtype=DT[dt], device="cuda")
+    gq, gk, gv = g[:, :hq * d], g[:, hq * d:(hq + hkv) * d], g[:, (hq + hkv) * d:]
+    gpu.attention_bwd(do, q, k, v, o, lse, hq, hkv, d, dq=gq, dk=gk, dv=gv)
+    dq_d, dk_d, dv_d = gpu.attention_bwd(do, *dense, o_d, lse_d, hq, hkv, d)
+    torch.cuda.synchronize()
+    for a, b, what in ((q, dense[0], "rope q"), (k, dense[1], "rope k"), (o, o_d, "o"), (lse, lse_d, "lse"),
+                       (gq, dq_d, "dq"), (gk, dk_d, "dk"), (gv, dv_d, "dv")):
+        assert torch.equal(a.contiguous(), b), what
+
+
+@pytest.mark.parametrize("rows,width", [(512, 14336), (37, 100)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_strided_swiglu_matches_dense(gpu, rows, width, dt):
+    """g and u as the two column blocks of one [rows, 2 width] array (the
+    fused gate/up projection output), dg and du written into the blocks of
+    another: equal to the dense calls bit for bit, and a dense."""
+    if (width * (2 if dt == "bf16" else 4)) % 16:
+        width += 8 - width % 8  # keep the second block 16-byte aligned
+    gu = rnd((rows, 2 * width), 2.0, 41, dt)
+    da = rnd((rows, width), 1.0, 42, dt)
+    g, u = gu[:, :width], gu[:, width:]
+    a = gpu.swiglu(g, u)
+    a_d = gpu.swiglu(g.contiguous(), u.contiguous())
+    dgu = torch.full((rows, 2 * width), 3.0, dtype=DT[dt], device="cuda")
+    gpu.swiglu_bwd(da, g, u, dg=dgu[:, :width], du=dgu[:, width:])
+    dg_d, du_d = gpu.swiglu_bwd(da, g.contiguous(), u.contiguous())
+    torch.cuda.synchronize()
+    assert a.is_contiguous() and torch.equal(a, a_d)
+    assert torch.equal(dgu[:, :width].contiguous(), dg_d) and torch.equal(dgu[:, width:].contiguous(), du_d)
+
+
 @pytest.mark.parametrize("T,V,dt", [(512, 128256, "bf16"), (7, 1000, "f32"), (1, 3, "bf16"), (9, 1000, "bf16")])
 def test_cross_entropy(gpu, T, V, dt):
     z = rnd((T, V), 2.0, 31, dt)

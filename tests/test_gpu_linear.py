@@ -55,6 +55,9 @@ CASES = [
     (64, 1536, 576, 8),
     (200, 576, 1536, 16),
     (33, 129, 65, 5),
+    # 512 tokens through 2048-wide reductions: the side products take the split
+    # skinny GEMM at rank 16 in both directions
+    (512, 2048, 2048, 16),
 ]
 
 
@@ -193,6 +196,9 @@ RAGGED_LARGE = [
     (4096, 64, 4096),
     (4096, 4096, 576),
     (4096, 4096, 64),
+    # 8196 output columns (not a multiple of 8): the forward's 8-byte output
+    # stores instead of the staged 16-byte ones
+    (1024, 1024, 8196),
 ]
 
 

@@ -57,7 +57,19 @@ def decoded(orc, w, bf16):
 
 
 def oracle_params(orc, host, targets, bf16):
-    p = {"W_" + n: decoded(orc, w, bf16) for n, w in host["W"].items()}
+    """The oracle layer's parameters: every projection's decoded weight, taken
+    from the matrix it is stored in (the model packs q/k/v and gate/up as one
+    NF4 matrix each, so the oracle quantizes the same stacks and slices them)."""
+    from qlora_adapter_amd import llama
+    p = {}
+    for mem in llama.STACKS.values():
+        w = np.concatenate([host["W"][n] for n in mem])
+        dw = decoded(orc, w, bf16)
+        off = 0
+        for n in mem:
+            rows = host["W"][n].shape[0]
+            p["W_" + n] = dw[off:off + rows]
+            off += rows
     p["gamma1"], p["gamma2"] = host["g1"], host["g2"]
     for n in targets:
         p["A_" + n], p["B_" + n] = host["A"][n], host["B"][n]
@@ -147,7 +159,7 @@ def test_recompute_is_bitwise(gpu):
     first = {k: v.clone() for k, v in m.b.items()}
     m.layer_forward(L, x)
     torch.cuda.synchronize()
-    for k in ("h1", "q", "k", "v", "a", "lse", "o", "x2", "h2", "g", "u", "sw", "dn"):
+    for k in ("h1", "qkv", "a", "lse", "o", "x2", "h2", "gu", "sw", "dn"):
         assert torch.equal(first[k], m.b[k]), k
 
 
@@ -196,7 +208,9 @@ def test_training_step(gpu, orc):
     B0 = [ad["B"].clone() for ad in m.adapters()]
     loss = m.forward_backward(ids, tgt)
     torch.cuda.synchronize()
-    grads = [(ad["dA"].cpu().numpy(), ad["dB"].cpu().numpy()) for ad in m.adapters()]
+    # per projection: its views inside the layer's stacked adapter
+    grads = [[(L.lora[n]["dA"].cpu().numpy(), L.lora[n]["dB"].cpu().numpy()) for n in cfg.lora_targets]
+             for L in layers]
 
     ocfg = oracle_cfg(cfg, m.s)
     ps = [oracle_params(orc, h, cfg.lora_targets, True) for h in hosts]
@@ -210,13 +224,11 @@ def test_training_step(gpu, orc):
     # through two layers of bf16 storage the adapter gradients carry about 1%
     # rounding noise on both sides (check_bf16_chain)
     got, r16, r64 = {}, {}, {}
-    k = 0
     for i in range(len(ps)):
-        for n in cfg.lora_targets:
+        for t, n in enumerate(cfg.lora_targets):
             for j, name in ((0, "dA"), (1, "dB")):
                 key = f"layer {i} {n} {name}"
-                got[key], r16[key], r64[key] = grads[k][j], g16[i][n][j], g64[i][n][j]
-            k += 1
+                got[key], r16[key], r64[key] = grads[i][t][j], g16[i][n][j], g64[i][n][j]
     check_bf16_chain(got, r16, r64)
     m.optimizer_step(lr=1e-3)
     torch.cuda.synchronize()
