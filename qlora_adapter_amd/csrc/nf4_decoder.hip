@@ -485,29 +485,55 @@ __global__ __launch_bounds__(256) void k_add3(const T* a, const T* b, const T* c
 // ---------------------------------------------------------------- SwiGLU
 
 // Rows of `width` entries; g, u (and dg, du) are rows ld apart, a and da dense.
-// Workgroup (x, y): columns 256 x .. + 255 of rows y, y + gridDim.y, ...
-template <typename T>
+// Thread t of workgroup (x, y) takes entries V (256 x + t) .. + V - 1 of rows
+// y, y + gridDim.y, ...: V = 16 / sizeof(T) (one 16-byte access per array)
+// when width, ld and the pointers allow it, else 1. The arithmetic per entry
+// is the same either way.
+template <typename T, int V>
+struct Vec {
+  T v[V];
+};
+
+template <typename T, int V>
+__device__ __forceinline__ Vec<T, V> ldv(const T* p) {
+  return *reinterpret_cast<const Vec<T, V>*>(p);
+}
+
+template <typename T, int V>
 __global__ __launch_bounds__(256) void k_swiglu(const T* __restrict__ g, const T* __restrict__ u, int64_t rows,
                                                 int64_t width, int64_t ld, T* __restrict__ a) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (j >= width) return;
   for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
-    const float z = ldf(g, m * ld + j);
-    stf(a, m * width + j, z / (1.0f + expf(-z)) * ldf(u, m * ld + j));
+    const Vec<T, V> gv = ldv<T, V>(g + m * ld + j), uv = ldv<T, V>(u + m * ld + j);
+    Vec<T, V> av;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float z = (float)gv.v[e];
+      av.v[e] = (T)(z / (1.0f + expf(-z)) * (float)uv.v[e]);
+    }
+    *reinterpret_cast<Vec<T, V>*>(a + m * width + j) = av;
   }
 }
 
-template <typename T>
+template <typename T, int V>
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const T* __restrict__ da, const T* __restrict__ g,
                                                     const T* __restrict__ u, int64_t rows, int64_t width, int64_t ld,
                                                     T* __restrict__ dg, T* __restrict__ du) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (j >= width) return;
   for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
-    const int64_t e = m * ld + j;
-    const float z = ldf(g, e), s = 1.0f / (1.0f + expf(-z)), dav = ldf(da, m * width + j);
-    stf(dg, e, dav * ldf(u, e) * s * (1.0f + z * (1.0f - s)));
-    stf(du, e, dav * z * s);
+    const int64_t e0 = m * ld + j;
+    const Vec<T, V> gv = ldv<T, V>(g + e0), uv = ldv<T, V>(u + e0), dav = ldv<T, V>(da + m * width + j);
+    Vec<T, V> dgv, duv;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float z = (float)gv.v[e], s = 1.0f / (1.0f + expf(-z)), d = (float)dav.v[e];
+      dgv.v[e] = (T)(d * (float)uv.v[e] * s * (1.0f + z * (1.0f - s)));
+      duv.v[e] = (T)(d * z * s);
+    }
+    *reinterpret_cast<Vec<T, V>*>(dg + e0) = dgv;
+    *reinterpret_cast<Vec<T, V>*>(du + e0) = duv;
   }
 }
 
@@ -711,25 +737,49 @@ int launch_add3(const void* a, const void* b, const void* c, nf4_dtype dt, int64
   return launch_status();
 }
 
-// Grid of the row-wise SwiGLU kernels: column blocks of 256 times up to 65535
-// row groups (rows beyond loop).
-dim3 swiglu_grid(int64_t rows, int64_t width) {
-  return dim3((unsigned)ceil_div(width, 256), (unsigned)(rows < 65535 ? rows : 65535));
+// Grid of the row-wise SwiGLU kernels for V entries per thread: column blocks
+// of 256 V times up to 65535 row groups (rows beyond loop).
+dim3 swiglu_grid(int64_t rows, int64_t width, int v) {
+  return dim3((unsigned)ceil_div(width, 256 * (int64_t)v), (unsigned)(rows < 65535 ? rows : 65535));
+}
+
+// 16-byte vectors apply when every row start of every array is 16-byte aligned.
+template <typename T>
+bool swiglu_vec(int64_t width, int64_t ld, std::initializer_list<const void*> ptrs) {
+  constexpr int V = 16 / sizeof(T);
+  if (width % V != 0 || ld % V != 0) return false;
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return false;
+  return true;
 }
 
 int launch_swiglu(const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width, int64_t ld, void* a,
                   hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu<T>, swiglu_grid(rows, width), dim3(256), 0, st,
-                                      static_cast<const T*>(g), static_cast<const T*>(u), rows, width, ld,
-                                      static_cast<T*>(a)));
+  NF4_DISPATCH(dt, {
+    constexpr int V = 16 / sizeof(T);
+    if (swiglu_vec<T>(width, ld, {g, u, a}))
+      hipLaunchKernelGGL((k_swiglu<T, V>), swiglu_grid(rows, width, V), dim3(256), 0, st, static_cast<const T*>(g),
+                         static_cast<const T*>(u), rows, width, ld, static_cast<T*>(a));
+    else
+      hipLaunchKernelGGL((k_swiglu<T, 1>), swiglu_grid(rows, width, 1), dim3(256), 0, st, static_cast<const T*>(g),
+                         static_cast<const T*>(u), rows, width, ld, static_cast<T*>(a));
+  });
   return launch_status();
 }
 
 int launch_swiglu_bwd(const void* da, const void* g, const void* u, nf4_dtype dt, int64_t rows, int64_t width,
                       int64_t ld, void* dg, void* du, hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_swiglu_bwd<T>, swiglu_grid(rows, width), dim3(256), 0, st,
-                                      static_cast<const T*>(da), static_cast<const T*>(g), static_cast<const T*>(u),
-                                      rows, width, ld, static_cast<T*>(dg), static_cast<T*>(du)));
+  NF4_DISPATCH(dt, {
+    constexpr int V = 16 / sizeof(T);
+    if (swiglu_vec<T>(width, ld, {da, g, u, dg, du}))
+      hipLaunchKernelGGL((k_swiglu_bwd<T, V>), swiglu_grid(rows, width, V), dim3(256), 0, st,
+                         static_cast<const T*>(da), static_cast<const T*>(g), static_cast<const T*>(u), rows, width,
+                         ld, static_cast<T*>(dg), static_cast<T*>(du));
+    else
+      hipLaunchKernelGGL((k_swiglu_bwd<T, 1>), swiglu_grid(rows, width, 1), dim3(256), 0, st,
+                         static_cast<const T*>(da), static_cast<const T*>(g), static_cast<const T*>(u), rows, width,
+                         ld, static_cast<T*>(dg), static_cast<T*>(du));
+  });
   return launch_status();
 }
 

@@ -87,9 +87,9 @@ def test_attention_forward_backward(gpu, S, hq, hkv, d, dt):
         assert torch.equal(a, b), "attention backward not run-to-run identical"
 
 
+@pytest.mark.parametrize("n", [(512, 14336), (3, 100)])  # 16-byte vectors; 100 bf16 per row: one entry per lane
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_swiglu(gpu, dt):
-    n = (512, 14336)
+def test_swiglu(gpu, dt, n):
     g, u, da = rnd(n, 2.0, 21, dt), rnd(n, 1.0, 22, dt), rnd(n, 1.0, 23, dt)
     a = gpu.swiglu(g, u)
     dg, du = gpu.swiglu_bwd(da, g, u)
