@@ -58,6 +58,8 @@ def parse():
                    help="only the Llama-8B-shaped training step (--steps timed after --warmup), for profiling")
     p.add_argument("--throughput-only", action="store_true",
                    help="only the 7.5e9-parameter quantize/dequantize pass (one timed pass; for counter runs)")
+    p.add_argument("--gemm-sustained-only", action="store_true",
+                   help="only the back-to-back fused calls of gate_proj and down_proj (for profiling)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run device-to-device copies of a known size (counter calibration for rocprofv3)")
     return p.parse_args()
@@ -219,6 +221,51 @@ def gpu_time_ms(fn, dev, reps: int = 20, block: int = 1) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def gemm_sustained(nl, dev, reps: int = 100, warm: int = 100):
+    """The fused NF4 + LoRA calls of the two widest projections (gate_proj
+    4096 -> 14336 and down_proj 14336 -> 4096, 4096 tokens, r = 16, the layer
+    step's inputs), each direction called `warm` times and then `reps` times
+    back to back: the rate the GPU sustains on a stream of such calls once its
+    clock has settled (in the layer step the same calls alternate with the
+    memory-bound quantize and dequantize passes). Event-timed per direction."""
+    import torch
+    import workloads
+    wl = workloads.WORKLOADS["llama8b_layer"]
+    M, r = wl["tokens"], wl["layers"][0].lora_rank
+    s = nl.lora_scale(wl["alpha"], r)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for i, name in ((4, "gate_proj"), (6, "down_proj")):
+        L = wl["layers"][i]
+        inp = workloads.lora_inputs(L, M, seed_offset=i, device="cuda")
+        W = nl.quantize(workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(i), "cuda"), True)
+        y = torch.empty((M, L.n_out), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((M, L.k_in), dtype=torch.bfloat16, device=dev)
+        T = torch.empty((M, r), dtype=torch.float32, device=dev)
+        U = torch.empty((M, r), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(nl.linear_workspace_bytes(M, L.k_in, L.n_out, r, backward=b) for b in (False, True)) or 1,
+                         dtype=torch.uint8, device=dev)
+        calls = {"fwd": lambda: nl.linear_fwd(inp["x"], W, inp["A"], inp["B"], s, y=y, t_out=T, workspace=ws),
+                 "bwd_input": lambda: nl.linear_bwd_input(inp["dy"], W, inp["A"], inp["B"], s, dx=dx, u_out=U,
+                                                          workspace=ws)}
+        flops = 2 * M * L.n_out * L.k_in + 2 * M * r * (L.n_out + L.k_in)
+        for kind, fn in calls.items():
+            for _ in range(warm):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[f"{name}_{kind}"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                                     "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del W, inp
+    out["calls"] = f"{warm} warm-up + {reps} timed back-to-back calls per entry"
+    return out
+
+
 def lorafa_measure(nl, dev, reps: int = 20):
     """LoRA-FA optimizer step on the rank-64 down_proj adapter (A [64, 14336]
     frozen, B [4096, 64]): the one-off preconditioner and the preconditioned
@@ -249,9 +296,10 @@ def lorafa_measure(nl, dev, reps: int = 20):
 
 def paged_adamw_measure(nl, dev, reps: int = 10):
     """The AdamW update of the seven Llama-8B adapters (r = 16) with the moments
-    in pinned host memory, moved in 2 MiB pages (lora_adamw_step_paged), against
-    the same update with device-resident moments. Per update 16 bytes of moments
-    per parameter cross PCIe (m and v, in and out)."""
+    in pinned host memory, read and written in place by the update kernel
+    (lora_adamw_step_paged), against the same update with device-resident
+    moments. Per update 16 bytes of moments per parameter cross PCIe (m and v,
+    in and out)."""
     import torch
     import workloads
     ads_dev, ads_host = [], []
@@ -269,12 +317,11 @@ def paged_adamw_measure(nl, dev, reps: int = 10):
         ads_dev.append(d)
         ads_host.append(h)
     page = 2 << 20
-    staging = torch.empty(2 * page, dtype=torch.uint8, device=dev)
     k = [0]
 
     def paged():
         k[0] += 1
-        nl.lora_adamw_step_paged(ads_host, step=k[0], staging=staging, page_bytes=page, **ADAMW)
+        nl.lora_adamw_step_paged(ads_host, step=k[0], page_bytes=page, **ADAMW)
 
     def resident():
         k[0] += 1
@@ -530,6 +577,12 @@ def main():
         nl.load()
         print(json.dumps(quant_dequant_throughput(nl, torch.device("cuda:0"), passes=1)), flush=True)
         return
+    if args.gemm_sustained_only:
+        import torch
+        from qlora_adapter_amd import nf4lora as nl
+        nl.load()
+        print(json.dumps(gemm_sustained(nl, torch.device("cuda:0"))), flush=True)
+        return
     if args.decoder_step_only:
         import torch
         from qlora_adapter_amd import nf4lora as nl
@@ -559,13 +612,9 @@ def main():
     for i, L in enumerate(layers):
         inp = workloads.lora_inputs(L, M, seed_offset=i, device="cuda")
         W = workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(i), "cuda")
-        n = W.numel()
-        lay = nl.layout(n, True)
         P.append(dict(
             L=L, W=W, x=inp["x"], dy=inp["dy"], A=inp["A"], B=inp["B"],
             Wq=nl.NF4Tensor.empty(W.shape, True, dev),
-            qws=torch.empty(lay["quantize_workspace_bytes"], dtype=torch.uint8, device=dev),
-            status=torch.zeros(1, dtype=torch.int32, device=dev),
             y=torch.empty((M, L.n_out), dtype=torch.bfloat16, device=dev),
             T=torch.empty((M, r), dtype=torch.float32, device=dev),
             dx=torch.empty((M, L.k_in), dtype=torch.bfloat16, device=dev),
@@ -583,6 +632,9 @@ def main():
     adapters = [dict(A=p["A"], dA=p["dA"], mA=p["mA"], vA=p["vA"], B=p["B"], dB=p["dB"], mB=p["mB"], vB=p["vB"])
                 for p in P]
     wq_all, wd_all = [p["Wq"] for p in P], [p["Wd"] for p in P]
+    w_all = [p["W"] for p in P]
+    qm_ws = torch.empty(nl.quantize_many_workspace_bytes(wq_all), dtype=torch.uint8, device=dev)
+    q_status = torch.zeros(1, dtype=torch.int32, device=dev)
     kinds = ["quantize", "fwd", "bwd", "grad", "adamw", "dequant"]
     opt_step = [0]
 
@@ -599,9 +651,8 @@ def main():
             fn()
             e1.record(stream)
             events.append((kind, i, e0, e1))
-        for i, p in enumerate(P):
-            mark("quantize", i, lambda p=p: nl.quantize(p["W"], True, out=p["Wq"], workspace=p["qws"],
-                                                        status=p["status"]))
+        # one launch set packs all seven matrices
+        mark("quantize", 0, lambda: nl.quantize_many(w_all, True, outs=wq_all, workspace=qm_ws, status=q_status))
         for i, p in enumerate(P):
             mark("fwd", i, lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"], t_out=p["T"]))
         for i, p in enumerate(P):
@@ -618,7 +669,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    assert all(int(p["status"].item()) == 0 for p in P)
+    assert int(q_status.item()) == 0
 
     # ---- timed region: whole steps, no per-call events ----
     torch.cuda.synchronize()
@@ -655,7 +706,7 @@ def main():
         dq_bytes += pb + 2 * n
         dq_ms += per["dequant"][i]  # the whole decode is recorded at index 0
         q_bytes += 4 * n + pb
-        q_ms += per["quantize"][i]
+        q_ms += per["quantize"][i]  # the whole pack is recorded at index 0
         ad_bytes += ADAMW_BYTES * r * (L.k_in + L.n_out)
         ad_ms += per["adamw"][i]  # the whole update is recorded at index 0
     total_flops = flops_base + flops_lora
@@ -667,6 +718,7 @@ def main():
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
     ad_gbps = ad_bytes / (ad_ms * 1e-3) / 1e9
     qd = None if args.no_throughput else quant_dequant_throughput(nl, dev)
+    sustained = gemm_sustained(nl, dev)
     fa = lorafa_measure(nl, dev)
     emb = embedding_measure(nl, dev)
     paged = paged_adamw_measure(nl, dev)
@@ -718,11 +770,12 @@ def main():
                     "dequant_gbps": round(dq_gbps, 1), "adamw_ms": round(ad_ms, 4),
                     "adamw_gbps": round(ad_gbps, 1),
                     "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds
-                                          if k not in ("adamw", "dequant")}},
+                                          if k not in ("adamw", "dequant", "quantize")}},
         "roofline_adamw": {"kernel": "lora_adamw_step_many (A and B of all 7 adapters, one launch)",
                            "bound": "hbm", "achieved": round(ad_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                            "frac": round(ad_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                            "note": "28 B per parameter, 1.31 M parameters (36.7 MB) per launch"},
+        "gemm_sustained": sustained,
         "lorafa": fa,
         "embedding_rows": emb,
         "paged_adamw": paged,

@@ -378,18 +378,19 @@ int lora_adamw_step_many(const nf4_adamw* opt, const nf4_lora_state* adapters, i
 
 /* Paged moments (Aner docs "Native model adaptation and NF4", section "Paged
  * AdamW uses real CUDA managed memory"): the pages keep both FP32 moment
- * tensors in managed memory that prefers the CPU, bring each chunk of
- * page_bytes to the GPU for the update and send it back. The MI355X devices
- * this library targets report no managed-memory support, so the same schedule
- * is expressed with explicit copies: every mA/vA/mB/vB of `adapters` is PINNED
- * HOST memory (hipHostMalloc, or a pinned tensor; pageable or device memory is
- * NF4_EINVAL), and each page of moments is copied into `staging` (device,
- * 16-byte aligned, at least 2 * page_bytes), updated by the same kernel as
- * lora_adamw_step_many, and copied back, all in order on `stream`. The host
- * must synchronize the stream before it reads the moments. page_bytes is a
- * multiple of 4096 in [4096, 64 MiB], as on the pages. Parameters, gradients
- * and preconditioners are device memory. Results equal lora_adamw_step_many's
- * bit for bit. */
+ * tensors in managed memory that prefers the CPU and let the update reach them
+ * chunk by chunk. The MI355X devices this library targets report no
+ * managed-memory support, so the moments stay in PINNED HOST memory instead:
+ * every mA/vA/mB/vB of `adapters` is pinned host memory (hipHostMalloc, or a
+ * pinned tensor; pageable or device memory is NF4_EINVAL), and the same
+ * kernel as lora_adamw_step_many, in one launch for all adapters, reads and
+ * writes them in place through their device-visible addresses (the host link
+ * carries each moment once in each direction, with no staging copies). The
+ * host must synchronize the stream before it reads the moments. `staging` and
+ * `staging_bytes` are accepted and unused (NULL is fine); page_bytes, the
+ * pages' chunk size, is still checked: a multiple of 4096 in [4096, 64 MiB].
+ * Parameters, gradients and preconditioners are device memory. Results equal
+ * lora_adamw_step_many's bit for bit. */
 int lora_adamw_step_paged(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,
                           const float* grad_scale, void* staging, size_t staging_bytes, size_t page_bytes,
                           nf4_stream_t stream);

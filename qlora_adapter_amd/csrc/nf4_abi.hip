@@ -494,13 +494,15 @@ int check_adamw(const nf4_adamw* opt) {
   return NF4_OK;
 }
 
-bool is_pinned_host(const void* p) {
+// The device-visible address of pinned host memory p (NULL for pageable or
+// device memory).
+void* pinned_host_device_ptr(const void* p) {
   hipPointerAttribute_t at;
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
     (void)hipGetLastError();  // clear the error an unknown (pageable) pointer leaves
-    return false;
+    return nullptr;
   }
-  return at.type == hipMemoryTypeHost;
+  return at.type == hipMemoryTypeHost ? at.devicePointer : nullptr;
 }
 
 int check_lora_state(const nf4_lora_state& a) {
@@ -539,19 +541,26 @@ int lora_adamw_step_paged(const nf4_adamw* opt, const nf4_lora_state* adapters, 
   if (int rc = check_adamw(opt)) return rc;
   if (!adapters || count < 1 || count > NF4_MAX_ADAPTERS_PER_CALL) return NF4_EINVAL;
   if (page_bytes < 4096 || page_bytes > (size_t(64) << 20) || page_bytes % 4096 != 0) return NF4_EINVAL;
-  if (!staging || staging_bytes < 2 * page_bytes) return NF4_EWORKSPACE;
-  if (!aligned(staging, 16)) return NF4_EALIGN;
+  (void)staging;  // accepted for callers written against the staged schedule; not used
+  (void)staging_bytes;
   for (int32_t i = 0; i < count; ++i)
     if (int rc = check_lora_state(adapters[i])) return rc;
   if (grad_scale && !aligned(grad_scale, 4)) return NF4_EALIGN;
   if (int rc = check_device()) return rc;
+  // the same update kernel, reading and writing every moment in place through
+  // its device-visible address
+  nf4_lora_state dev[NF4_MAX_ADAPTERS_PER_CALL];
   for (int32_t i = 0; i < count; ++i) {
-    const nf4_lora_state& a = adapters[i];
-    const void* host[] = {a.mA, a.vA, a.mB, a.vB};
-    for (const void* p : host)
-      if (p && !is_pinned_host(p)) return NF4_EINVAL;
+    dev[i] = adapters[i];
+    float** mom[] = {&dev[i].mA, &dev[i].vA, &dev[i].mB, &dev[i].vB};
+    for (float** m : mom) {
+      if (!*m) continue;
+      void* d = pinned_host_device_ptr(*m);
+      if (!d) return NF4_EINVAL;
+      *m = static_cast<float*>(d);
+    }
   }
-  return launch_lora_adamw_paged(*opt, adapters, count, grad_scale, staging, page_bytes, as_stream(stream));
+  return launch_lora_adamw(*opt, dev, count, grad_scale, as_stream(stream));
 }
 
 int lora_adamw_step_many(const nf4_adamw* opt, const nf4_lora_state* adapters, int32_t count,

@@ -95,10 +95,6 @@ int launch_lorafa_preconditioner(const float* A, int32_t r, int64_t K, float* P,
 // One AdamW update of `count` adapters (validated) in one launch.
 int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
                       hipStream_t st);
-// The same update with the moments in pinned host memory, page by page through
-// `staging` (two pages of page_bytes).
-int launch_lora_adamw_paged(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
-                            void* staging, size_t page_bytes, hipStream_t st);
 
 // Decoder-layer operations (nf4_decoder.hip).
 int launch_add_rmsnorm(const void* x, const void* res, nf4_dtype dt, int64_t rows, int64_t D, const float* gamma,

@@ -376,42 +376,4 @@ int launch_lora_adamw(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t co
   return launch_status();
 }
 
-int launch_lora_adamw_paged(const nf4_adamw& opt, const nf4_lora_state* ad, int32_t count, const float* grad_scale,
-                            void* staging, size_t page_bytes, hipStream_t st) {
-  const AdamwConst c = make_adamw_const(opt);
-  const int64_t page = (int64_t)(page_bytes / sizeof(float));
-  float* ms = static_cast<float*>(staging);
-  float* vs = ms + page;
-  // One tensor in pages: moments in, update, moments out, all in stream order.
-  auto run = [&](float* p, const float* g, float* mh, float* vh, int64_t n, const float* P, int32_t r,
-                 float s) -> int {
-    const int mode = seg_mode(P, r);
-    const int64_t unit = mode == 0 ? 4 : 4 * (int64_t)r;  // a page holds whole rows of a preconditioned B
-    const int64_t chunk = page / unit * unit;
-    for (int64_t off = 0; off < n; off += chunk) {
-      const int64_t len = (n - off < chunk) ? n - off : chunk;
-      const size_t bytes = sizeof(float) * (size_t)len;
-      if (hipMemcpyAsync(ms, mh + off, bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
-          hipMemcpyAsync(vs, vh + off, bytes, hipMemcpyHostToDevice, st) != hipSuccess)
-        return NF4_EDEVICE;
-      AdamwTable tab{};
-      tab.seg[0] = AdamwSeg{p + off, g + off, ms, vs, P, len, 0, r, mode, seg_pscale(P, s)};
-      tab.count = 1;
-      hipLaunchKernelGGL(k_lora_adamw, dim3((unsigned)seg_blocks(mode, len)), dim3(256), 0, st, tab, grad_scale, c);
-      if (int rc = launch_status()) return rc;
-      if (hipMemcpyAsync(mh + off, ms, bytes, hipMemcpyDeviceToHost, st) != hipSuccess ||
-          hipMemcpyAsync(vh + off, vs, bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
-        return NF4_EDEVICE;
-    }
-    return NF4_OK;
-  };
-  for (int32_t i = 0; i < count; ++i) {
-    const nf4_lora_state& a = ad[i];
-    if (a.A)
-      if (int rc = run(a.A, a.dA, a.mA, a.vA, (int64_t)a.r * a.K, nullptr, a.r, a.s)) return rc;
-    if (int rc = run(a.B, a.dB, a.mB, a.vB, a.N * a.r, a.precond, a.r, a.s)) return rc;
-  }
-  return NF4_OK;
-}
-
 }  // namespace nf4

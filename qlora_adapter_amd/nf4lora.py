@@ -616,22 +616,23 @@ def lora_adamw_step_many(adapters, *, step: int, lr: float, beta1: float = 0.9, 
                                                                _ptr(grad_scale), _stream(adapters[0]["B"].device)))
 
 
-def lora_adamw_step_paged(adapters, *, step: int, lr: float, staging: torch.Tensor, page_bytes: int = 2 << 20,
-                          beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01,
-                          grad_scale: Optional[torch.Tensor] = None) -> None:
+def lora_adamw_step_paged(adapters, *, step: int, lr: float, staging: Optional[torch.Tensor] = None,
+                          page_bytes: int = 2 << 20, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                          weight_decay: float = 0.01, grad_scale: Optional[torch.Tensor] = None) -> None:
     """lora_adamw_step_many with every moment tensor in pinned host memory,
-    moved page by page through `staging` (a device uint8 tensor of at least
-    2 * page_bytes). Synchronize the stream before reading the moments."""
+    which the update kernel reads and writes in place (one launch for all
+    adapters; `staging` is accepted and unused). Synchronize the stream before
+    reading the moments."""
     adapters = list(adapters)
     if not adapters:
         return
     _grad_scale(grad_scale)
-    _dev(staging, "staging")
     arr = (_LoraState * len(adapters))(*[_state(a, paged=True) for a in adapters])
     opt = _Adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
     _check("lora_adamw_step_paged",
            load().lora_adamw_step_paged(ctypes.byref(opt), arr, len(adapters), _ptr(grad_scale), _ptr(staging),
-                                        staging.numel() * staging.element_size(), int(page_bytes),
+                                        0 if staging is None else staging.numel() * staging.element_size(),
+                                        int(page_bytes),
                                         _stream(adapters[0]["B"].device)))
 
 

@@ -403,17 +403,21 @@ def test_quantize_many_argument_errors(lib):
 
 def test_paged_step_argument_errors(lib):
     L, m = lib
-    EINVAL, EALIGN, EWS = -1, -2, -6
+    EINVAL = -1
     opt = m._Adamw(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
     st = (m._LoraState * 1)(m._LoraState(r=16, K=64, N=32, A=256, dA=256, mA=256, vA=256, B=256, dB=256, mB=256,
                                          vB=256, precond=None, s=2.0))
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 8192, 4095, None) == EINVAL
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 8192, 2048, None) == EINVAL
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 1 << 28, 128 << 20, None) == EINVAL
-    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 256, 4096, 4096, None) == EWS
-    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, None, 8192, 4096, None) == EWS
-    assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, 264, 8192, 4096, None) == EALIGN
     assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 0, None, 256, 8192, 4096, None) == EINVAL
+    # staging is not used (the kernel reads the moments in place), so any staging argument gets as far as
+    # the device check (no device: NF4_EDEVICE) or, with a device, the pinned-memory check of the moments
+    # (these are not host pointers: NF4_EINVAL)
+    import torch
+    expect = EINVAL if torch.cuda.is_available() else -4
+    for staging, nbytes in ((None, 0), (264, 8192), (256, 4096)):
+        assert L.lora_adamw_step_paged(ctypes.byref(opt), st, 1, None, staging, nbytes, 4096, None) == expect
 
 
 def test_decoder_op_argument_errors(lib):

@@ -227,9 +227,9 @@ def _to_pinned(t: torch.Tensor) -> torch.Tensor:
 
 @pytest.mark.parametrize("page_bytes", [4096, 2 << 20])
 def test_paged_moments_equal_device_moments(gpu, page_bytes):
-    """lora_adamw_step_paged with the moments in pinned host memory, moved page
-    by page, gives the same parameters and moments as lora_adamw_step_many, bit
-    for bit: LoRA, LoRA-FA with the preconditioner (r % 4 == 0 and r = 6), and
+    """lora_adamw_step_paged with the moments in pinned host memory (read and
+    written in place by the update kernel) gives the same parameters and
+    moments as lora_adamw_step_many, bit for bit: LoRA, LoRA-FA with the preconditioner (r % 4 == 0 and r = 6), and
     tensors spanning many 4 KiB pages."""
     specs = [(16, 4096, 4096, False, False), (5, 333, 77, False, False), (16, 1024, 512, True, True),
              (6, 100, 37, True, True), (64, 14336, 4096, False, False)]
