@@ -622,6 +622,8 @@ def main():
             dA=torch.empty((r, L.k_in), dtype=torch.float32, device=dev),
             dB=torch.empty((L.n_out, r), dtype=torch.float32, device=dev),
             gws=torch.empty(nl.lora_grad_workspace_bytes(M, L.k_in, L.n_out, r), dtype=torch.uint8, device=dev),
+            lws=torch.empty(max(1, *(nl.linear_workspace_bytes(M, L.k_in, L.n_out, r, backward=b) for b in (False, True))),
+                            dtype=torch.uint8, device=dev),
             mA=torch.zeros((r, L.k_in), dtype=torch.float32, device=dev),
             vA=torch.zeros((r, L.k_in), dtype=torch.float32, device=dev),
             mB=torch.zeros((L.n_out, r), dtype=torch.float32, device=dev),
@@ -654,10 +656,11 @@ def main():
         # one launch set packs all seven matrices
         mark("quantize", 0, lambda: nl.quantize_many(w_all, True, outs=wq_all, workspace=qm_ws, status=q_status))
         for i, p in enumerate(P):
-            mark("fwd", i, lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"], t_out=p["T"]))
+            mark("fwd", i, lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"], t_out=p["T"],
+                                                     workspace=p["lws"]))
         for i, p in enumerate(P):
             mark("bwd", i, lambda p=p: nl.linear_bwd_input(p["dy"], p["Wq"], p["A"], p["B"], s, dx=p["dx"],
-                                                           u_out=p["U"]))
+                                                           u_out=p["U"], workspace=p["lws"]))
         for i, p in enumerate(P):
             mark("grad", i, lambda p=p: nl.lora_grad(p["x"], p["dy"], p["T"], p["U"], s, dA=p["dA"], dB=p["dB"],
                                                      workspace=p["gws"]))

@@ -260,8 +260,9 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
  * rank r (0: no adapter). Three parts, each rounded up to 256 bytes: (1) bf16
  * only: a long reduction over few output tiles (short sequences through a
  * wide layer, e.g. 512 tokens through a 4096 x 14336 projection) is split in
- * parts whose fp32 partial sums the workspace holds; (2) r > 32, or fewer
- * than 4096 token rows with a reduction of at least 2048: the side product's
+ * parts whose fp32 partial sums the workspace holds; (2) r > 32, a reduction
+ * of at least 8192, or fewer than 4096 token rows with a reduction of at least
+ * 2048: the side product's
  * reduction (over K forward, N backward) is split in parts whose fp32 partial
  * sums of the M x r product the workspace holds; (3) with
  * NF4_WS_NO_SIDE_OUT, M * r fp32 for the side product itself. Partial sums are

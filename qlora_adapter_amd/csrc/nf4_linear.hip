@@ -811,12 +811,15 @@ __global__ __launch_bounds__(256) void k_lora_combine(LoraSum q0, LoraSum q1, in
 }
 
 // The side product takes the split skinny GEMM (k_side_wide, then k_side_sum
-// over the parts) for ranks beyond 32, and for ranks up to 32 when k_side_bf16
-// (16 rows per workgroup) would leave most of the chip idle: fewer than 256
+// over the parts) for ranks beyond 32; for ranks up to 32 when k_side_bf16
+// (16 rows per workgroup) would leave most of the chip idle, fewer than 256
 // workgroups over a reduction of at least 2048 (a 512-token step through a
-// 4096-wide layer: 32 workgroups of k_side_bf16).
+// 4096-wide layer: 32 workgroups of k_side_bf16); and for reductions of 8192
+// or more, where k_side_bf16's workgroups would each read the whole fp32
+// factor (twice the activation bytes for a 14336-long reduction at r = 16)
+// while k_side_wide reads it once per 128 rows.
 bool side_split_path(int64_t M, int64_t I, int32_t r) {
-  return r > 32 || (ceil_div(M, SR) < 256 && I >= 2048);
+  return r > 32 || I >= 8192 || (ceil_div(M, SR) < 256 && I >= 2048);
 }
 
 // Split of the wide side product's reduction: about 512 workgroups of 128

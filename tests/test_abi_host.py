@@ -165,14 +165,14 @@ def test_optional_side_products_and_recompute(lib):
 
 def test_wide_rank_side_product_workspace(lib):
     """The side product's reduction (over K forward, N backward) is split for
-    ranks beyond 32, and for ranks up to 32 when fewer than 4096 token rows
-    meet a reduction of at least 2048 (16-row workgroups would leave most of
-    the chip idle): parts of at least 128 indices, about 512 workgroups of 128
+    ranks beyond 32, for reductions of 8192 or more, and when fewer than 4096
+    token rows meet a reduction of at least 2048 (16-row workgroups would leave
+    most of the chip idle): parts of at least 128 indices, about 512 workgroups of 128
     rows x 64 ranks in all; the workspace holds one M x r fp32 partial product
     per part, and lora_grad's recomputation takes the larger of its two."""
     L, _ = lib
     def parts(M, I, r):
-        if not (r > 32 or (-(-M // 16) < 256 and I >= 2048)):
+        if not (r > 32 or I >= 8192 or (-(-M // 16) < 256 and I >= 2048)):
             return 1
         tiles = -(-M // 128) * -(-r // 64)
         steps = -(-I // 32)
@@ -182,7 +182,7 @@ def test_wide_rank_side_product_workspace(lib):
     rnd = lambda b: (b + 255) // 256 * 256
     cases = ((8192, 14336, 4096, 64), (4096, 4096, 4096, 100), (512, 4096, 14336, 256), (64, 576, 192, 33),
              (512, 4096, 1024, 16), (512, 14336, 4096, 8), (4080, 4096, 4096, 32), (512, 576, 1536, 8),
-             (4096, 4096, 4096, 16))
+             (4096, 4096, 4096, 16), (4096, 14336, 4096, 16), (4096, 4096, 14336, 16))
     for M, K, N, r in cases:
         for bwd in (0, 1):
             I = N if bwd else K
@@ -197,7 +197,8 @@ def test_wide_rank_side_product_workspace(lib):
         assert L.lora_grad_workspace_bytes(M, K, N, r, 0, 1) == base + side + pt
     # the split engages where the model says it does
     assert parts(512, 4096, 16) > 1 and parts(512, 1024, 16) == 1 and parts(4096, 4096, 16) == 1
-    # 32 and below at 4096 or more tokens: no split
+    assert parts(4096, 14336, 16) > 1 and parts(4096, 8191, 16) == 1
+    # 32 and below at 4096 or more tokens over a reduction under 8192: no split
     assert L.nf4_linear_workspace_bytes(8192, 14336, 4096, 32, 1) == L.nf4_linear_workspace_bytes(8192, 14336, 4096, 0, 1)
 
 
