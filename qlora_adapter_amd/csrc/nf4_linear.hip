@@ -950,12 +950,10 @@ int launch_linear(const LinearArgs& g, hipStream_t st) {
 
 // Tokens per chunk of the bf16 MFMA reduction (a multiple of the 32-token
 // step), for about 512 workgroups of 256 columns (two per CU):
-//  - dB (N columns): 512 / tiles(N) chunks, the same with or without dA, so
-//    that LoRA-FA's dB sums in the same order as the full call's;
-//  - dA (K columns): 512 / (tiles(K) + tiles(N)) chunks, so that a dA
-//    workgroup walks about as many steps as the whole call's work spread over
-//    512 slots; dA's workgroups come first in the grid and the short dB ones
-//    cycle through the remaining slots.
+//  - with dA, both reductions take 512 / (tiles(K) + tiles(N)) chunks, so every
+//    workgroup walks the same number of steps and the fp32 partial sums (written
+//    and read again by the combine) are as few as that parallelism allows;
+//  - LoRA-FA (dB alone) takes 512 / tiles(N) chunks.
 // Fewer, longer chunks than the general path keep the partial sums small next
 // to the input.
 int64_t lora_chunk_steps(int64_t M, int64_t tiles) {
@@ -1005,7 +1003,7 @@ void lora_side(const float* P, const T* Q, int64_t M, int64_t J, int32_t r, floa
 void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int64_t N, const float* t,
                     const float* u, int32_t r, float s, float* dA, float* dB, float* partA, float* partB,
                     hipStream_t st) {
-  const int64_t chB = lora_chunk_mfma_b(M, N), chA = lora_chunk_mfma_a(M, K, N);
+  const int64_t chA = lora_chunk_mfma_a(M, K, N), chB = dA ? chA : lora_chunk_mfma_b(M, N);
   const LoraProb pb{t, dy, N, chB, ceil_div(N, 256), partB};
   const LoraProb pa{u, x, K, chA, ceil_div(K, 256), partA};
   const int64_t blocksB = pb.col_tiles * ceil_div(M, chB);

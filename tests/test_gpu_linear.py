@@ -242,7 +242,9 @@ def test_backward_heavy_down_proj(gpu, orc):
     """The backward-heavy configuration: down_proj W [4096, 14336], 8192 tokens,
     dY ~ N(0, 0.01), rank-64 rsLoRA with alpha 16, in the launch configuration
     the benchmark times. dX and U on 24 sampled token rows; dA and dB in full,
-    then the LoRA-FA variant (dB only, bit-identical to the full call's dB)."""
+    then the LoRA-FA variant (dB only; at 8192 tokens it cuts its token reduction
+    differently from the full call, so it is held to the oracle and to run-to-run
+    identity)."""
     print("[linear] backward-heavy down_proj 8192 tokens r=64", flush=True)
     wl = workloads.WORKLOADS["down_proj_bwd"]
     L = wl["layers"][0]
@@ -251,8 +253,9 @@ def test_backward_heavy_down_proj(gpu, orc):
     c = make_case(M, L.k_in, L.n_out, r, torch.bfloat16, seed=21, dy_std=wl["dy_std"])
     Wq, y, T, dx, U, (dA, dB) = run_all(gpu, c, s)
     _, dB_fa = gpu.lora_grad(c["x"], c["dy"], T, None, s, fa=True)
+    _, dB_fa2 = gpu.lora_grad(c["x"], c["dy"], T, None, s, fa=True)
     torch.cuda.synchronize()
-    assert torch.equal(dB.view(torch.int32), dB_fa.view(torch.int32))
+    assert torch.equal(dB_fa.view(torch.int32), dB_fa2.view(torch.int32))  # fixed-order sums
     Wref = oracle_weight(orc, c["W"], torch.bfloat16)
     rows = np.sort(np.random.default_rng(5).choice(M, 24, replace=False))
     dy = to_np(c["dy"])
@@ -264,6 +267,7 @@ def test_backward_heavy_down_proj(gpu, orc):
     dA_ref, dB_ref = orc.lora_grad(x, dy, orc.lora_down(x, A), orc.lora_up_grad(dy, B), s)
     assert_close(dA.cpu().numpy(), dA_ref, "f32", "dA")
     assert_close(dB.cpu().numpy(), dB_ref, "f32", "dB")
+    assert_close(dB_fa.cpu().numpy(), dB_ref, "f32", "LoRA-FA dB")
 
 
 SPLIT = [
@@ -315,8 +319,8 @@ def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
     workspace): y and dX are bit-identical to the calls that return T and U.
     lora_grad recomputes T from x and A, and U from dY and B, when they are not
     given: bit-identical to the calls that pass them (the same kernels form
-    them), and dA, dB against the oracle; LoRA-FA recomputing T gives the same
-    dB."""
+    them), and dA, dB against the oracle; LoRA-FA recomputing T gives the dB
+    of LoRA-FA given T."""
     print(f"[linear] optional side products M={M} K={K} N={N} r={r}", flush=True)
     c = make_case(M, K, N, r, torch.bfloat16, seed=M + 7)
     s = gpu.lora_scale(32.0, r)
@@ -330,18 +334,23 @@ def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
     dA_u, dB_u = gpu.lora_grad(c["x"], c["dy"], T, None, s, B=c["B"])
     dA_tu, dB_tu = gpu.lora_grad(c["x"], c["dy"], None, None, s, A=c["A"], B=c["B"])
     _, dB_fa = gpu.lora_grad(c["x"], c["dy"], None, None, s, fa=True, A=c["A"])
+    _, dB_fa_t = gpu.lora_grad(c["x"], c["dy"], T, None, s, fa=True)
     torch.cuda.synchronize()
     assert T2 is None and U2 is None
     assert torch.equal(y, y2) and torch.equal(dx, dx2)
     for a in (dA_t, dA_u, dA_tu):
         assert torch.equal(a.view(torch.int32), dA.view(torch.int32))
-    for b in (dB_t, dB_u, dB_tu, dB_fa):
+    for b in (dB_t, dB_u, dB_tu):
         assert torch.equal(b.view(torch.int32), dB.view(torch.int32))
+    # LoRA-FA recomputing T equals LoRA-FA given T (its own token chunking,
+    # which matches the full call's up to a few hundred tokens)
+    assert torch.equal(dB_fa.view(torch.int32), dB_fa_t.view(torch.int32))
     x, dy = to_np(c["x"]), to_np(c["dy"])
     A, B = c["A"].cpu().numpy(), c["B"].cpu().numpy()
     dA_ref, dB_ref = orc.lora_grad(x, dy, orc.lora_down(x, A), orc.lora_up_grad(dy, B), s)
     assert_close(dA_tu.cpu().numpy(), dA_ref, "f32", "dA (T, U recomputed)")
     assert_close(dB_tu.cpu().numpy(), dB_ref, "f32", "dB (T, U recomputed)")
+    assert_close(dB_fa.cpu().numpy(), dB_ref, "f32", "LoRA-FA dB (T recomputed)")
 
 
 @pytest.mark.parametrize("M,K,N,r", [(300, 1024, 576, 64), (129, 576, 1536, 100), (200, 640, 512, 256),
@@ -350,8 +359,10 @@ def test_large_ranks(gpu, orc, M, K, N, r):
     """Ranks past 32 on the bf16 path (the side products in workgroups of 64
     ranks with a split reduction, the LoRA-gradient reduction in blocks of 32,
     64 or 128 ranks per launch): y, dX against the oracle at the bf16 bar, T, U,
-    dA, dB at the fp32 bar, LoRA-FA's dB equal to the full call's, and the
-    workspace-held and recomputed side products equal to the returned ones."""
+    dA, dB at the fp32 bar, LoRA-FA's dB equal to the full call's (at these
+    token counts both cut the token reduction into the same 32-token chunks),
+    and the workspace-held and recomputed side products equal to the returned
+    ones."""
     print(f"[linear] large rank M={M} K={K} N={N} r={r}", flush=True)
     c = make_case(M, K, N, r, torch.bfloat16, seed=M + r)
     s = gpu.lora_scale(16.0, r, rslora=True)
