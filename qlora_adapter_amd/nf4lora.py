@@ -701,44 +701,52 @@ def _rows(t: torch.Tensor, name: str, width: int) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else width
 
 
-def _dev_rows(t: torch.Tensor, name: str, dtype=None) -> None:
-    """Device, dtype and alignment checks of a possibly strided activation."""
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}")
+def _same_dtype(dtype, *named) -> None:
+    for name, t in named:
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _on_device(*named) -> None:
+    for name, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
 
 
 def rope_(x: torch.Tensor, heads: int, d: int, theta: float, inverse: bool = False) -> torch.Tensor:
     """Rotary embedding of x [S, heads*d] in place (x may be a column block of a
     wider array: its row stride is passed on)."""
-    _dev_rows(x, "x")
     ld = _rows(x, "x", int(heads) * int(d))
+    _on_device(("x", x))
     _check("nf4_rope", load().nf4_rope(_ptr(x), _DT[x.dtype], x.shape[0], int(heads), int(d), ld, float(theta),
                                        int(bool(inverse)), _stream(x.device)))
     return x
 
 
-def _qkv_stride(q, k, v, hq: int, hkv: int, d: int) -> int:
-    """Common row stride of q, k, v (0 when all three are dense)."""
-    lq, lk, lv = _rows(q, "q", hq * d), _rows(k, "k", hkv * d), _rows(v, "v", hkv * d)
+def _qkv_stride(q, k, v, hq: int, hkv: int, d: int, names=("q", "k", "v")) -> int:
+    """Common row stride of q, k, v (0 when all three are dense); shapes, row
+    counts and dtypes are checked here, the device by the caller."""
+    lq, lk, lv = _rows(q, names[0], hq * d), _rows(k, names[1], hkv * d), _rows(v, names[2], hkv * d)
+    if not (q.shape[0] == k.shape[0] == v.shape[0]):
+        raise ValueError(f"{', '.join(names)} must have the same number of rows")
+    _same_dtype(q.dtype, (names[1], k), (names[2], v))
     if lq == hq * d and lk == hkv * d and lv == hkv * d:
         return 0
     if not (lq == lk == lv):
-        raise ValueError("q, k and v must be dense or share one row stride")
+        raise ValueError(f"{', '.join(names)} must be dense or share one row stride")
     return lq
 
 
 def attention_fwd(q, k, v, hq: int, hkv: int, d: int, o=None, lse=None):
     """Causal GQA attention; q, k, v may be column blocks of one wider array."""
-    for n, t in (("q", q), ("k", k), ("v", v)):
-        _dev_rows(t, n, q.dtype)
     ld = _qkv_stride(q, k, v, hq, hkv, d)
     S = q.shape[0]
     if o is None:
         o = torch.empty((S, hq * d), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((hq, S), dtype=torch.float32, device=q.device)
+    _arrays((o, "o", q.dtype, (S, hq * d)), (lse, "lse", torch.float32, (hq, S)))
+    _on_device(("q", q), ("k", k), ("v", v))
     _check("nf4_attention_fwd", load().nf4_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], S, hq, hkv, d, ld,
                                                          _ptr(o), _ptr(lse), _stream(q.device)))
     return o, lse
@@ -754,24 +762,30 @@ def attention_bwd(dout, q, k, v, o, lse, hq: int, hkv: int, d: int, dq=None, dk=
     dq = torch.empty((S, hq * d), dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty((S, hkv * d), dtype=q.dtype, device=q.device) if dk is None else dk
     dv = torch.empty((S, hkv * d), dtype=q.dtype, device=q.device) if dv is None else dv
-    if _qkv_stride(dq, dk, dv, hq, hkv, d) != ld:
-        raise ValueError("dq, dk, dv must have the row stride of q, k, v")
+    if _qkv_stride(dq, dk, dv, hq, hkv, d, ("dq", "dk", "dv")) != ld or dq.shape[0] != S:
+        raise ValueError("dq, dk, dv must have the rows, dtype and row stride of q, k, v")
+    _same_dtype(q.dtype, ("dq", dq))
     if delta is None:
         delta = torch.empty((hq, S), dtype=torch.float32, device=q.device)
+    _arrays((dout, "dout", q.dtype, (S, hq * d)), (o, "o", q.dtype, (S, hq * d)),
+            (lse, "lse", torch.float32, (hq, S)), (delta, "delta", torch.float32, (hq, S)))
+    _on_device(("q", q), ("k", k), ("v", v), ("dq", dq), ("dk", dk), ("dv", dv))
     _check("nf4_attention_bwd", load().nf4_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                                          _DT[q.dtype], S, hq, hkv, d, ld, _ptr(delta), _ptr(dq),
                                                          _ptr(dk), _ptr(dv), _stream(q.device)))
     return dq, dk, dv
 
 
-def _gu_stride(g, u) -> Tuple[int, int, int]:
-    """(rows, width, row stride) of the SwiGLU inputs, which share one stride."""
+def _gu_stride(g, u, names=("g", "u")) -> Tuple[int, int, int]:
+    """(rows, width, row stride) of a SwiGLU pair, which share one shape,
+    dtype and stride (the device is checked by the caller)."""
     if g.dim() != 2 or u.shape != g.shape:
-        raise ValueError("g and u must be [rows, width] of one shape")
+        raise ValueError(f"{names[0]} and {names[1]} must be [rows, width] of one shape")
     rows, width = g.shape
-    lg, lu = _rows(g, "g", width), _rows(u, "u", width)
+    lg, lu = _rows(g, names[0], width), _rows(u, names[1], width)
     if lg != lu:
-        raise ValueError("g and u must share one row stride")
+        raise ValueError(f"{names[0]} and {names[1]} must share one row stride")
+    _same_dtype(g.dtype, (names[1], u))
     return rows, width, lg
 
 
@@ -780,8 +794,8 @@ def swiglu(g, u, a=None):
     wider array); a is dense."""
     rows, width, ld = _gu_stride(g, u)
     a = torch.empty((rows, width), dtype=g.dtype, device=g.device) if a is None else a
-    if not a.is_contiguous() or a.shape != g.shape:
-        raise ValueError("a must be a dense [rows, width] array")
+    _arrays((a, "a", g.dtype, (rows, width)))
+    _on_device(("g", g), ("u", u))
     _check("nf4_swiglu", load().nf4_swiglu(_ptr(g), _ptr(u), _DT[g.dtype], rows, width, ld, _ptr(a),
                                            _stream(g.device)))
     return a
@@ -796,10 +810,11 @@ def swiglu_bwd(da, g, u, dg=None, du=None):
         if ld != width:
             raise ValueError("dg and du must be given when g and u are strided")
         dg, du = torch.empty_like(g), torch.empty_like(u)
-    if _gu_stride(dg, du)[2] != ld:
-        raise ValueError("dg, du must have the row stride of g, u")
-    if not da.is_contiguous() or da.shape != g.shape:
-        raise ValueError("da must be a dense [rows, width] array")
+    if dg is None or du is None or dg.shape != g.shape or _gu_stride(dg, du, ("dg", "du"))[2] != ld:
+        raise ValueError("dg, du must have the shape and row stride of g, u")
+    _same_dtype(g.dtype, ("dg", dg))
+    _arrays((da, "da", g.dtype, (rows, width)))
+    _on_device(("g", g), ("u", u), ("dg", dg), ("du", du))
     _check("nf4_swiglu_bwd", load().nf4_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), _DT[g.dtype], rows, width, ld,
                                                    _ptr(dg), _ptr(du), _stream(g.device)))
     return dg, du

@@ -202,6 +202,52 @@ def test_wide_rank_side_product_workspace(lib):
     assert L.nf4_linear_workspace_bytes(8192, 14336, 4096, 32, 1) == L.nf4_linear_workspace_bytes(8192, 14336, 4096, 0, 1)
 
 
+def test_strided_decoder_ops_reject_bad_arrays(lib):
+    """Rotary, attention and SwiGLU accept column blocks of a wider array (one
+    shared row stride) and check every shape, row count, dtype and stride on
+    the host before the device check: a malformed call is a ValueError naming
+    the array, a well-formed one (host tensors here) stops at the device."""
+    import torch
+    _, m = lib
+    S, hq, hkv, d = 6, 4, 2, 16
+    qkv = torch.zeros(S, (hq + 2 * hkv) * d, dtype=torch.bfloat16)
+    q, k, v = qkv[:, :hq * d], qkv[:, hq * d:(hq + hkv) * d], qkv[:, (hq + hkv) * d:]
+    o, lse = torch.zeros(S, hq * d, dtype=torch.bfloat16), torch.zeros(hq, S)
+
+    def raises(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    raises(m.rope_, q, hq + 1, d, 1e4, match=r"x must be \[rows, 80\]")
+    raises(m.rope_, qkv[:, :hq * d], hq, d, 1e4, match="device")  # well-formed strided block
+    raises(m.attention_fwd, q, k, v[:5], hq, hkv, d, match="same number of rows")
+    raises(m.attention_fwd, q, k, v.contiguous(), hq, hkv, d, match="share one row stride")
+    raises(m.attention_fwd, q, k.float(), v, hq, hkv, d, match="k must be torch.bfloat16")
+    raises(m.attention_fwd, q, k, v, hq, hkv, d, o=torch.zeros(S, hq * d + 1, dtype=torch.bfloat16),
+           match="o must have shape")
+    raises(m.attention_fwd, q, k, v, hq, hkv, d, lse=torch.zeros(hq, S + 1), match="lse must have shape")
+    raises(m.attention_fwd, q, k, v, hq, hkv, d, o=o, lse=lse, match="device")
+    g = torch.zeros(S, 3 * hq * d, dtype=torch.bfloat16)
+    dq, dk, dv = g[:, :hq * d], g[:, hq * d:(hq + hkv) * d], g[:, (hq + hkv) * d:(hq + 2 * hkv) * d]
+    raises(m.attention_bwd, o, q, k, v, o, lse, hq, hkv, d, match="pass dq, dk, dv")
+    raises(m.attention_bwd, o, q, k, v, o, lse, hq, hkv, d, dq=dq, dk=dk, dv=dv, match="row stride")
+    raises(m.attention_bwd, o[:, 1:], q, k, v, o, lse, hq, hkv, d, dq=q, dk=k, dv=v, match="dout must have shape")
+    raises(m.attention_bwd, o, q, k, v, o, lse, hq, hkv, d, dq=q, dk=k, dv=v, delta=torch.zeros(hq + 1, S),
+           match="delta must have shape")
+    raises(m.attention_bwd, o, q, k, v, o, lse, hq, hkv, d, dq=q, dk=k, dv=v, match="device")
+    gu = torch.zeros(S, 2 * 40, dtype=torch.bfloat16)
+    gg, uu = gu[:, :40], gu[:, 40:]
+    raises(m.swiglu, gg, uu[:, :32], match="one shape")
+    raises(m.swiglu, gg, gu.float()[:, 40:], match="u must be torch.bfloat16")
+    raises(m.swiglu, gg, uu, a=torch.zeros(S, 41, dtype=torch.bfloat16), match="a must have shape")
+    raises(m.swiglu, gg, uu, match="device")
+    da = torch.zeros(S, 40, dtype=torch.bfloat16)
+    raises(m.swiglu_bwd, da, gg, uu, match="must be given when g and u are strided")
+    raises(m.swiglu_bwd, da, gg, uu, dg=gg[:, :32], du=uu[:, :32], match="shape and row stride")
+    raises(m.swiglu_bwd, da[:, 1:], gg, uu, dg=gg, du=uu, match="da must have shape")
+    raises(m.swiglu_bwd, da, gg, uu, dg=gg, du=uu, match="device")
+
+
 def test_small_kernel_offsets_stay_32_bit(lib):
     """The small-tile kernels keep per-lane activation offsets (tile row times
     reduction length) in 32 bits, so a reduction of 2^22 or more leaves the fast
