@@ -1253,13 +1253,20 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q * 4 >= M * C) return;
   f32x4 v = *reinterpret_cast<const f32x4*>(part + q * 4);
-  for (int p = 1; p < nsplit; ++p) {
-    const f32x4 u = *reinterpret_cast<const f32x4*>(part + (int64_t)p * M * C + q * 4);
-    v[0] += u[0];
-    v[1] += u[1];
-    v[2] += u[2];
-    v[3] += u[3];
-  }
+  // the other parts' loads are all in flight (at most 8 parts: predicated,
+  // not a chain of dependent loads), then added in part order
+  f32x4 u[7];
+#pragma unroll
+  for (int p = 1; p < 8; ++p)
+    u[p - 1] = p < nsplit ? *reinterpret_cast<const f32x4*>(part + (int64_t)p * M * C + q * 4) : f32x4{};
+#pragma unroll
+  for (int p = 1; p < 8; ++p)
+    if (p < nsplit) {
+      v[0] += u[p - 1][0];
+      v[1] += u[p - 1][1];
+      v[2] += u[p - 1][2];
+      v[3] += u[p - 1][3];
+    }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   u32x2 o;
   o[0] = pack_bf16x2(v[0], v[1]);

@@ -461,11 +461,181 @@ __global__ __launch_bounds__(256) void k_side_wide(const __bf16* __restrict__ L,
     }
 }
 
+// Side product for bf16 activations as a split skinny GEMM, streamed: workgroup
+// (b, ks, z) covers rows 128 b .. + 127, reduction indices [ks kc, ks kc + kc)
+// and the R = 16 RT ranks from R z. Per 64-wide reduction step the workgroup
+// stages the factor block (R ranks x 64 indices, fp32) once, as three bf16
+// parts whose sum is exact, in LDS where all four waves read them (so the split
+// and the factor traffic are paid once per 128 rows); wave w multiplies rows
+// 32 w .. + 31 (two 16-row tiles, activations loaded directly as 8 consecutive
+// indices per lane) on the 16x16x32 bf16 MFMA. Forward (A [r][I]) the parts are
+// stored [rank][index] and read with 16-byte loads; backward (B [I][r]) they
+// are stored [index][rank] and gathered with transposing reads. The loads of
+// the next D steps are in flight while a step multiplies (a ring of register
+// sets, each refilled right after its step's barrier). Each split writes its
+// sums to out + ks * part_stride; with more than one split k_side_sum adds them
+// in split order.
+template <bool BWD, int RT>
+__global__ __launch_bounds__(256, 2) void k_side_tile(const __bf16* __restrict__ L, int64_t M, int64_t I,
+                                                      const float* __restrict__ fac, int r, int64_t kc,
+                                                      float* __restrict__ out, int64_t part_stride) {
+  constexpr int R = 16 * RT;                  // ranks per workgroup
+  constexpr int D = 3;                        // steps whose loads are in flight
+  constexpr int FP = BWD ? R + 8 : 64 + 8;    // bf16 pitch of a staged factor row
+  constexpr int FSZ = BWD ? 64 * FP : R * FP;  // bf16 per part and stage
+  __shared__ __attribute__((aligned(16))) __bf16 fp[2][3][FSZ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t mw = (int64_t)blockIdx.x * 128 + 32 * wave;  // first row of this wave
+  const int64_t kb = (int64_t)blockIdx.y * kc, ke = (kb + kc < I) ? kb + kc : I;
+  const int rho0 = R * (int)blockIdx.z;
+  // factor staging: float4 q = tid + 256 u (u < RT) of the block; forward rank
+  // q / 16, indices 4 (q % 16) ..; backward index q / (R / 4), ranks 4 (q % (R / 4)) ..
+  auto fidx = [&](int u, int& i, int& rho) __attribute__((always_inline)) {
+    const int q = tid + 256 * u;
+    if (BWD) {
+      i = q / (R / 4);
+      rho = 4 * (q % (R / 4));
+    } else {
+      rho = q / 16;
+      i = 4 * (q % 16);
+    }
+  };
+  struct Set {
+    uint4 lv[2][2];  // [row tile][32-wide half of the step]
+    float4 fv[RT];
+  };
+  // Every 16-byte piece (I % 8 == 0, r % 4 == 0, 16-byte aligned arrays: the
+  // caller checks) is wholly in range or wholly out, so each is one
+  // unconditional load from a clamped address, masked at its use.
+  auto load = [&](int64_t k0, Set& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t m = mw + 16 * rt + row, mc = m < M ? m : M - 1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t i = k0 + 32 * h + 8 * kg;
+        S.lv[rt][h] = *reinterpret_cast<const uint4*>(L + mc * I + (i < ke ? i : kb));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      int il, rl;
+      fidx(u, il, rl);
+      const int64_t i = k0 + il;
+      const int rho = rho0 + rl;
+      const float* q = BWD ? fac + (i < ke ? i : kb) * r + (rho < r ? rho : 0)
+                           : fac + (int64_t)(rho < r ? rho : 0) * I + (i < ke ? i : kb);
+      S.fv[u] = *reinterpret_cast<const float4*>(q);
+    }
+  };
+  f32x4 acc[2][RT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[rt][t] = f32x4{};
+  auto step = [&](int64_t k0, Set& S, int buf) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    // the factor block's three exact bf16 parts into LDS stage buf
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      int il, rl;
+      fidx(u, il, rl);
+      const bool ok = k0 + il < ke && rho0 + rl < r;
+      const float v[4] = {S.fv[u].x, S.fv[u].y, S.fv[u].z, S.fv[u].w};
+      uint16_t h[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = ok ? v[e] : 0.0f;
+        const __bf16 a1 = (__bf16)x;
+        const float r1 = x - (float)a1;
+        const __bf16 a2 = (__bf16)r1;
+        const __bf16 a3 = (__bf16)(r1 - (float)a2);
+        h[0][e] = __builtin_bit_cast(uint16_t, a1);
+        h[1][e] = __builtin_bit_cast(uint16_t, a2);
+        h[2][e] = __builtin_bit_cast(uint16_t, a3);
+      }
+      const int off = BWD ? il * FP + rl : rl * FP + il;
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+        *reinterpret_cast<uint2*>(&fp[buf][pp][off]) =
+            make_uint2(h[pp][0] | ((uint32_t)h[pp][1] << 16), h[pp][2] | ((uint32_t)h[pp][3] << 16));
+    }
+    // this step's activations, zeroed out of range (integer masks, so that no
+    // branch waits for a load), copied out before the set is refilled
+    bf16x8 l[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool ok = mw + 16 * rt + row < M && k0 + 32 * h + 8 * kg < ke;
+        const uint32_t mk = ok ? 0xffffffffu : 0u;
+        const uint4 v = S.lv[rt][h];
+        l[rt][h] = __builtin_bit_cast(bf16x8, make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk));
+      }
+    __syncthreads();
+    load(k0 + 64 * D, S);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int pp = 2; pp >= 0; --pp) {
+          bf16x8 f;
+          if (BWD) {
+            bf16x4l v[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              v[hh] = lds_tr16(&fp[buf][pp][(32 * h + 8 * kg + 4 * hh + (row >> 2)) * FP + 16 * t + 4 * (row & 3)]);
+            f = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+          } else {
+            f = *reinterpret_cast<const bf16x8*>(&fp[buf][pp][(16 * t + row) * FP + 32 * h + 8 * kg]);
+          }
+          acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l[0][h], f, acc[0][t], 0, 0, 0);
+          acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l[1][h], f, acc[1][t], 0, 0, 0);
+        }
+  };
+  // whole rounds of D steps (no early exit, so the load waits are exact on
+  // the back edge), then the last steps % D; the loads of the first D steps
+  // are issued in order
+  const int64_t steps = (ke - kb + 63) / 64, rounds = steps / D;
+  Set S[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load(kb + 64 * d, S[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int64_t k0 = kb;
+  int par = 0;
+  for (int64_t i = 0; i < rounds; ++i) {
+#pragma unroll
+    for (int d = 0; d < D; ++d, k0 += 64, par ^= 1) step(k0, S[d], par);
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    if (d >= steps - rounds * D) break;
+    step(k0, S[d], par);
+    k0 += 64;
+    par ^= 1;
+  }
+  // accumulator element j of lane l: row 4 (l / 16) + j of the tile, rank 16 t + l % 16
+  float* o = out + (int64_t)blockIdx.y * part_stride;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int rho = rho0 + 16 * t + row;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = mw + 16 * rt + 4 * kg + j;
+        if (m < M && rho < r) o[m * r + rho] = acc[rt][t][j];
+      }
+    }
+}
+
 // out[e] = sum over splits ks = 0, 1, ... in order of part[ks * n + e]; four
 // consecutive elements per thread (n % 4 == 0 and 16-byte aligned arrays: the
-// caller checks) or one. The parts are loaded eight at a time before they are
-// added (in split order), so a short sum over many splits is not a chain of
-// dependent loads.
+// caller checks) or one.
 template <bool VEC4>
 __global__ __launch_bounds__(256) void k_side_sum(const float* __restrict__ part, int64_t n, int splits,
                                                   float* __restrict__ out) {
@@ -475,15 +645,16 @@ __global__ __launch_bounds__(256) void k_side_sum(const float* __restrict__ part
   const vec* p = reinterpret_cast<const vec*>(part + e);
   const int64_t nv = n / (VEC4 ? 4 : 1);  // parts apart, in vectors
   vec v = p[0];
-  int ks = 1;
-  for (; ks + 8 <= splits; ks += 8) {
-    vec w[8];
+  // sixteen parts' loads in flight per group (a shorter last group is
+  // predicated, not a chain of dependent loads), added in split order
+  for (int ks = 1; ks < splits; ks += 16) {
+    vec w[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = p[(int64_t)(ks + u) * nv];
+    for (int u = 0; u < 16; ++u) w[u] = ks + u < splits ? p[(int64_t)(ks + u) * nv] : vec{};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v += w[u];
+    for (int u = 0; u < 16; ++u)
+      if (ks + u < splits) v += w[u];
   }
-  for (; ks < splits; ++ks) v += p[(int64_t)ks * nv];
   *reinterpret_cast<vec*>(out + e) = v;
 }
 
@@ -604,8 +775,8 @@ __global__ __launch_bounds__(256) void k_lora_partial(const float* __restrict__ 
 // P[m .. m + 31][0 .. 31] (64-byte rows) in LDS; both MFMA operands need 8
 // consecutive tokens per lane and are gathered with ds_read_b64_tr_b16 (within
 // a 16-lane group, lane i receives element i % 4 of the 4-element pieces
-// addressed by lanes 4 e + i / 4). The next step's loads are in flight while
-// the current one multiplies.
+// addressed by lanes 4 e + i / 4). The loads of the next two or three steps
+// are in flight while the current one multiplies.
 constexpr int LQP = 288;  // bf16 per staged Q row
 constexpr int LPP = 32;   // bf16 per staged P row
 
@@ -624,9 +795,14 @@ struct LoraProb {
 // Both reductions of one lora_grad call (dB's and dA's) share the grid:
 // workgroups [0, blocks0) take problem 0, the rest problem 1; inside a problem
 // workgroup b covers column tile b % col_tiles of chunk b / col_tiles.
-template <int RB>
-__global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int64_t blocks0, int64_t M, int r,
-                                                   int rho0) {
+template <int RB, bool FAST>
+__global__ __launch_bounds__(256, RB <= 2 ? 2 : 1) void k_lora_mfma(LoraProb p0, LoraProb p1, int64_t blocks0,
+                                                                    int64_t M, int r, int rho0) {
+  // D token steps are loaded ahead into a ring of register sets, so that D
+  // steps' loads are in flight while one step multiplies (two for 128 ranks
+  // and for the element-wise loads, within the registers of two waves per
+  // SIMD up to 64 ranks; four measured slower than three).
+  constexpr int D = (RB == 4 || !FAST) ? 2 : 3;
   __shared__ __attribute__((aligned(16))) __bf16 qs[2][32 * LQP];
   __shared__ __attribute__((aligned(16))) __bf16 pls[2][RB][3][32 * LPP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -641,70 +817,64 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
   const int64_t j0 = (b % pr.col_tiles) * 256;
   const int64_t c = b / pr.col_tiles;
   const int64_t mb = c * chunk, me = (mb + chunk < M) ? mb + chunk : M;
-  const bool vecq = (J % 8) == 0;
   // staging roles: Q row 8 u + tid / 32 (u = 0..3), 16-byte chunk tid % 32;
   // P row tid / 8, ranks 4 (tid % 8) .. + 3
   const int qrow = tid >> 5, qch = tid & 31, prow = tid >> 3, prho = 4 * (tid & 7);
-  uint4 qv[4];
-  float pv[RB][4];
-  // full steps (32 tokens in the chunk, 256 columns in range, 16-byte rows)
-  // load without per-lane guards, so no load waits on another
-  const bool fullq = vecq && j0 + 256 <= J;
-  const bool fullp = (r % 4) == 0 && rho0 + 32 * RB <= r && (reinterpret_cast<uintptr_t>(P) % 16) == 0;
-  auto load = [&](int64_t m) __attribute__((always_inline)) {
-    if (m + 32 <= me && fullq) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        qv[u] = *reinterpret_cast<const uint4*>(Q + (m + 8 * u + qrow) * J + j0 + 8 * qch);
-    } else {
+  const int64_t jq = j0 + 8 * qch;
+  struct Set {
+    uint4 q[4];
+    float p[RB][4];
+  };
+  // FAST (J % 8 == 0, r % 4 == 0, 16-byte aligned Q and P): every 16-byte
+  // piece is wholly in range or wholly out, so each is one unconditional load
+  // from a clamped address, zeroed when it is staged if out of range (no load
+  // sits behind a branch, so the waits for one set leave the later sets in
+  // flight). Otherwise element-wise guards.
+  auto load = [&](int64_t m, Set& S) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t mm = m + 8 * u + qrow;
-      const int64_t j = j0 + 8 * qch;
-      if (mm < me && vecq && j + 8 <= J) {
-        qv[u] = *reinterpret_cast<const uint4*>(Q + mm * J + j);
+      if constexpr (FAST) {
+        S.q[u] = *reinterpret_cast<const uint4*>(Q + (mm < me ? mm : me - 1) * J + (jq < J ? jq : 0));
       } else {
         uint16_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          h[e] = (mm < me && j + e < J) ? __builtin_bit_cast(uint16_t, Q[mm * J + j + e]) : (uint16_t)0;
-        qv[u] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16),
-                           h[6] | ((uint32_t)h[7] << 16));
+          h[e] = (mm < me && jq + e < J) ? __builtin_bit_cast(uint16_t, Q[mm * J + jq + e]) : (uint16_t)0;
+        S.q[u] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                            h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
       }
-    }
     }
     const int64_t mm = m + prow;
-    if (m + 32 <= me && fullp) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float4 v = *reinterpret_cast<const float4*>(P + mm * r + rho0 + 32 * rb + prho);
-        pv[rb][0] = v.x; pv[rb][1] = v.y; pv[rb][2] = v.z; pv[rb][3] = v.w;
-      }
-    } else {
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho = rho0 + 32 * rb + prho;
+      if constexpr (FAST) {
+        const float4 v = *reinterpret_cast<const float4*>(P + (mm < me ? mm : me - 1) * r + (rho < r ? rho : 0));
+        S.p[rb][0] = v.x; S.p[rb][1] = v.y; S.p[rb][2] = v.z; S.p[rb][3] = v.w;
+      } else {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rho = rho0 + 32 * rb + prho + e;
-        pv[rb][e] = (mm < me && rho < r) ? P[mm * r + rho] : 0.0f;
+        for (int e = 0; e < 4; ++e) S.p[rb][e] = (mm < me && rho + e < r) ? P[mm * r + rho + e] : 0.0f;
       }
     }
   };
-  f32x16 acc[RB][2];
+  // the register set of step m into LDS stage buf: Q as loaded, P as the
+  // three bf16 parts of each value
+  auto stage = [&](int64_t m, const Set& S, int buf) __attribute__((always_inline)) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
-  int buf = 0;
-  if (mb < me) load(mb);
-  for (int64_t m = mb; m < me; m += 32, buf ^= 1) {
-    // stage this step
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&qs[buf][(8 * u + qrow) * LQP + 8 * qch]) = qv[u];
+    for (int u = 0; u < 4; ++u) {
+      // (an integer mask, not a select, so that no branch waits for the load)
+      const uint32_t mk = (!FAST || (m + 8 * u + qrow < me && jq < J)) ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(&qs[buf][(8 * u + qrow) * LQP + 8 * qch]) =
+          make_uint4(S.q[u].x & mk, S.q[u].y & mk, S.q[u].z & mk, S.q[u].w & mk);
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      const bool ok = !FAST || (m + prow < me && rho0 + 32 * rb + prho < r);
       uint16_t h[3][4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = pv[rb][e];
+        const float v = ok ? S.p[rb][e] : 0.0f;
         const __bf16 a1 = (__bf16)v;
         const float r1 = v - (float)a1;
         const __bf16 a2 = (__bf16)r1;
@@ -718,8 +888,11 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
         *reinterpret_cast<uint2*>(&pls[buf][rb][pp][prow * LPP + prho]) =
             make_uint2(h[pp][0] | ((uint32_t)h[pp][1] << 16), h[pp][2] | ((uint32_t)h[pp][3] << 16));
     }
-    __syncthreads();
-    if (m + 32 < me) load(m + 32);
+  };
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
+  auto multiply = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 b[2];
@@ -752,6 +925,42 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraProb p0, LoraProb p1, int
         }
       }
     }
+  };
+  // Step i of the chunk (tokens mb + 32 i ..) stages set i % D into LDS stage
+  // i % 2, then refills that set with step i + D while it multiplies. Every
+  // load is unconditional (loads of steps past the chunk read clamped rows
+  // that are never staged, or zeros), so the wait before each stage counts
+  // exactly the later sets' loads.
+  // (scheduling barriers keep the sets' loads in step order: the wait before
+  // set d's stage counts the loads issued after it)
+  Set S[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load(mb + 32 * d, S[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto step = [&](int64_t mm, Set& St) __attribute__((always_inline)) {
+    // (nothing is scheduled across step boundaries: staging a later set's
+    // registers early would wait for its loads)
+    __builtin_amdgcn_sched_barrier(0);
+    const int buf = (int)(((mm - mb) >> 5) & 1);
+    stage(mm, St, buf);
+    __syncthreads();
+    load(mm + 32 * D, St);
+    multiply(buf);
+  };
+  // whole rounds of D steps (a loop without early exits, so that the wait
+  // counts hold on its back edge), then the last nsteps % D steps
+  const int64_t nsteps = mb < me ? (me - mb + 31) / 32 : 0, rounds = nsteps / D;
+  int64_t m = mb;
+  for (int64_t i = 0; i < rounds; ++i, m += 32 * D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(m + 32 * d, S[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    if (d >= nsteps - rounds * D) break;
+    step(m + 32 * d, S[d]);
   }
   // element e of accumulator (rb, t): rank rho0 + 32 rb + 8 (e / 4) + 4 (lane / 32) + e % 4, column
   // 64 wave + 32 t + lane % 32
@@ -793,16 +1002,16 @@ __global__ __launch_bounds__(256) void k_lora_combine(LoraSum q0, LoraSum q1, in
   const float* p = partial + rho * J + j;
   const int64_t cs = (int64_t)r * J;  // stride between chunks
   float sum = 0.0f;
-  int64_t c = 0;
-  // eight chunks of loads in flight; the sum stays in chunk order
-  for (; c + 8 <= chunks; c += 8) {
-    float v[8];
+  // sixteen chunks' loads in flight (a shorter last group is predicated, not
+  // a chain of dependent loads); the sum stays in chunk order
+  for (int64_t c = 0; c < chunks; c += 16) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(c + u) * cs];
+    for (int u = 0; u < 16; ++u) v[u] = c + u < chunks ? p[(c + u) * cs] : 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum += v[u];
+    for (int u = 0; u < 16; ++u)
+      if (c + u < chunks) sum += v[u];
   }
-  for (; c < chunks; ++c) sum += p[c * cs];
   const float v = s * sum;
   if (transpose_out)
     out[j * r + rho] = v;
@@ -837,6 +1046,33 @@ SideSplit side_split_plan(int64_t M, int64_t I, int32_t r) {
   return {ceil_div(I, kc), kc};
 }
 
+// Split of the streamed side product (k_side_tile): about 512 workgroups of 128
+// rows x 16 ranks, at least 4 steps of 64 per split. It takes reductions of
+// 8192 or more at ranks up to 16 (23 us against 30 us for k_side_wide, which
+// always multiplies 64 ranks, on a 4096 x 14336 input); shorter reductions
+// stay on k_side_bf16 (one launch, no partial sums: 14 us against 10 us + the
+// 4.6 us sum at 4096 x 4096), larger ranks on k_side_wide.
+bool side_tile_shape(int64_t I, int32_t r) { return I % 8 == 0 && r % 4 == 0 && r <= 16 && I >= 8192; }
+SideSplit side_tile_plan(int64_t M, int64_t I, int32_t r) {
+  (void)r;
+  const int64_t tiles = ceil_div(M, 128), steps = ceil_div(I, 64);
+  int64_t ks = ceil_div(512, tiles);
+  const int64_t maxks = steps / 4 > 1 ? steps / 4 : 1;
+  if (ks > maxks) ks = maxks;
+  const int64_t kc = ceil_div(steps, ks) * 64;
+  return {ceil_div(I, kc), kc};
+}
+
+// sum of the parts of a split side product, in split order
+void launch_side_sum(const float* part, int64_t splits, int64_t n, float* out, hipStream_t st) {
+  if (n % 4 == 0 && aligned(out, 16) && aligned(part, 16))
+    hipLaunchKernelGGL(k_side_sum<true>, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256), 0, st, part, n, (int)splits,
+                       out);
+  else
+    hipLaunchKernelGGL(k_side_sum<false>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, part, n, (int)splits,
+                       out);
+}
+
 // Adapter side product (T = x A^T or U = dY B), needed by the main kernel's epilogue.
 template <typename T>
 void launch_side(const LinearArgs& g, hipStream_t st) {
@@ -846,6 +1082,18 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
   const dim3 sg((unsigned)ceil_div(g.M, SR));
   if constexpr (sizeof(T) == 2) {
     const float* fac = g.backward ? g.B : g.A;
+    if (side_tile_shape(I, g.r) && aligned(a, 16) && aligned(fac, 16)) {
+      const SideSplit sp = side_tile_plan(g.M, I, g.r);
+      const dim3 grid((unsigned)ceil_div(g.M, 128), (unsigned)sp.splits, 1);
+      float* dst = sp.splits > 1 ? g.side_part : g.side;
+      const int64_t stride = g.M * (int64_t)g.r;
+      if (g.backward)
+        hipLaunchKernelGGL((k_side_tile<true, 1>), grid, dim3(256), 0, st, a, g.M, I, fac, g.r, sp.kc, dst, stride);
+      else
+        hipLaunchKernelGGL((k_side_tile<false, 1>), grid, dim3(256), 0, st, a, g.M, I, fac, g.r, sp.kc, dst, stride);
+      if (sp.splits > 1) launch_side_sum(g.side_part, sp.splits, stride, g.side, st);
+      return;
+    }
     if (side_split_path(g.M, I, g.r)) {
       const SideSplit sp = side_split_plan(g.M, I, g.r);
       const dim3 grid((unsigned)ceil_div(g.M, 128), (unsigned)sp.splits, (unsigned)ceil_div((int64_t)g.r, 64));
@@ -859,14 +1107,7 @@ void launch_side(const LinearArgs& g, hipStream_t st) {
       else if (fast) NF4_WIDE(false, true);
       else NF4_WIDE(false, false);
 #undef NF4_WIDE
-      if (sp.splits > 1) {
-        if (stride % 4 == 0 && aligned(g.side, 16) && aligned(g.side_part, 16))
-          hipLaunchKernelGGL(k_side_sum<true>, dim3((unsigned)ceil_div(stride / 4, 256)), dim3(256), 0, st,
-                             g.side_part, stride, (int)sp.splits, g.side);
-        else
-          hipLaunchKernelGGL(k_side_sum<false>, dim3((unsigned)ceil_div(stride, 256)), dim3(256), 0, st, g.side_part,
-                             stride, (int)sp.splits, g.side);
-      }
+      if (sp.splits > 1) launch_side_sum(g.side_part, sp.splits, stride, g.side, st);
       return;
     }
 #define NF4_SIDE(BWD, RT) \
@@ -910,9 +1151,15 @@ int run_linear_general(const LinearArgs& g, hipStream_t st) {
 }  // namespace
 
 int64_t side_split_ws_bytes(int64_t M, int64_t I, int32_t r) {
-  if (r <= 0 || !side_split_path(M, I, r)) return 0;
-  const SideSplit sp = side_split_plan(M, I, r);
-  return sp.splits > 1 ? (int64_t)round_up(sizeof(float) * (size_t)(sp.splits * M * r), 256) : 0;
+  if (r <= 0) return 0;
+  // the larger of the two plans (which one runs also depends on the arrays' alignment)
+  int64_t splits = 1;
+  if (side_tile_shape(I, r)) splits = side_tile_plan(M, I, r).splits;
+  if (side_split_path(M, I, r)) {
+    const int64_t s2 = side_split_plan(M, I, r).splits;
+    if (s2 > splits) splits = s2;
+  }
+  return splits > 1 ? (int64_t)round_up(sizeof(float) * (size_t)(splits * M * r), 256) : 0;
 }
 
 int launch_side_product(const void* L, nf4_dtype dt, int64_t M, int64_t I, const float* fac, int32_t r, bool backward,
@@ -1012,15 +1259,20 @@ void lora_grad_mfma(const __bf16* x, const __bf16* dy, int64_t M, int64_t K, int
   // launches for the ranks past 128)
   const LoraProb& p0 = dA ? pa : pb;
   const int64_t blocks0 = dA ? blocksA : blocksB;
+  const bool fast = N % 8 == 0 && r % 4 == 0 && aligned(dy, 16) && aligned(t, 16) &&
+                    (!dA || (K % 8 == 0 && aligned(x, 16) && aligned(u, 16)));
   for (int r0 = 0; r0 < r; r0 += 128) {
     const int left = r - r0;
     const dim3 grid((unsigned)(blocksB + blocksA));
-    if (left <= 32)
-      hipLaunchKernelGGL(k_lora_mfma<1>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
-    else if (left <= 64)
-      hipLaunchKernelGGL(k_lora_mfma<2>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
-    else
-      hipLaunchKernelGGL(k_lora_mfma<4>, grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0);
+#define NF4_LORA(RB, FAST) hipLaunchKernelGGL((k_lora_mfma<RB, FAST>), grid, dim3(256), 0, st, p0, pb, blocks0, M, r, r0)
+    if (left <= 32) {
+      if (fast) NF4_LORA(1, true); else NF4_LORA(1, false);
+    } else if (left <= 64) {
+      if (fast) NF4_LORA(2, true); else NF4_LORA(2, false);
+    } else {
+      if (fast) NF4_LORA(4, true); else NF4_LORA(4, false);
+    }
+#undef NF4_LORA
   }
   const LoraSum qb{partB, ceil_div(M, chB), N, true, dB};
   const LoraSum qa{partA, ceil_div(M, chA), K, false, dA};

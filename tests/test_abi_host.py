@@ -168,10 +168,13 @@ def test_wide_rank_side_product_workspace(lib):
     ranks beyond 32, for reductions of 8192 or more, and when fewer than 4096
     token rows meet a reduction of at least 2048 (16-row workgroups would leave
     most of the chip idle): parts of at least 128 indices, about 512 workgroups of 128
-    rows x 64 ranks in all; the workspace holds one M x r fp32 partial product
-    per part, and lora_grad's recomputation takes the larger of its two."""
+    rows x 64 ranks in all. Reductions of 8192 or more (a multiple of 8) at
+    ranks up to 16 (a multiple of 4) may instead take the streamed kernel:
+    parts of at least 256 indices, about 512 workgroups of 128 rows. The
+    workspace holds one M x r fp32 partial product per part of the larger
+    plan, and lora_grad's recomputation takes the larger of its two."""
     L, _ = lib
-    def parts(M, I, r):
+    def wide_parts(M, I, r):
         if not (r > 32 or I >= 8192 or (-(-M // 16) < 256 and I >= 2048)):
             return 1
         tiles = -(-M // 128) * -(-r // 64)
@@ -179,6 +182,14 @@ def test_wide_rank_side_product_workspace(lib):
         ks = min(-(-512 // tiles), max(steps // 4, 1))
         kc = -(-steps // ks) * 32
         return -(-I // kc)
+    def tile_parts(M, I, r):
+        if not (I % 8 == 0 and r % 4 == 0 and r <= 16 and I >= 8192):
+            return 1
+        steps = -(-I // 64)
+        ks = min(-(-512 // -(-M // 128)), max(steps // 4, 1))
+        kc = -(-steps // ks) * 64
+        return -(-I // kc)
+    parts = lambda M, I, r: max(wide_parts(M, I, r), tile_parts(M, I, r))
     rnd = lambda b: (b + 255) // 256 * 256
     cases = ((8192, 14336, 4096, 64), (4096, 4096, 4096, 100), (512, 4096, 14336, 256), (64, 576, 192, 33),
              (512, 4096, 1024, 16), (512, 14336, 4096, 8), (4080, 4096, 4096, 32), (512, 576, 1536, 8),
@@ -198,6 +209,7 @@ def test_wide_rank_side_product_workspace(lib):
     # the split engages where the model says it does
     assert parts(512, 4096, 16) > 1 and parts(512, 1024, 16) == 1 and parts(4096, 4096, 16) == 1
     assert parts(4096, 14336, 16) > 1 and parts(4096, 8191, 16) == 1
+    assert tile_parts(4096, 14336, 16) == 16 and tile_parts(512, 14336, 8) == 56 and wide_parts(512, 14336, 8) == 112
     # 32 and below at 4096 or more tokens over a reduction under 8192: no split
     assert L.nf4_linear_workspace_bytes(8192, 14336, 4096, 32, 1) == L.nf4_linear_workspace_bytes(8192, 14336, 4096, 0, 1)
 

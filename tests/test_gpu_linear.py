@@ -353,6 +353,29 @@ def test_side_products_optional_and_recomputed(gpu, orc, M, K, N, r):
     assert_close(dB_fa.cpu().numpy(), dB_ref, "f32", "LoRA-FA dB (T recomputed)")
 
 
+@pytest.mark.parametrize("M,I,r", [(1000, 8200, 16), (1000, 8200, 4), (130, 16384, 12), (4096, 14336, 16),
+                                   (513, 8192, 8)])
+def test_side_product_streamed_split(gpu, orc, M, I, r):
+    """Reductions of 8192 or more at ranks up to 16 take the streamed split
+    side product (128-row workgroups, 64-wide steps, partial sums added in
+    split order): T = x A^T and U = dY B, whole, against the oracle, with ragged
+    rows, a last step shorter than 64 and ranks below 16; run to run bitwise."""
+    print(f"[linear] streamed side product M={M} I={I} r={r}", flush=True)
+    cf = make_case(M, I, 64, r, torch.bfloat16, seed=M + I)
+    cb = make_case(M, 64, I, r, torch.bfloat16, seed=M + I + 1)
+    s = gpu.lora_scale(32.0, r)
+    Wf = gpu.quantize(cf["W"], True)
+    Wb = gpu.quantize(cb["W"], True)
+    _, T = gpu.linear_fwd(cf["x"], Wf, cf["A"], cf["B"], s)
+    _, T2 = gpu.linear_fwd(cf["x"], Wf, cf["A"], cf["B"], s)
+    _, U = gpu.linear_bwd_input(cb["dy"], Wb, cb["A"], cb["B"], s)
+    _, U2 = gpu.linear_bwd_input(cb["dy"], Wb, cb["A"], cb["B"], s)
+    torch.cuda.synchronize()
+    assert torch.equal(T.view(torch.int32), T2.view(torch.int32)) and torch.equal(U.view(torch.int32), U2.view(torch.int32))
+    assert_close(T.cpu().numpy(), orc.lora_down(to_np(cf["x"]), cf["A"].cpu().numpy()), "f32", "T")
+    assert_close(U.cpu().numpy(), orc.lora_up_grad(to_np(cb["dy"]), cb["B"].cpu().numpy()), "f32", "U")
+
+
 @pytest.mark.parametrize("M,K,N,r", [(300, 1024, 576, 64), (129, 576, 1536, 100), (200, 640, 512, 256),
                                      (64, 256, 320, 33), (40, 448, 192, 128)])
 def test_large_ranks(gpu, orc, M, K, N, r):
