@@ -115,6 +115,13 @@ __device__ __forceinline__ bf16x8 decode_word(uint32_t w, const Bf16Table& t) {
   return __builtin_bit_cast(bf16x8, d);
 }
 
+// A workgroup-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Tile coordinates of workgroup b: a contiguous run of tiles per XCD (workgroups
 // are dealt to the 8 XCDs round-robin), then groups of GM token-tiles walked
 // token-tile-fastest.
@@ -1049,7 +1056,10 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   int64_t mt, ct;
   const int64_t xb = xcd_order(blockIdx.x, gridDim.x);
   group_map(tbase + (MS == 4 ? xb : xb >> 1), MT, CT, mt, ct);
-  const int64_t m0 = mt * GT + (MS == 4 ? 0 : BM * (xb & 1)), c0 = ct * GT;
+  // The tile origin is workgroup-uniform; stated explicitly (scalar registers),
+  // so that the activation loads' buffer resource is scalar too (otherwise the
+  // compiler may wrap each of those loads in a loop over distinct lane values).
+  const int64_t m0 = uniform64(mt * GT + (MS == 4 ? 0 : BM * (xb & 1))), c0 = uniform64(ct * GT);
   const int64_t KT = R / 64, KB = K / 64;
   if (DQ && tid < 256) d8s[tid] = dyn8_value((uint32_t)tid);
   const float mu = DQ ? w.offset[0] : 0.0f;
