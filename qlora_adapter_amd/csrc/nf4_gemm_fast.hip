@@ -68,6 +68,31 @@ __device__ __forceinline__ Bf16Table build_table(float a) {
   return t;
 }
 
+// The same table built by two adjacent lanes that decode the same block: the
+// lane of parity p multiplies the scale by its own eight code values cs =
+// entries 8p .. 8p + 7 (per-lane constants), splits them into byte planes and
+// takes the whole table from the pair through DPP quad permutations (the even
+// lane's planes give entries 0..7, the odd lane's 8..15). Identical entries to
+// build_table (each is the same rounded product). Every lane of the wave must
+// be active.
+__device__ __forceinline__ Bf16Table build_table_pair(float a, const float (&cs)[8]) {
+  uint32_t P[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) P[i] = pack_bf16x2(__fmul_rn(cs[2 * i], a), __fmul_rn(cs[2 * i + 1], a));
+  Bf16Table t;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int lo = (int)__builtin_amdgcn_perm(P[2 * j + 1], P[2 * j], 0x06040200u);
+    const int hi = (int)__builtin_amdgcn_perm(P[2 * j + 1], P[2 * j], 0x07050301u);
+    // quad_perm [0,0,2,2]: the even lane of each pair; [1,1,3,3]: the odd lane
+    t.lo[j] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0xA0, 0xF, 0xF, false);
+    t.lo[2 + j] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0xF5, 0xF, 0xF, false);
+    t.hi[j] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0xA0, 0xF, 0xF, false);
+    t.hi[2 + j] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0xF5, 0xF, 0xF, false);
+  }
+  return t;
+}
+
 // Table lookup of four 4-bit indices held one per byte: sel = index & 7 per byte,
 // hi8 = 0xFF in the bytes whose index is >= 8.
 __device__ __forceinline__ void lookup4(const Bf16Table& t, uint32_t sel, uint32_t hi8, uint32_t& lo, uint32_t& hi) {
@@ -104,14 +129,25 @@ __device__ __forceinline__ u32x4 decode_word_eo(uint32_t w, const Bf16Table& t) 
   return d;
 }
 
-// Decode one 32-bit code word into 8 bf16 values in weight order.
+// Decode one 32-bit code word into 8 bf16 values in weight order. The lookups
+// take weights 0 1 4 5 and 2 3 6 7 together (index bytes from w and w >> 4,
+// bit-3 masks from w, w << 4, w << 8 and w << 12 through the sign-replicating
+// selectors), so that one interleave of each pair's low and high bytes gives
+// the weight order directly.
 __device__ __forceinline__ bf16x8 decode_word(uint32_t w, const Bf16Table& t) {
-  const u32x4 e = decode_word_eo(w, t);
+  const uint32_t sh = w >> 4;
+  const uint32_t sel_a = __builtin_amdgcn_perm(sh, w, 0x02060004u) & 0x07070707u;  // weights 0 1 4 5
+  const uint32_t sel_b = __builtin_amdgcn_perm(sh, w, 0x03070105u) & 0x07070707u;  // weights 2 3 6 7
+  const uint32_t msk_a = __builtin_amdgcn_perm(w << 12, w << 8, 0x0B090A08u);     // bits 7 3 23 19
+  const uint32_t msk_b = __builtin_amdgcn_perm(w << 4, w, 0x0B090A08u);           // bits 15 11 31 27
+  uint32_t al, ah, bl, bh;
+  lookup4(t, sel_a, msk_a, al, ah);
+  lookup4(t, sel_b, msk_b, bl, bh);
   u32x4 d;
-  d[0] = __builtin_amdgcn_perm(e[2], e[0], 0x05040100u);
-  d[1] = __builtin_amdgcn_perm(e[2], e[0], 0x07060302u);
-  d[2] = __builtin_amdgcn_perm(e[3], e[1], 0x05040100u);
-  d[3] = __builtin_amdgcn_perm(e[3], e[1], 0x07060302u);
+  d[0] = __builtin_amdgcn_perm(ah, al, 0x05010400u);  // bf16(w0) | bf16(w1) << 16
+  d[1] = __builtin_amdgcn_perm(bh, bl, 0x05010400u);  // w2 w3
+  d[2] = __builtin_amdgcn_perm(ah, al, 0x07030602u);  // w4 w5
+  d[3] = __builtin_amdgcn_perm(bh, bl, 0x07030602u);  // w6 w7
   return __builtin_bit_cast(bf16x8, d);
 }
 
@@ -832,7 +868,8 @@ __device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, i
 // element wbase + 8 (u ^ wsx).
 template <bool BWD, bool DEC, int MS, int NT, int DW>
 __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f32x16 (&acc)[MS][NT], int lane, int wm,
-                                          int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx) {
+                                          int cw, const WCodes<DW>& c, float sc, __bf16* wdst, int wbase, int wsx,
+                                          const float (&cs)[8]) {
   Bf16Table tb;
   // The operands of MFMA step j + 1 are read while step j multiplies.
   bf16x8 a[2][MS], b[2][NT];
@@ -849,7 +886,7 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
     // issued early and complete well before the step barrier waits for them
     // (measured faster than one word after each of the four steps).
     if (DEC && j < 2) {
-      if (j == 0) tb = build_table(sc);
+      if (j == 0) tb = BWD ? build_table(sc) : build_table_pair(sc, cs);
 #pragma unroll
       for (int u = j * DW / 2; u < (j + 1) * DW / 2; ++u)
         gemm_decode_word<BWD>(c.q[u], tb, wdst + wbase + 8 * (u ^ wsx));
@@ -1122,9 +1159,16 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
   gemm_load_codes<DQ, DW>(w, w.codes, cofs, 0, blane, ca);
   gemm_load_codes<DQ, DW>(w, w.codes + second * cstep, cofs, second * bstep, blane, cb);
+  // Forward: the two lanes of a weight block (adjacent, LPR = 2) share its
+  // table; this lane's code values are entries 8 (lane % 2) ..
+  static_assert(BWD || LPR == 2, "pair tables need two lanes per block");
+  float cs[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cs[k] = __uint_as_float(kC4Bits[(lane & 1) ? 8 + k : k]);
   __syncthreads();  // d8s
   {
-    const Bf16Table tb = build_table(gemm_block_scale<DQ, DW>(ca, d8s, mu));
+    const float sc0 = gemm_block_scale<DQ, DW>(ca, d8s, mu);
+    const Bf16Table tb = BWD ? build_table(sc0) : build_table_pair(sc0, cs);
 #pragma unroll
     for (int u = 0; u < DW; ++u) gemm_decode_word<BWD>(ca.q[u], tb, ws0 + wbase + 8 * (u ^ wsx));
   }
@@ -1143,7 +1187,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k1), aoff, as1, wave);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k2 * cstep, cofs, k2 * bstep, blane, ca);
-    gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx);
+    gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx, cs);
     gemm_step_barrier<NCL>();
     if (kt + 1 >= KT) break;
     sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
@@ -1151,7 +1195,7 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k2), aoff, as0, wave);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_codes<DQ, DW>(w, w.codes + k3 * cstep, cofs, k3 * bstep, blane, cb);
-    gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx);
+    gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx, cs);
     gemm_step_barrier<NCL>();
   }
 
