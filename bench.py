@@ -199,11 +199,12 @@ def cpu_baseline(layers, M, r, s, rows):
                 seconds=round(t_total, 2))
 
 
-def gpu_time_ms(fn, dev, reps: int = 20, block: int = 1) -> float:
+def gpu_time_ms(fn, dev, reps: int = 20, block: int = 4) -> float:
     """Mean device time of fn() over `reps` back-to-back calls. `block` bf16
     GEMMs of ~1 ms each are queued first, so the calls are all enqueued before
-    the GPU reaches the start event and host-side call overhead does not leave
-    gaps in the measured region. HIP events on the launch stream."""
+    the GPU reaches the start event and host-side call overhead (argument
+    checks, ~50-100 us per call, longer than many of the calls measured) does
+    not leave gaps in the measured region. HIP events on the launch stream."""
     import torch
     for _ in range(3):
         fn()
