@@ -756,13 +756,15 @@ constexpr int GT = 256;          // output tile edge
 constexpr int GSTAGE = GT * 64;  // bf16 per activation stage (and per forward weight stage)
 
 // The [64][256] input-gradient weight slice has a row pitch of WPB = 288 bf16
-// (576 bytes) and keeps chunk c of row r at c ^ xbb(r), which only permutes
+// (576 bytes) and keeps chunk c of row r at c ^ (r % 4), which only permutes
 // chunks within aligned groups of 4, so the column tile enters the read address
-// as a constant offset. (Counters still show LDS bank conflicts on this
-// kernel's transposing reads, about a fifth of its LDS cycles; a 544-byte pitch
-// and plain reads at the same addresses measured the same.)
+// as a constant offset; the 8 lanes of a decoder store phase (4 rows x the two
+// halves of a block) and the 16 lanes of a transposing read phase then hit
+// different bank groups. (Counters still show LDS bank conflicts on this
+// kernel, about a fifth of its LDS cycles; a 544-byte pitch and plain reads at
+// the same addresses measured the same.)
 constexpr int WPB = 288;
-__device__ __forceinline__ int xbb(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int xbr(int r) { return r & 3; }
 
 // Codes of the DW code words (8 DW weights of one block) a lane decodes per
 // step, with the block's scale inputs.
@@ -849,7 +851,7 @@ __device__ __forceinline__ void gemm_frags(const __bf16* as, const __bf16* ws, i
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 8 * q + 4 * h + ((lane & 15) >> 2);
-        v[h] = lds_read_tr16(&ws[row * WPB + 8 * ((col >> 3) ^ xbb(row)) + (col & 7)]);
+        v[h] = lds_read_tr16(&ws[row * WPB + 8 * ((col >> 3) ^ xbr(row)) + (col & 7)]);
       }
       b[t] = bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
     }
@@ -886,7 +888,7 @@ __device__ __forceinline__ void gemm_step(const __bf16* as, const __bf16* ws, f3
     // issued early and complete well before the step barrier waits for them
     // (measured faster than one word after each of the four steps).
     if (DEC && j < 2) {
-      if (j == 0) tb = BWD ? build_table(sc) : build_table_pair(sc, cs);
+      if (j == 0) tb = build_table_pair(sc, cs);
 #pragma unroll
       for (int u = j * DW / 2; u < (j + 1) * DW / 2; ++u)
         gemm_decode_word<BWD>(c.q[u], tb, wdst + wbase + 8 * (u ^ wsx));
@@ -1134,14 +1136,17 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
     bstep = 1;
     wbase = rl * 64;
     wsx = swz(rl) ^ (DW * h);  // chunk (DW h + u) ^ swz(rl) = u ^ wsx for u < DW
-  } else {  // weight row 64 kt + lane, columns kc .. kc + 8 DW - 1 (clamped past K)
-    const int64_t kc = (c0 + 8 * DW * wave < K) ? c0 + 8 * DW * wave : K - 8 * DW;
-    cofs = (uint32_t)(lane * (K / 2) + kc / 2);
-    blane = (uint32_t)(lane * KB + kc / 64);
+  } else {  // weight row 64 kt + rr, columns kc .. kc + 8 DW - 1 (clamped past K): block wave / 2 of the
+            // tile, half lane % 2, so that the two halves of a block are adjacent lanes (LPR = 2)
+    const int rr = (lane >> 1) + 32 * (wave & 1), half = lane & 1;
+    const int64_t kcol = c0 + 64 * (wave >> 1) + 8 * DW * half;
+    const int64_t kc = kcol < K ? kcol : K - 8 * DW;
+    cofs = (uint32_t)(rr * (K / 2) + kc / 2);
+    blane = (uint32_t)(rr * KB + kc / 64);
     cstep = 64 * (K / 2);
     bstep = 64 * KB;
-    wbase = lane * WPB + 8 * DW * wave;  // chunks DW wave .. + DW - 1 (xbb permutes within groups of 4)
-    wsx = xbb(lane);
+    wbase = rr * WPB + 64 * (wave >> 1) + 8 * DW * half;  // chunks 8 (wave / 2) + 4 half .. + 3, permuted by rr % 4
+    wsx = xbr(rr);
   }
 
   f32x16 acc[MS][NT];
@@ -1159,16 +1164,16 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
   gemm_load_codes<DQ, DW>(w, w.codes, cofs, 0, blane, ca);
   gemm_load_codes<DQ, DW>(w, w.codes + second * cstep, cofs, second * bstep, blane, cb);
-  // Forward: the two lanes of a weight block (adjacent, LPR = 2) share its
-  // table; this lane's code values are entries 8 (lane % 2) ..
-  static_assert(BWD || LPR == 2, "pair tables need two lanes per block");
+  // The two lanes of a weight block (adjacent, LPR = 2) share its table; this
+  // lane's code values are entries 8 (lane % 2) ..
+  static_assert(LPR == 2 && DW == 4, "pair tables need two lanes per block");
   float cs[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) cs[k] = __uint_as_float(kC4Bits[(lane & 1) ? 8 + k : k]);
   __syncthreads();  // d8s
   {
     const float sc0 = gemm_block_scale<DQ, DW>(ca, d8s, mu);
-    const Bf16Table tb = BWD ? build_table(sc0) : build_table_pair(sc0, cs);
+    const Bf16Table tb = build_table_pair(sc0, cs);
 #pragma unroll
     for (int u = 0; u < DW; ++u) gemm_decode_word<BWD>(ca.q[u], tb, ws0 + wbase + 8 * (u ^ wsx));
   }
