@@ -776,25 +776,28 @@ struct WCodes {
 };
 
 // The step-dependent parts of the code address and block index are uniform
-// across the wave (cstep, bstep), the lane parts 32-bit offsets (cofs bytes,
-// blane blocks).
+// across the wave (scalar offsets cso bytes and bso blocks), the lane parts
+// 32-bit offsets (cofs bytes, blane blocks); codes and block scales are read
+// through buffer resources (rc, rs), so no per-lane 64-bit address arithmetic
+// runs per step. (Codes are under 4 GiB; every offset fits 32 bits.)
 template <bool DQ, int DW>
-__device__ __forceinline__ void gemm_load_codes(const NF4View& w, const uint8_t* cstep, uint32_t cofs, int64_t bstep,
-                                                uint32_t blane, WCodes<DW>& c) {
-  const uint4* p = reinterpret_cast<const uint4*>(cstep + cofs);
+__device__ __forceinline__ void gemm_load_codes(const __amdgpu_buffer_rsrc_t rc, const __amdgpu_buffer_rsrc_t rs,
+                                                const float* __restrict__ nested, uint32_t cso, uint32_t cofs,
+                                                uint32_t bso, uint32_t blane, WCodes<DW>& c) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int u = 0; u < DW / 4; ++u) {
-    const uint4 v = p[u];
-    c.q[4 * u] = v.x;
-    c.q[4 * u + 1] = v.y;
-    c.q[4 * u + 2] = v.z;
-    c.q[4 * u + 3] = v.w;
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(cofs + 16 * u), (int)cso, 0);
+    c.q[4 * u] = (uint32_t)v[0];
+    c.q[4 * u + 1] = (uint32_t)v[1];
+    c.q[4 * u + 2] = (uint32_t)v[2];
+    c.q[4 * u + 3] = (uint32_t)v[3];
   }
   if (DQ) {
-    c.qa = (static_cast<const uint8_t*>(w.scales) + bstep)[blane];
-    c.nv = w.nested[(bstep + blane) >> 8];
+    c.qa = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)blane, (int)bso, 0);
+    c.nv = nested[(bso + blane) >> 8];
   } else {
-    c.nv = (static_cast<const float*>(w.scales) + bstep)[blane];
+    c.nv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(4 * blane), (int)(4 * bso), 0));
   }
 }
 
@@ -1158,12 +1161,18 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   // Step indices past the end are clamped to the last step: the surplus loads
   // and decodes land in buffers that are not read again, and the loop body has
   // a single path.
-  const int64_t last = KT - 1;
-  const int64_t second = last < 1 ? last : 1;
+  // (KT < 2^16 and the codes under 4 GiB: step indices and offsets fit 32 bits)
+  const int last = (int)KT - 1;
+  const int second = last < 1 ? last : 1;
+  const uint32_t csu = (uint32_t)cstep, bsu = (uint32_t)bstep;
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w.codes), 0, (int)(uint32_t)(N * (K / 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(w.scales), 0, (int)(uint32_t)((DQ ? 1 : 4) * N * KB), 0x00020000);
   WCodes<DW> ca, cb;
   gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
-  gemm_load_codes<DQ, DW>(w, w.codes, cofs, 0, blane, ca);
-  gemm_load_codes<DQ, DW>(w, w.codes + second * cstep, cofs, second * bstep, blane, cb);
+  gemm_load_codes<DQ, DW>(rc, rs, w.nested, 0, cofs, 0, blane, ca);
+  gemm_load_codes<DQ, DW>(rc, rs, w.nested, second * csu, cofs, second * bsu, blane, cb);
   // The two lanes of a weight block (adjacent, LPR = 2) share its table; this
   // lane's code values are entries 8 (lane % 2) ..
   static_assert(LPR == 2 && DW == 4, "pair tables need two lanes per block");
@@ -1182,24 +1191,24 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   // Step kt multiplies stage kt % 2 while the activations of step kt + 1 land
   // in the other stage, the codes of step kt + 2 are loaded and the codes of
   // step kt + 1 are decoded into the other weight stage.
-  for (int64_t kt = 0; kt < KT; kt += 2) {
-    const int64_t k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
-                  k3 = kt + 3 < last ? kt + 3 : last;
+  for (int kt = 0; kt < (int)KT; kt += 2) {
+    const int k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
+              k3 = kt + 3 < last ? kt + 3 : last;
     // (The scale's table read precedes the activation loads: an LDS read
     // issued after them would wait for them.)
     float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
     __builtin_amdgcn_sched_barrier(0);
     gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k1), aoff, as1, wave);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load_codes<DQ, DW>(w, w.codes + k2 * cstep, cofs, k2 * bstep, blane, ca);
+    gemm_load_codes<DQ, DW>(rc, rs, w.nested, k2 * csu, cofs, k2 * bsu, blane, ca);
     gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx, cs);
     gemm_step_barrier<NCL>();
-    if (kt + 1 >= KT) break;
+    if (kt + 1 >= (int)KT) break;
     sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
     __builtin_amdgcn_sched_barrier(0);
     gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k2), aoff, as0, wave);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load_codes<DQ, DW>(w, w.codes + k3 * cstep, cofs, k3 * bstep, blane, cb);
+    gemm_load_codes<DQ, DW>(rc, rs, w.nested, k3 * csu, cofs, k3 * bsu, blane, cb);
     gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx, cs);
     gemm_step_barrier<NCL>();
   }
