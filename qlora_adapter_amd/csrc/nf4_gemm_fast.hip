@@ -243,32 +243,43 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
+// The small kernels' operand loads go through buffer resources: a wave-uniform
+// base (the tile's first activation row, the codes, the block scales), the
+// lanes' 32-bit byte offsets and a scalar step offset, so no per-lane 64-bit
+// address arithmetic runs per step.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0) : 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
 template <int XI>
-__device__ __forceinline__ void fwd_issue_x(const __bf16* __restrict__ x, const int32_t (&xoff)[XI], int64_t kt,
+__device__ __forceinline__ void fwd_issue_x(const __amdgpu_buffer_rsrc_t rx, const uint32_t (&xb)[XI], int kt,
                                             __bf16* buf, int wave) {
 #pragma unroll
   for (int i = 0; i < XI; ++i)
-    lds_dma16(x + xoff[i] + kt * 64, buf + (4 * i + wave) * 512);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(buf + (4 * i + wave) * 512),
+                                             16, (int)xb[i], __builtin_amdgcn_readfirstlane(128 * kt), 0, 0);
 }
 
 template <bool DQ, int NS>
-__device__ __forceinline__ void fwd_load_w(const NF4View& w, const uint8_t* const (&wp)[NS],
-                                           const int64_t (&blk0)[NS], int64_t kt, WStep<NS>& st) {
+__device__ __forceinline__ void fwd_load_w(const __amdgpu_buffer_rsrc_t rc, const __amdgpu_buffer_rsrc_t rs,
+                                           const float* __restrict__ nested, const uint32_t (&cb)[NS],
+                                           const uint32_t (&bb)[NS], int kt, WStep<NS>& st) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  kt = __builtin_amdgcn_readfirstlane(kt);  // (the step is wave-uniform: scalar offsets)
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
-    st.q[t] = *reinterpret_cast<const uint4*>(wp[t] + 32 * kt);
-    const int64_t blk = blk0[t] + kt;
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)cb[t], 32 * kt, 0);
+    st.q[t] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     if (DQ) {
-      st.qa[t] = static_cast<const uint8_t*>(w.scales)[blk];
-      st.nv[t] = w.nested[blk >> 8];
+      st.qa[t] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)bb[t], kt, 0);
+      st.nv[t] = nested[(bb[t] + (uint32_t)kt) >> 8];
     } else {
-      st.nv[t] = static_cast<const float*>(w.scales)[blk];
+      st.nv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(4 * bb[t]), 4 * kt, 0));
     }
   }
 }
 
-// Block scales of a loaded step (the D8 lookup is an LDS read, issued before
-// the step's direct activation loads: an LDS read after them would wait for them).
 template <bool DQ, int NS>
 __device__ __forceinline__ void fwd_scales(const WStep<NS>& st, const float* d8s, float mu, float (&a)[NS]) {
 #pragma unroll
@@ -344,12 +355,17 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   __shared__ __attribute__((aligned(16))) __bf16 xs0[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 xs1[STAGE];
   __shared__ float d8s[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t MT = (M + BM - 1) / BM, NT = (N + BN - 1) / BN;
   int64_t mt, nt, sp, kbeg, KT;
   split_coords(blockIdx.x, MT, NT, nsplit, K / 64, mt, nt, sp, kbeg, KT);
-  const int64_t m0 = mt * BM, n0 = nt * BN;
+  // (tile coordinates in scalar registers, so that the buffer resources built
+  // from them are scalar: otherwise each buffer load runs in a lane loop)
+  sp = uniform64(sp);
+  kbeg = uniform64(kbeg);
+  KT = uniform64(KT);
+  const int64_t m0 = uniform64(mt * BM), n0 = uniform64(nt * BN);
   if (DQ) d8s[tid] = dyn8_value((uint32_t)tid);
   const float mu = DQ ? w.offset[0] : 0.0f;
 
@@ -357,24 +373,28 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // lane l writes physical chunk l % 8 of row 8G + l / 8, i.e. logical chunk
   // (l % 8) ^ swz(row). Rows past M are clamped (their outputs are not stored).
   // (offsets relative to row m0, so they fit in 32 bits: rows < 256, K < 2^22)
-  const __bf16* xt = x + m0 * K + kbeg * 64;
-  int32_t xoff[XI];
+  const int64_t xfirst = m0 * K + kbeg * 64;
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + xfirst, 2 * (M * K - xfirst));
+  uint32_t xb[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int row = 8 * (4 * i + wave) + (lane >> 3);
     const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
-    xoff[i] = (int32_t)(m * K) + 8 * ((lane & 7) ^ swz(row));
+    xb[i] = (uint32_t)(2 * (m * K) + 16 * ((lane & 7) ^ swz(row)));
   }
-  // weight rows of this lane (clamped past N)
-  int64_t nrow[NS], blk0[NS];
-  const uint8_t* wp[NS];
+  // weight rows of this lane (clamped past N): byte offset of its code words
+  // and index of its first block at step 0 (the codes are under 4 GiB)
+  int64_t nrow[NS];
+  uint32_t cb[NS], bb[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     const int64_t n = n0 + wave * WN + 32 * t + l32;
     nrow[t] = n < N ? n : N - 1;
-    wp[t] = w.codes + nrow[t] * (K / 2) + 32 * kbeg + 16 * g;
-    blk0[t] = nrow[t] * (K / 64) + kbeg;
+    cb[t] = (uint32_t)(nrow[t] * (K / 2) + 32 * kbeg + 16 * g);
+    bb[t] = (uint32_t)(nrow[t] * (K / 64) + kbeg);
   }
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(w.codes, N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w.scales, (DQ ? 1 : 4) * N * (K / 64));
 
   f32x16 acc[MS][NS];
 #pragma unroll
@@ -384,9 +404,9 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
 
   WStep<NS> wa, wb;
   bf16x8 bopa[NS][4], bopb[NS][4];
-  fwd_issue_x<XI>(xt, xoff, 0, xs0, wave);
-  fwd_load_w<DQ, NS>(w, wp, blk0, 0, wb);
-  if (KT > 1) fwd_load_w<DQ, NS>(w, wp, blk0, 1, wa);
+  fwd_issue_x<XI>(rx, xb, 0, xs0, wave);
+  fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, 0, wb);
+  if (KT > 1) fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, 1, wa);
   __syncthreads();
   fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
 
@@ -394,7 +414,7 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   // next x stage lands in the other buffer, the codes of step kt + 2 are loaded
   // and the codes of step kt + 1 are decoded. Unrolled by two so that the two x
   // buffers and register sets keep fixed roles.
-  int64_t kt = 0;
+  int kt = 0;
   // Steady state: every load and decode of both half-steps is in range, so the
   // body has no branches (keeps the accumulators in place across iterations).
   // (The barriers wait only for the activation loads: the code loads issued
@@ -404,17 +424,17 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
     float sc[NS];
     fwd_scales<DQ, NS>(wa, d8s, mu, sc);
     __builtin_amdgcn_sched_barrier(0);
-    fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
+    fwd_issue_x<XI>(rx, xb, kt + 1, xs1, wave);
     __builtin_amdgcn_sched_barrier(0);
-    fwd_load_w<DQ, NS>(w, wp, blk0, kt + 2, wb);
+    fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, kt + 2, wb);
     fwd_decode_scaled<NS>(wa, sc, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     small_step_barrier<NCL>();
     fwd_scales<DQ, NS>(wb, d8s, mu, sc);
     __builtin_amdgcn_sched_barrier(0);
-    fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
+    fwd_issue_x<XI>(rx, xb, kt + 2, xs0, wave);
     __builtin_amdgcn_sched_barrier(0);
-    fwd_load_w<DQ, NS>(w, wp, blk0, kt + 3, wa);
+    fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, kt + 3, wa);
     fwd_decode_scaled<NS>(wb, sc, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
     small_step_barrier<NCL>();
@@ -422,14 +442,14 @@ void k_fwd(const __bf16* __restrict__ x, int64_t M, int64_t K, int64_t N, NF4Vie
   __syncthreads();
   // Last one to three steps.
   for (; kt < KT; kt += 2) {
-    if (kt + 1 < KT) fwd_issue_x<XI>(xt, xoff, kt + 1, xs1, wave);
-    if (kt + 2 < KT) fwd_load_w<DQ, NS>(w, wp, blk0, kt + 2, wb);
+    if (kt + 1 < KT) fwd_issue_x<XI>(rx, xb, kt + 1, xs1, wave);
+    if (kt + 2 < KT) fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, kt + 2, wb);
     if (kt + 1 < KT) fwd_decode<DQ, NS>(wa, d8s, mu, bopb);
     fwd_mfma<MS, NS>(xs0, bopa, acc, g, l32);
     __syncthreads();
     if (kt + 1 >= KT) break;
-    if (kt + 2 < KT) fwd_issue_x<XI>(xt, xoff, kt + 2, xs0, wave);
-    if (kt + 3 < KT) fwd_load_w<DQ, NS>(w, wp, blk0, kt + 3, wa);
+    if (kt + 2 < KT) fwd_issue_x<XI>(rx, xb, kt + 2, xs0, wave);
+    if (kt + 3 < KT) fwd_load_w<DQ, NS>(rc, rs, w.nested, cb, bb, kt + 3, wa);
     if (kt + 2 < KT) fwd_decode<DQ, NS>(wb, d8s, mu, bopa);
     fwd_mfma<MS, NS>(xs1, bopb, acc, g, l32);
     __syncthreads();
@@ -534,41 +554,59 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   __shared__ __attribute__((aligned(16))) __bf16 ys0[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 ys1[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 wts[4][64 * WTP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t MT = (M + BM - 1) / BM, KTL = (K + BKO - 1) / BKO;
   int64_t mt, kt_tile, sp, nbeg, NSTEP;
   split_coords(blockIdx.x, MT, KTL, nsplit, N / 64, mt, kt_tile, sp, nbeg, NSTEP);
-  const int64_t m0 = mt * BM, k0 = kt_tile * BKO;
+  // (scalar tile coordinates, as in k_fwd)
+  sp = uniform64(sp);
+  nbeg = uniform64(nbeg);
+  NSTEP = uniform64(NSTEP);
+  const int64_t m0 = uniform64(mt * BM), k0 = uniform64(kt_tile * BKO);
   const int64_t KB = K / 64;
   const float mu = DQ ? w.offset[0] : 0.0f;
 
-  const __bf16* yt = dy + m0 * N + nbeg * 64;
-  int32_t yoff[YI];
+  // (operand loads through buffer resources: wave-uniform bases, 32-bit lane
+  // offsets, scalar step offsets; dY offsets stay below 2^31, the codes under
+  // 4 GiB)
+  const int64_t yfirst = m0 * N + nbeg * 64;
+  const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(dy + yfirst, 2 * (M * N - yfirst));
+  uint32_t yb[YI];
 #pragma unroll
   for (int i = 0; i < YI; ++i) {
     const int row = 8 * (4 * i + wave) + (lane >> 3);
     const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
-    yoff[i] = (int32_t)(m * N) + 8 * ((lane & 7) ^ swz(row));
+    yb[i] = (uint32_t)(2 * (m * N) + 16 * ((lane & 7) ^ swz(row)));
   }
-  auto issue_y = [&](int64_t ns, __bf16* buf) __device__ {
+  auto issue_y = [&](int ns, __bf16* buf) __device__ {
+    const int so = __builtin_amdgcn_readfirstlane(128 * ns);  // (wave-uniform: a scalar offset)
 #pragma unroll
-    for (int i = 0; i < YI; ++i) lds_dma16(yt + yoff[i] + ns * 64, buf + (4 * i + wave) * 512);
+    for (int i = 0; i < YI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ry, (__attribute__((address_space(3))) void*)(buf + (4 * i + wave) * 512), 16, (int)yb[i], so, 0, 0);
   };
   // This lane's weight slice: row n = 64 ns + lane, columns kc .. kc + 31 (clamped past K).
   const int64_t kc = (k0 + 32 * wave < K) ? k0 + 32 * wave : K - 32;
-  const uint8_t* wbase = w.codes + kc / 2;
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(w.codes, N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w.scales, (DQ ? 1 : 4) * N * KB);
+  // step 0's byte offset of the lane's codes and index of its block; a step
+  // adds 64 rows
+  const uint32_t cl = (uint32_t)((64 * nbeg + lane) * (K / 2) + kc / 2);
+  const uint32_t bl = (uint32_t)((64 * nbeg + lane) * KB + kc / 64);
+  const uint32_t cstep = (uint32_t)(64 * (K / 2)), bstep = (uint32_t)(64 * KB);
   __bf16* wt = wts[wave];
   // 32 columns = 16 bytes of codes per lane
-  auto load_w = [&](int64_t ns, uint4& q, uint32_t& qa, float& nv) __device__ {
-    const int64_t n = 64 * (nbeg + ns) + lane;
-    q = *reinterpret_cast<const uint4*>(wbase + n * (K / 2));
-    const int64_t blk = n * KB + kc / 64;
+  auto load_w = [&](int ns, uint4& q, uint32_t& qa, float& nv) __device__ {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    ns = __builtin_amdgcn_readfirstlane(ns);  // (the step is wave-uniform: scalar offsets)
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)cl, (int)(ns * cstep), 0);
+    q = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     if (DQ) {
-      qa = static_cast<const uint8_t*>(w.scales)[blk];
-      nv = w.nested[blk >> 8];
+      qa = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)bl, (int)(ns * bstep), 0);
+      nv = w.nested[(bl + ns * bstep) >> 8];
     } else {
-      nv = static_cast<const float*>(w.scales)[blk];
+      nv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(4 * bl), (int)(4 * ns * bstep), 0));
     }
   };
   // Block scale a' = fl32(fl32(D8[qa] nv) + mu). The D8 value is a gather from
@@ -632,7 +670,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd(const __bf16* __restrict__ dy, i
   __syncthreads();
   decode_store(qa_, scale_of(d8_of(sa), va));
 
-  int64_t ns = 0;
+  int ns = 0;
   constexpr int NCL = DQ ? 3 : 2;
   for (; ns + 3 < NSTEP; ns += 2) {
     float d8 = d8_of(sb);
@@ -1237,8 +1275,10 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
 // gradient) and, in the input gradient, the output width in whole 64-wide
 // blocks; k_fwd and k_bwd keep per-lane activation offsets (rows < 256 of the
 // tile times the reduction length) in 32 bits, so the reduction stays below
-// 2^22. Other shapes go to the general kernel.
+// 2^22, and read the codes (under 4 GiB) through 32-bit buffer offsets. Other
+// shapes go to the general kernel.
 bool fast_shape_ok(int64_t K, int64_t N, bool backward) {
+  if (N * (K / 2) >= (int64_t(1) << 32)) return false;  // codes read through 32-bit buffer offsets
   if (backward) return K % 64 == 0 && N % 64 == 0 && N < (int64_t(1) << 22);
   return K % FBK == 0 && K < (int64_t(1) << 22);
 }
