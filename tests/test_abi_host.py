@@ -262,14 +262,19 @@ def test_strided_decoder_ops_reject_bad_arrays(lib):
 
 def test_small_kernel_offsets_stay_32_bit(lib):
     """The small-tile kernels keep per-lane activation offsets (tile row times
-    reduction length) in 32 bits, so a reduction of 2^22 or more leaves the fast
-    path: such shapes then need no split-reduction workspace (the general kernel
-    has none), while the longest accepted reduction still splits."""
+    reduction length) and code offsets in 32 bits, so a reduction of 2^22 or
+    more, or 4 GiB of codes, leaves the fast path: such shapes then need no
+    split-reduction workspace (the general kernel has none), while the longest
+    accepted reduction still splits."""
     L, _ = lib
     assert L.nf4_linear_workspace_bytes(512, (1 << 22) - 64, 128, 0, 0) > 0
     assert L.nf4_linear_workspace_bytes(512, 1 << 22, 128, 0, 0) == 0
     assert L.nf4_linear_workspace_bytes(512, 128, (1 << 22) - 64, 0, 1) > 0
     assert L.nf4_linear_workspace_bytes(512, 128, 1 << 22, 0, 1) == 0
+    # the codes are read through 32-bit buffer offsets: 4 GiB of codes or more
+    # (N x K / 2 >= 2^32) also leaves the fast path
+    assert L.nf4_linear_workspace_bytes(512, 1 << 21, 4032, 0, 0) > 0
+    assert L.nf4_linear_workspace_bytes(512, 1 << 21, 4096, 0, 0) == 0
 
 
 def test_binding_rejects_bad_shapes_and_dtypes(lib):
