@@ -247,9 +247,12 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
 // base (the tile's first activation row, the codes, the block scales), the
 // lanes' 32-bit byte offsets and a scalar step offset, so no per-lane 64-bit
 // address arithmetic runs per step.
+// (The record count is an unsigned 32-bit field: up to 4 GiB - 1 bytes, the
+// codes' limit on this path; larger activation ranges are clamped, their
+// offsets stay below 2^31.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
-  const int n = (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0) : 0x7fffffff);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+  const uint32_t n = (uint32_t)(bytes < 0xffffffffll ? (bytes > 0 ? bytes : 0) : 0xffffffffll);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
 template <int XI>
