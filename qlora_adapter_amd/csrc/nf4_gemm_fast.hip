@@ -1318,7 +1318,9 @@ bool use_gemm256(int64_t M, int64_t K, int64_t N, bool backward) {
 // tiles give fewer than 256 workgroups is split in parts over 128-token tiles
 // (256-token tiles when the reduction is long, >= 128 steps, or when they
 // alone give >= 200 workgroups in an input gradient), for about 512
-// workgroups. Otherwise: 256-token tiles when they give >= 448 workgroups,
+// workgroups (about 256 in the forward pass, where fewer parts' partial sums
+// to add outweigh the lost parallelism: -0.75 ms on the 512-token training
+// step). Otherwise: 256-token tiles when they give >= 448 workgroups,
 // else 128 or 64 when those give >= 200, else 32. Parts are a power of two, at
 // most 8, of at least 8 steps; their fp32 partial sums are added by
 // k_split_sum (part 0 carries the LoRA term).
@@ -1348,10 +1350,10 @@ SmallPlan small_plan(int64_t M, int64_t K, int64_t N, bool backward) {
   int64_t ns = 1;
   if (steps >= 128 || (backward && wg(8) >= 200)) {
     p.ms = 8;
-    ns = parts(512, 8);
+    ns = parts(backward ? 512 : 256, 8);
   } else if (wg(4) < 256) {
     p.ms = 4;
-    ns = parts(512, 4);
+    ns = parts(backward ? 512 : 256, 4);
   }
   if (ns >= 2) p.nsplit = (int)ceil_div(steps, ceil_div(steps, ns));  // every part non-empty
   return p;
