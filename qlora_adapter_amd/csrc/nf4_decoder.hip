@@ -22,7 +22,8 @@
 //                  g = dy gamma, n = x rstd, plus an optional residual
 //                  gradient.
 //  k_rope          one workgroup per token: the row's d/2 angles in fp64,
-//                  cos/sin rounded to fp32, applied to every head in place.
+//                  cos/sin rounded to fp32, applied to every head in place,
+//                  16 bytes of each half head per access where aligned.
 //  Attention in bf16 with a head dim that is a multiple of 32 (up to 128)
 //  runs on the matrix cores (nf4_attention.hip); the kernels below serve fp32
 //  and the other head dims.
@@ -227,27 +228,6 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const __bf16* __restrict_
 
 // ---------------------------------------------------------------- rotary embedding
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_rope(T* __restrict__ x, int64_t ld, int heads, int d, double theta,
-                                              int inverse) {
-  __shared__ float cs[2][256];
-  const int64_t pos = blockIdx.x;
-  const int h = d / 2;
-  for (int i = threadIdx.x; i < h; i += 256) {
-    const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)d);
-    cs[0][i] = (float)cos(ang);
-    cs[1][i] = (float)(inverse ? -sin(ang) : sin(ang));
-  }
-  __syncthreads();
-  T* row = x + pos * ld;
-  for (int e = threadIdx.x; e < heads * h; e += 256) {
-    const int hd = e / h, i = e - hd * h;
-    T* p = row + (int64_t)hd * d;
-    const float a = ldf(p, i), b = ldf(p, i + h);
-    stf(p, i, a * cs[0][i] - b * cs[1][i]);
-    stf(p, i + h, b * cs[0][i] + a * cs[1][i]);
-  }
-}
 
 // ---------------------------------------------------------------- attention
 
@@ -499,6 +479,42 @@ __device__ __forceinline__ Vec<T, V> ldv(const T* p) {
   return *reinterpret_cast<const Vec<T, V>*>(p);
 }
 
+// Rotary embedding of one token per workgroup: its d/2 angles pos theta^(-2i/d)
+// in fp64 (one sincos each), cos and sin rounded to fp32 in LDS, then every
+// head rotated in place, V consecutive pairs per thread (one 16-byte access to
+// each half of the head when d/2, ld and the row allow it, else V = 1).
+template <typename T, int V>
+__global__ __launch_bounds__(256) void k_rope(T* __restrict__ x, int64_t ld, int heads, int d, double theta,
+                                              int inverse) {
+  __shared__ float cs[2][256];
+  const int64_t pos = blockIdx.x;
+  const int h = d / 2;
+  for (int i = threadIdx.x; i < h; i += 256) {
+    const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)d);
+    double sn, cn;
+    sincos(ang, &sn, &cn);
+    cs[0][i] = (float)cn;
+    cs[1][i] = (float)(inverse ? -sn : sn);
+  }
+  __syncthreads();
+  T* row = x + pos * ld;
+  const int hv = h / V;  // accesses per half head
+  for (int e = threadIdx.x; e < heads * hv; e += 256) {
+    const int hd = e / hv, i = (e - hd * hv) * V;
+    T* p = row + (int64_t)hd * d + i;
+    const Vec<T, V> a = ldv<T, V>(p), b = ldv<T, V>(p + h);
+    Vec<T, V> ra, rb;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float af = (float)a.v[k], bf = (float)b.v[k], c = cs[0][i + k], sv = cs[1][i + k];
+      ra.v[k] = (T)(af * c - bf * sv);
+      rb.v[k] = (T)(bf * c + af * sv);
+    }
+    *reinterpret_cast<Vec<T, V>*>(p) = ra;
+    *reinterpret_cast<Vec<T, V>*>(p + h) = rb;
+  }
+}
+
 template <typename T, int V>
 __global__ __launch_bounds__(256) void k_swiglu(const T* __restrict__ g, const T* __restrict__ u, int64_t rows,
                                                 int64_t width, int64_t ld, T* __restrict__ a) {
@@ -695,8 +711,19 @@ int launch_rmsnorm_bwd(const void* dy, const void* x, const float* rstd, nf4_dty
 
 int launch_rope(void* x, nf4_dtype dt, int64_t S, int32_t heads, int32_t d, int64_t ld, double theta, int inverse,
                 hipStream_t st) {
-  NF4_DISPATCH(dt, hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)S), dim3(256), 0, st, static_cast<T*>(x), ld, heads,
-                                      d, theta, inverse));
+  constexpr int kVB = 8, kVF = 4;  // 16-byte accesses
+  const int64_t vw = dt == NF4_BF16 ? kVB : kVF;
+  const bool vec = (d / 2) % vw == 0 && ld % vw == 0 && aligned16(x);
+#define NF4_ROPE(T, V) \
+  hipLaunchKernelGGL((k_rope<T, V>), dim3((unsigned)S), dim3(256), 0, st, static_cast<T*>(x), ld, heads, d, theta, inverse)
+  if (dt == NF4_BF16) {
+    if (vec) NF4_ROPE(__bf16, kVB);
+    else NF4_ROPE(__bf16, 1);
+  } else {
+    if (vec) NF4_ROPE(float, kVF);
+    else NF4_ROPE(float, 1);
+  }
+#undef NF4_ROPE
   return launch_status();
 }
 
