@@ -132,8 +132,9 @@ def _counter_summary(name: str, sources):
 
 
 def counter_traffic(kernel: str):
-    """HBM-side bytes per nf4_linear_fwd / nf4_linear_bwd_input call (all its
-    dispatches, averaged over the layer's 7 projections) from the rocprofv3
+    """HBM-side bytes per forward / input-gradient call (all its dispatches,
+    averaged over the layer's calls of that kind: 4 forward calls, q, k, v and
+    gate, up grouped; 7 input-gradient calls) from the rocprofv3
     FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the copy-probe
     calibration; None when the kernel sources changed since the counters."""
     kv = _counter_summary("fused_gemm_counters_llama8b_layer.txt", ("nf4_gemm_fast.hip", "nf4_linear.hip"))
@@ -152,6 +153,23 @@ def dequant_counter_traffic():
         return float(kv["dequant_pass_hbm_bytes"]) if kv else None
     except KeyError:
         return None
+
+
+def fwd_groups(names):
+    """Index groups of the projections that read the same activation: q, k, v
+    and gate, up (each other projection alone), in layer order."""
+    shared = ({"q_proj", "k_proj", "v_proj"}, {"gate_proj", "up_proj"})
+    out, seen = [], set()
+    for i, n in enumerate(names):
+        if i in seen:
+            continue
+        g = [i]
+        for S in shared:
+            if n in S:
+                g = [j for j, m in enumerate(names) if m in S]
+        seen.update(g)
+        out.append(g)
+    return out
 
 
 def layer_flops(M, N, K, r):
@@ -609,9 +627,15 @@ def main():
     s = nl.lora_scale(wl["alpha"], r)
 
     # ---- resident inputs and outputs (untimed) ----
+    # q, k and v read one activation, and so do gate and up (as in the decoder
+    # block); their forward passes run as one grouped call each
+    groups = fwd_groups([L.name for L in layers])
+    first = {i: g[0] for g in groups for i in g}
     P = []
     for i, L in enumerate(layers):
         inp = workloads.lora_inputs(L, M, seed_offset=i, device="cuda")
+        if first[i] != i:
+            inp["x"] = P[first[i]]["x"]
         W = workloads.normal_f32((L.n_out, L.k_in), 0.02, workloads.weight_seed(i), "cuda")
         P.append(dict(
             L=L, W=W, x=inp["x"], dy=inp["dy"], A=inp["A"], B=inp["B"],
@@ -631,6 +655,9 @@ def main():
             vB=torch.zeros((L.n_out, r), dtype=torch.float32, device=dev),
             Wd=torch.empty(W.shape, dtype=torch.bfloat16, device=dev),
         ))
+    group_ws = {g[0]: torch.empty(max(1, nl.linear_fwd_group_workspace_bytes(
+        M, layers[g[0]].k_in, [layers[i].n_out for i in g], [r] * len(g))), dtype=torch.uint8, device=dev)
+        for g in groups if len(g) > 1}
     stream = torch.cuda.current_stream(dev)
     adapters = [dict(A=p["A"], dA=p["dA"], mA=p["mA"], vA=p["vA"], B=p["B"], dB=p["dB"], mB=p["mB"], vB=p["vB"])
                 for p in P]
@@ -656,9 +683,16 @@ def main():
             events.append((kind, i, e0, e1))
         # one launch set packs all seven matrices
         mark("quantize", 0, lambda: nl.quantize_many(w_all, True, outs=wq_all, workspace=qm_ws, status=q_status))
-        for i, p in enumerate(P):
-            mark("fwd", i, lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"], t_out=p["T"],
-                                                     workspace=p["lws"]))
+        for g in groups:  # a grouped call's time is recorded at its first projection
+            if len(g) == 1:
+                p = P[g[0]]
+                mark("fwd", g[0], lambda p=p: nl.linear_fwd(p["x"], p["Wq"], p["A"], p["B"], s, y=p["y"],
+                                                            t_out=p["T"], workspace=p["lws"]))
+            else:
+                q = [P[i] for i in g]
+                mark("fwd", g[0], lambda q=q, w=group_ws[g[0]]: nl.linear_fwd_group(
+                    q[0]["x"], [p["Wq"] for p in q], [p["A"] for p in q], [p["B"] for p in q], [s] * len(q),
+                    ys=[p["y"] for p in q], t_outs=[p["T"] for p in q], workspace=w))
         for i, p in enumerate(P):
             mark("bwd", i, lambda p=p: nl.linear_bwd_input(p["dy"], p["Wq"], p["A"], p["B"], s, dx=p["dx"],
                                                            u_out=p["U"], workspace=p["lws"]))
@@ -751,7 +785,8 @@ def main():
                    "intermediate": 14336, "projections": 7, "lora_rank": r, "lora_alpha": wl["alpha"],
                    "double_quant": True, "block": 64, "nested_block": 256,
                    "step": "quantize + fused fwd + fused bwd-input + lora_grad + AdamW(A, B) + dequantize, "
-                           "all 7 projections"},
+                           "all 7 projections (q, k, v read one x, gate, up another; their forward passes "
+                           "run as one grouped call each)"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic(dominant)},
@@ -773,6 +808,7 @@ def main():
                     "quantize_gbps": round(q_gbps, 1), "dequant_ms": round(dq_ms, 3),
                     "dequant_gbps": round(dq_gbps, 1), "adamw_ms": round(ad_ms, 4),
                     "adamw_gbps": round(ad_gbps, 1),
+                    "fwd_calls": [[layers[i].name for i in g] for g in groups],
                     "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds
                                           if k not in ("adamw", "dequant", "quantize")}},
         "roofline_adamw": {"kernel": "lora_adamw_step_many (A and B of all 7 adapters, one launch)",

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 6
+#define NF4LORA_ABI_VERSION 7
 
 enum nf4_status {
   NF4_OK = 0,
@@ -270,6 +270,36 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
  * NULL or smaller workspace than it needs fails with NF4_EWORKSPACE.
  * Host-only; a negative NF4_E* code for invalid sizes or flags. */
 int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int flags);
+
+#define NF4_MAX_PROJECTIONS_PER_GROUP 4
+
+/* nf4_linear_fwd for `count` (1 to NF4_MAX_PROJECTIONS_PER_GROUP) projections
+ * of the same activations x [M,K] (a block's q, k and v, or gate and up; Aner
+ * docs "Native model adaptation and NF4", section "Fused GPU NF4 decodes inside
+ * the matrix kernel", applied to every adapted projection): for each i,
+ * y[i] = x W[i]_hat^T + s[i] (x A[i]^T) B[i]^T with W[i]->n == N[i]*K, A[i],
+ * B[i], r[i], s[i], t_out[i] as in nf4_linear_fwd (A, B and t_out may be NULL
+ * arrays: all entries NULL). The host arrays are read during the call only.
+ * The outputs y[i] must not overlap one another or x. For bf16, when the
+ * projections are all single or all double quantized and together give more
+ * than half a round of 256 x 256 output tiles, their matrix products run as
+ * one launch set over all their tiles (each tile computed exactly as in a
+ * call of its projection alone; the side products T run first, one per
+ * projection); otherwise each projection runs as its own nf4_linear_fwd.
+ * `workspace` (256-byte aligned) holds at most
+ * nf4_linear_fwd_group_workspace_bytes(M, K, count, N, r) bytes (the sum of
+ * each projection's nf4_linear_workspace_bytes with NF4_WS_NO_SIDE_OUT, each
+ * rounded up to 256; projections that pass t_out need less), else
+ * NF4_EWORKSPACE. Every argument error is returned before any launch. */
+int nf4_linear_fwd_group(const void* x, nf4_dtype dtype, int64_t M, int64_t K, int32_t count,
+                         const nf4_tensor* const* W, const int64_t* N, const float* const* A, const float* const* B,
+                         const int32_t* r, const float* s, void* const* y, float* const* t_out, void* workspace,
+                         size_t workspace_bytes, nf4_stream_t stream);
+
+/* Workspace bytes of nf4_linear_fwd_group with no t_out (an upper bound for
+ * every call with these sizes). Host-only; NF4_EINVAL (negative) for NULL
+ * arrays, a count outside 1..NF4_MAX_PROJECTIONS_PER_GROUP or invalid sizes. */
+int64_t nf4_linear_fwd_group_workspace_bytes(int64_t M, int64_t K, int32_t count, const int64_t* N, const int32_t* r);
 
 /* LoRA factor gradients (Aner docs "Native model adaptation and NF4", sections
  * "Adapter API" and "LoRA FA includes gradient preconditioning"):

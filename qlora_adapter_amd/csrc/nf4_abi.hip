@@ -412,6 +412,50 @@ int nf4_linear_bwd_input(const void* dy, nf4_dtype dtype, int64_t M, int64_t N, 
   return linear_common(dy, dtype, M, K, N, W, A, B, r, s, dx, u_out, workspace, workspace_bytes, true, stream);
 }
 
+int nf4_linear_fwd_group(const void* x, nf4_dtype dtype, int64_t M, int64_t K, int32_t count,
+                         const nf4_tensor* const* W, const int64_t* N, const float* const* A, const float* const* B,
+                         const int32_t* r, const float* s, void* const* y, float* const* t_out, void* workspace,
+                         size_t workspace_bytes, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (count < 1 || count > NF4_MAX_PROJECTIONS_PER_GROUP || !W || !N || !r || !s || !y || !x) return NF4_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return NF4_EALIGN;
+  LinearArgs g[NF4_MAX_PROJECTIONS_PER_GROUP];
+  int64_t need = 0;
+  char* base = static_cast<char*>(workspace);
+  for (int i = 0; i < count; ++i) {
+    const float* Ai = A ? A[i] : nullptr;
+    const float* Bi = B ? B[i] : nullptr;
+    float* side = t_out ? t_out[i] : nullptr;
+    const int32_t ri = r[i];
+    if (!y[i] || !linear_sizes_ok(M, K, N[i])) return NF4_EINVAL;
+    if (int rc = check_tensor(W[i], N[i] * K)) return rc;
+    if (ri < 0 || ri > 256) return NF4_EINVAL;
+    if (ri > 0 && (!Ai || !Bi || ri > (K < N[i] ? K : N[i]) || !std::isfinite(s[i]))) return NF4_EINVAL;
+    if (!aligned(x, 16) || !aligned(y[i], 16)) return NF4_EALIGN;
+    if (ri > 0 && (!aligned(Ai, 4) || !aligned(Bi, 4) || (side && !aligned(side, 4)))) return NF4_EALIGN;
+    const LinearWs w = linear_ws(dtype, M, K, N[i], ri, ri > 0 && !side, false);
+    char* part = base ? base + need : nullptr;
+    float* side_part = w.side_part > 0 ? reinterpret_cast<float*>(part + w.split) : nullptr;
+    if (w.side > 0) side = reinterpret_cast<float*>(part + w.split + w.side_part);
+    g[i] = LinearArgs{x, dtype, M, K, N[i], W[i], Ai, Bi, ri, s[i], y[i], side, false, part, (size_t)w.split,
+                      side_part};
+    need += (int64_t)round_up((size_t)w.total(), 256);
+  }
+  if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return NF4_EWORKSPACE;
+  if (int rc = check_device()) return rc;
+  return launch_linear_group(g, count, as_stream(stream));
+}
+
+int64_t nf4_linear_fwd_group_workspace_bytes(int64_t M, int64_t K, int32_t count, const int64_t* N, const int32_t* r) {
+  if (count < 1 || count > NF4_MAX_PROJECTIONS_PER_GROUP || !N || !r) return NF4_EINVAL;
+  int64_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!linear_sizes_ok(M, K, N[i]) || r[i] < 0 || r[i] > 256) return NF4_EINVAL;
+    need += (int64_t)round_up((size_t)linear_ws(NF4_BF16, M, K, N[i], r[i], r[i] > 0, false).total(), 256);
+  }
+  return need;
+}
+
 int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int flags) {
   if (!linear_sizes_ok(M, K, N) || r < 0 || r > 256) return NF4_EINVAL;
   if (flags & ~(NF4_WS_BACKWARD | NF4_WS_NO_SIDE_OUT)) return NF4_EINVAL;

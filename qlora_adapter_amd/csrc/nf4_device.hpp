@@ -67,5 +67,7 @@ inline int64_t lora_chunk(int64_t M, int64_t J) {
 // Large-tile bf16 kernels (nf4_gemm_fast.hip).
 bool fast_linear_applies(const LinearArgs& g);
 int launch_linear_fast(const LinearArgs& g, hipStream_t st);
+bool group_gemm_applies(const LinearArgs* g, int n);
+int launch_linear_fast_group(const LinearArgs* g, int n, hipStream_t st);
 
 }  // namespace nf4

@@ -1115,11 +1115,34 @@ __device__ __forceinline__ void gemm_store_tile(const f32x16 (&acc)[MS][NT], __b
 // reduction length (K or N) is a multiple of 64 and below 2^22, the packed
 // codes are under 4 GiB, the output has a multiple of 4 columns and is under
 // 2 GiB.
+// Further projections of a grouped forward call, all reading the same
+// activations (such as q, k and v, or gate and up): the column tiles of the
+// call are those of the projections side by side, projection 0 (the kernel's
+// own arguments) first; part i owns the column tiles from ct0 on and brings its
+// weight, factor B, side product T, output, width and adapter rank and scale.
+// Each output tile is computed exactly as in a call of its projection alone.
+struct GemmPart {
+  NF4View w;
+  const float* F;
+  const float* S;
+  __bf16* out;
+  int64_t N, ct0;
+  int r;
+  float s;
+};
+constexpr int kGroupMax = 4;
+struct GemmGroup {
+  GemmPart p[kGroupMax - 1];
+  int n;       // projections in the call (1: projection 0 alone)
+  int64_t ct;  // column tiles of all of them
+};
+
 template <bool BWD, bool DQ, int NT, int MS>
 __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __restrict__ act, int64_t M, int64_t K,
                                                             int64_t N, NF4View w, const float* __restrict__ F, int r,
                                                             float s, const float* __restrict__ S,
-                                                            __bf16* __restrict__ out, int64_t tbase) {
+                                                            __bf16* __restrict__ out, int64_t tbase,
+                                                            GemmGroup grp) {
   constexpr int NW = 16 / NT;         // waves
   constexpr int BM = 64 * MS;         // tile rows
   constexpr int NA = BM / (8 * NW);   // activation loads per wave per step
@@ -1134,11 +1157,28 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
   __shared__ float d8s[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, cw = 32 * NT * (wave >> 1);
-  const int64_t R = BWD ? N : K, C = BWD ? K : N;
-  const int64_t MT = (M + GT - 1) / GT, CT = (C + GT - 1) / GT;
+  const int64_t MT = (M + GT - 1) / GT;
+  const int64_t CT = (!BWD && grp.n > 1) ? grp.ct : ((BWD ? K : N) + GT - 1) / GT;
   int64_t mt, ct;
   const int64_t xb = xcd_order(blockIdx.x, gridDim.x);
   group_map(tbase + (MS == 4 ? xb : xb >> 1), MT, CT, mt, ct);
+  if constexpr (!BWD) {  // the projection that owns column tile ct (workgroup-uniform)
+    const int64_t cg = ct;
+#pragma unroll
+    for (int i = 0; i < kGroupMax - 1; ++i)
+      if (i + 1 < grp.n && cg >= grp.p[i].ct0) {  // (ct0 ascending: the last match owns it)
+        const GemmPart& q = grp.p[i];
+        w = q.w;
+        F = q.F;
+        S = q.S;
+        out = q.out;
+        N = q.N;
+        r = q.r;
+        s = q.s;
+        ct = cg - q.ct0;
+      }
+  }
+  const int64_t R = BWD ? N : K, C = BWD ? K : N;
   // The tile origin is workgroup-uniform; stated explicitly (scalar registers),
   // so that the activation loads' buffer resource is scalar too (otherwise the
   // compiler may wrap each of those loads in a loop over distinct lane values).
@@ -1400,45 +1440,92 @@ int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backwa
   return (int64_t)p.nsplit * M * C * (int64_t)sizeof(float);
 }
 
+namespace {
+
+// The 256 x 256 shared-decode kernel over `tiles` output tiles (of projection 0
+// and the further parts in grp): whole tiles fill complete rounds of the chip
+// (one workgroup per CU); a last round of at most half the CUs is run as twice
+// as many half tiles.
+template <bool BWD, bool DQ>
+void launch_gemm256(const LinearArgs& g, const NF4View& w, const GemmGroup& grp, int64_t tiles, hipStream_t st) {
+  const __bf16* a = static_cast<const __bf16*>(g.a);
+  __bf16* o = static_cast<__bf16*>(g.out);
+  const float* F = g.backward ? g.A : g.B;
+  constexpr int NT = 2;  // 32x32 column tiles per wave (two waves per SIMD)
+  const dim3 block(64 * (16 / NT));
+  const int64_t cus = device_cu_count();
+  const int64_t tail = tiles > cus ? tiles % cus : 0;
+  const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
+  hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 4>), dim3((unsigned)whole), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s,
+                     g.side, o, (int64_t)0, grp);
+  if (whole < tiles)
+    hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 2>), dim3((unsigned)(2 * (tiles - whole))), block, 0, st, a, g.M, g.K,
+                       g.N, w, F, g.r, g.s, g.side, o, whole, grp);
+}
+
+}  // namespace
+
+// A grouped forward call takes the 256 x 256 kernel as one launch set when its
+// 2 to 4 projections read the same bf16 activations, are all single or all
+// double quantized, each meets the kernel's own bounds and together give more
+// than half a round of tiles.
+bool group_gemm_applies(const LinearArgs* g, int n) {
+  if (n < 2 || n > kGroupMax) return false;
+  int64_t ct = 0;
+  for (int i = 0; i < n; ++i) {
+    const LinearArgs& q = g[i];
+    if (q.dtype != NF4_BF16 || q.backward || q.a != g[0].a || q.M != g[0].M || q.K != g[0].K) return false;
+    if (q.W->double_quant != g[0].W->double_quant || !fast_shape_ok(q.K, q.N, false)) return false;
+    if (q.N % 4 != 0 || 2 * q.M * q.N >= (int64_t(1) << 31)) return false;
+    ct += ceil_div(q.N, GT);
+  }
+  return ceil_div(g[0].M, GT) * ct >= kGemmMinTiles;
+}
+
+// The grouped forward's matrix products (the side products T already written):
+// projection 0 through the kernel's arguments, the others through GemmGroup.
+int launch_linear_fast_group(const LinearArgs* g, int n, hipStream_t st) {
+  GemmGroup grp{};
+  grp.n = n;
+  int64_t ct = ceil_div(g[0].N, GT);
+  for (int i = 1; i < n; ++i) {
+    GemmPart& q = grp.p[i - 1];
+    q.w = make_view(g[i].W);
+    q.F = g[i].B;
+    q.S = g[i].side;
+    q.out = static_cast<__bf16*>(g[i].out);
+    q.N = g[i].N;
+    q.ct0 = ct;
+    q.r = g[i].r;
+    q.s = g[i].s;
+    ct += ceil_div(g[i].N, GT);
+  }
+  grp.ct = ct;
+  const int64_t tiles = ceil_div(g[0].M, GT) * ct;
+  const NF4View w = make_view(g[0].W);
+  if (g[0].W->double_quant)
+    launch_gemm256<false, true>(g[0], w, grp, tiles, st);
+  else
+    launch_gemm256<false, false>(g[0], w, grp, tiles, st);
+  return launch_status();
+}
+
 int launch_linear_fast(const LinearArgs& g, hipStream_t st) {
   const NF4View w = make_view(g.W);
   const bool dq = g.W->double_quant != 0;
   if (use_gemm256(g.M, g.K, g.N, g.backward)) {
-    // 256 x 256 shared-decode kernel when there are enough tiles to fill the chip.
     int64_t C, R;
     out_red(g.K, g.N, g.backward, C, R);
     const int64_t tiles = ceil_div(g.M, GT) * ceil_div(C, GT);
-    const __bf16* a = static_cast<const __bf16*>(g.a);
-    __bf16* o = static_cast<__bf16*>(g.out);
-    const float* F = g.backward ? g.A : g.B;
-    constexpr int NT = 2;  // 32x32 column tiles per wave (two waves per SIMD)
-    const dim3 block(64 * (16 / NT));
-    // Whole tiles fill complete rounds of the chip (one workgroup per CU); a
-    // last round of at most half the CUs is run as twice as many half tiles.
-    const int64_t cus = device_cu_count();
-    const int64_t tail = tiles > cus ? tiles % cus : 0;
-    const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
-#define NF4_GEMM(BWD, DQ, MS, NWG, TB)                                                                                 \
-  hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, MS>), dim3((unsigned)(NWG)), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s, \
-                     g.side, o, (int64_t)(TB))
-#define NF4_GEMM_BOTH(BWD, DQ)                                          \
-  do {                                                                  \
-    NF4_GEMM(BWD, DQ, 4, whole, 0);                                     \
-    if (whole < tiles) NF4_GEMM(BWD, DQ, 2, 2 * (tiles - whole), whole); \
-  } while (0)
+    GemmGroup one{};
+    one.n = 1;
     if (g.backward) {
-      if (dq)
-        NF4_GEMM_BOTH(true, true);
-      else
-        NF4_GEMM_BOTH(true, false);
+      if (dq) launch_gemm256<true, true>(g, w, one, tiles, st);
+      else launch_gemm256<true, false>(g, w, one, tiles, st);
     } else {
-      if (dq)
-        NF4_GEMM_BOTH(false, true);
-      else
-        NF4_GEMM_BOTH(false, false);
+      if (dq) launch_gemm256<false, true>(g, w, one, tiles, st);
+      else launch_gemm256<false, false>(g, w, one, tiles, st);
     }
-#undef NF4_GEMM_BOTH
-#undef NF4_GEMM
     return launch_status();
   }
   SmallPlan p = small_plan(g.M, g.K, g.N, g.backward);

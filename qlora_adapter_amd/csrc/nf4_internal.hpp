@@ -73,6 +73,7 @@ struct LinearArgs {
 // Workspace the bf16 fused path needs for these sizes (0 for most shapes).
 int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward);
 int launch_linear(const LinearArgs& a, hipStream_t s);
+int launch_linear_group(const LinearArgs* a, int n, hipStream_t s);
 // Side product alone: out[m][rho] = sum_i L[m][i] R[i][rho] (fp32 [M, r]), with
 // R[i][rho] = fac[rho][i] (backward = false: T = x A^T, I = K) or fac[i][rho]
 // (backward = true: U = dY B, I = N). `part` holds side_split_ws_bytes(M, I, r)

@@ -1195,6 +1195,19 @@ int launch_linear(const LinearArgs& g, hipStream_t st) {
   return run_linear_general<float>(g, st);
 }
 
+// Forward of n projections that read the same activations: their side
+// products, then one launch set of the matrix kernel over all their output
+// tiles when group_gemm_applies, else each projection as its own call.
+int launch_linear_group(const LinearArgs* g, int n, hipStream_t st) {
+  if (!group_gemm_applies(g, n)) {
+    for (int i = 0; i < n; ++i)
+      if (int rc = launch_linear(g[i], st)) return rc;
+    return NF4_OK;
+  }
+  for (int i = 0; i < n; ++i) launch_side<__bf16>(g[i], st);
+  return launch_linear_fast_group(g, n, st);
+}
+
 // Tokens per chunk of the bf16 MFMA reduction (a multiple of the 32-token
 // step), for about 512 workgroups of 256 columns (two per CU):
 //  - with dA, both reductions take 512 / (tiles(K) + tiles(N)) chunks, so every

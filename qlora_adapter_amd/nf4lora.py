@@ -12,7 +12,7 @@ import dataclasses
 import math
 import os
 import threading
-from typing import Optional, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -25,7 +25,7 @@ _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noalloc", "nf4_quantize_noalloc_max_elements",
            "nf4_quantize_many", "nf4_quantize_many_workspace_bytes", "nf4_dequantize", "nf4_dequantize_many",
-           "nf4_embedding_rows", "nf4_linear_fwd",
+           "nf4_embedding_rows", "nf4_linear_fwd", "nf4_linear_fwd_group", "nf4_linear_fwd_group_workspace_bytes",
            "nf4_linear_bwd_input", "nf4_linear_workspace_bytes", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
            "nf4_add_rmsnorm", "nf4_rmsnorm_bwd", "nf4_rope", "nf4_attention_fwd", "nf4_attention_bwd", "nf4_swiglu",
@@ -33,6 +33,7 @@ EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noallo
 
 MAX_ADAPTERS_PER_CALL = 16
 MAX_TENSORS_PER_CALL = 16
+MAX_PROJECTIONS_PER_GROUP = 4
 
 
 class NF4Error(RuntimeError):
@@ -95,6 +96,13 @@ def load() -> ctypes.CDLL:
             lib.nf4_embedding_rows.argtypes = [ctypes.POINTER(_Tensor), I64, I64, P, I64, ctypes.c_int, P, P, P]
             lib.nf4_linear_fwd.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32, F, P,
                                            P, P, ctypes.c_size_t, P]
+            lib.nf4_linear_fwd_group.argtypes = [P, ctypes.c_int, I64, I64, I32, ctypes.POINTER(ctypes.POINTER(_Tensor)),
+                                                 ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(I32),
+                                                 ctypes.POINTER(F), ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.POINTER(ctypes.c_void_p), P, ctypes.c_size_t, P]
+            lib.nf4_linear_fwd_group_workspace_bytes.restype = I64
+            lib.nf4_linear_fwd_group_workspace_bytes.argtypes = [I64, I64, I32, ctypes.POINTER(I64), ctypes.POINTER(I32)]
             lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
                                                  F, P, P, P, ctypes.c_size_t, P]
             lib.nf4_linear_workspace_bytes.restype = I64
@@ -140,6 +148,10 @@ def _check(fn: str, rc: int) -> None:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _addr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
 
 
 def _stream(device: torch.device):
@@ -434,6 +446,73 @@ def linear_fwd(x: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None, 
                                                    _ptr(B), r, float(s), _ptr(y), _ptr(t_out), _ptr(ws), wsb,
                                                    _stream(x.device)))
     return y, t_out
+
+
+def linear_fwd_group_workspace_bytes(M: int, K: int, N: Sequence[int], r: Sequence[int]) -> int:
+    """Workspace bytes of linear_fwd_group with these widths and ranks when no
+    projection passes t_out (an upper bound for every such call)."""
+    n = len(N)
+    if n != len(r):
+        raise ValueError("N and r have different lengths")
+    v = int(load().nf4_linear_fwd_group_workspace_bytes(int(M), int(K), n, (ctypes.c_int64 * n)(*map(int, N)),
+                                                        (ctypes.c_int32 * n)(*map(int, r))))
+    if v < 0:
+        _check("nf4_linear_fwd_group_workspace_bytes", v)
+    return v
+
+
+def linear_fwd_group(x: torch.Tensor, Ws: Sequence[NF4Tensor], As: Sequence[Optional[torch.Tensor]],
+                     Bs: Sequence[Optional[torch.Tensor]], s: Sequence[float],
+                     ys: Optional[Sequence[torch.Tensor]] = None,
+                     t_outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[List[torch.Tensor], List[Optional[torch.Tensor]]]:
+    """linear_fwd for up to MAX_PROJECTIONS_PER_GROUP projections of the same
+    x (e.g. q, k and v): y[i] = x W[i]^T + s[i] (x A[i]^T) B[i]^T in one call
+    whose matrix products share one launch set when the shapes allow. Returns
+    (ys, Ts); T[i] is allocated here for adapted projections when t_outs is
+    not given."""
+    n = len(Ws)
+    if not 1 <= n <= MAX_PROJECTIONS_PER_GROUP or not (len(As) == len(Bs) == len(s) == n):
+        raise ValueError(f"linear_fwd_group takes 1..{MAX_PROJECTIONS_PER_GROUP} projections with one A, B, s each")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be a bfloat16 or float32 [M, K] tensor")
+    M, K = x.shape
+    ys = list(ys) if ys is not None else [None] * n
+    t_outs = list(t_outs) if t_outs is not None else [None] * n
+    if len(ys) != n or len(t_outs) != n:
+        raise ValueError("ys and t_outs need one entry per projection")
+    Ns, rs = [], []
+    for i, W in enumerate(Ws):
+        if len(W.shape) != 2 or W.shape[1] != K:
+            raise ValueError(f"W[{i}] is {tuple(W.shape)} but x has {K} columns")
+        N = W.shape[0]
+        r = _lora_rank(As[i], Bs[i], "linear_fwd_group")
+        _arrays((As[i], f"A[{i}]", torch.float32, (r, K) if r else None),
+                (Bs[i], f"B[{i}]", torch.float32, (N, r) if r else None), (ys[i], f"y[{i}]", x.dtype, (M, N)),
+                (t_outs[i], f"t_out[{i}]", torch.float32, (M, r)))
+        if ys[i] is None:
+            ys[i] = torch.empty((M, N), dtype=x.dtype, device=x.device)
+        if r and t_outs[i] is None:
+            t_outs[i] = torch.empty((M, r), dtype=torch.float32, device=x.device)
+        Ns.append(N)
+        rs.append(r)
+    _arrays((x, "x", None, None))
+    if workspace is None:
+        need = linear_fwd_group_workspace_bytes(M, K, Ns, rs)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sts = [W.c_struct() for W in Ws]
+    VP = ctypes.c_void_p * n
+    _check("nf4_linear_fwd_group",
+           load().nf4_linear_fwd_group(_ptr(x), _DT[x.dtype], M, K, n,
+                                       (ctypes.POINTER(_Tensor) * n)(*[ctypes.pointer(t) for t in sts]),
+                                       (ctypes.c_int64 * n)(*Ns), VP(*[_addr(a) for a in As]), VP(*[_addr(b) for b in Bs]),
+                                       (ctypes.c_int32 * n)(*rs), (ctypes.c_float * n)(*map(float, s)),
+                                       VP(*[_addr(y) for y in ys]), VP(*[_addr(t) for t in t_outs]), _ptr(workspace), wsb,
+                                       _stream(x.device)))
+    return ys, t_outs
 
 
 def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None,

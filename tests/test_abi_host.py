@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 6
+    assert lib[0].nf4lora_abi_version() == 7
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -128,6 +128,38 @@ def test_argument_errors_before_device(lib):
     assert L.lora_grad_workspace_bytes(8, 64, 32, 4, 0, 4) == EINVAL
     assert L.lora_grad_workspace_bytes(4096, 4096, 4096, 16, 0, 0) > L.lora_grad_workspace_bytes(4096, 4096, 4096,
                                                                                                   16, 1, 0)
+
+
+def test_grouped_forward_arguments_before_device(lib):
+    L, m = lib
+    EINVAL, EALIGN, EWS = -1, -2, -6
+    I64s, I32s, Fs, VPs = ctypes.c_int64 * 4, ctypes.c_int32 * 4, ctypes.c_float * 4, ctypes.c_void_p * 4
+    # workspace query: the sum of each projection's own query with no side output, each rounded up to 256
+    N, r = I64s(4096, 1024, 1024, 0), I32s(16, 16, 0, 0)
+    want = sum((L.nf4_linear_workspace_bytes(4096, 4096, n, k, 2) + 255) // 256 * 256
+               for n, k in ((4096, 16), (1024, 16), (1024, 0)))
+    assert want > 0 and L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 3, N, r) == want
+    assert L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 0, N, r) == EINVAL
+    assert L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 5, N, r) == EINVAL
+    assert L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 2, None, r) == EINVAL
+    assert L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 2, N, I32s(16, 257)) == EINVAL
+    assert L.nf4_linear_fwd_group_workspace_bytes(4096, 4096, 4, N, r) == EINVAL  # a zero width
+    # the call: counts, NULL arrays, a part's size mismatch, alignment, and the workspace of a part without t_out
+    wa, wb = m._Tensor(16, 16, 16, 16, 64 * 32, 1), m._Tensor(16, 16, 16, 16, 64 * 16, 1)
+    Ws = (ctypes.POINTER(m._Tensor) * 4)(ctypes.pointer(wa), ctypes.pointer(wb))
+    Ng, rg, sg = I64s(32, 16), I32s(4, 4), Fs(1.0, 1.0)
+    ab, ys, ts = VPs(16, 16), VPs(16, 16), VPs(16, 16)
+    G = L.nf4_linear_fwd_group
+    assert G(16, 1, 8, 64, 0, Ws, Ng, ab, ab, rg, sg, ys, ts, None, 0, None) == EINVAL
+    assert G(16, 1, 8, 64, 5, Ws, Ng, ab, ab, rg, sg, ys, ts, None, 0, None) == EINVAL
+    assert G(16, 1, 8, 64, 2, None, Ng, ab, ab, rg, sg, ys, ts, None, 0, None) == EINVAL
+    assert G(None, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, ys, ts, None, 0, None) == EINVAL
+    assert G(16, 1, 8, 64, 2, Ws, I64s(32, 17), ab, ab, rg, sg, ys, ts, None, 0, None) == EINVAL
+    assert G(16, 1, 8, 64, 2, Ws, Ng, None, None, rg, sg, ys, ts, None, 0, None) == EINVAL  # r > 0 needs A, B
+    assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, Fs(1.0, float("inf")), ys, ts, None, 0, None) == EINVAL
+    assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, VPs(16, 24), ts, None, 0, None) == EALIGN
+    assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, ys, ts, 128, 1 << 20, None) == EALIGN
+    assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, ys, VPs(16, None), None, 0, None) == EWS
 
 
 def test_optional_side_products_and_recompute(lib):

@@ -415,3 +415,49 @@ def test_large_ranks(gpu, orc, M, K, N, r):
     assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16))
     assert torch.equal(dA2.view(torch.int32), dA.view(torch.int32))
     assert torch.equal(dB2.view(torch.int32), dB.view(torch.int32))
+
+
+GROUPS = [
+    # (M, K, widths, ranks, double quant): projections of one activation in one call
+    (4096, 4096, (4096, 1024, 1024), (16, 16, 16), True),     # q, k, v at 4096 tokens: 384 tiles, half-tile last round
+    (4096, 4096, (14336, 14336), (16, 16), True),              # gate, up at 4096 tokens: 1792 tiles, 7 whole rounds
+    (2000, 1024, (4160, 520, 1028), (8, 0, 4), False),         # ragged widths, a part with no adapter, single quant
+    (4000, 1024, (2304, 1100, 1028, 264), (16, 8, 4, 12), True),  # four parts, 336 tiles: a last round of 80
+    (512, 576, (576, 192, 192), (8, 8, 8), True),              # 10 tiles: each projection runs as its own call
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,rs,dq", GROUPS)
+def test_linear_fwd_group(gpu, orc, M, K, Ns, rs, dq):
+    """Grouped forward over projections of one x: every y[i] and T[i] against
+    the oracle on sampled token rows (including the last rows), T[i] bitwise
+    equal to the projection's own call, y[i] too where that call also takes the
+    256 x 256 kernel (at least 129 tiles), and run-to-run identical."""
+    print(f"[linear] group M={M} K={K} N={Ns} r={rs}", flush=True)
+    n = len(Ns)
+    cs = [make_case(M, K, N, max(r, 1), torch.bfloat16, seed=7 + i) for i, (N, r) in enumerate(zip(Ns, rs))]
+    x = cs[0]["x"]
+    Ws = [gpu.quantize(c["W"], dq) for c in cs]
+    As = [c["A"] if r else None for c, r in zip(cs, rs)]
+    Bs = [c["B"] if r else None for c, r in zip(cs, rs)]
+    ss = [gpu.lora_scale(2.0 * r, r) if r else 0.0 for r in rs]
+    ys, Ts = gpu.linear_fwd_group(x, Ws, As, Bs, ss)
+    ys2, Ts2 = gpu.linear_fwd_group(x, Ws, As, Bs, ss)
+    alone = [gpu.linear_fwd(x, Ws[i], As[i], Bs[i], ss[i]) for i in range(n)]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + K + n)
+    rows = np.unique(np.concatenate([rng.choice(M - 4, 12, replace=False), np.arange(M - 4, M)]))
+    xs = to_np(x)[rows]
+    for i, (N, r) in enumerate(zip(Ns, rs)):
+        assert torch.equal(ys[i], ys2[i]), f"y[{i}] differs between runs"
+        if r:
+            assert torch.equal(Ts[i], Ts2[i]) and torch.equal(Ts[i], alone[i][1]), f"T[{i}]"
+        if ((M + 255) // 256) * ((N + 255) // 256) >= 129:
+            assert torch.equal(ys[i], alone[i][0]), f"y[{i}] differs from its own call"
+        Wref = oracle_weight(orc, cs[i]["W"], torch.bfloat16, dq)
+        A = As[i].cpu().numpy() if r else None
+        B = Bs[i].cpu().numpy() if r else None
+        y_ref, T_ref = orc.linear_fwd(xs, Wref, A, B, ss[i])
+        assert_close(to_np(ys[i])[rows], y_ref, "bf16", f"y[{i}] rows")
+        if r:
+            assert_close(Ts[i].cpu().numpy()[rows], T_ref, "f32", f"T[{i}] rows")
