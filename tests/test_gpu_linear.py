@@ -461,3 +461,28 @@ def test_linear_fwd_group(gpu, orc, M, K, Ns, rs, dq):
         assert_close(to_np(ys[i])[rows], y_ref, "bf16", f"y[{i}] rows")
         if r:
             assert_close(Ts[i].cpu().numpy()[rows], T_ref, "f32", f"T[{i}] rows")
+
+
+@pytest.mark.parametrize("case", ["f32", "mixed_quant"])
+def test_linear_fwd_group_fallbacks(gpu, orc, case):
+    """Groups the one-launch path does not take run each projection as its own
+    call: fp32 activations (the general kernel), and bf16 projections of which
+    one is single and one double quantized (enough tiles otherwise). Each y[i]
+    and T[i] equals its own call bit for bit."""
+    print(f"[linear] group fallback {case}", flush=True)
+    M, K, Ns, r = (300, 640, (576, 192), 8) if case == "f32" else (2048, 1024, (4096, 4096), 16)
+    dt = torch.float32 if case == "f32" else torch.bfloat16
+    cs = [make_case(M, K, N, r, dt, seed=3 + i) for i, N in enumerate(Ns)]
+    x = cs[0]["x"]
+    Ws = [gpu.quantize(c["W"], case == "f32" or i == 0) for i, c in enumerate(cs)]
+    As, Bs = [c["A"] for c in cs], [c["B"] for c in cs]
+    s = [gpu.lora_scale(16.0, r)] * len(Ns)
+    ys, Ts = gpu.linear_fwd_group(x, Ws, As, Bs, s)
+    for i in range(len(Ns)):
+        y1, T1 = gpu.linear_fwd(x, Ws[i], As[i], Bs[i], s[i])
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i], y1) and torch.equal(Ts[i], T1), f"part {i}"
+    if case == "f32":
+        Wref = oracle_weight(orc, cs[0]["W"], dt, True)
+        y_ref, _ = orc.linear_fwd(to_np(x), Wref, As[0].cpu().numpy(), Bs[0].cpu().numpy(), s[0])
+        assert_close(to_np(ys[0]), y_ref, "f32", "y[0]")
