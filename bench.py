@@ -133,8 +133,8 @@ def _counter_summary(name: str, sources):
 
 def counter_traffic(kernel: str):
     """HBM-side bytes per forward / input-gradient call (all its dispatches,
-    averaged over the layer's calls of that kind: 4 forward calls, q, k, v and
-    gate, up grouped; 7 input-gradient calls) from the rocprofv3
+    averaged over the layer's 4 calls of that kind: q, k, v and gate, up
+    grouped or summed, o and down alone) from the rocprofv3
     FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the copy-probe
     calibration; None when the kernel sources changed since the counters."""
     kv = _counter_summary("fused_gemm_counters_llama8b_layer.txt", ("nf4_gemm_fast.hip", "nf4_linear.hip"))
@@ -628,7 +628,9 @@ def main():
 
     # ---- resident inputs and outputs (untimed) ----
     # q, k and v read one activation, and so do gate and up (as in the decoder
-    # block); their forward passes run as one grouped call each
+    # block); their forward passes run as one grouped call each, and their
+    # input gradients as one summed call each (the gradient that activation
+    # receives)
     groups = fwd_groups([L.name for L in layers])
     first = {i: g[0] for g in groups for i in g}
     P = []
@@ -656,6 +658,9 @@ def main():
             Wd=torch.empty(W.shape, dtype=torch.bfloat16, device=dev),
         ))
     group_ws = {g[0]: torch.empty(max(1, nl.linear_fwd_group_workspace_bytes(
+        M, layers[g[0]].k_in, [layers[i].n_out for i in g], [r] * len(g))), dtype=torch.uint8, device=dev)
+        for g in groups if len(g) > 1}
+    sum_ws = {g[0]: torch.empty(max(1, nl.linear_bwd_input_sum_workspace_bytes(
         M, layers[g[0]].k_in, [layers[i].n_out for i in g], [r] * len(g))), dtype=torch.uint8, device=dev)
         for g in groups if len(g) > 1}
     stream = torch.cuda.current_stream(dev)
@@ -693,9 +698,16 @@ def main():
                 mark("fwd", g[0], lambda q=q, w=group_ws[g[0]]: nl.linear_fwd_group(
                     q[0]["x"], [p["Wq"] for p in q], [p["A"] for p in q], [p["B"] for p in q], [s] * len(q),
                     ys=[p["y"] for p in q], t_outs=[p["T"] for p in q], workspace=w))
-        for i, p in enumerate(P):
-            mark("bwd", i, lambda p=p: nl.linear_bwd_input(p["dy"], p["Wq"], p["A"], p["B"], s, dx=p["dx"],
-                                                           u_out=p["U"], workspace=p["lws"]))
+        for g in groups:  # a group's summed input gradient lands in its first projection's dx
+            if len(g) == 1:
+                p = P[g[0]]
+                mark("bwd", g[0], lambda p=p: nl.linear_bwd_input(p["dy"], p["Wq"], p["A"], p["B"], s, dx=p["dx"],
+                                                                  u_out=p["U"], workspace=p["lws"]))
+            else:
+                q = [P[i] for i in g]
+                mark("bwd", g[0], lambda q=q, w=sum_ws[g[0]]: nl.linear_bwd_input_sum(
+                    [p["dy"] for p in q], [p["Wq"] for p in q], [p["A"] for p in q], [p["B"] for p in q],
+                    [s] * len(q), dx=q[0]["dx"], u_outs=[p["U"] for p in q], workspace=w))
         for i, p in enumerate(P):
             mark("grad", i, lambda p=p: nl.lora_grad(p["x"], p["dy"], p["T"], p["U"], s, dA=p["dA"], dB=p["dB"],
                                                      workspace=p["gws"]))
@@ -786,7 +798,7 @@ def main():
                    "double_quant": True, "block": 64, "nested_block": 256,
                    "step": "quantize + fused fwd + fused bwd-input + lora_grad + AdamW(A, B) + dequantize, "
                            "all 7 projections (q, k, v read one x, gate, up another; their forward passes "
-                           "run as one grouped call each)"},
+                           "run as one grouped call each, their input gradients as one summed call each)"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic(dominant)},
@@ -809,6 +821,7 @@ def main():
                     "dequant_gbps": round(dq_gbps, 1), "adamw_ms": round(ad_ms, 4),
                     "adamw_gbps": round(ad_gbps, 1),
                     "fwd_calls": [[layers[i].name for i in g] for g in groups],
+                    "bwd_calls": [[layers[i].name for i in g] for g in groups],
                     "per_projection_ms": {k: [round(v, 4) for v in per[k]] for k in kinds
                                           if k not in ("adamw", "dequant", "quantize")}},
         "roofline_adamw": {"kernel": "lora_adamw_step_many (A and B of all 7 adapters, one launch)",

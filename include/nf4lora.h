@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 7
+#define NF4LORA_ABI_VERSION 8
 
 enum nf4_status {
   NF4_OK = 0,
@@ -300,6 +300,39 @@ int nf4_linear_fwd_group(const void* x, nf4_dtype dtype, int64_t M, int64_t K, i
  * every call with these sizes). Host-only; NF4_EINVAL (negative) for NULL
  * arrays, a count outside 1..NF4_MAX_PROJECTIONS_PER_GROUP or invalid sizes. */
 int64_t nf4_linear_fwd_group_workspace_bytes(int64_t M, int64_t K, int32_t count, const int64_t* N, const int32_t* r);
+
+/* Summed input gradient of `count` (1 to NF4_MAX_PROJECTIONS_PER_GROUP)
+ * projections of one activation (the gradient a block's x receives from q, k
+ * and v, or from gate and up; same page, sections "Adapter API" and "Fused GPU
+ * NF4 decodes inside the matrix kernel"): dX = sum_i (dY[i] W[i]_hat +
+ * s[i] (dY[i] B[i]) A[i]), dY[i] [M,N[i]] and dX [M,K] `dtype`, W[i]->n ==
+ * N[i]*K, A[i], B[i], r[i], s[i], u_out[i] as in nf4_linear_bwd_input (A, B
+ * and u_out may be NULL arrays: all entries NULL). The host arrays are read
+ * during the call only; dX must not overlap any dY[i]. For bf16, when the
+ * projections are all single or all double quantized, each N[i] is a multiple
+ * of 64 and dX has more than half a round of 256 x 256 tiles, the products
+ * run as one launch set whose fp32 accumulators take every projection's
+ * reduction in turn and then every adapter term in projection order (one
+ * rounding to bf16); otherwise each projection runs as its own
+ * nf4_linear_bwd_input (projection 0 into dX, the others into the workspace)
+ * and the parts are added in projection order, each rounded to `dtype` first.
+ * `workspace` (256-byte aligned) holds at most
+ * nf4_linear_bwd_input_sum_workspace_bytes(M, K, count, N, r, dtype) bytes,
+ * else NF4_EWORKSPACE. Every argument error is returned before any launch. */
+int nf4_linear_bwd_input_sum(const void* const* dy, nf4_dtype dtype, int64_t M, int64_t K, int32_t count,
+                             const nf4_tensor* const* W, const int64_t* N, const float* const* A,
+                             const float* const* B, const int32_t* r, const float* s, void* dx,
+                             float* const* u_out, void* workspace, size_t workspace_bytes, nf4_stream_t stream);
+
+/* Workspace bytes of nf4_linear_bwd_input_sum with no u_out, on either path
+ * (an upper bound for every call with these sizes): each projection's
+ * nf4_linear_workspace_bytes with NF4_WS_BACKWARD | NF4_WS_NO_SIDE_OUT and
+ * count - 1 outputs of M x K `dtype`, each rounded up to 256. Host-only;
+ * NF4_EINVAL (negative) for NULL arrays, a count outside
+ * 1..NF4_MAX_PROJECTIONS_PER_GROUP or invalid sizes; NF4_EUNSUPPORTED for an
+ * unknown dtype. */
+int64_t nf4_linear_bwd_input_sum_workspace_bytes(int64_t M, int64_t K, int32_t count, const int64_t* N,
+                                                 const int32_t* r, nf4_dtype dtype);
 
 /* LoRA factor gradients (Aner docs "Native model adaptation and NF4", sections
  * "Adapter API" and "LoRA FA includes gradient preconditioning"):

@@ -456,6 +456,59 @@ int64_t nf4_linear_fwd_group_workspace_bytes(int64_t M, int64_t K, int32_t count
   return need;
 }
 
+int nf4_linear_bwd_input_sum(const void* const* dy, nf4_dtype dtype, int64_t M, int64_t K, int32_t count,
+                             const nf4_tensor* const* W, const int64_t* N, const float* const* A,
+                             const float* const* B, const int32_t* r, const float* s, void* dx,
+                             float* const* u_out, void* workspace, size_t workspace_bytes, nf4_stream_t stream) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (count < 1 || count > NF4_MAX_PROJECTIONS_PER_GROUP || !dy || !W || !N || !r || !s || !dx) return NF4_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return NF4_EALIGN;
+  if (!aligned(dx, 16)) return NF4_EALIGN;
+  LinearArgs g[NF4_MAX_PROJECTIONS_PER_GROUP];
+  int64_t need = 0;
+  char* base = static_cast<char*>(workspace);
+  for (int i = 0; i < count; ++i) {
+    const float* Ai = A ? A[i] : nullptr;
+    const float* Bi = B ? B[i] : nullptr;
+    float* side = u_out ? u_out[i] : nullptr;
+    const int32_t ri = r[i];
+    if (!dy[i] || !linear_sizes_ok(M, K, N[i])) return NF4_EINVAL;
+    if (int rc = check_tensor(W[i], N[i] * K)) return rc;
+    if (ri < 0 || ri > 256) return NF4_EINVAL;
+    if (ri > 0 && (!Ai || !Bi || ri > (K < N[i] ? K : N[i]) || !std::isfinite(s[i]))) return NF4_EINVAL;
+    if (!aligned(dy[i], 16)) return NF4_EALIGN;
+    if (ri > 0 && (!aligned(Ai, 4) || !aligned(Bi, 4) || (side && !aligned(side, 4)))) return NF4_EALIGN;
+    const LinearWs w = linear_ws(dtype, M, K, N[i], ri, ri > 0 && !side, true);
+    char* part = base ? base + need : nullptr;
+    float* side_part = w.side_part > 0 ? reinterpret_cast<float*>(part + w.split) : nullptr;
+    if (w.side > 0) side = reinterpret_cast<float*>(part + w.split + w.side_part);
+    g[i] = LinearArgs{dy[i], dtype, M, K, N[i], W[i], Ai, Bi, ri, s[i], dx, side, true, part, (size_t)w.split,
+                      side_part};
+    need += (int64_t)round_up((size_t)w.total(), 256);
+  }
+  void* tmp = nullptr;
+  if (!linear_bwd_sum_one_launch(g, count) && count > 1) {
+    tmp = base ? base + need : nullptr;
+    need += (int64_t)round_up((size_t)(count - 1) * (dtype == NF4_BF16 ? 2 : 4) * (size_t)(M * K), 256);
+  }
+  if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return NF4_EWORKSPACE;
+  if (int rc = check_device()) return rc;
+  return launch_linear_bwd_sum(g, count, tmp, as_stream(stream));
+}
+
+int64_t nf4_linear_bwd_input_sum_workspace_bytes(int64_t M, int64_t K, int32_t count, const int64_t* N,
+                                                 const int32_t* r, nf4_dtype dtype) {
+  if (!valid_dtype(dtype)) return NF4_EUNSUPPORTED;
+  if (count < 1 || count > NF4_MAX_PROJECTIONS_PER_GROUP || !N || !r) return NF4_EINVAL;
+  int64_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!linear_sizes_ok(M, K, N[i]) || r[i] < 0 || r[i] > 256) return NF4_EINVAL;
+    need += (int64_t)round_up((size_t)linear_ws(dtype, M, K, N[i], r[i], r[i] > 0, true).total(), 256);
+  }
+  if (count > 1) need += (int64_t)round_up((size_t)(count - 1) * (dtype == NF4_BF16 ? 2 : 4) * (size_t)(M * K), 256);
+  return need;
+}
+
 int64_t nf4_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t r, int flags) {
   if (!linear_sizes_ok(M, K, N) || r < 0 || r > 256) return NF4_EINVAL;
   if (flags & ~(NF4_WS_BACKWARD | NF4_WS_NO_SIDE_OUT)) return NF4_EINVAL;

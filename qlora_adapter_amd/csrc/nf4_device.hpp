@@ -69,5 +69,7 @@ bool fast_linear_applies(const LinearArgs& g);
 int launch_linear_fast(const LinearArgs& g, hipStream_t st);
 bool group_gemm_applies(const LinearArgs* g, int n);
 int launch_linear_fast_group(const LinearArgs* g, int n, hipStream_t st);
+bool group_sum_applies(const LinearArgs* g, int n);
+int launch_linear_fast_sum(const LinearArgs* g, int n, hipStream_t st);
 
 }  // namespace nf4

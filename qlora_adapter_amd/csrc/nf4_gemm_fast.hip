@@ -1121,11 +1121,16 @@ __device__ __forceinline__ void gemm_store_tile(const f32x16 (&acc)[MS][NT], __b
 // own arguments) first; part i owns the column tiles from ct0 on and brings its
 // weight, factor B, side product T, output, width and adapter rank and scale.
 // Each output tile is computed exactly as in a call of its projection alone.
+// With GS (input gradient), the call instead sums the input gradients of the
+// projections: dX = sum_i (dY_i W_i + s_i U_i A_i), the reduction run as one
+// segment per projection (its dY, weight and width) into the same
+// accumulators, then every projection's adapter term, in projection order.
 struct GemmPart {
   NF4View w;
   const float* F;
   const float* S;
   __bf16* out;
+  const __bf16* act;  // (input-gradient sum: this projection's dY)
   int64_t N, ct0;
   int r;
   float s;
@@ -1137,7 +1142,7 @@ struct GemmGroup {
   int64_t ct;  // column tiles of all of them
 };
 
-template <bool BWD, bool DQ, int NT, int MS>
+template <bool BWD, bool DQ, int NT, int MS, bool GS = false>
 __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __restrict__ act, int64_t M, int64_t K,
                                                             int64_t N, NF4View w, const float* __restrict__ F, int r,
                                                             float s, const float* __restrict__ S,
@@ -1178,125 +1183,160 @@ __global__ __launch_bounds__(64 * (16 / NT), 1) void k_gemm(const __bf16* __rest
         ct = cg - q.ct0;
       }
   }
-  const int64_t R = BWD ? N : K, C = BWD ? K : N;
+  static_assert(!GS || BWD, "summed groups are input gradients");
+  int64_t R = BWD ? N : K;
+  const int64_t C = BWD ? K : N;
   // The tile origin is workgroup-uniform; stated explicitly (scalar registers),
   // so that the activation loads' buffer resource is scalar too (otherwise the
   // compiler may wrap each of those loads in a loop over distinct lane values).
   const int64_t m0 = uniform64(mt * GT + (MS == 4 ? 0 : BM * (xb & 1))), c0 = uniform64(ct * GT);
-  const int64_t KT = R / 64, KB = K / 64;
+  const int64_t KB = K / 64;
   if (DQ && tid < 256) d8s[tid] = dyn8_value((uint32_t)tid);
-  const float mu = DQ ? w.offset[0] : 0.0f;
-
-  // Activation loads: lane l of instruction i writes physical chunk l % 8 of
-  // stage row 8 (NW i + wave) + l / 8, i.e. logical chunk (l % 8) ^ swz(row).
-  // Rows past M are clamped (not stored).
-  // (every offset used stays below 256 rows x 2^23 bytes = 2^31)
-  const int64_t abytes = 2 * (M - m0) * R;
-  const __bf16* at = act + m0 * R;
-  const int an = (int)(abytes < 0x7fffffff ? abytes : 0x7fffffff);
-  uint32_t aoff[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = 8 * (NW * i + wave) + (lane >> 3);
-    const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
-    aoff[i] = (uint32_t)(2 * m * R) + 16 * ((lane & 7) ^ swz(row));
-  }
-
-  // This lane's code words per step (at w.codes + kt * cstep + cofs, block
-  // kt * bstep + blane) and where its decoded chunks go: word u to element
-  // wbase + 8 (u ^ wsx) of the weight stage.
-  uint32_t cofs, blane;
-  int64_t cstep, bstep;
-  int wbase, wsx;
-  if (!BWD) {  // weight row c0 + rl (clamped past N), words h DW .. of block kt, h = tid % LPR
-    // Within each group of 8 rows, lane pairs take rows 0 2 4 6 1 3 5 7: the 8
-    // lanes of one 128-byte store phase then write 8 different bank groups.
-    const int t = tid / LPR, h = tid % LPR;
-    const int rl = (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1);
-    const int64_t n = (c0 + rl < N) ? c0 + rl : N - 1;
-    cofs = (uint32_t)(n * (K / 2) + 4 * DW * h);
-    blane = (uint32_t)(n * KB);
-    cstep = 32;
-    bstep = 1;
-    wbase = rl * 64;
-    wsx = swz(rl) ^ (DW * h);  // chunk (DW h + u) ^ swz(rl) = u ^ wsx for u < DW
-  } else {  // weight row 64 kt + rr, columns kc .. kc + 8 DW - 1 (clamped past K): block wave / 2 of the
-            // tile, half lane % 2, so that the two halves of a block are adjacent lanes (LPR = 2)
-    const int rr = (lane >> 1) + 32 * (wave & 1), half = lane & 1;
-    const int64_t kcol = c0 + 64 * (wave >> 1) + 8 * DW * half;
-    const int64_t kc = kcol < K ? kcol : K - 8 * DW;
-    cofs = (uint32_t)(rr * (K / 2) + kc / 2);
-    blane = (uint32_t)(rr * KB + kc / 64);
-    cstep = 64 * (K / 2);
-    bstep = 64 * KB;
-    wbase = rr * WPB + 64 * (wave >> 1) + 8 * DW * half;  // chunks 8 (wave / 2) + 4 half .. + 3, permuted by rr % 4
-    wsx = xbr(rr);
-  }
-
   f32x16 acc[MS][NT];
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x16{};
 
-  // Step indices past the end are clamped to the last step: the surplus loads
-  // and decodes land in buffers that are not read again, and the loop body has
-  // a single path.
-  // (KT < 2^16 and the codes under 4 GiB: step indices and offsets fit 32 bits)
-  const int last = (int)KT - 1;
-  const int second = last < 1 ? last : 1;
-  const uint32_t csu = (uint32_t)cstep, bsu = (uint32_t)bstep;
-  const __amdgpu_buffer_rsrc_t rc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w.codes), 0, (int)(uint32_t)(N * (K / 2)), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(w.scales), 0, (int)(uint32_t)((DQ ? 1 : 4) * N * KB), 0x00020000);
-  WCodes<DW> ca, cb;
-  gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
-  gemm_load_codes<DQ, DW>(rc, rs, w.nested, 0, cofs, 0, blane, ca);
-  gemm_load_codes<DQ, DW>(rc, rs, w.nested, second * csu, cofs, second * bsu, blane, cb);
-  // The two lanes of a weight block (adjacent, LPR = 2) share its table; this
-  // lane's code values are entries 8 (lane % 2) ..
-  static_assert(LPR == 2 && DW == 4, "pair tables need two lanes per block");
-  float cs[8];
+  // One reduction segment (GS: one per projection of the group, each with its
+  // own dY, weight and width; the stages are reused once every wave is done
+  // with the previous segment's).
+  const int nseg = GS ? grp.n : 1;
+  for (int seg = 0; seg < nseg; ++seg) {
+    if constexpr (GS) {
+      if (seg > 0) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) cs[k] = __uint_as_float(kC4Bits[(lane & 1) ? 8 + k : k]);
-  __syncthreads();  // d8s
-  {
-    const float sc0 = gemm_block_scale<DQ, DW>(ca, d8s, mu);
-    const Bf16Table tb = build_table_pair(sc0, cs);
-#pragma unroll
-    for (int u = 0; u < DW; ++u) gemm_decode_word<BWD>(ca.q[u], tb, ws0 + wbase + 8 * (u ^ wsx));
-  }
-  __syncthreads();  // stage 0 complete
+        for (int i = 0; i < kGroupMax - 1; ++i)
+          if (seg == i + 1) {
+            act = grp.p[i].act;
+            w = grp.p[i].w;
+            N = grp.p[i].N;
+          }
+        R = N;
+        __syncthreads();
+      }
+    }
+    const int64_t KT = R / 64;
+    const float mu = DQ ? w.offset[0] : 0.0f;
 
-  // Step kt multiplies stage kt % 2 while the activations of step kt + 1 land
-  // in the other stage, the codes of step kt + 2 are loaded and the codes of
-  // step kt + 1 are decoded into the other weight stage.
-  for (int kt = 0; kt < (int)KT; kt += 2) {
-    const int k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
-              k3 = kt + 3 < last ? kt + 3 : last;
-    // (The scale's table read precedes the activation loads: an LDS read
-    // issued after them would wait for them.)
-    float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
-    __builtin_amdgcn_sched_barrier(0);
-    gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k1), aoff, as1, wave);
-    __builtin_amdgcn_sched_barrier(0);
-    gemm_load_codes<DQ, DW>(rc, rs, w.nested, k2 * csu, cofs, k2 * bsu, blane, ca);
-    gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx, cs);
-    gemm_step_barrier<NCL>();
-    if (kt + 1 >= (int)KT) break;
-    sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
-    __builtin_amdgcn_sched_barrier(0);
-    gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k2), aoff, as0, wave);
-    __builtin_amdgcn_sched_barrier(0);
-    gemm_load_codes<DQ, DW>(rc, rs, w.nested, k3 * csu, cofs, k3 * bsu, blane, cb);
-    gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx, cs);
-    gemm_step_barrier<NCL>();
-  }
+    // Activation loads: lane l of instruction i writes physical chunk l % 8 of
+    // stage row 8 (NW i + wave) + l / 8, i.e. logical chunk (l % 8) ^ swz(row).
+    // Rows past M are clamped (not stored).
+    // (every offset used stays below 256 rows x 2^23 bytes = 2^31)
+    const int64_t abytes = 2 * (M - m0) * R;
+    const __bf16* at = act + m0 * R;
+    const int an = (int)(abytes < 0x7fffffff ? abytes : 0x7fffffff);
+    uint32_t aoff[NA];
+  #pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int row = 8 * (NW * i + wave) + (lane >> 3);
+      const int64_t m = (m0 + row < M) ? row : M - 1 - m0;
+      aoff[i] = (uint32_t)(2 * m * R) + 16 * ((lane & 7) ^ swz(row));
+    }
+
+    // This lane's code words per step (at w.codes + kt * cstep + cofs, block
+    // kt * bstep + blane) and where its decoded chunks go: word u to element
+    // wbase + 8 (u ^ wsx) of the weight stage.
+    uint32_t cofs, blane;
+    int64_t cstep, bstep;
+    int wbase, wsx;
+    if (!BWD) {  // weight row c0 + rl (clamped past N), words h DW .. of block kt, h = tid % LPR
+      // Within each group of 8 rows, lane pairs take rows 0 2 4 6 1 3 5 7: the 8
+      // lanes of one 128-byte store phase then write 8 different bank groups.
+      const int t = tid / LPR, h = tid % LPR;
+      const int rl = (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1);
+      const int64_t n = (c0 + rl < N) ? c0 + rl : N - 1;
+      cofs = (uint32_t)(n * (K / 2) + 4 * DW * h);
+      blane = (uint32_t)(n * KB);
+      cstep = 32;
+      bstep = 1;
+      wbase = rl * 64;
+      wsx = swz(rl) ^ (DW * h);  // chunk (DW h + u) ^ swz(rl) = u ^ wsx for u < DW
+    } else {  // weight row 64 kt + rr, columns kc .. kc + 8 DW - 1 (clamped past K): block wave / 2 of the
+              // tile, half lane % 2, so that the two halves of a block are adjacent lanes (LPR = 2)
+      const int rr = (lane >> 1) + 32 * (wave & 1), half = lane & 1;
+      const int64_t kcol = c0 + 64 * (wave >> 1) + 8 * DW * half;
+      const int64_t kc = kcol < K ? kcol : K - 8 * DW;
+      cofs = (uint32_t)(rr * (K / 2) + kc / 2);
+      blane = (uint32_t)(rr * KB + kc / 64);
+      cstep = 64 * (K / 2);
+      bstep = 64 * KB;
+      wbase = rr * WPB + 64 * (wave >> 1) + 8 * DW * half;  // chunks 8 (wave / 2) + 4 half .. + 3, permuted by rr % 4
+      wsx = xbr(rr);
+    }
+
+
+    // Step indices past the end are clamped to the last step: the surplus loads
+    // and decodes land in buffers that are not read again, and the loop body has
+    // a single path.
+    // (KT < 2^16 and the codes under 4 GiB: step indices and offsets fit 32 bits)
+    const int last = (int)KT - 1;
+    const int second = last < 1 ? last : 1;
+    const uint32_t csu = (uint32_t)cstep, bsu = (uint32_t)bstep;
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w.codes), 0, (int)(uint32_t)(N * (K / 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(w.scales), 0, (int)(uint32_t)((DQ ? 1 : 4) * N * KB), 0x00020000);
+    WCodes<DW> ca, cb;
+    gemm_issue_act<NA, NW>(at, an, 0, aoff, as0, wave);
+    gemm_load_codes<DQ, DW>(rc, rs, w.nested, 0, cofs, 0, blane, ca);
+    gemm_load_codes<DQ, DW>(rc, rs, w.nested, second * csu, cofs, second * bsu, blane, cb);
+    // The two lanes of a weight block (adjacent, LPR = 2) share its table; this
+    // lane's code values are entries 8 (lane % 2) ..
+    static_assert(LPR == 2 && DW == 4, "pair tables need two lanes per block");
+    float cs[8];
+  #pragma unroll
+    for (int k = 0; k < 8; ++k) cs[k] = __uint_as_float(kC4Bits[(lane & 1) ? 8 + k : k]);
+    __syncthreads();  // d8s
+    {
+      const float sc0 = gemm_block_scale<DQ, DW>(ca, d8s, mu);
+      const Bf16Table tb = build_table_pair(sc0, cs);
+  #pragma unroll
+      for (int u = 0; u < DW; ++u) gemm_decode_word<BWD>(ca.q[u], tb, ws0 + wbase + 8 * (u ^ wsx));
+    }
+    __syncthreads();  // stage 0 complete
+
+    // Step kt multiplies stage kt % 2 while the activations of step kt + 1 land
+    // in the other stage, the codes of step kt + 2 are loaded and the codes of
+    // step kt + 1 are decoded into the other weight stage.
+    for (int kt = 0; kt < (int)KT; kt += 2) {
+      const int k1 = kt + 1 < last ? kt + 1 : last, k2 = kt + 2 < last ? kt + 2 : last,
+                k3 = kt + 3 < last ? kt + 3 : last;
+      // (The scale's table read precedes the activation loads: an LDS read
+      // issued after them would wait for them.)
+      float sc = gemm_block_scale<DQ, DW>(cb, d8s, mu);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k1), aoff, as1, wave);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_load_codes<DQ, DW>(rc, rs, w.nested, k2 * csu, cofs, k2 * bsu, blane, ca);
+      gemm_step<BWD, true, MS, NT, DW>(as0, ws0, acc, lane, wm, cw, cb, sc, ws1, wbase, wsx, cs);
+      gemm_step_barrier<NCL>();
+      if (kt + 1 >= (int)KT) break;
+      sc = gemm_block_scale<DQ, DW>(ca, d8s, mu);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_issue_act<NA, NW>(at, an, (uint32_t)(128 * k2), aoff, as0, wave);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_load_codes<DQ, DW>(rc, rs, w.nested, k3 * csu, cofs, k3 * bsu, blane, cb);
+      gemm_step<BWD, true, MS, NT, DW>(as1, ws1, acc, lane, wm, cw, ca, sc, ws0, wbase, wsx, cs);
+      gemm_step_barrier<NCL>();
+    }
+  }  // segments
 
   // (The two paths store separately, so that no join merges the accumulators.)
   const int64_t cc = c0 + cw;
   const bool whole = C % 8 == 0;
+  if constexpr (GS) {  // every projection's adapter term, in projection order, then the store
+    if (r > 0) gemm_lora<BWD, MS, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
+#pragma unroll
+    for (int i = 0; i < kGroupMax - 1; ++i)
+      if (i + 1 < grp.n && grp.p[i].r > 0)
+        gemm_lora<BWD, MS, NT>(acc, M, K, N, grp.p[i].F, grp.p[i].r, grp.p[i].s, grp.p[i].S, m0, cc, lane, wm);
+    if (whole)
+      gemm_store_tile<BWD, MS, NT>(acc, out, M, C, m0, c0, cw, tid, wm, ws0, ws1, as0, as1);
+    else
+      gemm_store<BWD, MS, NT>(acc, out, M, C, m0, cc, lane, wm);
+    return;
+  }
   if (r > 0) {
     gemm_lora<BWD, MS, NT>(acc, M, K, N, F, r, s, S, m0, cc, lane, wm);
     if (whole)
@@ -1446,7 +1486,7 @@ namespace {
 // and the further parts in grp): whole tiles fill complete rounds of the chip
 // (one workgroup per CU); a last round of at most half the CUs is run as twice
 // as many half tiles.
-template <bool BWD, bool DQ>
+template <bool BWD, bool DQ, bool GS = false>
 void launch_gemm256(const LinearArgs& g, const NF4View& w, const GemmGroup& grp, int64_t tiles, hipStream_t st) {
   const __bf16* a = static_cast<const __bf16*>(g.a);
   __bf16* o = static_cast<__bf16*>(g.out);
@@ -1456,11 +1496,11 @@ void launch_gemm256(const LinearArgs& g, const NF4View& w, const GemmGroup& grp,
   const int64_t cus = device_cu_count();
   const int64_t tail = tiles > cus ? tiles % cus : 0;
   const int64_t whole = (tail > 0 && 2 * tail <= cus) ? tiles - tail : tiles;
-  hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 4>), dim3((unsigned)whole), block, 0, st, a, g.M, g.K, g.N, w, F, g.r, g.s,
-                     g.side, o, (int64_t)0, grp);
+  hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 4, GS>), dim3((unsigned)whole), block, 0, st, a, g.M, g.K, g.N, w, F, g.r,
+                     g.s, g.side, o, (int64_t)0, grp);
   if (whole < tiles)
-    hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 2>), dim3((unsigned)(2 * (tiles - whole))), block, 0, st, a, g.M, g.K,
-                       g.N, w, F, g.r, g.s, g.side, o, whole, grp);
+    hipLaunchKernelGGL((k_gemm<BWD, DQ, NT, 2, GS>), dim3((unsigned)(2 * (tiles - whole))), block, 0, st, a, g.M,
+                       g.K, g.N, w, F, g.r, g.s, g.side, o, whole, grp);
 }
 
 }  // namespace
@@ -1507,6 +1547,46 @@ int launch_linear_fast_group(const LinearArgs* g, int n, hipStream_t st) {
     launch_gemm256<false, true>(g[0], w, grp, tiles, st);
   else
     launch_gemm256<false, false>(g[0], w, grp, tiles, st);
+  return launch_status();
+}
+
+// A summed input gradient takes the 256 x 256 kernel as one launch set when its
+// 2 to 4 projections share M and K (the output), are all single or all double
+// quantized, each meets the input-gradient bounds, and the output has more than
+// half a round of tiles.
+bool group_sum_applies(const LinearArgs* g, int n) {
+  if (n < 2 || n > kGroupMax) return false;
+  for (int i = 0; i < n; ++i) {
+    const LinearArgs& q = g[i];
+    if (q.dtype != NF4_BF16 || !q.backward || q.M != g[0].M || q.K != g[0].K) return false;
+    if (q.W->double_quant != g[0].W->double_quant || !fast_shape_ok(q.K, q.N, true)) return false;
+  }
+  const int64_t M = g[0].M, K = g[0].K;
+  return K % 4 == 0 && 2 * M * K < (int64_t(1) << 31) && ceil_div(M, GT) * ceil_div(K, GT) >= kGemmMinTiles;
+}
+
+// The summed input gradient's matrix products (the side products U already
+// written), into g[0].out: projection 0 through the kernel's arguments, the
+// others through GemmGroup.
+int launch_linear_fast_sum(const LinearArgs* g, int n, hipStream_t st) {
+  GemmGroup grp{};
+  grp.n = n;
+  for (int i = 1; i < n; ++i) {
+    GemmPart& q = grp.p[i - 1];
+    q.w = make_view(g[i].W);
+    q.F = g[i].A;
+    q.S = g[i].side;
+    q.act = static_cast<const __bf16*>(g[i].a);
+    q.N = g[i].N;
+    q.r = g[i].r;
+    q.s = g[i].s;
+  }
+  const int64_t tiles = ceil_div(g[0].M, GT) * ceil_div(g[0].K, GT);
+  const NF4View w = make_view(g[0].W);
+  if (g[0].W->double_quant)
+    launch_gemm256<true, true, true>(g[0], w, grp, tiles, st);
+  else
+    launch_gemm256<true, false, true>(g[0], w, grp, tiles, st);
   return launch_status();
 }
 

@@ -74,6 +74,10 @@ struct LinearArgs {
 int64_t linear_fast_workspace_bytes(int64_t M, int64_t K, int64_t N, bool backward);
 int launch_linear(const LinearArgs& a, hipStream_t s);
 int launch_linear_group(const LinearArgs* a, int n, hipStream_t s);
+// Summed input gradient of n projections into a[0].out; `tmp` holds n - 1
+// outputs of M x K (dtype) when the one-launch path does not apply.
+bool linear_bwd_sum_one_launch(const LinearArgs* a, int n);
+int launch_linear_bwd_sum(const LinearArgs* a, int n, void* tmp, hipStream_t s);
 // Side product alone: out[m][rho] = sum_i L[m][i] R[i][rho] (fp32 [M, r]), with
 // R[i][rho] = fac[rho][i] (backward = false: T = x A^T, I = K) or fac[i][rho]
 // (backward = true: U = dY B, I = N). `part` holds side_split_ws_bytes(M, I, r)

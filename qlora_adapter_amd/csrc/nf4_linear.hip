@@ -1260,6 +1260,35 @@ int launch_linear_group(const LinearArgs* g, int n, hipStream_t st) {
   return launch_linear_fast_group(g, n, st);
 }
 
+bool linear_bwd_sum_one_launch(const LinearArgs* g, int n) { return group_sum_applies(g, n); }
+
+// Summed input gradient dX = sum_i (dY_i W_i + s_i U_i A_i) of n projections
+// of one activation: their side products U_i, then one launch set of the
+// matrix kernel whose reduction runs over every projection in turn; otherwise
+// projection 0's call into dX and each other's into tmp, added in projection
+// order (each part rounded to the output type first).
+int launch_linear_bwd_sum(const LinearArgs* g, int n, void* tmp, hipStream_t st) {
+  if (group_sum_applies(g, n)) {
+    for (int i = 0; i < n; ++i) launch_side<__bf16>(g[i], st);
+    return launch_linear_fast_sum(g, n, st);
+  }
+  const size_t esz = g[0].dtype == NF4_BF16 ? 2 : 4;
+  const int64_t MK = g[0].M * g[0].K;
+  if (int rc = launch_linear(g[0], st)) return rc;
+  for (int i = 1; i < n; ++i) {
+    LinearArgs q = g[i];
+    q.out = static_cast<char*>(tmp) + (size_t)(i - 1) * esz * (size_t)MK;
+    if (int rc = launch_linear(q, st)) return rc;
+  }
+  char* t = static_cast<char*>(tmp);
+  for (int i = 1; i < n; i += 2) {
+    const void* c = i + 1 < n ? t + (size_t)i * esz * (size_t)MK : nullptr;
+    if (int rc = launch_add3(g[0].out, t + (size_t)(i - 1) * esz * (size_t)MK, c, g[0].dtype, MK, g[0].out, st))
+      return rc;
+  }
+  return launch_status();
+}
+
 // Tokens per chunk of the bf16 MFMA reduction (a multiple of the 32-token
 // step), for about 512 workgroups of 256 columns (two per CU):
 //  - with dA, both reductions take 512 / (tiles(K) + tiles(N)) chunks, so every

@@ -26,6 +26,7 @@ _DT = {torch.float32: NF4_F32, torch.bfloat16: NF4_BF16}
 EXPORTS = ["nf4_layout", "nf4_code_tables", "nf4_quantize", "nf4_quantize_noalloc", "nf4_quantize_noalloc_max_elements",
            "nf4_quantize_many", "nf4_quantize_many_workspace_bytes", "nf4_dequantize", "nf4_dequantize_many",
            "nf4_embedding_rows", "nf4_linear_fwd", "nf4_linear_fwd_group", "nf4_linear_fwd_group_workspace_bytes",
+           "nf4_linear_bwd_input_sum", "nf4_linear_bwd_input_sum_workspace_bytes",
            "nf4_linear_bwd_input", "nf4_linear_workspace_bytes", "lora_grad", "lora_grad_workspace_bytes", "lorafa_preconditioner",
            "lorafa_preconditioner_workspace_bytes", "lora_adamw_step", "lora_adamw_step_many", "lora_adamw_step_paged",
            "nf4_add_rmsnorm", "nf4_rmsnorm_bwd", "nf4_rope", "nf4_attention_fwd", "nf4_attention_bwd", "nf4_swiglu",
@@ -103,6 +104,14 @@ def load() -> ctypes.CDLL:
                                                  ctypes.POINTER(ctypes.c_void_p), P, ctypes.c_size_t, P]
             lib.nf4_linear_fwd_group_workspace_bytes.restype = I64
             lib.nf4_linear_fwd_group_workspace_bytes.argtypes = [I64, I64, I32, ctypes.POINTER(I64), ctypes.POINTER(I32)]
+            lib.nf4_linear_bwd_input_sum.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, I64, I64, I32,
+                                                     ctypes.POINTER(ctypes.POINTER(_Tensor)), ctypes.POINTER(I64),
+                                                     ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.POINTER(I32), ctypes.POINTER(F), P,
+                                                     ctypes.POINTER(ctypes.c_void_p), P, ctypes.c_size_t, P]
+            lib.nf4_linear_bwd_input_sum_workspace_bytes.restype = I64
+            lib.nf4_linear_bwd_input_sum_workspace_bytes.argtypes = [I64, I64, I32, ctypes.POINTER(I64),
+                                                                     ctypes.POINTER(I32), ctypes.c_int]
             lib.nf4_linear_bwd_input.argtypes = [P, ctypes.c_int, I64, I64, ctypes.POINTER(_Tensor), I64, P, P, I32,
                                                  F, P, P, P, ctypes.c_size_t, P]
             lib.nf4_linear_workspace_bytes.restype = I64
@@ -513,6 +522,74 @@ def linear_fwd_group(x: torch.Tensor, Ws: Sequence[NF4Tensor], As: Sequence[Opti
                                        VP(*[_addr(y) for y in ys]), VP(*[_addr(t) for t in t_outs]), _ptr(workspace), wsb,
                                        _stream(x.device)))
     return ys, t_outs
+
+
+def linear_bwd_input_sum_workspace_bytes(M: int, K: int, N: Sequence[int], r: Sequence[int],
+                                         dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of linear_bwd_input_sum with these widths and ranks and
+    no u_outs (an upper bound for every such call)."""
+    n = len(N)
+    if n != len(r) or dtype not in _DT:
+        raise ValueError("N and r need equal lengths and dtype bfloat16 or float32")
+    v = int(load().nf4_linear_bwd_input_sum_workspace_bytes(int(M), int(K), n, (ctypes.c_int64 * n)(*map(int, N)),
+                                                            (ctypes.c_int32 * n)(*map(int, r)), _DT[dtype]))
+    if v < 0:
+        _check("nf4_linear_bwd_input_sum_workspace_bytes", v)
+    return v
+
+
+def linear_bwd_input_sum(dys: Sequence[torch.Tensor], Ws: Sequence[NF4Tensor], As: Sequence[Optional[torch.Tensor]],
+                         Bs: Sequence[Optional[torch.Tensor]], s: Sequence[float], dx: Optional[torch.Tensor] = None,
+                         u_outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                         workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, List[Optional[torch.Tensor]]]:
+    """Input gradient of one activation read by up to MAX_PROJECTIONS_PER_GROUP
+    projections (e.g. q, k and v): dX = sum_i (dY[i] W[i] + s[i] (dY[i] B[i])
+    A[i]). Returns (dX, Us); U[i] = dY[i] B[i] is allocated here for adapted
+    projections when u_outs is not given."""
+    n = len(Ws)
+    if not 1 <= n <= MAX_PROJECTIONS_PER_GROUP or not (len(dys) == len(As) == len(Bs) == len(s) == n):
+        raise ValueError(f"linear_bwd_input_sum takes 1..{MAX_PROJECTIONS_PER_GROUP} projections with one dY, A, B, "
+                         "s each")
+    dt = dys[0].dtype
+    if dt not in _DT or any(d.dim() != 2 or d.dtype != dt for d in dys):
+        raise ValueError("every dY must be a [M, N] tensor of one dtype, bfloat16 or float32")
+    M = dys[0].shape[0]
+    K = Ws[0].shape[1]
+    u_outs = list(u_outs) if u_outs is not None else [None] * n
+    if len(u_outs) != n:
+        raise ValueError("u_outs needs one entry per projection")
+    Ns, rs = [], []
+    for i, W in enumerate(Ws):
+        N = W.shape[0]
+        if len(W.shape) != 2 or W.shape[1] != K or tuple(dys[i].shape) != (M, N):
+            raise ValueError(f"W[{i}] is {tuple(W.shape)} and dY[{i}] {tuple(dys[i].shape)}; want [N, {K}] and [{M}, N]")
+        r = _lora_rank(As[i], Bs[i], "linear_bwd_input_sum")
+        _arrays((dys[i], f"dY[{i}]", None, None), (As[i], f"A[{i}]", torch.float32, (r, K) if r else None),
+                (Bs[i], f"B[{i}]", torch.float32, (N, r) if r else None),
+                (u_outs[i], f"u_out[{i}]", torch.float32, (M, r)))
+        if r and u_outs[i] is None:
+            u_outs[i] = torch.empty((M, r), dtype=torch.float32, device=dys[0].device)
+        Ns.append(N)
+        rs.append(r)
+    _arrays((dx, "dx", dt, (M, K)))
+    if dx is None:
+        dx = torch.empty((M, K), dtype=dt, device=dys[0].device)
+    if workspace is None:
+        need = linear_bwd_input_sum_workspace_bytes(M, K, Ns, rs, dt)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dx.device) if need else None
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sts = [W.c_struct() for W in Ws]
+    VP = ctypes.c_void_p * n
+    _check("nf4_linear_bwd_input_sum",
+           load().nf4_linear_bwd_input_sum(VP(*[_addr(d) for d in dys]), _DT[dt], M, K, n,
+                                           (ctypes.POINTER(_Tensor) * n)(*[ctypes.pointer(t) for t in sts]),
+                                           (ctypes.c_int64 * n)(*Ns), VP(*[_addr(a) for a in As]),
+                                           VP(*[_addr(b) for b in Bs]), (ctypes.c_int32 * n)(*rs),
+                                           (ctypes.c_float * n)(*map(float, s)), _ptr(dx),
+                                           VP(*[_addr(u) for u in u_outs]), _ptr(workspace), wsb, _stream(dx.device)))
+    return dx, u_outs
 
 
 def linear_bwd_input(dy: torch.Tensor, W: NF4Tensor, A: Optional[torch.Tensor] = None,

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib[0].nf4lora_abi_version() == 7
+    assert lib[0].nf4lora_abi_version() == 8
 
 
 def test_layout_matches_oracle(lib, orc):
@@ -160,6 +160,36 @@ def test_grouped_forward_arguments_before_device(lib):
     assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, VPs(16, 24), ts, None, 0, None) == EALIGN
     assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, ys, ts, 128, 1 << 20, None) == EALIGN
     assert G(16, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, ys, VPs(16, None), None, 0, None) == EWS
+
+
+def test_summed_input_gradient_arguments_before_device(lib):
+    L, m = lib
+    EINVAL, EALIGN, EUNSUP, EWS = -1, -2, -3, -6
+    I64s, I32s, Fs, VPs = ctypes.c_int64 * 4, ctypes.c_int32 * 4, ctypes.c_float * 4, ctypes.c_void_p * 4
+    Q = L.nf4_linear_bwd_input_sum_workspace_bytes
+    # the per-projection workspaces with no side output plus count - 1 outputs of M x K, each rounded up to 256
+    want = sum((L.nf4_linear_workspace_bytes(4096, 4096, n, 16, 3) + 255) // 256 * 256 for n in (4096, 1024, 1024))
+    assert Q(4096, 4096, 3, I64s(4096, 1024, 1024), I32s(16, 16, 16), 1) == want + 2 * 4096 * 4096 * 2
+    assert Q(4096, 4096, 1, I64s(4096), I32s(0), 0) == L.nf4_linear_workspace_bytes(4096, 4096, 4096, 0, 1)
+    assert Q(4096, 4096, 0, I64s(1), I32s(1), 1) == EINVAL
+    assert Q(4096, 4096, 5, I64s(1), I32s(1), 1) == EINVAL
+    assert Q(4096, 4096, 2, I64s(64, 64), I32s(16, 300), 1) == EINVAL
+    assert Q(4096, 4096, 2, I64s(64, 64), I32s(16, 16), 9) == EUNSUP
+    wa, wb = m._Tensor(16, 16, 16, 16, 64 * 32, 1), m._Tensor(16, 16, 16, 16, 64 * 16, 1)
+    Ws = (ctypes.POINTER(m._Tensor) * 4)(ctypes.pointer(wa), ctypes.pointer(wb))
+    Ng, rg, sg, ab, us = I64s(32, 16), I32s(4, 4), Fs(1.0, 1.0), VPs(16, 16), VPs(16, 16)
+    G = L.nf4_linear_bwd_input_sum
+    assert G(VPs(16, 16), 7, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EUNSUP
+    assert G(VPs(16, 16), 1, 8, 64, 0, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EINVAL
+    assert G(None, 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EINVAL
+    assert G(VPs(16, None), 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EINVAL
+    assert G(VPs(16, 16), 1, 8, 64, 2, Ws, I64s(32, 15), ab, ab, rg, sg, 16, us, None, 0, None) == EINVAL
+    assert G(VPs(16, 16), 1, 8, 64, 2, Ws, Ng, None, None, rg, sg, 16, us, None, 0, None) == EINVAL
+    assert G(VPs(16, 16), 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, None, us, None, 0, None) == EINVAL
+    assert G(VPs(16, 24), 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EALIGN
+    assert G(VPs(16, 16), 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 24, us, None, 0, None) == EALIGN
+    # too few tiles for one launch: the parts' sum needs room for the other part's output
+    assert G(VPs(16, 16), 1, 8, 64, 2, Ws, Ng, ab, ab, rg, sg, 16, us, None, 0, None) == EWS
 
 
 def test_optional_side_products_and_recompute(lib):

@@ -486,3 +486,45 @@ def test_linear_fwd_group_fallbacks(gpu, orc, case):
         Wref = oracle_weight(orc, cs[0]["W"], dt, True)
         y_ref, _ = orc.linear_fwd(to_np(x), Wref, As[0].cpu().numpy(), Bs[0].cpu().numpy(), s[0])
         assert_close(to_np(ys[0]), y_ref, "f32", "y[0]")
+
+
+SUMS = [
+    # (M, K, widths, ranks, double quant): the input gradient of one activation read by several projections
+    (4096, 4096, (4096, 1024, 1024), (16, 16, 16), True),         # q, k, v at 4096 tokens: 64 + 16 + 16 steps
+    (4096, 4096, (14336, 14336), (16, 16), True),                 # gate, up at 4096 tokens: 448 steps
+    (4000, 2304, (576, 128, 1088), (8, 0, 4), False),             # odd step counts, a part with no adapter, ragged M
+    (512, 576, (576, 192, 192), (8, 8, 8), True),                 # 6 tiles: separate calls added in order
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,rs,dq", SUMS)
+def test_linear_bwd_input_sum(gpu, orc, M, K, Ns, rs, dq):
+    """Summed input gradient against the oracle's sum of the projections'
+    input gradients on sampled token rows (including the last rows), each U[i]
+    bitwise equal to its projection's own call, the whole run-to-run identical."""
+    print(f"[linear] bwd sum M={M} K={K} N={Ns} r={rs}", flush=True)
+    n = len(Ns)
+    cs = [make_case(M, K, N, max(r, 1), torch.bfloat16, seed=21 + i) for i, (N, r) in enumerate(zip(Ns, rs))]
+    dys = [c["dy"] for c in cs]
+    Ws = [gpu.quantize(c["W"], dq) for c in cs]
+    As = [c["A"] if r else None for c, r in zip(cs, rs)]
+    Bs = [c["B"] if r else None for c, r in zip(cs, rs)]
+    ss = [gpu.lora_scale(2.0 * r, r) if r else 0.0 for r in rs]
+    dx, Us = gpu.linear_bwd_input_sum(dys, Ws, As, Bs, ss)
+    dx2, _ = gpu.linear_bwd_input_sum(dys, Ws, As, Bs, ss)
+    alone = [gpu.linear_bwd_input(dys[i], Ws[i], As[i], Bs[i], ss[i]) for i in range(n)]
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2), "dx differs between runs"
+    for i, r in enumerate(rs):
+        if r:
+            assert torch.equal(Us[i], alone[i][1]), f"U[{i}]"
+    rng = np.random.default_rng(M + K + 7 * n)
+    rows = np.unique(np.concatenate([rng.choice(M - 4, 12, replace=False), np.arange(M - 4, M)]))
+    ref = 0.0
+    for i, r in enumerate(rs):
+        Wref = oracle_weight(orc, cs[i]["W"], torch.bfloat16, dq)
+        A = As[i].cpu().numpy() if r else None
+        B = Bs[i].cpu().numpy() if r else None
+        d, _ = orc.linear_bwd_input(to_np(dys[i])[rows], Wref, A, B, ss[i])
+        ref = ref + d
+    assert_close(to_np(dx)[rows], ref, "bf16", "dx rows")
