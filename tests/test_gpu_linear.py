@@ -494,6 +494,7 @@ SUMS = [
     (4096, 4096, (14336, 14336), (16, 16), True),                 # gate, up at 4096 tokens: 448 steps
     (4000, 2304, (576, 128, 1088), (8, 0, 4), False),             # odd step counts, a part with no adapter, ragged M
     (512, 576, (576, 192, 192), (8, 8, 8), True),                 # 6 tiles: separate calls added in order
+    (4000, 4352, (1024, 512), (16, 8), True),                     # 272 tiles: a last round of 16, half tiles
 ]
 
 
@@ -528,3 +529,23 @@ def test_linear_bwd_input_sum(gpu, orc, M, K, Ns, rs, dq):
         d, _ = orc.linear_bwd_input(to_np(dys[i])[rows], Wref, A, B, ss[i])
         ref = ref + d
     assert_close(to_np(dx)[rows], ref, "bf16", "dx rows")
+
+
+def test_linear_bwd_input_sum_f32(gpu, orc):
+    """fp32 summed input gradient (separate general-kernel calls added in
+    order) against the oracle's sum, in full."""
+    print("[linear] bwd sum f32", flush=True)
+    M, K, Ns, r = 300, 640, (576, 192, 64), 8
+    cs = [make_case(M, K, N, r, torch.float32, seed=31 + i) for i, N in enumerate(Ns)]
+    Ws = [gpu.quantize(c["W"], True) for c in cs]
+    s = gpu.lora_scale(16.0, r)
+    dx, Us = gpu.linear_bwd_input_sum([c["dy"] for c in cs], Ws, [c["A"] for c in cs], [c["B"] for c in cs],
+                                      [s] * len(Ns))
+    torch.cuda.synchronize()
+    ref = 0.0
+    for i, c in enumerate(cs):
+        Wref = oracle_weight(orc, c["W"], torch.float32, True)
+        d, U_ref = orc.linear_bwd_input(to_np(c["dy"]), Wref, c["A"].cpu().numpy(), c["B"].cpu().numpy(), s)
+        assert_close(Us[i].cpu().numpy(), U_ref, "f32", f"U[{i}]")
+        ref = ref + d
+    assert_close(to_np(dx), ref, "f32", "dx")
