@@ -211,9 +211,9 @@ __device__ __forceinline__ bf16x4l lds_tr16(const __bf16* p) {
 // indices 8 (l / 16) .. + 8 of each 32-wide chunk; PD chunks of loads are in
 // flight before any arithmetic (fewer for many rank tiles, to bound registers).
 // The slice sums are reduced through LDS four rank tiles at a time.
-// GRP (forward only): rank tile t is the whole adapter (rank <= 16) of
-// projection t of a grouped call, factor grp.fac[t] and output grp.out[t]
-// (so the activation rows are read once for all of them).
+// GRP (forward only, one rank tile): grid row y is projection y of a grouped
+// call, its adapter (rank <= 16) grp.fac[y] and output grp.out[y], so one
+// launch covers the side products of all the projections of a group.
 struct SideGroup {
   const float* fac[4];
   float* out[4];
@@ -224,7 +224,12 @@ template <bool BWD, int RT, bool GRP = false>
 __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L, int64_t M, int64_t I,
                                                     const float* __restrict__ fac, int r, int rho0,
                                                     float* __restrict__ outS, SideGroup grp = {}) {
-  static_assert(!GRP || !BWD, "grouped side products are forward ones");
+  static_assert(!GRP || (!BWD && RT == 1), "grouped side products are forward ones, one rank tile each");
+  if constexpr (GRP) {  // this workgroup's projection (workgroup-uniform)
+    fac = grp.fac[blockIdx.y];
+    outS = grp.out[blockIdx.y];
+    r = grp.r[blockIdx.y];
+  }
   static_assert(RT <= 4, "rank tiles per launch");
   constexpr int SW = 16, PD = RT <= 2 ? 4 : 2;
   constexpr int RR = RT < 4 ? RT : 4;  // rank tiles per reduction round
@@ -239,11 +244,7 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
   const int64_t cpw = (NC + SW - 1) / SW;
   const int64_t cb = wave * cpw, ce = (cb + cpw < NC) ? cb + cpw : NC;
   const bool vec_l = (I % 8) == 0;
-  bool vec_f = !BWD && (I % 4) == 0 && (reinterpret_cast<uintptr_t>(fac) % 16) == 0;
-  if constexpr (GRP) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) vec_f = vec_f && (reinterpret_cast<uintptr_t>(grp.fac[t]) % 16) == 0;
-  }
+  const bool vec_f = !BWD && (I % 4) == 0 && (reinterpret_cast<uintptr_t>(fac) % 16) == 0;
   f32x4 acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4{};
@@ -264,21 +265,18 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
       if (!(cok && mok)) lv[u] = bf16x8{};
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const int rho = GRP ? row : rho0 + 16 * t + row;
-        const float* __restrict__ fac_t = GRP ? grp.fac[t] : fac;
-        const int r_t = GRP ? grp.r[t] : r;
+        const int rho = rho0 + 16 * t + row;
         if (BWD) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r_t && i + e < I) ? fac_t[(i + e) * r_t + rho] : 0.0f;
-        } else if (vec_f && i + 8 <= I && rho < r_t) {
-          const float4 a = *reinterpret_cast<const float4*>(fac_t + (int64_t)rho * I + i);
-          const float4 b = *reinterpret_cast<const float4*>(fac_t + (int64_t)rho * I + i + 4);
+          for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r && i + e < I) ? fac[(i + e) * r + rho] : 0.0f;
+        } else if (vec_f && i + 8 <= I && rho < r) {
+          const float4 a = *reinterpret_cast<const float4*>(fac + (int64_t)rho * I + i);
+          const float4 b = *reinterpret_cast<const float4*>(fac + (int64_t)rho * I + i + 4);
           rv[u][t][0] = a.x; rv[u][t][1] = a.y; rv[u][t][2] = a.z; rv[u][t][3] = a.w;
           rv[u][t][4] = b.x; rv[u][t][5] = b.y; rv[u][t][6] = b.z; rv[u][t][7] = b.w;
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            rv[u][t][e] = (rho < r_t && i + e < I) ? fac_t[(int64_t)rho * I + i + e] : 0.0f;
+          for (int e = 0; e < 8; ++e) rv[u][t][e] = (rho < r && i + e < I) ? fac[(int64_t)rho * I + i + e] : 0.0f;
         }
       }
     }
@@ -319,20 +317,8 @@ __global__ __launch_bounds__(1024) void k_side_bf16(const __bf16* __restrict__ L
 #pragma unroll
       for (int w2 = 0; w2 < SW; ++w2) v += red[w2][q][e];
       const int64_t mm = m0 + (e >> 4);
-      if constexpr (GRP) {  // rank tile t0 + q is projection t0 + q's adapter
-        float* o = grp.out[0];
-        int rq = grp.r[0];
-#pragma unroll
-        for (int k = 1; k < RT; ++k)
-          if (t0 + q == k) {
-            o = grp.out[k];
-            rq = grp.r[k];
-          }
-        if (mm < M && (e & 15) < rq) o[mm * rq + (e & 15)] = v;
-      } else {
-        const int rho = rho0 + 16 * (t0 + q) + (e & 15);
-        if (mm < M && rho < r) outS[mm * r + rho] = v;
-      }
+      const int rho = rho0 + 16 * (t0 + q) + (e & 15);
+      if (mm < M && rho < r) outS[mm * r + rho] = v;
     }
   }
 }
@@ -1246,14 +1232,9 @@ int launch_linear_group(const LinearArgs* g, int n, hipStream_t st) {
       sgp.r[i] = g[i].r;
     }
     const __bf16* x = static_cast<const __bf16*>(g[0].a);
-    const dim3 grid((unsigned)ceil_div(g[0].M, SR));
-#define NF4_SIDE_GRP(RT)                                                                                           \
-  hipLaunchKernelGGL((k_side_bf16<false, RT, true>), grid, dim3(1024), 0, st, x, g[0].M, g[0].K, g[0].A, g[0].r, 0, \
-                     g[0].side, sgp)
-    if (n == 2) NF4_SIDE_GRP(2);
-    else if (n == 3) NF4_SIDE_GRP(3);
-    else NF4_SIDE_GRP(4);
-#undef NF4_SIDE_GRP
+    const dim3 grid((unsigned)ceil_div(g[0].M, SR), (unsigned)n);
+    hipLaunchKernelGGL((k_side_bf16<false, 1, true>), grid, dim3(1024), 0, st, x, g[0].M, g[0].K, g[0].A, g[0].r, 0,
+                       g[0].side, sgp);
   } else {
     for (int i = 0; i < n; ++i) launch_side<__bf16>(g[i], st);
   }
